@@ -1,0 +1,132 @@
+/*
+ * ssm_oracle.c -- plain, slow fp64 reference of the selective SSM scan.
+ *
+ * TEST INFRASTRUCTURE ONLY (see ssm_oracle.h).  Deliberately naive: one
+ * channel at a time, one token at a time, one state at a time, in the order
+ * the pages write the recurrence.  No blocking, no reordering, no threads.
+ * Callers that want several cores call it on disjoint channel ranges.
+ */
+#include "ssm_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+
+/* softplus(x) = log(1 + exp(x)).  Written so neither branch overflows or
+ * loses the small result: for x <= 0, log1p(e^x); for x > 0,
+ * x + log1p(e^-x).  No threshold: the value is the mathematical one to
+ * within libm's rounding. */
+double oracle_softplus(double x)
+{
+    if (x <= 0.0)
+        return log1p(exp(x));
+    return x + log1p(exp(-x));
+}
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^-z).  For z very negative e^-z
+ * overflows to +inf and the quotient is -0, which is the limit. */
+static double oracle_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+/* Input discretisation of one state.
+ *  zoh_b == 0: Euler, dB = dt * B ("SSM as RNN": B_scaled = B * delta).
+ *  zoh_b == 1: exact zero-order hold for a diagonal A,
+ *              dB = (exp(dt*a) - 1) / a * B  ("Discretisation", Guide
+ *              Complet section 1); at a == 0 this is its limit dt * B. */
+static double oracle_input_coeff(double dt, double a, int zoh_b)
+{
+    if (!zoh_b || a == 0.0)
+        return dt;
+    return (exp(dt * a) - 1.0) / a;
+}
+
+/* One token for one channel: updates h[0..N-1] in place and returns y.
+ * This is the loop body of the S6 forward: discretise with the token's
+ * delta, advance every state, read out through C, add the D skip, gate. */
+static double oracle_token(double *h, int64_t N, double u, double draw,
+                           const double *A_d, const double *B_t,
+                           int64_t B_stride, const double *C_t,
+                           int64_t C_stride, const double *D_d,
+                           const double *z_t, const double *bias_d,
+                           int delta_softplus, int zoh_b)
+{
+    double x = draw + (bias_d ? *bias_d : 0.0);
+    double dt = delta_softplus ? oracle_softplus(x) : x;
+    double yv = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double a = A_d[n];
+        double dA = exp(dt * a);
+        double dBu = oracle_input_coeff(dt, a, zoh_b) * B_t[n * B_stride] * u;
+        h[n] = dA * h[n] + dBu;
+    }
+    for (int64_t n = 0; n < N; ++n)
+        yv += C_t[n * C_stride] * h[n];
+    if (D_d)
+        yv += (*D_d) * u;
+    if (z_t)
+        yv *= oracle_silu(*z_t);
+    return yv;
+}
+
+int oracle_scan_f64(const double *u, const double *delta, const double *A,
+                    const double *B, const double *C, const double *D,
+                    const double *z, const double *delta_bias,
+                    int delta_softplus, int zoh_b, const double *h0,
+                    double *y, double *h_final, int64_t batch, int64_t dim,
+                    int64_t dstate, int64_t seqlen)
+{
+    double h[4096];
+    if (!u || !delta || !A || !B || !C || !y)
+        return -1;
+    if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0 || dstate > 4096)
+        return -1;
+
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            int64_t row = (b * dim + d) * seqlen;      /* (b, d, :) */
+            int64_t srow = (b * dim + d) * dstate;     /* (b, d, :) state */
+            for (int64_t n = 0; n < dstate; ++n)
+                h[n] = h0 ? h0[srow + n] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                /* B[b, n, t] and C[b, n, t]: stride seqlen between states */
+                const double *B_t = B + b * dstate * seqlen + t;
+                const double *C_t = C + b * dstate * seqlen + t;
+                y[row + t] = oracle_token(
+                    h, dstate, u[row + t], delta[row + t], A + d * dstate,
+                    B_t, seqlen, C_t, seqlen, D ? D + d : NULL,
+                    z ? z + row + t : NULL, delta_bias ? delta_bias + d : NULL,
+                    delta_softplus, zoh_b);
+            }
+            if (h_final)
+                for (int64_t n = 0; n < dstate; ++n)
+                    h_final[srow + n] = h[n];
+        }
+    }
+    return 0;
+}
+
+int oracle_step_f64(double *state, const double *x, const double *delta,
+                    const double *A, const double *B, const double *C,
+                    const double *D, const double *z,
+                    const double *delta_bias, int delta_softplus, int zoh_b,
+                    double *y, int64_t batch, int64_t dim, int64_t dstate)
+{
+    if (!state || !x || !delta || !A || !B || !C || !y)
+        return -1;
+    if (batch < 0 || dim < 0 || dstate < 0)
+        return -1;
+
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            int64_t e = b * dim + d;                   /* (b, d) */
+            y[e] = oracle_token(state + e * dstate, dstate, x[e], delta[e],
+                                A + d * dstate, B + b * dstate, 1,
+                                C + b * dstate, 1, D ? D + d : NULL,
+                                z ? z + e : NULL,
+                                delta_bias ? delta_bias + d : NULL,
+                                delta_softplus, zoh_b);
+        }
+    }
+    return 0;
+}

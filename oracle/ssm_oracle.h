@@ -1,0 +1,75 @@
+/*
+ * ssm_oracle.h -- fp64 CPU oracle for the selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this code; only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or constant with the
+ * HIP library.
+ *
+ * What it computes (every array is fp64, C-contiguous, owned by the caller):
+ *
+ *   for every (b, d):                      channels are independent
+ *     h[n] = h0[b,d,n]  (or 0)
+ *     for t = 0 .. L-1:
+ *       x      = delta[b,d,t] + bias[d]          (bias may be NULL -> 0)
+ *       dt     = softplus(x) if delta_softplus else x
+ *       for n:  dA    = exp(dt * A[d,n])
+ *               dBu   = dt * B[b,n,t] * u[b,d,t]                 (zoh_b == 0)
+ *                     = (exp(dt*A[d,n]) - 1) / A[d,n] * B[b,n,t] * u[b,d,t]
+ *                                                               (zoh_b == 1)
+ *               h[n]  = dA * h[n] + dBu
+ *       yv = sum_n C[b,n,t] * h[n]  (+ D[d] * u[b,d,t])
+ *       y[b,d,t] = yv * silu(z[b,d,t])   (z may be NULL -> no gate)
+ *     h_final[b,d,:] = h
+ *
+ * Sources (web pages this follows):
+ *  - "Mamba & State Space Models - Guide Complet", section 4 "Implementation du
+ *    SSM selectif (S6)": per-token loop with A = -exp(A_log) fixed per channel,
+ *    delta = softplus(dt_proj(x)) (bias inside the projection), A_bar =
+ *    exp(delta*A), h = h*A_bar + (..)*x_t, readout y_t = h.C_t + D*x_t;
+ *    section 1 "Discretisation": exact ZOH  B_bar = (exp(dA)-I) A^-1 B.
+ *  - "Mamba и State Space Models: альтернатива Transformer", section "SSM as
+ *    RNN": B_scaled = B*delta (Euler input discretisation), y = C*h_new
+ *    (readout after the update); section "Selective SSM": y * silu(gate).
+ *  - "Mamba: co potrafia modele przestrzeni stanow", section on selection:
+ *    delta, B and C are functions of the current token; A stays fixed.
+ */
+#ifndef SSM_ORACLE_H
+#define SSM_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Full sequential scan.  Shapes:
+ *   u, delta, z, y : (batch, dim, seqlen)     A : (dim, dstate)
+ *   B, C           : (batch, dstate, seqlen)  D, delta_bias : (dim)
+ *   h0, h_final    : (batch, dim, dstate)
+ * Nullable: D, z, delta_bias, h0, h_final.  Returns 0, or -1 on a bad
+ * argument (NULL required pointer, negative size, dstate > 4096). */
+int oracle_scan_f64(const double *u, const double *delta, const double *A,
+                    const double *B, const double *C, const double *D,
+                    const double *z, const double *delta_bias,
+                    int delta_softplus, int zoh_b, const double *h0,
+                    double *y, double *h_final, int64_t batch, int64_t dim,
+                    int64_t dstate, int64_t seqlen);
+
+/* One token of the same recurrence (the recurrent / decoding mode).
+ *   state : (batch, dim, dstate), read and written in place
+ *   x, delta, z, y : (batch, dim)     B, C : (batch, dstate)
+ * Nullable: D, z, delta_bias. */
+int oracle_step_f64(double *state, const double *x, const double *delta,
+                    const double *A, const double *B, const double *C,
+                    const double *D, const double *z,
+                    const double *delta_bias, int delta_softplus, int zoh_b,
+                    double *y, int64_t batch, int64_t dim, int64_t dstate);
+
+/* softplus(x) = log(1 + e^x), evaluated without overflow or cancellation. */
+double oracle_softplus(double x);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_ORACLE_H */
