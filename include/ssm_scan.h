@@ -1,0 +1,158 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan.
+ *
+ * Two operations, both from the Mamba selective SSM ("S6"):
+ *
+ *  ssm_scan_fwd      the whole-sequence scan.  For every (batch b, channel d)
+ *                    with a diagonal A of N states and every token t:
+ *                      dt      = softplus(delta[b,d,t] + bias[d])
+ *                      h[n]    = exp(dt*A[d,n]) * h[n] + dt*B[b,n,t]*u[b,d,t]
+ *                      y[b,d,t]= (sum_n C[b,n,t]*h[n] + D[d]*u[b,d,t])
+ *                                * silu(z[b,d,t])
+ *                    Sources: "Mamba & State Space Models - Guide Complet",
+ *                    section 4 "Implementation du SSM selectif (S6)" (A fixed
+ *                    and negative, delta/B/C per token, A_bar = exp(delta*A),
+ *                    readout h.C_t + D*x_t); the johe.ru page "Mamba и State
+ *                    Space Models", sections "SSM as RNN" (input term
+ *                    B*delta, readout after the update) and "Selective SSM"
+ *                    (output times silu(gate)); the inferownia.pl page, the
+ *                    section on the selective scan (discretisation and
+ *                    recurrence fused on chip, the expanded state never
+ *                    written to HBM).
+ *
+ *  ssm_state_update  one token of the same recurrence for every (b, d), on a
+ *                    state kept in HBM and updated in place: the recurrent
+ *                    (decoding) mode of "SSM as RNN", whose state has a fixed
+ *                    size whatever the context length.
+ *
+ * Conventions shared by all entry points
+ *  - Every array pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or retains memory; scratch space for the
+ *    long-sequence split comes from the caller (see the workspace below).
+ *  - Arrays are dense and row-major with the token axis fastest:
+ *      u, delta, z, y : (batch, dim, seqlen)      B, C : (batch, dstate, seqlen)
+ *      A              : (dim, dstate) fp32        D, delta_bias : (dim) fp32
+ *      h0, h_final    : (batch, dim, dstate) fp32
+ *    For the decode step: x, delta, z, y : (batch, dim); B, C : (batch,
+ *    dstate); state : (batch, dim, dstate) fp32.
+ *  - One activation dtype (ssm_dtype) covers u, delta, B, C, z and y.  A, D,
+ *    the bias and every state are fp32.  Arithmetic is fp32 throughout.
+ *  - Base pointers must be 4-byte aligned (2-byte for bf16 activations);
+ *    wider alignment enables vector loads but is not required.
+ *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *    and return without synchronising.  Results are valid once the stream
+ *    has reached that point.  Calls that overlap in time must not write the
+ *    same buffers.
+ *  - Errors: every call returns an ssm_status.  All argument checks run
+ *    before any HIP call, so an invalid call touches neither the device nor
+ *    any buffer.  A failing HIP call returns SSM_ERR_HIP.  The message of the
+ *    last non-OK status on the calling thread is ssm_last_error().
+ *    Nothing is thrown across this ABI.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_ABI_VERSION 1
+
+typedef enum {
+    SSM_DTYPE_F32 = 0,   /* activations in fp32 */
+    SSM_DTYPE_BF16 = 1   /* activations in bfloat16; y rounded to nearest-even */
+} ssm_dtype;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size, aliasing, misalignment */
+    SSM_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (e.g. dstate != 16) */
+    SSM_ERR_WORKSPACE = 3,    /* workspace missing or smaller than ssm_scan_workspace_size() */
+    SSM_ERR_HIP = 4           /* a HIP runtime call failed (no device, launch failure) */
+} ssm_status;
+
+/* flags (bitwise OR) */
+#define SSM_FLAG_DELTA_SOFTPLUS 1u  /* dt = softplus(delta + bias); without it dt = delta + bias */
+
+/* Returns SSM_SCAN_ABI_VERSION. */
+int ssm_abi_version(void);
+
+/* Tokens per sequence chunk that ssm_scan_fwd will use for this shape.
+ * requested_chunk = 0 lets the library choose; a positive value asks for
+ * chunks of that many tokens (rounded up to the kernel's block of 256).
+ * *chunk_len_out == seqlen means the sequence is not split.  When it is
+ * split, chunks are scanned in parallel from a zero state, their end states
+ * are chained in order (the affine maps compose: the associative operator of
+ * the Guide Complet's "Parallel Associative Scan"), and each later chunk's
+ * outputs are corrected for its true incoming state (see ssm_scan_fwd). */
+int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                  int64_t requested_chunk, int64_t *chunk_len_out);
+
+/* Bytes of caller-provided device workspace ssm_scan_fwd needs for this
+ * shape and chunk request (0 when the sequence is not split). */
+int ssm_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                            int64_t seqlen, int64_t requested_chunk,
+                            size_t *bytes);
+
+/* Selective scan forward.
+ *  u, delta, B, C      required, activation dtype
+ *  A                   required fp32 (dim, dstate); used as given (negative
+ *                      for a decaying state; positive values are accepted)
+ *  D                   nullable fp32 (dim): skip term D*u, added before the gate
+ *  z                   nullable, activation dtype: gate y * silu(z)
+ *  delta_bias          nullable fp32 (dim), added to delta before softplus
+ *  flags               SSM_FLAG_DELTA_SOFTPLUS or 0
+ *  h0                  nullable fp32 initial state (zero state if NULL)
+ *  y                   required output, activation dtype; must not overlap
+ *                      any input
+ *  h_final             nullable fp32 output: the state after the last token;
+ *                      must not overlap h0
+ *  batch, dim, seqlen  >= 1;  dstate must be 16 in this build
+ *  requested_chunk     0 = automatic; see ssm_scan_plan
+ *  workspace           device scratch of >= ssm_scan_workspace_size() bytes,
+ *                      256-byte aligned; may be NULL when that size is 0.  Its
+ *                      contents on entry do not matter; it is in use until
+ *                      the enqueued work completes.
+ *  stream              hipStream_t or NULL
+ * Long sequences with few channels are split into chunks (ssm_scan_plan).
+ * A later chunk starts from a zero state; its outputs are then corrected by
+ * silu(z_t) * sum_n C[t,n] * exp(A[n]*S_t) * h_in[n], S_t being the running
+ * sum of dt inside the chunk, until every decay factor exp(A[n]*S_t) has
+ * fallen below 2^-40 (valid because the factors never grow when A <= 0 and
+ * dt >= 0).  When a channel has some A > 0, or softplus is off so dt may be
+ * negative, the correction runs over the whole chunk. */
+int ssm_scan_fwd(const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z,
+                 const float *delta_bias, unsigned flags, const float *h0,
+                 void *y, float *h_final, int64_t batch, int64_t dim,
+                 int64_t dstate, int64_t seqlen, int dtype,
+                 int64_t requested_chunk, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* One decoding step, in place on `state`.
+ *  state      required fp32 (batch, dim, dstate): read, advanced by one token
+ *             and written back
+ *  x, delta   required, activation dtype (batch, dim)
+ *  A          required fp32 (dim, dstate)
+ *  B, C       required, activation dtype (batch, dstate)
+ *  D, z, delta_bias, flags   as for ssm_scan_fwd
+ *  y          required output, activation dtype (batch, dim)
+ * Applying it to tokens 0..L-1 in order reproduces ssm_scan_fwd's y and,
+ * in `state`, its h_final. */
+int ssm_state_update(float *state, const void *x, const void *delta,
+                     const float *A, const void *B, const void *C,
+                     const float *D, const void *z, const float *delta_bias,
+                     unsigned flags, void *y, int64_t batch, int64_t dim,
+                     int64_t dstate, int dtype, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char *ssm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,221 @@
+"""Python binding of ``libssmscan.so`` -- the MI355X selective-scan library.
+
+Argument marshalling only: tensors become device pointers, the current HIP
+stream is passed along, and every step of the computation runs in the HIP
+kernels behind the C ABI (``include/ssm_scan.h``).  There is no CPU or
+PyTorch fallback: if the library cannot be loaded, or a call returns an error
+status, these functions raise.
+
+Names follow the C ABI:
+
+* :func:`ssm_scan_fwd` -- whole-sequence selective scan (Mamba's S6 forward):
+  dt = softplus(delta + bias), h_t = exp(dt*A) h_{t-1} + dt*B_t*u_t,
+  y_t = (C_t . h_t + D*u_t) * silu(z_t).
+* :func:`ssm_state_update` -- one decoding step on an in-place fp32 state.
+* :func:`ssm_scan_plan`, :func:`ssm_scan_workspace_size`,
+  :func:`ssm_last_error`, :func:`ssm_abi_version`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssmscan.so")
+
+SSM_DTYPE_F32 = 0
+SSM_DTYPE_BF16 = 1
+SSM_FLAG_DELTA_SOFTPLUS = 1
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
+          3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
+EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
+           "ssm_scan_fwd", "ssm_state_update", "ssm_last_error")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library (built in-tree by ``__graft_entry__.build()``).
+    Raises if it is missing: there is no fallback."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                "libssmscan.so not found at %s; build it first "
+                "(python -c 'import __graft_entry__ as g; g.build()')" % p)
+        lib = ctypes.CDLL(p)
+        P, I, I64, U = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                        ctypes.c_uint)
+        lib.ssm_abi_version.argtypes = []
+        lib.ssm_abi_version.restype = I
+        lib.ssm_scan_plan.argtypes = [I64, I64, I64, I64, I64,
+                                      ctypes.POINTER(I64)]
+        lib.ssm_scan_plan.restype = I
+        lib.ssm_scan_workspace_size.argtypes = [I64, I64, I64, I64, I64,
+                                                ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssm_scan_workspace_size.restype = I
+        lib.ssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, U, P, P, P,
+                                     I64, I64, I64, I64, I, I64, P,
+                                     ctypes.c_size_t, P]
+        lib.ssm_scan_fwd.restype = I
+        lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, U, P,
+                                         I64, I64, I64, I, P]
+        lib.ssm_state_update.restype = I
+        lib.ssm_last_error.argtypes = []
+        lib.ssm_last_error.restype = ctypes.c_char_p
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def ssm_last_error() -> str:
+    return load_library().ssm_last_error().decode()
+
+
+def ssm_abi_version() -> int:
+    return load_library().ssm_abi_version()
+
+
+def _check(status):
+    if status != 0:
+        raise SSMError(status, ssm_last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSM_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_DTYPE_BF16
+    raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s"
+                         % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device (HIP) tensor" % name)
+    return t.data_ptr()
+
+
+def _stream_handle(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def ssm_scan_plan(batch, dim, dstate, seqlen, requested_chunk=0) -> int:
+    out = ctypes.c_int64(0)
+    _check(load_library().ssm_scan_plan(batch, dim, dstate, seqlen,
+                                        requested_chunk, ctypes.byref(out)))
+    return out.value
+
+
+def ssm_scan_workspace_size(batch, dim, dstate, seqlen, requested_chunk=0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ssm_scan_workspace_size(
+        batch, dim, dstate, seqlen, requested_chunk, ctypes.byref(out)))
+    return out.value
+
+
+def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                 delta_softplus=True, h0=None, return_final_state=True,
+                 chunk_len=0, y=None, h_final=None, workspace=None,
+                 stream=None):
+    """Selective scan forward on device tensors.
+
+    u, delta, z: (batch, dim, L); B, C: (batch, N, L) -- all one dtype
+    (float32 or bfloat16).  A: (dim, N) fp32; D, delta_bias: (dim,) fp32;
+    h0: (batch, dim, N) fp32 or None.  Returns ``(y, h_final)``
+    (``h_final`` is None unless ``return_final_state``).  Outputs and the
+    workspace are allocated here with torch unless passed in.
+    """
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    N = A.shape[-1] if A.dim() == 2 else 0
+    dev = u.device
+    act = u.dtype
+    code = _dtype_code(u)
+    pu = _ptr(u, "u", act, (batch, dim, L), dev)
+    pd = _ptr(delta, "delta", act, (batch, dim, L), dev)
+    pA = _ptr(A, "A", torch.float32, (dim, N), dev)
+    pB = _ptr(B, "B", act, (batch, N, L), dev)
+    pC = _ptr(C, "C", act, (batch, N, L), dev)
+    pD = _ptr(D, "D", torch.float32, (dim,), dev)
+    pz = _ptr(z, "z", act, (batch, dim, L), dev)
+    pbias = _ptr(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    ph0 = _ptr(h0, "h0", torch.float32, (batch, dim, N), dev)
+    if y is None:
+        y = torch.empty((batch, dim, L), dtype=act, device=dev)
+    py = _ptr(y, "y", act, (batch, dim, L), dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    if not return_final_state:
+        h_final = None
+    ph = _ptr(h_final, "h_final", torch.float32, (batch, dim, N), dev)
+    ws_bytes = ssm_scan_workspace_size(batch, dim, N, L, chunk_len)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    pws = workspace.data_ptr() if workspace is not None else None
+    wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    flags = SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    _check(load_library().ssm_scan_fwd(
+        pu, pd, pA, pB, pC, pD, pz, pbias, flags, ph0, py, ph,
+        batch, dim, N, L, code, chunk_len, pws, wsn,
+        _stream_handle(dev, stream)))
+    return y, h_final
+
+
+def ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
+                     delta_bias=None, delta_softplus=True, y=None,
+                     stream=None):
+    """One decoding step: advances ``state`` (batch, dim, N) fp32 in place
+    and returns y (batch, dim).  x, delta, z: (batch, dim); B, C:
+    (batch, N), all one activation dtype."""
+    if state.dim() != 3:
+        raise ValueError("state must be (batch, dim, N)")
+    batch, dim, N = state.shape
+    dev = state.device
+    act = x.dtype
+    code = _dtype_code(x)
+    ps = _ptr(state, "state", torch.float32, (batch, dim, N), dev)
+    px = _ptr(x, "x", act, (batch, dim), dev)
+    pd = _ptr(delta, "delta", act, (batch, dim), dev)
+    pA = _ptr(A, "A", torch.float32, (dim, N), dev)
+    pB = _ptr(B, "B", act, (batch, N), dev)
+    pC = _ptr(C, "C", act, (batch, N), dev)
+    pD = _ptr(D, "D", torch.float32, (dim,), dev)
+    pz = _ptr(z, "z", act, (batch, dim), dev)
+    pbias = _ptr(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    if y is None:
+        y = torch.empty((batch, dim), dtype=act, device=dev)
+    py = _ptr(y, "y", act, (batch, dim), dev)
+    flags = SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    _check(load_library().ssm_state_update(
+        ps, px, pd, pA, pB, pC, pD, pz, pbias, flags, py, batch, dim, N,
+        code, _stream_handle(dev, stream)))
+    return y

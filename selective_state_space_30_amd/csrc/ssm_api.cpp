@@ -1,0 +1,286 @@
+// ssm_api.cpp -- the C ABI declared in include/ssm_scan.h: argument checks,
+// the sequence-chunking plan and dispatch to the gfx950 kernels.  Every check
+// runs before the first HIP call, so an invalid request never touches the
+// device.
+#include "ssm_scan.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "ssm_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SSM_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+// [p, p + n) and [q, q + m) intersect (both non-null, non-empty).
+bool overlaps(const void *p, int64_t n, const void *q, int64_t m) {
+  if (!p || !q || n <= 0 || m <= 0) return false;
+  const char *a = static_cast<const char *>(p);
+  const char *b = static_cast<const char *>(q);
+  return a < b + m && b < a + n;
+}
+
+bool aligned(const void *p, size_t k) {
+  return (reinterpret_cast<uintptr_t>(p) % k) == 0;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+constexpr int64_t kMaxGridYZ = 65535;
+// Waves the scan needs to keep all 1024 SIMDs of an MI355X busy; below this
+// (with one wave per 4 channels) long sequences are split into chunks.
+constexpr int64_t kTargetWaves = 4096;
+constexpr int64_t kMinAutoChunk = 8192;
+
+int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0)
+    return fail(SSM_ERR_INVALID_ARG,
+                "sizes must be positive (batch=%lld dim=%lld dstate=%lld seqlen=%lld)",
+                (long long)batch, (long long)dim, (long long)dstate, (long long)seqlen);
+  if (dstate != ssm::kStates)
+    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld: this build supports dstate=16 only",
+                (long long)dstate);
+  int64_t e, e2;
+  if (!mul_ok(batch, dim, &e) || !mul_ok(e, seqlen, &e2) || !mul_ok(e2, 8, &e2))
+    return fail(SSM_ERR_INVALID_ARG, "batch*dim*seqlen overflows");
+  if (batch > kMaxGridYZ)
+    return fail(SSM_ERR_UNSUPPORTED, "batch=%lld exceeds %lld", (long long)batch,
+                (long long)kMaxGridYZ);
+  return SSM_OK;
+}
+
+int64_t choose_chunk(int64_t batch, int64_t dim, int64_t seqlen, int64_t requested) {
+  int64_t chunk;
+  if (requested > 0) {
+    chunk = round_up(requested, ssm::kBlockTokens);
+  } else {
+    const int64_t groups = (dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
+    const int64_t waves = batch * groups * ssm::kWavesPerGroup;
+    if (waves >= kTargetWaves / 2) return seqlen;
+    const int64_t n_c = (kTargetWaves + waves - 1) / waves;
+    chunk = round_up((seqlen + n_c - 1) / n_c, ssm::kBlockTokens);
+    if (chunk < kMinAutoChunk) chunk = kMinAutoChunk;
+  }
+  return chunk >= seqlen ? seqlen : chunk;
+}
+
+}  // namespace
+
+namespace ssm {
+SplitLayout split_layout(int64_t batch, int64_t dim, int64_t n_chunks) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t bdc = static_cast<size_t>(batch) * dim * n_chunks;
+  SplitLayout l;
+  l.off_H = 0;
+  l.off_S = up(l.off_H + bdc * kStates * sizeof(float));
+  l.off_hin = up(l.off_S + bdc * sizeof(float));
+  l.total_bytes = up(l.off_hin + bdc * kStates * sizeof(float));
+  return l;
+}
+}  // namespace ssm
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_SCAN_ABI_VERSION; }
+
+const char *ssm_last_error(void) { return g_last_error.c_str(); }
+
+int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                  int64_t requested_chunk, int64_t *chunk_len_out) {
+  if (!chunk_len_out) return fail(SSM_ERR_INVALID_ARG, "chunk_len_out is NULL");
+  int st = check_sizes(batch, dim, dstate, seqlen);
+  if (st != SSM_OK) return st;
+  if (requested_chunk < 0)
+    return fail(SSM_ERR_INVALID_ARG, "requested_chunk must be >= 0");
+  const int64_t chunk = choose_chunk(batch, dim, seqlen, requested_chunk);
+  if ((seqlen + chunk - 1) / chunk > kMaxGridYZ)
+    return fail(SSM_ERR_UNSUPPORTED, "more than %lld chunks requested",
+                (long long)kMaxGridYZ);
+  *chunk_len_out = chunk;
+  return ok();
+}
+
+int ssm_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                            int64_t seqlen, int64_t requested_chunk,
+                            size_t *bytes) {
+  if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
+  int64_t chunk = 0;
+  int st = ssm_scan_plan(batch, dim, dstate, seqlen, requested_chunk, &chunk);
+  if (st != SSM_OK) return st;
+  const int64_t n_chunks = (seqlen + chunk - 1) / chunk;
+  *bytes = n_chunks > 1 ? ssm::split_layout(batch, dim, n_chunks).total_bytes : 0;
+  return ok();
+}
+
+int ssm_scan_fwd(const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z,
+                 const float *delta_bias, unsigned flags, const float *h0,
+                 void *y, float *h_final, int64_t batch, int64_t dim,
+                 int64_t dstate, int64_t seqlen, int dtype,
+                 int64_t requested_chunk, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+  if (!u || !delta || !A || !B || !C || !y)
+    return fail(SSM_ERR_INVALID_ARG,
+                "required pointer is NULL (u=%p delta=%p A=%p B=%p C=%p y=%p)", u,
+                delta, (const void *)A, B, C, y);
+  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & ~static_cast<unsigned>(SSM_FLAG_DELTA_SOFTPLUS))
+    return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  int st = check_sizes(batch, dim, dstate, seqlen);
+  if (st != SSM_OK) return st;
+  if (requested_chunk < 0)
+    return fail(SSM_ERR_INVALID_ARG, "requested_chunk must be >= 0");
+
+  const bool bf16 = dtype == SSM_DTYPE_BF16;
+  const int64_t es = bf16 ? 2 : 4;
+  const void *acts[] = {u, delta, B, C, z, y};
+  for (const void *p : acts)
+    if (p && !aligned(p, es))
+      return fail(SSM_ERR_INVALID_ARG, "activation pointer %p not %lld-byte aligned", p,
+                  (long long)es);
+  const void *f32s[] = {A, D, delta_bias, h0, h_final};
+  for (const void *p : f32s)
+    if (p && !aligned(p, 4))
+      return fail(SSM_ERR_INVALID_ARG, "fp32 pointer %p not 4-byte aligned", p);
+
+  const int64_t big = batch * dim * seqlen * es;
+  const int64_t bc = batch * dstate * seqlen * es;
+  const int64_t sts = batch * dim * dstate * 4;
+  const struct { const void *p; int64_t n; const char *name; } ins[] = {
+      {u, big, "u"}, {delta, big, "delta"}, {z, big, "z"}, {B, bc, "B"},
+      {C, bc, "C"}, {A, dim * dstate * 4, "A"}, {D, dim * 4, "D"},
+      {delta_bias, dim * 4, "delta_bias"}, {h0, sts, "h0"}};
+  for (const auto &in : ins) {
+    if (overlaps(y, big, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "y overlaps input %s", in.name);
+    if (overlaps(h_final, sts, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "h_final overlaps input %s", in.name);
+  }
+  if (overlaps(y, big, h_final, sts))
+    return fail(SSM_ERR_INVALID_ARG, "y overlaps h_final");
+
+  const int64_t chunk = choose_chunk(batch, dim, seqlen, requested_chunk);
+  const int64_t n_chunks = (seqlen + chunk - 1) / chunk;
+  if (n_chunks > kMaxGridYZ)
+    return fail(SSM_ERR_UNSUPPORTED, "more than %lld chunks requested",
+                (long long)kMaxGridYZ);
+
+  ssm::ScanArgs a{};
+  if (n_chunks > 1) {
+    const ssm::SplitLayout l = ssm::split_layout(batch, dim, n_chunks);
+    if (!workspace || workspace_bytes < l.total_bytes)
+      return fail(SSM_ERR_WORKSPACE,
+                  "workspace of %zu bytes needed (got %zu bytes at %p)", l.total_bytes,
+                  workspace_bytes, workspace);
+    if (!aligned(workspace, 256))
+      return fail(SSM_ERR_INVALID_ARG, "workspace %p not 256-byte aligned", workspace);
+    const void *all[] = {u, delta, z, B, C, A, D, delta_bias, h0, y, h_final};
+    const int64_t sizes[] = {big, big, big, bc, bc, dim * dstate * 4, dim * 4, dim * 4,
+                             sts, big, sts};
+    for (int i = 0; i < 11; ++i)
+      if (overlaps(workspace, static_cast<int64_t>(l.total_bytes), all[i], sizes[i]))
+        return fail(SSM_ERR_INVALID_ARG, "workspace overlaps an argument array");
+    char *w = static_cast<char *>(workspace);
+    a.ws_H = reinterpret_cast<float *>(w + l.off_H);
+    a.ws_S = reinterpret_cast<float *>(w + l.off_S);
+    a.ws_hin = reinterpret_cast<float *>(w + l.off_hin);
+  }
+
+  // 16-byte vector loads need every activation row to start 16-byte aligned.
+  bool vec = (seqlen * es) % 16 == 0;
+  for (const void *p : acts)
+    if (p && !aligned(p, 16)) vec = false;
+
+  a.u = u; a.delta = delta; a.B = B; a.C = C; a.z = z;
+  a.A = A; a.D = D; a.bias = delta_bias; a.h0 = h0;
+  a.y = y; a.h_final = h_final;
+  a.batch = batch; a.dim = dim; a.L = seqlen;
+  a.chunk_len = chunk;
+  a.n_chunks = static_cast<int>(n_chunks);
+  a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+  const int err = ssm::launch_scan(a, bf16, vec, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  return ok();
+}
+
+int ssm_state_update(float *state, const void *x, const void *delta,
+                     const float *A, const void *B, const void *C,
+                     const float *D, const void *z, const float *delta_bias,
+                     unsigned flags, void *y, int64_t batch, int64_t dim,
+                     int64_t dstate, int dtype, void *stream) {
+  if (!state || !x || !delta || !A || !B || !C || !y)
+    return fail(SSM_ERR_INVALID_ARG, "required pointer is NULL");
+  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & ~static_cast<unsigned>(SSM_FLAG_DELTA_SOFTPLUS))
+    return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  int st = check_sizes(batch, dim, dstate, 1);
+  if (st != SSM_OK) return st;
+  int64_t threads;
+  if (!mul_ok(batch * dim, 4, &threads) || threads / 256 >= (int64_t(1) << 31))
+    return fail(SSM_ERR_UNSUPPORTED, "batch*dim too large");
+
+  const bool bf16 = dtype == SSM_DTYPE_BF16;
+  const int64_t es = bf16 ? 2 : 4;
+  const void *acts[] = {x, delta, B, C, z, y};
+  for (const void *p : acts)
+    if (p && !aligned(p, es))
+      return fail(SSM_ERR_INVALID_ARG, "activation pointer %p not %lld-byte aligned", p,
+                  (long long)es);
+  const void *f32s[] = {state, A, D, delta_bias};
+  for (const void *p : f32s)
+    if (p && !aligned(p, 4))
+      return fail(SSM_ERR_INVALID_ARG, "fp32 pointer %p not 4-byte aligned", p);
+
+  const int64_t bdn = batch * dim * dstate * 4;
+  const int64_t bd = batch * dim * es;
+  const int64_t bn = batch * dstate * es;
+  const struct { const void *p; int64_t n; const char *name; } ins[] = {
+      {x, bd, "x"}, {delta, bd, "delta"}, {z, bd, "z"}, {B, bn, "B"}, {C, bn, "C"},
+      {A, dim * dstate * 4, "A"}, {D, dim * 4, "D"}, {delta_bias, dim * 4, "delta_bias"}};
+  for (const auto &in : ins) {
+    if (overlaps(state, bdn, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "state overlaps input %s", in.name);
+    if (overlaps(y, bd, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "y overlaps input %s", in.name);
+  }
+  if (overlaps(y, bd, state, bdn))
+    return fail(SSM_ERR_INVALID_ARG, "y overlaps state");
+
+  const bool vec = aligned(state, 16) && aligned(A, 16);
+  ssm::StepArgs a{};
+  a.state = state; a.x = x; a.delta = delta; a.B = B; a.C = C; a.z = z;
+  a.A = A; a.D = D; a.bias = delta_bias; a.y = y;
+  a.batch = batch; a.dim = dim;
+  a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+  const int err = ssm::launch_step(a, bf16, vec, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// ssm_internal.h -- launch interface between the C-ABI layer (ssm_api.cpp)
+// and the gfx950 kernels (ssm_kernels.hip).  Not installed; not part of the
+// public ABI in include/ssm_scan.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace ssm {
+
+constexpr int kStates = 16;          // d_state supported by this build
+constexpr int kRowLanes = 16;        // lanes that share one channel's tokens
+constexpr int kRowsPerWave = 4;      // channels per 64-lane wave
+constexpr int kWavesPerGroup = 4;    // waves per workgroup
+constexpr int kChannelsPerGroup = kRowsPerWave * kWavesPerGroup;  // 16
+constexpr int kTokensPerLane = 16;   // consecutive tokens owned by one lane
+constexpr int kBlockTokens = kRowLanes * kTokensPerLane;          // 256
+
+struct ScanArgs {
+  const void *u, *delta, *B, *C, *z;  // activations (dtype)
+  const float *A, *D, *bias, *h0;     // fp32 parameters / initial state
+  void *y;                            // output (dtype)
+  float *h_final;                     // fp32 (batch, dim, 16) or null
+  float *ws_H;                        // split mode: chunk end states (b,d,c,n)
+  float *ws_S;                        // split mode: chunk sums of dt (b,d,c)
+  float *ws_hin;                      // split mode: chunk incoming states (b,d,c,n)
+  int64_t batch, dim, L;
+  int64_t chunk_len;                  // tokens per chunk (== L when not split)
+  int n_chunks;
+  int softplus;                       // 1: dt = softplus(delta + bias)
+};
+
+struct StepArgs {
+  float *state;
+  const void *x, *delta, *B, *C, *z;
+  const float *A, *D, *bias;
+  void *y;
+  int64_t batch, dim;
+  int softplus;
+};
+
+// Workspace layout of the split (chunked) scan, in floats, each part
+// starting on a 256-byte boundary.
+struct SplitLayout {
+  size_t off_H, off_S, off_hin, total_bytes;
+};
+SplitLayout split_layout(int64_t batch, int64_t dim, int64_t n_chunks);
+
+// Kernel launchers.  Return a hipError_t value as int (0 = success).
+// `vec` selects 16-byte vector loads (the caller has checked alignment).
+int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream);
+int launch_step(const StepArgs &a, bool bf16, bool vec, void *stream);
+const char *hip_error_string(int err);
+
+}  // namespace ssm

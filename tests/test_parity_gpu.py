@@ -1,0 +1,223 @@
+"""Parity of the HIP scan (through the C ABI) with the fp64 oracle.
+
+Bars: fp32 activations 1e-4, bf16 activations 2e-2, measured as
+max |gpu - oracle| / (|oracle| + rms(oracle)) per output tensor (see
+parity_metrics.py).  Small shapes are compared element by element over the
+whole output; the full-size workloads run exactly as the benchmark launches
+them and are compared on sampled channels, which the oracle computes one by
+one (channels are independent).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_30_amd as ssm
+import synthetic as syn
+from parity_metrics import report, scaled_max_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v)
+            for k, v in inp.items()}
+
+
+def gpu_scan(inp, chunk_len=0, return_final_state=True):
+    y, hf = ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"],
+                             inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                             inp["delta_softplus"], inp["h0"],
+                             return_final_state=return_final_state,
+                             chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    return y, hf
+
+
+def oracle_scan(inp):
+    return oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                       inp["D"], inp["z"], inp["delta_bias"],
+                       inp["delta_softplus"], False, inp["h0"])
+
+
+def check(got, ref, tol, what):
+    err = scaled_max_err(got, ref)
+    assert err <= tol, "%s: %s (tol %g)" % (what, report(got, ref), tol)
+    return err
+
+
+SMALL_CASES = [
+    # (batch, dim, L, dtype, with_z, with_D, with_h0)
+    (1, 64, 256, "f32", True, True, False),     # the tiny workload's shape
+    (2, 37, 1000, "f32", True, True, True),     # ragged channels and tail
+    (2, 37, 999, "f32", False, False, True),    # unaligned rows: scalar loads
+    (1, 16, 1, "f32", True, True, True),        # a single token
+    (1, 1, 300, "f32", True, True, False),      # a single channel
+    (3, 20, 777, "bf16", True, True, False),    # unaligned bf16 rows
+    (2, 48, 1536, "bf16", True, True, True),    # aligned bf16, 6 blocks
+    (1, 5, 4096, "bf16", False, True, False),   # no gate
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: "b%d_d%d_l%d_%s_z%d_D%d_h%d" % c)
+def test_small_shapes_match_oracle(case):
+    batch, dim, L, dt, wz, wD, wh = case
+    inp = syn.make_scan_inputs(syn.TINY, "cpu", batch=batch, dim=dim, seqlen=L,
+                               dtype=dt, with_z=wz, with_D=wD, with_h0=wh,
+                               seed=77 + L)
+    y_ref, h_ref = oracle_scan(inp)
+    y, hf = gpu_scan(to_dev(inp))
+    check(y, y_ref, TOL[dt], "y")
+    check(hf, h_ref, TOL[dt], "h_final")
+
+
+def test_tiny_workload_exactly_as_specified():
+    inp = syn.make_scan_inputs(syn.TINY, "cpu")
+    y_ref, h_ref = oracle_scan(inp)
+    y, hf = gpu_scan(to_dev(inp))
+    check(y, y_ref, 1e-4, "y")
+    check(hf, h_ref, 1e-4, "h_final")
+
+
+CHUNK_CASES = [
+    # (dtype, L, chunk, softplus, A kind)
+    ("f32", 3000, 512, True, "arange"),      # decays: fix-up stops early
+    ("f32", 2049, 256, True, "arange"),      # last chunk of one token
+    ("f32", 3000, 768, False, "arange"),     # softplus off: full fix-up
+    ("f32", 3000, 512, True, "positive"),    # an A > 0: full fix-up
+    ("bf16", 4096, 1024, True, "arange"),
+    ("bf16", 2500, 512, True, "slow"),       # slow decay: long fix-up
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "%s_l%d_c%d_sp%d_%s" % c)
+def test_chunked_scan_matches_oracle(case):
+    dt, L, chunk, sp, akind = case
+    inp = syn.make_scan_inputs(syn.TINY, "cpu", batch=2, dim=24, seqlen=L,
+                               dtype=dt, with_h0=True, seed=5 + L)
+    if not sp:
+        # a positive step used as given, small enough to stay stable
+        inp["delta"] = (0.05 * inp["delta"].float().abs()).to(inp["delta"].dtype)
+        inp["delta_softplus"] = False
+        inp["delta_bias"] = None
+    if akind == "positive":
+        inp["A"][:, 0] = 0.002
+    elif akind == "slow":
+        inp["A"] = inp["A"] * 0.01
+    assert ssm.ssm_scan_plan(2, 24, 16, L, chunk) == chunk
+    y_ref, h_ref = oracle_scan(inp)
+    y, hf = gpu_scan(to_dev(inp), chunk_len=chunk)
+    check(y, y_ref, TOL[dt], "y")
+    check(hf, h_ref, TOL[dt], "h_final")
+
+
+def test_chunked_and_unsplit_agree():
+    inp = to_dev(syn.make_scan_inputs(syn.TINY, "cpu", batch=1, dim=32,
+                                      seqlen=5000, dtype="f32", seed=3))
+    y1, h1 = gpu_scan(inp)
+    y2, h2 = gpu_scan(inp, chunk_len=1024)
+    check(y2, y1.double(), 1e-5, "y")
+    check(h2, h1.double(), 1e-5, "h_final")
+
+
+def test_resume_from_final_state():
+    """Associativity: scanning [0, L1) and then [L1, L) from the first
+    part's final state gives the whole scan."""
+    L, L1 = 2000, 777
+    inp = to_dev(syn.make_scan_inputs(syn.TINY, "cpu", batch=2, dim=40,
+                                      seqlen=L, dtype="f32", with_h0=True,
+                                      seed=11))
+    y, hf = gpu_scan(inp)
+    a = dict(inp)
+    b = dict(inp)
+    for k in ("u", "delta", "B", "C", "z"):
+        a[k] = inp[k][..., :L1].contiguous()
+        b[k] = inp[k][..., L1:].contiguous()
+    ya, ha = gpu_scan(a)
+    b["h0"] = ha
+    yb, hb = gpu_scan(b)
+    check(torch.cat([ya, yb], dim=-1), y.double(), 1e-5, "y")
+    check(hb, hf.double(), 1e-5, "h_final")
+
+
+def test_bitwise_deterministic():
+    inp = to_dev(syn.make_scan_inputs(syn.MAMBA_130M, "cpu", batch=1, dim=64,
+                                      seqlen=2048))
+    y1, h1 = gpu_scan(inp)
+    y2, h2 = gpu_scan(inp)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_zero_step_keeps_state_exactly():
+    inp = syn.make_scan_inputs(syn.TINY, "cpu", batch=2, dim=20, seqlen=600,
+                               dtype="f32", with_h0=True, seed=9)
+    inp["delta"] = torch.zeros_like(inp["delta"])
+    inp["delta_bias"] = None
+    inp["delta_softplus"] = False
+    y_ref, h_ref = oracle_scan(inp)
+    y, hf = gpu_scan(to_dev(inp))
+    assert torch.equal(hf.cpu(), inp["h0"])
+    check(y, y_ref, 1e-4, "y")
+
+
+def test_nan_propagates_forward():
+    inp = syn.make_scan_inputs(syn.TINY, "cpu", batch=1, dim=16, seqlen=512,
+                               dtype="f32", with_z=False, seed=4)
+    inp["u"][0, 3, 300] = float("nan")
+    y, hf = gpu_scan(to_dev(inp))
+    y = y.cpu()
+    assert torch.isfinite(y[0, 3, :300]).all()
+    assert torch.isnan(y[0, 3, 300:]).all() and torch.isnan(hf[0, 3].cpu()).all()
+    others = torch.cat([y[0, :3], y[0, 4:]])
+    assert torch.isfinite(others).all()
+
+
+def test_workspace_too_small_is_rejected_on_device():
+    inp = to_dev(syn.make_scan_inputs(syn.TINY, "cpu", batch=1, dim=16,
+                                      seqlen=2048, seed=2))
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ssm.SSMError) as e:
+        ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                         chunk_len=256, workspace=ws)
+    assert e.value.status == 3
+
+
+# ------------------------------------------------------- full workloads
+def sample_channels(batch, dim, k, seed):
+    r = np.random.default_rng(seed)
+    picks = {(0, 0), (batch - 1, dim - 1)}
+    while len(picks) < k:
+        picks.add((int(r.integers(batch)), int(r.integers(dim))))
+    return sorted(picks)
+
+
+def full_workload_check(cfg, k, tol):
+    inp = syn.make_scan_inputs(cfg, DEV)
+    chans = sample_channels(cfg.batch, cfg.dim, k, cfg.seed)
+    y, hf = gpu_scan(inp)
+    y_ref, h_ref = oracle.scan_channels(
+        inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+        inp["z"], inp["delta_bias"], inp["delta_softplus"], False, inp["h0"],
+        channels=chans)
+    bi = torch.tensor([c[0] for c in chans], device=DEV)
+    di = torch.tensor([c[1] for c in chans], device=DEV)
+    check(y[bi, di], y_ref, tol, "y (sampled)")
+    check(hf[bi, di], h_ref, tol, "h_final (sampled)")
+    # Properties at full size: everything finite.
+    assert torch.isfinite(y.float()).all() and torch.isfinite(hf).all()
+
+
+def test_mamba130m_workload_sampled():
+    full_workload_check(syn.MAMBA_130M, 48, 2e-2)
+
+
+def test_mamba2p8b_workload_sampled():
+    full_workload_check(syn.MAMBA_2P8B, 32, 2e-2)
+
+
+def test_long_context_workload_sampled():
+    cfg = syn.LONG_1M
+    assert ssm.ssm_scan_plan(cfg.batch, cfg.dim, 16, cfg.seqlen) < cfg.seqlen
+    full_workload_check(cfg, 4, 1e-4)
