@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Throughput of the selective scan on one MI355X.
+
+One step = one ``ssm_scan_fwd`` over the Mamba-2.8B-shaped layer workload
+(batch=2, D=5120, N=16, L=4096, bf16 activations, fp32 state, gate and D
+skip, final state returned) -- the whole hot path for that shape: B/C
+staging, softplus, discretisation, scan, readout, gate and store in one
+kernel.  Inputs are resident in HBM before the timed region; three input
+sets are rotated so the 256 MB last-level cache cannot serve them.
+
+Prints ONE JSON line.  ``value`` is GB/s of algorithmic traffic (bytes the
+method must move: every input read once, y and the final state written
+once).  ``roofline`` relates the scan kernel's average duration (HIP events
+on its stream over the timed region) to the ALU ceiling that bounds it.
+``cpu_baseline`` is the fp64 oracle on the same inputs on the host cores.
+
+Options beyond the contract: --no-cpu-baseline, --no-extra (skip the
+long-context and decode figures), --only-scan (nothing but the timed steps;
+for profiler runs).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+# fp32 vector peak without packed math (packed FP32 forms are disabled in
+# this build): 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz.
+VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# Algorithmic flops: per state-update dt*A (1), exp (1), dt*u*B (1),
+# h = dA*h + dBu (2), y += C*h (2); per element bias add, softplus (exp,
+# log1p), dt*u, D*u + add, silu (exp, add, reciprocal, multiply), gate.
+FLOP_PER_STATE_UPDATE = 7
+FLOP_PER_ELEMENT = 13
+TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                            "scan_kernel_mamba2p8b_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_30_amd", "csrc",
+                          "ssm_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(n_launch_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or
+    None if the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(t["hbm_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only-scan", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the scan on a "
+              "single MI355X (no collectives or sharding); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_30_amd as ssm
+    import synthetic as syn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = ssm.load_library()
+    cfg = syn.MAMBA_2P8B
+    E = cfg.elements
+    nbytes = syn.algorithmic_bytes(cfg)
+
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    log("workload %s: generating 3 input sets on %s" % (cfg.name, dev))
+    sets = []
+    for i in range(3):
+        inp = syn.make_scan_inputs(cfg, dev, seed=cfg.seed + 100 * i)
+        inp["y"] = torch.empty_like(inp["u"])
+        inp["h_final"] = torch.empty(cfg.batch, cfg.dim, 16, device=dev)
+        sets.append(inp)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        s = sets[i % 3]
+        ssm.ssm_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"],
+                         s["z"], s["delta_bias"], True, None,
+                         y=s["y"], h_final=s["h_final"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_events = ev0.elapsed_time(ev1) / args.steps
+    ms_wall = wall * 1e3 / args.steps
+    ms = ms_events
+    sec = ms * 1e-3
+    gbps = nbytes / sec / 1e9
+    log("scan: %.1f us/step (events), %.1f us/step (wall), %.0f GB/s"
+        % (ms * 1e3, ms_wall * 1e3, gbps))
+    if args.only_scan:
+        return
+
+    flops = (E * cfg.dstate * FLOP_PER_STATE_UPDATE + E * FLOP_PER_ELEMENT)
+    achieved = flops / sec / 1e12
+    traffic = measured_traffic(nbytes)
+    result = {
+        "metric": "selective-scan HBM GB/s (% of peak) + elements/s, "
+                  "D=5120 L=4096 N=16",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Mamba-2.8B-shaped layer)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "dim": cfg.dim,
+                   "dstate": cfg.dstate, "seqlen": cfg.seqlen,
+                   "activations": "bf16", "state": "fp32", "gate": True,
+                   "D_skip": True, "final_state": True,
+                   "A": "-exp(log(1..16)) fp32", "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "elements_per_s": round(E / sec),
+        "state_updates_per_s": round(E * cfg.dstate / sec),
+        "algorithmic_bytes_per_step": nbytes,
+        "ms_per_step_wall": round(ms_wall, 5),
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(achieved, 3),
+            "peak": round(VALU_PEAK_TFLOPS, 2),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / VALU_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "scan_kernel<bf16, vec>",
+            "flop_per_launch": flops,
+        },
+    }
+
+    # Copy ceiling: a plain device-to-device copy of 1 GiB (read + write).
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        b.copy_(a)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * a.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del a, b
+    result["copy_ceiling_GBps"] = round(copy_gbps, 1)
+    result["pct_of_copy_ceiling"] = round(100 * gbps / copy_gbps, 2)
+
+    if not args.no_extra:
+        result["other_workloads"] = extra_workloads(torch, ssm, syn, dev,
+                                                    stream, log)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sets[0], cfg, nbytes, log)
+
+    del sets
+    print(json.dumps(result), flush=True)
+
+
+def extra_workloads(torch, ssm, syn, dev, stream, log):
+    """Long-context scan (chunked) and the decode step, timed with events.
+    Reported for information beside the main line."""
+    out = {}
+    cfg = syn.LONG_1M
+    log("long-context workload %s" % cfg.name)
+    inp = syn.make_scan_inputs(cfg, dev)
+    y = torch.empty_like(inp["u"])
+    hf = torch.empty(cfg.batch, cfg.dim, 16, device=dev)
+    ws_bytes = ssm.ssm_scan_workspace_size(cfg.batch, cfg.dim, 16, cfg.seqlen)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def run():
+        ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["z"], inp["delta_bias"], True, None,
+                         y=y, h_final=hf, workspace=ws, stream=stream)
+    run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb = syn.algorithmic_bytes(cfg)
+    out[cfg.name] = {
+        "ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+        "elements_per_s": round(cfg.elements / (ms * 1e-3)),
+        "chunk_len": ssm.ssm_scan_plan(cfg.batch, cfg.dim, 16, cfg.seqlen),
+        "algorithmic_bytes": nb}
+    del inp, y, hf, ws
+    torch.cuda.empty_cache()
+
+    dcfg = syn.DECODE
+    log("decode workload %s" % dcfg.name)
+    dinp = syn.make_decode_inputs(dcfg, dev)
+    steps = [syn.step_slice(dinp, t) for t in range(dcfg.steps)]
+    state = torch.zeros(dcfg.batch, dcfg.dim, 16, device=dev)
+    ys = [torch.empty(dcfg.batch, dcfg.dim, dtype=torch.bfloat16, device=dev)
+          for _ in range(dcfg.steps)]
+    calls = [ssm.bind_state_update(state, s["x"], s["delta"], dinp["A"],
+                                   s["B"], s["C"], dinp["D"], s["z"],
+                                   dinp["delta_bias"], True, y=ys[t],
+                                   stream=stream)
+             for t, s in enumerate(steps)]
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for c in calls:
+        c()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / dcfg.steps
+    nb = syn.decode_step_bytes(dcfg)
+    out[dcfg.name] = {"us_per_step": round(us, 3),
+                      "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                      "bytes_per_step": nb}
+    return out
+
+
+def cpu_baseline(inp, cfg, nbytes, log):
+    """The fp64 oracle, as it stands, over the whole workload on the host
+    cores (disjoint channel ranges on threads)."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    log("cpu baseline: oracle on %d threads" % threads)
+    host = {k: (v.detach().to("cpu").double().numpy() if hasattr(v, "detach")
+                else v) for k, v in inp.items()
+            if k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    t0 = time.perf_counter()
+    oracle.scan_threaded(host["u"], host["delta"], host["A"], host["B"],
+                         host["C"], host["D"], host["z"], host["delta_bias"],
+                         True, False, None, threads=threads)
+    sec = time.perf_counter() - t0
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "the whole workload (%d x %d channels x %d tokens), "
+                      "fp64, %.2f s wall" % (cfg.batch, cfg.dim, cfg.seqlen,
+                                             sec),
+            "elements_per_s": round(cfg.elements / sec)}
+
+
+if __name__ == "__main__":
+    main()

@@ -219,3 +219,40 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
         ps, px, pd, pA, pB, pC, pD, pz, pbias, flags, py, batch, dim, N,
         code, _stream_handle(dev, stream)))
     return y
+
+
+def bind_state_update(state, x, delta, A, B, C, D=None, z=None,
+                      delta_bias=None, delta_softplus=True, y=None,
+                      stream=None):
+    """Checks and marshals the arguments of one decoding step once and
+    returns a zero-argument callable that enqueues exactly that step (the
+    same C call as :func:`ssm_state_update`, without per-call Python
+    checks).  For launch-bound decode loops; the tensors must stay alive."""
+    if state.dim() != 3:
+        raise ValueError("state must be (batch, dim, N)")
+    batch, dim, N = state.shape
+    dev = state.device
+    act = x.dtype
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty((batch, dim), dtype=act, device=dev)
+    args = (_ptr(state, "state", torch.float32, (batch, dim, N), dev),
+            _ptr(x, "x", act, (batch, dim), dev),
+            _ptr(delta, "delta", act, (batch, dim), dev),
+            _ptr(A, "A", torch.float32, (dim, N), dev),
+            _ptr(B, "B", act, (batch, N), dev),
+            _ptr(C, "C", act, (batch, N), dev),
+            _ptr(D, "D", torch.float32, (dim,), dev),
+            _ptr(z, "z", act, (batch, dim), dev),
+            _ptr(delta_bias, "delta_bias", torch.float32, (dim,), dev),
+            SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0,
+            _ptr(y, "y", act, (batch, dim), dev),
+            batch, dim, N, code, _stream_handle(dev, stream))
+    fn = load_library().ssm_state_update
+    keep = (state, x, delta, A, B, C, D, z, delta_bias, y)
+
+    def call():
+        _check(fn(*args))
+        return keep[-1]
+    call.y = y
+    return call

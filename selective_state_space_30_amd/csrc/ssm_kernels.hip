@@ -92,12 +92,18 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
   return __uint_as_float(w & 0xffff0000u);
 }
 
-// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two fp32 -> one word of two bf16 (lo = first), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t r;
+  r.x = static_cast<__bf16>(lo);
+  r.y = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 template <typename T>
@@ -171,10 +177,10 @@ __device__ __forceinline__ void store_run(T *__restrict__ row, int64_t t,
 #pragma unroll
       for (int q = 0; q < K / 8; ++q) {
         uint4 w;
-        w.x = f32_to_bf16_bits(v[8 * q + 0]) | (f32_to_bf16_bits(v[8 * q + 1]) << 16);
-        w.y = f32_to_bf16_bits(v[8 * q + 2]) | (f32_to_bf16_bits(v[8 * q + 3]) << 16);
-        w.z = f32_to_bf16_bits(v[8 * q + 4]) | (f32_to_bf16_bits(v[8 * q + 5]) << 16);
-        w.w = f32_to_bf16_bits(v[8 * q + 6]) | (f32_to_bf16_bits(v[8 * q + 7]) << 16);
+        w.x = pack_bf16x2(v[8 * q + 0], v[8 * q + 1]);
+        w.y = pack_bf16x2(v[8 * q + 2], v[8 * q + 3]);
+        w.z = pack_bf16x2(v[8 * q + 4], v[8 * q + 5]);
+        w.w = pack_bf16x2(v[8 * q + 6], v[8 * q + 7]);
         p[q] = w;
       }
     } else {
@@ -202,32 +208,158 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
 }
 
 // ---------------------------------------------------------------- scan ---
+// Value of lane 15 of the row in lane 0, zero in the other lanes.
+__device__ __forceinline__ float row_last_to_first(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x10F,
+                                                 0xF, 0xF, true));
+}
+// x from lane i - s of the row, zero where that lane does not exist.
+template <int kCtrl>
+__device__ __forceinline__ float row_shift_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl,
+                                                 0xF, 0xF, true));
+}
+
+struct ScanLane {
+  int tid, wave, lane, row, li, ch;
+};
+
+// One block of 256 tokens for the 16 channels of the workgroup.  kFull:
+// the block lies wholly inside [ct0, ct1) (no masking); otherwise positions
+// past ct1 act as identity steps (dt = 0, u = 0) and are not stored.
+template <typename T, bool kVec, bool kFull>
+__device__ __forceinline__ void scan_block(
+    const ScanArgs &p, const ScanLane &L, int64_t t0, int64_t ct1,
+    const T *__restrict__ Bb, const T *__restrict__ Cb,
+    const T *__restrict__ urow, const T *__restrict__ drow,
+    const T *__restrict__ zrow, T *__restrict__ yrow, bool row_ok,
+    float bias, float Dd, float *sB, float *sC, const float *sA,
+    float (&hlast)[kStates], float &sdt_total) {
+  constexpr int K = kTokensPerLane;
+  constexpr int KP = K + 4;
+  const int64_t tend = kFull ? t0 + kBlockTokens : ct1;
+  // B and C of this block: thread (n, q) fetches state n, lane run q.
+  float vb[K], vc[K];
+  {
+    const int n = L.tid >> 4, q = L.tid & 15;
+    const int64_t t = t0 + q * K;
+    load_run<T, K, kVec>(Bb + n * p.L, t, tend, vb);
+    load_run<T, K, kVec>(Cb + n * p.L, t, tend, vc);
+  }
+  // This lane's tokens: discretisation step, dt*u and the D skip.
+  const int64_t tl = t0 + L.li * K;
+  float dt[K], du[K], y[K];
+  float sdt = 0.0f;
+  {
+    float uu[K], dr[K];
+    load_run<T, K, kVec>(urow, tl, tend, uu);
+    load_run<T, K, kVec>(drow, tl, tend, dr);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const float x = dr[j] + bias;
+      float v = p.softplus ? softplus_f(x) : x;
+      if (!kFull) v = (tl + j < tend) ? v : 0.0f;  // identity step
+      dt[j] = v;
+      du[j] = v * uu[j];
+      y[j] = Dd * uu[j];
+      sdt += v;
+    }
+  }
+
+  __syncthreads();  // the previous block's tile is no longer read
+  {
+    const int n = L.tid >> 4, q = L.tid & 15;
+    float4 *pb = reinterpret_cast<float4 *>(&sB[(n * kRowLanes + q) * KP]);
+    float4 *pc = reinterpret_cast<float4 *>(&sC[(n * kRowLanes + q) * KP]);
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) {
+      pb[j] = make_float4(vb[4 * j], vb[4 * j + 1], vb[4 * j + 2], vb[4 * j + 3]);
+      pc[j] = make_float4(vc[4 * j], vc[4 * j + 1], vc[4 * j + 2], vc[4 * j + 3]);
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int n = 0; n < kStates; ++n) {
+    const float Aq = sA[L.ch * kStates + n];
+    const float *pb = &sB[(n * kRowLanes + L.li) * KP];
+    const float *pc = &sC[(n * kRowLanes + L.li) * KP];
+    float a[K], bb[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      a[j] = fast_exp2(dt[j] * Aq);
+      bb[j] = du[j] * pb[j];
+    }
+    // Fold the lane's tokens into one affine map h -> P*h + H.
+    float H = bb[0];
+#pragma unroll
+    for (int j = 1; j < K; ++j) H = fmaf(a[j], H, bb[j]);
+    float P = fast_exp2(sdt * Aq);
+    // The carried state (lane 15's, from the previous block) enters lane 0;
+    // X is zero in the other lanes.
+    const float X = row_last_to_first(hlast[n]);
+    H = fmaf(P, X, H);
+    // Inclusive scan of the affine maps over the 16 lanes of the row:
+    // (P, H) <- (P * P', P * H' + H) with (P', H') from lane i - s.  Where
+    // lane i - s does not exist H is unchanged (H' reads 0); P then becomes
+    // 0, but a lane whose composition already starts at lane 0 never has
+    // its P read again (the carry has entered before the scan).
+    H = fmaf(P, row_shift_zero<kRowShr1>(H), H);
+    P *= row_shift_zero<kRowShr1>(P);
+    H = fmaf(P, row_shift_zero<kRowShr2>(H), H);
+    P *= row_shift_zero<kRowShr2>(P);
+    H = fmaf(P, row_shift_zero<kRowShr4>(H), H);
+    P *= row_shift_zero<kRowShr4>(P);
+    H = fmaf(P, row_shift_zero<kRowShr8>(H), H);
+    // H is now the true state after this lane's last token; the lane's
+    // incoming state is its left neighbour's (lane 0: the carried X).
+    float h = row_shift_zero<kRowShr1>(H) + X;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      h = fmaf(a[j], h, bb[j]);
+      y[j] = fmaf(pc[j], h, y[j]);
+    }
+    hlast[n] = h;
+  }
+
+  if (zrow) {
+    float zz[K];
+    load_run<T, K, kVec>(zrow, tl, tend, zz);
+#pragma unroll
+    for (int j = 0; j < K; ++j) y[j] *= silu_f(zz[j]);
+  }
+  if (row_ok) store_run<T, K, kVec && kFull>(yrow, tl, tend, y);
+  sdt_total += sdt;
+}
+
 template <typename T, bool kVec>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void scan_kernel(ScanArgs p) {
   constexpr int K = kTokensPerLane;
   constexpr int KP = K + 4;  // padded LDS stride per lane run (bank spread)
   __shared__ float sB[kStates * kRowLanes * KP];
   __shared__ float sC[kStates * kRowLanes * KP];
   __shared__ float sA[kChannelsPerGroup * kStates];
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int row = lane >> 4;
-  const int li = lane & 15;
-  const int ch = wave * kRowsPerWave + row;  // channel slot in the group
+  ScanLane L;
+  L.tid = threadIdx.x;
+  L.wave = L.tid >> 6;
+  L.lane = L.tid & 63;
+  L.row = L.lane >> 4;
+  L.li = L.lane & 15;
+  L.ch = L.wave * kRowsPerWave + L.row;  // channel slot in the group
   const int64_t b = blockIdx.y;
   const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kChannelsPerGroup;
-  const bool row_ok = d0 + ch < p.dim;
-  const int64_t d = row_ok ? d0 + ch : p.dim - 1;  // clamped for reads
+  const bool row_ok = d0 + L.ch < p.dim;
+  const int64_t d = row_ok ? d0 + L.ch : p.dim - 1;  // clamped for reads
   const int chunk = blockIdx.z;
   const int64_t ct0 = static_cast<int64_t>(chunk) * p.chunk_len;
   const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
 
   {
-    const int c = tid >> 4, n = tid & 15;
+    const int c = L.tid >> 4, n = L.tid & 15;
     const int64_t dd = d0 + c < p.dim ? d0 + c : p.dim - 1;
-    sA[tid] = p.A[dd * kStates + n] * kLog2e;  // 256 threads = 16 x 16
+    sA[L.tid] = p.A[dd * kStates + n] * kLog2e;  // 256 threads = 16 x 16
   }
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
@@ -248,109 +380,17 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
   const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
   float sdt_total = 0.0f;
 
-  for (int64_t t0 = ct0; t0 < ct1; t0 += kBlockTokens) {
-    // B and C of this block: thread (n, q) fetches state n, lane run q.
-    float vb[K], vc[K];
-    {
-      const int n = tid >> 4, q = tid & 15;
-      const int64_t t = t0 + q * K;
-      load_run<T, K, kVec>(Bb + n * p.L, t, ct1, vb);
-      load_run<T, K, kVec>(Cb + n * p.L, t, ct1, vc);
-    }
-    // This lane's tokens: discretisation step, dt*u, and the D skip.
-    const int64_t tl = t0 + li * K;
-    float dt[K], du[K], y[K];
-    float sdt = 0.0f;
-    {
-      float uu[K], dr[K];
-      load_run<T, K, kVec>(urow, tl, ct1, uu);
-      load_run<T, K, kVec>(drow, tl, ct1, dr);
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const float x = dr[j] + bias;
-        float v = p.softplus ? softplus_f(x) : x;
-        v = (tl + j < ct1) ? v : 0.0f;  // past the end: identity step
-        dt[j] = v;
-        du[j] = v * uu[j];
-        y[j] = Dd * uu[j];
-        sdt += v;
-      }
-    }
-    float zz[K];
-    if (zrow) load_run<T, K, kVec>(zrow, tl, ct1, zz);
-
-    __syncthreads();  // the previous block's tile is no longer read
-    {
-      const int n = tid >> 4, q = tid & 15;
-      float4 *pb = reinterpret_cast<float4 *>(&sB[(n * kRowLanes + q) * KP]);
-      float4 *pc = reinterpret_cast<float4 *>(&sC[(n * kRowLanes + q) * KP]);
-#pragma unroll
-      for (int j = 0; j < K / 4; ++j) {
-        pb[j] = make_float4(vb[4 * j], vb[4 * j + 1], vb[4 * j + 2], vb[4 * j + 3]);
-        pc[j] = make_float4(vc[4 * j], vc[4 * j + 1], vc[4 * j + 2], vc[4 * j + 3]);
-      }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int n = 0; n < kStates; ++n) {
-      const float Aq = sA[ch * kStates + n];
-      const float *pb = &sB[(n * kRowLanes + li) * KP];
-      const float *pc = &sC[(n * kRowLanes + li) * KP];
-      float a[K], bb[K];
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        a[j] = fast_exp2(dt[j] * Aq);
-        bb[j] = du[j] * pb[j];
-      }
-      // Fold the lane's tokens into one affine map h -> P*h + H.
-      float H = bb[0];
-#pragma unroll
-      for (int j = 1; j < K; ++j) H = fmaf(a[j], H, bb[j]);
-      float P = fast_exp2(sdt * Aq);
-      // Carried state from the previous block (lane 15) enters lane 0.
-      const float X = dpp<kRowRor1>(hlast[n], hlast[n]);
-      if (li == 0) H = fmaf(P, X, H);
-      // Inclusive scan of the affine maps over the 16 lanes of the row:
-      // (P, H) <- (P * P', P * H' + H) with (P', H') from lane i - s.
-      {
-        float hs = dpp<kRowShr1, 0xF, 0xF, true>(0.0f, H);
-        float ps = dpp<kRowShr1, 0xF, 0xF, false>(1.0f, P);
-        H = fmaf(P, hs, H);
-        P *= ps;
-        hs = dpp<kRowShr2, 0xF, 0xF, true>(0.0f, H);
-        ps = dpp<kRowShr2, 0xF, 0xF, false>(1.0f, P);
-        H = fmaf(P, hs, H);
-        P *= ps;
-        hs = dpp<kRowShr4, 0xF, 0xF, true>(0.0f, H);
-        ps = dpp<kRowShr4, 0xF, 0xF, false>(1.0f, P);
-        H = fmaf(P, hs, H);
-        P *= ps;
-        hs = dpp<kRowShr8, 0xF, 0xF, true>(0.0f, H);
-        H = fmaf(P, hs, H);
-      }
-      // H is now the true state after this lane's last token; the lane's
-      // incoming state is its left neighbour's (lane 0: the carried X).
-      float h = dpp<kRowShr1, 0xF, 0xF, false>(X, H);
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        h = fmaf(a[j], h, bb[j]);
-        y[j] = fmaf(pc[j], h, y[j]);
-      }
-      hlast[n] = h;
-    }
-
-    if (zrow) {
-#pragma unroll
-      for (int j = 0; j < K; ++j) y[j] *= silu_f(zz[j]);
-    }
-    if (row_ok) store_run<T, K, kVec>(yrow, tl, ct1, y);
-    sdt_total += sdt;
-  }
+  int64_t t0 = ct0;
+  for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens)
+    scan_block<T, kVec, true>(p, L, t0, ct1, Bb, Cb, urow, drow, zrow, yrow,
+                              row_ok, bias, Dd, sB, sC, sA, hlast, sdt_total);
+  if (t0 < ct1)
+    scan_block<T, kVec, false>(p, L, t0, ct1, Bb, Cb, urow, drow, zrow, yrow,
+                               row_ok, bias, Dd, sB, sC, sA, hlast, sdt_total);
 
   if (!row_ok) return;
   if (p.n_chunks == 1) {
-    if (p.h_final && li == 15) {
+    if (p.h_final && L.li == 15) {
 #pragma unroll
       for (int n = 0; n < kStates; ++n) p.h_final[bd * kStates + n] = hlast[n];
     }
@@ -360,7 +400,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
     s += dpp<kRowRor4>(s, s);
     s += dpp<kRowRor2>(s, s);
     s += dpp<kRowRor1>(s, s);
-    if (li == 15) {
+    if (L.li == 15) {
       const int64_t base = bd * p.n_chunks + chunk;
 #pragma unroll
       for (int n = 0; n < kStates; ++n) p.ws_H[base * kStates + n] = hlast[n];
