@@ -50,9 +50,10 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int64_t kMaxGridYZ = 65535;
 // Waves the scan needs to keep all 1024 SIMDs of an MI355X busy; below this
-// (with one wave per 4 channels) long sequences are split into chunks.
+// (one wave per channel) long sequences are split into chunks.
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kMinAutoChunk = 8192;
+constexpr int64_t kSimds = 1024;  // 256 CUs x 4 SIMDs
 
 int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
   if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0)
@@ -76,10 +77,14 @@ int64_t choose_chunk(int64_t batch, int64_t dim, int64_t seqlen, int64_t request
   if (requested > 0) {
     chunk = round_up(requested, ssm::kBlockTokens);
   } else {
-    const int64_t groups = (dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
-    const int64_t waves = batch * groups * ssm::kWavesPerGroup;
+    // one wave per (batch, channel)
+    const int64_t waves = batch * dim;
     if (waves >= kTargetWaves / 2) return seqlen;
-    const int64_t n_c = (kTargetWaves + waves - 1) / waves;
+    int64_t n_c = (kTargetWaves + waves - 1) / waves;
+    // prefer a whole number of waves per SIMD (1024 SIMDs) when that costs
+    // at most three more chunks
+    for (int64_t k = n_c; k < n_c + 4; ++k)
+      if ((waves * k) % kSimds == 0) { n_c = k; break; }
     chunk = round_up((seqlen + n_c - 1) / n_c, ssm::kBlockTokens);
     if (chunk < kMinAutoChunk) chunk = kMinAutoChunk;
   }

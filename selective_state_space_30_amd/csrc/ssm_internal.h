@@ -9,12 +9,12 @@
 namespace ssm {
 
 constexpr int kStates = 16;          // d_state supported by this build
-constexpr int kRowLanes = 16;        // lanes that share one channel's tokens
-constexpr int kRowsPerWave = 4;      // channels per 64-lane wave
-constexpr int kWavesPerGroup = 4;    // waves per workgroup
-constexpr int kChannelsPerGroup = kRowsPerWave * kWavesPerGroup;  // 16
+constexpr int kWaveLanes = 64;       // one channel per 64-lane wave
+constexpr int kWavesPerGroup = 4;    // waves (channels) per workgroup
+constexpr int kChannelsPerGroup = kWavesPerGroup;                  // 4
 constexpr int kTokensPerLane = 16;   // consecutive tokens owned by one lane
-constexpr int kBlockTokens = kRowLanes * kTokensPerLane;          // 256
+constexpr int kBlockTokens = kWaveLanes * kTokensPerLane;         // 1024
+constexpr int kPhaseStates = 4;      // states whose B/C share the LDS tile
 
 struct ScanArgs {
   const void *u, *delta, *B, *C, *z;  // activations (dtype)

@@ -14,16 +14,18 @@
 // (discretise and recur on chip, fuse the steps, never write the expanded
 // (token x state) quantities to HBM).
 //
-// Work layout of the scan kernel (one workgroup = 4 waves = 16 channels of
-// one batch entry; one wave = 4 channel rows of 16 lanes; one lane = 16
-// consecutive tokens of its row's channel; a block = 256 tokens):
-//   * B and C of the block (16 states x 256 tokens) are read from HBM once per
-//     workgroup, widened to fp32 and kept in LDS, shared by its 16 channels;
+// Work layout of the scan kernel (one wave = one channel; one workgroup = 4
+// channels of one batch entry; one lane = 16 consecutive tokens; a block =
+// 64 lanes x 16 = 1024 tokens):
+//   * B and C of the block are read from HBM once per workgroup, four states
+//     at a time, widened to fp32 and kept in LDS, shared by its 4 channels;
 //   * per lane and state n: dA and dB*u of its 16 tokens stay in registers;
-//     the lane folds them into one affine pair (P, H); a 4-step DPP scan over
-//     the 16 lanes of the row composes the pairs (the state carried in from
-//     the previous block enters lane 0 first); each lane then replays its 16
-//     tokens from its true incoming state and accumulates C_t,n * h into y;
+//     the lane folds them into one affine pair (P, H); a 6-step DPP scan over
+//     the 64 lanes composes the pairs (the state carried in from the previous
+//     block enters lane 0 first); each lane then replays its 16 tokens from
+//     its true incoming state and accumulates C_t,n * h into y;
+//   * the channel's A, D, bias and carried state are wave-uniform (scalar
+//     registers);
 //   * the epilogue applies the gate and writes y; the state after the last
 //     token goes to h_final.
 // All arithmetic is fp32.  No MFMA: the work is a recurrence, not a dense
@@ -131,10 +133,10 @@ __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
 // Loads K consecutive activations row[t .. t+K) as fp32; positions >= tend
 // read as 0.  With kVec the run is fetched with 16-byte loads when it is
 // wholly in range (the caller guarantees 16-byte alignment of row + t).
-template <typename T, int K, bool kVec>
+template <typename T, int K, bool kVec, bool kInRange = false>
 __device__ __forceinline__ void load_run(const T *__restrict__ row, int64_t t,
                                          int64_t tend, float (&v)[K]) {
-  if (kVec && t + K <= tend) {
+  if (kVec && (kInRange || t + K <= tend)) {
     if constexpr (sizeof(T) == 2) {
       const uint4 *p = reinterpret_cast<const uint4 *>(row + t);
 #pragma unroll
@@ -161,17 +163,22 @@ __device__ __forceinline__ void load_run(const T *__restrict__ row, int64_t t,
       }
     }
   } else {
+    // Branch-free: out-of-range positions read a valid element (the last
+    // one in range) and are then replaced by 0.
 #pragma unroll
-    for (int j = 0; j < K; ++j)
-      v[j] = (t + j < tend) ? to_f32<T>(row[t + j]) : 0.0f;
+    for (int j = 0; j < K; ++j) {
+      const bool in = kInRange || t + j < tend;
+      const float x = to_f32<T>(row[in ? t + j : tend - 1]);
+      v[j] = in ? x : 0.0f;
+    }
   }
 }
 
 // Stores the in-range part (positions < tend) of a K-token run.
-template <typename T, int K, bool kVec>
+template <typename T, int K, bool kVec, bool kInRange = false>
 __device__ __forceinline__ void store_run(T *__restrict__ row, int64_t t,
                                           int64_t tend, const float (&v)[K]) {
-  if (kVec && t + K <= tend) {
+  if (kVec && (kInRange || t + K <= tend)) {
     if constexpr (sizeof(T) == 2) {
       uint4 *p = reinterpret_cast<uint4 *>(row + t);
 #pragma unroll
@@ -208,169 +215,188 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
 }
 
 // ---------------------------------------------------------------- scan ---
-// Value of lane 15 of the row in lane 0, zero in the other lanes.
-__device__ __forceinline__ float row_last_to_first(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x10F,
-                                                 0xF, 0xF, true));
-}
-// x from lane i - s of the row, zero where that lane does not exist.
-template <int kCtrl>
-__device__ __forceinline__ float row_shift_zero(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl,
-                                                 0xF, 0xF, true));
+// Inclusive scan of affine maps h -> P*h + H over the 64 lanes of a wave,
+// earlier lanes composed into later ones:
+//   (P, H)_i <- (P_i * P_j, P_i * H_j + H_i),  j = i - s,  s = 1, 2, 4, 8
+// inside each 16-lane row, then across rows (lane 15 -> rows 1 and 3, lane
+// 31 -> rows 2 and 3).  Each step is one DPP-fused VALU operation: where the
+// source lane does not exist, H adds 0 (bound_ctrl) and P is left unwritten.
+// `s_nop 1` gives every DPP read the two wait states it needs after a VALU
+// write of its source.  On return H_i is the composition of lanes 0..i; P is
+// not meaningful any more.
+__device__ __forceinline__ void wave_affine_scan(float &P, float &H) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      : "+v"(P), "+v"(H));
 }
 
-struct ScanLane {
-  int tid, wave, lane, row, li, ch;
-};
+// Lane i receives H of lane i - 1; lane 0 receives `first`.
+__device__ __forceinline__ float wave_shift_in(float H, float first) {
+  float r = first;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mov_b32_dpp %0, %1 wave_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(r)
+      : "v"(H));
+  return r;
+}
 
-// One block of 256 tokens for the 16 channels of the workgroup.  kFull:
-// the block lies wholly inside [ct0, ct1) (no masking); otherwise positions
-// past ct1 act as identity steps (dt = 0, u = 0) and are not stored.
-template <typename T, bool kVec, bool kFull>
+__device__ __forceinline__ float lane_broadcast(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// One block of 1024 tokens of one channel per wave (4 channels of one batch
+// entry per workgroup).  kFull: the block lies wholly inside [t0, ct1), so
+// nothing is masked; otherwise positions from ct1 on are identity steps
+// (dt = 0, u = 0) and are not stored.  hc[n]: the channel's state carried in
+// (wave-uniform), replaced by the state after the block.
+template <typename T, bool kVec, bool kFull, bool kSoftplus>
 __device__ __forceinline__ void scan_block(
-    const ScanArgs &p, const ScanLane &L, int64_t t0, int64_t ct1,
+    const ScanArgs &p, int tid, int lane, int64_t t0, int64_t ct1,
     const T *__restrict__ Bb, const T *__restrict__ Cb,
     const T *__restrict__ urow, const T *__restrict__ drow,
-    const T *__restrict__ zrow, T *__restrict__ yrow, bool row_ok,
-    float bias, float Dd, float *sB, float *sC, const float *sA,
-    float (&hlast)[kStates], float &sdt_total) {
+    const T *__restrict__ zrow, T *__restrict__ yrow, bool ch_ok, float bias,
+    float Dd, const float (&Ach)[kStates], float *sB, float *sC,
+    float (&hc)[kStates], float &sdt_total) {
   constexpr int K = kTokensPerLane;
-  constexpr int KP = K + 4;
+  constexpr int KP = K + 4;  // padded LDS stride of one lane's run
   const int64_t tend = kFull ? t0 + kBlockTokens : ct1;
-  // B and C of this block: thread (n, q) fetches state n, lane run q.
-  float vb[K], vc[K];
-  {
-    const int n = L.tid >> 4, q = L.tid & 15;
-    const int64_t t = t0 + q * K;
-    load_run<T, K, kVec>(Bb + n * p.L, t, tend, vb);
-    load_run<T, K, kVec>(Cb + n * p.L, t, tend, vc);
-  }
-  // This lane's tokens: discretisation step, dt*u and the D skip.
-  const int64_t tl = t0 + L.li * K;
-  float dt[K], du[K], y[K];
+  const int64_t tl = t0 + static_cast<int64_t>(lane) * K;
+
+  // This lane's tokens: the step dt (kept as dt*log2(e) for exp2), dt*u
+  // and the D skip.
+  float dtl[K], du[K], y[K];
   float sdt = 0.0f;
   {
     float uu[K], dr[K];
-    load_run<T, K, kVec>(urow, tl, tend, uu);
-    load_run<T, K, kVec>(drow, tl, tend, dr);
+    load_run<T, K, kVec, kFull>(urow, tl, tend, uu);
+    load_run<T, K, kVec, kFull>(drow, tl, tend, dr);
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const float x = dr[j] + bias;
-      float v = p.softplus ? softplus_f(x) : x;
+      float v = kSoftplus ? softplus_f(x) : x;
       if (!kFull) v = (tl + j < tend) ? v : 0.0f;  // identity step
-      dt[j] = v;
+      dtl[j] = v * kLog2e;
       du[j] = v * uu[j];
       y[j] = Dd * uu[j];
       sdt += v;
     }
   }
-
-  __syncthreads();  // the previous block's tile is no longer read
-  {
-    const int n = L.tid >> 4, q = L.tid & 15;
-    float4 *pb = reinterpret_cast<float4 *>(&sB[(n * kRowLanes + q) * KP]);
-    float4 *pc = reinterpret_cast<float4 *>(&sC[(n * kRowLanes + q) * KP]);
-#pragma unroll
-    for (int j = 0; j < K / 4; ++j) {
-      pb[j] = make_float4(vb[4 * j], vb[4 * j + 1], vb[4 * j + 2], vb[4 * j + 3]);
-      pc[j] = make_float4(vc[4 * j], vc[4 * j + 1], vc[4 * j + 2], vc[4 * j + 3]);
-    }
-  }
-  __syncthreads();
+  const float sdtl = sdt * kLog2e;
 
 #pragma unroll
-  for (int n = 0; n < kStates; ++n) {
-    const float Aq = sA[L.ch * kStates + n];
-    const float *pb = &sB[(n * kRowLanes + L.li) * KP];
-    const float *pc = &sC[(n * kRowLanes + L.li) * KP];
-    float a[K], bb[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      a[j] = fast_exp2(dt[j] * Aq);
-      bb[j] = du[j] * pb[j];
+  for (int ph = 0; ph < kStates / kPhaseStates; ++ph) {
+    asm volatile("" ::: "memory");  // fetch this phase's B/C only now
+    // B and C of kPhaseStates states for the block: thread (s, q) fetches
+    // state ph*4 + s, lane run q; the tile is shared by the 4 waves.
+    float vb[K], vc[K];
+    {
+      const int st = tid >> 6, q = tid & 63;
+      const int64_t n = ph * kPhaseStates + st;
+      const int64_t t = t0 + static_cast<int64_t>(q) * K;
+      load_run<T, K, kVec, kFull>(Bb + n * p.L, t, tend, vb);
+      load_run<T, K, kVec, kFull>(Cb + n * p.L, t, tend, vc);
     }
-    // Fold the lane's tokens into one affine map h -> P*h + H.
-    float H = bb[0];
+    __syncthreads();  // the previous tile is no longer read
+    {
+      const int st = tid >> 6, q = tid & 63;
+      float4 *pb = reinterpret_cast<float4 *>(&sB[(st * kWaveLanes + q) * KP]);
+      float4 *pc = reinterpret_cast<float4 *>(&sC[(st * kWaveLanes + q) * KP]);
 #pragma unroll
-    for (int j = 1; j < K; ++j) H = fmaf(a[j], H, bb[j]);
-    float P = fast_exp2(sdt * Aq);
-    // The carried state (lane 15's, from the previous block) enters lane 0;
-    // X is zero in the other lanes.
-    const float X = row_last_to_first(hlast[n]);
-    H = fmaf(P, X, H);
-    // Inclusive scan of the affine maps over the 16 lanes of the row:
-    // (P, H) <- (P * P', P * H' + H) with (P', H') from lane i - s.  Where
-    // lane i - s does not exist H is unchanged (H' reads 0); P then becomes
-    // 0, but a lane whose composition already starts at lane 0 never has
-    // its P read again (the carry has entered before the scan).
-    H = fmaf(P, row_shift_zero<kRowShr1>(H), H);
-    P *= row_shift_zero<kRowShr1>(P);
-    H = fmaf(P, row_shift_zero<kRowShr2>(H), H);
-    P *= row_shift_zero<kRowShr2>(P);
-    H = fmaf(P, row_shift_zero<kRowShr4>(H), H);
-    P *= row_shift_zero<kRowShr4>(P);
-    H = fmaf(P, row_shift_zero<kRowShr8>(H), H);
-    // H is now the true state after this lane's last token; the lane's
-    // incoming state is its left neighbour's (lane 0: the carried X).
-    float h = row_shift_zero<kRowShr1>(H) + X;
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      h = fmaf(a[j], h, bb[j]);
-      y[j] = fmaf(pc[j], h, y[j]);
+      for (int j = 0; j < K / 4; ++j) {
+        pb[j] = make_float4(vb[4 * j], vb[4 * j + 1], vb[4 * j + 2], vb[4 * j + 3]);
+        pc[j] = make_float4(vc[4 * j], vc[4 * j + 1], vc[4 * j + 2], vc[4 * j + 3]);
+      }
     }
-    hlast[n] = h;
+    __syncthreads();
+
+#pragma unroll
+    for (int s4 = 0; s4 < kPhaseStates; ++s4) {
+      const int n = ph * kPhaseStates + s4;
+      float An = Ach[n];
+      asm volatile("" : "+s"(An));  // keep this state's work after the previous state's
+      const float *pb = &sB[(s4 * kWaveLanes + lane) * KP];
+      const float *pc = &sC[(s4 * kWaveLanes + lane) * KP];
+      float a[K], bb[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        a[j] = fast_exp2(dtl[j] * An);
+        bb[j] = du[j] * pb[j];
+      }
+      // Fold the lane's tokens into one affine map h -> P*h + H.
+      float H = bb[0];
+#pragma unroll
+      for (int j = 1; j < K; ++j) H = fmaf(a[j], H, bb[j]);
+      float P = fast_exp2(sdtl * An);
+      // The carried state enters through lane 0, then the maps compose.
+      H = fmaf(P, lane == 0 ? hc[n] : 0.0f, H);
+      wave_affine_scan(P, H);
+      // H_i is the true state after lane i's last token; lane i starts from
+      // lane i-1's (lane 0 from the carried state) and replays its tokens.
+      float h = wave_shift_in(H, hc[n]);
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        h = fmaf(a[j], h, bb[j]);
+        y[j] = fmaf(pc[j], h, y[j]);
+      }
+      hc[n] = lane_broadcast(h, kWaveLanes - 1);
+    }
   }
 
   if (zrow) {
     float zz[K];
-    load_run<T, K, kVec>(zrow, tl, tend, zz);
+    load_run<T, K, kVec, kFull>(zrow, tl, tend, zz);
 #pragma unroll
     for (int j = 0; j < K; ++j) y[j] *= silu_f(zz[j]);
   }
-  if (row_ok) store_run<T, K, kVec && kFull>(yrow, tl, tend, y);
+  if (ch_ok) store_run<T, K, kVec, kFull>(yrow, tl, tend, y);
   sdt_total += sdt;
 }
 
-template <typename T, bool kVec>
+template <typename T, bool kVec, bool kSoftplus>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_kernel(ScanArgs p) {
-  constexpr int K = kTokensPerLane;
-  constexpr int KP = K + 4;  // padded LDS stride per lane run (bank spread)
-  __shared__ float sB[kStates * kRowLanes * KP];
-  __shared__ float sC[kStates * kRowLanes * KP];
-  __shared__ float sA[kChannelsPerGroup * kStates];
+  constexpr int KP = kTokensPerLane + 4;
+  __shared__ float sB[kPhaseStates * kWaveLanes * KP];
+  __shared__ float sC[kPhaseStates * kWaveLanes * KP];
 
-  ScanLane L;
-  L.tid = threadIdx.x;
-  L.wave = L.tid >> 6;
-  L.lane = L.tid & 63;
-  L.row = L.lane >> 4;
-  L.li = L.lane & 15;
-  L.ch = L.wave * kRowsPerWave + L.row;  // channel slot in the group
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t b = blockIdx.y;
-  const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kChannelsPerGroup;
-  const bool row_ok = d0 + L.ch < p.dim;
-  const int64_t d = row_ok ? d0 + L.ch : p.dim - 1;  // clamped for reads
+  const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kChannelsPerGroup + wave;
+  const bool ch_ok = d_raw < p.dim;
+  const int64_t d = ch_ok ? d_raw : p.dim - 1;  // clamped for reads
   const int chunk = blockIdx.z;
   const int64_t ct0 = static_cast<int64_t>(chunk) * p.chunk_len;
   const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
-
-  {
-    const int c = L.tid >> 4, n = L.tid & 15;
-    const int64_t dd = d0 + c < p.dim ? d0 + c : p.dim - 1;
-    sA[L.tid] = p.A[dd * kStates + n] * kLog2e;  // 256 threads = 16 x 16
-  }
-  const float bias = p.bias ? p.bias[d] : 0.0f;
-  const float Dd = p.D ? p.D[d] : 0.0f;
   const int64_t bd = b * p.dim + d;
 
-  // hlast[n]: this lane's state after its last token of the previous block;
-  // lane 15 of the row holds the row's true carried state.
-  float hlast[kStates];
+  float Ach[kStates];  // the channel's A (wave-uniform)
+#pragma unroll
+  for (int n = 0; n < kStates; ++n) Ach[n] = p.A[d * kStates + n];
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float Dd = p.D ? p.D[d] : 0.0f;
+  float hc[kStates];  // the channel's carried state (wave-uniform)
 #pragma unroll
   for (int n = 0; n < kStates; ++n)
-    hlast[n] = (chunk == 0 && p.h0) ? p.h0[bd * kStates + n] : 0.0f;
+    hc[n] = (chunk == 0 && p.h0) ? p.h0[bd * kStates + n] : 0.0f;
 
   const T *urow = static_cast<const T *>(p.u) + bd * p.L;
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
@@ -381,29 +407,29 @@ void scan_kernel(ScanArgs p) {
   float sdt_total = 0.0f;
 
   int64_t t0 = ct0;
+#pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens)
-    scan_block<T, kVec, true>(p, L, t0, ct1, Bb, Cb, urow, drow, zrow, yrow,
-                              row_ok, bias, Dd, sB, sC, sA, hlast, sdt_total);
+    scan_block<T, kVec, true, kSoftplus>(p, tid, lane, t0, ct1, Bb, Cb, urow, drow, zrow,
+                              yrow, ch_ok, bias, Dd, Ach, sB, sC, hc, sdt_total);
   if (t0 < ct1)
-    scan_block<T, kVec, false>(p, L, t0, ct1, Bb, Cb, urow, drow, zrow, yrow,
-                               row_ok, bias, Dd, sB, sC, sA, hlast, sdt_total);
+    // the last, partial block: branch-free scalar loads (rare; keeps the
+    // register budget of the full-block loop)
+    scan_block<T, false, false, kSoftplus>(p, tid, lane, t0, ct1, Bb, Cb, urow, drow, zrow,
+                               yrow, ch_ok, bias, Dd, Ach, sB, sC, hc, sdt_total);
 
-  if (!row_ok) return;
+  if (!ch_ok) return;
   if (p.n_chunks == 1) {
-    if (p.h_final && L.li == 15) {
+    if (p.h_final && lane == 0) {
 #pragma unroll
-      for (int n = 0; n < kStates; ++n) p.h_final[bd * kStates + n] = hlast[n];
+      for (int n = 0; n < kStates; ++n) p.h_final[bd * kStates + n] = hc[n];
     }
   } else {
-    float s = sdt_total;  // sum of dt over the chunk, reduced over the row
-    s += dpp<kRowRor8>(s, s);
-    s += dpp<kRowRor4>(s, s);
-    s += dpp<kRowRor2>(s, s);
-    s += dpp<kRowRor1>(s, s);
-    if (L.li == 15) {
+    // sum of dt over the chunk (all lanes), for the chunk carry
+    const float s = lane_broadcast(wave_inclusive_sum(sdt_total), kWaveLanes - 1);
+    if (lane == 0) {
       const int64_t base = bd * p.n_chunks + chunk;
 #pragma unroll
-      for (int n = 0; n < kStates; ++n) p.ws_H[base * kStates + n] = hlast[n];
+      for (int n = 0; n < kStates; ++n) p.ws_H[base * kStates + n] = hc[n];
       p.ws_S[base] = s;
     }
   }
@@ -553,7 +579,10 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
                                         kChannelsPerGroup),
                   static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(a.n_chunks));
-  hipLaunchKernelGGL((scan_kernel<T, kVec>), grid, dim3(256), 0, s, a);
+  if (a.softplus)
+    hipLaunchKernelGGL((scan_kernel<T, kVec, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_kernel<T, kVec, false>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
   const int64_t nthreads = a.batch * a.dim * kStates;

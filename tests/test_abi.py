@@ -94,10 +94,10 @@ INVALID_SCAN_CASES = [
     ("h_final overlaps y", dict(h_final=FAKE + 0x50000000 + 128), 1),
     ("batch beyond grid", dict(batch=70000), 2),
     ("size overflow", dict(batch=1 << 20, dim=1 << 30, seqlen=1 << 30), 1),
-    ("split without workspace", dict(chunk=256, seqlen=1024), 3),
-    ("split with small workspace", dict(chunk=256, seqlen=1024,
+    ("split without workspace", dict(chunk=1024, seqlen=4096), 3),
+    ("split with small workspace", dict(chunk=1024, seqlen=4096,
                                         ws=FAKE + 0x70000000, ws_bytes=64), 3),
-    ("misaligned workspace", dict(chunk=256, seqlen=1024,
+    ("misaligned workspace", dict(chunk=1024, seqlen=4096,
                                   ws=FAKE + 0x70000000 + 4, ws_bytes=1 << 20), 1),
 ]
 
@@ -148,14 +148,15 @@ def test_plan_and_workspace(lib):
     # Plenty of channels: no split, no workspace.
     assert ssm.ssm_scan_plan(2, 5120, 16, 4096) == 4096
     assert ssm.ssm_scan_workspace_size(2, 5120, 16, 4096) == 0
-    # Few channels and a very long sequence: split into chunks of 256k.
+    # Few channels and a very long sequence: split into whole blocks.
     c = ssm.ssm_scan_plan(1, 1536, 16, 1 << 20)
-    assert c < (1 << 20) and c % 256 == 0
+    assert c < (1 << 20) and c % 1024 == 0
+    assert (1536 * (-(-(1 << 20) // c))) % 1024 == 0  # whole waves per SIMD
     n = -(-(1 << 20) // c)
     ws = ssm.ssm_scan_workspace_size(1, 1536, 16, 1 << 20)
     assert ws >= 1536 * n * (16 + 1 + 16) * 4
-    # Explicit chunk requests are rounded up to the 256-token block.
-    assert ssm.ssm_scan_plan(1, 4, 16, 1000, 100) == 256
+    # Explicit chunk requests are rounded up to the 1024-token block.
+    assert ssm.ssm_scan_plan(1, 4, 16, 3000, 100) == 1024
     assert ssm.ssm_scan_plan(1, 4, 16, 1000, 5000) == 1000
     with pytest.raises(ssm.SSMError):
         ssm.ssm_scan_plan(1, 4, 8, 1000)

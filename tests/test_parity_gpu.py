@@ -58,6 +58,8 @@ SMALL_CASES = [
     (3, 20, 777, "bf16", True, True, False),    # unaligned bf16 rows
     (2, 48, 1536, "bf16", True, True, True),    # aligned bf16, 6 blocks
     (1, 5, 4096, "bf16", False, True, False),   # no gate
+    (2, 37, 2048, "f32", True, True, True),     # aligned fp32, full blocks
+    (1, 6, 3072, "bf16", True, False, True),    # 3 full blocks, no D
 ]
 
 
@@ -82,13 +84,13 @@ def test_tiny_workload_exactly_as_specified():
 
 
 CHUNK_CASES = [
-    # (dtype, L, chunk, softplus, A kind)
-    ("f32", 3000, 512, True, "arange"),      # decays: fix-up stops early
-    ("f32", 2049, 256, True, "arange"),      # last chunk of one token
-    ("f32", 3000, 768, False, "arange"),     # softplus off: full fix-up
-    ("f32", 3000, 512, True, "positive"),    # an A > 0: full fix-up
-    ("bf16", 4096, 1024, True, "arange"),
-    ("bf16", 2500, 512, True, "slow"),       # slow decay: long fix-up
+    # (dtype, L, chunk, softplus, A kind); chunks are whole 1024-token blocks
+    ("f32", 3000, 1024, True, "arange"),     # decays: fix-up stops early
+    ("f32", 2049, 1024, True, "arange"),     # last chunk of one token
+    ("f32", 5000, 2048, False, "arange"),    # softplus off: full fix-up
+    ("f32", 3000, 1024, True, "positive"),   # an A > 0: full fix-up
+    ("bf16", 8192, 2048, True, "arange"),
+    ("bf16", 4500, 1024, True, "slow"),      # slow decay: long fix-up
 ]
 
 
@@ -117,7 +119,7 @@ def test_chunked_and_unsplit_agree():
     inp = to_dev(syn.make_scan_inputs(syn.TINY, "cpu", batch=1, dim=32,
                                       seqlen=5000, dtype="f32", seed=3))
     y1, h1 = gpu_scan(inp)
-    y2, h2 = gpu_scan(inp, chunk_len=1024)
+    y2, h2 = gpu_scan(inp, chunk_len=2048)
     check(y2, y1.double(), 1e-5, "y")
     check(h2, h1.double(), 1e-5, "h_final")
 
@@ -180,7 +182,7 @@ def test_workspace_too_small_is_rejected_on_device():
     ws = torch.empty(16, dtype=torch.uint8, device=DEV)
     with pytest.raises(ssm.SSMError) as e:
         ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
-                         chunk_len=256, workspace=ws)
+                         chunk_len=1024, workspace=ws)
     assert e.value.status == 3
 
 
