@@ -16,7 +16,17 @@ on its stream over the timed region) to the ALU ceiling that bounds it.
 
 Options beyond the contract: --no-cpu-baseline, --no-extra (skip the
 long-context and decode figures), --only-scan (nothing but the timed steps;
-for profiler runs).
+for profiler runs), --summarize DIR (no GPU: turn the rocprofv3 CSV output
+of the profiling commands below into the summaries under profiles/).
+
+Profiling commands (run from /tmp with TMPDIR=/tmp; DIR = an output folder):
+  rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o bench \
+      -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o fetch \
+      -- python3 bench.py --steps 3 --warmup 1 --no-extra --no-cpu-baseline
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write \
+      -- python3 bench.py --steps 3 --warmup 1 --no-extra --no-cpu-baseline
+  python3 bench.py --summarize DIR
 """
 from __future__ import annotations
 
@@ -71,7 +81,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only-scan", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs the scan on a "
               "single MI355X (no collectives or sharding); run with --gpus 1.",
@@ -286,6 +300,103 @@ def cpu_baseline(inp, cfg, nbytes, log):
                       "fp64, %.2f s wall" % (cfg.batch, cfg.dim, cfg.seqlen,
                                              sec),
             "elements_per_s": round(cfg.elements / sec)}
+
+
+SCAN_KERNEL = "scan_kernel<unsigned short, true, true>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30  # each calibration copy reads and writes 1 GiB
+
+
+def _csvs(d, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", "*" + suffix),
+                            recursive=True))
+
+
+def _kernel_key(name):
+    return name.replace("void ssm::(anonymous namespace)::", "").split("(")[0]
+
+
+def summarize_profiles(d):
+    """Writes profiles/scan_kernel_mamba2p8b_{kernel_stats.txt,traffic.json,
+    traffic.txt} from rocprofv3 CSVs under ``d`` (see the module doc)."""
+    import csv
+    import statistics
+    cmd_trace = ("rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace "
+                 "-o bench -- python3 bench.py --steps 20 --warmup 5 "
+                 "--no-cpu-baseline")
+    cmd_pmc = ("rocprofv3 --pmc {c} --output-format csv -d DIR/{d} -o {d} -- "
+               "python3 bench.py --steps 3 --warmup 1 --no-extra "
+               "--no-cpu-baseline")
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    # kernel statistics
+    rows = []
+    for f in _csvs(os.path.join(d, "trace"), "_kernel_stats.csv"):
+        rows += list(csv.DictReader(open(f)))
+    lines = ["# rocprofv3 kernel statistics, Mamba-2.8B-shaped scan benchmark",
+             "# command (from /tmp, TMPDIR=/tmp): " + cmd_trace,
+             "# summarized by: python3 bench.py --summarize DIR",
+             "# kernel | calls | average us | min us | max us | total ms"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
+        lines.append("%s | %s | %.2f | %.2f | %.2f | %.3f" % (
+            _kernel_key(r["Name"])[:90], r["Calls"],
+            float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6))
+    with open(os.path.join(prof, "scan_kernel_mamba2p8b_kernel_stats.txt"),
+              "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # HBM traffic from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by
+    # what the same counter reads for the 1 GiB calibration copy.
+    def per_dispatch(sub, counter):
+        vals = {}
+        for f in _csvs(os.path.join(d, sub), "_counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = _kernel_key(r["Kernel_Name"])
+                vals.setdefault(k, []).append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in vals.items()}
+    fetch = per_dispatch("fetch", "FETCH_SIZE")
+    write = per_dispatch("write", "WRITE_SIZE")
+    fetch_scale = COPY_BYTES / 1024 / fetch[COPY_KERNEL]
+    write_scale = COPY_BYTES / 1024 / write[COPY_KERNEL]
+    fb = fetch[SCAN_KERNEL] * fetch_scale * 1024
+    wb = write[SCAN_KERNEL] * write_scale * 1024
+    import synthetic as syn
+    alg = syn.algorithmic_bytes(syn.MAMBA_2P8B)
+    out = {"kernel": SCAN_KERNEL, "workload": syn.MAMBA_2P8B.name,
+           "kernel_source_sha256_16": kernel_source_hash(),
+           "fetch_kib_raw": fetch[SCAN_KERNEL], "write_kib_raw": write[SCAN_KERNEL],
+           "copy_fetch_kib_raw": fetch[COPY_KERNEL],
+           "copy_write_kib_raw": write[COPY_KERNEL],
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "hbm_read_bytes_per_launch": int(fb),
+           "hbm_write_bytes_per_launch": int(wb),
+           "hbm_bytes_per_launch": int(fb + wb),
+           "algorithmic_bytes_per_launch": alg,
+           "traffic_over_algorithmic": (fb + wb) / alg,
+           "commands": [cmd_pmc.format(c="FETCH_SIZE", d="fetch"),
+                        cmd_pmc.format(c="WRITE_SIZE", d="write"),
+                        "python3 bench.py --summarize DIR"]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    txt = ["# HBM traffic of the scan kernel, Mamba-2.8B-shaped workload",
+           "# commands (from /tmp, TMPDIR=/tmp):"] + ["#   " + c for c in out["commands"]]
+    txt += ["calibration: %s reads+writes 1 GiB per dispatch; FETCH_SIZE reads "
+            "%.0f KiB (scale %.3f), WRITE_SIZE %.0f KiB (scale %.3f)" % (
+                COPY_KERNEL, fetch[COPY_KERNEL], fetch_scale,
+                write[COPY_KERNEL], write_scale),
+            "scan kernel per dispatch: FETCH_SIZE %.0f KiB -> %.1f MB read; "
+            "WRITE_SIZE %.0f KiB -> %.1f MB written" % (
+                fetch[SCAN_KERNEL], fb / 1e6, write[SCAN_KERNEL], wb / 1e6),
+            "HBM bytes per launch %.1f MB vs algorithmic %.1f MB (ratio %.3f)" % (
+                (fb + wb) / 1e6, alg / 1e6, (fb + wb) / alg),
+            "kernel source sha256[:16] %s" % out["kernel_source_sha256_16"]]
+    with open(os.path.join(prof, "scan_kernel_mamba2p8b_traffic.txt"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print("\n".join(lines + txt))
 
 
 if __name__ == "__main__":

@@ -14,7 +14,7 @@ constexpr int kWavesPerGroup = 4;    // waves (channels) per workgroup
 constexpr int kChannelsPerGroup = kWavesPerGroup;                  // 4
 constexpr int kTokensPerLane = 16;   // consecutive tokens owned by one lane
 constexpr int kBlockTokens = kWaveLanes * kTokensPerLane;         // 1024
-constexpr int kPhaseStates = 4;      // states whose B/C share the LDS tile
+constexpr int kPhaseStates = 2;      // states per double-buffered B/C LDS tile
 
 struct ScanArgs {
   const void *u, *delta, *B, *C, *z;  // activations (dtype)

@@ -17,8 +17,10 @@
 // Work layout of the scan kernel (one wave = one channel; one workgroup = 4
 // channels of one batch entry; one lane = 16 consecutive tokens; a block =
 // 64 lanes x 16 = 1024 tokens):
-//   * B and C of the block are read from HBM once per workgroup, four states
-//     at a time, widened to fp32 and kept in LDS, shared by its 4 channels;
+//   * B and C of the block are read from HBM once per workgroup, two states
+//     at a time into a double-buffered LDS tile (the next pair is fetched
+//     while the current one is used), widened to fp32 and shared by the
+//     workgroup's 4 channels;
 //   * per lane and state n: dA and dB*u of its 16 tokens stay in registers;
 //     the lane folds them into one affine pair (P, H); a 6-step DPP scan over
 //     the 64 lanes composes the pairs (the state carried in from the previous
@@ -261,6 +263,52 @@ __device__ __forceinline__ float lane_broadcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// One thread's share of a B or C tile: K consecutive tokens of one state.
+// bf16 runs of full blocks stay packed (K/2 words) until they are written to
+// LDS as fp32; otherwise the run is held as fp32.
+template <typename T, int K, bool kVec, bool kInRange>
+struct TileRun {
+  static constexpr bool kPacked = kVec && kInRange && sizeof(T) == 2;
+  static constexpr int kWords = kPacked ? K / 2 : K;
+  uint32_t w[kWords];
+
+  __device__ __forceinline__ void load(const T *__restrict__ row, int64_t t,
+                                       int64_t tend) {
+    if constexpr (kPacked) {
+      const uint4 *q = reinterpret_cast<const uint4 *>(row + t);
+#pragma unroll
+      for (int i = 0; i < K / 8; ++i) {
+        const uint4 v = q[i];
+        w[4 * i + 0] = v.x;
+        w[4 * i + 1] = v.y;
+        w[4 * i + 2] = v.z;
+        w[4 * i + 3] = v.w;
+      }
+    } else {
+      float v[K];
+      load_run<T, K, kVec, kInRange>(row, t, tend, v);
+#pragma unroll
+      for (int j = 0; j < K; ++j) w[j] = __float_as_uint(v[j]);
+    }
+  }
+  __device__ __forceinline__ float at(int j) const {
+    if constexpr (kPacked)
+      return (j & 1) ? bf16_hi(w[j / 2]) : bf16_lo(w[j / 2]);
+    else
+      return __uint_as_float(w[j]);
+  }
+  // Writes the run as fp32 into tile[state st][matrix mat][run q].
+  __device__ __forceinline__ void store(float *tile, int st, int mat,
+                                        int q) const {
+    constexpr int KP = K + 4;
+    float4 *dst = reinterpret_cast<float4 *>(
+        &tile[((st * 2 + mat) * kWaveLanes + q) * KP]);
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j)
+      dst[j] = make_float4(at(4 * j), at(4 * j + 1), at(4 * j + 2), at(4 * j + 3));
+  }
+};
+
 // One block of 1024 tokens of one channel per wave (4 channels of one batch
 // entry per workgroup).  kFull: the block lies wholly inside [t0, ct1), so
 // nothing is masked; otherwise positions from ct1 on are identity steps
@@ -272,12 +320,21 @@ __device__ __forceinline__ void scan_block(
     const T *__restrict__ Bb, const T *__restrict__ Cb,
     const T *__restrict__ urow, const T *__restrict__ drow,
     const T *__restrict__ zrow, T *__restrict__ yrow, bool ch_ok, float bias,
-    float Dd, const float (&Ach)[kStates], float *sB, float *sC,
-    float (&hc)[kStates], float &sdt_total) {
+    float Dd, const float (&Ach)[kStates], float *sT, float (&hc)[kStates],
+    float &sdt_total) {
   constexpr int K = kTokensPerLane;
   constexpr int KP = K + 4;  // padded LDS stride of one lane's run
   const int64_t tend = kFull ? t0 + kBlockTokens : ct1;
   const int64_t tl = t0 + static_cast<int64_t>(lane) * K;
+  constexpr int kPhases = kStates / 2;
+  constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
+
+  // Staging role of this thread: state (2*ph + st), matrix B or C, run q.
+  const int st = tid >> 7, mat = (tid >> 6) & 1, q = tid & 63;
+  const T *src = mat ? Cb : Bb;
+  const int64_t tq = t0 + static_cast<int64_t>(q) * K;
+  TileRun<T, K, kVec, kFull> run;
+  run.load(src + st * p.L, tq, tend);
 
   // This lane's tokens: the step dt (kept as dt*log2(e) for exp2), dt*u
   // and the D skip.
@@ -298,41 +355,26 @@ __device__ __forceinline__ void scan_block(
       sdt += v;
     }
   }
+  // Phase 0's tile: its buffer was last read two phases ago, by every wave.
+  run.store(sT, st, mat, q);
   const float sdtl = sdt * kLog2e;
 
+  // B and C are staged two states at a time in a double-buffered LDS tile
+  // (tile[buffer][state][B|C][lane run][KP]); while the 4 waves compute
+  // phase ph, each thread already holds phase ph+1's run in registers.
 #pragma unroll
-  for (int ph = 0; ph < kStates / kPhaseStates; ++ph) {
-    asm volatile("" ::: "memory");  // fetch this phase's B/C only now
-    // B and C of kPhaseStates states for the block: thread (s, q) fetches
-    // state ph*4 + s, lane run q; the tile is shared by the 4 waves.
-    float vb[K], vc[K];
-    {
-      const int st = tid >> 6, q = tid & 63;
-      const int64_t n = ph * kPhaseStates + st;
-      const int64_t t = t0 + static_cast<int64_t>(q) * K;
-      load_run<T, K, kVec, kFull>(Bb + n * p.L, t, tend, vb);
-      load_run<T, K, kVec, kFull>(Cb + n * p.L, t, tend, vc);
-    }
-    __syncthreads();  // the previous tile is no longer read
-    {
-      const int st = tid >> 6, q = tid & 63;
-      float4 *pb = reinterpret_cast<float4 *>(&sB[(st * kWaveLanes + q) * KP]);
-      float4 *pc = reinterpret_cast<float4 *>(&sC[(st * kWaveLanes + q) * KP]);
+  for (int ph = 0; ph < kPhases; ++ph) {
+    if (ph + 1 < kPhases)
+      run.load(src + (2 * (ph + 1) + st) * p.L, tq, tend);
+    __syncthreads();  // phase ph's tile is complete and visible
+    const float *tile = sT + (ph & 1) * kTileFloats;
 #pragma unroll
-      for (int j = 0; j < K / 4; ++j) {
-        pb[j] = make_float4(vb[4 * j], vb[4 * j + 1], vb[4 * j + 2], vb[4 * j + 3]);
-        pc[j] = make_float4(vc[4 * j], vc[4 * j + 1], vc[4 * j + 2], vc[4 * j + 3]);
-      }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int s4 = 0; s4 < kPhaseStates; ++s4) {
-      const int n = ph * kPhaseStates + s4;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int n = 2 * ph + s2;
       float An = Ach[n];
       asm volatile("" : "+s"(An));  // keep this state's work after the previous state's
-      const float *pb = &sB[(s4 * kWaveLanes + lane) * KP];
-      const float *pc = &sC[(s4 * kWaveLanes + lane) * KP];
+      const float *pb = &tile[((s2 * 2 + 0) * kWaveLanes + lane) * KP];
+      const float *pc = &tile[((s2 * 2 + 1) * kWaveLanes + lane) * KP];
       float a[K], bb[K];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
@@ -357,6 +399,9 @@ __device__ __forceinline__ void scan_block(
       }
       hc[n] = lane_broadcast(h, kWaveLanes - 1);
     }
+    // Every wave has passed this phase's barrier, so the other buffer (read
+    // in phase ph-1) is free: fill it with phase ph+1.
+    if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, st, mat, q);
   }
 
   if (zrow) {
@@ -373,8 +418,7 @@ template <typename T, bool kVec, bool kSoftplus>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_kernel(ScanArgs p) {
   constexpr int KP = kTokensPerLane + 4;
-  __shared__ float sB[kPhaseStates * kWaveLanes * KP];
-  __shared__ float sC[kPhaseStates * kWaveLanes * KP];
+  __shared__ float sT[2 * 2 * 2 * kWaveLanes * KP];  // 40 KB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -410,12 +454,12 @@ void scan_kernel(ScanArgs p) {
 #pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens)
     scan_block<T, kVec, true, kSoftplus>(p, tid, lane, t0, ct1, Bb, Cb, urow, drow, zrow,
-                              yrow, ch_ok, bias, Dd, Ach, sB, sC, hc, sdt_total);
+                              yrow, ch_ok, bias, Dd, Ach, sT, hc, sdt_total);
   if (t0 < ct1)
     // the last, partial block: branch-free scalar loads (rare; keeps the
     // register budget of the full-block loop)
     scan_block<T, false, false, kSoftplus>(p, tid, lane, t0, ct1, Bb, Cb, urow, drow, zrow,
-                               yrow, ch_ok, bias, Dd, Ach, sB, sC, hc, sdt_total);
+                               yrow, ch_ok, bias, Dd, Ach, sT, hc, sdt_total);
 
   if (!ch_ok) return;
   if (p.n_chunks == 1) {
