@@ -15,6 +15,9 @@ and state at a time).  This module only marshals numpy arrays into it:
   that page's "Selective SSM" section.
 * :func:`step` -- one token of the same recurrence, the recurrent (decoding)
   mode.
+* :func:`causal_conv1d_silu` -- the depthwise causal convolution and SiLU
+  that produce the scan's input u inside the Mamba block (the Guide
+  Complet's section 4 architecture figure and section 7 block).
 * :func:`scan_threaded` -- the same scan run on disjoint channel ranges from
   several Python threads (ctypes releases the GIL), used to time the oracle on
   all host cores.  It does not change the arithmetic.
@@ -68,6 +71,9 @@ def _load():
         lib.oracle_step_f64.restype = I
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_softplus.restype = ctypes.c_double
+        lib.oracle_causal_conv1d_silu_f64.argtypes = [P, P, P, I64, P, I64,
+                                                      I64, I64]
+        lib.oracle_causal_conv1d_silu_f64.restype = I
         _lib = lib
         return lib
 
@@ -89,6 +95,23 @@ def _ptr(a):
 
 def softplus(x: float) -> float:
     return _load().oracle_softplus(float(x))
+
+
+def causal_conv1d_silu(x, w, bias=None):
+    """u = silu(bias + depthwise causal conv1d(x, w)); x (batch, dim, L),
+    w (dim, K), bias (dim,) or None.  fp64 numpy result."""
+    x = _f64(x)
+    batch, dim, L = x.shape
+    w = _f64(w)
+    K = w.shape[1]
+    w = _f64(w, (dim, K))
+    bias = _f64(bias, (dim,))
+    u = np.empty((batch, dim, L), np.float64)
+    rc = _load().oracle_causal_conv1d_silu_f64(_ptr(x), _ptr(w), _ptr(bias),
+                                               K, _ptr(u), batch, dim, L)
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d_silu_f64 rejected its arguments")
+    return u
 
 
 def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,

@@ -130,3 +130,27 @@ int oracle_step_f64(double *state, const double *x, const double *delta,
     }
     return 0;
 }
+
+int oracle_causal_conv1d_silu_f64(const double *x, const double *w,
+                                  const double *bias, int64_t K, double *u,
+                                  int64_t batch, int64_t dim, int64_t seqlen)
+{
+    if (!x || !w || !u || K < 1 || batch < 0 || dim < 0 || seqlen < 0)
+        return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const double *xr = x + (b * dim + d) * seqlen;
+            double *ur = u + (b * dim + d) * seqlen;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                double acc = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    int64_t s = t - (K - 1) + k;   /* causal: past and present */
+                    if (s >= 0)
+                        acc += w[d * K + k] * xr[s];
+                }
+                ur[t] = oracle_silu(acc);
+            }
+        }
+    }
+    return 0;
+}

@@ -69,6 +69,19 @@ int oracle_step_f64(double *state, const double *x, const double *delta,
 /* softplus(x) = log(1 + e^x), evaluated without overflow or cancellation. */
 double oracle_softplus(double x);
 
+/* Depthwise causal 1-D convolution followed by SiLU, the step before the
+ * SSM in the Mamba block ("Mamba & State Space Models - Guide Complet",
+ * section 4 architecture figure: Linear -> Conv1D -> SiLU -> SSM; the
+ * convolution is depthwise (groups = channels) with padding d_conv - 1 and
+ * its output trimmed to the first L positions, section 7; d_conv = 4 on the
+ * inferownia.pl page, "Zrob to sam"):
+ *   u[b,d,t] = silu(bias[d] + sum_{k=0}^{K-1} w[d,k] * x[b,d,t-(K-1)+k])
+ * with x = 0 before t = 0.  x, u: (batch, dim, seqlen); w: (dim, K);
+ * bias: (dim) or NULL.  Returns 0, or -1 on a bad argument. */
+int oracle_causal_conv1d_silu_f64(const double *x, const double *w,
+                                  const double *bias, int64_t K, double *u,
+                                  int64_t batch, int64_t dim, int64_t seqlen);
+
 #ifdef __cplusplus
 }
 #endif

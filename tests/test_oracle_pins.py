@@ -408,3 +408,36 @@ def test_oracle_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.scan(np.zeros((1, 2, 3)), np.zeros((1, 2, 4)), np.zeros((2, 4)),
                     np.zeros((1, 4, 3)), np.zeros((1, 4, 3)))
+
+
+# ------------------------------------------ causal conv1d + SiLU prologue
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_causal_conv1d_silu_matches_numpy_convolve(K):
+    r = rng(20 + K)
+    batch, dim, L = 2, 5, 70
+    x = r.normal(size=(batch, dim, L))
+    w = r.normal(size=(dim, K))
+    bias = r.normal(size=dim)
+    u = oracle.causal_conv1d_silu(x, w, bias)
+    for b in range(batch):
+        for d in range(dim):
+            # PyTorch-style cross-correlation with K-1 zeros of left padding
+            # and the output trimmed to L is a full convolution with the
+            # reversed taps, truncated to the first L samples.
+            pre = np.convolve(x[b, d], w[d][::-1])[:L] + bias[d]
+            ref = pre * special.expit(pre)
+            assert np.allclose(u[b, d], ref, rtol=1e-13, atol=1e-14)
+
+
+def test_causal_conv1d_is_causal_and_zero_padded():
+    r = rng(31)
+    x = r.normal(size=(1, 3, 40))
+    w = r.normal(size=(3, 4))
+    u1 = oracle.causal_conv1d_silu(x, w, None)
+    x2 = x.copy()
+    x2[..., 25:] = r.normal(size=(1, 3, 15))      # change only the future
+    u2 = oracle.causal_conv1d_silu(x2, w, None)
+    assert np.array_equal(u1[..., :25], u2[..., :25])
+    # the first output sees only x[0] through the last tap
+    pre0 = w[:, 3] * x[0, :, 0]
+    assert np.allclose(u1[0, :, 0], pre0 * special.expit(pre0), rtol=1e-14)
