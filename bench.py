@@ -252,6 +252,36 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     del inp, y, hf, ws
     torch.cuda.empty_cache()
 
+    # the 2.8B layer with the fused conv prologue (x in place of u)
+    ccfg = syn.MAMBA_2P8B
+    log("conv-prologue workload %s" % ccfg.name)
+    cinp = syn.make_conv_inputs(ccfg, dev)
+    cy = torch.empty_like(cinp["x"])
+    chf = torch.empty(ccfg.batch, ccfg.dim, 16, device=dev)
+
+    def crun():
+        ssm.ssm_conv_scan_fwd(cinp["x"], cinp["conv_w"], cinp["delta"],
+                              cinp["A"], cinp["B"], cinp["C"], cinp["D"],
+                              cinp["z"], cinp["delta_bias"], True, None,
+                              conv_b=cinp["conv_b"], y=cy, h_final=chf,
+                              stream=stream)
+    crun()
+    torch.cuda.synchronize()
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        crun()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb = syn.algorithmic_bytes(ccfg) + ccfg.dim * 4 * 5  # + conv w, b
+    out[ccfg.name + "_conv_prologue"] = {
+        "ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+        "elements_per_s": round(ccfg.elements / (ms * 1e-3)),
+        "note": "x read in place of u; u = silu(conv1d(x)) formed in the kernel"}
+    del cinp, cy, chf
+    torch.cuda.empty_cache()
+
     dcfg = syn.DECODE
     log("decode workload %s" % dcfg.name)
     dinp = syn.make_decode_inputs(dcfg, dev)

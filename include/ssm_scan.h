@@ -82,7 +82,7 @@ int ssm_abi_version(void);
 
 /* Tokens per sequence chunk that ssm_scan_fwd will use for this shape.
  * requested_chunk = 0 lets the library choose; a positive value asks for
- * chunks of that many tokens (rounded up to the kernel's block of 256).
+ * chunks of that many tokens (rounded up to the kernel's block of 1024).
  * *chunk_len_out == seqlen means the sequence is not split.  When it is
  * split, chunks are scanned in parallel from a zero state, their end states
  * are chained in order (the affine maps compose: the associative operator of
@@ -131,6 +131,29 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A,
                  int64_t dstate, int64_t seqlen, int dtype,
                  int64_t requested_chunk, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/* Selective scan whose input u is produced inside the kernel from the
+ * pre-convolution activations x by the Mamba block's depthwise causal
+ * convolution and SiLU ("Mamba & State Space Models - Guide Complet",
+ * section 4 architecture figure: Conv1D -> SiLU -> SSM; section 7: a
+ * depthwise Conv1d with padding d_conv - 1 whose output is trimmed to the
+ * first L positions; d_conv = 4 on the inferownia.pl page):
+ *   u[b,d,t] = silu(conv_b[d] + sum_{k<d_conv} conv_w[d,k] * x[b,d,t-d_conv+1+k])
+ * with x = 0 before t = 0; then exactly ssm_scan_fwd with that u (the D
+ * skip uses u).  u never touches HBM.
+ *  x        required, activation dtype (batch, dim, seqlen)
+ *  conv_w   required fp32 (dim, d_conv); conv_b nullable fp32 (dim)
+ *  d_conv   1..4 (SSM_ERR_UNSUPPORTED above 4)
+ * All other arguments, conventions, the chunk plan and the workspace are
+ * those of ssm_scan_fwd. */
+int ssm_conv_scan_fwd(const void *x, const float *conv_w, const float *conv_b,
+                      int d_conv, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D,
+                      const void *z, const float *delta_bias, unsigned flags,
+                      const float *h0, void *y, float *h_final, int64_t batch,
+                      int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                      int64_t requested_chunk, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* One decoding step, in place on `state`.
  *  state      required fp32 (batch, dim, dstate): read, advanced by one token

@@ -11,6 +11,9 @@ Names follow the C ABI:
 * :func:`ssm_scan_fwd` -- whole-sequence selective scan (Mamba's S6 forward):
   dt = softplus(delta + bias), h_t = exp(dt*A) h_{t-1} + dt*B_t*u_t,
   y_t = (C_t . h_t + D*u_t) * silu(z_t).
+* :func:`ssm_conv_scan_fwd` -- the same scan whose input u = silu(causal
+  depthwise conv1d(x)) is formed inside the kernel (the Mamba block's
+  convolution before the SSM).
 * :func:`ssm_state_update` -- one decoding step on an in-place fp32 state.
 * :func:`ssm_scan_plan`, :func:`ssm_scan_workspace_size`,
   :func:`ssm_last_error`, :func:`ssm_abi_version`.
@@ -32,7 +35,8 @@ SSM_FLAG_DELTA_SOFTPLUS = 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
           3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
 EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
-           "ssm_scan_fwd", "ssm_state_update", "ssm_last_error")
+           "ssm_scan_fwd", "ssm_conv_scan_fwd", "ssm_state_update",
+           "ssm_last_error")
 
 _lib = None
 _lock = threading.Lock()
@@ -71,6 +75,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                      I64, I64, I64, I64, I, I64, P,
                                      ctypes.c_size_t, P]
         lib.ssm_scan_fwd.restype = I
+        lib.ssm_conv_scan_fwd.argtypes = [P, P, P, I, P, P, P, P, P, P, P, U,
+                                          P, P, P, I64, I64, I64, I64, I, I64,
+                                          P, ctypes.c_size_t, P]
+        lib.ssm_conv_scan_fwd.restype = I
         lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, U, P,
                                          I64, I64, I64, I, P]
         lib.ssm_state_update.restype = I
@@ -185,6 +193,56 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     flags = SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0
     _check(load_library().ssm_scan_fwd(
         pu, pd, pA, pB, pC, pD, pz, pbias, flags, ph0, py, ph,
+        batch, dim, N, L, code, chunk_len, pws, wsn,
+        _stream_handle(dev, stream)))
+    return y, h_final
+
+
+def ssm_conv_scan_fwd(x, conv_w, delta, A, B, C, D=None, z=None,
+                      delta_bias=None, delta_softplus=True, h0=None,
+                      conv_b=None, return_final_state=True, chunk_len=0,
+                      y=None, h_final=None, workspace=None, stream=None):
+    """Scan with the fused conv prologue: u = silu(conv_b + causal depthwise
+    conv1d(x, conv_w)) inside the kernel, then as :func:`ssm_scan_fwd`.
+    x: (batch, dim, L) activation dtype; conv_w: (dim, d_conv) fp32 with
+    d_conv <= 4; conv_b: (dim,) fp32 or None."""
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, dim, L)")
+    batch, dim, L = x.shape
+    N = A.shape[-1] if A.dim() == 2 else 0
+    dev = x.device
+    act = x.dtype
+    code = _dtype_code(x)
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be (dim, d_conv)")
+    d_conv = conv_w.shape[1]
+    px = _ptr(x, "x", act, (batch, dim, L), dev)
+    pw = _ptr(conv_w, "conv_w", torch.float32, (dim, d_conv), dev)
+    pcb = _ptr(conv_b, "conv_b", torch.float32, (dim,), dev)
+    pd = _ptr(delta, "delta", act, (batch, dim, L), dev)
+    pA = _ptr(A, "A", torch.float32, (dim, N), dev)
+    pB = _ptr(B, "B", act, (batch, N, L), dev)
+    pC = _ptr(C, "C", act, (batch, N, L), dev)
+    pD = _ptr(D, "D", torch.float32, (dim,), dev)
+    pz = _ptr(z, "z", act, (batch, dim, L), dev)
+    pbias = _ptr(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    ph0 = _ptr(h0, "h0", torch.float32, (batch, dim, N), dev)
+    if y is None:
+        y = torch.empty((batch, dim, L), dtype=act, device=dev)
+    py = _ptr(y, "y", act, (batch, dim, L), dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    if not return_final_state:
+        h_final = None
+    ph = _ptr(h_final, "h_final", torch.float32, (batch, dim, N), dev)
+    ws_bytes = ssm_scan_workspace_size(batch, dim, N, L, chunk_len)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    pws = workspace.data_ptr() if workspace is not None else None
+    wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    flags = SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    _check(load_library().ssm_conv_scan_fwd(
+        px, pw, pcb, d_conv, pd, pA, pB, pC, pD, pz, pbias, flags, ph0, py, ph,
         batch, dim, N, L, code, chunk_len, pws, wsn,
         _stream_handle(dev, stream)))
     return y, h_final

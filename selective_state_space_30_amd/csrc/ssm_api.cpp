@@ -139,16 +139,32 @@ int ssm_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
   return ok();
 }
 
-int ssm_scan_fwd(const void *u, const void *delta, const float *A,
-                 const void *B, const void *C, const float *D, const void *z,
-                 const float *delta_bias, unsigned flags, const float *h0,
-                 void *y, float *h_final, int64_t batch, int64_t dim,
-                 int64_t dstate, int64_t seqlen, int dtype,
-                 int64_t requested_chunk, void *workspace,
-                 size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by ssm_scan_fwd (u given) and ssm_conv_scan_fwd (x, conv_w given;
+// u = silu(conv1d(x)) is formed inside the kernel).
+int scan_impl(const void *u, const void *x, const float *conv_w,
+              const float *conv_b, int d_conv, const void *delta,
+              const float *A, const void *B, const void *C, const float *D,
+              const void *z, const float *delta_bias, unsigned flags,
+              const float *h0, void *y, float *h_final, int64_t batch,
+              int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+              int64_t requested_chunk, void *workspace, size_t workspace_bytes,
+              void *stream) {
+  if (x) {
+    if (!conv_w) return fail(SSM_ERR_INVALID_ARG, "conv_w is NULL");
+    if (d_conv < 1 || d_conv > ssm::kMaxConv)
+      return fail(d_conv < 1 ? SSM_ERR_INVALID_ARG : SSM_ERR_UNSUPPORTED,
+                  "d_conv=%d: supported 1..%d", d_conv, ssm::kMaxConv);
+    if (!aligned(conv_w, 4) || (conv_b && !aligned(conv_b, 4)))
+      return fail(SSM_ERR_INVALID_ARG, "conv weights not 4-byte aligned");
+    u = x;  // the checks below apply to x in u's place
+  }
   if (!u || !delta || !A || !B || !C || !y)
     return fail(SSM_ERR_INVALID_ARG,
-                "required pointer is NULL (u=%p delta=%p A=%p B=%p C=%p y=%p)", u,
+                "required pointer is NULL (u/x=%p delta=%p A=%p B=%p C=%p y=%p)", u,
                 delta, (const void *)A, B, C, y);
   if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
     return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
@@ -175,9 +191,11 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A,
   const int64_t bc = batch * dstate * seqlen * es;
   const int64_t sts = batch * dim * dstate * 4;
   const struct { const void *p; int64_t n; const char *name; } ins[] = {
-      {u, big, "u"}, {delta, big, "delta"}, {z, big, "z"}, {B, bc, "B"},
+      {u, big, x ? "x" : "u"}, {delta, big, "delta"}, {z, big, "z"}, {B, bc, "B"},
       {C, bc, "C"}, {A, dim * dstate * 4, "A"}, {D, dim * 4, "D"},
-      {delta_bias, dim * 4, "delta_bias"}, {h0, sts, "h0"}};
+      {delta_bias, dim * 4, "delta_bias"}, {h0, sts, "h0"},
+      {conv_w, x ? dim * d_conv * 4 : 0, "conv_w"},
+      {conv_b, x ? dim * 4 : 0, "conv_b"}};
   for (const auto &in : ins) {
     if (overlaps(y, big, in.p, in.n))
       return fail(SSM_ERR_INVALID_ARG, "y overlaps input %s", in.name);
@@ -219,7 +237,8 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A,
   for (const void *p : acts)
     if (p && !aligned(p, 16)) vec = false;
 
-  a.u = u; a.delta = delta; a.B = B; a.C = C; a.z = z;
+  a.u = x ? nullptr : u; a.delta = delta; a.B = B; a.C = C; a.z = z;
+  a.x = x; a.conv_w = conv_w; a.conv_b = conv_b; a.d_conv = x ? d_conv : 0;
   a.A = A; a.D = D; a.bias = delta_bias; a.h0 = h0;
   a.y = y; a.h_final = h_final;
   a.batch = batch; a.dim = dim; a.L = seqlen;
@@ -230,6 +249,39 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A,
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z,
+                 const float *delta_bias, unsigned flags, const float *h0,
+                 void *y, float *h_final, int64_t batch, int64_t dim,
+                 int64_t dstate, int64_t seqlen, int dtype,
+                 int64_t requested_chunk, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+  if (!u) return fail(SSM_ERR_INVALID_ARG, "u is NULL");
+  return scan_impl(u, nullptr, nullptr, nullptr, 0, delta, A, B, C, D, z,
+                   delta_bias, flags, h0, y, h_final, batch, dim, dstate,
+                   seqlen, dtype, requested_chunk, workspace, workspace_bytes,
+                   stream);
+}
+
+int ssm_conv_scan_fwd(const void *x, const float *conv_w, const float *conv_b,
+                      int d_conv, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D,
+                      const void *z, const float *delta_bias, unsigned flags,
+                      const float *h0, void *y, float *h_final, int64_t batch,
+                      int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                      int64_t requested_chunk, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!x) return fail(SSM_ERR_INVALID_ARG, "x is NULL");
+  return scan_impl(nullptr, x, conv_w, conv_b, d_conv, delta, A, B, C, D, z,
+                   delta_bias, flags, h0, y, h_final, batch, dim, dstate,
+                   seqlen, dtype, requested_chunk, workspace, workspace_bytes,
+                   stream);
 }
 
 int ssm_state_update(float *state, const void *x, const void *delta,

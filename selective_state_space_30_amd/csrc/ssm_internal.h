@@ -15,9 +15,13 @@ constexpr int kChannelsPerGroup = kWavesPerGroup;                  // 4
 constexpr int kTokensPerLane = 16;   // consecutive tokens owned by one lane
 constexpr int kBlockTokens = kWaveLanes * kTokensPerLane;         // 1024
 constexpr int kPhaseStates = 2;      // states per double-buffered B/C LDS tile
+constexpr int kMaxConv = 4;          // taps of the fused causal conv1d prologue
 
 struct ScanArgs {
-  const void *u, *delta, *B, *C, *z;  // activations (dtype)
+  const void *u, *delta, *B, *C, *z;  // activations (dtype); u null with conv
+  const void *x;                      // conv prologue: pre-conv input (dtype)
+  const float *conv_w, *conv_b;       // conv prologue: (dim, d_conv), (dim)
+  int d_conv;                         // conv prologue taps (1..4), 0 = none
   const float *A, *D, *bias, *h0;     // fp32 parameters / initial state
   void *y;                            // output (dtype)
   float *h_final;                     // fp32 (batch, dim, 16) or null

@@ -314,14 +314,15 @@ struct TileRun {
 // nothing is masked; otherwise positions from ct1 on are identity steps
 // (dt = 0, u = 0) and are not stored.  hc[n]: the channel's state carried in
 // (wave-uniform), replaced by the state after the block.
-template <typename T, bool kVec, bool kFull, bool kSoftplus>
+template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kConv>
 __device__ __forceinline__ void scan_block(
     const ScanArgs &p, int tid, int lane, int64_t t0, int64_t ct1,
     const T *__restrict__ Bb, const T *__restrict__ Cb,
     const T *__restrict__ urow, const T *__restrict__ drow,
     const T *__restrict__ zrow, T *__restrict__ yrow, bool ch_ok, float bias,
     float Dd, const float (&Ach)[kStates], float *sT, float (&hc)[kStates],
-    float &sdt_total) {
+    float &sdt_total, const float (&wc)[kMaxConv], float cb,
+    float (&xc)[kMaxConv - 1]) {
   constexpr int K = kTokensPerLane;
   constexpr int KP = K + 4;  // padded LDS stride of one lane's run
   const int64_t tend = kFull ? t0 + kBlockTokens : ct1;
@@ -343,6 +344,31 @@ __device__ __forceinline__ void scan_block(
   {
     float uu[K], dr[K];
     load_run<T, K, kVec, kFull>(urow, tl, tend, uu);
+    if constexpr (kConv) {
+      // urow holds the pre-conv input x: u = silu(cb + sum_k wc[k] *
+      // x[t-3+k]).  The three values before the lane's first token come
+      // from the left neighbour (lane 0: from the previous block / chunk).
+      float xm[kMaxConv - 1];
+#pragma unroll
+      for (int k = 0; k < kMaxConv - 1; ++k)
+        xm[k] = wave_shift_in(uu[K - (kMaxConv - 1) + k], xc[k]);
+#pragma unroll
+      for (int k = 0; k < kMaxConv - 1; ++k)
+        xc[k] = lane_broadcast(uu[K - (kMaxConv - 1) + k], kWaveLanes - 1);
+      float xs[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) xs[j] = uu[j];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        float acc = cb;
+#pragma unroll
+        for (int k = 0; k < kMaxConv; ++k) {
+          const int s = j - (kMaxConv - 1) + k;  // token of tap k
+          acc = fmaf(wc[k], s >= 0 ? xs[s] : xm[s + kMaxConv - 1], acc);
+        }
+        uu[j] = silu_f(acc);
+      }
+    }
     load_run<T, K, kVec, kFull>(drow, tl, tend, dr);
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -414,7 +440,7 @@ __device__ __forceinline__ void scan_block(
   sdt_total += sdt;
 }
 
-template <typename T, bool kVec, bool kSoftplus>
+template <typename T, bool kVec, bool kSoftplus, bool kConv>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_kernel(ScanArgs p) {
   constexpr int KP = kTokensPerLane + 4;
@@ -442,7 +468,7 @@ void scan_kernel(ScanArgs p) {
   for (int n = 0; n < kStates; ++n)
     hc[n] = (chunk == 0 && p.h0) ? p.h0[bd * kStates + n] : 0.0f;
 
-  const T *urow = static_cast<const T *>(p.u) + bd * p.L;
+  const T *urow = static_cast<const T *>(kConv ? p.x : p.u) + bd * p.L;
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
   T *yrow = static_cast<T *>(p.y) + bd * p.L;
@@ -450,16 +476,34 @@ void scan_kernel(ScanArgs p) {
   const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
   float sdt_total = 0.0f;
 
+  // Conv prologue (wave-uniform): taps aligned to the last kMaxConv tokens
+  // (fewer taps: leading zeros), bias, and the kMaxConv-1 inputs before the
+  // chunk (zero before t = 0).
+  float wc[kMaxConv], cb = 0.0f, xc[kMaxConv - 1];
+#pragma unroll
+  for (int k = 0; k < kMaxConv; ++k) {
+    const int i = k - (kMaxConv - p.d_conv);
+    wc[k] = (kConv && i >= 0) ? p.conv_w[d * p.d_conv + i] : 0.0f;
+  }
+  if (kConv && p.conv_b) cb = p.conv_b[d];
+#pragma unroll
+  for (int k = 0; k < kMaxConv - 1; ++k) {
+    const int64_t t = ct0 - (kMaxConv - 1) + k;
+    xc[k] = (kConv && t >= 0) ? to_f32<T>(urow[t]) : 0.0f;
+  }
+
   int64_t t0 = ct0;
 #pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens)
-    scan_block<T, kVec, true, kSoftplus>(p, tid, lane, t0, ct1, Bb, Cb, urow, drow, zrow,
-                              yrow, ch_ok, bias, Dd, Ach, sT, hc, sdt_total);
+    scan_block<T, kVec, true, kSoftplus, kConv>(p, tid, lane, t0, ct1, Bb, Cb, urow,
+                                               drow, zrow, yrow, ch_ok, bias, Dd, Ach,
+                                               sT, hc, sdt_total, wc, cb, xc);
   if (t0 < ct1)
     // the last, partial block: branch-free scalar loads (rare; keeps the
     // register budget of the full-block loop)
-    scan_block<T, false, false, kSoftplus>(p, tid, lane, t0, ct1, Bb, Cb, urow, drow, zrow,
-                               yrow, ch_ok, bias, Dd, Ach, sT, hc, sdt_total);
+    scan_block<T, false, false, kSoftplus, kConv>(p, tid, lane, t0, ct1, Bb, Cb, urow,
+                                                  drow, zrow, yrow, ch_ok, bias, Dd, Ach,
+                                                  sT, hc, sdt_total, wc, cb, xc);
 
   if (!ch_ok) return;
   if (p.n_chunks == 1) {
@@ -623,10 +667,17 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
                                         kChannelsPerGroup),
                   static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(a.n_chunks));
-  if (a.softplus)
-    hipLaunchKernelGGL((scan_kernel<T, kVec, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((scan_kernel<T, kVec, false>), grid, dim3(256), 0, s, a);
+  if (a.x) {
+    if (a.softplus)
+      hipLaunchKernelGGL((scan_kernel<T, kVec, true, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((scan_kernel<T, kVec, false, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.softplus)
+      hipLaunchKernelGGL((scan_kernel<T, kVec, true, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((scan_kernel<T, kVec, false, false>), grid, dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
   const int64_t nthreads = a.batch * a.dim * kStates;

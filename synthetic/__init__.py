@@ -152,6 +152,24 @@ def make_scan_inputs(cfg: ScanConfig, device="cpu", **over) -> dict:
     return out
 
 
+def make_conv_inputs(cfg: ScanConfig, device="cpu", d_conv: int = 4,
+                     with_bias: bool = True, **over) -> dict:
+    """Inputs of the scan with the fused conv prologue: the scan workload's
+    tensors with ``x`` (the pre-convolution activations, N(0,1), in place of
+    u), ``conv_w`` ~ U(-1/sqrt(d_conv), 1/sqrt(d_conv)) of shape
+    (dim, d_conv) and ``conv_b`` of the same distribution, both fp32 (the
+    default initialisation range of a depthwise Conv1d)."""
+    out = make_scan_inputs(cfg, device, **over)
+    if over:
+        cfg = replace(cfg, **over)
+    out["x"] = out.pop("u")
+    lim = 1.0 / math.sqrt(d_conv)
+    out["conv_w"] = _uniform((cfg.dim, d_conv), -lim, lim, device, cfg.seed, 9)
+    out["conv_b"] = (_uniform((cfg.dim,), -lim, lim, device, cfg.seed, 10)
+                     if with_bias else None)
+    return out
+
+
 def make_decode_inputs(cfg: DecodeConfig, device="cpu", with_h0=False,
                        **over) -> dict:
     """A ``steps``-token sequence for the decode workload, laid out like a

@@ -186,3 +186,40 @@ def test_valid_call_without_device_reports_hip_error(lib):
     st = _scan(lib)
     assert st == 4
     assert lib.ssm_last_error().decode()
+
+
+def _conv(lib, **kw):
+    a = dict(x=FAKE, w=FAKE + 0x08000000, cb=None, d_conv=4,
+             delta=FAKE + 0x10000000, A=FAKE + 0x20000000,
+             B=FAKE + 0x30000000, C=FAKE + 0x40000000, D=None, z=None,
+             bias=None, flags=1, h0=None, y=FAKE + 0x50000000, h_final=None,
+             batch=1, dim=16, dstate=16, seqlen=256, dtype=ssm.SSM_DTYPE_F32,
+             chunk=0, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.ssm_conv_scan_fwd(a["x"], a["w"], a["cb"], a["d_conv"],
+                                 a["delta"], a["A"], a["B"], a["C"], a["D"],
+                                 a["z"], a["bias"], a["flags"], a["h0"],
+                                 a["y"], a["h_final"], a["batch"], a["dim"],
+                                 a["dstate"], a["seqlen"], a["dtype"],
+                                 a["chunk"], a["ws"], a["ws_bytes"],
+                                 a["stream"])
+
+
+INVALID_CONV_CASES = [
+    ("null x", dict(x=None), 1),
+    ("null conv_w", dict(w=None), 1),
+    ("zero taps", dict(d_conv=0), 1),
+    ("five taps", dict(d_conv=5), 2),
+    ("misaligned conv_w", dict(w=FAKE + 0x08000002), 1),
+    ("y aliases x", dict(y=FAKE + 32), 1),
+    ("y overlaps conv_w", dict(y=FAKE + 0x08000000 - 16), 1),
+    ("dstate 32", dict(dstate=32), 2),
+    ("split without workspace", dict(chunk=1024, seqlen=4096), 3),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_CONV_CASES,
+                         ids=[c[0] for c in INVALID_CONV_CASES])
+def test_conv_scan_rejects_invalid_arguments(lib, name, kw, status):
+    assert _conv(lib, **kw) == status
+    assert lib.ssm_last_error().decode()
