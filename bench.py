@@ -282,6 +282,33 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     del cinp, cy, chf
     torch.cuda.empty_cache()
 
+    # the 2.8B layer with the exact zero-order-hold input term
+    log("ZOH input term on %s" % ccfg.name)
+    zinp = syn.make_scan_inputs(ccfg, dev)
+    zy = torch.empty_like(zinp["u"])
+    zhf = torch.empty(ccfg.batch, ccfg.dim, 16, device=dev)
+
+    def zrun():
+        ssm.ssm_scan_fwd(zinp["u"], zinp["delta"], zinp["A"], zinp["B"],
+                         zinp["C"], zinp["D"], zinp["z"], zinp["delta_bias"],
+                         True, None, y=zy, h_final=zhf, stream=stream,
+                         zoh_b=True)
+    zrun()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        zrun()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb = syn.algorithmic_bytes(ccfg)
+    out[ccfg.name + "_zoh"] = {
+        "ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+        "elements_per_s": round(ccfg.elements / (ms * 1e-3)),
+        "note": "exact zero-order-hold input term (flag)"}
+    del zinp, zy, zhf
+    torch.cuda.empty_cache()
+
     dcfg = syn.DECODE
     log("decode workload %s" % dcfg.name)
     dinp = syn.make_decode_inputs(dcfg, dev)

@@ -76,6 +76,11 @@ typedef enum {
 
 /* flags (bitwise OR) */
 #define SSM_FLAG_DELTA_SOFTPLUS 1u  /* dt = softplus(delta + bias); without it dt = delta + bias */
+/* Input term by exact zero-order hold instead of Euler: dB*u = (exp(dt*A) -
+ * 1)/A * B*u per state ("Mamba & State Space Models - Guide Complet",
+ * section 1 "Discretisation": B_bar = (exp(dt A) - I) A^-1 B), dt*B*u where
+ * A = 0.  Costs about twice the VALU work of the default Euler term. */
+#define SSM_FLAG_ZOH_B 2u
 
 /* Returns SSM_SCAN_ABI_VERSION. */
 int ssm_abi_version(void);
@@ -104,7 +109,7 @@ int ssm_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *  D                   nullable fp32 (dim): skip term D*u, added before the gate
  *  z                   nullable, activation dtype: gate y * silu(z)
  *  delta_bias          nullable fp32 (dim), added to delta before softplus
- *  flags               SSM_FLAG_DELTA_SOFTPLUS or 0
+ *  flags               SSM_FLAG_DELTA_SOFTPLUS and/or SSM_FLAG_ZOH_B
  *  h0                  nullable fp32 initial state (zero state if NULL)
  *  y                   required output, activation dtype; must not overlap
  *                      any input

@@ -32,6 +32,7 @@ LIB_PATH = os.path.join(_PKG, "libssmscan.so")
 SSM_DTYPE_F32 = 0
 SSM_DTYPE_BF16 = 1
 SSM_FLAG_DELTA_SOFTPLUS = 1
+SSM_FLAG_ZOH_B = 2
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
           3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
 EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
@@ -149,17 +150,23 @@ def ssm_scan_workspace_size(batch, dim, dstate, seqlen, requested_chunk=0) -> in
     return out.value
 
 
+def _flags(delta_softplus, zoh_b):
+    return ((SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0) |
+            (SSM_FLAG_ZOH_B if zoh_b else 0))
+
+
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                  delta_softplus=True, h0=None, return_final_state=True,
                  chunk_len=0, y=None, h_final=None, workspace=None,
-                 stream=None):
+                 stream=None, zoh_b=False):
     """Selective scan forward on device tensors.
 
     u, delta, z: (batch, dim, L); B, C: (batch, N, L) -- all one dtype
     (float32 or bfloat16).  A: (dim, N) fp32; D, delta_bias: (dim,) fp32;
     h0: (batch, dim, N) fp32 or None.  Returns ``(y, h_final)``
     (``h_final`` is None unless ``return_final_state``).  Outputs and the
-    workspace are allocated here with torch unless passed in.
+    workspace are allocated here with torch unless passed in.  ``zoh_b``
+    selects the exact zero-order-hold input term.
     """
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, L)")
@@ -190,7 +197,7 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     pws = workspace.data_ptr() if workspace is not None else None
     wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    flags = SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    flags = _flags(delta_softplus, zoh_b)
     _check(load_library().ssm_scan_fwd(
         pu, pd, pA, pB, pC, pD, pz, pbias, flags, ph0, py, ph,
         batch, dim, N, L, code, chunk_len, pws, wsn,
@@ -201,7 +208,8 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 def ssm_conv_scan_fwd(x, conv_w, delta, A, B, C, D=None, z=None,
                       delta_bias=None, delta_softplus=True, h0=None,
                       conv_b=None, return_final_state=True, chunk_len=0,
-                      y=None, h_final=None, workspace=None, stream=None):
+                      y=None, h_final=None, workspace=None, stream=None,
+                      zoh_b=False):
     """Scan with the fused conv prologue: u = silu(conv_b + causal depthwise
     conv1d(x, conv_w)) inside the kernel, then as :func:`ssm_scan_fwd`.
     x: (batch, dim, L) activation dtype; conv_w: (dim, d_conv) fp32 with
@@ -240,7 +248,7 @@ def ssm_conv_scan_fwd(x, conv_w, delta, A, B, C, D=None, z=None,
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     pws = workspace.data_ptr() if workspace is not None else None
     wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    flags = SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    flags = _flags(delta_softplus, zoh_b)
     _check(load_library().ssm_conv_scan_fwd(
         px, pw, pcb, d_conv, pd, pA, pB, pC, pD, pz, pbias, flags, ph0, py, ph,
         batch, dim, N, L, code, chunk_len, pws, wsn,
@@ -250,7 +258,7 @@ def ssm_conv_scan_fwd(x, conv_w, delta, A, B, C, D=None, z=None,
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
                      delta_bias=None, delta_softplus=True, y=None,
-                     stream=None):
+                     stream=None, zoh_b=False):
     """One decoding step: advances ``state`` (batch, dim, N) fp32 in place
     and returns y (batch, dim).  x, delta, z: (batch, dim); B, C:
     (batch, N), all one activation dtype."""
@@ -272,7 +280,7 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
     if y is None:
         y = torch.empty((batch, dim), dtype=act, device=dev)
     py = _ptr(y, "y", act, (batch, dim), dev)
-    flags = SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    flags = _flags(delta_softplus, zoh_b)
     _check(load_library().ssm_state_update(
         ps, px, pd, pA, pB, pC, pD, pz, pbias, flags, py, batch, dim, N,
         code, _stream_handle(dev, stream)))
@@ -281,7 +289,7 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
 
 def bind_state_update(state, x, delta, A, B, C, D=None, z=None,
                       delta_bias=None, delta_softplus=True, y=None,
-                      stream=None):
+                      stream=None, zoh_b=False):
     """Checks and marshals the arguments of one decoding step once and
     returns a zero-argument callable that enqueues exactly that step (the
     same C call as :func:`ssm_state_update`, without per-call Python
@@ -303,7 +311,7 @@ def bind_state_update(state, x, delta, A, B, C, D=None, z=None,
             _ptr(D, "D", torch.float32, (dim,), dev),
             _ptr(z, "z", act, (batch, dim), dev),
             _ptr(delta_bias, "delta_bias", torch.float32, (dim,), dev),
-            SSM_FLAG_DELTA_SOFTPLUS if delta_softplus else 0,
+            _flags(delta_softplus, zoh_b),
             _ptr(y, "y", act, (batch, dim), dev),
             batch, dim, N, code, _stream_handle(dev, stream))
     fn = load_library().ssm_state_update

@@ -54,6 +54,7 @@ constexpr int64_t kMaxGridYZ = 65535;
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kMinAutoChunk = 8192;
 constexpr int64_t kSimds = 1024;  // 256 CUs x 4 SIMDs
+constexpr unsigned kKnownFlags = SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_ZOH_B;
 
 int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
   if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0)
@@ -168,7 +169,7 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
                 delta, (const void *)A, B, C, y);
   if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
     return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (flags & ~static_cast<unsigned>(SSM_FLAG_DELTA_SOFTPLUS))
+  if (flags & ~kKnownFlags)
     return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   int st = check_sizes(batch, dim, dstate, seqlen);
   if (st != SSM_OK) return st;
@@ -245,6 +246,7 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
   a.chunk_len = chunk;
   a.n_chunks = static_cast<int>(n_chunks);
   a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+  a.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
   const int err = ssm::launch_scan(a, bf16, vec, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
@@ -293,7 +295,7 @@ int ssm_state_update(float *state, const void *x, const void *delta,
     return fail(SSM_ERR_INVALID_ARG, "required pointer is NULL");
   if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
     return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (flags & ~static_cast<unsigned>(SSM_FLAG_DELTA_SOFTPLUS))
+  if (flags & ~kKnownFlags)
     return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   int st = check_sizes(batch, dim, dstate, 1);
   if (st != SSM_OK) return st;
@@ -334,6 +336,7 @@ int ssm_state_update(float *state, const void *x, const void *delta,
   a.A = A; a.D = D; a.bias = delta_bias; a.y = y;
   a.batch = batch; a.dim = dim;
   a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+  a.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
   const int err = ssm::launch_step(a, bf16, vec, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));

@@ -32,6 +32,7 @@ struct ScanArgs {
   int64_t chunk_len;                  // tokens per chunk (== L when not split)
   int n_chunks;
   int softplus;                       // 1: dt = softplus(delta + bias)
+  int zoh;                            // 1: exact ZOH input term
 };
 
 struct StepArgs {
@@ -41,6 +42,7 @@ struct StepArgs {
   void *y;
   int64_t batch, dim;
   int softplus;
+  int zoh;
 };
 
 // Workspace layout of the split (chunked) scan, in floats, each part

@@ -263,6 +263,24 @@ __device__ __forceinline__ float lane_broadcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Exact zero-order-hold input coefficient of one state, (exp(dt*A) - 1) / A
+// ("Mamba & State Space Models - Guide Complet", section 1: B_bar =
+// (exp(dt A) - I) A^-1 B; for a diagonal A, per state).  `arg` = dt*A*log2(e)
+// (the exp2 argument), `a` = exp2(arg), `dt`, `inv_a` = 1/A.  Where |arg| <
+// 2^-5 the difference a - 1 would lose up to ~2^-18 relative accuracy, so
+// the series dt * (1 + x/2 + x^2/6), x = dt*A, is used instead (truncation
+// below 4e-7 relative there).  A = 0 takes the series (arg = 0) and gives
+// dt, the limit; the infinite inv_a of the other operand is not selected.
+__device__ __forceinline__ float zoh_coeff(float arg, float a, float dt,
+                                           float inv_a) {
+  constexpr float c1 = 0.34657359027997264f;   // ln2 / 2
+  constexpr float c2 = 0.080075075008187500f;  // ln2^2 / 6
+  const float q = fmaf(arg, fmaf(arg, c2, c1), 1.0f);
+  const float series = dt * q;
+  const float direct = (a - 1.0f) * inv_a;
+  return fabsf(arg) < 0x1p-5f ? series : direct;
+}
+
 // One thread's share of a B or C tile: K consecutive tokens of one state.
 // bf16 runs of full blocks stay packed (K/2 words) until they are written to
 // LDS as fp32; otherwise the run is held as fp32.
@@ -314,7 +332,8 @@ struct TileRun {
 // nothing is masked; otherwise positions from ct1 on are identity steps
 // (dt = 0, u = 0) and are not stored.  hc[n]: the channel's state carried in
 // (wave-uniform), replaced by the state after the block.
-template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kConv>
+template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kConv,
+          bool kZoh>
 __device__ __forceinline__ void scan_block(
     const ScanArgs &p, int tid, int lane, int64_t t0, int64_t ct1,
     const T *__restrict__ Bb, const T *__restrict__ Cb,
@@ -376,7 +395,7 @@ __device__ __forceinline__ void scan_block(
       float v = kSoftplus ? softplus_f(x) : x;
       if (!kFull) v = (tl + j < tend) ? v : 0.0f;  // identity step
       dtl[j] = v * kLog2e;
-      du[j] = v * uu[j];
+      du[j] = kZoh ? uu[j] : v * uu[j];  // ZOH: the coefficient carries dt
       y[j] = Dd * uu[j];
       sdt += v;
     }
@@ -402,10 +421,22 @@ __device__ __forceinline__ void scan_block(
       const float *pb = &tile[((s2 * 2 + 0) * kWaveLanes + lane) * KP];
       const float *pc = &tile[((s2 * 2 + 1) * kWaveLanes + lane) * KP];
       float a[K], bb[K];
+      if constexpr (kZoh) {
+        // A = 0 needs no branch: its argument is 0, the series is selected
+        // and gives dt (the 1/A = inf of the other operand is not used).
+        const float inv_a = 1.0f / An;
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        a[j] = fast_exp2(dtl[j] * An);
-        bb[j] = du[j] * pb[j];
+        for (int j = 0; j < K; ++j) {
+          const float arg = dtl[j] * An;
+          a[j] = fast_exp2(arg);
+          bb[j] = zoh_coeff(arg, a[j], dtl[j] * kLn2, inv_a) * (du[j] * pb[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          a[j] = fast_exp2(dtl[j] * An);
+          bb[j] = du[j] * pb[j];
+        }
       }
       // Fold the lane's tokens into one affine map h -> P*h + H.
       float H = bb[0];
@@ -440,7 +471,7 @@ __device__ __forceinline__ void scan_block(
   sdt_total += sdt;
 }
 
-template <typename T, bool kVec, bool kSoftplus, bool kConv>
+template <typename T, bool kVec, bool kSoftplus, bool kConv, bool kZoh>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_kernel(ScanArgs p) {
   constexpr int KP = kTokensPerLane + 4;
@@ -495,13 +526,13 @@ void scan_kernel(ScanArgs p) {
   int64_t t0 = ct0;
 #pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens)
-    scan_block<T, kVec, true, kSoftplus, kConv>(p, tid, lane, t0, ct1, Bb, Cb, urow,
+    scan_block<T, kVec, true, kSoftplus, kConv, kZoh>(p, tid, lane, t0, ct1, Bb, Cb, urow,
                                                drow, zrow, yrow, ch_ok, bias, Dd, Ach,
                                                sT, hc, sdt_total, wc, cb, xc);
   if (t0 < ct1)
     // the last, partial block: branch-free scalar loads (rare; keeps the
     // register budget of the full-block loop)
-    scan_block<T, false, false, kSoftplus, kConv>(p, tid, lane, t0, ct1, Bb, Cb, urow,
+    scan_block<T, false, false, kSoftplus, kConv, kZoh>(p, tid, lane, t0, ct1, Bb, Cb, urow,
                                                   drow, zrow, yrow, ch_ok, bias, Dd, Ach,
                                                   sT, hc, sdt_total, wc, cb, xc);
 
@@ -642,7 +673,12 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs p) {
   float part = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    h[i] = fmaf(fast_exp2(dt * a4[i] * kLog2e), h[i], dx * b4[i]);
+    const float arg = dt * a4[i] * kLog2e;
+    const float e = fast_exp2(arg);
+    float inp = dx * b4[i];
+    if (p.zoh)  // exact ZOH: coefficient (e - 1)/A in place of dt
+      inp = zoh_coeff(arg, e, dt, 1.0f / a4[i]) * (x * b4[i]);
+    h[i] = fmaf(e, h[i], inp);
     part = fmaf(c4[i], h[i], part);
   }
   part += dpp<kQuadXor1>(part, part);
@@ -667,17 +703,15 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
                                         kChannelsPerGroup),
                   static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(a.n_chunks));
-  if (a.x) {
-    if (a.softplus)
-      hipLaunchKernelGGL((scan_kernel<T, kVec, true, true>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((scan_kernel<T, kVec, false, true>), grid, dim3(256), 0, s, a);
-  } else {
-    if (a.softplus)
-      hipLaunchKernelGGL((scan_kernel<T, kVec, true, false>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((scan_kernel<T, kVec, false, false>), grid, dim3(256), 0, s, a);
-  }
+  // (conv prologue, softplus, ZOH) -> kernel instance
+  using KernelFn = void (*)(ScanArgs);
+  static constexpr KernelFn kernels[8] = {
+      scan_kernel<T, kVec, false, false, false>, scan_kernel<T, kVec, true, false, false>,
+      scan_kernel<T, kVec, false, true, false>,  scan_kernel<T, kVec, true, true, false>,
+      scan_kernel<T, kVec, false, false, true>,  scan_kernel<T, kVec, true, false, true>,
+      scan_kernel<T, kVec, false, true, true>,   scan_kernel<T, kVec, true, true, true>};
+  const int which = (a.softplus ? 1 : 0) | (a.x ? 2 : 0) | (a.zoh ? 4 : 0);
+  hipLaunchKernelGGL(kernels[which], grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
   const int64_t nthreads = a.batch * a.dim * kStates;

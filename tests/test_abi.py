@@ -84,6 +84,7 @@ INVALID_SCAN_CASES = [
     ("dstate 64 unsupported", dict(dstate=64), 2),
     ("bad dtype", dict(dtype=7), 1),
     ("unknown flag", dict(flags=0x10), 1),
+    ("unknown flag bit 2", dict(flags=0x4), 1),
     ("negative chunk", dict(chunk=-1), 1),
     ("misaligned fp32 activation", dict(u=FAKE + 2), 1),
     ("misaligned bf16 activation", dict(u=FAKE + 1, dtype=1), 1),

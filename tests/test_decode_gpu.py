@@ -104,3 +104,27 @@ def test_decode_without_optional_inputs():
         torch.cuda.synchronize()
         check(y, y_ref, 1e-4, "y step %d" % t)
     check(state, ref_state, 1e-4, "state")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_zoh_matches_oracle_every_step(dtype):
+    cfg = syn.DecodeConfig("zoh", 2, 21, 16, 12, dtype=dtype, seed=33)
+    inp = syn.make_decode_inputs(cfg, "cpu", with_h0=True)
+    inp["A"][:, 5] = 0.0
+    dinp = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v)
+            for k, v in inp.items()}
+    state = dinp["h0"].clone()
+    ref_state = inp["h0"].double().numpy().copy()
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for t in range(cfg.steps):
+        s = syn.step_slice(dinp, t)
+        y = ssm.ssm_state_update(state, s["x"], s["delta"], dinp["A"], s["B"],
+                                 s["C"], dinp["D"], s["z"],
+                                 dinp["delta_bias"], True, zoh_b=True)
+        sh = syn.step_slice(inp, t)
+        y_ref = oracle.step(ref_state, sh["x"], sh["delta"], inp["A"],
+                            sh["B"], sh["C"], inp["D"], sh["z"],
+                            inp["delta_bias"], True, True)
+        torch.cuda.synchronize()
+        check(y, y_ref, tol, "y step %d" % t)
+        check(state, ref_state, tol, "state step %d" % t)
