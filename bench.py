@@ -359,7 +359,8 @@ def cpu_baseline(inp, cfg, nbytes, log):
             "elements_per_s": round(cfg.elements / sec)}
 
 
-SCAN_KERNEL = "scan_kernel<unsigned short, true, true>"
+# bf16 activations, vector loads, softplus on, no conv prologue, Euler input
+SCAN_KERNEL = "scan_kernel<unsigned short, true, true, false, false>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30  # each calibration copy reads and writes 1 GiB
 
@@ -417,6 +418,10 @@ def summarize_profiles(d):
         return {k: statistics.median(v) for k, v in vals.items()}
     fetch = per_dispatch("fetch", "FETCH_SIZE")
     write = per_dispatch("write", "WRITE_SIZE")
+    for k in (SCAN_KERNEL, COPY_KERNEL):
+        if k not in fetch or k not in write:
+            raise SystemExit("summarize: no counters for %r; kernels seen: %s"
+                             % (k, sorted(set(fetch) | set(write))))
     fetch_scale = COPY_BYTES / 1024 / fetch[COPY_KERNEL]
     write_scale = COPY_BYTES / 1024 / write[COPY_KERNEL]
     fb = fetch[SCAN_KERNEL] * fetch_scale * 1024
