@@ -49,10 +49,6 @@ constexpr int kRowShr1 = 0x111;
 constexpr int kRowShr2 = 0x112;
 constexpr int kRowShr4 = 0x114;
 constexpr int kRowShr8 = 0x118;
-constexpr int kRowRor1 = 0x121;
-constexpr int kRowRor2 = 0x122;
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;
 constexpr int kRowBcast15 = 0x142;
 constexpr int kRowBcast31 = 0x143;
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
@@ -132,13 +128,34 @@ __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
   return static_cast<uint16_t>(f32_to_bf16_bits(v));
 }
 
-// Loads K consecutive activations row[t .. t+K) as fp32; positions >= tend
-// read as 0.  With kVec the run is fetched with 16-byte loads when it is
-// wholly in range (the caller guarantees 16-byte alignment of row + t).
-template <typename T, int K, bool kVec, bool kInRange = false>
-__device__ __forceinline__ void load_run(const T *__restrict__ row, int64_t t,
-                                         int64_t tend, float (&v)[K]) {
-  if (kVec && (kInRange || t + K <= tend)) {
+// Buffer resource (V#) word 3 for gfx9-family untyped buffer access: 32-bit
+// data format, no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Wave-uniform byte view of row[t0, tend) for buffer loads and stores.  The
+// hardware range check makes a load past the end return 0 and drops a store
+// past it, so the last, partial block of a chunk needs no per-element
+// bounds arithmetic.  `row + t0` must be the same in every lane.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_view(const T *row,
+                                                           int64_t t0,
+                                                           int64_t tend) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(row + t0), 0,
+      static_cast<int>((tend - t0) * static_cast<int64_t>(sizeof(T))),
+      kBufferWord3);
+}
+
+// Loads K consecutive activations row[t .. t+K) as fp32.  kInRange: the run
+// lies wholly inside the data, fetched with 16-byte loads under kVec (the
+// caller guarantees 16-byte alignment of row + t), else element by element.
+// Otherwise the run belongs to the partial block [t0, tend) (t0 wave-uniform)
+// and is read through its buffer view: positions >= tend read as 0.
+template <typename T, int K, bool kVec, bool kInRange>
+__device__ __forceinline__ void load_run(const T *__restrict__ row, int64_t t0,
+                                         int64_t t, int64_t tend,
+                                         float (&v)[K]) {
+  if constexpr (kInRange && kVec) {
     if constexpr (sizeof(T) == 2) {
       const uint4 *p = reinterpret_cast<const uint4 *>(row + t);
 #pragma unroll
@@ -164,23 +181,31 @@ __device__ __forceinline__ void load_run(const T *__restrict__ row, int64_t t,
         v[4 * q + 3] = w.w;
       }
     }
+  } else if constexpr (kInRange) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = to_f32<T>(row[t + j]);
   } else {
-    // Branch-free: out-of-range positions read a valid element (the last
-    // one in range) and are then replaced by 0.
+    const __amdgpu_buffer_rsrc_t r = row_view(row, t0, tend);
+    const int off = static_cast<int>(t - t0) * static_cast<int>(sizeof(T));
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const bool in = kInRange || t + j < tend;
-      const float x = to_f32<T>(row[in ? t + j : tend - 1]);
-      v[j] = in ? x : 0.0f;
+      if constexpr (sizeof(T) == 2)
+        v[j] = __uint_as_float(static_cast<uint32_t>(
+                                   __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * j, 0, 0))
+                               << 16);
+      else
+        v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * j, 0, 0));
     }
   }
 }
 
-// Stores the in-range part (positions < tend) of a K-token run.
-template <typename T, int K, bool kVec, bool kInRange = false>
-__device__ __forceinline__ void store_run(T *__restrict__ row, int64_t t,
-                                          int64_t tend, const float (&v)[K]) {
-  if (kVec && (kInRange || t + K <= tend)) {
+// Stores a K-token run; the counterpart of load_run (positions >= tend of a
+// partial block are dropped).
+template <typename T, int K, bool kVec, bool kInRange>
+__device__ __forceinline__ void store_run(T *__restrict__ row, int64_t t0,
+                                          int64_t t, int64_t tend,
+                                          const float (&v)[K]) {
+  if constexpr (kInRange && kVec) {
     if constexpr (sizeof(T) == 2) {
       uint4 *p = reinterpret_cast<uint4 *>(row + t);
 #pragma unroll
@@ -198,10 +223,20 @@ __device__ __forceinline__ void store_run(T *__restrict__ row, int64_t t,
       for (int q = 0; q < K / 4; ++q)
         p[q] = make_float4(v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     }
-  } else {
+  } else if constexpr (kInRange) {
 #pragma unroll
-    for (int j = 0; j < K; ++j)
-      if (t + j < tend) row[t + j] = from_f32<T>(v[j]);
+    for (int j = 0; j < K; ++j) row[t + j] = from_f32<T>(v[j]);
+  } else {
+    const __amdgpu_buffer_rsrc_t r = row_view(static_cast<const T *>(row), t0, tend);
+    const int off = static_cast<int>(t - t0) * static_cast<int>(sizeof(T));
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if constexpr (sizeof(T) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(
+            static_cast<unsigned short>(f32_to_bf16_bits(v[j])), r, off + 2 * j, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), r, off + 4 * j, 0, 0);
+    }
   }
 }
 
@@ -290,8 +325,8 @@ struct TileRun {
   static constexpr int kWords = kPacked ? K / 2 : K;
   uint32_t w[kWords];
 
-  __device__ __forceinline__ void load(const T *__restrict__ row, int64_t t,
-                                       int64_t tend) {
+  __device__ __forceinline__ void load(const T *__restrict__ row, int64_t t0,
+                                       int64_t t, int64_t tend) {
     if constexpr (kPacked) {
       const uint4 *q = reinterpret_cast<const uint4 *>(row + t);
 #pragma unroll
@@ -304,7 +339,7 @@ struct TileRun {
       }
     } else {
       float v[K];
-      load_run<T, K, kVec, kInRange>(row, t, tend, v);
+      load_run<T, K, kVec, kInRange>(row, t0, t, tend, v);
 #pragma unroll
       for (int j = 0; j < K; ++j) w[j] = __float_as_uint(v[j]);
     }
@@ -315,12 +350,9 @@ struct TileRun {
     else
       return __uint_as_float(w[j]);
   }
-  // Writes the run as fp32 into tile[state st][matrix mat][run q].
-  __device__ __forceinline__ void store(float *tile, int st, int mat,
-                                        int q) const {
-    constexpr int KP = K + 4;
-    float4 *dst = reinterpret_cast<float4 *>(
-        &tile[((st * 2 + mat) * kWaveLanes + q) * KP]);
+  // Writes the run as fp32 at tile + off (16-byte aligned).
+  __device__ __forceinline__ void store(float *tile, int off) const {
+    float4 *dst = reinterpret_cast<float4 *>(tile + off);
 #pragma unroll
     for (int j = 0; j < K / 4; ++j)
       dst[j] = make_float4(at(4 * j), at(4 * j + 1), at(4 * j + 2), at(4 * j + 3));
@@ -335,7 +367,7 @@ struct TileRun {
 template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kConv,
           bool kZoh>
 __device__ __forceinline__ void scan_block(
-    const ScanArgs &p, int tid, int lane, int64_t t0, int64_t ct1,
+    const ScanArgs &p, int wave, int lane, int64_t t0, int64_t ct1,
     const T *__restrict__ Bb, const T *__restrict__ Cb,
     const T *__restrict__ urow, const T *__restrict__ drow,
     const T *__restrict__ zrow, T *__restrict__ yrow, bool ch_ok, float bias,
@@ -349,12 +381,16 @@ __device__ __forceinline__ void scan_block(
   constexpr int kPhases = kStates / 2;
   constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
 
-  // Staging role of this thread: state (2*ph + st), matrix B or C, run q.
-  const int st = tid >> 7, mat = (tid >> 6) & 1, q = tid & 63;
+  // Staging role of this wave: state (2*ph + st) of matrix B or C (both
+  // wave-uniform, so the row is a valid buffer base in the partial block);
+  // this lane: run `lane` of that row.
+  static_assert(kWavesPerGroup == 2 * kPhaseStates, "one staging row per wave");
+  const int st = wave >> 1, mat = wave & 1;
   const T *src = mat ? Cb : Bb;
-  const int64_t tq = t0 + static_cast<int64_t>(q) * K;
+  const int64_t tq = tl;
+  const int toff = ((st * 2 + mat) * kWaveLanes + lane) * KP;
   TileRun<T, K, kVec, kFull> run;
-  run.load(src + st * p.L, tq, tend);
+  run.load(src + st * p.L, t0, tq, tend);
 
   // This lane's tokens: the step dt (kept as dt*log2(e) for exp2), dt*u
   // and the D skip.
@@ -362,7 +398,7 @@ __device__ __forceinline__ void scan_block(
   float sdt = 0.0f;
   {
     float uu[K], dr[K];
-    load_run<T, K, kVec, kFull>(urow, tl, tend, uu);
+    load_run<T, K, kVec, kFull>(urow, t0, tl, tend, uu);
     if constexpr (kConv) {
       // urow holds the pre-conv input x: u = silu(cb + sum_k wc[k] *
       // x[t-3+k]).  The three values before the lane's first token come
@@ -388,7 +424,7 @@ __device__ __forceinline__ void scan_block(
         uu[j] = silu_f(acc);
       }
     }
-    load_run<T, K, kVec, kFull>(drow, tl, tend, dr);
+    load_run<T, K, kVec, kFull>(drow, t0, tl, tend, dr);
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const float x = dr[j] + bias;
@@ -401,7 +437,7 @@ __device__ __forceinline__ void scan_block(
     }
   }
   // Phase 0's tile: its buffer was last read two phases ago, by every wave.
-  run.store(sT, st, mat, q);
+  run.store(sT, toff);
   const float sdtl = sdt * kLog2e;
 
   // B and C are staged two states at a time in a double-buffered LDS tile
@@ -410,7 +446,7 @@ __device__ __forceinline__ void scan_block(
 #pragma unroll
   for (int ph = 0; ph < kPhases; ++ph) {
     if (ph + 1 < kPhases)
-      run.load(src + (2 * (ph + 1) + st) * p.L, tq, tend);
+      run.load(src + (2 * (ph + 1) + st) * p.L, t0, tq, tend);
     __syncthreads();  // phase ph's tile is complete and visible
     const float *tile = sT + (ph & 1) * kTileFloats;
 #pragma unroll
@@ -458,24 +494,34 @@ __device__ __forceinline__ void scan_block(
     }
     // Every wave has passed this phase's barrier, so the other buffer (read
     // in phase ph-1) is free: fill it with phase ph+1.
-    if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, st, mat, q);
+    if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
   }
 
   if (zrow) {
     float zz[K];
-    load_run<T, K, kVec, kFull>(zrow, tl, tend, zz);
+    load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
 #pragma unroll
     for (int j = 0; j < K; ++j) y[j] *= silu_f(zz[j]);
   }
-  if (ch_ok) store_run<T, K, kVec, kFull>(yrow, tl, tend, y);
+  if (ch_ok) store_run<T, K, kVec, kFull>(yrow, t0, tl, tend, y);
   sdt_total += sdt;
 }
 
+// Waves per SIMD the register budget is sized for: 4 (128 VGPRs; 4
+// workgroups x 40 KB fill a CU's 160 KB of LDS) for aligned bf16 rows with
+// the Euler input term; 3 (168 VGPRs) otherwise, where the longer ZOH state
+// loop, the wider fp32 loads or the element-wise loads of unaligned rows
+// would spill or stall at 128 (measured: fp32 and unaligned bf16 run faster
+// at 3).
+template <typename T, bool kVec, bool kZoh>
+constexpr int kOccupancy = (sizeof(T) == 2 && kVec && !kZoh) ? 4 : 3;
+
 template <typename T, bool kVec, bool kSoftplus, bool kConv, bool kZoh>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kWaveLanes * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(kOccupancy<T, kVec, kZoh>)))
 void scan_kernel(ScanArgs p) {
   constexpr int KP = kTokensPerLane + 4;
-  __shared__ float sT[2 * 2 * 2 * kWaveLanes * KP];  // 40 KB
+  __shared__ float sT[2 * 2 * 2 * kWaveLanes * KP];  // 2 buffers x 2 states x B, C
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -526,13 +572,13 @@ void scan_kernel(ScanArgs p) {
   int64_t t0 = ct0;
 #pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens)
-    scan_block<T, kVec, true, kSoftplus, kConv, kZoh>(p, tid, lane, t0, ct1, Bb, Cb, urow,
+    scan_block<T, kVec, true, kSoftplus, kConv, kZoh>(p, wave, lane, t0, ct1, Bb, Cb, urow,
                                                drow, zrow, yrow, ch_ok, bias, Dd, Ach,
                                                sT, hc, sdt_total, wc, cb, xc);
   if (t0 < ct1)
     // the last, partial block: branch-free scalar loads (rare; keeps the
     // register budget of the full-block loop)
-    scan_block<T, false, false, kSoftplus, kConv, kZoh>(p, tid, lane, t0, ct1, Bb, Cb, urow,
+    scan_block<T, false, false, kSoftplus, kConv, kZoh>(p, wave, lane, t0, ct1, Bb, Cb, urow,
                                                   drow, zrow, yrow, ch_ok, bias, Dd, Ach,
                                                   sT, hc, sdt_total, wc, cb, xc);
 
@@ -711,7 +757,7 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
       scan_kernel<T, kVec, false, false, true>,  scan_kernel<T, kVec, true, false, true>,
       scan_kernel<T, kVec, false, true, true>,   scan_kernel<T, kVec, true, true, true>};
   const int which = (a.softplus ? 1 : 0) | (a.x ? 2 : 0) | (a.zoh ? 4 : 0);
-  hipLaunchKernelGGL(kernels[which], grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(kernels[which], grid, dim3(kWaveLanes * kWavesPerGroup), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
   const int64_t nthreads = a.batch * a.dim * kStates;
