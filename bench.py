@@ -21,7 +21,7 @@ of the profiling commands below into the summaries under profiles/).
 
 Profiling commands (run from /tmp with TMPDIR=/tmp; DIR = an output folder):
   rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o bench \
-      -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline
+      -- python3 bench.py --no-cpu-baseline
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o fetch \
       -- python3 bench.py --steps 3 --warmup 1 --no-extra --no-cpu-baseline
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write \
@@ -76,8 +76,8 @@ def measured_traffic(n_launch_bytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only-scan", action="store_true")
@@ -381,7 +381,7 @@ def summarize_profiles(d):
     import csv
     import statistics
     cmd_trace = ("rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace "
-                 "-o bench -- python3 bench.py --steps 20 --warmup 5 "
+                 "-o bench -- python3 bench.py "
                  "--no-cpu-baseline")
     cmd_pmc = ("rocprofv3 --pmc {c} --output-format csv -d DIR/{d} -o {d} -- "
                "python3 bench.py --steps 3 --warmup 1 --no-extra "
@@ -458,7 +458,35 @@ def summarize_profiles(d):
             "kernel source sha256[:16] %s" % out["kernel_source_sha256_16"]]
     with open(os.path.join(prof, "scan_kernel_mamba2p8b_traffic.txt"), "w") as f:
         f.write("\n".join(txt) + "\n")
-    print("\n".join(lines + txt))
+
+    # SQ counters (VALU issue, transcendentals, LDS), if that pass was run
+    sq_counters = ["SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
+                   "SQ_INSTS_VALU_TRANS_F32", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY",
+                   "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT"]
+    sq = {c: per_dispatch("sq", c).get(SCAN_KERNEL) for c in sq_counters}
+    sq_txt = []
+    if all(v is not None for v in sq.values()):
+        upd = syn.MAMBA_2P8B.elements * syn.MAMBA_2P8B.dstate
+        slots = sq["SQ_ACTIVE_INST_VALU"]
+        sq_txt = [
+            "# SQ counters of the scan kernel, Mamba-2.8B-shaped workload",
+            "# kernel: " + SCAN_KERNEL,
+            "# command (from /tmp, TMPDIR=/tmp): " + cmd_pmc.format(
+                c=" ".join(sq_counters), d="sq"),
+            "# median per dispatch over the timed calls"]
+        sq_txt += ["%-24s %14.0f" % (c, sq[c]) for c in sq_counters]
+        sq_txt += [
+            "VALU instructions per state-update: %.2f (x64 lanes / %d)" % (
+                sq["SQ_INSTS_VALU"] * 64 / upd, upd),
+            "VALU issue slots per state-update: %.2f" % (slots * 64 / upd),
+            "transcendentals per state-update: %.2f" % (
+                sq["SQ_INSTS_VALU_TRANS_F32"] * 64 / upd),
+            "VALU busy time at 2.4 GHz, 4 cycles per wave64 slot, 1024 SIMDs: "
+            "%.1f us" % (slots * 4 / (1024 * 2.4e9) * 1e6)]
+        with open(os.path.join(prof, "scan_kernel_mamba2p8b_sq_counters.txt"),
+                  "w") as f:
+            f.write("\n".join(sq_txt) + "\n")
+    print("\n".join(lines + txt + sq_txt))
 
 
 if __name__ == "__main__":
