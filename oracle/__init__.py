@@ -18,6 +18,8 @@ and state at a time).  This module only marshals numpy arrays into it:
 * :func:`causal_conv1d_silu` -- the depthwise causal convolution and SiLU
   that produce the scan's input u inside the Mamba block (the Guide
   Complet's section 4 architecture figure and section 7 block).
+* :func:`scan_bwd` -- gradients of :func:`scan` (Euler input term) by the
+  chain rule through the recurrence, in reverse token order.
 * :func:`scan_threaded` -- the same scan run on disjoint channel ranges from
   several Python threads (ctypes releases the GIL), used to time the oracle on
   all host cores.  It does not change the arithmetic.
@@ -74,6 +76,8 @@ def _load():
         lib.oracle_causal_conv1d_silu_f64.argtypes = [P, P, P, I64, P, I64,
                                                       I64, I64]
         lib.oracle_causal_conv1d_silu_f64.restype = I
+        lib.oracle_scan_bwd_f64.argtypes = [P] * 8 + [I] + [P] * 12 + [I64] * 4
+        lib.oracle_scan_bwd_f64.restype = I
         _lib = lib
         return lib
 
@@ -144,6 +148,46 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise ValueError("oracle_scan_f64 rejected its arguments")
     return y, hf
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+             delta_softplus=True, h0=None, dy=None, dh_final=None):
+    """Gradients of ``scan`` (Euler input term) for a loss whose gradient is
+    ``dy`` with respect to y and ``dh_final`` (or 0) with respect to the
+    final state.  Returns a dict of fp64 arrays: du, ddelta, dA, dB, dC and,
+    where the matching input is given, dD, ddelta_bias, dz; dh0 always."""
+    u = _f64(u)
+    batch, dim, L = u.shape
+    A = _f64(A)
+    N = A.shape[1]
+    delta = _f64(delta, (batch, dim, L))
+    B = _f64(B, (batch, N, L))
+    C = _f64(C, (batch, N, L))
+    D = _f64(D, (dim,))
+    z = _f64(z, (batch, dim, L))
+    delta_bias = _f64(delta_bias, (dim,))
+    h0 = _f64(h0, (batch, dim, N))
+    dy = _f64(dy, (batch, dim, L))
+    dh_final = _f64(dh_final, (batch, dim, N))
+    out = {"du": np.empty((batch, dim, L)), "ddelta": np.empty((batch, dim, L)),
+           "dA": np.empty((dim, N)), "dB": np.empty((batch, N, L)),
+           "dC": np.empty((batch, N, L)), "dh0": np.empty((batch, dim, N))}
+    if D is not None:
+        out["dD"] = np.empty(dim)
+    if delta_bias is not None:
+        out["ddelta_bias"] = np.empty(dim)
+    if z is not None:
+        out["dz"] = np.empty((batch, dim, L))
+    rc = _load().oracle_scan_bwd_f64(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy),
+        _ptr(dh_final), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
+        _ptr(out.get("ddelta_bias")), _ptr(out.get("dz")), _ptr(out["dh0"]),
+        batch, dim, N, L)
+    if rc != 0:
+        raise ValueError("oracle_scan_bwd_f64 rejected its arguments")
+    return out
 
 
 def step(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,

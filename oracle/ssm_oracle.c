@@ -10,6 +10,8 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
 
 /* softplus(x) = log(1 + exp(x)).  Written so neither branch overflows or
  * loses the small result: for x <= 0, log1p(e^x); for x > 0,
@@ -152,5 +154,115 @@ int oracle_causal_conv1d_silu_f64(const double *x, const double *w,
             }
         }
     }
+    return 0;
+}
+
+/* sigmoid(x) = 1 / (1 + e^-x); the derivative of softplus. */
+static double oracle_sigmoid(double x)
+{
+    return 1.0 / (1.0 + exp(-x));
+}
+
+/* d silu(z) / dz = sigmoid(z) * (1 + z * (1 - sigmoid(z))). */
+static double oracle_dsilu(double z)
+{
+    double s = oracle_sigmoid(z);
+    return s * (1.0 + z * (1.0 - s));
+}
+
+int oracle_scan_bwd_f64(const double *u, const double *delta, const double *A,
+                        const double *B, const double *C, const double *D,
+                        const double *z, const double *delta_bias,
+                        int delta_softplus, const double *h0, const double *dy,
+                        const double *dh_final, double *du, double *ddelta,
+                        double *dA, double *dB, double *dC, double *dD,
+                        double *ddelta_bias, double *dz, double *dh0,
+                        int64_t batch, int64_t dim, int64_t N, int64_t L)
+{
+    if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA ||
+        !dB || !dC || (D && !dD))
+        return -1;
+    if (batch < 0 || dim < 0 || N < 0 || L < 0)
+        return -1;
+    double *hs = malloc(sizeof(double) * (size_t)((L + 1) * N + 2 * L + N + 1));
+    if (!hs)
+        return -1;
+    double *yc = hs + (L + 1) * N;   /* pre-gate output per token */
+    double *dts = yc + L;            /* dt per token */
+    double *g = dts + L;             /* dL/dh, one channel */
+
+    memset(dA, 0, sizeof(double) * (size_t)(dim * N));
+    memset(dB, 0, sizeof(double) * (size_t)(batch * N * L));
+    memset(dC, 0, sizeof(double) * (size_t)(batch * N * L));
+    if (D)
+        memset(dD, 0, sizeof(double) * (size_t)dim);
+    if (ddelta_bias)
+        memset(ddelta_bias, 0, sizeof(double) * (size_t)dim);
+
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            int64_t row = (b * dim + d) * L;
+            int64_t srow = (b * dim + d) * N;
+            const double *Bb = B + b * N * L;   /* B[b, n, t] = Bb[n*L + t] */
+            const double *Cb = C + b * N * L;
+            const double *Ad = A + d * N;
+            /* forward, keeping every state: hs[(t+1)*N + n] = h_t[n] */
+            for (int64_t n = 0; n < N; ++n)
+                hs[n] = h0 ? h0[srow + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                double x = delta[row + t] + (delta_bias ? delta_bias[d] : 0.0);
+                double dt = delta_softplus ? oracle_softplus(x) : x;
+                dts[t] = dt;
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    double h = exp(dt * Ad[n]) * hs[t * N + n] +
+                               dt * Bb[n * L + t] * u[row + t];
+                    hs[(t + 1) * N + n] = h;
+                    acc += Cb[n * L + t] * h;
+                }
+                if (D)
+                    acc += D[d] * u[row + t];
+                yc[t] = acc;
+            }
+            /* reverse */
+            for (int64_t n = 0; n < N; ++n)
+                g[n] = dh_final ? dh_final[srow + n] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                double x = delta[row + t] + (delta_bias ? delta_bias[d] : 0.0);
+                double dt = dts[t];
+                double ut = u[row + t];
+                double s = z ? oracle_silu(z[row + t]) : 1.0;
+                double gc = dy[row + t] * s;
+                if (z && dz)
+                    dz[row + t] = dy[row + t] * yc[t] * oracle_dsilu(z[row + t]);
+                double dut = 0.0, ddt = 0.0;
+                if (D) {
+                    dD[d] += gc * ut;
+                    dut = gc * D[d];
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    double a = exp(dt * Ad[n]);
+                    double hprev = hs[t * N + n];
+                    double Bn = Bb[n * L + t];
+                    g[n] += gc * Cb[n * L + t];
+                    dC[b * N * L + n * L + t] += gc * hs[(t + 1) * N + n];
+                    ddt += g[n] * (Ad[n] * a * hprev + Bn * ut);
+                    dA[d * N + n] += g[n] * dt * a * hprev;
+                    dB[b * N * L + n * L + t] += g[n] * dt * ut;
+                    dut += g[n] * dt * Bn;
+                    g[n] *= a;
+                }
+                du[row + t] = dut;
+                double dx = delta_softplus ? ddt * oracle_sigmoid(x) : ddt;
+                ddelta[row + t] = dx;
+                if (ddelta_bias)
+                    ddelta_bias[d] += dx;
+            }
+            if (dh0)
+                for (int64_t n = 0; n < N; ++n)
+                    dh0[srow + n] = g[n];
+        }
+    }
+    free(hs);
     return 0;
 }

@@ -1,0 +1,153 @@
+"""Pins of the oracle's backward pass (oracle.scan_bwd) to things other than
+itself.
+
+* Central finite differences of the forward oracle (pinned on its own in
+  test_oracle_pins.py): for a loss L = sum(dy * y) + sum(dh_final * h_final),
+  every element of every input is nudged both ways and the slope compared
+  with the analytic gradient.  A dropped chain-rule term, a wrong sign or a
+  transposed index changes at least one slope.
+* Exact linearity identities at a larger size, where differencing every
+  element would be slow: with the steps, A, D and z held fixed, y and h_final
+  are jointly linear in (u, h0), and jointly linear in (B, h0) and in C up to
+  terms that do not depend on them, so L equals the inner product of those
+  inputs with their gradients (Euler's theorem for homogeneous functions of
+  degree one).
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def loss(inp, dy, dhf):
+    y, hf = oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                        inp["D"], inp["z"], inp["delta_bias"],
+                        inp["delta_softplus"], False, inp["h0"])
+    return float(np.sum(dy * y) + (np.sum(dhf * hf) if dhf is not None else 0.0))
+
+
+def make(seed, batch, dim, N, L, softplus=True, with_z=True, with_D=True,
+         with_bias=True, with_h0=True):
+    r = np.random.default_rng(seed)
+    inp = {
+        "u": r.normal(size=(batch, dim, L)),
+        "delta": (r.normal(size=(batch, dim, L)) if softplus
+                  else r.uniform(0.05, 0.4, size=(batch, dim, L))),
+        "A": -r.uniform(0.3, 3.0, size=(dim, N)),
+        "B": r.normal(size=(batch, N, L)),
+        "C": r.normal(size=(batch, N, L)),
+        "D": r.normal(size=dim) if with_D else None,
+        "z": r.normal(size=(batch, dim, L)) if with_z else None,
+        "delta_bias": r.normal(scale=0.5, size=dim) if with_bias else None,
+        "h0": r.normal(size=(batch, dim, N)) if with_h0 else None,
+        "delta_softplus": softplus,
+    }
+    dy = r.normal(size=(batch, dim, L))
+    dhf = r.normal(size=(batch, dim, N))
+    return inp, dy, dhf
+
+
+def grads(inp, dy, dhf):
+    return oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"],
+                           inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                           inp["delta_softplus"], inp["h0"], dy, dhf)
+
+
+GRAD_OF = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC",
+           "D": "dD", "z": "dz", "delta_bias": "ddelta_bias", "h0": "dh0"}
+
+VARIANTS = [
+    dict(softplus=True, with_z=True, with_D=True, with_bias=True, with_h0=True),
+    dict(softplus=False, with_z=False, with_D=False, with_bias=False,
+         with_h0=False),
+    dict(softplus=True, with_z=True, with_D=False, with_bias=False,
+         with_h0=True),
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=["all", "bare", "mixed"])
+def test_finite_differences_every_element(variant):
+    inp, dy, dhf = make(11, 2, 3, 4, 6, **variant)
+    g = grads(inp, dy, dhf)
+    eps = 1e-5
+    for name, gname in GRAD_OF.items():
+        if inp[name] is None:
+            assert gname not in g or name == "h0"
+            continue
+        x = inp[name]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss(inp, dy, dhf)
+            x[idx] = keep - eps
+            lm = loss(inp, dy, dhf)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(fd - g[gname]) / (1.0 + np.abs(g[gname])))
+        assert err < 1e-7, "%s: max scaled error %.3g" % (name, err)
+
+
+def test_finite_differences_without_final_state_gradient():
+    inp, dy, _ = make(12, 1, 2, 3, 5)
+    g = grads(inp, dy, None)
+    eps = 1e-5
+    for name in ("u", "delta", "A", "h0"):
+        x = inp[name]
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss(inp, dy, None)
+            x[idx] = keep - eps
+            lm = loss(inp, dy, None)
+            x[idx] = keep
+            fd = (lp - lm) / (2 * eps)
+            an = g[GRAD_OF[name]][idx]
+            assert abs(fd - an) < 1e-7 * (1.0 + abs(an)), (name, idx, fd, an)
+
+
+def _dot(a, b):
+    return float(np.sum(a * b))
+
+
+def test_linearity_in_u_and_h0():
+    """L(u, h0) = <du, u> + <dh0, h0> with steps, A, B, C, D, z fixed."""
+    inp, dy, dhf = make(13, 2, 6, 16, 200)
+    g = grads(inp, dy, dhf)
+    lhs = loss(inp, dy, dhf)
+    rhs = _dot(g["du"], inp["u"]) + _dot(g["dh0"], inp["h0"])
+    assert abs(lhs - rhs) <= 1e-10 * (abs(lhs) + 1.0)
+
+
+def test_linearity_in_B_and_h0():
+    """h is jointly linear in (B, h0); the D skip does not depend on them."""
+    inp, dy, dhf = make(14, 2, 6, 16, 200)
+    g = grads(inp, dy, dhf)
+    y, _ = oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                       inp["D"], inp["z"], inp["delta_bias"], True, False,
+                       inp["h0"])
+    s = inp["z"] / (1.0 + np.exp(-inp["z"]))
+    skip = _dot(dy * s, inp["D"][None, :, None] * inp["u"])
+    lhs = loss(inp, dy, dhf) - skip
+    rhs = _dot(g["dB"], inp["B"]) + _dot(g["dh0"], inp["h0"])
+    assert abs(lhs - rhs) <= 1e-10 * (abs(lhs) + 1.0)
+
+
+def test_linearity_in_C():
+    """With no final-state gradient, y is linear in C plus the D skip."""
+    inp, dy, _ = make(15, 2, 6, 16, 200)
+    g = grads(inp, dy, None)
+    s = inp["z"] / (1.0 + np.exp(-inp["z"]))
+    skip = _dot(dy * s, inp["D"][None, :, None] * inp["u"])
+    lhs = loss(inp, dy, None) - skip
+    assert abs(lhs - _dot(g["dC"], inp["C"])) <= 1e-10 * (abs(lhs) + 1.0)
+
+
+def test_gate_gradient_is_zero_where_output_vanishes():
+    """C = 0 and D = 0 give y = 0 for every z, so dz = 0 and dC = gc * h."""
+    inp, dy, _ = make(16, 1, 3, 4, 20)
+    inp["C"][:] = 0.0
+    inp["D"][:] = 0.0
+    g = grads(inp, dy, None)
+    assert np.all(g["dz"] == 0.0)
+    assert np.all(g["du"] == 0.0) and np.all(g["dA"] == 0.0)
