@@ -176,6 +176,60 @@ int ssm_state_update(float *state, const void *x, const void *delta,
                      unsigned flags, void *y, int64_t batch, int64_t dim,
                      int64_t dstate, int dtype, void *stream);
 
+/* Bytes of caller-provided device workspace ssm_scan_bwd needs for this
+ * shape: the block-start checkpoints (batch*dim*ceil(seqlen/1024)*16 fp32)
+ * and per-workgroup partial sums of dB and dC (2 * batch*ceil(dim/4)*16*
+ * seqlen fp32), plus per-channel partials of dA, dD and the bias. */
+int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                int64_t seqlen, size_t *bytes);
+
+/* Backward pass of ssm_scan_fwd with the Euler input term: the gradients of
+ * a scalar loss with respect to every input, given its gradient dy with
+ * respect to y and dh_final (nullable -> 0) with respect to the final state.
+ * The chain rule through the recurrence, taken in reverse token order; the
+ * states are recomputed from block-start checkpoints rather than stored
+ * (the inferownia.pl page on the selective scan, "Cena selekcji": the
+ * backward pass recomputes the intermediate states).  Definitions:
+ *   lambda_t = dL/dh_t = dy_t silu(z_t) C_t + exp(dt_{t+1} A) lambda_{t+1},
+ *              lambda_{L-1} also gets dh_final
+ *   du_t     = sum_n lambda_t,n dt_t B_t,n + dy_t silu(z_t) D
+ *   ddelta_t = (sum_n lambda_t,n (B_t,n u_t + A_n exp(dt_t A_n) h_t-1,n))
+ *              * sigmoid(delta_t + bias)        (without softplus: * 1)
+ *   dA_n     = sum_b,t lambda_t,n exp(dt_t A_n) h_t-1,n dt_t
+ *   dB_t,n   = sum_d lambda_t,n dt_t u_t     dC_t,n = sum_d dy_t silu(z_t) h_t,n
+ *   dD       = sum_b,t dy_t silu(z_t) u_t    dbias  = sum_b,t ddelta_t
+ *   dz_t     = dy_t yc_t silu'(z_t), yc_t = sum_n C_t,n h_t,n + D u_t
+ *   dh0      = exp(dt_0 A) lambda_0
+ * Arguments:
+ *  u, delta, A, B, C, D, z, delta_bias, flags, h0   as for ssm_scan_fwd
+ *                      (flags: SSM_FLAG_DELTA_SOFTPLUS only; SSM_FLAG_ZOH_B
+ *                      returns SSM_ERR_UNSUPPORTED)
+ *  dy                  required, activation dtype (batch, dim, seqlen)
+ *  dh_final            nullable fp32 (batch, dim, dstate)
+ *  du, ddelta          required outputs, activation dtype (batch, dim, seqlen)
+ *  dA                  required output fp32 (dim, dstate)
+ *  dB, dC              required outputs fp32 (batch, dstate, seqlen)
+ *  dD, ddelta_bias     nullable outputs fp32 (dim); when given they receive
+ *                      the gradient (with respect to a zero D / bias where
+ *                      D / delta_bias is NULL)
+ *  dz                  nullable output, activation dtype; only with z
+ *  dh0                 nullable output fp32 (batch, dim, dstate)
+ *  workspace           device scratch of >= ssm_scan_bwd_workspace_size()
+ *                      bytes, 256-byte aligned, in use until the enqueued work
+ *                      completes; its contents on entry do not matter
+ * No output may overlap an input, another output or the workspace.  The
+ * sequence is not split across waves (one wave per channel over the whole
+ * sequence), so shapes with few channels and very long sequences run with
+ * few waves. */
+int ssm_scan_bwd(const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z,
+                 const float *delta_bias, unsigned flags, const float *h0,
+                 const void *dy, const float *dh_final, void *du, void *ddelta,
+                 float *dA, float *dB, float *dC, float *dD,
+                 float *ddelta_bias, void *dz, float *dh0, int64_t batch,
+                 int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */
 const char *ssm_last_error(void);

@@ -15,6 +15,9 @@ Names follow the C ABI:
   depthwise conv1d(x)) is formed inside the kernel (the Mamba block's
   convolution before the SSM).
 * :func:`ssm_state_update` -- one decoding step on an in-place fp32 state.
+* :func:`ssm_scan_bwd` -- gradients of :func:`ssm_scan_fwd` (Euler input
+  term) with respect to every input, recomputing the states from block
+  checkpoints; :func:`ssm_scan_bwd_workspace_size`.
 * :func:`ssm_scan_plan`, :func:`ssm_scan_workspace_size`,
   :func:`ssm_last_error`, :func:`ssm_abi_version`.
 """
@@ -37,7 +40,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
           3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
 EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
            "ssm_scan_fwd", "ssm_conv_scan_fwd", "ssm_state_update",
-           "ssm_last_error")
+           "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_last_error")
 
 _lib = None
 _lock = threading.Lock()
@@ -83,6 +86,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, U, P,
                                          I64, I64, I64, I, P]
         lib.ssm_state_update.restype = I
+        lib.ssm_scan_bwd_workspace_size.argtypes = [
+            I64, I64, I64, I64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssm_scan_bwd_workspace_size.restype = I
+        lib.ssm_scan_bwd.argtypes = ([P] * 8 + [U] + [P] * 12 +
+                                     [I64, I64, I64, I64, I, P,
+                                      ctypes.c_size_t, P])
+        lib.ssm_scan_bwd.restype = I
         lib.ssm_last_error.argtypes = []
         lib.ssm_last_error.restype = ctypes.c_char_p
         if path is None:
@@ -322,3 +332,68 @@ def bind_state_update(state, x, delta, A, B, C, D=None, z=None,
         return keep[-1]
     call.y = y
     return call
+
+
+def ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ssm_scan_bwd_workspace_size(
+        batch, dim, dstate, seqlen, ctypes.byref(out)))
+    return out.value
+
+
+def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                 delta_softplus=True, h0=None, dy=None, dh_final=None,
+                 want_dz=True, want_dh0=True, out=None, workspace=None,
+                 stream=None):
+    """Gradients of :func:`ssm_scan_fwd` (Euler input term) for a loss with
+    gradient ``dy`` (batch, dim, L; activation dtype) with respect to y and
+    ``dh_final`` (batch, dim, N; fp32, or None) with respect to the final
+    state.  Returns a dict: du, ddelta (activation dtype), dA, dB, dC, dD,
+    ddelta_bias, dh0 (fp32) and dz (activation dtype, when z is given).
+    ``out`` may supply any of these tensors; the rest, and the workspace,
+    are allocated here with torch."""
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    N = A.shape[-1] if A.dim() == 2 else 0
+    dev = u.device
+    act = u.dtype
+    code = _dtype_code(u)
+    f32 = torch.float32
+    if dy is None:
+        raise ValueError("dy is required")
+    out = dict(out or {})
+    shapes = {"du": ((batch, dim, L), act), "ddelta": ((batch, dim, L), act),
+              "dA": ((dim, N), f32), "dB": ((batch, N, L), f32),
+              "dC": ((batch, N, L), f32), "dD": ((dim,), f32),
+              "ddelta_bias": ((dim,), f32)}
+    if z is not None and want_dz:
+        shapes["dz"] = ((batch, dim, L), act)
+    if want_dh0:
+        shapes["dh0"] = ((batch, dim, N), f32)
+    for k, (shp, dt) in shapes.items():
+        if k not in out:
+            out[k] = torch.empty(shp, dtype=dt, device=dev)
+    p = {k: _ptr(out[k], k, shapes[k][1], shapes[k][0], dev) for k in shapes}
+    ws_bytes = ssm_scan_bwd_workspace_size(batch, dim, N, L)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsn = workspace.numel() * workspace.element_size()
+    _check(load_library().ssm_scan_bwd(
+        _ptr(u, "u", act, (batch, dim, L), dev),
+        _ptr(delta, "delta", act, (batch, dim, L), dev),
+        _ptr(A, "A", f32, (dim, N), dev),
+        _ptr(B, "B", act, (batch, N, L), dev),
+        _ptr(C, "C", act, (batch, N, L), dev),
+        _ptr(D, "D", f32, (dim,), dev),
+        _ptr(z, "z", act, (batch, dim, L), dev),
+        _ptr(delta_bias, "delta_bias", f32, (dim,), dev),
+        _flags(delta_softplus, False),
+        _ptr(h0, "h0", f32, (batch, dim, N), dev),
+        _ptr(dy, "dy", act, (batch, dim, L), dev),
+        _ptr(dh_final, "dh_final", f32, (batch, dim, N), dev),
+        p["du"], p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"],
+        p["ddelta_bias"], p.get("dz"), p.get("dh0"),
+        batch, dim, N, L, code, workspace.data_ptr(), wsn,
+        _stream_handle(dev, stream)))
+    return {k: out[k] for k in shapes}

@@ -25,10 +25,9 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
              "-ffp-contract=fast", "-munsafe-fp-atomics", "-Wall"]
 
 
-def _run(cmd):
-    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                          text=True)
-    out = "\n".join(l for l in proc.stdout.splitlines()
+def _finish(cmd, proc):
+    out, _ = proc.communicate()
+    out = "\n".join(l for l in out.splitlines()
                     if "packed-fp32-ops" not in l and "--hip-link" not in l)
     if proc.returncode != 0:
         sys.stderr.write(out + "\n")
@@ -36,22 +35,38 @@ def _run(cmd):
     return out
 
 
+def _start(cmd):
+    return cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                 stderr=subprocess.STDOUT, text=True)
+
+
+def _run(cmd):
+    return _finish(*_start(cmd))
+
+
+HIP_SOURCES = ["ssm_kernels.hip", "ssm_bwd.hip"]
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = os.path.join(ROCM, "bin", "hipcc")
-    k_obj = os.path.join(BUILD_DIR, "ssm_kernels.o")
+    objs = []
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        jobs.append(_start([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                                  os.path.join(CSRC, src), "-o", obj]))
     a_obj = os.path.join(BUILD_DIR, "ssm_api.o")
-    out = _run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
-                                      os.path.join(CSRC, "ssm_kernels.hip"),
-                                      "-o", k_obj])
-    out += _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
-                 "-I", INCLUDE, "-I", CSRC, "-c",
-                 os.path.join(CSRC, "ssm_api.cpp"), "-o", a_obj])
+    objs.append(a_obj)
+    jobs.append(_start(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+                        "-I", INCLUDE, "-I", CSRC, "-c",
+                        os.path.join(CSRC, "ssm_api.cpp"), "-o", a_obj]))
+    out = "".join(_finish(*j) for j in jobs)
     tmp = LIB + ".tmp%d" % os.getpid()
-    out += _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH,
-                 "-o", tmp, k_obj, a_obj,
-                 "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
-                 "-Wl,-rpath," + os.path.join(ROCM, "lib")])
+    out += _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp]
+                + objs + ["-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+                          "-Wl,-rpath," + os.path.join(ROCM, "lib")])
     os.replace(tmp, LIB)
     if verbose and out.strip():
         print(out)

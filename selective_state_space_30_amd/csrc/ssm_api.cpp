@@ -95,6 +95,23 @@ int64_t choose_chunk(int64_t batch, int64_t dim, int64_t seqlen, int64_t request
 }  // namespace
 
 namespace ssm {
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t bd = static_cast<size_t>(batch) * dim;
+  const size_t nblk = static_cast<size_t>((seqlen + kBlockTokens - 1) / kBlockTokens);
+  const size_t groups = static_cast<size_t>((dim + kChannelsPerGroup - 1) / kChannelsPerGroup);
+  const size_t part = static_cast<size_t>(batch) * groups * kStates * seqlen * sizeof(float);
+  BwdLayout l;
+  l.off_ckpt = 0;
+  l.off_pB = up(l.off_ckpt + bd * nblk * kStates * sizeof(float));
+  l.off_pC = up(l.off_pB + part);
+  l.off_pA = up(l.off_pC + part);
+  l.off_pD = up(l.off_pA + bd * kStates * sizeof(float));
+  l.off_pbias = up(l.off_pD + bd * sizeof(float));
+  l.total_bytes = up(l.off_pbias + bd * sizeof(float));
+  return l;
+}
+
 SplitLayout split_layout(int64_t batch, int64_t dim, int64_t n_chunks) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t bdc = static_cast<size_t>(batch) * dim * n_chunks;
@@ -338,6 +355,146 @@ int ssm_state_update(float *state, const void *x, const void *delta,
   a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
   a.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
   const int err = ssm::launch_step(a, bf16, vec, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Sizes of the backward pass that fit its grid and its workspace arithmetic.
+int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  int st = check_sizes(batch, dim, dstate, seqlen);
+  if (st != SSM_OK) return st;
+  const int64_t groups = (dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
+  int64_t e;
+  if (groups >= (int64_t(1) << 31) || !mul_ok(batch * groups, ssm::kStates * seqlen, &e) ||
+      !mul_ok(e, 8, &e))
+    return fail(SSM_ERR_UNSUPPORTED, "backward workspace of this shape overflows");
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                int64_t seqlen, size_t *bytes) {
+  if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
+  int st = check_bwd_sizes(batch, dim, dstate, seqlen);
+  if (st != SSM_OK) return st;
+  *bytes = ssm::bwd_layout(batch, dim, seqlen).total_bytes;
+  return ok();
+}
+
+int ssm_scan_bwd(const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z,
+                 const float *delta_bias, unsigned flags, const float *h0,
+                 const void *dy, const float *dh_final, void *du, void *ddelta,
+                 float *dA, float *dB, float *dC, float *dD,
+                 float *ddelta_bias, void *dz, float *dh0, int64_t batch,
+                 int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+  if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
+    return fail(SSM_ERR_INVALID_ARG, "required pointer is NULL");
+  if (dz && !z) return fail(SSM_ERR_INVALID_ARG, "dz given without z");
+  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & ~kKnownFlags)
+    return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (flags & SSM_FLAG_ZOH_B)
+    return fail(SSM_ERR_UNSUPPORTED, "the backward pass implements the Euler input term only");
+  int st = check_bwd_sizes(batch, dim, dstate, seqlen);
+  if (st != SSM_OK) return st;
+
+  const bool bf16 = dtype == SSM_DTYPE_BF16;
+  const int64_t es = bf16 ? 2 : 4;
+  const void *acts[] = {u, delta, B, C, z, dy, du, ddelta, dz};
+  for (const void *p : acts)
+    if (p && !aligned(p, es))
+      return fail(SSM_ERR_INVALID_ARG, "activation pointer %p not %lld-byte aligned", p,
+                  (long long)es);
+  const void *f32s[] = {A, D, delta_bias, h0, dh_final, dA, dB, dC, dD, ddelta_bias, dh0};
+  for (const void *p : f32s)
+    if (p && !aligned(p, 4))
+      return fail(SSM_ERR_INVALID_ARG, "fp32 pointer %p not 4-byte aligned", p);
+
+  const int64_t big = batch * dim * seqlen * es;
+  const int64_t bc = batch * dstate * seqlen * es;
+  const int64_t bcf = batch * dstate * seqlen * 4;
+  const int64_t sts = batch * dim * dstate * 4;
+  const struct { const void *p; int64_t n; const char *name; } ins[] = {
+      {u, big, "u"}, {delta, big, "delta"}, {z, big, "z"}, {dy, big, "dy"},
+      {B, bc, "B"}, {C, bc, "C"}, {A, dim * dstate * 4, "A"}, {D, dim * 4, "D"},
+      {delta_bias, dim * 4, "delta_bias"}, {h0, sts, "h0"}, {dh_final, sts, "dh_final"}};
+  const struct { const void *p; int64_t n; const char *name; } outs[] = {
+      {du, big, "du"}, {ddelta, big, "ddelta"}, {dz, big, "dz"}, {dA, dim * dstate * 4, "dA"},
+      {dB, bcf, "dB"}, {dC, bcf, "dC"}, {dD, dim * 4, "dD"},
+      {ddelta_bias, dim * 4, "ddelta_bias"}, {dh0, sts, "dh0"}};
+  for (const auto &o : outs) {
+    for (const auto &in : ins)
+      if (overlaps(o.p, o.n, in.p, in.n))
+        return fail(SSM_ERR_INVALID_ARG, "%s overlaps input %s", o.name, in.name);
+    for (const auto &o2 : outs)
+      if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n))
+        return fail(SSM_ERR_INVALID_ARG, "%s overlaps %s", o.name, o2.name);
+  }
+
+  const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen);
+  if (!workspace || workspace_bytes < l.total_bytes)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu bytes at %p)",
+                l.total_bytes, workspace_bytes, workspace);
+  if (!aligned(workspace, 256))
+    return fail(SSM_ERR_INVALID_ARG, "workspace %p not 256-byte aligned", workspace);
+  for (const auto &in : ins)
+    if (overlaps(workspace, static_cast<int64_t>(l.total_bytes), in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "workspace overlaps input %s", in.name);
+  for (const auto &o : outs)
+    if (overlaps(workspace, static_cast<int64_t>(l.total_bytes), o.p, o.n))
+      return fail(SSM_ERR_INVALID_ARG, "workspace overlaps output %s", o.name);
+
+  bool vec = (seqlen * es) % 16 == 0;
+  for (const void *p : acts)
+    if (p && !aligned(p, 16)) vec = false;
+
+  char *w = static_cast<char *>(workspace);
+  float *ckpt = reinterpret_cast<float *>(w + l.off_ckpt);
+
+  // 1. checkpoint pass: the forward scan keeping only block-start states
+  //    (and forming dz, which needs the pre-gate output)
+  ssm::ScanArgs fa{};
+  fa.u = u; fa.delta = delta; fa.B = B; fa.C = C; fa.z = z;
+  fa.dy = dy; fa.dz = dz;  // the gate's gradient needs the pre-gate output
+  fa.A = A; fa.D = D; fa.bias = delta_bias; fa.h0 = h0;
+  fa.y = nullptr; fa.h_final = nullptr;
+  fa.batch = batch; fa.dim = dim; fa.L = seqlen;
+  fa.chunk_len = seqlen; fa.n_chunks = 1;
+  fa.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+  fa.zoh = 0;
+  fa.ckpt = ckpt;
+  int err = ssm::launch_scan(fa, bf16, vec, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+
+  // 2. reverse sweep and 3. reductions
+  ssm::BwdArgs a{};
+  a.u = u; a.delta = delta; a.B = B; a.C = C; a.z = z; a.dy = dy;
+  a.A = A; a.D = D; a.bias = delta_bias; a.h0 = h0; a.dh_final = dh_final;
+  a.ckpt = ckpt;
+  a.du = du; a.ddelta = ddelta; a.dh0 = dh0;
+  a.pB = reinterpret_cast<float *>(w + l.off_pB);
+  a.pC = reinterpret_cast<float *>(w + l.off_pC);
+  a.pA = reinterpret_cast<float *>(w + l.off_pA);
+  a.pD = reinterpret_cast<float *>(w + l.off_pD);
+  a.pbias = reinterpret_cast<float *>(w + l.off_pbias);
+  a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dbias = ddelta_bias;
+  a.batch = batch; a.dim = dim; a.L = seqlen;
+  a.groups = (dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
+  a.nblk = static_cast<int>((seqlen + ssm::kBlockTokens - 1) / ssm::kBlockTokens);
+  a.softplus = fa.softplus;
+  err = ssm::launch_bwd(a, bf16, vec, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
   return ok();

@@ -1,0 +1,393 @@
+// ssm_bwd.hip -- gfx950 (CDNA4) kernels of the selective scan's backward
+// pass (Euler input term).
+//
+// Gradients of a loss with respect to u, delta (before softplus), A, B, C,
+// D, z, the delta bias and the initial state, given its gradients dy and
+// dh_final, by the chain rule through the recurrence h_t = a_t h_{t-1} + b_t
+// (a_t = exp(dt_t A), b_t = dt_t B_t u_t) of "Mamba & State Space Models -
+// Guide Complet", section 4.  As the inferownia.pl page says of the
+// selective scan ("Cena selekcji"), the backward pass recomputes the states
+// instead of reading them from HBM: a checkpoint pass (the forward kernel)
+// keeps only the state entering each 1024-token block, and each block is
+// recomputed on chip before its gradients are formed.
+//
+// With lambda_t = dL/dh_t and mu_t = a_t lambda_t (what flows from token t
+// to token t-1), the reverse recurrence is
+//   lambda_t = gc_t C_t + mu_{t+1},   gc_t = dy_t silu(z_t),
+// itself a scan of affine maps mu_{t+1} -> a_t (gc_t C_t + mu_{t+1}), run in
+// reverse token order (the associativity of the Guide Complet's "Parallel
+// Associative Scan" holds in either direction).  Per (t, n):
+//   ddt_t += lambda (B u + A a h_{t-1}),  dA_n += lambda a h_{t-1} dt_t,
+//   dB_{t,n} += lambda dt u,  du_t += lambda dt B,  dC_{t,n} += gc_t h_t.
+//
+// Work layout, as in the forward kernel: one wave = one channel, a
+// workgroup = 4 channels of one batch entry, a lane = 16 consecutive tokens;
+// blocks are visited from the last to the first.  For each state the lane
+// recomputes its 16 states (fold, 64-lane scan, replay from the block's
+// checkpoint), folds the reverse maps of its tokens, and a reverse 64-lane
+// scan (lanes reversed with ds_bpermute, then the forward DPP scan) gives
+// each lane the mu entering from its right.  dB and dC are sums over all
+// channels of a batch entry: the 4 channels of a workgroup add theirs into
+// an LDS tile with float atomics, the tile is written as a per-workgroup
+// partial sum, and a reduction kernel sums the partials.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+using namespace dev;
+
+// Lane i receives lane 63 - i's value (LDS crossbar, no memory access).
+__device__ __forceinline__ float wave_reverse(float v, int lane) {
+  return __int_as_float(
+      __builtin_amdgcn_ds_bpermute((kWaveLanes - 1 - lane) << 2, __float_as_int(v)));
+}
+
+// Writes the 16-token run of partial sums held at LDS `acc + off` to
+// row[t ..] (16-byte stores when kVec: rows of a multiple of 4 tokens; the
+// partial block through the buffer view), then clears the LDS run for the
+// next phase.
+template <bool kVec, bool kFull>
+__device__ __forceinline__ void flush_run(float *acc, int off, float *row,
+                                          int64_t t0, int64_t t, int64_t tend) {
+  constexpr int K = kTokensPerLane;
+  float4 *src = reinterpret_cast<float4 *>(acc + off);
+  float v[K];
+#pragma unroll
+  for (int q = 0; q < K / 4; ++q) {
+    const float4 w = src[q];
+    v[4 * q + 0] = w.x;
+    v[4 * q + 1] = w.y;
+    v[4 * q + 2] = w.z;
+    v[4 * q + 3] = w.w;
+  }
+  store_run<float, K, kVec, kFull>(row, t0, t, tend, v);
+#pragma unroll
+  for (int q = 0; q < K / 4; ++q) src[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+// Per-state values of one channel kept one state per lane (lane n holds
+// state n) in a single register instead of 16 scalar registers.
+__device__ __forceinline__ float state_of(float v, int n) { return lane_broadcast(v, n); }
+__device__ __forceinline__ float set_state(float v, int lane, int n, float x) {
+  return lane == n ? x : v;
+}
+
+// One block of one channel, in reverse.  hfv: the forward states entering
+// the block (checkpoint; lane n = state n); muv: dL/dh flowing in from the
+// right of the block (replaced by what flows out of its first token); dAv:
+// running dA sums of the channel (lane n = state n, already times 1/ln2).
+template <typename T, bool kVec, bool kFull, bool kSoftplus>
+__device__ __forceinline__ void bwd_block(
+    const BwdArgs &p, int wave, int lane, int64_t t0, int64_t tend, int64_t b,
+    int64_t bd, int64_t g, const T *__restrict__ Bb, const T *__restrict__ Cb,
+    bool ch_ok, float bias, float Dd, float Av, float hfv, float &muv, float &dAv,
+    float &dDl, float &dbl, float *sT, float *sG) {
+  constexpr int K = kTokensPerLane;
+  constexpr int KP = K + 4;
+  constexpr int kPhases = kStates / 2;
+  constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
+  const int64_t tl = t0 + static_cast<int64_t>(lane) * K;
+  const T *urow = static_cast<const T *>(p.u) + bd * p.L;
+  const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
+  const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
+  const T *gyrow = static_cast<const T *>(p.dy) + bd * p.L;
+
+  // staging / flushing role of this wave: state (2*ph + st), matrix mat
+  const int st = wave >> 1, mat = wave & 1;
+  const T *src = mat ? Cb : Bb;
+  const int toff = staging_offset(wave, lane);
+  float *prow = (mat ? p.pC : p.pB) + (b * p.groups + g) * kStates * p.L;
+  TileRun<T, K, kVec, kFull> run;
+  run.load(src + st * p.L, t0, tl, tend);
+
+  // per token: dt (as dt*log2 e), dt*u, the gated output gradient gc and
+  // the sums over states s1 = sum lambda B, s2 = sum lambda a h_prev A
+  float dtl[K], du[K], gc[K], s1[K], s2[K];
+  float sdt = 0.0f;
+  {
+    float uu[K], dr[K];
+    load_run<T, K, kVec, kFull>(urow, t0, tl, tend, uu);
+    load_run<T, K, kVec, kFull>(drow, t0, tl, tend, dr);
+    load_run<T, K, kVec, kFull>(gyrow, t0, tl, tend, gc);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const float x = dr[j] + bias;
+      float v = kSoftplus ? softplus_f(x) : x;
+      if (!kFull) v = (tl + j < tend) ? v : 0.0f;  // identity step
+      dtl[j] = v * kLog2e;
+      du[j] = v * uu[j];
+      sdt += v;
+      s1[j] = 0.0f;
+      s2[j] = 0.0f;
+    }
+  }
+  if (zrow) {
+    float zz[K];
+    load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
+#pragma unroll
+    for (int j = 0; j < K; ++j) gc[j] *= silu_f(zz[j]);
+  }
+  run.store(sT, toff);
+  const float sdtl = sdt * kLog2e;
+
+#pragma unroll 1
+  for (int ph = 0; ph < kPhases; ++ph) {
+    if (ph + 1 < kPhases) run.load(src + (2 * (ph + 1) + st) * p.L, t0, tl, tend);
+    __syncthreads();  // tile ph complete; every wave's atomics of phase ph-1 done
+    if (ph > 0)
+      flush_run<kVec, kFull>(sG + ((ph - 1) & 1) * kTileFloats, toff,
+                             prow + (2 * (ph - 1) + st) * p.L, t0, tl, tend);
+    const float *tile = sT + (ph & 1) * kTileFloats;
+    float *acc = sG + (ph & 1) * kTileFloats;
+#pragma unroll
+    for (int s2i = 0; s2i < 2; ++s2i) {
+      const int n = 2 * ph + s2i;
+      float An = state_of(Av, n);
+      asm volatile("" : "+s"(An));  // keep this state's work after the previous state's
+      const float hfn = state_of(hfv, n);
+      const float mun = state_of(muv, n);
+      const float *pb = &tile[((s2i * 2 + 0) * kWaveLanes + lane) * KP];
+      const float *pc = &tile[((s2i * 2 + 1) * kWaveLanes + lane) * KP];
+      float *ab = acc + ((s2i * 2 + 0) * kWaveLanes + lane) * KP;
+      float *ac = acc + ((s2i * 2 + 1) * kWaveLanes + lane) * KP;
+      // forward recomputation of this lane's 16 states:
+      // hin = the state before the lane's first token, hs[j] = after token j
+      float a[K], hs[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        a[j] = fast_exp2(dtl[j] * An);
+        hs[j] = du[j] * pb[j];  // dt B u, replaced by the state below
+      }
+      float H = hs[0];
+#pragma unroll
+      for (int j = 1; j < K; ++j) H = fmaf(a[j], H, hs[j]);
+      const float Pl = fast_exp2(sdtl * An);  // product of the lane's a
+      float P = Pl;
+      H = fmaf(P, lane == 0 ? hfn : 0.0f, H);
+      wave_affine_scan(P, H);
+      const float hin = wave_shift_in(H, hfn);
+      {
+        float h = hin;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          h = fmaf(a[j], h, hs[j]);
+          hs[j] = h;
+        }
+      }
+      // reverse: the lane's map mu_in -> mu_out (tokens 15 .. 0), then the
+      // 64 lanes composed from the right (reversed lane order, forward scan)
+      float M = 0.0f;
+#pragma unroll
+      for (int j = K - 1; j >= 0; --j) M = fmaf(gc[j], pc[j], M) * a[j];
+      float Pr = wave_reverse(Pl, lane);
+      float Mr = wave_reverse(M, lane);
+      Mr = fmaf(Pr, lane == 0 ? mun : 0.0f, Mr);
+      wave_affine_scan(Pr, Mr);
+      // cross-lane results are formed by the whole wave and pinned in a
+      // scalar register before one lane takes them: otherwise the compiler
+      // may move the DPP / readlane under the lane == n mask
+      float mu_out = lane_broadcast(Mr, kWaveLanes - 1);
+      asm volatile("" : "+s"(mu_out));
+      muv = set_state(muv, lane, n, mu_out);
+      float m = wave_reverse(wave_shift_in(Mr, mun), lane);
+      // reverse replay: lambda_j = dL/dh_j, then the gradients of token j
+      float dA_acc = 0.0f;
+#pragma unroll
+      for (int j = K - 1; j >= 0; --j) {
+        const float lam = fmaf(gc[j], pc[j], m);
+        s1[j] = fmaf(lam, pb[j], s1[j]);
+        m = a[j] * lam;                                  // lambda a
+        const float q = m * (j > 0 ? hs[j - 1] : hin);   // lambda a h_{j-1}
+        s2[j] = fmaf(q, An, s2[j]);
+        dA_acc = fmaf(q, dtl[j], dA_acc);
+        if (ch_ok) {
+          atomicAdd(ab + j, lam * du[j]);
+          atomicAdd(ac + j, gc[j] * hs[j]);
+        }
+      }
+      float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
+      asm volatile("" : "+s"(dA_sum));
+      dAv += lane == n ? dA_sum : 0.0f;
+    }
+    if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
+  }
+  __syncthreads();  // every wave's atomics of the last phase done
+  flush_run<kVec, kFull>(sG + ((kPhases - 1) & 1) * kTileFloats, toff,
+                         prow + (2 * (kPhases - 1) + st) * p.L, t0, tl, tend);
+
+  // per-token gradients
+  float uu[K], dr[K];
+  load_run<T, K, kVec, kFull>(urow, t0, tl, tend, uu);
+  load_run<T, K, kVec, kFull>(drow, t0, tl, tend, dr);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const float x = dr[j] + bias;
+    const float dt = kSoftplus ? softplus_f(x) : x;
+    const float ddt = fmaf(uu[j], s1[j], s2[j]);
+    const float dx = kSoftplus ? ddt * sigmoid_f(x) : ddt;
+    dbl += (kFull || tl + j < tend) ? dx : 0.0f;
+    dDl = fmaf(gc[j], uu[j], dDl);
+    s1[j] = fmaf(dt, s1[j], gc[j] * Dd);  // du
+    s2[j] = dx;                            // ddelta
+  }
+  if (ch_ok) {
+    store_run<T, K, kVec, kFull>(static_cast<T *>(p.du) + bd * p.L, t0, tl, tend, s1);
+    store_run<T, K, kVec, kFull>(static_cast<T *>(p.ddelta) + bd * p.L, t0, tl, tend, s2);
+  }
+}
+
+template <typename T, bool kVec, bool kSoftplus>
+__global__ __launch_bounds__(kWaveLanes * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(2)))
+void bwd_kernel(BwdArgs p) {
+  constexpr int KP = kTokensPerLane + 4;
+  constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
+  __shared__ float sT[2 * kTileFloats];  // staged B, C (fp32), double-buffered
+  __shared__ float sG[2 * kTileFloats];  // dB, dC of the 4 channels, double-buffered
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t b = blockIdx.y;
+  const int64_t g = blockIdx.x;
+  const int64_t d_raw = g * kChannelsPerGroup + wave;
+  const bool ch_ok = d_raw < p.dim;
+  const int64_t d = ch_ok ? d_raw : p.dim - 1;  // clamped for reads
+  const int64_t bd = b * p.dim + d;
+  const int ls = lane < kStates ? lane : 0;  // lane n <-> state n
+
+  const float Av = p.A[d * kStates + ls];
+  float muv = p.dh_final ? p.dh_final[bd * kStates + ls] : 0.0f;
+  float dAv = 0.0f;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float Dd = p.D ? p.D[d] : 0.0f;
+  const T *Bb = static_cast<const T *>(p.B) + b * kStates * p.L;
+  const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
+  float dDl = 0.0f, dbl = 0.0f;
+
+  // the partial-sum tiles start at zero; each thread clears the runs it
+  // later flushes
+  {
+    const int off = staging_offset(wave, lane);
+#pragma unroll
+    for (int buf = 0; buf < 2; ++buf) {
+      float4 *z4 = reinterpret_cast<float4 *>(sG + buf * kTileFloats + off);
+#pragma unroll
+      for (int q = 0; q < kTokensPerLane / 4; ++q) z4[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  }
+
+  const float *ck = p.ckpt + bd * p.nblk * kStates;
+  const int64_t nfull = p.L / kBlockTokens;
+  if (nfull * kBlockTokens < p.L)  // the partial last block comes first
+    bwd_block<T, false, false, kSoftplus>(p, wave, lane, nfull * kBlockTokens, p.L, b, bd, g,
+                                          Bb, Cb, ch_ok, bias, Dd, Av,
+                                          ck[nfull * kStates + ls], muv, dAv, dDl, dbl, sT,
+                                          sG);
+#pragma unroll 1
+  for (int64_t k = nfull - 1; k >= 0; --k)
+    bwd_block<T, kVec, true, kSoftplus>(p, wave, lane, k * kBlockTokens,
+                                        (k + 1) * kBlockTokens, b, bd, g, Bb, Cb, ch_ok, bias,
+                                        Dd, Av, ck[k * kStates + ls], muv, dAv, dDl, dbl, sT,
+                                        sG);
+
+  if (!ch_ok) return;
+  if (lane < kStates) {
+    p.pA[bd * kStates + lane] = dAv * kLn2;  // sum of q * dt = q * dtl * ln2
+    if (p.dh0) p.dh0[bd * kStates + lane] = muv;
+  }
+  float sD = lane_broadcast(wave_inclusive_sum(dDl), kWaveLanes - 1);
+  float sb = lane_broadcast(wave_inclusive_sum(dbl), kWaveLanes - 1);
+  asm volatile("" : "+s"(sD), "+s"(sb));  // formed by the whole wave first
+  if (lane == 0) {
+    p.pD[bd] = sD;
+    p.pbias[bd] = sb;
+  }
+}
+
+// dB[b, n, t] = sum over groups of the partial sums (dC alike); one thread
+// per four consecutive tokens.
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdArgs p) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t L4 = (p.L + 3) / 4;
+  const int64_t total = p.batch * kStates * L4;
+  if (q >= total) return;
+  const int mat = blockIdx.y;
+  const int64_t b = q / (kStates * L4);
+  const int64_t rem = q - b * kStates * L4;
+  const int64_t n = rem / L4;
+  const int64_t t = (rem - n * L4) * 4;
+  const float *part = (mat ? p.pC : p.pB) + (b * p.groups * kStates + n) * p.L + t;
+  float *out = (mat ? p.dC : p.dB) + (b * kStates + n) * p.L + t;
+  const int64_t stride = kStates * p.L;
+  const int cnt = p.L - t < 4 ? static_cast<int>(p.L - t) : 4;
+  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int64_t gi = 0; gi < p.groups; ++gi) {
+    const float *r = part + gi * stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < cnt) s[i] += r[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < cnt) out[i] = s[i];
+}
+
+// dA[d, n], dD[d], dbias[d]: sums over the batch of the per-(b, d) partials.
+__global__ __launch_bounds__(256) void bwd_reduce_param_kernel(BwdArgs p) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= p.dim * kStates) return;
+  const int64_t d = i / kStates;
+  float sa = 0.0f;
+  for (int64_t b = 0; b < p.batch; ++b) sa += p.pA[(b * p.dim) * kStates + i];
+  p.dA[i] = sa;
+  if ((i % kStates) == 0) {
+    float sd = 0.0f, sb = 0.0f;
+    for (int64_t b = 0; b < p.batch; ++b) {
+      sd += p.pD[b * p.dim + d];
+      sb += p.pbias[b * p.dim + d];
+    }
+    if (p.dD) p.dD[d] = sd;
+    if (p.dbias) p.dbias[d] = sb;
+  }
+}
+
+template <typename T, bool kVec>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.groups), static_cast<unsigned>(a.batch));
+  if (a.softplus)
+    hipLaunchKernelGGL((bwd_kernel<T, kVec, true>), grid, dim3(kWaveLanes * kWavesPerGroup),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_kernel<T, kVec, false>), grid, dim3(kWaveLanes * kWavesPerGroup),
+                       0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nq = a.batch * kStates * ((a.L + 3) / 4);
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>((nq + 255) / 256), 2),
+                     dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_reduce_param_kernel,
+                     dim3(static_cast<unsigned>((a.dim * kStates + 255) / 256)), dim3(256), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_bwd(const BwdArgs &a, bool bf16, bool vec, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bf16)
+    return vec ? launch_bwd_t<uint16_t, true>(a, s) : launch_bwd_t<uint16_t, false>(a, s);
+  return vec ? launch_bwd_t<float, true>(a, s) : launch_bwd_t<float, false>(a, s);
+}
+
+}  // namespace ssm

@@ -33,6 +33,31 @@ struct ScanArgs {
   int n_chunks;
   int softplus;                       // 1: dt = softplus(delta + bias)
   int zoh;                            // 1: exact ZOH input term
+  float *ckpt;                        // or null: state at every block start,
+                                      // (batch, dim, ceil(L/1024), 16); y may
+                                      // then be null (nothing is stored)
+  const void *dy;                     // checkpoint pass with y null: with dy
+  void *dz;                           // and z given, dz = dy * yc * silu'(z),
+                                      // yc the pre-gate output
+};
+
+// Backward pass.  Per-workgroup partial sums (a workgroup = 4 channels of
+// one batch entry) are reduced by a second kernel.
+struct BwdArgs {
+  const void *u, *delta, *B, *C, *z, *dy;  // activation dtype
+  const float *A, *D, *bias, *h0, *dh_final;
+  const float *ckpt;                  // (batch, dim, nblk, 16) forward states
+  void *du, *ddelta;                  // activation dtype outputs (dz is
+                                      // formed by the checkpoint pass)
+  float *dh0;                         // (batch, dim, 16) or null
+  float *pB, *pC;                     // (batch, groups, 16, L) partial dB, dC
+  float *pA;                          // (batch, dim, 16) partial dA
+  float *pD, *pbias;                  // (batch, dim) partial dD, dbias
+  float *dA, *dB, *dC, *dD, *dbias;   // reduced outputs (dD, dbias: or null)
+  int64_t batch, dim, L;
+  int64_t groups;                     // ceil(dim / 4)
+  int nblk;                           // ceil(L / 1024)
+  int softplus;
 };
 
 struct StepArgs {
@@ -56,6 +81,13 @@ SplitLayout split_layout(int64_t batch, int64_t dim, int64_t n_chunks);
 // `vec` selects 16-byte vector loads (the caller has checked alignment).
 int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream);
 int launch_step(const StepArgs &a, bool bf16, bool vec, void *stream);
+int launch_bwd(const BwdArgs &a, bool bf16, bool vec, void *stream);
+
+// Workspace layout of the backward pass, in bytes, each part 256-aligned.
+struct BwdLayout {
+  size_t off_ckpt, off_pB, off_pC, off_pA, off_pD, off_pbias, total_bytes;
+};
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen);
 const char *hip_error_string(int err);
 
 }  // namespace ssm

@@ -224,3 +224,66 @@ INVALID_CONV_CASES = [
 def test_conv_scan_rejects_invalid_arguments(lib, name, kw, status):
     assert _conv(lib, **kw) == status
     assert lib.ssm_last_error().decode()
+
+
+def _bwd(lib, **kw):
+    step = 0x08000000
+    names = ["u", "delta", "A", "B", "C", "dy", "du", "ddelta", "dA", "dB",
+             "dC", "ws"]
+    a = {n: FAKE + i * step for i, n in enumerate(names)}
+    a.update(D=None, z=None, bias=None, flags=1, h0=None, dh_final=None,
+             dD=None, dbias=None, dz=None, dh0=None, batch=1, dim=16,
+             dstate=16, seqlen=256, dtype=ssm.SSM_DTYPE_F32, stream=None)
+    size = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, ctypes.byref(size)) == 0
+    a["ws_bytes"] = size.value
+    a.update(kw)
+    return lib.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"],
+                            a["z"], a["bias"], a["flags"], a["h0"], a["dy"],
+                            a["dh_final"], a["du"], a["ddelta"], a["dA"],
+                            a["dB"], a["dC"], a["dD"], a["dbias"], a["dz"],
+                            a["dh0"], a["batch"], a["dim"], a["dstate"],
+                            a["seqlen"], a["dtype"], a["ws"], a["ws_bytes"],
+                            a["stream"])
+
+
+INVALID_BWD_CASES = [
+    ("null u", dict(u=None), 1),
+    ("null dy", dict(dy=None), 1),
+    ("null du", dict(du=None), 1),
+    ("null ddelta", dict(ddelta=None), 1),
+    ("null dA", dict(dA=None), 1),
+    ("null dB", dict(dB=None), 1),
+    ("null dC", dict(dC=None), 1),
+    ("dz without z", dict(dz=FAKE + 0x70000000), 1),
+    ("zoh flag", dict(flags=3), 2),
+    ("unknown flag", dict(flags=8), 1),
+    ("dstate 8", dict(dstate=8), 2),
+    ("zero seqlen", dict(seqlen=0), 1),
+    ("bad dtype", dict(dtype=5), 1),
+    ("misaligned dy", dict(dy=FAKE + 5 * 0x08000000 + 2), 1),
+    ("du overlaps u", dict(du=FAKE + 64), 1),
+    ("dB overlaps dC", dict(dB=FAKE + 10 * 0x08000000 + 16), 1),
+    ("workspace missing", dict(ws=None), 3),
+    ("workspace too small", dict(ws_bytes=1024), 3),
+    ("workspace misaligned", dict(ws=FAKE + 11 * 0x08000000 + 16), 1),
+    ("workspace overlaps du", dict(ws=FAKE + 6 * 0x08000000), 1),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_BWD_CASES,
+                         ids=[c[0] for c in INVALID_BWD_CASES])
+def test_bwd_rejects_invalid_arguments(lib, name, kw, status):
+    assert _bwd(lib, **kw) == status, ssm.ssm_last_error()
+    assert ssm.ssm_last_error()
+
+
+def test_bwd_workspace_size(lib):
+    size = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(2, 5120, 16, 4096, ctypes.byref(size)) == 0
+    groups = 5120 // 4
+    partials = 2 * (2 * groups * 16 * 4096 * 4)
+    checkpoints = 2 * 5120 * 4 * 16 * 4
+    assert partials + checkpoints <= size.value < partials + checkpoints + 2 * 2**20
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 8, 256, ctypes.byref(size)) == 2
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, None) == 1

@@ -1,0 +1,195 @@
+"""Parity of the HIP backward pass (ssm_scan_bwd) with the fp64 oracle's
+chain rule (oracle.scan_bwd, pinned by finite differences).
+
+Small shapes are compared element by element on every gradient.  At the
+Mamba-layer sizes the per-channel gradients (du, ddelta, dz, dh0, and dA for
+a channel over the batch) are compared on sampled channels, and the channel
+sums dB, dC through identities that hold at any size (y is degree-one
+homogeneous in (u, h0), in (B, h0) and in C).
+
+Bars: fp32 activations 1e-4 on the scaled error max|g - r| / (|r| + rms r);
+bf16 activations 2e-2.  The summed gradients (dA, dB, dC, dD, dbias) add up
+to batch*L (dA, dD, dbias) or dim (dB, dC) fp32 terms, whose rounding stays
+far below the fp32 bar at these sizes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_30_amd as ssm
+import synthetic as syn
+from parity_metrics import report, scaled_max_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def check(got, ref, tol, what):
+    err = scaled_max_err(got, ref)
+    assert err <= tol, "%s: %s (tol %g)" % (what, report(got, ref), tol)
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v)
+            for k, v in inp.items()}
+
+
+def make(batch, dim, L, dt, seed, with_z=True, with_D=True, with_bias=True,
+         with_h0=True, with_dhf=True, softplus=True):
+    inp = syn.make_scan_inputs(syn.TINY, "cpu", batch=batch, dim=dim,
+                               seqlen=L, dtype=dt, with_h0=with_h0,
+                               with_z=with_z, with_D=with_D, seed=seed)
+    if not with_bias:
+        inp["delta_bias"] = None
+    if not softplus:
+        inp["delta"] = (0.05 * inp["delta"].float().abs()).to(inp["delta"].dtype)
+        inp["delta_softplus"] = False
+    g = torch.Generator().manual_seed(seed + 77)
+    inp["dy"] = torch.randn(batch, dim, L, generator=g).to(inp["u"].dtype)
+    inp["dh_final"] = (torch.randn(batch, dim, 16, generator=g)
+                       if with_dhf else None)
+    return inp
+
+
+def gpu_bwd(d):
+    g = ssm.ssm_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                         d["z"], d["delta_bias"], d["delta_softplus"], d["h0"],
+                         d["dy"], d["dh_final"])
+    torch.cuda.synchronize()
+    return g
+
+
+def oracle_bwd(inp):
+    return oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"],
+                           inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                           inp["delta_softplus"], inp["h0"], inp["dy"],
+                           inp["dh_final"])
+
+
+CASES = [
+    # (batch, dim, L, dtype, z, D, bias, h0, dh_final, softplus)
+    (1, 8, 256, "f32", 1, 1, 1, 1, 1, 1),     # one partial block
+    (2, 13, 2100, "f32", 1, 1, 1, 1, 1, 1),   # ragged tail, dim % 4 != 0
+    (2, 16, 2048, "f32", 1, 1, 1, 0, 0, 1),   # full blocks, no h0 / dh_final
+    (1, 6, 999, "f32", 1, 0, 1, 1, 1, 1),     # unaligned rows
+    (2, 8, 1024, "f32", 0, 0, 0, 0, 0, 0),    # bare, softplus off
+    (1, 5, 1, "f32", 1, 1, 1, 1, 1, 1),       # a single token
+    (2, 20, 3072, "bf16", 1, 1, 1, 1, 1, 1),
+    (1, 9, 1500, "bf16", 1, 1, 0, 0, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES,
+                         ids=lambda c: "b%d_d%d_l%d_%s_z%d_D%d_b%d_h%d_g%d_sp%d" % c)
+def test_bwd_matches_oracle(case):
+    batch, dim, L, dt, wz, wD, wb, wh, wg, sp = case
+    inp = make(batch, dim, L, dt, 500 + L + dim, bool(wz), bool(wD), bool(wb),
+               bool(wh), bool(wg), bool(sp))
+    ref = oracle_bwd(inp)
+    got = gpu_bwd(to_dev(inp))
+    tol = TOL[dt]
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dh0"):
+        check(got[k], ref[k], tol, k)
+    if wD:
+        check(got["dD"], ref["dD"], tol, "dD")
+    if wb:
+        check(got["ddelta_bias"], ref["ddelta_bias"], tol, "ddelta_bias")
+    if wz:
+        check(got["dz"], ref["dz"], tol, "dz")
+
+
+def test_bwd_zero_gradient_in_gives_zero_out():
+    inp = make(1, 8, 700, "f32", 9)
+    inp["dy"].zero_()
+    inp["dh_final"].zero_()
+    got = gpu_bwd(to_dev(inp))
+    for k, v in got.items():
+        assert torch.count_nonzero(v) == 0, k
+
+
+def test_bwd_deterministic_except_atomic_sums():
+    inp = to_dev(make(2, 24, 2500, "bf16", 10))
+    g1 = gpu_bwd(inp)
+    g2 = gpu_bwd(inp)
+    for k in g1:
+        if k in ("dB", "dC"):  # four channels meet in LDS float atomics
+            check(g2[k], g1[k].double(), 1e-6, k)
+        else:
+            assert torch.equal(g1[k], g2[k]), k
+
+
+def _sampled_channels(cfg, r, k=8):
+    return sorted({(0, 0), (cfg.batch - 1, cfg.dim - 1)} |
+                  {(int(r.integers(cfg.batch)), int(r.integers(cfg.dim)))
+                   for _ in range(k)})
+
+
+@pytest.mark.parametrize("cfg", [syn.MAMBA_130M, syn.MAMBA_2P8B],
+                         ids=lambda c: c.name)
+def test_bwd_layer_workload_sampled(cfg):
+    inp = syn.make_scan_inputs(cfg, DEV, with_h0=True)
+    g = torch.Generator(device=DEV).manual_seed(cfg.seed + 5)
+    inp["dy"] = torch.randn(cfg.batch, cfg.dim, cfg.seqlen, generator=g,
+                            device=DEV).to(inp["u"].dtype)
+    inp["dh_final"] = torch.randn(cfg.batch, cfg.dim, 16, generator=g,
+                                  device=DEV)
+    got = gpu_bwd(inp)
+    tol = TOL[cfg.dtype]
+    r = np.random.default_rng(3)
+    chans = _sampled_channels(cfg, r)
+    for b, d in chans:
+        sl = (slice(b, b + 1), slice(d, d + 1))
+        ref = oracle.scan_bwd(inp["u"][sl], inp["delta"][sl], inp["A"][d:d + 1],
+                              inp["B"][b:b + 1], inp["C"][b:b + 1],
+                              inp["D"][d:d + 1], inp["z"][sl],
+                              inp["delta_bias"][d:d + 1], True, inp["h0"][sl],
+                              inp["dy"][sl], inp["dh_final"][sl])
+        for k in ("du", "ddelta", "dz", "dh0"):
+            check(got[k][sl], ref[k], tol, "%s (b=%d, d=%d)" % (k, b, d))
+    # dA, dD, dbias of a channel: sums over the batch of per-channel terms
+    for d in sorted({c[1] for c in chans})[:4]:
+        refs = [oracle.scan_bwd(inp["u"][b:b + 1, d:d + 1],
+                                inp["delta"][b:b + 1, d:d + 1],
+                                inp["A"][d:d + 1], inp["B"][b:b + 1],
+                                inp["C"][b:b + 1], inp["D"][d:d + 1],
+                                inp["z"][b:b + 1, d:d + 1],
+                                inp["delta_bias"][d:d + 1], True,
+                                inp["h0"][b:b + 1, d:d + 1],
+                                inp["dy"][b:b + 1, d:d + 1],
+                                inp["dh_final"][b:b + 1, d:d + 1])
+                for b in range(cfg.batch)]
+        check(got["dA"][d], sum(x["dA"][0] for x in refs), 1e-4, "dA[%d]" % d)
+        check(got["dD"][d:d + 1], np.array([sum(x["dD"][0] for x in refs)]),
+              1e-4, "dD[%d]" % d)
+        check(got["ddelta_bias"][d:d + 1],
+              np.array([sum(x["ddelta_bias"][0] for x in refs)]), 1e-4,
+              "dbias[%d]" % d)
+    assert all(torch.isfinite(v.float()).all() for v in got.values())
+
+
+def test_bwd_channel_sums_by_homogeneity():
+    """dB and dC at a layer's size: y is degree-one homogeneous in (B, h0)
+    apart from the D skip, and in C when no final-state gradient flows, so
+    <dB, B> + <dh0, h0> and <dC, C> equal sum(dy * (y - skip))."""
+    cfg = syn.MAMBA_130M
+    inp = syn.make_scan_inputs(cfg, DEV, with_h0=True)
+    g = torch.Generator(device=DEV).manual_seed(cfg.seed + 6)
+    inp["dy"] = torch.randn(cfg.batch, cfg.dim, cfg.seqlen, generator=g,
+                            device=DEV).to(inp["u"].dtype)
+    inp["dh_final"] = None
+    y, _ = ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"],
+                            inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                            True, inp["h0"])
+    got = gpu_bwd(inp)
+    dy = inp["dy"].double()
+    s = torch.nn.functional.silu(inp["z"].double())
+    skip = inp["D"].double()[None, :, None] * inp["u"].double() * s
+    lhs = float((dy * (y.double() - skip)).sum())
+    rB = float((got["dB"].double() * inp["B"].double()).sum() +
+               (got["dh0"].double() * inp["h0"].double()).sum())
+    rC = float((got["dC"].double() * inp["C"].double()).sum())
+    scale = float((dy.abs() * y.double().abs()).sum())
+    assert abs(lhs - rB) <= 1e-2 * scale, (lhs, rB, scale)
+    assert abs(lhs - rC) <= 1e-2 * scale, (lhs, rC, scale)
