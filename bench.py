@@ -309,6 +309,42 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     del zinp, zy, zhf
     torch.cuda.empty_cache()
 
+    # backward pass of the 2.8B layer (checkpoint pass, reverse sweep,
+    # channel-sum reductions), outputs and workspace allocated up front
+    log("backward on %s" % ccfg.name)
+    binp = syn.make_scan_inputs(ccfg, dev)
+    g = torch.Generator(device=dev).manual_seed(ccfg.seed + 9)
+    bdy = torch.randn(ccfg.batch, ccfg.dim, ccfg.seqlen, generator=g,
+                      device=dev).to(binp["u"].dtype)
+    bws = torch.empty(ssm.ssm_scan_bwd_workspace_size(
+        ccfg.batch, ccfg.dim, 16, ccfg.seqlen), dtype=torch.uint8, device=dev)
+    bout = ssm.ssm_scan_bwd(binp["u"], binp["delta"], binp["A"], binp["B"],
+                            binp["C"], binp["D"], binp["z"], binp["delta_bias"],
+                            True, None, bdy, None, workspace=bws, stream=stream)
+
+    def brun():
+        ssm.ssm_scan_bwd(binp["u"], binp["delta"], binp["A"], binp["B"],
+                         binp["C"], binp["D"], binp["z"], binp["delta_bias"],
+                         True, None, bdy, None, out=bout, workspace=bws,
+                         stream=stream)
+    brun()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        brun()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb = syn.backward_bytes(ccfg)
+    out[ccfg.name + "_backward"] = {
+        "ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+        "elements_per_s": round(ccfg.elements / (ms * 1e-3)),
+        "algorithmic_bytes": nb, "workspace_bytes": bws.numel(),
+        "note": "gradients of u, delta, A, B, C, D, z, bias; states "
+                "recomputed from 1024-token checkpoints"}
+    del binp, bdy, bws, bout
+    torch.cuda.empty_cache()
+
     dcfg = syn.DECODE
     log("decode workload %s" % dcfg.name)
     dinp = syn.make_decode_inputs(dcfg, dev)

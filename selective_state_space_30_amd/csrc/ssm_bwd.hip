@@ -27,9 +27,10 @@
 // checkpoint), folds the reverse maps of its tokens, and a reverse 64-lane
 // scan (lanes reversed with ds_bpermute, then the forward DPP scan) gives
 // each lane the mu entering from its right.  dB and dC are sums over all
-// channels of a batch entry: the 4 channels of a workgroup add theirs into
-// an LDS tile with float atomics, the tile is written as a per-workgroup
-// partial sum, and a reduction kernel sums the partials.
+// channels of a batch entry: after each state the 4 channels of a workgroup
+// write their contributions to LDS, the workgroup sums them in a fixed order
+// (no atomics: deterministic) into a per-workgroup partial sum, and a
+// reduction kernel sums the partials.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,27 +49,36 @@ __device__ __forceinline__ float wave_reverse(float v, int lane) {
       __builtin_amdgcn_ds_bpermute((kWaveLanes - 1 - lane) << 2, __float_as_int(v)));
 }
 
-// Writes the 16-token run of partial sums held at LDS `acc + off` to
-// row[t ..] (16-byte stores when kVec: rows of a multiple of 4 tokens; the
-// partial block through the buffer view), then clears the LDS run for the
-// next phase.
+// Contributions of one state to dB and dC, one region per wave (channel):
+// sR[wave][B|C][token j of a lane run][lane], so a wave writing token j of
+// its 64 runs touches 64 consecutive words (no bank conflicts).
+constexpr int kRegionFloats = kWavesPerGroup * 2 * kTokensPerLane * kWaveLanes;  // 32 KB
+__device__ __forceinline__ int region_index(int wave, int mat, int j, int lane) {
+  return ((wave * 2 + mat) * kTokensPerLane + j) * kWaveLanes + lane;
+}
+
+// After every wave has written its region for state n: thread tid sums the
+// 4 channels' contributions (in channel order) for 8 consecutive tokens of
+// one matrix and writes them to the workgroup's partial-sum row (16-byte
+// stores when kVec; the partial block through the buffer view).
 template <bool kVec, bool kFull>
-__device__ __forceinline__ void flush_run(float *acc, int off, float *row,
-                                          int64_t t0, int64_t t, int64_t tend) {
-  constexpr int K = kTokensPerLane;
-  float4 *src = reinterpret_cast<float4 *>(acc + off);
-  float v[K];
+__device__ __forceinline__ void flush_state(const float *sR, int tid, float *pB_row,
+                                            float *pC_row, int64_t t0, int64_t tend) {
+  constexpr int kHalf = kTokensPerLane / 2;
+  const int mat = tid >> 7;          // threads 0..127: dB, 128..255: dC (wave-uniform)
+  const int r = tid & 127;
+  const int run = r >> 1;            // the lane run (16 tokens) ...
+  const int j0 = (r & 1) * kHalf;    // ... and which half of it
+  float v[kHalf];
 #pragma unroll
-  for (int q = 0; q < K / 4; ++q) {
-    const float4 w = src[q];
-    v[4 * q + 0] = w.x;
-    v[4 * q + 1] = w.y;
-    v[4 * q + 2] = w.z;
-    v[4 * q + 3] = w.w;
+  for (int jj = 0; jj < kHalf; ++jj) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) acc += sR[region_index(w, mat, j0 + jj, run)];
+    v[jj] = acc;
   }
-  store_run<float, K, kVec, kFull>(row, t0, t, tend, v);
-#pragma unroll
-  for (int q = 0; q < K / 4; ++q) src[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float *row = mat ? pC_row : pB_row;
+  store_run<float, kHalf, kVec, kFull>(row, t0, t0 + run * kTokensPerLane + j0, tend, v);
 }
 
 // Per-state values of one channel kept one state per lane (lane n holds
@@ -87,7 +97,7 @@ __device__ __forceinline__ void bwd_block(
     const BwdArgs &p, int wave, int lane, int64_t t0, int64_t tend, int64_t b,
     int64_t bd, int64_t g, const T *__restrict__ Bb, const T *__restrict__ Cb,
     bool ch_ok, float bias, float Dd, float Av, float hfv, float &muv, float &dAv,
-    float &dDl, float &dbl, float *sT, float *sG) {
+    float &dDl, float &dbl, float *sT, float *sR, int tid) {
   constexpr int K = kTokensPerLane;
   constexpr int KP = K + 4;
   constexpr int kPhases = kStates / 2;
@@ -102,7 +112,8 @@ __device__ __forceinline__ void bwd_block(
   const int st = wave >> 1, mat = wave & 1;
   const T *src = mat ? Cb : Bb;
   const int toff = staging_offset(wave, lane);
-  float *prow = (mat ? p.pC : p.pB) + (b * p.groups + g) * kStates * p.L;
+  float *pBg = p.pB + (b * p.groups + g) * kStates * p.L;  // this group's partial rows
+  float *pCg = p.pC + (b * p.groups + g) * kStates * p.L;
   TileRun<T, K, kVec, kFull> run;
   run.load(src + st * p.L, t0, tl, tend);
 
@@ -139,12 +150,8 @@ __device__ __forceinline__ void bwd_block(
 #pragma unroll 1
   for (int ph = 0; ph < kPhases; ++ph) {
     if (ph + 1 < kPhases) run.load(src + (2 * (ph + 1) + st) * p.L, t0, tl, tend);
-    __syncthreads();  // tile ph complete; every wave's atomics of phase ph-1 done
-    if (ph > 0)
-      flush_run<kVec, kFull>(sG + ((ph - 1) & 1) * kTileFloats, toff,
-                             prow + (2 * (ph - 1) + st) * p.L, t0, tl, tend);
+    __syncthreads();  // tile ph complete
     const float *tile = sT + (ph & 1) * kTileFloats;
-    float *acc = sG + (ph & 1) * kTileFloats;
 #pragma unroll
     for (int s2i = 0; s2i < 2; ++s2i) {
       const int n = 2 * ph + s2i;
@@ -152,17 +159,27 @@ __device__ __forceinline__ void bwd_block(
       asm volatile("" : "+s"(An));  // keep this state's work after the previous state's
       const float hfn = state_of(hfv, n);
       const float mun = state_of(muv, n);
-      const float *pb = &tile[((s2i * 2 + 0) * kWaveLanes + lane) * KP];
-      const float *pc = &tile[((s2i * 2 + 1) * kWaveLanes + lane) * KP];
-      float *ab = acc + ((s2i * 2 + 0) * kWaveLanes + lane) * KP;
-      float *ac = acc + ((s2i * 2 + 1) * kWaveLanes + lane) * KP;
+      // this state's B and C for the lane's 16 tokens, read from the tile once
+      float bv[K], cv[K];
+      {
+        const float4 *pb = reinterpret_cast<const float4 *>(
+            &tile[((s2i * 2 + 0) * kWaveLanes + lane) * KP]);
+        const float4 *pc = reinterpret_cast<const float4 *>(
+            &tile[((s2i * 2 + 1) * kWaveLanes + lane) * KP]);
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q) {
+          const float4 x = pb[q], y4 = pc[q];
+          bv[4 * q + 0] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
+          cv[4 * q + 0] = y4.x; cv[4 * q + 1] = y4.y; cv[4 * q + 2] = y4.z; cv[4 * q + 3] = y4.w;
+        }
+      }
       // forward recomputation of this lane's 16 states:
       // hin = the state before the lane's first token, hs[j] = after token j
       float a[K], hs[K];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         a[j] = fast_exp2(dtl[j] * An);
-        hs[j] = du[j] * pb[j];  // dt B u, replaced by the state below
+        hs[j] = du[j] * bv[j];  // dt B u, replaced by the state below
       }
       float H = hs[0];
 #pragma unroll
@@ -184,7 +201,7 @@ __device__ __forceinline__ void bwd_block(
       // 64 lanes composed from the right (reversed lane order, forward scan)
       float M = 0.0f;
 #pragma unroll
-      for (int j = K - 1; j >= 0; --j) M = fmaf(gc[j], pc[j], M) * a[j];
+      for (int j = K - 1; j >= 0; --j) M = fmaf(gc[j], cv[j], M) * a[j];
       float Pr = wave_reverse(Pl, lane);
       float Mr = wave_reverse(M, lane);
       Mr = fmaf(Pr, lane == 0 ? mun : 0.0f, Mr);
@@ -200,26 +217,24 @@ __device__ __forceinline__ void bwd_block(
       float dA_acc = 0.0f;
 #pragma unroll
       for (int j = K - 1; j >= 0; --j) {
-        const float lam = fmaf(gc[j], pc[j], m);
-        s1[j] = fmaf(lam, pb[j], s1[j]);
+        const float lam = fmaf(gc[j], cv[j], m);
+        s1[j] = fmaf(lam, bv[j], s1[j]);
         m = a[j] * lam;                                  // lambda a
         const float q = m * (j > 0 ? hs[j - 1] : hin);   // lambda a h_{j-1}
         s2[j] = fmaf(q, An, s2[j]);
         dA_acc = fmaf(q, dtl[j], dA_acc);
-        if (ch_ok) {
-          atomicAdd(ab + j, lam * du[j]);
-          atomicAdd(ac + j, gc[j] * hs[j]);
-        }
+        sR[region_index(wave, 0, j, lane)] = ch_ok ? lam * du[j] : 0.0f;
+        sR[region_index(wave, 1, j, lane)] = ch_ok ? gc[j] * hs[j] : 0.0f;
       }
       float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
       asm volatile("" : "+s"(dA_sum));
       dAv += lane == n ? dA_sum : 0.0f;
+      __syncthreads();  // every channel's contributions to state n are in sR
+      flush_state<kVec, kFull>(sR, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
+      __syncthreads();  // sR is free for the next state
     }
     if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
   }
-  __syncthreads();  // every wave's atomics of the last phase done
-  flush_run<kVec, kFull>(sG + ((kPhases - 1) & 1) * kTileFloats, toff,
-                         prow + (2 * (kPhases - 1) + st) * p.L, t0, tl, tend);
 
   // per-token gradients
   float uu[K], dr[K];
@@ -249,7 +264,7 @@ void bwd_kernel(BwdArgs p) {
   constexpr int KP = kTokensPerLane + 4;
   constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
   __shared__ float sT[2 * kTileFloats];  // staged B, C (fp32), double-buffered
-  __shared__ float sG[2 * kTileFloats];  // dB, dC of the 4 channels, double-buffered
+  __shared__ float sR[kRegionFloats];    // dB, dC contributions of the 4 channels
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -271,31 +286,19 @@ void bwd_kernel(BwdArgs p) {
   const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
   float dDl = 0.0f, dbl = 0.0f;
 
-  // the partial-sum tiles start at zero; each thread clears the runs it
-  // later flushes
-  {
-    const int off = staging_offset(wave, lane);
-#pragma unroll
-    for (int buf = 0; buf < 2; ++buf) {
-      float4 *z4 = reinterpret_cast<float4 *>(sG + buf * kTileFloats + off);
-#pragma unroll
-      for (int q = 0; q < kTokensPerLane / 4; ++q) z4[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
-  }
-
   const float *ck = p.ckpt + bd * p.nblk * kStates;
   const int64_t nfull = p.L / kBlockTokens;
   if (nfull * kBlockTokens < p.L)  // the partial last block comes first
     bwd_block<T, false, false, kSoftplus>(p, wave, lane, nfull * kBlockTokens, p.L, b, bd, g,
                                           Bb, Cb, ch_ok, bias, Dd, Av,
                                           ck[nfull * kStates + ls], muv, dAv, dDl, dbl, sT,
-                                          sG);
+                                          sR, tid);
 #pragma unroll 1
   for (int64_t k = nfull - 1; k >= 0; --k)
     bwd_block<T, kVec, true, kSoftplus>(p, wave, lane, k * kBlockTokens,
                                         (k + 1) * kBlockTokens, b, bd, g, Bb, Cb, ch_ok, bias,
                                         Dd, Av, ck[k * kStates + ls], muv, dAv, dDl, dbl, sT,
-                                        sG);
+                                        sR, tid);
 
   if (!ch_ok) return;
   if (lane < kStates) {

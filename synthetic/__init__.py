@@ -237,3 +237,20 @@ def decode_step_bytes(cfg: DecodeConfig) -> int:
     by += 2 * cfg.batch * cfg.dstate * elem
     by += cfg.dim * cfg.dstate * 4 + 2 * cfg.dim * 4
     return by
+
+
+def backward_bytes(cfg: ScanConfig) -> int:
+    """Bytes the backward pass must move at least once: u, delta, z and dy
+    read and du, ddelta, dz written (``elem`` bytes each); B and C read; dB
+    and dC written (fp32); A, D, bias read and dA, dD, dbias written; the
+    initial state read and its gradient written when given."""
+    elem = 2 if cfg.dtype == "bf16" else 4
+    e = cfg.elements
+    nz = 1 if cfg.with_z else 0
+    by = e * elem * (3 + 2 * nz + 2)   # u, delta, dy, (z, dz), du, ddelta
+    bnl = cfg.batch * cfg.dstate * cfg.seqlen
+    by += 2 * bnl * elem + 2 * bnl * 4
+    by += 2 * cfg.dim * cfg.dstate * 4 + 4 * cfg.dim * 4
+    if cfg.with_h0:
+        by += 2 * cfg.batch * cfg.dim * cfg.dstate * 4
+    return by

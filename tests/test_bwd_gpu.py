@@ -109,15 +109,14 @@ def test_bwd_zero_gradient_in_gives_zero_out():
         assert torch.count_nonzero(v) == 0, k
 
 
-def test_bwd_deterministic_except_atomic_sums():
+def test_bwd_bitwise_deterministic():
+    """Every sum is taken in a fixed order (no atomics), so a repeated call
+    gives the same bits."""
     inp = to_dev(make(2, 24, 2500, "bf16", 10))
     g1 = gpu_bwd(inp)
     g2 = gpu_bwd(inp)
     for k in g1:
-        if k in ("dB", "dC"):  # four channels meet in LDS float atomics
-            check(g2[k], g1[k].double(), 1e-6, k)
-        else:
-            assert torch.equal(g1[k], g2[k]), k
+        assert torch.equal(g1[k], g2[k]), k
 
 
 def _sampled_channels(cfg, r, k=8):
