@@ -178,8 +178,9 @@ int ssm_state_update(float *state, const void *x, const void *delta,
 
 /* Bytes of caller-provided device workspace ssm_scan_bwd needs for this
  * shape: the block-start checkpoints (batch*dim*ceil(seqlen/1024)*16 fp32)
- * and per-workgroup partial sums of dB and dC (2 * batch*ceil(dim/4)*16*
- * seqlen fp32), plus per-channel partials of dA, dD and the bias. */
+ * and per-workgroup partial sums of dB and dC (2 * batch*ceil(dim/8)*16*
+ * seqlen fp32: a workgroup holds 8 channels), plus per-channel partials of
+ * dA, dD and the bias. */
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                 int64_t seqlen, size_t *bytes);
 

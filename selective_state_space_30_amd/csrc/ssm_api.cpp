@@ -99,7 +99,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t bd = static_cast<size_t>(batch) * dim;
   const size_t nblk = static_cast<size_t>((seqlen + kBlockTokens - 1) / kBlockTokens);
-  const size_t groups = static_cast<size_t>((dim + kChannelsPerGroup - 1) / kChannelsPerGroup);
+  const size_t groups = static_cast<size_t>((dim + kBwdWaves - 1) / kBwdWaves);
   const size_t part = static_cast<size_t>(batch) * groups * kStates * seqlen * sizeof(float);
   BwdLayout l;
   l.off_ckpt = 0;
@@ -368,11 +368,15 @@ namespace {
 int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
   int st = check_sizes(batch, dim, dstate, seqlen);
   if (st != SSM_OK) return st;
-  const int64_t groups = (dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
+  const int64_t groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
   int64_t e;
   if (groups >= (int64_t(1) << 31) || !mul_ok(batch * groups, ssm::kStates * seqlen, &e) ||
       !mul_ok(e, 8, &e))
     return fail(SSM_ERR_UNSUPPORTED, "backward workspace of this shape overflows");
+  // the channel-sum reduction launches one workgroup per 256 tokens of each
+  // (batch, state) row
+  if (batch * ssm::kStates * ((seqlen + 255) / 256) >= (int64_t(1) << 31))
+    return fail(SSM_ERR_UNSUPPORTED, "batch*seqlen too large for the backward reduction");
   return SSM_OK;
 }
 
@@ -491,7 +495,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   a.pbias = reinterpret_cast<float *>(w + l.off_pbias);
   a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dbias = ddelta_bias;
   a.batch = batch; a.dim = dim; a.L = seqlen;
-  a.groups = (dim + ssm::kChannelsPerGroup - 1) / ssm::kChannelsPerGroup;
+  a.groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
   a.nblk = static_cast<int>((seqlen + ssm::kBlockTokens - 1) / ssm::kBlockTokens);
   a.softplus = fa.softplus;
   err = ssm::launch_bwd(a, bf16, vec, stream);

@@ -20,14 +20,14 @@
 //   ddt_t += lambda (B u + A a h_{t-1}),  dA_n += lambda a h_{t-1} dt_t,
 //   dB_{t,n} += lambda dt u,  du_t += lambda dt B,  dC_{t,n} += gc_t h_t.
 //
-// Work layout, as in the forward kernel: one wave = one channel, a
-// workgroup = 4 channels of one batch entry, a lane = 16 consecutive tokens;
+// Work layout: one wave = one channel, a workgroup = 8 channels of one
+// batch entry (2 waves per SIMD), a lane = 16 consecutive tokens;
 // blocks are visited from the last to the first.  For each state the lane
 // recomputes its 16 states (fold, 64-lane scan, replay from the block's
 // checkpoint), folds the reverse maps of its tokens, and a reverse 64-lane
 // scan (lanes reversed with ds_bpermute, then the forward DPP scan) gives
 // each lane the mu entering from its right.  dB and dC are sums over all
-// channels of a batch entry: after each state the 4 channels of a workgroup
+// channels of a batch entry: after each state the 8 channels of a workgroup
 // write their contributions to LDS, the workgroup sums them in a fixed order
 // (no atomics: deterministic) into a per-workgroup partial sum, and a
 // reduction kernel sums the partials.
@@ -49,36 +49,39 @@ __device__ __forceinline__ float wave_reverse(float v, int lane) {
       __builtin_amdgcn_ds_bpermute((kWaveLanes - 1 - lane) << 2, __float_as_int(v)));
 }
 
+constexpr int kBwdThreads = kBwdWaves * kWaveLanes;
+
 // Contributions of one state to dB and dC, one region per wave (channel):
 // sR[wave][B|C][token j of a lane run][lane], so a wave writing token j of
 // its 64 runs touches 64 consecutive words (no bank conflicts).
-constexpr int kRegionFloats = kWavesPerGroup * 2 * kTokensPerLane * kWaveLanes;  // 32 KB
+constexpr int kRegionFloats = kBwdWaves * 2 * kTokensPerLane * kWaveLanes;  // 64 KB
 __device__ __forceinline__ int region_index(int wave, int mat, int j, int lane) {
   return ((wave * 2 + mat) * kTokensPerLane + j) * kWaveLanes + lane;
 }
 
 // After every wave has written its region for state n: thread tid sums the
-// 4 channels' contributions (in channel order) for 8 consecutive tokens of
-// one matrix and writes them to the workgroup's partial-sum row (16-byte
-// stores when kVec; the partial block through the buffer view).
+// channels' contributions (in channel order) for 4 consecutive tokens of one
+// matrix and writes them to the workgroup's partial-sum row (a 16-byte
+// store when kVec; the partial block through the buffer view).
 template <bool kVec, bool kFull>
 __device__ __forceinline__ void flush_state(const float *sR, int tid, float *pB_row,
                                             float *pC_row, int64_t t0, int64_t tend) {
-  constexpr int kHalf = kTokensPerLane / 2;
-  const int mat = tid >> 7;          // threads 0..127: dB, 128..255: dC (wave-uniform)
-  const int r = tid & 127;
-  const int run = r >> 1;            // the lane run (16 tokens) ...
-  const int j0 = (r & 1) * kHalf;    // ... and which half of it
-  float v[kHalf];
+  constexpr int kPer = 2 * kTokensPerLane * kWaveLanes / kBwdThreads;  // 4
+  constexpr int kParts = kTokensPerLane / kPer;                        // per run
+  const int mat = tid / (kBwdThreads / 2);  // first half: dB, second: dC (wave-uniform)
+  const int r = tid % (kBwdThreads / 2);
+  const int run = r / kParts;               // the lane run (16 tokens) ...
+  const int j0 = (r % kParts) * kPer;       // ... and which part of it
+  float v[kPer];
 #pragma unroll
-  for (int jj = 0; jj < kHalf; ++jj) {
+  for (int jj = 0; jj < kPer; ++jj) {
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w) acc += sR[region_index(w, mat, j0 + jj, run)];
+    for (int w = 0; w < kBwdWaves; ++w) acc += sR[region_index(w, mat, j0 + jj, run)];
     v[jj] = acc;
   }
   float *row = mat ? pC_row : pB_row;
-  store_run<float, kHalf, kVec, kFull>(row, t0, t0 + run * kTokensPerLane + j0, tend, v);
+  store_run<float, kPer, kVec, kFull>(row, t0, t0 + run * kTokensPerLane + j0, tend, v);
 }
 
 // Per-state values of one channel kept one state per lane (lane n holds
@@ -108,14 +111,18 @@ __device__ __forceinline__ void bwd_block(
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
   const T *gyrow = static_cast<const T *>(p.dy) + bd * p.L;
 
-  // staging / flushing role of this wave: state (2*ph + st), matrix mat
-  const int st = wave >> 1, mat = wave & 1;
+  // staging role of this wave: state (2*ph + st) of matrix mat, half `half`
+  // of every lane run (8 tokens per lane)
+  constexpr int kHalfRun = K / 2;
+  const int row = wave & 3, half = wave >> 2;
+  const int st = row >> 1, mat = row & 1;
   const T *src = mat ? Cb : Bb;
-  const int toff = staging_offset(wave, lane);
+  const int toff = (row * kWaveLanes + lane) * KP + half * kHalfRun;
+  const int64_t tq = tl + half * kHalfRun;
   float *pBg = p.pB + (b * p.groups + g) * kStates * p.L;  // this group's partial rows
   float *pCg = p.pC + (b * p.groups + g) * kStates * p.L;
-  TileRun<T, K, kVec, kFull> run;
-  run.load(src + st * p.L, t0, tl, tend);
+  TileRun<T, kHalfRun, kVec, kFull> run;
+  run.load(src + st * p.L, t0, tq, tend);
 
   // per token: dt (as dt*log2 e), dt*u, the gated output gradient gc and
   // the sums over states s1 = sum lambda B, s2 = sum lambda a h_prev A
@@ -149,7 +156,7 @@ __device__ __forceinline__ void bwd_block(
 
 #pragma unroll 1
   for (int ph = 0; ph < kPhases; ++ph) {
-    if (ph + 1 < kPhases) run.load(src + (2 * (ph + 1) + st) * p.L, t0, tl, tend);
+    if (ph + 1 < kPhases) run.load(src + (2 * (ph + 1) + st) * p.L, t0, tq, tend);
     __syncthreads();  // tile ph complete
     const float *tile = sT + (ph & 1) * kTileFloats;
 #pragma unroll
@@ -258,8 +265,7 @@ __device__ __forceinline__ void bwd_block(
 }
 
 template <typename T, bool kVec, bool kSoftplus>
-__global__ __launch_bounds__(kWaveLanes * kWavesPerGroup)
-__attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs p) {
   constexpr int KP = kTokensPerLane + 4;
   constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
@@ -271,7 +277,7 @@ void bwd_kernel(BwdArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t b = blockIdx.y;
   const int64_t g = blockIdx.x;
-  const int64_t d_raw = g * kChannelsPerGroup + wave;
+  const int64_t d_raw = g * kBwdWaves + wave;
   const bool ch_ok = d_raw < p.dim;
   const int64_t d = ch_ok ? d_raw : p.dim - 1;  // clamped for reads
   const int64_t bd = b * p.dim + d;
@@ -314,33 +320,58 @@ void bwd_kernel(BwdArgs p) {
   }
 }
 
-// dB[b, n, t] = sum over groups of the partial sums (dC alike); one thread
-// per four consecutive tokens.
-__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdArgs p) {
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t L4 = (p.L + 3) / 4;
-  const int64_t total = p.batch * kStates * L4;
-  if (q >= total) return;
-  const int mat = blockIdx.y;
-  const int64_t b = q / (kStates * L4);
-  const int64_t rem = q - b * kStates * L4;
-  const int64_t n = rem / L4;
-  const int64_t t = (rem - n * L4) * 4;
-  const float *part = (mat ? p.pC : p.pB) + (b * p.groups * kStates + n) * p.L + t;
-  float *out = (mat ? p.dC : p.dB) + (b * kStates + n) * p.L + t;
-  const int64_t stride = kStates * p.L;
-  const int cnt = p.L - t < 4 ? static_cast<int>(p.L - t) : 4;
-  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+// dB[b, n, t] (blockIdx.y = 0) or dC (1): the sum over channel groups of
+// the partial rows.  A workgroup takes 256 consecutive tokens (64 lanes x 4)
+// of one (b, n) row; its 4 waves take every 4th group (16-byte loads, 1 KB
+// per wave and group) and add up in LDS at the end.
+constexpr int kReduceWaves = 4;
+constexpr int kReduceTokens = 4 * kWaveLanes;  // per workgroup
+__global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kernel(BwdArgs p) {
+  __shared__ float4 red[kReduceWaves - 1][kWaveLanes];
+  const int lane = threadIdx.x & 63;
+  const int slice = threadIdx.x >> 6;
+  const int64_t ntb = (p.L + kReduceTokens - 1) / kReduceTokens;
+  const int64_t row = blockIdx.x / ntb;  // b * 16 + n
+  const int64_t t = (blockIdx.x - row * ntb) * kReduceTokens + lane * 4;
+  const int64_t b = row / kStates, n = row - b * kStates;
+  const float *part = (blockIdx.y ? p.pC : p.pB) + (b * p.groups * kStates + n) * p.L;
+  const int64_t gstride = kStates * p.L;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if ((p.L & 3) == 0 && t < p.L) {
+    const float *q = part + t;
 #pragma unroll 4
-  for (int64_t gi = 0; gi < p.groups; ++gi) {
-    const float *r = part + gi * stride;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i < cnt) s[i] += r[i];
+    for (int64_t gi = slice; gi < p.groups; gi += kReduceWaves) {
+      const float4 v = *reinterpret_cast<const float4 *>(q + gi * gstride);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  } else if (t < p.L) {
+    const int cnt = p.L - t < 4 ? static_cast<int>(p.L - t) : 4;
+    for (int64_t gi = slice; gi < p.groups; gi += kReduceWaves) {
+      const float *q = part + gi * gstride + t;
+      acc.x += q[0];
+      if (cnt > 1) acc.y += q[1];
+      if (cnt > 2) acc.z += q[2];
+      if (cnt > 3) acc.w += q[3];
+    }
   }
+  if (slice > 0) red[slice - 1][lane] = acc;
+  __syncthreads();
+  if (slice != 0 || t >= p.L) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i < cnt) out[i] = s[i];
+  for (int i = 0; i < kReduceWaves - 1; ++i) {
+    acc.x += red[i][lane].x; acc.y += red[i][lane].y;
+    acc.z += red[i][lane].z; acc.w += red[i][lane].w;
+  }
+  float *out = (blockIdx.y ? p.dC : p.dB) + row * p.L + t;
+  if ((p.L & 3) == 0) {
+    *reinterpret_cast<float4 *>(out) = acc;
+  } else {
+    const int cnt = p.L - t < 4 ? static_cast<int>(p.L - t) : 4;
+    out[0] = acc.x;
+    if (cnt > 1) out[1] = acc.y;
+    if (cnt > 2) out[2] = acc.z;
+    if (cnt > 3) out[3] = acc.w;
+  }
 }
 
 // dA[d, n], dD[d], dbias[d]: sums over the batch of the per-(b, d) partials.
@@ -366,16 +397,14 @@ template <typename T, bool kVec>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.groups), static_cast<unsigned>(a.batch));
   if (a.softplus)
-    hipLaunchKernelGGL((bwd_kernel<T, kVec, true>), grid, dim3(kWaveLanes * kWavesPerGroup),
-                       0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<T, kVec, true>), grid, dim3(kBwdThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_kernel<T, kVec, false>), grid, dim3(kWaveLanes * kWavesPerGroup),
-                       0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<T, kVec, false>), grid, dim3(kBwdThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nq = a.batch * kStates * ((a.L + 3) / 4);
-  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>((nq + 255) / 256), 2),
-                     dim3(256), 0, s, a);
+  const int64_t nwg = a.batch * kStates * ((a.L + kReduceTokens - 1) / kReduceTokens);
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>(nwg), 2), dim3(256), 0,
+                     s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_param_kernel,

@@ -16,6 +16,7 @@ constexpr int kTokensPerLane = 16;   // consecutive tokens owned by one lane
 constexpr int kBlockTokens = kWaveLanes * kTokensPerLane;         // 1024
 constexpr int kPhaseStates = 2;      // states per double-buffered B/C LDS tile
 constexpr int kMaxConv = 4;          // taps of the fused causal conv1d prologue
+constexpr int kBwdWaves = 8;         // waves (channels) per backward workgroup
 
 struct ScanArgs {
   const void *u, *delta, *B, *C, *z;  // activations (dtype); u null with conv
@@ -41,8 +42,8 @@ struct ScanArgs {
                                       // yc the pre-gate output
 };
 
-// Backward pass.  Per-workgroup partial sums (a workgroup = 4 channels of
-// one batch entry) are reduced by a second kernel.
+// Backward pass.  Per-workgroup partial sums (a workgroup = kBwdWaves
+// channels of one batch entry) are reduced by a second kernel.
 struct BwdArgs {
   const void *u, *delta, *B, *C, *z, *dy;  // activation dtype
   const float *A, *D, *bias, *h0, *dh_final;
@@ -55,7 +56,7 @@ struct BwdArgs {
   float *pD, *pbias;                  // (batch, dim) partial dD, dbias
   float *dA, *dB, *dC, *dD, *dbias;   // reduced outputs (dD, dbias: or null)
   int64_t batch, dim, L;
-  int64_t groups;                     // ceil(dim / 4)
+  int64_t groups;                     // ceil(dim / kBwdWaves)
   int nblk;                           // ceil(L / 1024)
   int softplus;
 };

@@ -281,7 +281,7 @@ def test_bwd_rejects_invalid_arguments(lib, name, kw, status):
 def test_bwd_workspace_size(lib):
     size = ctypes.c_size_t(0)
     assert lib.ssm_scan_bwd_workspace_size(2, 5120, 16, 4096, ctypes.byref(size)) == 0
-    groups = 5120 // 4
+    groups = 5120 // 8  # channels per backward workgroup
     partials = 2 * (2 * groups * 16 * 4096 * 4)
     checkpoints = 2 * 5120 * 4 * 16 * 4
     assert partials + checkpoints <= size.value < partials + checkpoints + 2 * 2**20
