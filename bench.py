@@ -317,7 +317,8 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     bdy = torch.randn(ccfg.batch, ccfg.dim, ccfg.seqlen, generator=g,
                       device=dev).to(binp["u"].dtype)
     bws = torch.empty(ssm.ssm_scan_bwd_workspace_size(
-        ccfg.batch, ccfg.dim, 16, ccfg.seqlen), dtype=torch.uint8, device=dev)
+        ccfg.batch, ccfg.dim, 16, ccfg.seqlen, binp["u"].dtype),
+        dtype=torch.uint8, device=dev)
     bout = ssm.ssm_scan_bwd(binp["u"], binp["delta"], binp["A"], binp["B"],
                             binp["C"], binp["D"], binp["z"], binp["delta_bias"],
                             True, None, bdy, None, workspace=bws, stream=stream)
@@ -395,8 +396,9 @@ def cpu_baseline(inp, cfg, nbytes, log):
             "elements_per_s": round(cfg.elements / sec)}
 
 
-# bf16 activations, vector loads, softplus on, no conv prologue, Euler input
-SCAN_KERNEL = "scan_kernel<unsigned short, true, true, false, false>"
+# bf16 activations, vector loads, softplus on, no conv prologue, Euler input,
+# not the checkpoint pass
+SCAN_KERNEL = "scan_kernel<unsigned short, true, true, false, false, false>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30  # each calibration copy reads and writes 1 GiB
 

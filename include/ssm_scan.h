@@ -177,12 +177,13 @@ int ssm_state_update(float *state, const void *x, const void *delta,
                      int64_t dstate, int dtype, void *stream);
 
 /* Bytes of caller-provided device workspace ssm_scan_bwd needs for this
- * shape: the block-start checkpoints (batch*dim*ceil(seqlen/1024)*16 fp32)
- * and per-workgroup partial sums of dB and dC (2 * batch*ceil(dim/8)*16*
- * seqlen fp32: a workgroup holds 8 channels), plus per-channel partials of
- * dA, dD and the bias. */
+ * shape and activation dtype: the block-start checkpoints
+ * (batch*dim*ceil(seqlen/1024)*16 fp32), the pre-gate output (batch*dim*
+ * seqlen, activation dtype), per-workgroup partial sums of dB and dC
+ * (2 * batch*ceil(dim/8)*16*seqlen fp32: a workgroup holds 8 channels), and
+ * per-channel partials of dA, dD and the bias. */
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
-                                int64_t seqlen, size_t *bytes);
+                                int64_t seqlen, int dtype, size_t *bytes);
 
 /* Backward pass of ssm_scan_fwd with the Euler input term: the gradients of
  * a scalar loss with respect to every input, given its gradient dy with

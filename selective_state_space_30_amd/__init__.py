@@ -87,7 +87,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                          I64, I64, I64, I, P]
         lib.ssm_state_update.restype = I
         lib.ssm_scan_bwd_workspace_size.argtypes = [
-            I64, I64, I64, I64, ctypes.POINTER(ctypes.c_size_t)]
+            I64, I64, I64, I64, I, ctypes.POINTER(ctypes.c_size_t)]
         lib.ssm_scan_bwd_workspace_size.restype = I
         lib.ssm_scan_bwd.argtypes = ([P] * 8 + [U] + [P] * 12 +
                                      [I64, I64, I64, I64, I, P,
@@ -334,10 +334,12 @@ def bind_state_update(state, x, delta, A, B, C, D=None, z=None,
     return call
 
 
-def ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen) -> int:
+def ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen,
+                                dtype=torch.bfloat16) -> int:
     out = ctypes.c_size_t(0)
+    code = SSM_DTYPE_BF16 if dtype == torch.bfloat16 else SSM_DTYPE_F32
     _check(load_library().ssm_scan_bwd_workspace_size(
-        batch, dim, dstate, seqlen, ctypes.byref(out)))
+        batch, dim, dstate, seqlen, code, ctypes.byref(out)))
     return out.value
 
 
@@ -375,7 +377,7 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         if k not in out:
             out[k] = torch.empty(shp, dtype=dt, device=dev)
     p = {k: _ptr(out[k], k, shapes[k][1], shapes[k][0], dev) for k in shapes}
-    ws_bytes = ssm_scan_bwd_workspace_size(batch, dim, N, L)
+    ws_bytes = ssm_scan_bwd_workspace_size(batch, dim, N, L, act)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     wsn = workspace.numel() * workspace.element_size()

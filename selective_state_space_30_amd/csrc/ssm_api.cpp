@@ -95,7 +95,7 @@ int64_t choose_chunk(int64_t batch, int64_t dim, int64_t seqlen, int64_t request
 }  // namespace
 
 namespace ssm {
-BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen) {
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t elem_bytes) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t bd = static_cast<size_t>(batch) * dim;
   const size_t nblk = static_cast<size_t>((seqlen + kBlockTokens - 1) / kBlockTokens);
@@ -103,7 +103,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen) {
   const size_t part = static_cast<size_t>(batch) * groups * kStates * seqlen * sizeof(float);
   BwdLayout l;
   l.off_ckpt = 0;
-  l.off_pB = up(l.off_ckpt + bd * nblk * kStates * sizeof(float));
+  l.off_yc = up(l.off_ckpt + bd * nblk * kStates * sizeof(float));
+  l.off_pB = up(l.off_yc + bd * static_cast<size_t>(seqlen) * elem_bytes);
   l.off_pC = up(l.off_pB + part);
   l.off_pA = up(l.off_pC + part);
   l.off_pD = up(l.off_pA + bd * kStates * sizeof(float));
@@ -385,11 +386,13 @@ int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) 
 extern "C" {
 
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
-                                int64_t seqlen, size_t *bytes) {
+                                int64_t seqlen, int dtype, size_t *bytes) {
   if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
+  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int st = check_bwd_sizes(batch, dim, dstate, seqlen);
   if (st != SSM_OK) return st;
-  *bytes = ssm::bwd_layout(batch, dim, seqlen).total_bytes;
+  *bytes = ssm::bwd_layout(batch, dim, seqlen, dtype == SSM_DTYPE_BF16 ? 2 : 4).total_bytes;
   return ok();
 }
 
@@ -446,7 +449,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
         return fail(SSM_ERR_INVALID_ARG, "%s overlaps %s", o.name, o2.name);
   }
 
-  const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen);
+  const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen, es);
   if (!workspace || workspace_bytes < l.total_bytes)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu bytes at %p)",
                 l.total_bytes, workspace_bytes, workspace);
@@ -466,13 +469,14 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   char *w = static_cast<char *>(workspace);
   float *ckpt = reinterpret_cast<float *>(w + l.off_ckpt);
 
-  // 1. checkpoint pass: the forward scan keeping only block-start states
-  //    (and forming dz, which needs the pre-gate output)
+  void *yc = w + l.off_yc;
+
+  // 1. checkpoint pass: the forward scan without the gate, keeping the
+  //    block-start states and the pre-gate output (for dz)
   ssm::ScanArgs fa{};
-  fa.u = u; fa.delta = delta; fa.B = B; fa.C = C; fa.z = z;
-  fa.dy = dy; fa.dz = dz;  // the gate's gradient needs the pre-gate output
+  fa.u = u; fa.delta = delta; fa.B = B; fa.C = C; fa.z = nullptr;
   fa.A = A; fa.D = D; fa.bias = delta_bias; fa.h0 = h0;
-  fa.y = nullptr; fa.h_final = nullptr;
+  fa.y = yc; fa.h_final = nullptr;
   fa.batch = batch; fa.dim = dim; fa.L = seqlen;
   fa.chunk_len = seqlen; fa.n_chunks = 1;
   fa.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
@@ -486,7 +490,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   ssm::BwdArgs a{};
   a.u = u; a.delta = delta; a.B = B; a.C = C; a.z = z; a.dy = dy;
   a.A = A; a.D = D; a.bias = delta_bias; a.h0 = h0; a.dh_final = dh_final;
-  a.ckpt = ckpt;
+  a.ckpt = ckpt; a.yc = yc; a.dz = dz;
   a.du = du; a.ddelta = ddelta; a.dh0 = dh0;
   a.pB = reinterpret_cast<float *>(w + l.off_pB);
   a.pC = reinterpret_cast<float *>(w + l.off_pC);

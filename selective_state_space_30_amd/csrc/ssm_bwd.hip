@@ -262,6 +262,18 @@ __device__ __forceinline__ void bwd_block(
     store_run<T, K, kVec, kFull>(static_cast<T *>(p.du) + bd * p.L, t0, tl, tend, s1);
     store_run<T, K, kVec, kFull>(static_cast<T *>(p.ddelta) + bd * p.L, t0, tl, tend, s2);
   }
+  if (zrow && p.dz) {
+    // the gate: dz = dy * yc * silu'(z), yc the pre-gate output the
+    // checkpoint pass stored
+    float zz[K], gy[K], yv[K];
+    load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
+    load_run<T, K, kVec, kFull>(gyrow, t0, tl, tend, gy);
+    load_run<T, K, kVec, kFull>(static_cast<const T *>(p.yc) + bd * p.L, t0, tl, tend, yv);
+#pragma unroll
+    for (int j = 0; j < K; ++j) yv[j] = gy[j] * yv[j] * dsilu_f(zz[j]);
+    if (ch_ok)
+      store_run<T, K, kVec, kFull>(static_cast<T *>(p.dz) + bd * p.L, t0, tl, tend, yv);
+  }
 }
 
 template <typename T, bool kVec, bool kSoftplus>

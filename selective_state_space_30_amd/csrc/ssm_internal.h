@@ -34,12 +34,9 @@ struct ScanArgs {
   int n_chunks;
   int softplus;                       // 1: dt = softplus(delta + bias)
   int zoh;                            // 1: exact ZOH input term
-  float *ckpt;                        // or null: state at every block start,
-                                      // (batch, dim, ceil(L/1024), 16); y may
-                                      // then be null (nothing is stored)
-  const void *dy;                     // checkpoint pass with y null: with dy
-  void *dz;                           // and z given, dz = dy * yc * silu'(z),
-                                      // yc the pre-gate output
+  float *ckpt;                        // backward's checkpoint pass: the state
+                                      // at every block start, (batch, dim,
+                                      // ceil(L/1024), 16)
 };
 
 // Backward pass.  Per-workgroup partial sums (a workgroup = kBwdWaves
@@ -48,8 +45,9 @@ struct BwdArgs {
   const void *u, *delta, *B, *C, *z, *dy;  // activation dtype
   const float *A, *D, *bias, *h0, *dh_final;
   const float *ckpt;                  // (batch, dim, nblk, 16) forward states
-  void *du, *ddelta;                  // activation dtype outputs (dz is
-                                      // formed by the checkpoint pass)
+  const void *yc;                     // (batch, dim, L) pre-gate output, dtype
+  void *dz;                           // activation dtype output, or null
+  void *du, *ddelta;                  // activation dtype outputs
   float *dh0;                         // (batch, dim, 16) or null
   float *pB, *pC;                     // (batch, groups, 16, L) partial dB, dC
   float *pA;                          // (batch, dim, 16) partial dA
@@ -86,9 +84,9 @@ int launch_bwd(const BwdArgs &a, bool bf16, bool vec, void *stream);
 
 // Workspace layout of the backward pass, in bytes, each part 256-aligned.
 struct BwdLayout {
-  size_t off_ckpt, off_pB, off_pC, off_pA, off_pD, off_pbias, total_bytes;
+  size_t off_ckpt, off_yc, off_pB, off_pC, off_pA, off_pD, off_pbias, total_bytes;
 };
-BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen);
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t elem_bytes);
 const char *hip_error_string(int err);
 
 }  // namespace ssm

@@ -181,21 +181,6 @@ __device__ __forceinline__ void scan_block(
     if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
   }
 
-  if (!yrow) {  // checkpoint pass of the backward: states, and the gate's gradient
-    if (zrow && p.dz) {
-      const int64_t roff = zrow - static_cast<const T *>(p.z);  // this channel's row
-      const T *gyrow = static_cast<const T *>(p.dy) + roff;
-      float zz[K], gy[K];
-      load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
-      load_run<T, K, kVec, kFull>(gyrow, t0, tl, tend, gy);
-#pragma unroll
-      for (int j = 0; j < K; ++j) y[j] = gy[j] * y[j] * dsilu_f(zz[j]);
-      if (ch_ok)
-        store_run<T, K, kVec, kFull>(static_cast<T *>(p.dz) + roff, t0, tl, tend, y);
-    }
-    sdt_total += sdt;
-    return;
-  }
   if (zrow) {
     float zz[K];
     load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
@@ -215,7 +200,7 @@ __device__ __forceinline__ void scan_block(
 template <typename T, bool kVec, bool kZoh>
 constexpr int kOccupancy = (sizeof(T) == 2 && kVec && !kZoh) ? 4 : 3;
 
-template <typename T, bool kVec, bool kSoftplus, bool kConv, bool kZoh>
+template <typename T, bool kVec, bool kSoftplus, bool kConv, bool kZoh, bool kCkpt = false>
 __global__ __launch_bounds__(kWaveLanes * kWavesPerGroup)
 __attribute__((amdgpu_waves_per_eu(kOccupancy<T, kVec, kZoh>)))
 void scan_kernel(ScanArgs p) {
@@ -247,7 +232,7 @@ void scan_kernel(ScanArgs p) {
   const T *urow = static_cast<const T *>(kConv ? p.x : p.u) + bd * p.L;
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
-  T *yrow = p.y ? static_cast<T *>(p.y) + bd * p.L : nullptr;
+  T *yrow = static_cast<T *>(p.y) + bd * p.L;
   const T *Bb = static_cast<const T *>(p.B) + b * kStates * p.L;
   const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
   float sdt_total = 0.0f;
@@ -268,15 +253,15 @@ void scan_kernel(ScanArgs p) {
     xc[k] = (kConv && t >= 0) ? to_f32<T>(urow[t]) : 0.0f;
   }
 
-  // checkpoint pass (unsplit sequences only): the state entering block k
-  // goes to ckpt[b, d, k, :]
+  // checkpoint pass of the backward (kCkpt; unsplit sequences, no gate, y =
+  // the pre-gate output): the state entering block k goes to ckpt[b, d, k, :]
   const int64_t nblk = (p.L + kBlockTokens - 1) / kBlockTokens;
-  float *ck = (p.ckpt && ch_ok) ? p.ckpt + bd * nblk * kStates : nullptr;
+  float *ck = (kCkpt && ch_ok) ? p.ckpt + bd * nblk * kStates : nullptr;
 
   int64_t t0 = ct0;
 #pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens) {
-    if (ck && lane == 0) {
+    if (kCkpt && ck && lane == 0) {
 #pragma unroll
       for (int n = 0; n < kStates; ++n)
         ck[(t0 / kBlockTokens) * kStates + n] = hc[n];
@@ -285,7 +270,7 @@ void scan_kernel(ScanArgs p) {
                                                drow, zrow, yrow, ch_ok, bias, Dd, Ach,
                                                sT, hc, sdt_total, wc, cb, xc);
   }
-  if (t0 < ct1 && ck && lane == 0) {
+  if (kCkpt && t0 < ct1 && ck && lane == 0) {
 #pragma unroll
     for (int n = 0; n < kStates; ++n) ck[(t0 / kBlockTokens) * kStates + n] = hc[n];
   }
@@ -365,7 +350,7 @@ __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
   const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
-  T *yrow = p.y ? static_cast<T *>(p.y) + bd * p.L : nullptr;
+  T *yrow = static_cast<T *>(p.y) + bd * p.L;
   float S = 0.0f;
   for (int64_t t0 = ct0; t0 < ct1; t0 += 64) {
     const int64_t t = t0 + lane;
@@ -473,7 +458,12 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
       scan_kernel<T, kVec, false, false, true>,  scan_kernel<T, kVec, true, false, true>,
       scan_kernel<T, kVec, false, true, true>,   scan_kernel<T, kVec, true, true, true>};
   const int which = (a.softplus ? 1 : 0) | (a.x ? 2 : 0) | (a.zoh ? 4 : 0);
-  hipLaunchKernelGGL(kernels[which], grid, dim3(kWaveLanes * kWavesPerGroup), 0, s, a);
+  // the backward's checkpoint pass (Euler, no conv prologue, unsplit) has
+  // instances of its own, so the forward instances carry none of its code
+  static constexpr KernelFn ckpt_kernels[2] = {scan_kernel<T, kVec, false, false, false, true>,
+                                               scan_kernel<T, kVec, true, false, false, true>};
+  hipLaunchKernelGGL(a.ckpt ? ckpt_kernels[a.softplus ? 1 : 0] : kernels[which], grid,
+                     dim3(kWaveLanes * kWavesPerGroup), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
   const int64_t nthreads = a.batch * a.dim * kStates;

@@ -235,7 +235,7 @@ def _bwd(lib, **kw):
              dD=None, dbias=None, dz=None, dh0=None, batch=1, dim=16,
              dstate=16, seqlen=256, dtype=ssm.SSM_DTYPE_F32, stream=None)
     size = ctypes.c_size_t(0)
-    assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, ctypes.byref(size)) == 0
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 0, ctypes.byref(size)) == 0
     a["ws_bytes"] = size.value
     a.update(kw)
     return lib.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"],
@@ -280,10 +280,13 @@ def test_bwd_rejects_invalid_arguments(lib, name, kw, status):
 
 def test_bwd_workspace_size(lib):
     size = ctypes.c_size_t(0)
-    assert lib.ssm_scan_bwd_workspace_size(2, 5120, 16, 4096, ctypes.byref(size)) == 0
+    assert lib.ssm_scan_bwd_workspace_size(2, 5120, 16, 4096, 1, ctypes.byref(size)) == 0
     groups = 5120 // 8  # channels per backward workgroup
     partials = 2 * (2 * groups * 16 * 4096 * 4)
     checkpoints = 2 * 5120 * 4 * 16 * 4
-    assert partials + checkpoints <= size.value < partials + checkpoints + 2 * 2**20
-    assert lib.ssm_scan_bwd_workspace_size(1, 16, 8, 256, ctypes.byref(size)) == 2
-    assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, None) == 1
+    pregate = 2 * 5120 * 4096 * 2  # bf16
+    assert partials + checkpoints + pregate <= size.value < (
+        partials + checkpoints + pregate + 2 * 2**20)
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 7, ctypes.byref(size)) == 1
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 8, 256, 0, ctypes.byref(size)) == 2
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 0, None) == 1
