@@ -20,6 +20,9 @@ and state at a time).  This module only marshals numpy arrays into it:
   Complet's section 4 architecture figure and section 7 block).
 * :func:`scan_bwd` -- gradients of :func:`scan` (Euler input term) by the
   chain rule through the recurrence, in reverse token order.
+* :func:`ssd` -- the Mamba-2 "state space dual" form with one scalar decay
+  per head: the masked matrix product y = (L o S) x of the Guide Complet's
+  section 5, computed directly.
 * :func:`scan_threaded` -- the same scan run on disjoint channel ranges from
   several Python threads (ctypes releases the GIL), used to time the oracle on
   all host cores.  It does not change the arithmetic.
@@ -78,6 +81,8 @@ def _load():
         lib.oracle_causal_conv1d_silu_f64.restype = I
         lib.oracle_scan_bwd_f64.argtypes = [P] * 8 + [I] + [P] * 12 + [I64] * 4
         lib.oracle_scan_bwd_f64.restype = I
+        lib.oracle_ssd_f64.argtypes = [P] * 8 + [I] + [P] * 3 + [I64] * 6
+        lib.oracle_ssd_f64.restype = I
         _lib = lib
         return lib
 
@@ -188,6 +193,35 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise ValueError("oracle_scan_bwd_f64 rejected its arguments")
     return out
+
+
+def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
+        h0=None):
+    """Mamba-2 SSD forward as the O(L^2) masked product.  x, z: (batch,
+    nheads, headdim, L); dt: (batch, nheads, L); A, D, dt_bias: (nheads,);
+    B, C: (batch, ngroups, N, L); h0: (batch, nheads, headdim, N).  Returns
+    ``(y, h_final)`` as fp64 arrays."""
+    x = _f64(x)
+    batch, nheads, P, L = x.shape
+    B = _f64(B)
+    ngroups, N = B.shape[1], B.shape[2]
+    B = _f64(B, (batch, ngroups, N, L))
+    C = _f64(C, (batch, ngroups, N, L))
+    dt = _f64(dt, (batch, nheads, L))
+    A = _f64(A, (nheads,))
+    D = _f64(D, (nheads,))
+    z = _f64(z, (batch, nheads, P, L))
+    dt_bias = _f64(dt_bias, (nheads,))
+    h0 = _f64(h0, (batch, nheads, P, N))
+    y = np.empty((batch, nheads, P, L))
+    hf = np.empty((batch, nheads, P, N))
+    rc = _load().oracle_ssd_f64(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(dt_bias), int(bool(dt_softplus)), _ptr(h0), _ptr(y), _ptr(hf),
+        batch, nheads, P, ngroups, N, L)
+    if rc != 0:
+        raise ValueError("oracle_ssd_f64 rejected its arguments")
+    return y, hf
 
 
 def step(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,

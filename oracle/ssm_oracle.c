@@ -266,3 +266,73 @@ int oracle_scan_bwd_f64(const double *u, const double *delta, const double *A,
     free(hs);
     return 0;
 }
+
+int oracle_ssd_f64(const double *x, const double *dt, const double *A,
+                   const double *B, const double *C, const double *D,
+                   const double *z, const double *dt_bias, int dt_softplus,
+                   const double *h0, double *y, double *h_final,
+                   int64_t batch, int64_t nheads, int64_t P, int64_t ngroups,
+                   int64_t N, int64_t L)
+{
+    if (!x || !dt || !A || !B || !C || !y)
+        return -1;
+    if (batch < 0 || nheads < 1 || P < 1 || ngroups < 1 || N < 1 || L < 0 ||
+        nheads % ngroups != 0)
+        return -1;
+    double *cum = malloc(sizeof(double) * (size_t)(2 * L + 1));
+    if (!cum)
+        return -1;
+    double *dts = cum + L;
+    const int64_t hpg = nheads / ngroups;   /* heads per group */
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t h = 0; h < nheads; ++h) {
+            const int64_t g = h / hpg;
+            const double *Bg = B + (b * ngroups + g) * N * L;  /* [n*L + t] */
+            const double *Cg = C + (b * ngroups + g) * N * L;
+            const double *dtr = dt + (b * nheads + h) * L;
+            double run = 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                double v = dtr[t] + (dt_bias ? dt_bias[h] : 0.0);
+                dts[t] = dt_softplus ? oracle_softplus(v) : v;
+                run += dts[t];
+                cum[t] = run;
+            }
+            for (int64_t p = 0; p < P; ++p) {
+                const int64_t row = ((b * nheads + h) * P + p) * L;
+                const int64_t srow = ((b * nheads + h) * P + p) * N;
+                for (int64_t t = 0; t < L; ++t) {
+                    double acc = 0.0;
+                    for (int64_t s = 0; s <= t; ++s) {      /* the causal mask */
+                        double cb = 0.0;
+                        for (int64_t n = 0; n < N; ++n)
+                            cb += Cg[n * L + t] * Bg[n * L + s];
+                        acc += cb * exp(A[h] * (cum[t] - cum[s])) * dts[s] *
+                               x[row + s];
+                    }
+                    if (h0) {
+                        double decay = exp(A[h] * cum[t]);
+                        for (int64_t n = 0; n < N; ++n)
+                            acc += Cg[n * L + t] * decay * h0[srow + n];
+                    }
+                    if (D)
+                        acc += D[h] * x[row + t];
+                    if (z)
+                        acc *= oracle_silu(z[row + t]);
+                    y[row + t] = acc;
+                }
+                if (h_final) {
+                    for (int64_t n = 0; n < N; ++n) {
+                        double st = L > 0 && h0 ? exp(A[h] * cum[L - 1]) * h0[srow + n]
+                                                : (h0 ? h0[srow + n] : 0.0);
+                        for (int64_t s = 0; s < L; ++s)
+                            st += exp(A[h] * (cum[L - 1] - cum[s])) * dts[s] *
+                                  x[row + s] * Bg[n * L + s];
+                        h_final[srow + n] = st;
+                    }
+                }
+            }
+        }
+    }
+    free(cum);
+    return 0;
+}

@@ -117,6 +117,32 @@ int oracle_scan_bwd_f64(const double *u, const double *delta, const double *A,
                         int64_t batch, int64_t dim, int64_t dstate,
                         int64_t seqlen);
 
+/* Mamba-2 "SSD" (state space dual) form ("Mamba & State Space Models -
+ * Guide Complet", section 5: d_state 64-256, y = (L o S) u with L the causal
+ * mask (1 where t >= s) and S a structured semiseparable matrix).  Reading
+ * taken (the page gives no more): one scalar decay A[h] per head, a step
+ * dt[b,h,t] = softplus(dt_raw + dt_bias[h]) per head and token, B and C
+ * shared by the heads of a group (nheads / ngroups heads per group), Euler
+ * input term; then
+ *   S[t,s]     = (sum_n C[b,g,n,t] B[b,g,n,s]) * exp(A[h] (cum_t - cum_s)) * dt_s,
+ *                cum_t = sum_{r<=t} dt_r
+ *   y[b,h,p,t] = sum_{s<=t} S[t,s] x[b,h,p,s]
+ *              + sum_n C[b,g,n,t] exp(A[h] cum_t) h0[b,h,p,n]     (h0 given)
+ *              + D[h] x[b,h,p,t],   then * silu(z[b,h,p,t])        (z given)
+ *   h_final[b,h,p,n] = exp(A[h] cum_{L-1}) h0[b,h,p,n]
+ *              + sum_s exp(A[h] (cum_{L-1} - cum_s)) dt_s x[b,h,p,s] B[b,g,n,s]
+ * computed directly as the O(L^2) masked matrix product (the definition).
+ * Shapes: x, z, y (batch, nheads, headdim, L); dt (batch, nheads, L);
+ * A, D, dt_bias (nheads); B, C (batch, ngroups, N, L); h0, h_final (batch,
+ * nheads, headdim, N).  Nullable: D, z, dt_bias, h0, h_final.  Returns 0,
+ * or -1 on a bad argument. */
+int oracle_ssd_f64(const double *x, const double *dt, const double *A,
+                   const double *B, const double *C, const double *D,
+                   const double *z, const double *dt_bias, int dt_softplus,
+                   const double *h0, double *y, double *h_final,
+                   int64_t batch, int64_t nheads, int64_t headdim,
+                   int64_t ngroups, int64_t dstate, int64_t seqlen);
+
 #ifdef __cplusplus
 }
 #endif
