@@ -232,6 +232,42 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
                  int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of caller-provided device workspace ssm_ssd_fwd needs: per chunk of
+ * 64 tokens and group, G = C^T B (64 x 64 fp32) and C transposed (64 x dstate
+ * bf16). */
+int ssm_ssd_workspace_size(int64_t batch, int64_t ngroups, int64_t dstate,
+                           int64_t seqlen, size_t *bytes);
+
+/* Mamba-2 "SSD" (state space dual) forward ("Mamba & State Space Models -
+ * Guide Complet", section 5: d_state 64-256; y = (L o S) u with L the
+ * causal mask and S a structured semiseparable matrix), with one scalar
+ * decay per head and B, C shared by the heads of a group:
+ *   dt[b,h,t]  = softplus(dt_raw[b,h,t] + dt_bias[h])   (flag; else + only)
+ *   S[t,s]     = (C[b,g,:,t] . B[b,g,:,s]) exp(A[h] sum_{s<r<=t} dt_r) dt_s
+ *   y[b,h,p,t] = (sum_{s<=t} S[t,s] x[b,h,p,s] + C[b,g,:,t] . (exp(A[h]
+ *                sum_{r<=t} dt_r) h0[b,h,p,:]) + D[h] x[b,h,p,t]) silu(z)
+ *   h_final    = the state after the last token (the same recurrence as
+ *                ssm_scan_fwd with A[h] for every state)
+ * computed in chunks of 64 tokens: the masked products inside a chunk and
+ * the carried head state run on the matrix cores (bf16 operands, fp32
+ * accumulation; the carried state is fp32).
+ *  x, z, y        bf16 (batch, nheads, headdim, seqlen); z nullable
+ *  dt             bf16 (batch, nheads, seqlen)
+ *  A, D, dt_bias  fp32 (nheads); D, dt_bias nullable
+ *  B, C           bf16 (batch, ngroups, dstate, seqlen); nheads % ngroups == 0
+ *  h0, h_final    fp32 (batch, nheads, headdim, dstate), nullable
+ *  flags          SSM_FLAG_DELTA_SOFTPLUS (SSM_FLAG_ZOH_B: SSM_ERR_UNSUPPORTED)
+ *  dtype          SSM_DTYPE_BF16 (SSM_DTYPE_F32: SSM_ERR_UNSUPPORTED)
+ *  headdim 64 and dstate 64, 128 or 256 in this build (else
+ *  SSM_ERR_UNSUPPORTED); workspace as ssm_ssd_workspace_size(), 256-byte
+ *  aligned.  Conventions as for ssm_scan_fwd. */
+int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
+                const void *C, const float *D, const void *z,
+                const float *dt_bias, unsigned flags, const float *h0, void *y,
+                float *h_final, int64_t batch, int64_t nheads, int64_t headdim,
+                int64_t ngroups, int64_t dstate, int64_t seqlen, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */
 const char *ssm_last_error(void);

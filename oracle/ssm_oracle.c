@@ -279,10 +279,11 @@ int oracle_ssd_f64(const double *x, const double *dt, const double *A,
     if (batch < 0 || nheads < 1 || P < 1 || ngroups < 1 || N < 1 || L < 0 ||
         nheads % ngroups != 0)
         return -1;
-    double *cum = malloc(sizeof(double) * (size_t)(2 * L + 1));
+    double *cum = malloc(sizeof(double) * (size_t)(2 * L + P + 1));
     if (!cum)
         return -1;
     double *dts = cum + L;
+    double *acc = dts + L;   /* one output column, all rows of the head */
     const int64_t hpg = nheads / ngroups;   /* heads per group */
     for (int64_t b = 0; b < batch; ++b) {
         for (int64_t h = 0; h < nheads; ++h) {
@@ -297,33 +298,42 @@ int oracle_ssd_f64(const double *x, const double *dt, const double *A,
                 run += dts[t];
                 cum[t] = run;
             }
-            for (int64_t p = 0; p < P; ++p) {
-                const int64_t row = ((b * nheads + h) * P + p) * L;
-                const int64_t srow = ((b * nheads + h) * P + p) * N;
-                for (int64_t t = 0; t < L; ++t) {
-                    double acc = 0.0;
-                    for (int64_t s = 0; s <= t; ++s) {      /* the causal mask */
-                        double cb = 0.0;
-                        for (int64_t n = 0; n < N; ++n)
-                            cb += Cg[n * L + t] * Bg[n * L + s];
-                        acc += cb * exp(A[h] * (cum[t] - cum[s])) * dts[s] *
-                               x[row + s];
-                    }
+            /* y[:, t] = sum_{s <= t} S[t,s] x[:, s]: S[t,s] is formed once per
+             * (t, s) and applied to every row p of the head */
+            for (int64_t t = 0; t < L; ++t) {
+                for (int64_t p = 0; p < P; ++p)
+                    acc[p] = 0.0;
+                for (int64_t s = 0; s <= t; ++s) {          /* the causal mask */
+                    double cb = 0.0;
+                    for (int64_t n = 0; n < N; ++n)
+                        cb += Cg[n * L + t] * Bg[n * L + s];
+                    double w = cb * exp(A[h] * (cum[t] - cum[s])) * dts[s];
+                    for (int64_t p = 0; p < P; ++p)
+                        acc[p] += w * x[((b * nheads + h) * P + p) * L + s];
+                }
+                for (int64_t p = 0; p < P; ++p) {
+                    const int64_t row = ((b * nheads + h) * P + p) * L;
+                    const int64_t srow = ((b * nheads + h) * P + p) * N;
+                    double v = acc[p];
                     if (h0) {
                         double decay = exp(A[h] * cum[t]);
                         for (int64_t n = 0; n < N; ++n)
-                            acc += Cg[n * L + t] * decay * h0[srow + n];
+                            v += Cg[n * L + t] * decay * h0[srow + n];
                     }
                     if (D)
-                        acc += D[h] * x[row + t];
+                        v += D[h] * x[row + t];
                     if (z)
-                        acc *= oracle_silu(z[row + t]);
-                    y[row + t] = acc;
+                        v *= oracle_silu(z[row + t]);
+                    y[row + t] = v;
                 }
-                if (h_final) {
+            }
+            if (h_final) {
+                for (int64_t p = 0; p < P; ++p) {
+                    const int64_t row = ((b * nheads + h) * P + p) * L;
+                    const int64_t srow = ((b * nheads + h) * P + p) * N;
                     for (int64_t n = 0; n < N; ++n) {
-                        double st = L > 0 && h0 ? exp(A[h] * cum[L - 1]) * h0[srow + n]
-                                                : (h0 ? h0[srow + n] : 0.0);
+                        double st = h0 ? exp(A[h] * (L > 0 ? cum[L - 1] : 0.0)) * h0[srow + n]
+                                       : 0.0;
                         for (int64_t s = 0; s < L; ++s)
                             st += exp(A[h] * (cum[L - 1] - cum[s])) * dts[s] *
                                   x[row + s] * Bg[n * L + s];

@@ -15,6 +15,8 @@ Names follow the C ABI:
   depthwise conv1d(x)) is formed inside the kernel (the Mamba block's
   convolution before the SSM).
 * :func:`ssm_state_update` -- one decoding step on an in-place fp32 state.
+* :func:`ssm_ssd_fwd` -- the Mamba-2 SSD form (one scalar decay per head,
+  d_state 64-256) on the matrix cores; :func:`ssm_ssd_workspace_size`.
 * :func:`ssm_scan_bwd` -- gradients of :func:`ssm_scan_fwd` (Euler input
   term) with respect to every input, recomputing the states from block
   checkpoints; :func:`ssm_scan_bwd_workspace_size`.
@@ -40,7 +42,8 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
           3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
 EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
            "ssm_scan_fwd", "ssm_conv_scan_fwd", "ssm_state_update",
-           "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_last_error")
+           "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
+           "ssm_ssd_workspace_size", "ssm_ssd_fwd", "ssm_last_error")
 
 _lib = None
 _lock = threading.Lock()
@@ -93,6 +96,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                      [I64, I64, I64, I64, I, P,
                                       ctypes.c_size_t, P])
         lib.ssm_scan_bwd.restype = I
+        lib.ssm_ssd_workspace_size.argtypes = [
+            I64, I64, I64, I64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssm_ssd_workspace_size.restype = I
+        lib.ssm_ssd_fwd.argtypes = ([P] * 8 + [U] + [P] * 3 +
+                                    [I64] * 6 + [I, P, ctypes.c_size_t, P])
+        lib.ssm_ssd_fwd.restype = I
         lib.ssm_last_error.argtypes = []
         lib.ssm_last_error.restype = ctypes.c_char_p
         if path is None:
@@ -399,3 +408,55 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         batch, dim, N, L, code, workspace.data_ptr(), wsn,
         _stream_handle(dev, stream)))
     return {k: out[k] for k in shapes}
+
+
+def ssm_ssd_workspace_size(batch, ngroups, dstate, seqlen) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().ssm_ssd_workspace_size(batch, ngroups, dstate,
+                                                 seqlen, ctypes.byref(out)))
+    return out.value
+
+
+def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                dt_softplus=True, h0=None, return_final_state=True, y=None,
+                h_final=None, workspace=None, stream=None):
+    """Mamba-2 SSD forward.  x, z: (batch, nheads, headdim, L) bf16; dt:
+    (batch, nheads, L) bf16; A, D, dt_bias: (nheads,) fp32; B, C: (batch,
+    ngroups, N, L) bf16; h0: (batch, nheads, headdim, N) fp32 or None.
+    Returns ``(y, h_final)``."""
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, nheads, headdim, L)")
+    batch, nheads, P, L = x.shape
+    if B.dim() != 4:
+        raise ValueError("B must be (batch, ngroups, N, L)")
+    ngroups, N = B.shape[1], B.shape[2]
+    dev = x.device
+    act = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    if y is None:
+        y = torch.empty((batch, nheads, P, L), dtype=act, device=dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, nheads, P, N), dtype=f32, device=dev)
+    if not return_final_state:
+        h_final = None
+    if workspace is None:
+        workspace = torch.empty(ssm_ssd_workspace_size(batch, ngroups, N, L),
+                                dtype=torch.uint8, device=dev)
+    wsn = workspace.numel() * workspace.element_size()
+    _check(load_library().ssm_ssd_fwd(
+        _ptr(x, "x", act, (batch, nheads, P, L), dev),
+        _ptr(dt, "dt", act, (batch, nheads, L), dev),
+        _ptr(A, "A", f32, (nheads,), dev),
+        _ptr(B, "B", act, (batch, ngroups, N, L), dev),
+        _ptr(C, "C", act, (batch, ngroups, N, L), dev),
+        _ptr(D, "D", f32, (nheads,), dev),
+        _ptr(z, "z", act, (batch, nheads, P, L), dev),
+        _ptr(dt_bias, "dt_bias", f32, (nheads,), dev),
+        _flags(dt_softplus, False),
+        _ptr(h0, "h0", f32, (batch, nheads, P, N), dev),
+        _ptr(y, "y", act, (batch, nheads, P, L), dev),
+        _ptr(h_final, "h_final", f32, (batch, nheads, P, N), dev),
+        batch, nheads, P, ngroups, N, L, code, workspace.data_ptr(), wsn,
+        _stream_handle(dev, stream)))
+    return y, h_final

@@ -509,3 +509,135 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
 }
 
 }  // extern "C"
+
+namespace {
+
+// Workspace of the SSD forward: G = C^T B per chunk (fp32 64 x 64) and C
+// transposed per chunk (bf16 64 x N), each part 256-byte aligned.
+struct SsdLayout {
+  size_t off_G, off_Ct, total_bytes;
+};
+SsdLayout ssd_layout(int64_t batch, int64_t ngroups, int64_t dstate, int64_t seqlen) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t chunks = static_cast<size_t>(batch) * ngroups *
+                        static_cast<size_t>((seqlen + ssm::kSsdChunk - 1) / ssm::kSsdChunk);
+  SsdLayout l;
+  l.off_G = 0;
+  l.off_Ct = up(chunks * ssm::kSsdChunk * ssm::kSsdChunk * sizeof(float));
+  l.total_bytes = up(l.off_Ct + chunks * ssm::kSsdChunk * static_cast<size_t>(dstate) * 2);
+  return l;
+}
+
+int check_ssd_sizes(int64_t batch, int64_t nheads, int64_t headdim, int64_t ngroups,
+                    int64_t dstate, int64_t seqlen) {
+  if (batch <= 0 || nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0 ||
+      seqlen <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "sizes must be positive");
+  if (nheads % ngroups != 0)
+    return fail(SSM_ERR_INVALID_ARG, "nheads=%lld is not a multiple of ngroups=%lld",
+                (long long)nheads, (long long)ngroups);
+  if (headdim != ssm::kSsdHeadDim)
+    return fail(SSM_ERR_UNSUPPORTED, "headdim=%lld: this build supports %d",
+                (long long)headdim, ssm::kSsdHeadDim);
+  if (dstate != 64 && dstate != 128 && dstate != 256)
+    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld: this build supports 64, 128, 256",
+                (long long)dstate);
+  int64_t e;
+  if (!mul_ok(batch * nheads, headdim * seqlen, &e) || !mul_ok(e, 8, &e) ||
+      !mul_ok(batch * ngroups, dstate * seqlen, &e) || !mul_ok(e, 8, &e))
+    return fail(SSM_ERR_INVALID_ARG, "sizes overflow");
+  if (batch > kMaxGridYZ || nheads >= (int64_t(1) << 31) ||
+      (seqlen + ssm::kSsdChunk - 1) / ssm::kSsdChunk > (int64_t(1) << 30))
+    return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_ssd_workspace_size(int64_t batch, int64_t ngroups, int64_t dstate,
+                           int64_t seqlen, size_t *bytes) {
+  if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
+  int st = check_ssd_sizes(batch, ngroups, ssm::kSsdHeadDim, ngroups, dstate, seqlen);
+  if (st != SSM_OK) return st;
+  *bytes = ssd_layout(batch, ngroups, dstate, seqlen).total_bytes;
+  return ok();
+}
+
+int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
+                const void *C, const float *D, const void *z,
+                const float *dt_bias, unsigned flags, const float *h0, void *y,
+                float *h_final, int64_t batch, int64_t nheads, int64_t headdim,
+                int64_t ngroups, int64_t dstate, int64_t seqlen, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream) {
+  if (!x || !dt || !A || !B || !C || !y)
+    return fail(SSM_ERR_INVALID_ARG, "required pointer is NULL");
+  if (dtype == SSM_DTYPE_F32)
+    return fail(SSM_ERR_UNSUPPORTED, "the SSD form runs on bf16 activations only");
+  if (dtype != SSM_DTYPE_BF16) return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & ~kKnownFlags) return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (flags & SSM_FLAG_ZOH_B)
+    return fail(SSM_ERR_UNSUPPORTED, "the SSD form implements the Euler input term only");
+  int st = check_ssd_sizes(batch, nheads, headdim, ngroups, dstate, seqlen);
+  if (st != SSM_OK) return st;
+
+  const void *acts[] = {x, dt, B, C, z, y};
+  for (const void *p : acts)
+    if (p && !aligned(p, 2))
+      return fail(SSM_ERR_INVALID_ARG, "bf16 pointer %p not 2-byte aligned", p);
+  const void *f32s[] = {A, D, dt_bias, h0, h_final};
+  for (const void *p : f32s)
+    if (p && !aligned(p, 4))
+      return fail(SSM_ERR_INVALID_ARG, "fp32 pointer %p not 4-byte aligned", p);
+  const int64_t big = batch * nheads * headdim * seqlen * 2;
+  const int64_t bc = batch * ngroups * dstate * seqlen * 2;
+  const int64_t sts = batch * nheads * headdim * dstate * 4;
+  const struct { const void *p; int64_t n; const char *name; } ins[] = {
+      {x, big, "x"}, {z, big, "z"}, {dt, batch * nheads * seqlen * 2, "dt"},
+      {B, bc, "B"}, {C, bc, "C"}, {A, nheads * 4, "A"}, {D, nheads * 4, "D"},
+      {dt_bias, nheads * 4, "dt_bias"}, {h0, sts, "h0"}};
+  for (const auto &in : ins) {
+    if (overlaps(y, big, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "y overlaps input %s", in.name);
+    if (overlaps(h_final, sts, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "h_final overlaps input %s", in.name);
+  }
+  if (overlaps(y, big, h_final, sts)) return fail(SSM_ERR_INVALID_ARG, "y overlaps h_final");
+  const SsdLayout l = ssd_layout(batch, ngroups, dstate, seqlen);
+  if (!workspace || workspace_bytes < l.total_bytes)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu bytes at %p)",
+                l.total_bytes, workspace_bytes, workspace);
+  if (!aligned(workspace, 256))
+    return fail(SSM_ERR_INVALID_ARG, "workspace %p not 256-byte aligned", workspace);
+  for (const auto &in : ins)
+    if (overlaps(workspace, static_cast<int64_t>(l.total_bytes), in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "workspace overlaps input %s", in.name);
+  if (overlaps(workspace, static_cast<int64_t>(l.total_bytes), y, big) ||
+      overlaps(workspace, static_cast<int64_t>(l.total_bytes), h_final, sts))
+    return fail(SSM_ERR_INVALID_ARG, "workspace overlaps an output");
+
+  // 16-byte loads and stores need every row to start 16-byte aligned
+  bool vec = (seqlen % 8) == 0;
+  const void *rows[] = {x, z, y, B, C};
+  for (const void *p : rows)
+    if (p && !aligned(p, 16)) vec = false;
+
+  char *w = static_cast<char *>(workspace);
+  ssm::SsdArgs a{};
+  a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z;
+  a.A = A; a.D = D; a.dt_bias = dt_bias; a.h0 = h0;
+  a.y = y; a.h_final = h_final;
+  a.G = reinterpret_cast<float *>(w + l.off_G);
+  a.Ct = w + l.off_Ct;
+  a.batch = batch; a.nheads = nheads; a.ngroups = ngroups; a.L = seqlen;
+  a.nchunks = static_cast<int>((seqlen + ssm::kSsdChunk - 1) / ssm::kSsdChunk);
+  a.dstate = static_cast<int>(dstate);
+  a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+  const int err = ssm::launch_ssd(a, vec, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  return ok();
+}
+
+}  // extern "C"

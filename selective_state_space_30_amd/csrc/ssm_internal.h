@@ -59,6 +59,21 @@ struct BwdArgs {
   int softplus;
 };
 
+// Mamba-2 SSD forward (one scalar decay per head; bf16 activations).
+constexpr int kSsdChunk = 64;        // tokens per chunk
+constexpr int kSsdHeadDim = 64;      // rows (headdim) per head
+struct SsdArgs {
+  const void *x, *dt, *B, *C, *z;     // bf16: (b,h,P,L), (b,h,L), (b,g,N,L) x2, (b,h,P,L)
+  const float *A, *D, *dt_bias, *h0;  // (h), (h), (h), (b,h,P,N)
+  void *y;                            // bf16 (b,h,P,L)
+  float *h_final;                     // (b,h,P,N) or null
+  float *G;                           // workspace: (b,g,chunk,64,64) C^T B per chunk
+  void *Ct;                           // workspace: bf16 (b,g,chunk,64,N) C transposed
+  int64_t batch, nheads, ngroups, L;
+  int nchunks, dstate;
+  int softplus;
+};
+
 struct StepArgs {
   float *state;
   const void *x, *delta, *B, *C, *z;
@@ -81,6 +96,7 @@ SplitLayout split_layout(int64_t batch, int64_t dim, int64_t n_chunks);
 int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream);
 int launch_step(const StepArgs &a, bool bf16, bool vec, void *stream);
 int launch_bwd(const BwdArgs &a, bool bf16, bool vec, void *stream);
+int launch_ssd(const SsdArgs &a, bool vec, void *stream);
 
 // Workspace layout of the backward pass, in bytes, each part 256-aligned.
 struct BwdLayout {

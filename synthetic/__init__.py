@@ -80,6 +80,86 @@ DECODE = DecodeConfig("decode_b256_d5120_n16_bf16", 256, 5120, 16, 64,
 SCAN_CONFIGS = {c.name: c for c in (TINY, MAMBA_130M, MAMBA_2P8B, LONG_1M)}
 
 
+@dataclass(frozen=True)
+class SsdConfig:
+    """A Mamba-2 SSD layer: nheads heads of headdim rows (d_inner = nheads *
+    headdim), dstate states, ngroups groups sharing B and C."""
+    name: str
+    batch: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    seqlen: int
+    with_z: bool = True
+    with_D: bool = True
+    with_h0: bool = False
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.nheads * self.headdim * self.seqlen
+
+
+# d_inner 5120 (the 2.8B layer's inner width) as 80 heads of 64, d_state 128
+# (inside the 64-256 the Guide Complet gives for Mamba-2), one group.
+MAMBA2_LAYER = SsdConfig("mamba2_b2_h80_p64_n128_l4096_bf16", 2, 80, 64, 1, 128,
+                         4096, seed=1005,
+                         note="batch=2, 80 heads x 64, N=128, L=4096, bf16")
+
+
+def make_ssd_inputs(cfg: SsdConfig, device="cpu", **over) -> dict:
+    """Seeded SSD inputs (bf16 activations): x, z ~ N(0,1); dt_raw ~ N(0,1)
+    with a per-head bias log(expm1(U[1e-3, 1e-1])) and softplus on (as the
+    scan workloads); A[h] = -U[1, 16] (Mamba-2 keeps A = -exp(A_log) per
+    head with A_log in [log 1, log 16]); B, C ~ N(0,1); D ~ N(0,1)."""
+    if over:
+        cfg = replace(cfg, **over)
+    b, h, P, g, n, L, s = (cfg.batch, cfg.nheads, cfg.headdim, cfg.ngroups,
+                           cfg.dstate, cfg.seqlen, cfg.seed)
+    act = torch.bfloat16
+    out = {}
+    out["x"] = _normal((b, h, P, L), device, s, 1).to(act)
+    out["dt"] = _normal((b, h, L), device, s, 2).to(act)
+    target = _uniform((h,), 1e-3, 1e-1, device, s, 3)
+    out["dt_bias"] = torch.log(torch.expm1(target)).contiguous()
+    out["A"] = -_uniform((h,), 1.0, 16.0, device, s, 4)
+    out["B"] = _normal((b, g, n, L), device, s, 5).to(act)
+    out["C"] = _normal((b, g, n, L), device, s, 6).to(act)
+    out["D"] = _normal((h,), device, s, 7) if cfg.with_D else None
+    out["z"] = _normal((b, h, P, L), device, s, 8).to(act) if cfg.with_z else None
+    out["h0"] = _normal((b, h, P, n), device, s, 9) if cfg.with_h0 else None
+    out["dt_softplus"] = True
+    return out
+
+
+def ssd_bytes(cfg: SsdConfig) -> int:
+    """Bytes the SSD forward must move: x, z read and y written (bf16), dt
+    read (bf16), B and C read, A, D, bias read, the final state written (and
+    the initial one read when given)."""
+    e = cfg.elements
+    by = e * 2 * (2 + (1 if cfg.with_z else 0))
+    by += cfg.batch * cfg.nheads * cfg.seqlen * 2
+    by += 2 * cfg.batch * cfg.ngroups * cfg.dstate * cfg.seqlen * 2
+    by += 3 * cfg.nheads * 4
+    st = cfg.batch * cfg.nheads * cfg.headdim * cfg.dstate * 4
+    by += st * (2 if cfg.with_h0 else 1)
+    return by
+
+
+def ssd_flops(cfg: SsdConfig, chunk: int = 64) -> int:
+    """Matrix-core flops of the chunked SSD form: per chunk and head the
+    y products exp(A cum) S C (headdim x N x chunk) and X M^T (headdim x
+    chunk x chunk) and the state update (X w) B^T (headdim x chunk x N);
+    per chunk and group G = C^T B (chunk x N x chunk)."""
+    nch = (cfg.seqlen + chunk - 1) // chunk
+    P, N, T = cfg.headdim, cfg.dstate, chunk
+    per_head = 2 * (P * N * T + P * T * T + P * T * N)
+    per_group = 2 * T * N * T
+    return nch * cfg.batch * (cfg.nheads * per_head + cfg.ngroups * per_group)
+
+
 def torch_dtype(tag: str) -> torch.dtype:
     return {"f32": torch.float32, "bf16": torch.bfloat16}[tag]
 

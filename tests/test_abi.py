@@ -290,3 +290,55 @@ def test_bwd_workspace_size(lib):
     assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 7, ctypes.byref(size)) == 1
     assert lib.ssm_scan_bwd_workspace_size(1, 16, 8, 256, 0, ctypes.byref(size)) == 2
     assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 0, None) == 1
+
+
+def _ssd(lib, **kw):
+    step = 0x08000000
+    names = ["x", "dt", "A", "B", "C", "y", "ws"]
+    a = {n: FAKE + i * step for i, n in enumerate(names)}
+    a.update(D=None, z=None, bias=None, flags=1, h0=None, h_final=None,
+             batch=1, nheads=4, headdim=64, ngroups=1, dstate=128, seqlen=256,
+             dtype=ssm.SSM_DTYPE_BF16, stream=None)
+    size = ctypes.c_size_t(0)
+    assert lib.ssm_ssd_workspace_size(1, 1, 128, 256, ctypes.byref(size)) == 0
+    a["ws_bytes"] = size.value
+    a.update(kw)
+    return lib.ssm_ssd_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"],
+                           a["z"], a["bias"], a["flags"], a["h0"], a["y"],
+                           a["h_final"], a["batch"], a["nheads"], a["headdim"],
+                           a["ngroups"], a["dstate"], a["seqlen"], a["dtype"],
+                           a["ws"], a["ws_bytes"], a["stream"])
+
+
+INVALID_SSD_CASES = [
+    ("null x", dict(x=None), 1),
+    ("null dt", dict(dt=None), 1),
+    ("null y", dict(y=None), 1),
+    ("fp32 activations", dict(dtype=ssm.SSM_DTYPE_F32), 2),
+    ("bad dtype", dict(dtype=9), 1),
+    ("headdim 32", dict(headdim=32), 2),
+    ("dstate 96", dict(dstate=96), 2),
+    ("groups do not divide heads", dict(ngroups=3), 1),
+    ("zoh flag", dict(flags=3), 2),
+    ("zero seqlen", dict(seqlen=0), 1),
+    ("y overlaps x", dict(y=FAKE + 64), 1),
+    ("misaligned A", dict(A=FAKE + 2 * 0x08000000 + 2), 1),
+    ("workspace missing", dict(ws=None), 3),
+    ("workspace too small", dict(ws_bytes=256), 3),
+    ("workspace misaligned", dict(ws=FAKE + 6 * 0x08000000 + 64), 1),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_SSD_CASES,
+                         ids=[c[0] for c in INVALID_SSD_CASES])
+def test_ssd_rejects_invalid_arguments(lib, name, kw, status):
+    assert _ssd(lib, **kw) == status, ssm.ssm_last_error()
+    assert ssm.ssm_last_error()
+
+
+def test_ssd_workspace_size(lib):
+    size = ctypes.c_size_t(0)
+    assert lib.ssm_ssd_workspace_size(2, 1, 128, 4096, ctypes.byref(size)) == 0
+    chunks = 2 * 1 * 64
+    assert size.value >= chunks * (64 * 64 * 4 + 64 * 128 * 2)
+    assert lib.ssm_ssd_workspace_size(2, 1, 100, 4096, ctypes.byref(size)) == 2

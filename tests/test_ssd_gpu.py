@@ -1,0 +1,125 @@
+"""Parity of the HIP Mamba-2 SSD forward (ssm_ssd_fwd) with the fp64 oracle.
+
+Small shapes are compared element by element with oracle.ssd (the masked
+quadratic form, pinned to the recurrence); at the Mamba-2 layer's size,
+sampled heads are compared with the recurrent scan oracle on the same
+computation (A broadcast over the states; the two oracles are pinned to
+each other), which is linear in L.
+
+Bar: 2e-2 on the scaled error (bf16 activations; the chunk products take
+bf16 operands with fp32 accumulation, the carried state is fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_30_amd as ssm
+import synthetic as syn
+from parity_metrics import report, scaled_max_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 2e-2
+
+
+def check(got, ref, what):
+    err = scaled_max_err(got, ref)
+    assert err <= TOL, "%s: %s (tol %g)" % (what, report(got, ref), TOL)
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v)
+            for k, v in inp.items()}
+
+
+def gpu_ssd(d):
+    y, hf = ssm.ssm_ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                            d["z"], d["dt_bias"], d["dt_softplus"], d["h0"])
+    torch.cuda.synchronize()
+    return y, hf
+
+
+CASES = [
+    # (batch, nheads, ngroups, dstate, L, z, D, h0)
+    (1, 2, 1, 64, 64, 1, 1, 0),      # one full chunk
+    (2, 4, 2, 128, 200, 1, 1, 1),    # ragged last chunk, 2 groups
+    (1, 3, 1, 256, 130, 1, 0, 1),    # N = 256
+    (2, 2, 1, 128, 333, 0, 1, 1),    # L % 8 != 0: element-wise loads
+    (1, 2, 2, 64, 1, 1, 1, 1),       # a single token
+    (1, 4, 4, 128, 512, 1, 1, 0),    # one head per group, 8 chunks
+]
+
+
+@pytest.mark.parametrize("case", CASES,
+                         ids=lambda c: "b%d_h%d_g%d_n%d_l%d_z%d_D%d_h%d" % c)
+def test_ssd_matches_oracle(case):
+    batch, nheads, ngroups, N, L, wz, wD, wh = case
+    inp = syn.make_ssd_inputs(syn.MAMBA2_LAYER, "cpu", batch=batch,
+                              nheads=nheads, ngroups=ngroups, dstate=N,
+                              seqlen=L, with_z=bool(wz), with_D=bool(wD),
+                              with_h0=bool(wh), seed=700 + L + N)
+    y_ref, h_ref = oracle.ssd(inp["x"], inp["dt"], inp["A"], inp["B"],
+                              inp["C"], inp["D"], inp["z"], inp["dt_bias"],
+                              True, inp["h0"])
+    y, hf = gpu_ssd(to_dev(inp))
+    check(y, y_ref, "y")
+    check(hf, h_ref, "h_final")
+
+
+def test_ssd_deterministic_and_resumable():
+    inp = to_dev(syn.make_ssd_inputs(syn.MAMBA2_LAYER, "cpu", batch=1,
+                                     nheads=3, seqlen=640, seed=5))
+    y1, h1 = gpu_ssd(inp)
+    y2, h2 = gpu_ssd(inp)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    # split at a chunk boundary and resume from the final state
+    L1 = 256
+    a = {k: (v[..., :L1].contiguous() if k in ("x", "dt", "B", "C", "z") else v)
+         for k, v in inp.items()}
+    b = {k: (v[..., L1:].contiguous() if k in ("x", "dt", "B", "C", "z") else v)
+         for k, v in inp.items()}
+    ya, ha = gpu_ssd(a)
+    b["h0"] = ha
+    yb, hb = gpu_ssd(b)
+    check(torch.cat([ya, yb], dim=-1), y1.double(), "y (split)")
+    check(hb, h1.double(), "h_final (split)")
+
+
+def test_ssd_rejects_unsupported():
+    inp = to_dev(syn.make_ssd_inputs(syn.MAMBA2_LAYER, "cpu", batch=1,
+                                     nheads=2, dstate=96, seqlen=64, seed=1))
+    with pytest.raises(ssm.SSMError) as e:
+        gpu_ssd(inp)
+    assert e.value.status == 2
+
+
+def _as_scan_channel(inp, b, h, p):
+    """Inputs of one head row (b, h, p) as a one-channel Mamba-1 scan."""
+    cfg_g = inp["B"].shape[1]
+    g = h // (inp["x"].shape[1] // cfg_g)
+    N = inp["B"].shape[2]
+    return dict(
+        u=inp["x"][b:b + 1, h, p:p + 1], delta=inp["dt"][b:b + 1, h:h + 1],
+        A=np.full((1, N), float(inp["A"][h])), B=inp["B"][b:b + 1, g],
+        C=inp["C"][b:b + 1, g],
+        D=None if inp["D"] is None else np.array([float(inp["D"][h])]),
+        z=None if inp["z"] is None else inp["z"][b:b + 1, h, p:p + 1],
+        delta_bias=np.array([float(inp["dt_bias"][h])]))
+
+
+def test_ssd_layer_workload_sampled():
+    cfg = syn.MAMBA2_LAYER
+    inp = syn.make_ssd_inputs(cfg, DEV)
+    y, hf = gpu_ssd(inp)
+    r = np.random.default_rng(11)
+    rows = sorted({(0, 0, 0), (cfg.batch - 1, cfg.nheads - 1, cfg.headdim - 1)} |
+                  {(int(r.integers(cfg.batch)), int(r.integers(cfg.nheads)),
+                    int(r.integers(cfg.headdim))) for _ in range(6)})
+    for b, h, p in rows:
+        a = _as_scan_channel(inp, b, h, p)
+        yr, hr = oracle.scan(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"],
+                             a["z"], a["delta_bias"], True, False, None)
+        check(y[b, h, p:p + 1], yr[0], "y (b=%d h=%d p=%d)" % (b, h, p))
+        check(hf[b, h, p:p + 1], hr[0], "h_final (b=%d h=%d p=%d)" % (b, h, p))
+    assert torch.isfinite(y.float()).all()
