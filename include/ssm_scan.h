@@ -233,8 +233,8 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of caller-provided device workspace ssm_ssd_fwd needs: per chunk of
- * 64 tokens and group, G = C^T B (64 x 64 fp32) and C transposed (64 x dstate
- * bf16). */
+ * 64 tokens and group, the causal G = C^T B (64 x 64, as two bf16 arrays:
+ * the value and its rounding error) and C transposed (64 x dstate bf16). */
 int ssm_ssd_workspace_size(int64_t batch, int64_t ngroups, int64_t dstate,
                            int64_t seqlen, size_t *bytes);
 

@@ -523,7 +523,7 @@ SsdLayout ssd_layout(int64_t batch, int64_t ngroups, int64_t dstate, int64_t seq
                         static_cast<size_t>((seqlen + ssm::kSsdChunk - 1) / ssm::kSsdChunk);
   SsdLayout l;
   l.off_G = 0;
-  l.off_Ct = up(chunks * ssm::kSsdChunk * ssm::kSsdChunk * sizeof(float));
+  l.off_Ct = up(chunks * ssm::kSsdChunk * ssm::kSsdChunk * 2 * 2);
   l.total_bytes = up(l.off_Ct + chunks * ssm::kSsdChunk * static_cast<size_t>(dstate) * 2);
   return l;
 }
@@ -628,7 +628,7 @@ int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
   a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z;
   a.A = A; a.D = D; a.dt_bias = dt_bias; a.h0 = h0;
   a.y = y; a.h_final = h_final;
-  a.G = reinterpret_cast<float *>(w + l.off_G);
+  a.G = w + l.off_G;
   a.Ct = w + l.off_Ct;
   a.batch = batch; a.nheads = nheads; a.ngroups = ngroups; a.L = seqlen;
   a.nchunks = static_cast<int>((seqlen + ssm::kSsdChunk - 1) / ssm::kSsdChunk);

@@ -67,7 +67,7 @@ struct SsdArgs {
   const float *A, *D, *dt_bias, *h0;  // (h), (h), (h), (b,h,P,N)
   void *y;                            // bf16 (b,h,P,L)
   float *h_final;                     // (b,h,P,N) or null
-  float *G;                           // workspace: (b,g,chunk,64,64) C^T B per chunk
+  void *G;                            // workspace: bf16 (b,g,chunk,2,64,64) causal C^T B, hi and lo
   void *Ct;                           // workspace: bf16 (b,g,chunk,64,N) C transposed
   int64_t batch, nheads, ngroups, L;
   int nchunks, dstate;

@@ -6,23 +6,32 @@
 // product with a structured matrix, y = (L o S) u, L the causal mask and S
 // semiseparable.  With one scalar decay A per head the masked matrix of a
 // chunk of T tokens factors into small dense products; between chunks a
-// P x N state carries the past (the recurrent form):
-//   cum_t   = sum_{r <= t in the chunk} dt_r,  dt = softplus(dt_raw + bias)
-//   G       = C^T B                     (T x T, shared by a group's heads)
-//   M[t,s]  = G[t,s] exp(A (cum_t - cum_s)) dt_s   for s <= t, else 0
-//   y       = exp(A cum_t) (S C)[:, t] + (X M^T)[:, t] + D x,  then silu(z)
-//   S      <- exp(A cum_T) S + (X diag(exp(A (cum_T - cum_s)) dt_s)) B^T
-// All four products run on v_mfma_f32_16x16x32_bf16 (A operand: lane l,
-// element e = A[l%16][8*(l/16)+e]; B: B[8*(l/16)+e][l%16]; result: lane l,
-// element e = D[4*(l/16)+e][l%16], checked on the hardware).
+// P x N state carries the past (the recurrent form).  With a_t = A cum_t,
+// cum_t = sum_{r <= t in the chunk} dt_r and dt = softplus(dt_raw + bias):
+//   G       = C^T B, causal (G[t,s] = 0 for s > t; shared by a group's heads)
+//   y_t     = exp(a_t) (C^T S^T)[t] + sum_{s<=t} G[t,s] exp(a_t - a_s) dt_s x_s
+//             + D x_t,  then times silu(z_t)
+//   S      <- exp(a_T) S + (X diag(exp(a_T - a_s) dt_s)) B^T
+// The decay inside the chunk splits at a reference token m:
+// exp(a_t - a_s) = u_t v_s / dt_s with u_t = exp(a_t - a_m) and v_s =
+// exp(a_m - a_s) dt_s, so the chunk's own term is u_t (G (X diag v)^T)[t]: a
+// plain product with the group's G.  While every |a_t - a_m| stays below
+// kFactorLimit (base 2) the factors cannot overflow fp32 or bf16; a chunk
+// with a steeper decay forms M = G o exp(a_t - a_s) dt_s element by element.
+// G and the carried state enter the products as a pair of bf16 values (the
+// value and its rounding error), so that neither is rounded to bf16 alone.
+// All products run on v_mfma_f32_16x16x32_bf16 (A operand: lane l, element
+// e = A[l%16][8*(l/16)+e]; B: B[8*(l/16)+e][l%16]; result: lane l, element
+// e = D[4*(l/16)+e][l%16], checked on the hardware).
 //
-// Work layout: ssd_prep_kernel forms G and C^T per (batch, group, chunk);
-// ssd_kernel runs one workgroup per (batch, head) over the chunks in order,
-// its 4 waves owning 16 head rows each; a wave's share of the state S (16 x
-// N fp32) stays in matrix-core accumulators for the whole sequence.
+// Work layout: ssd_prep_kernel forms the causal G (bf16 pair) and C^T per
+// (batch, group, chunk); ssd_kernel runs one workgroup per (batch, head,
+// slice of the head's rows) over the chunks in order, the state staying in
+// matrix-core accumulators for the whole sequence.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "ssm_device.h"
 #include "ssm_internal.h"
@@ -34,11 +43,17 @@ using namespace dev;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int T = kSsdChunk;     // 64 tokens per chunk
 constexpr int P = kSsdHeadDim;   // 64 rows per head
 constexpr int kPad = 8;          // bf16 padding of LDS rows
 constexpr int kRowT = T + kPad;  // row stride of [row][token] tiles
+// largest |a_t - a_m| (base-2 exponent) of the factored chunk term
+constexpr float kFactorLimit = 96.0f;
+constexpr int kRef = 31;         // reference token m of the factored decay
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -63,26 +78,34 @@ __device__ __forceinline__ void stage8(__bf16 *dst, const uint16_t *row, int64_t
   }
 }
 
-// 8 consecutive bf16 of a row (positions t .. t+7, those >= tend as 0) as
-// one 16-byte word; kVec: 16-byte load when all 8 are in range.
+// 8 consecutive bf16 of a row of length tend, positions t .. t+7, as one
+// 16-byte word, read unconditionally: positions past the row read some
+// element of the row instead (callers give them zero weight), so the load
+// has one path and no select on its result.  kVec: 16-byte aligned rows and
+// tend % 8 == 0, so a group of 8 is wholly in or wholly past the row.
 template <bool kVec>
-__device__ __forceinline__ uint4 load8(const uint16_t *row, int64_t t, int64_t tend) {
-  if (kVec && t + 8 <= tend) return *reinterpret_cast<const uint4 *>(row + t);
-  uint16_t v[8];
+__device__ __forceinline__ u32x4 load8_clamped(const uint16_t *row, int64_t t, int64_t tend) {
+  if (kVec) return *reinterpret_cast<const u32x4 *>(row + (t + 8 <= tend ? t : tend - 8));
+  u32x4 w;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = t + i < tend ? row[t + i] : uint16_t(0);
-  return make_uint4(v[0] | (uint32_t(v[1]) << 16), v[2] | (uint32_t(v[3]) << 16),
-                    v[4] | (uint32_t(v[5]) << 16), v[6] | (uint32_t(v[7]) << 16));
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = row[t + 2 * i < tend ? t + 2 * i : tend - 1];
+    const uint32_t hi = row[t + 2 * i + 1 < tend ? t + 2 * i + 1 : tend - 1];
+    w[i] = lo | (hi << 16);
+  }
+  return w;
 }
 
 // ----------------------------------------------------------- chunk prep ---
-// Per (batch, group, chunk): G = C^T B (64 x 64 fp32) and C transposed to
+// Per (batch, group, chunk): the causal G = C^T B (64 x 64, [t][s], zero
+// for s > t) as bf16 G_hi and G_lo = bf16(G - G_hi), and C transposed to
 // [token][state] (the layout the y product reads).  Positions past L are 0.
 template <int N, bool kVec>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
   constexpr int kRowN = N + kPad;
-  __shared__ __bf16 CtL[T * kRowN];  // [t][n]
-  __shared__ __bf16 BtL[T * kRowN];  // [s][n]
+  __shared__ __align__(16) __bf16 CtL[T * kRowN];  // [t][n]
+  __shared__ __align__(16) __bf16 BtL[T * kRowN];  // [s][n]
+  __shared__ __align__(16) __bf16 GL[2][T * kRowT];  // [t][s]: hi, lo
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -106,7 +129,6 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
   __syncthreads();
 
   // G rows 16*wave .. +16 (t), all 64 columns (s); K = N
-  float *Gc = p.G + (bg * p.nchunks + c) * T * T;
 #pragma unroll
   for (int sj = 0; sj < T / 16; ++sj) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -116,9 +138,22 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
       const bf16x8 bb = lds8(&BtL[(16 * sj + (lane & 15)) * kRowN + 32 * ks + 8 * (lane >> 4)]);
       acc = mfma(a, bb, acc);
     }
+    const int s = 16 * sj + (lane & 15);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      Gc[(16 * wave + 4 * (lane >> 4) + e) * T + 16 * sj + (lane & 15)] = acc[e];
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * wave + 4 * (lane >> 4) + e;
+      const float gv = s <= t ? acc[e] : 0.0f;
+      const __bf16 hi = static_cast<__bf16>(gv);
+      GL[0][t * kRowT + s] = hi;
+      GL[1][t * kRowT + s] = static_cast<__bf16>(gv - static_cast<float>(hi));
+    }
+  }
+  __syncthreads();
+  uint16_t *Gw = static_cast<uint16_t *>(p.G) + (bg * p.nchunks + c) * 2 * T * T;
+  for (int q = tid; q < 2 * T * (T / 8); q += 256) {
+    const int part = q / (T * (T / 8)), t = (q / (T / 8)) % T, s8 = (q % (T / 8)) * 8;
+    *reinterpret_cast<uint4 *>(Gw + (part * T + t) * T + s8) =
+        *reinterpret_cast<const uint4 *>(&GL[part][t * kRowT + s8]);
   }
   // C^T of this chunk, [t][n] contiguous
   uint16_t *Ctw = static_cast<uint16_t *>(p.Ct) + (bg * p.nchunks + c) * T * N;
@@ -130,240 +165,356 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
 }
 
 // ------------------------------------------------------------- the scan ---
-template <int N, bool kVec>
-__global__ __launch_bounds__(256) void ssd_kernel(SsdArgs p) {
+// One workgroup = one (batch, head) and R = 16*RP of the head's 64 rows (the
+// rows of the state are independent; splitting them across workgroups buys
+// parallelism at the price of re-reading the group's B, C^T and G).  kW = 4
+// or 8 waves: wave w takes token tile tt = w % 4 and row group w / 4 (the
+// row tiles split over kW/4 groups); per chunk it computes the y tiles of
+// tokens 16 tt .. 16 tt + 15 of its row tiles and owns their state tiles of
+// states [tt N/4, (tt+1) N/4).  The products are set up transposed (token
+// or state as the matrix-core row index) so that a lane holds 4 consecutive
+// tokens or states of one row.
+//
+// Each wave reads its own rows of C^T and G (the y products) and of B (the
+// state update), so those go from memory straight into operand registers;
+// the next chunk's are requested right after the last use.  LDS holds what
+// the waves share: x (plain, times v, times w), z (then y), the state
+// entering the chunk, and per-wave copies of the chunk's step quantities.
+//
+// Per chunk: the state tiles into LDS; barrier; the products, the new state,
+// y into LDS; barrier; coalesced y stores, the next chunk's step quantities
+// (each wave for itself) and its x, z into LDS.
+template <int N, bool kVec, int RP, int kW>
+__global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
+  constexpr int R = 16 * RP;          // rows of the head in this workgroup
   constexpr int kRowN = N + kPad;
-  constexpr int kNT = N / 16;  // state tiles per wave
-  __shared__ __bf16 Xs[P * kRowT];   // [p][t]
-  __shared__ __bf16 Zs[P * kRowT];   // [p][t]: z, then y
-  __shared__ __bf16 Bs[N * kRowT];   // [n][t]
-  __shared__ __bf16 Cs[T * kRowN];   // [t][n]
-  __shared__ __bf16 Ms[T * kRowT];   // [t][s]
-  __shared__ __bf16 Ss[P * kRowN];   // [p][n]: the state entering the chunk
-  __shared__ float cums[T], dts[T], ets[T], wts[T];
+  constexpr int kNTW = N / 64;        // state tiles per wave (per row tile)
+  constexpr int kThreads = 64 * kW;
+  constexpr int RPW = RP / (kW / 4);  // row tiles per wave
+  static_assert((kW == 4 || kW == 8) && RPW >= 1 && RP % (kW / 4) == 0, "wave layout");
+  __shared__ __align__(16) __bf16 Xs[R * kRowT];   // [p][t]
+  __shared__ __align__(16) __bf16 XVs[R * kRowT];  // [p][t]: x_t v_t
+  __shared__ __align__(16) __bf16 XWs[R * kRowT];  // [p][t]: x_t w_t
+  __shared__ __align__(16) __bf16 Zs[R * kRowT];   // [p][t]: z, then y
+  __shared__ __align__(16) __bf16 Ss[2][R * kRowN];  // [p][n]: the state entering the chunk, hi, lo
+  // per wave: dt, cum, exp(a_t), u_t, v_t, w_t of the chunk
+  __shared__ __align__(16) float Wq[kW][6][T];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t h = blockIdx.x, b = blockIdx.y;
+  const int li = lane & 15, lq = lane >> 4;
+  const int tt = wave & 3;                       // token tile and state slice
+  const int pr = 16 * (wave >> 2) * RPW;         // first row (in the workgroup) of this wave
+  constexpr int kSplit = P / R;
+  const int64_t h = blockIdx.x / kSplit, b = blockIdx.y;
+  const int row0 = (blockIdx.x % kSplit) * R;
   const int64_t g = h / (p.nheads / p.ngroups);
   const int64_t bh = b * p.nheads + h;
   const int64_t bg = b * p.ngroups + g;
   const float Aq = p.A[h] * kLog2e;
   const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
   const float Dh = p.D ? p.D[h] : 0.0f;
-  const uint16_t *xh = static_cast<const uint16_t *>(p.x) + bh * P * p.L;
-  const uint16_t *zh = p.z ? static_cast<const uint16_t *>(p.z) + bh * P * p.L : nullptr;
-  const uint16_t *dth = static_cast<const uint16_t *>(p.dt) + bh * p.L;
-  const uint16_t *Bg = static_cast<const uint16_t *>(p.B) + bg * N * p.L;
-  uint16_t *yh = static_cast<uint16_t *>(p.y) + bh * P * p.L;
+  const int64_t L = p.L;
+  const uint16_t *xh = static_cast<const uint16_t *>(p.x) + (bh * P + row0) * L;
+  const uint16_t *zh = p.z ? static_cast<const uint16_t *>(p.z) + (bh * P + row0) * L : nullptr;
+  const uint16_t *dth = static_cast<const uint16_t *>(p.dt) + bh * L;
+  const uint16_t *Bg = static_cast<const uint16_t *>(p.B) + bg * N * L;
+  const uint16_t *Ctg = static_cast<const uint16_t *>(p.Ct) + bg * p.nchunks * T * N;
+  const uint16_t *Gg = static_cast<const uint16_t *>(p.G) + bg * p.nchunks * 2 * T * T;
+  uint16_t *yh = static_cast<uint16_t *>(p.y) + (bh * P + row0) * L;
+  float *qdt = Wq[wave][0], *qcum = Wq[wave][1], *qet = Wq[wave][2];
+  float *qu = Wq[wave][3], *qv = Wq[wave][4], *qw = Wq[wave][5];
+  const int kq = 8 * lq;                         // operand k offset of this lane
+  const int ta = 16 * tt + li;                   // token row of this lane's A operands
+  const int tq = 16 * tt + 4 * lq;               // first token of this lane's outputs
 
-  // this wave's rows of the state, in accumulator layout: S[k][e] =
-  // S[row 16*wave + 4*(lane/16) + e][state 16*k + lane%16]
-  f32x4 S[kNT];
-  const int prow = 16 * wave + 4 * (lane >> 4);
+  // State tiles in accumulator layout, transposed: S[pt][k][e] is the state
+  // of row pr + 16*pt + li, state n = 16*(kNTW*tt + k) + 4*lq + e.
+  f32x4 S[RPW][kNTW];
 #pragma unroll
-  for (int k = 0; k < kNT; ++k)
+  for (int pt = 0; pt < RPW; ++pt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S[k][e] = p.h0 ? p.h0[(bh * P + prow + e) * N + 16 * k + (lane & 15)] : 0.0f;
+    for (int k = 0; k < kNTW; ++k) {
+      const int n = 16 * (kNTW * tt + k) + 4 * lq;
+      if (p.h0) {  // 4-byte aligned rows: copied, not cast
+        __builtin_memcpy(&S[pt][k], p.h0 + (bh * P + row0 + pr + 16 * pt + li) * N + n, 16);
+      } else {
+        S[pt][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
 
-  // One thread's share of a chunk's inputs, loaded a chunk ahead into
-  // registers (x, z: 2 x 8 tokens of a row; B: N/32 x 8 tokens of a state;
-  // C^T: N/32 x 8 states of a token; G: 16 entries of row tid/4; dt: one
-  // token, wave 0) and written to LDS once the previous chunk is done.
-  constexpr int kXQ = P * (T / 8) / 256;   // 2
-  constexpr int kBQ = N * (T / 8) / 256;   // N/32
-  uint4 rx[kXQ], rz[kXQ], rb[kBQ], rc[kBQ];
-  float4 rg[4];
-  uint16_t rdt = 0;
-  const int gt = tid >> 2, gs0 = (tid & 3) * 16;  // this thread's G entries
-  auto fetch = [&](int c) {
+  // operand registers of the chunk being computed: C^T row ta (states
+  // 32 ks + kq ..), G row ta (tokens 32 ks + kq .., hi and lo), B rows of
+  // this wave's state tiles (tokens 32 ks + kq ..)
+  bf16x8 ca[N / 32], ga[2][2], ba[2][kNTW];
+  auto load_ct = [&](int c) __attribute__((always_inline)) {
+    const uint16_t *r = Ctg + (static_cast<int64_t>(c) * T + ta) * N + kq;
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks)
+      ca[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(r + 32 * ks));
+  };
+  auto load_g = [&](int c) __attribute__((always_inline)) {
+    const uint16_t *r = Gg + (static_cast<int64_t>(c) * 2 * T + ta) * T + kq;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        ga[part][ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4 *>(r + part * T * T + 32 * ks));
+  };
+  auto load_b = [&](int c) __attribute__((always_inline)) {
+    const int64_t t0 = static_cast<int64_t>(c) * T;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int k = 0; k < kNTW; ++k)
+        ba[ks][k] = __builtin_bit_cast(
+            bf16x8, load8_clamped<kVec>(Bg + (16 * (kNTW * tt + k) + li) * L,
+                                        t0 + 32 * ks + kq, L));
+  };
+  // x and z as 16-byte pieces of rows (for LDS; with fewer pieces than
+  // threads the upper threads repeat the lower ones' loads), dt one token a
+  // lane.  Every load is unconditional (z repeats x when there is no gate),
+  // so no register ever waits on a load just to be merged with another path.
+  constexpr int kXP = R * (T / 8);
+  constexpr int kXQ = (kXP + kThreads - 1) / kThreads;
+  const uint16_t *zsrc = zh ? zh : xh;
+  u32x4 rx[kXQ], rz[kXQ];
+  auto load_xz = [&](int c) __attribute__((always_inline)) {
     const int64_t t0 = static_cast<int64_t>(c) * T;
 #pragma unroll
     for (int i = 0; i < kXQ; ++i) {
-      const int q = tid + 256 * i, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
-      rx[i] = load8<kVec>(xh + r * p.L, t0 + t8, p.L);
-      if (zh) rz[i] = load8<kVec>(zh + r * p.L, t0 + t8, p.L);
+      const int q = (tid + kThreads * i) % kXP, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
+      rx[i] = load8_clamped<kVec>(xh + r * L, t0 + t8, L);
+      rz[i] = load8_clamped<kVec>(zsrc + r * L, t0 + t8, L);
     }
-#pragma unroll
-    for (int i = 0; i < kBQ; ++i) {
-      const int q = tid + 256 * i, n = q / (T / 8), t8 = (q % (T / 8)) * 8;
-      rb[i] = load8<kVec>(Bg + n * p.L, t0 + t8, p.L);
-    }
-    const uint16_t *Cw = static_cast<const uint16_t *>(p.Ct) + (bg * p.nchunks + c) * T * N;
-#pragma unroll
-    for (int i = 0; i < kBQ; ++i) {
-      const int q = tid + 256 * i, t = q / (N / 8), n8 = (q % (N / 8)) * 8;
-      rc[i] = *reinterpret_cast<const uint4 *>(Cw + t * N + n8);
-    }
-    const float4 *Gr = reinterpret_cast<const float4 *>(
-        p.G + ((bg * p.nchunks + c) * T + gt) * T + gs0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rg[i] = Gr[i];
-    if (wave == 0) rdt = t0 + lane < p.L ? dth[t0 + lane] : uint16_t(0);
   };
-  auto deposit = [&]() {
+  auto load_dt = [&](int c) __attribute__((always_inline)) {
+    const int64_t t = static_cast<int64_t>(c) * T + lane;
+    return dth[t < L ? t : L - 1];  // steps past L count as 0 in steps()
+  };
+
+  // The chunk's step quantities from its raw steps (one token a lane) into
+  // this wave's copy; returns whether the factored form is safe (wave-
+  // uniform: every lane of every wave sees the same values).
+  auto steps = [&](uint16_t raw16, int64_t t0) __attribute__((always_inline)) {
+    float v = 0.0f;
+    if (t0 + lane < L) {
+      const float raw = __uint_as_float(static_cast<uint32_t>(raw16) << 16) + bias;
+      v = p.softplus ? softplus_f(raw) : raw;
+    }
+    const float cum = wave_inclusive_sum(v);
+    const float a = Aq * cum;
+    float aend = lane_broadcast(a, kWaveLanes - 1);
+    float aref = lane_broadcast(a, kRef);
+    asm volatile("" : "+s"(aend), "+s"(aref));  // formed by the whole wave first
+    qdt[lane] = v;
+    qcum[lane] = cum;
+    qet[lane] = fast_exp2(a);                    // decay of the incoming state
+    qu[lane] = fast_exp2(a - aref);
+    qv[lane] = fast_exp2(aref - a) * v;
+    qw[lane] = fast_exp2(aend - a) * v;          // weight of token s in the new state
+    return !__any(!(fabsf(a - aref) <= kFactorLimit));
+  };
+  // x, x v, x w and z of the chunk into LDS (the step quantities of this
+  // wave's copy are complete: written by this wave, in order)
+  auto deposit = [&](bool factored) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kXQ; ++i) {
-      const int q = tid + 256 * i, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&Xs[r * kRowT + t8]) = rx[i];
-      if (zh) *reinterpret_cast<uint4 *>(&Zs[r * kRowT + t8]) = rz[i];
-    }
+      const int q = tid + kThreads * i, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
+      if (kXP % kThreads == 0 || q < kXP) {
+        *reinterpret_cast<u32x4 *>(&Xs[r * kRowT + t8]) = rx[i];
+        if (zh) *reinterpret_cast<u32x4 *>(&Zs[r * kRowT + t8]) = rz[i];
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, rx[i]);
+        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&qw[t8]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&qw[t8 + 4]);
+        bf16x8 o;
 #pragma unroll
-    for (int i = 0; i < kBQ; ++i) {
-      const int q = tid + 256 * i, n = q / (T / 8), t8 = (q % (T / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&Bs[n * kRowT + t8]) = rb[i];
-    }
+        for (int e = 0; e < 4; ++e) {
+          o[e] = static_cast<__bf16>(static_cast<float>(xv[e]) * w0[e]);
+          o[e + 4] = static_cast<__bf16>(static_cast<float>(xv[e + 4]) * w1[e]);
+        }
+        *reinterpret_cast<bf16x8 *>(&XWs[r * kRowT + t8]) = o;
+        if (factored) {
+          const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&qv[t8]);
+          const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&qv[t8 + 4]);
 #pragma unroll
-    for (int i = 0; i < kBQ; ++i) {
-      const int q = tid + 256 * i, t = q / (N / 8), n8 = (q % (N / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&Cs[t * kRowN + n8]) = rc[i];
+          for (int e = 0; e < 4; ++e) {
+            o[e] = static_cast<__bf16>(static_cast<float>(xv[e]) * v0[e]);
+            o[e + 4] = static_cast<__bf16>(static_cast<float>(xv[e + 4]) * v1[e]);
+          }
+          *reinterpret_cast<bf16x8 *>(&XVs[r * kRowT + t8]) = o;
+        }
+      }
     }
   };
-  fetch(0);
-  deposit();
-  float gcur[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    gcur[4 * i] = rg[i].x; gcur[4 * i + 1] = rg[i].y;
-    gcur[4 * i + 2] = rg[i].z; gcur[4 * i + 3] = rg[i].w;
-  }
-  uint16_t dtcur = rdt;
+
+  load_xz(0);
+  load_b(0);
+  load_ct(0);
+  load_g(0);
+  bool factored = steps(load_dt(0), 0);
+  deposit(factored);
+  uint16_t dtn = load_dt(1);
+  load_xz(p.nchunks > 1 ? 1 : 0);
 
 #pragma unroll 1
   for (int c = 0; c < p.nchunks; ++c) {
     const int64_t t0 = static_cast<int64_t>(c) * T;
-    // 1. steps, running sums and weights of the chunk (wave 0)
-    if (wave == 0) {
-      float v = 0.0f;
-      if (t0 + lane < p.L) {
-        const float raw = __uint_as_float(static_cast<uint32_t>(dtcur) << 16) + bias;
-        v = p.softplus ? softplus_f(raw) : raw;
+    const bool more = c + 1 < p.nchunks;
+    const int cn = more ? c + 1 : c;  // the chunk whose operands load next
+    // 1. the state entering the chunk as bf16 pairs, rows [p][n] (4 states
+    //    a lane)
+#pragma unroll
+    for (int pt = 0; pt < RPW; ++pt)
+#pragma unroll
+      for (int k = 0; k < kNTW; ++k) {
+        const int n = 16 * (kNTW * tt + k) + 4 * lq;
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = static_cast<__bf16>(S[pt][k][e]);
+          lo[e] = static_cast<__bf16>(S[pt][k][e] - static_cast<float>(hi[e]));
+        }
+        *reinterpret_cast<bf16x4 *>(&Ss[0][(pr + 16 * pt + li) * kRowN + n]) = hi;
+        *reinterpret_cast<bf16x4 *>(&Ss[1][(pr + 16 * pt + li) * kRowN + n]) = lo;
       }
-      float cum = wave_inclusive_sum(v);
-      float cend = lane_broadcast(cum, kWaveLanes - 1);
-      asm volatile("" : "+s"(cend));  // formed by the whole wave first
-      dts[lane] = v;
-      cums[lane] = cum;
-      ets[lane] = fast_exp2(Aq * cum);               // decay of the incoming state
-      wts[lane] = fast_exp2(Aq * (cend - cum)) * v;  // weight of token s in the new state
-    }
-    // 2. the state entering the chunk, as bf16 rows [p][n]
-#pragma unroll
-    for (int k = 0; k < kNT; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Ss[(prow + e) * kRowN + 16 * k + (lane & 15)] = static_cast<__bf16>(S[k][e]);
     __syncthreads();
-    if (c + 1 < p.nchunks) fetch(c + 1);  // in flight during this chunk's work
 
-    // 3. M = G o decay mask o dt_s, bf16 [t][s]; thread -> row gt, 16 columns
+    // 2. y^T tiles of tokens 16*wave.. : (C^T S^T)[t, p] (scaled by exp(a_t)
+    //    in the epilogue), then the chunk's own term; G is zero above the
+    //    diagonal, so the second 32 tokens of s only reach waves 2 and 3
+    // (independent accumulators for the two halves of the state pair and
+    // for each row tile keep the matrix-core chains short)
+    f32x4 ao[RPW], ad[RPW], ao2[RPW], ad2[RPW];
+#pragma unroll
+    for (int pt = 0; pt < RPW; ++pt) {
+      ao[pt] = ao2[pt] = ad[pt] = ad2[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks)
+#pragma unroll
+      for (int pt = 0; pt < RPW; ++pt) {
+        ao[pt] = mfma(ca[ks], lds8(&Ss[0][(pr + 16 * pt + li) * kRowN + 32 * ks + kq]), ao[pt]);
+        ao2[pt] = mfma(ca[ks], lds8(&Ss[1][(pr + 16 * pt + li) * kRowN + 32 * ks + kq]), ao2[pt]);
+      }
+    load_ct(cn);
+    const int nks = tt < 2 ? 1 : 2;
+    if (factored) {
+      // u_t (G (X diag v)^T)[t, p]
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        if (ks < nks)
+#pragma unroll
+          for (int pt = 0; pt < RPW; ++pt) {
+            const bf16x8 xv = lds8(&XVs[(pr + 16 * pt + li) * kRowT + 32 * ks + kq]);
+            ad[pt] = mfma(ga[0][ks], xv, ad[pt]);
+            ad2[pt] = mfma(ga[1][ks], xv, ad2[pt]);
+          }
+    } else {
+      // M[t, s] = G[t, s] exp(a_t - a_s) dt_s formed in the operand registers
+      const float ct = qcum[ta];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        if (ks < nks) {
+          const int s0 = 32 * ks + kq;
+          bf16x8 m;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float ex = s0 + e <= ta ? Aq * (ct - qcum[s0 + e]) : -INFINITY;
+            const float gv = static_cast<float>(ga[0][ks][e]) + static_cast<float>(ga[1][ks][e]);
+            m[e] = static_cast<__bf16>(gv * fast_exp2(ex) * qdt[s0 + e]);
+          }
+#pragma unroll
+          for (int pt = 0; pt < RPW; ++pt)
+            ad[pt] = mfma(m, lds8(&Xs[(pr + 16 * pt + li) * kRowT + 32 * ks + kq]), ad[pt]);
+        }
+    }
+    load_g(cn);
+
+    // 3. the state after the chunk: S^T <- exp(a_T) S^T + B (X w)^T
     {
-      const float ct = cums[gt];
-      __bf16 mv[16];
+      const float dend = qet[T - 1];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int sidx = gs0 + i;
-        const float m = gcur[i] * fast_exp2(Aq * (ct - cums[sidx])) * dts[sidx];
-        mv[i] = static_cast<__bf16>(sidx <= gt ? m : 0.0f);
-      }
-      *reinterpret_cast<bf16x8 *>(&Ms[gt * kRowT + gs0]) =
-          bf16x8{mv[0], mv[1], mv[2], mv[3], mv[4], mv[5], mv[6], mv[7]};
-      *reinterpret_cast<bf16x8 *>(&Ms[gt * kRowT + gs0 + 8]) =
-          bf16x8{mv[8], mv[9], mv[10], mv[11], mv[12], mv[13], mv[14], mv[15]};
-    }
-    __syncthreads();
-    // 4. y tiles of this wave's 16 rows: the incoming state's share
-    //    exp(A cum_t) (S C)[p, t], then the chunk's own X M^T
-    const int arow = 16 * wave + (lane & 15);  // A-operand row
-    const int kq = 8 * (lane >> 4);            // A/B-operand k offset
-    f32x4 acc[T / 16];
+      for (int pt = 0; pt < RPW; ++pt)
 #pragma unroll
-    for (int tj = 0; tj < T / 16; ++tj) {
-      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < kNTW; ++k) S[pt][k] *= dend;
 #pragma unroll
-      for (int ks = 0; ks < N / 32; ++ks)
-        a4 = mfma(lds8(&Ss[arow * kRowN + 32 * ks + kq]),
-                  lds8(&Cs[(16 * tj + (lane & 15)) * kRowN + 32 * ks + kq]), a4);
-      const float et = ets[16 * tj + (lane & 15)];
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a4[e] *= et;
+        for (int pt = 0; pt < RPW; ++pt) {
+          const bf16x8 xw = lds8(&XWs[(pr + 16 * pt + li) * kRowT + 32 * ks + kq]);
 #pragma unroll
-      for (int ks = 0; ks < T / 32; ++ks)
-        a4 = mfma(lds8(&Xs[arow * kRowT + 32 * ks + kq]),
-                  lds8(&Ms[(16 * tj + (lane & 15)) * kRowT + 32 * ks + kq]), a4);
-      acc[tj] = a4;
+          for (int k = 0; k < kNTW; ++k) S[pt][k] = mfma(ba[ks][k], xw, S[pt][k]);
+        }
+      load_b(cn);
     }
 
-    // 5. the state after the chunk: exp(A cum_T) S + (X w) B^T
+    // 4. y = exp(a_t) (C^T S^T) + u_t (own term) + D x, times silu(z); this
+    //    lane's 4 tokens replace z in Zs (each element has one owner)
     {
-      const float dend = fast_exp2(Aq * cums[T - 1]);
+      const f32x4 et = *reinterpret_cast<const f32x4 *>(&qet[tq]);
+      const f32x4 ut = factored ? *reinterpret_cast<const f32x4 *>(&qu[tq])
+                                : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int k = 0; k < kNT; ++k)
+      for (int pt = 0; pt < RPW; ++pt) {
+        const int r = pr + 16 * pt + li;
+        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&Xs[r * kRowT + tq]);
+        float yv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[k][e] *= dend;
+        for (int e = 0; e < 4; ++e)
+          yv[e] = et[e] * (ao[pt][e] + ao2[pt][e]) + ut[e] * (ad[pt][e] + ad2[pt][e]) +
+                  Dh * static_cast<float>(xv[e]);
+        if (zh) {
+          const bf16x4 zv = *reinterpret_cast<const bf16x4 *>(&Zs[r * kRowT + tq]);
 #pragma unroll
-      for (int ks = 0; ks < T / 32; ++ks) {
-        const bf16x8 xa = lds8(&Xs[arow * kRowT + 32 * ks + kq]);
-        bf16x8 xw;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          xw[i] = static_cast<__bf16>(static_cast<float>(xa[i]) * wts[32 * ks + kq + i]);
-#pragma unroll
-        for (int k = 0; k < kNT; ++k)
-          S[k] = mfma(xw, lds8(&Bs[(16 * k + (lane & 15)) * kRowT + 32 * ks + kq]), S[k]);
+          for (int e = 0; e < 4; ++e) yv[e] *= silu_f(static_cast<float>(zv[e]));
+        }
+        *reinterpret_cast<bf16x4 *>(&Zs[r * kRowT + tq]) =
+            bf16x4{static_cast<__bf16>(yv[0]), static_cast<__bf16>(yv[1]),
+                   static_cast<__bf16>(yv[2]), static_cast<__bf16>(yv[3])};
       }
     }
-
-    // 6. skip and gate; y of this lane's elements goes into Zs (each element
-    //    has one owner), then a coalesced store
+    __syncthreads();  // y complete; the chunk's tiles are free for the next one
+    // 5. coalesced y stores; the next chunk's step quantities, x and z (the
+    //    same thread reads a y piece before writing that piece's z)
 #pragma unroll
-    for (int tj = 0; tj < T / 16; ++tj) {
-      const int t = 16 * tj + (lane & 15);
+    for (int i = 0; i < kXQ; ++i) {
+      const int q = tid + kThreads * i, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
+      if (kXP % kThreads == 0 || q < kXP) {
+        const int64_t t = t0 + t8;
+        uint16_t *yr = yh + r * L + t;
+        if (kVec && t + 8 <= L) {
+          *reinterpret_cast<u32x4 *>(yr) = *reinterpret_cast<const u32x4 *>(&Zs[r * kRowT + t8]);
+        } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = prow + e;
-        float yv = acc[tj][e] + Dh * static_cast<float>(Xs[r * kRowT + t]);
-        if (zh) yv *= silu_f(static_cast<float>(Zs[r * kRowT + t]));
-        Zs[r * kRowT + t] = static_cast<__bf16>(yv);
+          for (int e = 0; e < 8; ++e)
+            if (t + e < L) yr[e] = __builtin_bit_cast(uint16_t, Zs[r * kRowT + t8 + e]);
+        }
       }
     }
-    __syncthreads();
-    for (int q = tid; q < P * (T / 8); q += 256) {
-      const int r = q / (T / 8), t8 = (q % (T / 8)) * 8;
-      const int64_t t = t0 + t8;
-      if (kVec && t + 8 <= p.L) {
-        *reinterpret_cast<uint4 *>(yh + r * p.L + t) =
-            *reinterpret_cast<const uint4 *>(&Zs[r * kRowT + t8]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (t + i < p.L)
-            yh[r * p.L + t + i] = __builtin_bit_cast(uint16_t, Zs[r * kRowT + t8 + i]);
-      }
-    }
-    __syncthreads();  // the chunk's tiles are free for the next one
-    if (c + 1 < p.nchunks) {
-      deposit();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gcur[4 * i] = rg[i].x; gcur[4 * i + 1] = rg[i].y;
-        gcur[4 * i + 2] = rg[i].z; gcur[4 * i + 3] = rg[i].w;
-      }
-      dtcur = rdt;
+    if (more) {
+      factored = steps(dtn, t0 + T);
+      deposit(factored);
+      dtn = load_dt(c + 2);
+      // x and z two chunks ahead: requested a whole chunk before they are
+      // written to LDS
+      load_xz(c + 2 < p.nchunks ? c + 2 : c + 1);
     }
   }
 
   if (p.h_final) {
 #pragma unroll
-    for (int k = 0; k < kNT; ++k)
+    for (int pt = 0; pt < RPW; ++pt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p.h_final[(bh * P + prow + e) * N + 16 * k + (lane & 15)] = S[k][e];
+      for (int k = 0; k < kNTW; ++k) {
+        const int n = 16 * (kNTW * tt + k) + 4 * lq;
+        __builtin_memcpy(p.h_final + (bh * P + row0 + pr + 16 * pt + li) * N + n, &S[pt][k], 16);
+      }
   }
 }
 
-template <int N, bool kVec>
+template <int N, bool kVec, int RP, int kW>
 hipError_t launch_ssd_t(const SsdArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((ssd_prep_kernel<N, kVec>),
                      dim3(static_cast<unsigned>(a.nchunks), static_cast<unsigned>(a.ngroups),
@@ -371,10 +522,36 @@ hipError_t launch_ssd_t(const SsdArgs &a, hipStream_t s) {
                      dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ssd_kernel<N, kVec>),
-                     dim3(static_cast<unsigned>(a.nheads), static_cast<unsigned>(a.batch)),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ssd_kernel<N, kVec, RP, kW>),
+                     dim3(static_cast<unsigned>(a.nheads * (P / (16 * RP))),
+                          static_cast<unsigned>(a.batch)),
+                     dim3(64 * kW), 0, s, a);
   return hipGetLastError();
+}
+
+// Waves per workgroup (4 or 8; 8 measured slower on the 80-head layer: the
+// extra waves repeat the loads of C^T, G and B and the step quantities).
+#ifndef SSM_SSD_WAVES
+#define SSM_SSD_WAVES 4
+#endif
+
+// Rows of a head per workgroup: the fewest splits that still give one
+// workgroup per compute unit (256), since each split re-reads the group's B,
+// C^T and G and repeats the step quantities.  SSM_SSD_RP fixes the choice
+// (row tiles of 16 per workgroup) for measurements.
+template <int N, bool kVec>
+hipError_t launch_ssd_n(const SsdArgs &a, hipStream_t s) {
+  constexpr int kW = SSM_SSD_WAVES;
+  const int64_t seqs = a.batch * a.nheads;
+  constexpr int64_t kCUs = 256;
+#ifdef SSM_SSD_RP
+  const int rp = SSM_SSD_RP;
+#else
+  const int rp = seqs >= kCUs ? 4 : 2 * seqs >= kCUs ? 2 : 1;
+#endif
+  if (rp == 4) return launch_ssd_t<N, kVec, 4, kW>(a, s);
+  if (rp == 2 || kW == 8) return launch_ssd_t<N, kVec, 2, kW>(a, s);
+  return launch_ssd_t<N, kVec, 1, 4>(a, s);
 }
 
 }  // namespace
@@ -383,11 +560,11 @@ int launch_ssd(const SsdArgs &a, bool vec, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (a.dstate) {
     case 64:
-      return vec ? launch_ssd_t<64, true>(a, s) : launch_ssd_t<64, false>(a, s);
+      return vec ? launch_ssd_n<64, true>(a, s) : launch_ssd_n<64, false>(a, s);
     case 128:
-      return vec ? launch_ssd_t<128, true>(a, s) : launch_ssd_t<128, false>(a, s);
+      return vec ? launch_ssd_n<128, true>(a, s) : launch_ssd_n<128, false>(a, s);
     case 256:
-      return vec ? launch_ssd_t<256, true>(a, s) : launch_ssd_t<256, false>(a, s);
+      return vec ? launch_ssd_n<256, true>(a, s) : launch_ssd_n<256, false>(a, s);
     default:
       return static_cast<int>(hipErrorInvalidValue);
   }

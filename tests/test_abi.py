@@ -340,5 +340,5 @@ def test_ssd_workspace_size(lib):
     size = ctypes.c_size_t(0)
     assert lib.ssm_ssd_workspace_size(2, 1, 128, 4096, ctypes.byref(size)) == 0
     chunks = 2 * 1 * 64
-    assert size.value >= chunks * (64 * 64 * 4 + 64 * 128 * 2)
+    assert size.value >= chunks * (2 * 64 * 64 * 2 + 64 * 128 * 2)
     assert lib.ssm_ssd_workspace_size(2, 1, 100, 4096, ctypes.byref(size)) == 2
