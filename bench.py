@@ -16,6 +16,7 @@ on its stream over the timed region) to the ALU ceiling that bounds it.
 
 Options beyond the contract: --no-cpu-baseline, --no-extra (skip the
 long-context and decode figures), --only-scan (nothing but the timed steps;
+for profiler runs), --only-ssd (only the Mamba-2 SSD figure, --steps calls;
 for profiler runs), --summarize DIR (no GPU: turn the rocprofv3 CSV output
 of the profiling commands below into the summaries under profiles/).
 
@@ -26,6 +27,10 @@ Profiling commands (run from /tmp with TMPDIR=/tmp; DIR = an output folder):
       -- python3 bench.py --steps 3 --warmup 1 --no-extra --no-cpu-baseline
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o write \
       -- python3 bench.py --steps 3 --warmup 1 --no-extra --no-cpu-baseline
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/ssdfetch -o ssdfetch \
+      -- python3 bench.py --only-ssd --steps 3
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/ssdwrite -o ssdwrite \
+      -- python3 bench.py --only-ssd --steps 3
   python3 bench.py --summarize DIR
 """
 from __future__ import annotations
@@ -81,6 +86,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only-scan", action="store_true")
+    ap.add_argument("--only-ssd", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     args = ap.parse_args()
     if args.summarize:
@@ -99,6 +105,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = ssm.load_library()
+    if args.only_ssd:
+        stream = torch.cuda.current_stream(dev)
+        r = ssd_measure(ssm, syn, dev, stream, args.steps,
+                        lambda m: print("[bench] " + m, file=sys.stderr, flush=True))
+        print(json.dumps({syn.MAMBA2_LAYER.name: r}))
+        return
     cfg = syn.MAMBA_2P8B
     E = cfg.elements
     nbytes = syn.algorithmic_bytes(cfg)
@@ -346,6 +358,9 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     del binp, bdy, bws, bout
     torch.cuda.empty_cache()
 
+    out[syn.MAMBA2_LAYER.name] = ssd_measure(ssm, syn, dev, stream, reps, log)
+    torch.cuda.empty_cache()
+
     dcfg = syn.DECODE
     log("decode workload %s" % dcfg.name)
     dinp = syn.make_decode_inputs(dcfg, dev)
@@ -372,6 +387,46 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
                       "GBps": round(nb / (us * 1e-6) / 1e9, 1),
                       "bytes_per_step": nb}
     return out
+
+
+def ssd_measure(ssm, syn, dev, stream, reps, log):
+    """Mamba-2 SSD form (one scalar decay per head, matrix-core chunk
+    products) on an 80-head layer; workspace and outputs allocated up front,
+    inputs resident before the timed calls."""
+    import torch
+    scfg = syn.MAMBA2_LAYER
+    log("SSD form on %s" % scfg.name)
+    sinp = syn.make_ssd_inputs(scfg, dev)
+    sws = torch.empty(ssm.ssm_ssd_workspace_size(
+        scfg.batch, scfg.ngroups, scfg.dstate, scfg.seqlen),
+        dtype=torch.uint8, device=dev)
+    sy = torch.empty_like(sinp["x"])
+    shf = torch.empty(scfg.batch, scfg.nheads, scfg.headdim, scfg.dstate,
+                      device=dev)
+
+    def srun():
+        ssm.ssm_ssd_fwd(sinp["x"], sinp["dt"], sinp["A"], sinp["B"], sinp["C"],
+                        sinp["D"], sinp["z"], sinp["dt_bias"], True, None,
+                        y=sy, h_final=shf, workspace=sws, stream=stream)
+    srun()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        srun()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb, nf = syn.ssd_bytes(scfg), syn.ssd_flops(scfg)
+    return {
+        "ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+        "TFLOPs": round(nf / (ms * 1e-3) / 1e12, 1),
+        "hbm_frac": round(nb / (ms * 1e-3) / 8.0e12, 4),
+        "algorithmic_bytes": nb, "flops": nf,
+        "workspace_bytes": sws.numel(),
+        "note": "prep (causal C^T B as a bf16 pair, C^T) + chunked scan; "
+                "bound by per-chunk latency, not by HBM or the matrix cores"}
 
 
 def cpu_baseline(inp, cfg, nbytes, log):
@@ -410,7 +465,9 @@ def _csvs(d, suffix):
 
 
 def _kernel_key(name):
-    return name.replace("void ssm::(anonymous namespace)::", "").split("(")[0]
+    # demangled names come with or without the "void " of the return type
+    n = name.replace("void ", "", 1) if name.startswith("void ssm::") else name
+    return n.replace("ssm::(anonymous namespace)::", "").split("(")[0]
 
 
 def summarize_profiles(d):
@@ -524,7 +581,54 @@ def summarize_profiles(d):
         with open(os.path.join(prof, "scan_kernel_mamba2p8b_sq_counters.txt"),
                   "w") as f:
             f.write("\n".join(sq_txt) + "\n")
-    print("\n".join(lines + txt + sq_txt))
+    ssd_txt = summarize_ssd(d, rows, per_dispatch, fetch_scale, write_scale,
+                            cmd_trace, prof)
+    print("\n".join(lines + txt + sq_txt + ssd_txt))
+
+
+def summarize_ssd(d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace,
+                  prof):
+    """profiles/ssd_kernel_mamba2_b2_h80_p64_n128_l4096.txt: the SSD
+    kernels' trace statistics (from the full benchmark run) and their HBM
+    traffic (from the --only-ssd counter passes, scaled by the same copy
+    calibration as the scan kernel's)."""
+    import synthetic as syn
+    scfg = syn.MAMBA2_LAYER
+    txt = ["# Mamba-2 SSD form, workload " + scfg.name,
+           "# kernel statistics from: " + cmd_trace,
+           "# kernel | calls | average us | min us | max us | total ms"]
+    for r in rows:
+        k = _kernel_key(r["Name"])
+        if k.startswith("ssd_"):
+            txt.append("%s | %s | %.2f | %.2f | %.2f | %.3f" % (
+                k[:90], r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                float(r["TotalDurationNs"]) / 1e6))
+    if not os.path.isdir(os.path.join(d, "ssdfetch")):
+        return []
+    fetch = per_dispatch("ssdfetch", "FETCH_SIZE")
+    write = per_dispatch("ssdwrite", "WRITE_SIZE")
+    cmd = ("rocprofv3 --pmc {c} --output-format csv -d DIR/{d} -o {d} -- "
+           "python3 bench.py --only-ssd --steps 3")
+    txt += ["# HBM traffic per dispatch from (from /tmp, TMPDIR=/tmp):",
+            "#   " + cmd.format(c="FETCH_SIZE", d="ssdfetch"),
+            "#   " + cmd.format(c="WRITE_SIZE", d="ssdwrite"),
+            "# scaled by the 1 GiB copy calibration (fetch x %.3f, write x %.3f)"
+            % (fetch_scale, write_scale)]
+    total = 0.0
+    for k in sorted(fetch):
+        if not k.startswith("ssd_") or k not in write:
+            continue
+        fb = fetch[k] * fetch_scale * 1024
+        wb = write[k] * write_scale * 1024
+        total += fb + wb
+        txt.append("%s: read %.1f MB, written %.1f MB" % (k, fb / 1e6, wb / 1e6))
+    alg = syn.ssd_bytes(scfg)
+    txt.append("both kernels: %.1f MB per call vs algorithmic %.1f MB (ratio %.3f)"
+               % (total / 1e6, alg / 1e6, total / alg))
+    with open(os.path.join(prof, "ssd_kernel_%s.txt" % scfg.name), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    return txt
 
 
 if __name__ == "__main__":
