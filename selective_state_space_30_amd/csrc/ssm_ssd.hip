@@ -178,12 +178,16 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
 // Each wave reads its own rows of C^T and G (the y products) and of B (the
 // state update), so those go from memory straight into operand registers;
 // the next chunk's are requested right after the last use.  LDS holds what
-// the waves share: x (plain, times v, times w), z (then y), the state
-// entering the chunk, and per-wave copies of the chunk's step quantities.
+// the waves share, double-buffered by chunk parity: x, x v and x w, z then
+// y, the state entering the chunk (a bf16 pair), and the chunk's step
+// quantities (every wave computes them and writes the same values; a wave
+// reads only after its own write).
 //
-// Per chunk: the state tiles into LDS; barrier; the products, the new state,
-// y into LDS; barrier; coalesced y stores, the next chunk's step quantities
-// (each wave for itself) and its x, z into LDS.
+// One barrier per chunk c: before it, the state entering c into LDS; after
+// it, the y stores of chunk c-1, the step quantities and the x, z deposit of
+// chunk c+1, then chunk c's products, new state and y (into LDS).  A buffer
+// of parity c is written again only in iteration c+1 (deposit of c+2) or
+// c+2 (state), after every wave has passed the barrier that ends its reads.
 template <int N, bool kVec, int RP, int kW>
 __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   constexpr int R = 16 * RP;          // rows of the head in this workgroup
@@ -192,13 +196,13 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   constexpr int kThreads = 64 * kW;
   constexpr int RPW = RP / (kW / 4);  // row tiles per wave
   static_assert((kW == 4 || kW == 8) && RPW >= 1 && RP % (kW / 4) == 0, "wave layout");
-  __shared__ __align__(16) __bf16 Xs[R * kRowT];   // [p][t]
-  __shared__ __align__(16) __bf16 XVs[R * kRowT];  // [p][t]: x_t v_t
-  __shared__ __align__(16) __bf16 XWs[R * kRowT];  // [p][t]: x_t w_t
-  __shared__ __align__(16) __bf16 Zs[R * kRowT];   // [p][t]: z, then y
-  __shared__ __align__(16) __bf16 Ss[2][R * kRowN];  // [p][n]: the state entering the chunk, hi, lo
-  // per wave: dt, cum, exp(a_t), u_t, v_t, w_t of the chunk
-  __shared__ __align__(16) float Wq[kW][6][T];
+  __shared__ __align__(16) __bf16 Xs[2][R * kRowT];     // [p][t]: x_t
+  __shared__ __align__(16) __bf16 XVs[2][R * kRowT];    // [p][t]: x_t v_t
+  __shared__ __align__(16) __bf16 XWs[2][R * kRowT];    // [p][t]: x_t w_t
+  __shared__ __align__(16) __bf16 Zs[2][R * kRowT];     // [p][t]: z, then y
+  __shared__ __align__(16) __bf16 Ss[2][2][R * kRowN];  // [p][n]: entering state, hi, lo
+  // dt, cum, exp(a_t), u_t, v_t, w_t of the chunk
+  __shared__ __align__(16) float Wq[2][6][T];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,15 +219,14 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
   const float Dh = p.D ? p.D[h] : 0.0f;
   const int64_t L = p.L;
+  const int nch = p.nchunks;
   const uint16_t *xh = static_cast<const uint16_t *>(p.x) + (bh * P + row0) * L;
   const uint16_t *zh = p.z ? static_cast<const uint16_t *>(p.z) + (bh * P + row0) * L : nullptr;
   const uint16_t *dth = static_cast<const uint16_t *>(p.dt) + bh * L;
   const uint16_t *Bg = static_cast<const uint16_t *>(p.B) + bg * N * L;
-  const uint16_t *Ctg = static_cast<const uint16_t *>(p.Ct) + bg * p.nchunks * T * N;
-  const uint16_t *Gg = static_cast<const uint16_t *>(p.G) + bg * p.nchunks * 2 * T * T;
+  const uint16_t *Ctg = static_cast<const uint16_t *>(p.Ct) + bg * nch * T * N;
+  const uint16_t *Gg = static_cast<const uint16_t *>(p.G) + bg * nch * 2 * T * T;
   uint16_t *yh = static_cast<uint16_t *>(p.y) + (bh * P + row0) * L;
-  float *qdt = Wq[wave][0], *qcum = Wq[wave][1], *qet = Wq[wave][2];
-  float *qu = Wq[wave][3], *qv = Wq[wave][4], *qw = Wq[wave][5];
   const int kq = 8 * lq;                         // operand k offset of this lane
   const int ta = 16 * tt + li;                   // token row of this lane's A operands
   const int tq = 16 * tt + 4 * lq;               // first token of this lane's outputs
@@ -295,9 +298,9 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   };
 
   // The chunk's step quantities from its raw steps (one token a lane) into
-  // this wave's copy; returns whether the factored form is safe (wave-
-  // uniform: every lane of every wave sees the same values).
-  auto steps = [&](uint16_t raw16, int64_t t0) __attribute__((always_inline)) {
+  // q[0..5]; returns whether the factored form is safe (wave-uniform: every
+  // lane of every wave sees the same values).
+  auto steps = [&](uint16_t raw16, int64_t t0, float (*q)[T]) __attribute__((always_inline)) {
     float v = 0.0f;
     if (t0 + lane < L) {
       const float raw = __uint_as_float(static_cast<uint32_t>(raw16) << 16) + bias;
@@ -308,61 +311,103 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     float aend = lane_broadcast(a, kWaveLanes - 1);
     float aref = lane_broadcast(a, kRef);
     asm volatile("" : "+s"(aend), "+s"(aref));  // formed by the whole wave first
-    qdt[lane] = v;
-    qcum[lane] = cum;
-    qet[lane] = fast_exp2(a);                    // decay of the incoming state
-    qu[lane] = fast_exp2(a - aref);
-    qv[lane] = fast_exp2(aref - a) * v;
-    qw[lane] = fast_exp2(aend - a) * v;          // weight of token s in the new state
+    q[0][lane] = v;
+    q[1][lane] = cum;
+    q[2][lane] = fast_exp2(a);                   // decay of the incoming state
+    q[3][lane] = fast_exp2(a - aref);
+    q[4][lane] = fast_exp2(aref - a) * v;
+    q[5][lane] = fast_exp2(aend - a) * v;        // weight of token s in the new state
     return !__any(!(fabsf(a - aref) <= kFactorLimit));
   };
-  // x, x v, x w and z of the chunk into LDS (the step quantities of this
-  // wave's copy are complete: written by this wave, in order)
-  auto deposit = [&](bool factored) __attribute__((always_inline)) {
+  // x, x v, x w and z of a chunk into the LDS buffers of parity `buf` (the
+  // step quantities q were just written by this wave, in order)
+  auto deposit = [&](bool factored, int buf, float (*q)[T]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kXQ; ++i) {
-      const int q = tid + kThreads * i, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
-      if (kXP % kThreads == 0 || q < kXP) {
-        *reinterpret_cast<u32x4 *>(&Xs[r * kRowT + t8]) = rx[i];
-        if (zh) *reinterpret_cast<u32x4 *>(&Zs[r * kRowT + t8]) = rz[i];
+      const int pc = tid + kThreads * i, r = pc / (T / 8), t8 = (pc % (T / 8)) * 8;
+      if (kXP % kThreads == 0 || pc < kXP) {
+        *reinterpret_cast<u32x4 *>(&Xs[buf][r * kRowT + t8]) = rx[i];
+        if (zh) *reinterpret_cast<u32x4 *>(&Zs[buf][r * kRowT + t8]) = rz[i];
         const bf16x8 xv = __builtin_bit_cast(bf16x8, rx[i]);
-        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&qw[t8]);
-        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&qw[t8 + 4]);
+        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&q[5][t8]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&q[5][t8 + 4]);
         bf16x8 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           o[e] = static_cast<__bf16>(static_cast<float>(xv[e]) * w0[e]);
           o[e + 4] = static_cast<__bf16>(static_cast<float>(xv[e + 4]) * w1[e]);
         }
-        *reinterpret_cast<bf16x8 *>(&XWs[r * kRowT + t8]) = o;
+        *reinterpret_cast<bf16x8 *>(&XWs[buf][r * kRowT + t8]) = o;
         if (factored) {
-          const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&qv[t8]);
-          const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&qv[t8 + 4]);
+          const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&q[4][t8]);
+          const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&q[4][t8 + 4]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             o[e] = static_cast<__bf16>(static_cast<float>(xv[e]) * v0[e]);
             o[e + 4] = static_cast<__bf16>(static_cast<float>(xv[e + 4]) * v1[e]);
           }
-          *reinterpret_cast<bf16x8 *>(&XVs[r * kRowT + t8]) = o;
+          *reinterpret_cast<bf16x8 *>(&XVs[buf][r * kRowT + t8]) = o;
+        }
+      }
+    }
+  };
+  // coalesced y stores of chunk c: this thread's pieces of the y in
+  // Zs[buf] are read into registers first (the deposit of chunk c+2 reuses
+  // the buffer), and the stores go out after the deposit, so that its wait
+  // for x and z does not also wait for them
+  u32x4 ry[kXQ];
+  auto read_y = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kXQ; ++i) {
+      const int pc = tid + kThreads * i, r = pc / (T / 8), t8 = (pc % (T / 8)) * 8;
+      if (kXP % kThreads == 0 || pc < kXP)
+        ry[i] = *reinterpret_cast<const u32x4 *>(&Zs[buf][r * kRowT + t8]);
+    }
+  };
+  auto store_y = [&](int c) __attribute__((always_inline)) {
+    const int64_t t0 = static_cast<int64_t>(c) * T;
+#pragma unroll
+    for (int i = 0; i < kXQ; ++i) {
+      const int pc = tid + kThreads * i, r = pc / (T / 8), t8 = (pc % (T / 8)) * 8;
+      if (kXP % kThreads == 0 || pc < kXP) {
+        const int64_t t = t0 + t8;
+        uint16_t *yr = yh + r * L + t;
+        if (kVec && t + 8 <= L) {
+          *reinterpret_cast<u32x4 *>(yr) = ry[i];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t w = ry[i][e >> 1];
+            if (t + e < L) yr[e] = static_cast<uint16_t>((e & 1) ? w >> 16 : w);
+          }
         }
       }
     }
   };
 
+  // The loads are issued in the order the loop issues them (x and z of the
+  // next chunk, then this chunk's operand rows): the wait counters retire
+  // in order, and a different order at the loop entry makes the compiler
+  // wait for every load in flight before the deposit.
   load_xz(0);
-  load_b(0);
-  load_ct(0);
-  load_g(0);
-  bool factored = steps(load_dt(0), 0);
-  deposit(factored);
+  bool factored = steps(load_dt(0), 0, Wq[0]);
+  deposit(factored, 0, Wq[0]);
   uint16_t dtn = load_dt(1);
-  load_xz(p.nchunks > 1 ? 1 : 0);
+  load_xz(nch > 1 ? 1 : 0);
+  __builtin_amdgcn_sched_barrier(0);  // keep that order through scheduling
+  load_ct(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_g(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_b(0);
 
 #pragma unroll 1
-  for (int c = 0; c < p.nchunks; ++c) {
+  for (int c = 0; c < nch; ++c) {
     const int64_t t0 = static_cast<int64_t>(c) * T;
-    const bool more = c + 1 < p.nchunks;
+    const int cur = c & 1, nxt = cur ^ 1;
+    const bool more = c + 1 < nch;
     const int cn = more ? c + 1 : c;  // the chunk whose operands load next
+    float (*q)[T] = Wq[cur];
     // 1. the state entering the chunk as bf16 pairs, rows [p][n] (4 states
     //    a lane)
 #pragma unroll
@@ -376,16 +421,29 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
           hi[e] = static_cast<__bf16>(S[pt][k][e]);
           lo[e] = static_cast<__bf16>(S[pt][k][e] - static_cast<float>(hi[e]));
         }
-        *reinterpret_cast<bf16x4 *>(&Ss[0][(pr + 16 * pt + li) * kRowN + n]) = hi;
-        *reinterpret_cast<bf16x4 *>(&Ss[1][(pr + 16 * pt + li) * kRowN + n]) = lo;
+        *reinterpret_cast<bf16x4 *>(&Ss[cur][0][(pr + 16 * pt + li) * kRowN + n]) = hi;
+        *reinterpret_cast<bf16x4 *>(&Ss[cur][1][(pr + 16 * pt + li) * kRowN + n]) = lo;
       }
     __syncthreads();
+    // 2. the previous chunk's y out; the next chunk's step quantities, x w,
+    //    x v and z in (x and z were requested a chunk ago)
+    if (c > 0) read_y(nxt);
+    bool factored_next = false;
+    if (more) {
+      factored_next = steps(dtn, t0 + T, Wq[nxt]);
+      deposit(factored_next, nxt, Wq[nxt]);
+    }
+    if (c > 0) store_y(c - 1);
+    if (more) {
+      dtn = load_dt(c + 2);
+      load_xz(c + 2 < nch ? c + 2 : c + 1);
+    }
 
-    // 2. y^T tiles of tokens 16*wave.. : (C^T S^T)[t, p] (scaled by exp(a_t)
+    // 3. y^T tiles of tokens 16*tt.. : (C^T S^T)[t, p] (scaled by exp(a_t)
     //    in the epilogue), then the chunk's own term; G is zero above the
-    //    diagonal, so the second 32 tokens of s only reach waves 2 and 3
-    // (independent accumulators for the two halves of the state pair and
-    // for each row tile keep the matrix-core chains short)
+    //    diagonal, so the second 32 tokens of s only reach token tiles 2, 3
+    //    (independent accumulators for the two halves of each pair keep the
+    //    matrix-core chains short)
     f32x4 ao[RPW], ad[RPW], ao2[RPW], ad2[RPW];
 #pragma unroll
     for (int pt = 0; pt < RPW; ++pt) {
@@ -395,8 +453,8 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     for (int ks = 0; ks < N / 32; ++ks)
 #pragma unroll
       for (int pt = 0; pt < RPW; ++pt) {
-        ao[pt] = mfma(ca[ks], lds8(&Ss[0][(pr + 16 * pt + li) * kRowN + 32 * ks + kq]), ao[pt]);
-        ao2[pt] = mfma(ca[ks], lds8(&Ss[1][(pr + 16 * pt + li) * kRowN + 32 * ks + kq]), ao2[pt]);
+        ao[pt] = mfma(ca[ks], lds8(&Ss[cur][0][(pr + 16 * pt + li) * kRowN + 32 * ks + kq]), ao[pt]);
+        ao2[pt] = mfma(ca[ks], lds8(&Ss[cur][1][(pr + 16 * pt + li) * kRowN + 32 * ks + kq]), ao2[pt]);
       }
     load_ct(cn);
     const int nks = tt < 2 ? 1 : 2;
@@ -407,13 +465,14 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
         if (ks < nks)
 #pragma unroll
           for (int pt = 0; pt < RPW; ++pt) {
-            const bf16x8 xv = lds8(&XVs[(pr + 16 * pt + li) * kRowT + 32 * ks + kq]);
+            const bf16x8 xv = lds8(&XVs[cur][(pr + 16 * pt + li) * kRowT + 32 * ks + kq]);
             ad[pt] = mfma(ga[0][ks], xv, ad[pt]);
             ad2[pt] = mfma(ga[1][ks], xv, ad2[pt]);
           }
     } else {
-      // M[t, s] = G[t, s] exp(a_t - a_s) dt_s formed in the operand registers
-      const float ct = qcum[ta];
+      // M[t, s] = G[t, s] exp(a_t - a_s) dt_s formed in the operand
+      // registers
+      const float ct = q[1][ta];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         if (ks < nks) {
@@ -421,20 +480,20 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
           bf16x8 m;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float ex = s0 + e <= ta ? Aq * (ct - qcum[s0 + e]) : -INFINITY;
+            const float ex = s0 + e <= ta ? Aq * (ct - q[1][s0 + e]) : -INFINITY;
             const float gv = static_cast<float>(ga[0][ks][e]) + static_cast<float>(ga[1][ks][e]);
-            m[e] = static_cast<__bf16>(gv * fast_exp2(ex) * qdt[s0 + e]);
+            m[e] = static_cast<__bf16>(gv * fast_exp2(ex) * q[0][s0 + e]);
           }
 #pragma unroll
           for (int pt = 0; pt < RPW; ++pt)
-            ad[pt] = mfma(m, lds8(&Xs[(pr + 16 * pt + li) * kRowT + 32 * ks + kq]), ad[pt]);
+            ad[pt] = mfma(m, lds8(&Xs[cur][(pr + 16 * pt + li) * kRowT + s0]), ad[pt]);
         }
     }
     load_g(cn);
 
-    // 3. the state after the chunk: S^T <- exp(a_T) S^T + B (X w)^T
+    // 4. the state after the chunk: S^T <- exp(a_T) S^T + B (X w)^T
     {
-      const float dend = qet[T - 1];
+      const float dend = q[2][T - 1];
 #pragma unroll
       for (int pt = 0; pt < RPW; ++pt)
 #pragma unroll
@@ -443,65 +502,43 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int pt = 0; pt < RPW; ++pt) {
-          const bf16x8 xw = lds8(&XWs[(pr + 16 * pt + li) * kRowT + 32 * ks + kq]);
+          const bf16x8 xw = lds8(&XWs[cur][(pr + 16 * pt + li) * kRowT + 32 * ks + kq]);
 #pragma unroll
           for (int k = 0; k < kNTW; ++k) S[pt][k] = mfma(ba[ks][k], xw, S[pt][k]);
         }
       load_b(cn);
     }
 
-    // 4. y = exp(a_t) (C^T S^T) + u_t (own term) + D x, times silu(z); this
+    // 5. y = exp(a_t) (C^T S^T) + u_t (own term) + D x, times silu(z); this
     //    lane's 4 tokens replace z in Zs (each element has one owner)
     {
-      const f32x4 et = *reinterpret_cast<const f32x4 *>(&qet[tq]);
-      const f32x4 ut = factored ? *reinterpret_cast<const f32x4 *>(&qu[tq])
+      const f32x4 et = *reinterpret_cast<const f32x4 *>(&q[2][tq]);
+      const f32x4 ut = factored ? *reinterpret_cast<const f32x4 *>(&q[3][tq])
                                 : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
       for (int pt = 0; pt < RPW; ++pt) {
         const int r = pr + 16 * pt + li;
-        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&Xs[r * kRowT + tq]);
+        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&Xs[cur][r * kRowT + tq]);
         float yv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           yv[e] = et[e] * (ao[pt][e] + ao2[pt][e]) + ut[e] * (ad[pt][e] + ad2[pt][e]) +
                   Dh * static_cast<float>(xv[e]);
         if (zh) {
-          const bf16x4 zv = *reinterpret_cast<const bf16x4 *>(&Zs[r * kRowT + tq]);
+          const bf16x4 zv = *reinterpret_cast<const bf16x4 *>(&Zs[cur][r * kRowT + tq]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) yv[e] *= silu_f(static_cast<float>(zv[e]));
         }
-        *reinterpret_cast<bf16x4 *>(&Zs[r * kRowT + tq]) =
+        *reinterpret_cast<bf16x4 *>(&Zs[cur][r * kRowT + tq]) =
             bf16x4{static_cast<__bf16>(yv[0]), static_cast<__bf16>(yv[1]),
                    static_cast<__bf16>(yv[2]), static_cast<__bf16>(yv[3])};
       }
     }
-    __syncthreads();  // y complete; the chunk's tiles are free for the next one
-    // 5. coalesced y stores; the next chunk's step quantities, x and z (the
-    //    same thread reads a y piece before writing that piece's z)
-#pragma unroll
-    for (int i = 0; i < kXQ; ++i) {
-      const int q = tid + kThreads * i, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
-      if (kXP % kThreads == 0 || q < kXP) {
-        const int64_t t = t0 + t8;
-        uint16_t *yr = yh + r * L + t;
-        if (kVec && t + 8 <= L) {
-          *reinterpret_cast<u32x4 *>(yr) = *reinterpret_cast<const u32x4 *>(&Zs[r * kRowT + t8]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (t + e < L) yr[e] = __builtin_bit_cast(uint16_t, Zs[r * kRowT + t8 + e]);
-        }
-      }
-    }
-    if (more) {
-      factored = steps(dtn, t0 + T);
-      deposit(factored);
-      dtn = load_dt(c + 2);
-      // x and z two chunks ahead: requested a whole chunk before they are
-      // written to LDS
-      load_xz(c + 2 < p.nchunks ? c + 2 : c + 1);
-    }
+    factored = factored_next;
   }
+  __syncthreads();
+  read_y((nch - 1) & 1);
+  store_y(nch - 1);
 
   if (p.h_final) {
 #pragma unroll
@@ -549,8 +586,10 @@ hipError_t launch_ssd_n(const SsdArgs &a, hipStream_t s) {
 #else
   const int rp = seqs >= kCUs ? 4 : 2 * seqs >= kCUs ? 2 : 1;
 #endif
-  if (rp == 4) return launch_ssd_t<N, kVec, 4, kW>(a, s);
-  if (rp == 2 || kW == 8) return launch_ssd_t<N, kVec, 2, kW>(a, s);
+  // 64 rows of a 256-state head would need more than the CU's 160 KB of LDS
+  if constexpr (N < 256)
+    if (rp == 4) return launch_ssd_t<N, kVec, 4, kW>(a, s);
+  if (rp >= 2 || kW == 8) return launch_ssd_t<N, kVec, 2, kW>(a, s);
   return launch_ssd_t<N, kVec, 1, 4>(a, s);
 }
 
