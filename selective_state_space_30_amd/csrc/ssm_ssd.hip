@@ -191,16 +191,18 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
 template <int N, bool kVec, int RP, int kW>
 __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   constexpr int R = 16 * RP;          // rows of the head in this workgroup
-  constexpr int kRowN = N + kPad;
   constexpr int kNTW = N / 64;        // state tiles per wave (per row tile)
   constexpr int kThreads = 64 * kW;
   constexpr int RPW = RP / (kW / 4);  // row tiles per wave
   static_assert((kW == 4 || kW == 8) && RPW >= 1 && RP % (kW / 4) == 0, "wave layout");
-  __shared__ __align__(16) __bf16 Xs[2][R * kRowT];     // [p][t]: x_t
-  __shared__ __align__(16) __bf16 XVs[2][R * kRowT];    // [p][t]: x_t v_t
-  __shared__ __align__(16) __bf16 XWs[2][R * kRowT];    // [p][t]: x_t w_t
-  __shared__ __align__(16) __bf16 Zs[2][R * kRowT];     // [p][t]: z, then y
-  __shared__ __align__(16) __bf16 Ss[2][2][R * kRowN];  // [p][n]: entering state, hi, lo
+  // Tiles are unpadded; the 16-byte groups of a row are permuted by the row
+  // (group g of row r at g ^ (r % 8)) so that 8 rows read at one group hit
+  // 8 different bank sets.
+  __shared__ __align__(16) __bf16 Xs[2][R * T];         // [p][t]: x_t
+  __shared__ __align__(16) __bf16 XVs[2][R * T];        // [p][t]: x_t v_t
+  __shared__ __align__(16) __bf16 XWs[2][2][R * T];     // [p][t]: x_t w_t, hi, lo
+  __shared__ __align__(16) __bf16 Zs[2][R * T];         // [p][t]: z, then y
+  __shared__ __align__(16) __bf16 Ss[2][2][R * N];      // [p][n]: entering state, hi, lo
   // dt, cum, exp(a_t), u_t, v_t, w_t of the chunk
   __shared__ __align__(16) float Wq[2][6][T];
 
@@ -230,6 +232,10 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   const int kq = 8 * lq;                         // operand k offset of this lane
   const int ta = 16 * tt + li;                   // token row of this lane's A operands
   const int tq = 16 * tt + 4 * lq;               // first token of this lane's outputs
+  // element (row r, column j) of a [row][T] or [row][N] tile, j in a
+  // 16-byte group (8 elements) that is permuted by the row
+  auto at = [](int r, int j) { return r * T + ((((j >> 3) ^ r) & 7) | (j >> 3 & ~7)) * 8 + (j & 7); };
+  auto an = [](int r, int j) { return r * N + ((((j >> 3) ^ r) & 7) | (j >> 3 & ~7)) * 8 + (j & 7); };
 
   // State tiles in accumulator layout, transposed: S[pt][k][e] is the state
   // of row pr + 16*pt + li, state n = 16*(kNTW*tt + k) + 4*lq + e.
@@ -326,8 +332,8 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     for (int i = 0; i < kXQ; ++i) {
       const int pc = tid + kThreads * i, r = pc / (T / 8), t8 = (pc % (T / 8)) * 8;
       if (kXP % kThreads == 0 || pc < kXP) {
-        *reinterpret_cast<u32x4 *>(&Xs[buf][r * kRowT + t8]) = rx[i];
-        if (zh) *reinterpret_cast<u32x4 *>(&Zs[buf][r * kRowT + t8]) = rz[i];
+        *reinterpret_cast<u32x4 *>(&Xs[buf][at(r, t8)]) = rx[i];
+        if (zh) *reinterpret_cast<u32x4 *>(&Zs[buf][at(r, t8)]) = rz[i];
         const bf16x8 xv = __builtin_bit_cast(bf16x8, rx[i]);
         const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&q[5][t8]);
         const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&q[5][t8 + 4]);
@@ -337,7 +343,15 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
           o[e] = static_cast<__bf16>(static_cast<float>(xv[e]) * w0[e]);
           o[e + 4] = static_cast<__bf16>(static_cast<float>(xv[e + 4]) * w1[e]);
         }
-        *reinterpret_cast<bf16x8 *>(&XWs[buf][r * kRowT + t8]) = o;
+        bf16x8 lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = static_cast<__bf16>(static_cast<float>(xv[e]) * w0[e] - static_cast<float>(o[e]));
+          lo[e + 4] = static_cast<__bf16>(static_cast<float>(xv[e + 4]) * w1[e] -
+                                          static_cast<float>(o[e + 4]));
+        }
+        *reinterpret_cast<bf16x8 *>(&XWs[buf][0][at(r, t8)]) = o;
+        *reinterpret_cast<bf16x8 *>(&XWs[buf][1][at(r, t8)]) = lo;
         if (factored) {
           const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&q[4][t8]);
           const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&q[4][t8 + 4]);
@@ -346,7 +360,7 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
             o[e] = static_cast<__bf16>(static_cast<float>(xv[e]) * v0[e]);
             o[e + 4] = static_cast<__bf16>(static_cast<float>(xv[e + 4]) * v1[e]);
           }
-          *reinterpret_cast<bf16x8 *>(&XVs[buf][r * kRowT + t8]) = o;
+          *reinterpret_cast<bf16x8 *>(&XVs[buf][at(r, t8)]) = o;
         }
       }
     }
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     for (int i = 0; i < kXQ; ++i) {
       const int pc = tid + kThreads * i, r = pc / (T / 8), t8 = (pc % (T / 8)) * 8;
       if (kXP % kThreads == 0 || pc < kXP)
-        ry[i] = *reinterpret_cast<const u32x4 *>(&Zs[buf][r * kRowT + t8]);
+        ry[i] = *reinterpret_cast<const u32x4 *>(&Zs[buf][at(r, t8)]);
     }
   };
   auto store_y = [&](int c) __attribute__((always_inline)) {
@@ -421,8 +435,8 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
           hi[e] = static_cast<__bf16>(S[pt][k][e]);
           lo[e] = static_cast<__bf16>(S[pt][k][e] - static_cast<float>(hi[e]));
         }
-        *reinterpret_cast<bf16x4 *>(&Ss[cur][0][(pr + 16 * pt + li) * kRowN + n]) = hi;
-        *reinterpret_cast<bf16x4 *>(&Ss[cur][1][(pr + 16 * pt + li) * kRowN + n]) = lo;
+        *reinterpret_cast<bf16x4 *>(&Ss[cur][0][an(pr + 16 * pt + li, n)]) = hi;
+        *reinterpret_cast<bf16x4 *>(&Ss[cur][1][an(pr + 16 * pt + li, n)]) = lo;
       }
     __syncthreads();
     // 2. the previous chunk's y out; the next chunk's step quantities, x w,
@@ -453,8 +467,8 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     for (int ks = 0; ks < N / 32; ++ks)
 #pragma unroll
       for (int pt = 0; pt < RPW; ++pt) {
-        ao[pt] = mfma(ca[ks], lds8(&Ss[cur][0][(pr + 16 * pt + li) * kRowN + 32 * ks + kq]), ao[pt]);
-        ao2[pt] = mfma(ca[ks], lds8(&Ss[cur][1][(pr + 16 * pt + li) * kRowN + 32 * ks + kq]), ao2[pt]);
+        ao[pt] = mfma(ca[ks], lds8(&Ss[cur][0][an(pr + 16 * pt + li, 32 * ks + kq)]), ao[pt]);
+        ao2[pt] = mfma(ca[ks], lds8(&Ss[cur][1][an(pr + 16 * pt + li, 32 * ks + kq)]), ao2[pt]);
       }
     load_ct(cn);
     const int nks = tt < 2 ? 1 : 2;
@@ -465,7 +479,7 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
         if (ks < nks)
 #pragma unroll
           for (int pt = 0; pt < RPW; ++pt) {
-            const bf16x8 xv = lds8(&XVs[cur][(pr + 16 * pt + li) * kRowT + 32 * ks + kq]);
+            const bf16x8 xv = lds8(&XVs[cur][at(pr + 16 * pt + li, 32 * ks + kq)]);
             ad[pt] = mfma(ga[0][ks], xv, ad[pt]);
             ad2[pt] = mfma(ga[1][ks], xv, ad2[pt]);
           }
@@ -486,7 +500,7 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
           }
 #pragma unroll
           for (int pt = 0; pt < RPW; ++pt)
-            ad[pt] = mfma(m, lds8(&Xs[cur][(pr + 16 * pt + li) * kRowT + s0]), ad[pt]);
+            ad[pt] = mfma(m, lds8(&Xs[cur][at(pr + 16 * pt + li, s0)]), ad[pt]);
         }
     }
     load_g(cn);
@@ -502,9 +516,13 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int pt = 0; pt < RPW; ++pt) {
-          const bf16x8 xw = lds8(&XWs[cur][(pr + 16 * pt + li) * kRowT + 32 * ks + kq]);
+          const bf16x8 xw = lds8(&XWs[cur][0][at(pr + 16 * pt + li, 32 * ks + kq)]);
+          const bf16x8 xl = lds8(&XWs[cur][1][at(pr + 16 * pt + li, 32 * ks + kq)]);
 #pragma unroll
-          for (int k = 0; k < kNTW; ++k) S[pt][k] = mfma(ba[ks][k], xw, S[pt][k]);
+          for (int k = 0; k < kNTW; ++k) {
+            S[pt][k] = mfma(ba[ks][k], xw, S[pt][k]);
+            S[pt][k] = mfma(ba[ks][k], xl, S[pt][k]);
+          }
         }
       load_b(cn);
     }
@@ -518,18 +536,18 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
 #pragma unroll
       for (int pt = 0; pt < RPW; ++pt) {
         const int r = pr + 16 * pt + li;
-        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&Xs[cur][r * kRowT + tq]);
+        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&Xs[cur][at(r, tq)]);
         float yv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           yv[e] = et[e] * (ao[pt][e] + ao2[pt][e]) + ut[e] * (ad[pt][e] + ad2[pt][e]) +
                   Dh * static_cast<float>(xv[e]);
         if (zh) {
-          const bf16x4 zv = *reinterpret_cast<const bf16x4 *>(&Zs[cur][r * kRowT + tq]);
+          const bf16x4 zv = *reinterpret_cast<const bf16x4 *>(&Zs[cur][at(r, tq)]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) yv[e] *= silu_f(static_cast<float>(zv[e]));
         }
-        *reinterpret_cast<bf16x4 *>(&Zs[cur][r * kRowT + tq]) =
+        *reinterpret_cast<bf16x4 *>(&Zs[cur][at(r, tq)]) =
             bf16x4{static_cast<__bf16>(yv[0]), static_cast<__bf16>(yv[1]),
                    static_cast<__bf16>(yv[2]), static_cast<__bf16>(yv[3])};
       }

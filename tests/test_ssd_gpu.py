@@ -86,6 +86,43 @@ def test_ssd_deterministic_and_resumable():
     check(hb, h1.double(), "h_final (split)")
 
 
+# Decay regimes of the chunk's own term: the kernel splits exp(A (cum_t -
+# cum_s)) at a reference token while every |A (cum_t - cum_ref)| stays below
+# 96 (base 2) and forms the decay element by element otherwise.
+REGIMES = {
+    # every chunk over the bound: the element-wise path throughout
+    "steep": dict(A=-60.0),
+    # far below it: the factored path throughout
+    "flat": dict(A=-0.05),
+    # softplus off, steps of both signs: the running sum is not monotone
+    "signed_steps": dict(A=-4.0, softplus=False),
+    # steps of ~3: the decay underflows to 0 within a few tokens
+    "underflow": dict(A=-16.0, dt_shift=6.0),
+}
+
+
+@pytest.mark.parametrize("regime", sorted(REGIMES))
+def test_ssd_decay_regimes(regime):
+    spec = REGIMES[regime]
+    inp = syn.make_ssd_inputs(syn.MAMBA2_LAYER, "cpu", batch=1, nheads=2,
+                              dstate=64, seqlen=200, seed=900)
+    inp["A"] = torch.full_like(inp["A"], spec["A"])
+    if not spec.get("softplus", True):
+        g = torch.Generator().manual_seed(901)
+        inp["dt"] = (torch.rand(inp["dt"].shape, generator=g) * 0.35
+                     - 0.05).to(inp["dt"].dtype)
+        inp["dt_bias"] = None
+        inp["dt_softplus"] = False
+    if "dt_shift" in spec:
+        inp["dt"] = (inp["dt"].float() + spec["dt_shift"]).to(inp["dt"].dtype)
+    y_ref, h_ref = oracle.ssd(inp["x"], inp["dt"], inp["A"], inp["B"],
+                              inp["C"], inp["D"], inp["z"], inp["dt_bias"],
+                              inp["dt_softplus"], inp["h0"])
+    y, hf = gpu_ssd(to_dev(inp))
+    check(y, y_ref, "y")
+    check(hf, h_ref, "h_final")
+
+
 def test_ssd_rejects_unsupported():
     inp = to_dev(syn.make_ssd_inputs(syn.MAMBA2_LAYER, "cpu", batch=1,
                                      nheads=2, dstate=96, seqlen=64, seed=1))
