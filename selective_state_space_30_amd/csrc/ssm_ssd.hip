@@ -179,13 +179,13 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
 // state update), so those go from memory straight into operand registers;
 // the next chunk's are requested right after the last use.  LDS holds what
 // the waves share, double-buffered by chunk parity: x, x v and x w, z then
-// y, the state entering the chunk (a bf16 pair), and the chunk's step
-// quantities (every wave computes them and writes the same values; a wave
-// reads only after its own write).
+// y, the state entering the chunk (a bf16 pair); and the step quantities of
+// three chunks (chunk c+2's are formed during chunk c by wave (c+2) mod 4).
 //
 // One barrier per chunk c: before it, the state entering c into LDS; after
-// it, the y stores of chunk c-1, the step quantities and the x, z deposit of
-// chunk c+1, then chunk c's products, new state and y (into LDS).  A buffer
+// it, the y stores of chunk c-1, the step quantities of chunk c+2 (one
+// wave), the x, z deposit of chunk c+1, then chunk c's products, new state
+// and y (into LDS).  A buffer
 // of parity c is written again only in iteration c+1 (deposit of c+2) or
 // c+2 (state), after every wave has passed the barrier that ends its reads.
 template <int N, bool kVec, int RP, int kW>
@@ -203,8 +203,11 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   __shared__ __align__(16) __bf16 XWs[2][2][R * T];     // [p][t]: x_t w_t, hi, lo
   __shared__ __align__(16) __bf16 Zs[2][R * T];         // [p][t]: z, then y
   __shared__ __align__(16) __bf16 Ss[2][2][R * N];      // [p][n]: entering state, hi, lo
-  // dt, cum, exp(a_t), u_t, v_t, w_t of the chunk
-  __shared__ __align__(16) float Wq[2][6][T];
+  // dt, cum, exp(a_t), u_t, v_t, w_t of a chunk and whether its decay may
+  // be factored; formed two chunks ahead by one wave (in turn), so three
+  // sets are live
+  __shared__ __align__(16) float Wq[3][6][T];
+  __shared__ int Wf[3];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -404,9 +407,18 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   // in order, and a different order at the loop entry makes the compiler
   // wait for every load in flight before the deposit.
   load_xz(0);
-  bool factored = steps(load_dt(0), 0, Wq[0]);
-  deposit(factored, 0, Wq[0]);
-  uint16_t dtn = load_dt(1);
+  {
+    // chunks 0 and 1: every wave forms them (the same values); chunk 0's
+    // deposit reads what this wave wrote
+    const bool f0 = steps(load_dt(0), 0, Wq[0]);
+    const bool f1 = steps(load_dt(1), T, Wq[1]);
+    if (tid == 0) {
+      Wf[0] = f0;
+      Wf[1] = f1;
+    }
+    deposit(f0, 0, Wq[0]);
+  }
+  uint16_t dtn = load_dt(2);
   load_xz(nch > 1 ? 1 : 0);
   __builtin_amdgcn_sched_barrier(0);  // keep that order through scheduling
   load_ct(0);
@@ -415,13 +427,14 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   __builtin_amdgcn_sched_barrier(0);
   load_b(0);
 
+  int q0 = 0, q1 = 1, q2 = 2;  // step-quantity sets of chunks c, c+1, c+2
 #pragma unroll 1
   for (int c = 0; c < nch; ++c) {
     const int64_t t0 = static_cast<int64_t>(c) * T;
     const int cur = c & 1, nxt = cur ^ 1;
     const bool more = c + 1 < nch;
     const int cn = more ? c + 1 : c;  // the chunk whose operands load next
-    float (*q)[T] = Wq[cur];
+    float (*q)[T] = Wq[q0];
     // 1. the state entering the chunk as bf16 pairs, rows [p][n] (4 states
     //    a lane)
 #pragma unroll
@@ -439,17 +452,19 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
         *reinterpret_cast<bf16x4 *>(&Ss[cur][1][an(pr + 16 * pt + li, n)]) = lo;
       }
     __syncthreads();
-    // 2. the previous chunk's y out; the next chunk's step quantities, x w,
-    //    x v and z in (x and z were requested a chunk ago)
+    const bool factored = __builtin_amdgcn_readfirstlane(Wf[q0]) != 0;
+    // 2. the previous chunk's y out; chunk c+2's step quantities (one
+    //    wave); the next chunk's x w, x v and z in (x and z were requested
+    //    a chunk ago)
     if (c > 0) read_y(nxt);
-    bool factored_next = false;
-    if (more) {
-      factored_next = steps(dtn, t0 + T, Wq[nxt]);
-      deposit(factored_next, nxt, Wq[nxt]);
+    if (wave == ((c + 2) & 3) && c + 2 < nch) {
+      const bool f = steps(dtn, t0 + 2 * T, Wq[q2]);
+      if (lane == 0) Wf[q2] = f;
     }
+    if (more) deposit(__builtin_amdgcn_readfirstlane(Wf[q1]) != 0, nxt, Wq[q1]);
     if (c > 0) store_y(c - 1);
     if (more) {
-      dtn = load_dt(c + 2);
+      dtn = load_dt(c + 3);
       load_xz(c + 2 < nch ? c + 2 : c + 1);
     }
 
@@ -552,7 +567,10 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
                    static_cast<__bf16>(yv[2]), static_cast<__bf16>(yv[3])};
       }
     }
-    factored = factored_next;
+    const int qn = q0;
+    q0 = q1;
+    q1 = q2;
+    q2 = qn;
   }
   __syncthreads();
   read_y((nch - 1) & 1);
