@@ -259,20 +259,25 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   // 32 ks + kq ..), G row ta (tokens 32 ks + kq .., hi and lo), B rows of
   // this wave's state tiles (tokens 32 ks + kq ..)
   bf16x8 ca[N / 32], ga[2][2], ba[2][kNTW];
+  // (a chunk's C^T and G are small: a wave-uniform base and a 32-bit lane
+  // offset address them)
+  const int ct_off = ta * N + kq, g_off = ta * T + kq;
   auto load_ct = [&](int c) __attribute__((always_inline)) {
-    const uint16_t *r = Ctg + (static_cast<int64_t>(c) * T + ta) * N + kq;
+    const uint16_t *base = Ctg + static_cast<int64_t>(c) * T * N;
 #pragma unroll
     for (int ks = 0; ks < N / 32; ++ks)
-      ca[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(r + 32 * ks));
+      ca[ks] = __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const u32x4 *>(base + (ct_off + 32 * ks)));
   };
   auto load_g = [&](int c) __attribute__((always_inline)) {
-    const uint16_t *r = Gg + (static_cast<int64_t>(c) * 2 * T + ta) * T + kq;
+    const uint16_t *base = Gg + static_cast<int64_t>(c) * 2 * T * T;
 #pragma unroll
     for (int part = 0; part < 2; ++part)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         ga[part][ks] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4 *>(r + part * T * T + 32 * ks));
+            bf16x8,
+            *reinterpret_cast<const u32x4 *>(base + (g_off + part * T * T + 32 * ks)));
   };
   auto load_b = [&](int c) __attribute__((always_inline)) {
     const int64_t t0 = static_cast<int64_t>(c) * T;
