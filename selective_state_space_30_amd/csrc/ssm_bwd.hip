@@ -52,11 +52,13 @@ __device__ __forceinline__ float wave_reverse(float v, int lane) {
 constexpr int kBwdThreads = kBwdWaves * kWaveLanes;
 
 // Contributions of one state to dB and dC, one region per wave (channel):
-// sR[wave][B|C][token j of a lane run][lane], so a wave writing token j of
-// its 64 runs touches 64 consecutive words (no bank conflicts).
+// sR[wave][B|C][token j of a lane run][lane'], so a wave writing token j of
+// its 64 runs touches 64 consecutive words.  lane' = lane ^ 16 (j / 4): the
+// reduction's 4 threads that share a run read tokens 4 apart, which this
+// puts 16 banks apart instead of on one bank.
 constexpr int kRegionFloats = kBwdWaves * 2 * kTokensPerLane * kWaveLanes;  // 64 KB
 __device__ __forceinline__ int region_index(int wave, int mat, int j, int lane) {
-  return ((wave * 2 + mat) * kTokensPerLane + j) * kWaveLanes + lane;
+  return ((wave * 2 + mat) * kTokensPerLane + j) * kWaveLanes + (lane ^ ((j >> 2) << 4));
 }
 
 // After every wave has written its region for state n: thread tid sums the
