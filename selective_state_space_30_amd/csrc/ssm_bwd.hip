@@ -53,12 +53,13 @@ constexpr int kBwdThreads = kBwdWaves * kWaveLanes;
 
 // Contributions of one state to dB and dC, one region per wave (channel):
 // sR[wave][B|C][token j of a lane run][lane'], so a wave writing token j of
-// its 64 runs touches 64 consecutive words.  lane' = lane ^ 16 (j / 4): the
-// reduction's 4 threads that share a run read tokens 4 apart, which this
-// puts 16 banks apart instead of on one bank.
+// its 64 runs touches 64 consecutive words.  lane' = lane ^ 8 (j / 4): the
+// reduction's 4 threads that share a run read tokens 4 apart; LDS serves a
+// wave's 32-bit accesses 32 lanes at a time, where this puts the 8 runs x 4
+// token groups of each half-wave on 32 different banks.
 constexpr int kRegionFloats = kBwdWaves * 2 * kTokensPerLane * kWaveLanes;  // 64 KB
 __device__ __forceinline__ int region_index(int wave, int mat, int j, int lane) {
-  return ((wave * 2 + mat) * kTokensPerLane + j) * kWaveLanes + (lane ^ ((j >> 2) << 4));
+  return ((wave * 2 + mat) * kTokensPerLane + j) * kWaveLanes + (lane ^ ((j >> 2) << 3));
 }
 
 // After every wave has written its region for state n: thread tid sums the
