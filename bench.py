@@ -365,10 +365,13 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     log("decode workload %s" % dcfg.name)
     dinp = syn.make_decode_inputs(dcfg, dev)
     steps = [syn.step_slice(dinp, t) for t in range(dcfg.steps)]
-    state = torch.zeros(dcfg.batch, dcfg.dim, 16, device=dev)
+    # four states (one per layer of a stack) take the steps in turn: 336 MB,
+    # more than the last-level cache holds
+    states = [torch.zeros(dcfg.batch, dcfg.dim, 16, device=dev)
+              for _ in range(4)]
     ys = [torch.empty(dcfg.batch, dcfg.dim, dtype=torch.bfloat16, device=dev)
           for _ in range(dcfg.steps)]
-    calls = [ssm.bind_state_update(state, s["x"], s["delta"], dinp["A"],
+    calls = [ssm.bind_state_update(states[t % 4], s["x"], s["delta"], dinp["A"],
                                    s["B"], s["C"], dinp["D"], s["z"],
                                    dinp["delta_bias"], True, y=ys[t],
                                    stream=stream)

@@ -348,7 +348,8 @@ int ssm_state_update(float *state, const void *x, const void *delta,
   if (overlaps(y, bd, state, bdn))
     return fail(SSM_ERR_INVALID_ARG, "y overlaps state");
 
-  const bool vec = aligned(state, 16) && aligned(A, 16);
+  const bool vec = aligned(state, 16) && aligned(A, 16) && aligned(B, 4 * es) &&
+                   aligned(C, 4 * es);
   ssm::StepArgs a{};
   a.state = state; a.x = x; a.delta = delta; a.B = B; a.C = C; a.z = z;
   a.A = A; a.D = D; a.bias = delta_bias; a.y = y;

@@ -128,3 +128,42 @@ def test_decode_zoh_matches_oracle_every_step(dtype):
         torch.cuda.synchronize()
         check(y, y_ref, tol, "y step %d" % t)
         check(state, ref_state, tol, "state step %d" % t)
+
+
+def _offset_copy(t, offset):
+    """t's values in a buffer that starts `offset` elements into a larger
+    allocation: the data pointer loses its 8- and 16-byte alignment."""
+    flat = torch.empty(t.numel() + offset, dtype=t.dtype, device=DEV)
+    v = flat[offset:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("what", ["all", "B_only"])
+def test_decode_unaligned_inputs(dtype, what):
+    """Pointers without 16-byte alignment (the element-wise load path):
+    every step against the oracle, odd batch and a channel count that is
+    not a multiple of the workgroup's 64 channels."""
+    cfg = syn.DecodeConfig("unaligned", 5, 70, 16, 6, dtype=dtype, seed=41)
+    inp = syn.make_decode_inputs(cfg, "cpu", with_h0=True)
+    dinp = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v)
+            for k, v in inp.items()}
+    state = (_offset_copy(dinp["h0"], 1) if what == "all"
+             else dinp["h0"].clone())
+    A = _offset_copy(dinp["A"], 1) if what == "all" else dinp["A"]
+    ref_state = inp["h0"].double().numpy().copy()
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for t in range(cfg.steps):
+        s = syn.step_slice(dinp, t)
+        B = _offset_copy(s["B"], 1)
+        C = _offset_copy(s["C"], 1) if what == "all" else s["C"]
+        y = ssm.ssm_state_update(state, s["x"], s["delta"], A, B, C,
+                                 dinp["D"], s["z"], dinp["delta_bias"], True)
+        sh = syn.step_slice(inp, t)
+        y_ref = oracle.step(ref_state, sh["x"], sh["delta"], inp["A"],
+                            sh["B"], sh["C"], inp["D"], sh["z"],
+                            inp["delta_bias"], True, False)
+        torch.cuda.synchronize()
+        check(y, y_ref, tol, "y step %d" % t)
+        check(state, ref_state, tol, "state step %d" % t)
