@@ -44,7 +44,7 @@ def _run(cmd):
     return _finish(*_start(cmd))
 
 
-HIP_SOURCES = ["ssm_kernels.hip", "ssm_bwd.hip", "ssm_ssd.hip"]
+HIP_SOURCES = ["ssm_kernels.hip", "ssm_step.hip", "ssm_bwd.hip", "ssm_ssd.hip"]
 
 
 def build(verbose: bool = False) -> str:

@@ -376,135 +376,6 @@ __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
   }
 }
 
-// ------------------------------------------------------ decode step -----
-// Four lanes per (batch, channel), four states each: the fp32 state is read
-// and written with 16-byte accesses, fully coalesced; the 4-lane readout is
-// a two-step DPP reduction inside each quad.  A thread serves one channel
-// for kStepBatch batch entries, so A, D and the bias are read once for
-// them, and the loads of both states are in flight together.  The state is
-// touched once per step: its loads and stores are non-temporal.
-constexpr int kStepBatch = 2;
-constexpr int kStepThreads = 256;
-constexpr int kStepChannels = kStepThreads / 4;  // per workgroup
-
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <bool kVec>
-__device__ __forceinline__ void load_state4(const float *p, float (&h)[4]) {
-  if constexpr (kVec) {
-    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
-    h[0] = v[0]; h[1] = v[1]; h[2] = v[2]; h[3] = v[3];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = __builtin_nontemporal_load(p + i);
-  }
-}
-
-template <bool kVec>
-__device__ __forceinline__ void store_state4(float *p, const float (&h)[4]) {
-  if constexpr (kVec) {
-    const f32x4_t v = {h[0], h[1], h[2], h[3]};
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(p));
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(h[i], p + i);
-  }
-}
-
-// Four consecutive activations (B or C states) as fp32: one 8- or 16-byte
-// load when kVec (the caller has checked the alignment).
-template <typename T, bool kVec>
-__device__ __forceinline__ void load_act4(const T *p, float (&v)[4]) {
-  if constexpr (kVec && sizeof(T) == 2) {
-    const uint2 w = *reinterpret_cast<const uint2 *>(p);
-    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-  } else if constexpr (kVec) {
-    const float4 w = *reinterpret_cast<const float4 *>(p);
-    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = to_f32<T>(p[i]);
-  }
-}
-
-// grid: (ceil(dim / kStepChannels), ceil(batch / kStepBatch)); thread =
-// (channel d, states 4q .. 4q+3) for batch entries kStepBatch*blockIdx.y + u.
-template <typename T, bool kVec>
-__global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
-  constexpr int U = kStepBatch;
-  const uint32_t dim = static_cast<uint32_t>(p.dim);
-  const uint32_t batch = static_cast<uint32_t>(p.batch);
-  const int q = threadIdx.x & 3;
-  const uint32_t d_raw = blockIdx.x * kStepChannels + (threadIdx.x >> 2);
-  const bool d_ok = d_raw < dim;
-  const uint32_t d = d_ok ? d_raw : dim - 1;  // clamped for reads
-  uint32_t bc[U];  // batch entry, clamped for reads
-  size_t ch[U];
-  bool ok[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t b = blockIdx.y * U + u;
-    ok[u] = d_ok && b < batch;
-    bc[u] = b < batch ? b : batch - 1;
-    ch[u] = static_cast<size_t>(bc[u]) * dim + d;
-  }
-
-  float h[U][4], a4[4];
-#pragma unroll
-  for (int u = 0; u < U; ++u) load_state4<kVec>(p.state + ch[u] * kStates + 4 * q, h[u]);
-  if constexpr (kVec) {
-    const float4 av = *reinterpret_cast<const float4 *>(p.A + d * kStates + 4 * q);
-    a4[0] = av.x; a4[1] = av.y; a4[2] = av.z; a4[3] = av.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a4[i] = p.A[d * kStates + 4 * q + i];
-  }
-  const float bias = p.bias ? p.bias[d] : 0.0f;
-  const float Dd = p.D ? p.D[d] : 0.0f;
-  float x[U], xr[U], zz[U], b4[U][4], c4[U][4];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const size_t bsel = bc[u];
-    x[u] = to_f32<T>(static_cast<const T *>(p.x)[ch[u]]);
-    xr[u] = to_f32<T>(static_cast<const T *>(p.delta)[ch[u]]) + bias;
-    zz[u] = p.z ? to_f32<T>(static_cast<const T *>(p.z)[ch[u]]) : 0.0f;
-    load_act4<T, kVec>(static_cast<const T *>(p.B) + bsel * kStates + 4 * q, b4[u]);
-    load_act4<T, kVec>(static_cast<const T *>(p.C) + bsel * kStates + 4 * q, c4[u]);
-  }
-
-  float part[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const float dt = p.softplus ? softplus_f(xr[u]) : xr[u];
-    const float dx = dt * x[u];
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float arg = dt * a4[i] * kLog2e;
-      const float e = fast_exp2(arg);
-      float inp = dx * b4[u][i];
-      if (p.zoh)  // exact ZOH: coefficient (e - 1)/A in place of dt
-        inp = zoh_coeff(arg, e, dt, 1.0f / a4[i]) * (x[u] * b4[u][i]);
-      h[u][i] = fmaf(e, h[u][i], inp);
-      acc = fmaf(c4[u][i], h[u][i], acc);
-    }
-    acc += dpp<kQuadXor1>(acc, acc);
-    acc += dpp<kQuadXor2>(acc, acc);
-    asm volatile("" : "+v"(acc));  // reduced by all four lanes before any branch
-    part[u] = acc;
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (!ok[u]) continue;
-    store_state4<kVec>(p.state + ch[u] * kStates + 4 * q, h[u]);
-    if (q == 0) {
-      float yv = fmaf(Dd, x[u], part[u]);
-      if (p.z) yv *= silu_f(zz[u]);
-      static_cast<T *>(p.y)[ch[u]] = from_f32<T>(yv);
-    }
-  }
-}
-
 template <typename T, bool kVec>
 hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.dim + kChannelsPerGroup - 1) /
@@ -538,14 +409,6 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, bool kVec>
-hipError_t launch_step_t(const StepArgs &a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((a.dim + kStepChannels - 1) / kStepChannels),
-                  static_cast<unsigned>((a.batch + kStepBatch - 1) / kStepBatch));
-  hipLaunchKernelGGL((step_kernel<T, kVec>), grid, dim3(kStepThreads), 0, s, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream) {
@@ -553,13 +416,6 @@ int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream) {
   if (bf16)
     return vec ? launch_scan_t<uint16_t, true>(a, s) : launch_scan_t<uint16_t, false>(a, s);
   return vec ? launch_scan_t<float, true>(a, s) : launch_scan_t<float, false>(a, s);
-}
-
-int launch_step(const StepArgs &a, bool bf16, bool vec, void *stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (bf16)
-    return vec ? launch_step_t<uint16_t, true>(a, s) : launch_step_t<uint16_t, false>(a, s);
-  return vec ? launch_step_t<float, true>(a, s) : launch_step_t<float, false>(a, s);
 }
 
 const char *hip_error_string(int err) {
