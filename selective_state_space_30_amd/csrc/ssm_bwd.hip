@@ -154,6 +154,13 @@ __device__ __forceinline__ void bwd_block(
 #pragma unroll
     for (int j = 0; j < K; ++j) gc[j] *= silu_f(zz[j]);
   }
+  if (!ch_ok) {
+    // a wave past the last channel: with gc = dt*u = 0 its dB and dC
+    // contributions (lambda dt u and gc h) vanish; nothing else of it is
+    // stored
+#pragma unroll
+    for (int j = 0; j < K; ++j) gc[j] = du[j] = 0.0f;
+  }
   run.store(sT, toff);
   const float sdtl = sdt * kLog2e;
 
@@ -233,8 +240,8 @@ __device__ __forceinline__ void bwd_block(
         const float q = m * (j > 0 ? hs[j - 1] : hin);   // lambda a h_{j-1}
         s2[j] = fmaf(q, An, s2[j]);
         dA_acc = fmaf(q, dtl[j], dA_acc);
-        sR[region_index(wave, 0, j, lane)] = ch_ok ? lam * du[j] : 0.0f;
-        sR[region_index(wave, 1, j, lane)] = ch_ok ? gc[j] * hs[j] : 0.0f;
+        sR[region_index(wave, 0, j, lane)] = lam * du[j];
+        sR[region_index(wave, 1, j, lane)] = gc[j] * hs[j];
       }
       float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
       asm volatile("" : "+s"(dA_sum));
