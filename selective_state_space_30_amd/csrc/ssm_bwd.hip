@@ -58,6 +58,9 @@ constexpr int kBwdThreads = kBwdWaves * kWaveLanes;
 // wave's 32-bit accesses 32 lanes at a time, where this puts the 8 runs x 4
 // token groups of each half-wave on 32 different banks.
 constexpr int kRegionFloats = kBwdWaves * 2 * kTokensPerLane * kWaveLanes;  // 64 KB
+// One state's B and C for the block: [B|C][lane run][token], runs padded to
+// 20 floats (a lane's 16-byte reads of 8 consecutive runs hit 32 banks).
+constexpr int kBwdTileFloats = 2 * kWaveLanes * (kTokensPerLane + 4);  // 10 KB
 __device__ __forceinline__ int region_index(int wave, int mat, int j, int lane) {
   return ((wave * 2 + mat) * kTokensPerLane + j) * kWaveLanes + (lane ^ ((j >> 2) << 3));
 }
@@ -106,26 +109,23 @@ __device__ __forceinline__ void bwd_block(
     float &dDl, float &dbl, float *sT, float *sR, int tid) {
   constexpr int K = kTokensPerLane;
   constexpr int KP = K + 4;
-  constexpr int kPhases = kStates / 2;
-  constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
   const int64_t tl = t0 + static_cast<int64_t>(lane) * K;
   const T *urow = static_cast<const T *>(p.u) + bd * p.L;
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
   const T *gyrow = static_cast<const T *>(p.dy) + bd * p.L;
 
-  // staging role of this wave: state (2*ph + st) of matrix mat, half `half`
-  // of every lane run (8 tokens per lane)
-  constexpr int kHalfRun = K / 2;
-  const int row = wave & 3, half = wave >> 2;
-  const int st = row >> 1, mat = row & 1;
+  // staging role of this wave: matrix mat (B or C) of the next state,
+  // quarter `qr` of every lane run (4 tokens per lane)
+  constexpr int kQuarterRun = K / 4;
+  const int mat = wave & 1, qr = wave >> 1;
   const T *src = mat ? Cb : Bb;
-  const int toff = (row * kWaveLanes + lane) * KP + half * kHalfRun;
-  const int64_t tq = tl + half * kHalfRun;
+  const int toff = (mat * kWaveLanes + lane) * KP + qr * kQuarterRun;
+  const int64_t tq = tl + qr * kQuarterRun;
   float *pBg = p.pB + (b * p.groups + g) * kStates * p.L;  // this group's partial rows
   float *pCg = p.pC + (b * p.groups + g) * kStates * p.L;
-  TileRun<T, kHalfRun, kVec, kFull> run;
-  run.load(src + st * p.L, t0, tq, tend);
+  TileRun<T, kQuarterRun, kVec, kFull> run;
+  run.load(src, t0, tq, tend);  // state 0
 
   // per token: dt (as dt*log2 e), dt*u, the gated output gradient gc and
   // the sums over states s1 = sum lambda B, s2 = sum lambda a h_prev A
@@ -163,94 +163,93 @@ __device__ __forceinline__ void bwd_block(
   }
   run.store(sT, toff);
   const float sdtl = sdt * kLog2e;
+  // One barrier per state: state n reads tile buffer n & 1 and writes
+  // region buffer n & 1; before its barrier each wave stores its share of
+  // state n+1's tile into the other tile buffer (last read by state n-1,
+  // before the previous barrier); after it, the workgroup sums state n's
+  // region, which is written again by state n+2, after the next barrier.
+  __syncthreads();  // the tile of state 0 (and the previous block's last sums read)
 
 #pragma unroll 1
-  for (int ph = 0; ph < kPhases; ++ph) {
-    if (ph + 1 < kPhases) run.load(src + (2 * (ph + 1) + st) * p.L, t0, tq, tend);
-    __syncthreads();  // tile ph complete
-    const float *tile = sT + (ph & 1) * kTileFloats;
+  for (int n = 0; n < kStates; ++n) {
+    if (n + 1 < kStates) run.load(src + (n + 1) * p.L, t0, tq, tend);
+    const float *tile = sT + (n & 1) * kBwdTileFloats;
+    float *reg = sR + (n & 1) * kRegionFloats;
+    float An = state_of(Av, n);
+    asm volatile("" : "+s"(An));  // keep this state's work after the previous state's
+    const float hfn = state_of(hfv, n);
+    const float mun = state_of(muv, n);
+    // this state's B and C for the lane's 16 tokens, read from the tile once
+    float bv[K], cv[K];
+    {
+      const float4 *pb = reinterpret_cast<const float4 *>(&tile[lane * KP]);
+      const float4 *pc = reinterpret_cast<const float4 *>(&tile[(kWaveLanes + lane) * KP]);
 #pragma unroll
-    for (int s2i = 0; s2i < 2; ++s2i) {
-      const int n = 2 * ph + s2i;
-      float An = state_of(Av, n);
-      asm volatile("" : "+s"(An));  // keep this state's work after the previous state's
-      const float hfn = state_of(hfv, n);
-      const float mun = state_of(muv, n);
-      // this state's B and C for the lane's 16 tokens, read from the tile once
-      float bv[K], cv[K];
-      {
-        const float4 *pb = reinterpret_cast<const float4 *>(
-            &tile[((s2i * 2 + 0) * kWaveLanes + lane) * KP]);
-        const float4 *pc = reinterpret_cast<const float4 *>(
-            &tile[((s2i * 2 + 1) * kWaveLanes + lane) * KP]);
-#pragma unroll
-        for (int q = 0; q < K / 4; ++q) {
-          const float4 x = pb[q], y4 = pc[q];
-          bv[4 * q + 0] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
-          cv[4 * q + 0] = y4.x; cv[4 * q + 1] = y4.y; cv[4 * q + 2] = y4.z; cv[4 * q + 3] = y4.w;
-        }
+      for (int q = 0; q < K / 4; ++q) {
+        const float4 x = pb[q], y4 = pc[q];
+        bv[4 * q + 0] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
+        cv[4 * q + 0] = y4.x; cv[4 * q + 1] = y4.y; cv[4 * q + 2] = y4.z; cv[4 * q + 3] = y4.w;
       }
-      // forward recomputation of this lane's 16 states:
-      // hin = the state before the lane's first token, hs[j] = after token j
-      float a[K], hs[K];
+    }
+    // forward recomputation of this lane's 16 states:
+    // hin = the state before the lane's first token, hs[j] = after token j
+    float a[K], hs[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      a[j] = fast_exp2(dtl[j] * An);
+      hs[j] = du[j] * bv[j];  // dt B u, replaced by the state below
+    }
+    float H = hs[0];
+#pragma unroll
+    for (int j = 1; j < K; ++j) H = fmaf(a[j], H, hs[j]);
+    const float Pl = fast_exp2(sdtl * An);  // product of the lane's a
+    float P = Pl;
+    H = fmaf(P, lane == 0 ? hfn : 0.0f, H);
+    wave_affine_scan(P, H);
+    const float hin = wave_shift_in(H, hfn);
+    {
+      float h = hin;
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        a[j] = fast_exp2(dtl[j] * An);
-        hs[j] = du[j] * bv[j];  // dt B u, replaced by the state below
+        h = fmaf(a[j], h, hs[j]);
+        hs[j] = h;
       }
-      float H = hs[0];
-#pragma unroll
-      for (int j = 1; j < K; ++j) H = fmaf(a[j], H, hs[j]);
-      const float Pl = fast_exp2(sdtl * An);  // product of the lane's a
-      float P = Pl;
-      H = fmaf(P, lane == 0 ? hfn : 0.0f, H);
-      wave_affine_scan(P, H);
-      const float hin = wave_shift_in(H, hfn);
-      {
-        float h = hin;
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-          h = fmaf(a[j], h, hs[j]);
-          hs[j] = h;
-        }
-      }
-      // reverse: the lane's map mu_in -> mu_out (tokens 15 .. 0), then the
-      // 64 lanes composed from the right (reversed lane order, forward scan)
-      float M = 0.0f;
-#pragma unroll
-      for (int j = K - 1; j >= 0; --j) M = fmaf(gc[j], cv[j], M) * a[j];
-      float Pr = wave_reverse(Pl, lane);
-      float Mr = wave_reverse(M, lane);
-      Mr = fmaf(Pr, lane == 0 ? mun : 0.0f, Mr);
-      wave_affine_scan(Pr, Mr);
-      // cross-lane results are formed by the whole wave and pinned in a
-      // scalar register before one lane takes them: otherwise the compiler
-      // may move the DPP / readlane under the lane == n mask
-      float mu_out = lane_broadcast(Mr, kWaveLanes - 1);
-      asm volatile("" : "+s"(mu_out));
-      muv = set_state(muv, lane, n, mu_out);
-      float m = wave_reverse(wave_shift_in(Mr, mun), lane);
-      // reverse replay: lambda_j = dL/dh_j, then the gradients of token j
-      float dA_acc = 0.0f;
-#pragma unroll
-      for (int j = K - 1; j >= 0; --j) {
-        const float lam = fmaf(gc[j], cv[j], m);
-        s1[j] = fmaf(lam, bv[j], s1[j]);
-        m = a[j] * lam;                                  // lambda a
-        const float q = m * (j > 0 ? hs[j - 1] : hin);   // lambda a h_{j-1}
-        s2[j] = fmaf(q, An, s2[j]);
-        dA_acc = fmaf(q, dtl[j], dA_acc);
-        sR[region_index(wave, 0, j, lane)] = lam * du[j];
-        sR[region_index(wave, 1, j, lane)] = gc[j] * hs[j];
-      }
-      float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
-      asm volatile("" : "+s"(dA_sum));
-      dAv += lane == n ? dA_sum : 0.0f;
-      __syncthreads();  // every channel's contributions to state n are in sR
-      flush_state<kVec, kFull>(sR, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
-      __syncthreads();  // sR is free for the next state
     }
-    if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
+    // reverse: the lane's map mu_in -> mu_out (tokens 15 .. 0), then the
+    // 64 lanes composed from the right (reversed lane order, forward scan)
+    float M = 0.0f;
+#pragma unroll
+    for (int j = K - 1; j >= 0; --j) M = fmaf(gc[j], cv[j], M) * a[j];
+    float Pr = wave_reverse(Pl, lane);
+    float Mr = wave_reverse(M, lane);
+    Mr = fmaf(Pr, lane == 0 ? mun : 0.0f, Mr);
+    wave_affine_scan(Pr, Mr);
+    // cross-lane results are formed by the whole wave and pinned in a
+    // scalar register before one lane takes them: otherwise the compiler
+    // may move the DPP / readlane under the lane == n mask
+    float mu_out = lane_broadcast(Mr, kWaveLanes - 1);
+    asm volatile("" : "+s"(mu_out));
+    muv = set_state(muv, lane, n, mu_out);
+    float m = wave_reverse(wave_shift_in(Mr, mun), lane);
+    // reverse replay: lambda_j = dL/dh_j, then the gradients of token j
+    float dA_acc = 0.0f;
+#pragma unroll
+    for (int j = K - 1; j >= 0; --j) {
+      const float lam = fmaf(gc[j], cv[j], m);
+      s1[j] = fmaf(lam, bv[j], s1[j]);
+      m = a[j] * lam;                                  // lambda a
+      const float q = m * (j > 0 ? hs[j - 1] : hin);   // lambda a h_{j-1}
+      s2[j] = fmaf(q, An, s2[j]);
+      dA_acc = fmaf(q, dtl[j], dA_acc);
+      reg[region_index(wave, 0, j, lane)] = lam * du[j];
+      reg[region_index(wave, 1, j, lane)] = gc[j] * hs[j];
+    }
+    float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
+    asm volatile("" : "+s"(dA_sum));
+    dAv += lane == n ? dA_sum : 0.0f;
+    if (n + 1 < kStates) run.store(sT + ((n + 1) & 1) * kBwdTileFloats, toff);
+    __syncthreads();  // state n's contributions and state n+1's tile are in LDS
+    flush_state<kVec, kFull>(reg, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
   }
 
   // per-token gradients
@@ -289,10 +288,8 @@ __device__ __forceinline__ void bwd_block(
 template <typename T, bool kVec, bool kSoftplus>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs p) {
-  constexpr int KP = kTokensPerLane + 4;
-  constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
-  __shared__ float sT[2 * kTileFloats];  // staged B, C (fp32), double-buffered
-  __shared__ float sR[kRegionFloats];    // dB, dC contributions of the 4 channels
+  __shared__ float sT[2 * kBwdTileFloats];  // one state's B, C (fp32), double-buffered
+  __shared__ float sR[2 * kRegionFloats];   // dB, dC contributions of the 8 channels, double-buffered
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -311,7 +311,12 @@ struct TileRun {
 
   __device__ __forceinline__ void load(const T *__restrict__ row, int64_t t0,
                                        int64_t t, int64_t tend) {
-    if constexpr (kPacked) {
+    if constexpr (kPacked && K == 4) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(row + t);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else if constexpr (kPacked) {
+      static_assert(K % 8 == 0, "packed runs of 4 or a multiple of 8 tokens");
       const uint4 *q = reinterpret_cast<const uint4 *>(row + t);
 #pragma unroll
       for (int i = 0; i < K / 8; ++i) {
