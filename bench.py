@@ -17,7 +17,9 @@ on its stream over the timed region) to the ALU ceiling that bounds it.
 Options beyond the contract: --no-cpu-baseline, --no-extra (skip the
 long-context and decode figures), --only-scan (nothing but the timed steps;
 for profiler runs), --only-ssd (only the Mamba-2 SSD figure, --steps calls;
-for profiler runs), --summarize DIR (no GPU: turn the rocprofv3 CSV output
+for profiler runs), --only-decode (the decode workload, --steps passes of
+its 64 steps), --only-bwd (the 2.8B-layer backward, --steps calls),
+--summarize DIR (no GPU: turn the rocprofv3 CSV output
 of the profiling commands below into the summaries under profiles/).
 
 Profiling commands (run from /tmp with TMPDIR=/tmp; DIR = an output folder):
@@ -31,6 +33,8 @@ Profiling commands (run from /tmp with TMPDIR=/tmp; DIR = an output folder):
       -- python3 bench.py --only-ssd --steps 3
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/ssdwrite -o ssdwrite \
       -- python3 bench.py --only-ssd --steps 3
+  (the same two passes with --only-decode into DIR/decodefetch and
+  DIR/decodewrite, and with --only-bwd into DIR/bwdfetch and DIR/bwdwrite)
   python3 bench.py --summarize DIR
 """
 from __future__ import annotations
@@ -87,6 +91,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only-scan", action="store_true")
     ap.add_argument("--only-ssd", action="store_true")
+    ap.add_argument("--only-decode", action="store_true")
+    ap.add_argument("--only-bwd", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     args = ap.parse_args()
     if args.summarize:
@@ -105,12 +111,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = ssm.load_library()
-    if args.only_ssd:
-        stream = torch.cuda.current_stream(dev)
-        r = ssd_measure(ssm, syn, dev, stream, args.steps,
+    only = {"only_ssd": (syn.MAMBA2_LAYER.name, ssd_measure),
+            "only_decode": (syn.DECODE.name, decode_measure),
+            "only_bwd": (syn.MAMBA_2P8B.name + "_backward", bwd_measure)}
+    for flag, (name, measure) in only.items():
+        if getattr(args, flag):
+            stream = torch.cuda.current_stream(dev)
+            r = measure(ssm, syn, dev, stream, args.steps,
                         lambda m: print("[bench] " + m, file=sys.stderr, flush=True))
-        print(json.dumps({syn.MAMBA2_LAYER.name: r}))
-        return
+            print(json.dumps({name: r}))
+            return
     cfg = syn.MAMBA_2P8B
     E = cfg.elements
     nbytes = syn.algorithmic_bytes(cfg)
@@ -321,8 +331,22 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     del zinp, zy, zhf
     torch.cuda.empty_cache()
 
-    # backward pass of the 2.8B layer (checkpoint pass, reverse sweep,
-    # channel-sum reductions), outputs and workspace allocated up front
+    out[syn.MAMBA_2P8B.name + "_backward"] = bwd_measure(ssm, syn, dev, stream,
+                                                         reps, log)
+    torch.cuda.empty_cache()
+
+    out[syn.MAMBA2_LAYER.name] = ssd_measure(ssm, syn, dev, stream, reps, log)
+    torch.cuda.empty_cache()
+
+    out[syn.DECODE.name] = decode_measure(ssm, syn, dev, stream, 1, log)
+    return out
+
+
+def bwd_measure(ssm, syn, dev, stream, reps, log):
+    """Backward pass of the 2.8B layer (checkpoint pass, reverse sweep,
+    channel-sum reductions); outputs and workspace allocated up front."""
+    import torch
+    ccfg = syn.MAMBA_2P8B
     log("backward on %s" % ccfg.name)
     binp = syn.make_scan_inputs(ccfg, dev)
     g = torch.Generator(device=dev).manual_seed(ccfg.seed + 9)
@@ -342,6 +366,8 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
                          stream=stream)
     brun()
     torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
         brun()
@@ -349,24 +375,23 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     nb = syn.backward_bytes(ccfg)
-    out[ccfg.name + "_backward"] = {
-        "ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
-        "elements_per_s": round(ccfg.elements / (ms * 1e-3)),
-        "algorithmic_bytes": nb, "workspace_bytes": bws.numel(),
-        "note": "gradients of u, delta, A, B, C, D, z, bias; states "
-                "recomputed from 1024-token checkpoints"}
-    del binp, bdy, bws, bout
-    torch.cuda.empty_cache()
+    return {"ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+            "elements_per_s": round(ccfg.elements / (ms * 1e-3)),
+            "algorithmic_bytes": nb, "workspace_bytes": bws.numel(),
+            "note": "gradients of u, delta, A, B, C, D, z, bias; states "
+                    "recomputed from 1024-token checkpoints"}
 
-    out[syn.MAMBA2_LAYER.name] = ssd_measure(ssm, syn, dev, stream, reps, log)
-    torch.cuda.empty_cache()
 
+def decode_measure(ssm, syn, dev, stream, passes, log):
+    """The decode workload: ``passes`` times its 64 steps, each step one
+    ssm_state_update call bound in advance.  Four states (one per layer of a
+    stack) take the steps in turn: 336 MB, more than the last-level cache
+    holds."""
+    import torch
     dcfg = syn.DECODE
     log("decode workload %s" % dcfg.name)
     dinp = syn.make_decode_inputs(dcfg, dev)
     steps = [syn.step_slice(dinp, t) for t in range(dcfg.steps)]
-    # four states (one per layer of a stack) take the steps in turn: 336 MB,
-    # more than the last-level cache holds
     states = [torch.zeros(dcfg.batch, dcfg.dim, 16, device=dev)
               for _ in range(4)]
     ys = [torch.empty(dcfg.batch, dcfg.dim, dtype=torch.bfloat16, device=dev)
@@ -379,17 +404,18 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     for c in calls:
         c()
     torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for c in calls:
-        c()
+    for _ in range(passes):
+        for c in calls:
+            c()
     e1.record(stream)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / dcfg.steps
+    us = e0.elapsed_time(e1) * 1e3 / (dcfg.steps * passes)
     nb = syn.decode_step_bytes(dcfg)
-    out[dcfg.name] = {"us_per_step": round(us, 3),
-                      "GBps": round(nb / (us * 1e-6) / 1e9, 1),
-                      "bytes_per_step": nb}
-    return out
+    return {"us_per_step": round(us, 3), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+            "bytes_per_step": nb}
 
 
 def ssd_measure(ssm, syn, dev, stream, reps, log):
@@ -461,6 +487,7 @@ def cpu_baseline(inp, cfg, nbytes, log):
 # bf16 activations, vector loads, softplus on, no conv prologue, Euler input,
 # not the checkpoint pass
 SCAN_KERNEL = "scan_kernel<unsigned short, true, true, false, false, false>"
+CKPT_KERNEL = "scan_kernel<unsigned short, true, true, false, false, true>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30  # each calibration copy reads and writes 1 GiB
 
@@ -588,55 +615,86 @@ def summarize_profiles(d):
         with open(os.path.join(prof, "scan_kernel_mamba2p8b_sq_counters.txt"),
                   "w") as f:
             f.write("\n".join(sq_txt) + "\n")
-    ssd_txt = summarize_ssd(d, rows, per_dispatch, fetch_scale, write_scale,
-                            cmd_trace, prof)
-    print("\n".join(lines + txt + sq_txt + ssd_txt))
+    extra_txt = summarize_extras(d, rows, per_dispatch, fetch_scale, write_scale,
+                                 cmd_trace, prof)
+    print("\n".join(lines + txt + sq_txt + extra_txt))
 
 
-def summarize_ssd(d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace,
-                  prof):
-    """profiles/ssd_kernel_mamba2_b2_h80_p64_n128_l4096.txt: the SSD
-    kernels' trace statistics (from the full benchmark run) and their HBM
-    traffic (from the --only-ssd counter passes, scaled by the same copy
-    calibration as the scan kernel's)."""
-    import synthetic as syn
-    scfg = syn.MAMBA2_LAYER
-    txt = ["# Mamba-2 SSD form, workload " + scfg.name,
+def summarize_workload(d, rows, per_dispatch, fetch_scale, write_scale,
+                       cmd_trace, prof, *, title, fname, keys, tag, only,
+                       alg_bytes, alg_note):
+    """profiles/<fname>: the trace statistics (from the full benchmark run)
+    of the kernels whose names start with one of ``keys``, and their HBM
+    traffic per dispatch from the ``--<only> --steps 3`` counter passes under
+    DIR/<tag>fetch and DIR/<tag>write, scaled by the same copy calibration
+    as the scan kernel's; every listed kernel runs once per call."""
+    def match(k):
+        return any(k.startswith(p) for p in keys)
+    txt = ["# %s" % title,
            "# kernel statistics from: " + cmd_trace,
            "# kernel | calls | average us | min us | max us | total ms"]
     for r in rows:
         k = _kernel_key(r["Name"])
-        if k.startswith("ssd_"):
+        if match(k):
             txt.append("%s | %s | %.2f | %.2f | %.2f | %.3f" % (
                 k[:90], r["Calls"], float(r["AverageNs"]) / 1e3,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
                 float(r["TotalDurationNs"]) / 1e6))
-    if not os.path.isdir(os.path.join(d, "ssdfetch")):
+    if not os.path.isdir(os.path.join(d, tag + "fetch")):
         return []
-    fetch = per_dispatch("ssdfetch", "FETCH_SIZE")
-    write = per_dispatch("ssdwrite", "WRITE_SIZE")
+    fetch = per_dispatch(tag + "fetch", "FETCH_SIZE")
+    write = per_dispatch(tag + "write", "WRITE_SIZE")
     cmd = ("rocprofv3 --pmc {c} --output-format csv -d DIR/{d} -o {d} -- "
-           "python3 bench.py --only-ssd --steps 3")
+           "python3 bench.py --%s --steps 3" % only)
     txt += ["# HBM traffic per dispatch from (from /tmp, TMPDIR=/tmp):",
-            "#   " + cmd.format(c="FETCH_SIZE", d="ssdfetch"),
-            "#   " + cmd.format(c="WRITE_SIZE", d="ssdwrite"),
+            "#   " + cmd.format(c="FETCH_SIZE", d=tag + "fetch"),
+            "#   " + cmd.format(c="WRITE_SIZE", d=tag + "write"),
             "# scaled by the 1 GiB copy calibration (fetch x %.3f, write x %.3f)"
             % (fetch_scale, write_scale)]
     total = 0.0
     for k in sorted(fetch):
-        if not k.startswith("ssd_") or k not in write:
+        if not match(k) or k not in write:
             continue
         fb = fetch[k] * fetch_scale * 1024
         wb = write[k] * write_scale * 1024
         total += fb + wb
         txt.append("%s: read %.1f MB, written %.1f MB" % (k, fb / 1e6, wb / 1e6))
-    alg = syn.ssd_bytes(scfg)
-    txt.append("both kernels: %.1f MB per call vs algorithmic %.1f MB (ratio %.3f)"
-               % (total / 1e6, alg / 1e6, total / alg))
-    with open(os.path.join(prof, "ssd_kernel_%s.txt" % scfg.name), "w") as f:
+    txt.append("per call: %.1f MB vs algorithmic %.1f MB (ratio %.3f; %s)"
+               % (total / 1e6, alg_bytes / 1e6, total / alg_bytes, alg_note))
+    with open(os.path.join(prof, fname), "w") as f:
         f.write("\n".join(txt) + "\n")
     return txt
 
+
+def summarize_extras(d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace,
+                     prof):
+    """The SSD, decode and backward summaries under profiles/."""
+    import synthetic as syn
+    scfg, dcfg, bcfg = syn.MAMBA2_LAYER, syn.DECODE, syn.MAMBA_2P8B
+    out = []
+    out += summarize_workload(
+        d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace, prof,
+        title="Mamba-2 SSD form, workload " + scfg.name,
+        fname="ssd_kernel_%s.txt" % scfg.name, keys=["ssd_"], tag="ssd",
+        only="only-ssd", alg_bytes=syn.ssd_bytes(scfg),
+        alg_note="x, z, dt, B, C read, y written once")
+    out += summarize_workload(
+        d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace, prof,
+        title="decode step, workload %s (one ssm_state_update call)" % dcfg.name,
+        fname="step_kernel_%s.txt" % dcfg.name, keys=["step_kernel"],
+        tag="decode", only="only-decode", alg_bytes=syn.decode_step_bytes(dcfg),
+        alg_note="fp32 state read and written, x, delta, z, B, C read, y "
+                 "written")
+    out += summarize_workload(
+        d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace, prof,
+        title="backward, workload %s (checkpoint pass, sweep, reductions)"
+              % bcfg.name,
+        fname="bwd_kernels_%s.txt" % bcfg.name,
+        keys=["bwd_", CKPT_KERNEL], tag="bwd", only="only-bwd",
+        alg_bytes=syn.backward_bytes(bcfg),
+        alg_note="inputs and dy read, gradients written once; the per-group "
+                 "partial sums of dB and dC are extra by design")
+    return out
 
 if __name__ == "__main__":
     main()
