@@ -374,12 +374,43 @@ def bwd_measure(ssm, syn, dev, stream, reps, log):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+
+    # a training step's pair: the forward that keeps the checkpoints, then
+    # the backward that reuses them (no checkpoint pass)
+    fy = torch.empty_like(binp["u"])
+    fh = torch.empty(ccfg.batch, ccfg.dim, 16, device=dev)
+
+    def frun():
+        ssm.ssm_scan_fwd_save(binp["u"], binp["delta"], binp["A"], binp["B"],
+                              binp["C"], binp["D"], binp["z"], binp["delta_bias"],
+                              True, None, y=fy, h_final=fh, workspace=bws,
+                              stream=stream)
+
+    def srun():
+        ssm.ssm_scan_bwd(binp["u"], binp["delta"], binp["A"], binp["B"],
+                         binp["C"], binp["D"], binp["z"], binp["delta_bias"],
+                         True, None, bdy, None, out=bout, workspace=bws,
+                         stream=stream, saved=True)
+    frun()
+    srun()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        frun()
+        srun()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pair_ms = e0.elapsed_time(e1) / reps
     nb = syn.backward_bytes(ccfg)
     return {"ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
             "elements_per_s": round(ccfg.elements / (ms * 1e-3)),
             "algorithmic_bytes": nb, "workspace_bytes": bws.numel(),
+            "fwd_save_plus_bwd_saved_ms": round(pair_ms, 4),
             "note": "gradients of u, delta, A, B, C, D, z, bias; states "
-                    "recomputed from 1024-token checkpoints"}
+                    "recomputed from 1024-token checkpoints (ms_per_call: "
+                    "the backward alone, with its own checkpoint pass; "
+                    "fwd_save_plus_bwd_saved_ms: ssm_scan_fwd_save then "
+                    "ssm_scan_bwd reusing its checkpoints)"}
 
 
 def decode_measure(ssm, syn, dev, stream, passes, log):

@@ -81,6 +81,10 @@ typedef enum {
  * section 1 "Discretisation": B_bar = (exp(dt A) - I) A^-1 B), dt*B*u where
  * A = 0.  Costs about twice the VALU work of the default Euler term. */
 #define SSM_FLAG_ZOH_B 2u
+/* ssm_scan_bwd only: the workspace already holds the block checkpoints and
+ * the pre-gate output that ssm_scan_fwd_save wrote for the same inputs, so
+ * the backward skips its own checkpoint pass (a forward recomputation). */
+#define SSM_FLAG_BWD_SAVED 4u
 
 /* Returns SSM_SCAN_ABI_VERSION. */
 int ssm_abi_version(void);
@@ -218,7 +222,11 @@ int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *  dh0                 nullable output fp32 (batch, dim, dstate)
  *  workspace           device scratch of >= ssm_scan_bwd_workspace_size()
  *                      bytes, 256-byte aligned, in use until the enqueued work
- *                      completes; its contents on entry do not matter
+ *                      completes; its contents on entry do not matter, except
+ *                      with SSM_FLAG_BWD_SAVED (flags may add it): then its
+ *                      checkpoint region must hold what ssm_scan_fwd_save
+ *                      wrote for the same u, delta, A, B, C, D, delta_bias,
+ *                      h0 and softplus flag (not checked)
  * No output may overlap an input, another output or the workspace.  The
  * sequence is not split across waves (one wave per channel over the whole
  * sequence), so shapes with few channels and very long sequences run with
@@ -231,6 +239,29 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
                  float *ddelta_bias, void *dz, float *dh0, int64_t batch,
                  int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Forward pass for training: the same computation and outputs (y, h_final)
+ * as ssm_scan_fwd over whole sequences (no split), which in addition keeps
+ * what the backward recomputes otherwise -- the state entering every
+ * 1024-token block and the output before the gate -- in the backward's
+ * workspace.  A following ssm_scan_bwd on the same inputs with
+ * SSM_FLAG_BWD_SAVED and that workspace then skips its checkpoint pass.
+ * (The inferownia.pl page on Mamba, section "Cena selekcji": the backward
+ * recomputes the intermediate states rather than storing them; here one
+ * state per block is kept.)
+ *  arguments as for ssm_scan_fwd, except:
+ *  flags           SSM_FLAG_DELTA_SOFTPLUS (SSM_FLAG_ZOH_B: SSM_ERR_UNSUPPORTED,
+ *                  the backward implements the Euler term only)
+ *  bwd_workspace   required, >= ssm_scan_bwd_workspace_size() bytes for the
+ *                  same shape and dtype, 256-byte aligned, not overlapping any
+ *                  argument; its checkpoint region is overwritten
+ * The shape limits of ssm_scan_bwd apply. */
+int ssm_scan_fwd_save(const void *u, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D, const void *z,
+                      const float *delta_bias, unsigned flags, const float *h0,
+                      void *y, float *h_final, int64_t batch, int64_t dim,
+                      int64_t dstate, int64_t seqlen, int dtype, void *bwd_workspace,
+                      size_t bwd_workspace_bytes, void *stream);
 
 /* Bytes of caller-provided device workspace ssm_ssd_fwd needs: per chunk of
  * 64 tokens and group, the causal G = C^T B (64 x 64, as two bf16 arrays:

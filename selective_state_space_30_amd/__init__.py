@@ -19,7 +19,9 @@ Names follow the C ABI:
   d_state 64-256) on the matrix cores; :func:`ssm_ssd_workspace_size`.
 * :func:`ssm_scan_bwd` -- gradients of :func:`ssm_scan_fwd` (Euler input
   term) with respect to every input, recomputing the states from block
-  checkpoints; :func:`ssm_scan_bwd_workspace_size`.
+  checkpoints; :func:`ssm_scan_bwd_workspace_size`;
+  :func:`ssm_scan_fwd_save`, the forward that keeps those checkpoints for
+  the backward (which then skips its own checkpoint pass).
 * :func:`ssm_scan_plan`, :func:`ssm_scan_workspace_size`,
   :func:`ssm_last_error`, :func:`ssm_abi_version`.
 """
@@ -38,11 +40,12 @@ SSM_DTYPE_F32 = 0
 SSM_DTYPE_BF16 = 1
 SSM_FLAG_DELTA_SOFTPLUS = 1
 SSM_FLAG_ZOH_B = 2
+SSM_FLAG_BWD_SAVED = 4
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
           3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
 EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
            "ssm_scan_fwd", "ssm_conv_scan_fwd", "ssm_state_update",
-           "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
+           "ssm_scan_bwd_workspace_size", "ssm_scan_fwd_save", "ssm_scan_bwd",
            "ssm_ssd_workspace_size", "ssm_ssd_fwd", "ssm_last_error")
 
 _lib = None
@@ -96,6 +99,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                      [I64, I64, I64, I64, I, P,
                                       ctypes.c_size_t, P])
         lib.ssm_scan_bwd.restype = I
+        lib.ssm_scan_fwd_save.argtypes = ([P] * 8 + [U] + [P] * 3 +
+                                          [I64, I64, I64, I64, I, P,
+                                           ctypes.c_size_t, P])
+        lib.ssm_scan_fwd_save.restype = I
         lib.ssm_ssd_workspace_size.argtypes = [
             I64, I64, I64, I64, ctypes.POINTER(ctypes.c_size_t)]
         lib.ssm_ssd_workspace_size.restype = I
@@ -352,17 +359,64 @@ def ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen,
     return out.value
 
 
+def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                      delta_softplus=True, h0=None, return_final_state=True,
+                      y=None, h_final=None, workspace=None, stream=None):
+    """:func:`ssm_scan_fwd` (whole sequences) that also keeps, in the
+    backward's workspace, the state entering every 1024-token block and the
+    pre-gate output.  Returns ``(y, h_final, workspace)``; pass that
+    workspace to :func:`ssm_scan_bwd` with ``saved=True`` (same inputs) to
+    skip the backward's checkpoint pass."""
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    N = A.shape[-1] if A.dim() == 2 else 0
+    dev = u.device
+    act = u.dtype
+    code = _dtype_code(u)
+    f32 = torch.float32
+    if y is None:
+        y = torch.empty((batch, dim, L), dtype=act, device=dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, dim, N), dtype=f32, device=dev)
+    if not return_final_state:
+        h_final = None
+    ws_bytes = ssm_scan_bwd_workspace_size(batch, dim, N, L, act)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsn = workspace.numel() * workspace.element_size()
+    _check(load_library().ssm_scan_fwd_save(
+        _ptr(u, "u", act, (batch, dim, L), dev),
+        _ptr(delta, "delta", act, (batch, dim, L), dev),
+        _ptr(A, "A", f32, (dim, N), dev),
+        _ptr(B, "B", act, (batch, N, L), dev),
+        _ptr(C, "C", act, (batch, N, L), dev),
+        _ptr(D, "D", f32, (dim,), dev),
+        _ptr(z, "z", act, (batch, dim, L), dev),
+        _ptr(delta_bias, "delta_bias", f32, (dim,), dev),
+        _flags(delta_softplus, False),
+        _ptr(h0, "h0", f32, (batch, dim, N), dev),
+        _ptr(y, "y", act, (batch, dim, L), dev),
+        _ptr(h_final, "h_final", f32, (batch, dim, N), dev),
+        batch, dim, N, L, code, workspace.data_ptr(), wsn,
+        _stream_handle(dev, stream)))
+    return y, h_final, workspace
+
+
 def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                  delta_softplus=True, h0=None, dy=None, dh_final=None,
                  want_dz=True, want_dh0=True, out=None, workspace=None,
-                 stream=None):
+                 stream=None, saved=False):
     """Gradients of :func:`ssm_scan_fwd` (Euler input term) for a loss with
     gradient ``dy`` (batch, dim, L; activation dtype) with respect to y and
     ``dh_final`` (batch, dim, N; fp32, or None) with respect to the final
     state.  Returns a dict: du, ddelta (activation dtype), dA, dB, dC, dD,
     ddelta_bias, dh0 (fp32) and dz (activation dtype, when z is given).
     ``out`` may supply any of these tensors; the rest, and the workspace,
-    are allocated here with torch."""
+    are allocated here with torch.  ``saved``: ``workspace`` holds what
+    :func:`ssm_scan_fwd_save` kept for these inputs (no checkpoint pass)."""
+    if saved and workspace is None:
+        raise ValueError("saved=True needs the workspace ssm_scan_fwd_save filled")
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, L)")
     batch, dim, L = u.shape
@@ -399,7 +453,7 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(D, "D", f32, (dim,), dev),
         _ptr(z, "z", act, (batch, dim, L), dev),
         _ptr(delta_bias, "delta_bias", f32, (dim,), dev),
-        _flags(delta_softplus, False),
+        _flags(delta_softplus, False) | (SSM_FLAG_BWD_SAVED if saved else 0),
         _ptr(h0, "h0", f32, (batch, dim, N), dev),
         _ptr(dy, "dy", act, (batch, dim, L), dev),
         _ptr(dh_final, "dh_final", f32, (batch, dim, N), dev),

@@ -172,8 +172,26 @@ int ssm_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
 
 namespace {
 
-// Shared by ssm_scan_fwd (u given) and ssm_conv_scan_fwd (x, conv_w given;
-// u = silu(conv1d(x)) is formed inside the kernel).
+// Sizes of the backward pass that fit its grid and its workspace arithmetic.
+int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  int st = check_sizes(batch, dim, dstate, seqlen);
+  if (st != SSM_OK) return st;
+  const int64_t groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
+  int64_t e;
+  if (groups >= (int64_t(1) << 31) || !mul_ok(batch * groups, ssm::kStates * seqlen, &e) ||
+      !mul_ok(e, 8, &e))
+    return fail(SSM_ERR_UNSUPPORTED, "backward workspace of this shape overflows");
+  // the channel-sum reduction launches one workgroup per 256 tokens of each
+  // (batch, state) row
+  if (batch * ssm::kStates * ((seqlen + 255) / 256) >= (int64_t(1) << 31))
+    return fail(SSM_ERR_UNSUPPORTED, "batch*seqlen too large for the backward reduction");
+  return SSM_OK;
+}
+
+// Shared by ssm_scan_fwd (u given), ssm_conv_scan_fwd (x, conv_w given;
+// u = silu(conv1d(x)) is formed inside the kernel) and ssm_scan_fwd_save
+// (saved = a backward workspace that receives the block checkpoints and the
+// pre-gate output; whole sequences, no split).
 int scan_impl(const void *u, const void *x, const float *conv_w,
               const float *conv_b, int d_conv, const void *delta,
               const float *A, const void *B, const void *C, const float *D,
@@ -181,7 +199,7 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
               const float *h0, void *y, float *h_final, int64_t batch,
               int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
               int64_t requested_chunk, void *workspace, size_t workspace_bytes,
-              void *stream) {
+              void *saved, size_t saved_bytes, void *stream) {
   if (x) {
     if (!conv_w) return fail(SSM_ERR_INVALID_ARG, "conv_w is NULL");
     if (d_conv < 1 || d_conv > ssm::kMaxConv)
@@ -234,7 +252,29 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
   if (overlaps(y, big, h_final, sts))
     return fail(SSM_ERR_INVALID_ARG, "y overlaps h_final");
 
-  const int64_t chunk = choose_chunk(batch, dim, seqlen, requested_chunk);
+  if (saved) {
+    if (flags & SSM_FLAG_ZOH_B)
+      return fail(SSM_ERR_UNSUPPORTED,
+                  "saving for the backward: the backward implements the Euler input term only");
+    if (requested_chunk != 0)
+      return fail(SSM_ERR_INVALID_ARG, "saving for the backward runs whole sequences "
+                                       "(requested_chunk must be 0)");
+    st = check_bwd_sizes(batch, dim, dstate, seqlen);
+    if (st != SSM_OK) return st;
+    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen, es);
+    if (saved_bytes < l.total_bytes)
+      return fail(SSM_ERR_WORKSPACE, "backward workspace of %zu bytes needed (got %zu bytes at %p)",
+                  l.total_bytes, saved_bytes, saved);
+    if (!aligned(saved, 256))
+      return fail(SSM_ERR_INVALID_ARG, "backward workspace %p not 256-byte aligned", saved);
+    const void *all[] = {u, delta, z, B, C, A, D, delta_bias, h0, y, h_final};
+    const int64_t sizes[] = {big, big, big, bc, bc, dim * dstate * 4, dim * 4, dim * 4,
+                             sts, big, sts};
+    for (int i = 0; i < 11; ++i)
+      if (overlaps(saved, static_cast<int64_t>(l.total_bytes), all[i], sizes[i]))
+        return fail(SSM_ERR_INVALID_ARG, "backward workspace overlaps an argument array");
+  }
+  const int64_t chunk = saved ? seqlen : choose_chunk(batch, dim, seqlen, requested_chunk);
   const int64_t n_chunks = (seqlen + chunk - 1) / chunk;
   if (n_chunks > kMaxGridYZ)
     return fail(SSM_ERR_UNSUPPORTED, "more than %lld chunks requested",
@@ -275,6 +315,11 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
   a.n_chunks = static_cast<int>(n_chunks);
   a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
   a.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
+  if (saved) {
+    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen, es);
+    a.ckpt = reinterpret_cast<float *>(static_cast<char *>(saved) + l.off_ckpt);
+    a.yc = static_cast<char *>(saved) + l.off_yc;
+  }
   const int err = ssm::launch_scan(a, bf16, vec, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
@@ -296,6 +341,20 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A,
   return scan_impl(u, nullptr, nullptr, nullptr, 0, delta, A, B, C, D, z,
                    delta_bias, flags, h0, y, h_final, batch, dim, dstate,
                    seqlen, dtype, requested_chunk, workspace, workspace_bytes,
+                   nullptr, 0, stream);
+}
+
+int ssm_scan_fwd_save(const void *u, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D, const void *z,
+                      const float *delta_bias, unsigned flags, const float *h0,
+                      void *y, float *h_final, int64_t batch, int64_t dim,
+                      int64_t dstate, int64_t seqlen, int dtype, void *bwd_workspace,
+                      size_t bwd_workspace_bytes, void *stream) {
+  if (!u) return fail(SSM_ERR_INVALID_ARG, "u is NULL");
+  if (!bwd_workspace) return fail(SSM_ERR_WORKSPACE, "bwd_workspace is NULL");
+  return scan_impl(u, nullptr, nullptr, nullptr, 0, delta, A, B, C, D, z,
+                   delta_bias, flags, h0, y, h_final, batch, dim, dstate,
+                   seqlen, dtype, 0, nullptr, 0, bwd_workspace, bwd_workspace_bytes,
                    stream);
 }
 
@@ -311,7 +370,7 @@ int ssm_conv_scan_fwd(const void *x, const float *conv_w, const float *conv_b,
   return scan_impl(nullptr, x, conv_w, conv_b, d_conv, delta, A, B, C, D, z,
                    delta_bias, flags, h0, y, h_final, batch, dim, dstate,
                    seqlen, dtype, requested_chunk, workspace, workspace_bytes,
-                   stream);
+                   nullptr, 0, stream);
 }
 
 int ssm_state_update(float *state, const void *x, const void *delta,
@@ -376,21 +435,6 @@ int ssm_state_update(float *state, const void *x, const void *delta,
 
 namespace {
 
-// Sizes of the backward pass that fit its grid and its workspace arithmetic.
-int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
-  int st = check_sizes(batch, dim, dstate, seqlen);
-  if (st != SSM_OK) return st;
-  const int64_t groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
-  int64_t e;
-  if (groups >= (int64_t(1) << 31) || !mul_ok(batch * groups, ssm::kStates * seqlen, &e) ||
-      !mul_ok(e, 8, &e))
-    return fail(SSM_ERR_UNSUPPORTED, "backward workspace of this shape overflows");
-  // the channel-sum reduction launches one workgroup per 256 tokens of each
-  // (batch, state) row
-  if (batch * ssm::kStates * ((seqlen + 255) / 256) >= (int64_t(1) << 31))
-    return fail(SSM_ERR_UNSUPPORTED, "batch*seqlen too large for the backward reduction");
-  return SSM_OK;
-}
 
 }  // namespace
 
@@ -420,7 +464,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   if (dz && !z) return fail(SSM_ERR_INVALID_ARG, "dz given without z");
   if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
     return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (flags & ~kKnownFlags)
+  if (flags & ~(kKnownFlags | SSM_FLAG_BWD_SAVED))
     return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (flags & SSM_FLAG_ZOH_B)
     return fail(SSM_ERR_UNSUPPORTED, "the backward pass implements the Euler input term only");
@@ -483,7 +527,9 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   void *yc = w + l.off_yc;
 
   // 1. checkpoint pass: the forward scan without the gate, keeping the
-  //    block-start states and the pre-gate output (for dz)
+  //    block-start states and the pre-gate output (for dz); skipped when
+  //    ssm_scan_fwd_save already left them in this workspace
+  const bool saved = (flags & SSM_FLAG_BWD_SAVED) != 0;
   ssm::ScanArgs fa{};
   fa.u = u; fa.delta = delta; fa.B = B; fa.C = C; fa.z = nullptr;
   fa.A = A; fa.D = D; fa.bias = delta_bias; fa.h0 = h0;
@@ -493,7 +539,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   fa.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
   fa.zoh = 0;
   fa.ckpt = ckpt;
-  int err = ssm::launch_scan(fa, bf16, vec, stream);
+  int err = saved ? 0 : ssm::launch_scan(fa, bf16, vec, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
 

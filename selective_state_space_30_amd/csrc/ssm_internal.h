@@ -37,6 +37,8 @@ struct ScanArgs {
   float *ckpt;                        // backward's checkpoint pass: the state
                                       // at every block start, (batch, dim,
                                       // ceil(L/1024), 16)
+  void *yc;                           // with ckpt: the pre-gate output (dtype),
+                                      // or null
 };
 
 // Backward pass.  Per-workgroup partial sums (a workgroup = kBwdWaves

@@ -50,14 +50,14 @@ using namespace dev;
 // (dt = 0, u = 0) and are not stored.  hc[n]: the channel's state carried in
 // (wave-uniform), replaced by the state after the block.
 template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kConv,
-          bool kZoh>
+          bool kZoh, bool kCkpt>
 __device__ __forceinline__ void scan_block(
     const ScanArgs &p, int wave, int lane, int64_t t0, int64_t ct1,
     const T *__restrict__ Bb, const T *__restrict__ Cb,
     const T *__restrict__ urow, const T *__restrict__ drow,
-    const T *__restrict__ zrow, T *__restrict__ yrow, bool ch_ok, float bias,
-    float Dd, const float (&Ach)[kStates], float *sT, float (&hc)[kStates],
-    float &sdt_total, const float (&wc)[kMaxConv], float cb,
+    const T *__restrict__ zrow, T *__restrict__ yrow, T *__restrict__ ycrow,
+    bool ch_ok, float bias, float Dd, const float (&Ach)[kStates], float *sT,
+    float (&hc)[kStates], float &sdt_total, const float (&wc)[kMaxConv], float cb,
     float (&xc)[kMaxConv - 1]) {
   constexpr int K = kTokensPerLane;
   constexpr int KP = K + 4;  // padded LDS stride of one lane's run
@@ -181,6 +181,8 @@ __device__ __forceinline__ void scan_block(
     if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
   }
 
+  // checkpoint instance: the pre-gate output, for the backward's dz
+  if (kCkpt && ycrow && ch_ok) store_run<T, K, kVec, kFull>(ycrow, t0, tl, tend, y);
   if (zrow) {
     float zz[K];
     load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
@@ -233,6 +235,7 @@ void scan_kernel(ScanArgs p) {
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
   T *yrow = static_cast<T *>(p.y) + bd * p.L;
+  T *ycrow = (kCkpt && p.yc) ? static_cast<T *>(p.yc) + bd * p.L : nullptr;
   const T *Bb = static_cast<const T *>(p.B) + b * kStates * p.L;
   const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
   float sdt_total = 0.0f;
@@ -253,8 +256,10 @@ void scan_kernel(ScanArgs p) {
     xc[k] = (kConv && t >= 0) ? to_f32<T>(urow[t]) : 0.0f;
   }
 
-  // checkpoint pass of the backward (kCkpt; unsplit sequences, no gate, y =
-  // the pre-gate output): the state entering block k goes to ckpt[b, d, k, :]
+  // checkpoint instance (kCkpt; unsplit sequences): the state entering
+  // block k goes to ckpt[b, d, k, :]; with p.yc the pre-gate output goes
+  // there as well (the backward's own checkpoint pass runs without a gate
+  // and takes y itself as the pre-gate output)
   const int64_t nblk = (p.L + kBlockTokens - 1) / kBlockTokens;
   float *ck = (kCkpt && ch_ok) ? p.ckpt + bd * nblk * kStates : nullptr;
 
@@ -266,9 +271,9 @@ void scan_kernel(ScanArgs p) {
       for (int n = 0; n < kStates; ++n)
         ck[(t0 / kBlockTokens) * kStates + n] = hc[n];
     }
-    scan_block<T, kVec, true, kSoftplus, kConv, kZoh>(p, wave, lane, t0, ct1, Bb, Cb, urow,
-                                               drow, zrow, yrow, ch_ok, bias, Dd, Ach,
-                                               sT, hc, sdt_total, wc, cb, xc);
+    scan_block<T, kVec, true, kSoftplus, kConv, kZoh, kCkpt>(
+        p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, Ach,
+        sT, hc, sdt_total, wc, cb, xc);
   }
   if (kCkpt && t0 < ct1 && ck && lane == 0) {
 #pragma unroll
@@ -277,9 +282,9 @@ void scan_kernel(ScanArgs p) {
   if (t0 < ct1)
     // the last, partial block: branch-free scalar loads (rare; keeps the
     // register budget of the full-block loop)
-    scan_block<T, false, false, kSoftplus, kConv, kZoh>(p, wave, lane, t0, ct1, Bb, Cb, urow,
-                                                  drow, zrow, yrow, ch_ok, bias, Dd, Ach,
-                                                  sT, hc, sdt_total, wc, cb, xc);
+    scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt>(
+        p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, Ach,
+        sT, hc, sdt_total, wc, cb, xc);
 
   if (!ch_ok) return;
   if (p.n_chunks == 1) {

@@ -257,6 +257,7 @@ INVALID_BWD_CASES = [
     ("null dC", dict(dC=None), 1),
     ("dz without z", dict(dz=FAKE + 0x70000000), 1),
     ("zoh flag", dict(flags=3), 2),
+    ("zoh flag with saved", dict(flags=7), 2),
     ("unknown flag", dict(flags=8), 1),
     ("dstate 8", dict(dstate=8), 2),
     ("zero seqlen", dict(seqlen=0), 1),
@@ -275,6 +276,47 @@ INVALID_BWD_CASES = [
                          ids=[c[0] for c in INVALID_BWD_CASES])
 def test_bwd_rejects_invalid_arguments(lib, name, kw, status):
     assert _bwd(lib, **kw) == status, ssm.ssm_last_error()
+    assert ssm.ssm_last_error()
+
+
+def _save(lib, **kw):
+    step = 0x08000000
+    names = ["u", "delta", "A", "B", "C", "y", "ws"]
+    a = {n: FAKE + i * step for i, n in enumerate(names)}
+    a.update(D=None, z=None, bias=None, flags=1, h0=None, h_final=None,
+             batch=1, dim=16, dstate=16, seqlen=256, dtype=ssm.SSM_DTYPE_F32,
+             stream=None)
+    size = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 0, ctypes.byref(size)) == 0
+    a["ws_bytes"] = size.value
+    a.update(kw)
+    return lib.ssm_scan_fwd_save(a["u"], a["delta"], a["A"], a["B"], a["C"],
+                                 a["D"], a["z"], a["bias"], a["flags"], a["h0"],
+                                 a["y"], a["h_final"], a["batch"], a["dim"],
+                                 a["dstate"], a["seqlen"], a["dtype"], a["ws"],
+                                 a["ws_bytes"], a["stream"])
+
+
+INVALID_SAVE_CASES = [
+    ("null u", dict(u=None), 1),
+    ("null y", dict(y=None), 1),
+    ("null workspace", dict(ws=None), 3),
+    ("workspace too small", dict(ws_bytes=4096), 3),
+    ("workspace misaligned", dict(ws=FAKE + 6 * 0x08000000 + 64), 1),
+    ("workspace overlaps y", dict(ws=FAKE + 5 * 0x08000000 + 256), 1),
+    ("y overlaps u", dict(y=FAKE + 64), 1),
+    ("zoh flag", dict(flags=3), 2),
+    ("backward-only flag", dict(flags=5), 1),
+    ("dstate 8", dict(dstate=8), 2),
+    ("zero seqlen", dict(seqlen=0), 1),
+    ("misaligned bf16 activation", dict(u=FAKE + 1, dtype=1), 1),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_SAVE_CASES,
+                         ids=[c[0] for c in INVALID_SAVE_CASES])
+def test_fwd_save_rejects_invalid_arguments(lib, name, kw, status):
+    assert _save(lib, **kw) == status, ssm.ssm_last_error()
     assert ssm.ssm_last_error()
 
 

@@ -192,3 +192,49 @@ def test_bwd_channel_sums_by_homogeneity():
     scale = float((dy.abs() * y.double().abs()).sum())
     assert abs(lhs - rB) <= 1e-2 * scale, (lhs, rB, scale)
     assert abs(lhs - rC) <= 1e-2 * scale, (lhs, rC, scale)
+
+
+SAVE_CASES = [
+    # (batch, dim, L, dtype, z, h0, softplus)
+    (2, 13, 2100, "f32", 1, 1, 1),    # ragged tail, dim % 8 != 0
+    (2, 20, 3072, "bf16", 1, 1, 1),   # full blocks, aligned bf16 rows
+    (1, 9, 1500, "bf16", 0, 0, 1),    # no gate: y is the pre-gate output
+    (2, 8, 1024, "f32", 1, 0, 0),     # softplus off (and no bias: dt > 0)
+]
+
+
+@pytest.mark.parametrize("case", SAVE_CASES,
+                         ids=lambda c: "b%d_d%d_l%d_%s_z%d_h%d_sp%d" % c)
+def test_fwd_save_then_bwd_skips_the_checkpoint_pass(case):
+    """ssm_scan_fwd_save gives the forward's outputs and leaves in the
+    backward's workspace what its checkpoint pass would compute: the
+    backward with saved=True gives the same bits as the one that recomputes,
+    and the forward's y and h_final match the oracle."""
+    batch, dim, L, dt, wz, wh, sp = case
+    inp = make(batch, dim, L, dt, 800 + L + dim, with_z=bool(wz),
+               with_bias=bool(sp), with_h0=bool(wh), softplus=bool(sp))
+    d = to_dev(inp)
+    y, hf, ws = ssm.ssm_scan_fwd_save(d["u"], d["delta"], d["A"], d["B"],
+                                      d["C"], d["D"], d["z"], d["delta_bias"],
+                                      d["delta_softplus"], d["h0"])
+    ws.view(-1)[ws.numel() // 2:].fill_(0x7F)  # partial sums: must not matter
+    g_saved = ssm.ssm_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"],
+                               d["D"], d["z"], d["delta_bias"],
+                               d["delta_softplus"], d["h0"], d["dy"],
+                               d["dh_final"], workspace=ws, saved=True)
+    g_full = gpu_bwd(d)
+    torch.cuda.synchronize()
+    for k in g_full:
+        assert torch.isfinite(g_full[k].float()).all(), k
+        assert torch.equal(g_saved[k], g_full[k]), k
+    y_ref, h_ref = oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"],
+                               inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                               inp["delta_softplus"], False, inp["h0"])
+    check(y, y_ref, TOL[dt], "y")
+    check(hf, h_ref, TOL[dt], "h_final")
+    y2, h2 = ssm.ssm_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"],
+                              d["D"], d["z"], d["delta_bias"],
+                              d["delta_softplus"], d["h0"])
+    torch.cuda.synchronize()
+    check(y, y2.double(), TOL[dt], "y vs ssm_scan_fwd")
+    check(hf, h2.double(), TOL[dt], "h_final vs ssm_scan_fwd")
