@@ -167,3 +167,43 @@ def test_decode_unaligned_inputs(dtype, what):
         torch.cuda.synchronize()
         check(y, y_ref, tol, "y step %d" % t)
         check(state, ref_state, tol, "state step %d" % t)
+
+
+def test_decode_steps_replay_in_a_hip_graph():
+    """Serving loops capture decode steps once and replay them: 8 bound
+    steps captured into a graph (the library enqueues kernels only, no
+    memsets), replayed three times with eager work between the replays;
+    every replay gives the eager run's state and outputs bit for bit."""
+    cfg = syn.DecodeConfig("graph", 4, 96, 16, 8, dtype="bf16", seed=51)
+    inp = syn.make_decode_inputs(cfg, DEV, with_h0=True)
+    steps = [syn.step_slice(inp, t) for t in range(cfg.steps)]
+    side = torch.cuda.Stream()
+    state = inp["h0"].clone()
+    ys = [torch.empty(cfg.batch, cfg.dim, dtype=torch.bfloat16, device=DEV)
+          for _ in steps]
+    calls = [ssm.bind_state_update(state, s["x"], s["delta"], inp["A"],
+                                   s["B"], s["C"], inp["D"], s["z"],
+                                   inp["delta_bias"], True, y=ys[t],
+                                   stream=side)
+             for t, s in enumerate(steps)]
+    torch.cuda.synchronize()
+    for c in calls:
+        c()
+    side.synchronize()
+    ref_state = state.clone()
+    ref_ys = [y.clone() for y in ys]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for c in calls:
+            c()
+    for rep in range(3):
+        state.copy_(inp["h0"])
+        for y in ys:
+            y.fill_(rep + 1)
+        _ = (state * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state, ref_state), rep
+        for t, (y, r) in enumerate(zip(ys, ref_ys)):
+            assert torch.equal(y, r), (rep, t)
