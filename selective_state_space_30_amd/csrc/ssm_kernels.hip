@@ -49,6 +49,13 @@ using namespace dev;
 // nothing is masked; otherwise positions from ct1 on are identity steps
 // (dt = 0, u = 0) and are not stored.  hc[n]: the channel's state carried in
 // (wave-uniform), replaced by the state after the block.
+// Instances that carry the next block's u and delta in registers across
+// the block loop: aligned fp32 rows with the Euler term and no conv
+// prologue (their register budget, sized for 3 waves per SIMD, has the 32
+// registers free; the bf16 instance runs at its 128-register cap).
+template <typename T, bool kVec, bool kConv, bool kZoh, bool kCkpt>
+constexpr bool kPrefetch = sizeof(T) == 4 && kVec && !kConv && !kZoh && !kCkpt;
+
 template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kConv,
           bool kZoh, bool kCkpt>
 __device__ __forceinline__ void scan_block(
@@ -58,7 +65,8 @@ __device__ __forceinline__ void scan_block(
     const T *__restrict__ zrow, T *__restrict__ yrow, T *__restrict__ ycrow,
     bool ch_ok, float bias, float Dd, const float (&Ach)[kStates], float *sT,
     float (&hc)[kStates], float &sdt_total, const float (&wc)[kMaxConv], float cb,
-    float (&xc)[kMaxConv - 1]) {
+    float (&xc)[kMaxConv - 1], float (&upf)[kTokensPerLane],
+    float (&dpf)[kTokensPerLane], bool use_pf, int64_t pf_t0) {
   constexpr int K = kTokensPerLane;
   constexpr int KP = K + 4;  // padded LDS stride of one lane's run
   const int64_t tend = kFull ? t0 + kBlockTokens : ct1;
@@ -82,7 +90,12 @@ __device__ __forceinline__ void scan_block(
   float sdt = 0.0f;
   {
     float uu[K], dr[K];
-    load_run<T, K, kVec, kFull>(urow, t0, tl, tend, uu);
+    if (kPrefetch<T, kVec, kConv, kZoh, kCkpt> && kFull && use_pf) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) uu[j] = upf[j];
+    } else {
+      load_run<T, K, kVec, kFull>(urow, t0, tl, tend, uu);
+    }
     if constexpr (kConv) {
       // urow holds the pre-conv input x: u = silu(cb + sum_k wc[k] *
       // x[t-3+k]).  The three values before the lane's first token come
@@ -108,7 +121,12 @@ __device__ __forceinline__ void scan_block(
         uu[j] = silu_f(acc);
       }
     }
-    load_run<T, K, kVec, kFull>(drow, t0, tl, tend, dr);
+    if (kPrefetch<T, kVec, kConv, kZoh, kCkpt> && kFull && use_pf) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) dr[j] = dpf[j];
+    } else {
+      load_run<T, K, kVec, kFull>(drow, t0, tl, tend, dr);
+    }
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const float x = dr[j] + bias;
@@ -123,6 +141,13 @@ __device__ __forceinline__ void scan_block(
   // Phase 0's tile: its buffer was last read two phases ago, by every wave.
   run.store(sT, toff);
   const float sdtl = sdt * kLog2e;
+  // u and delta of the full block at pf_t0 (the next one, or this one
+  // again when none follows), in flight during this block's state loop
+  if constexpr (kPrefetch<T, kVec, kConv, kZoh, kCkpt> && kFull) {
+    const int64_t tlp = pf_t0 + static_cast<int64_t>(lane) * K;
+    load_run<T, K, kVec, true>(urow, pf_t0, tlp, pf_t0 + kBlockTokens, upf);
+    load_run<T, K, kVec, true>(drow, pf_t0, tlp, pf_t0 + kBlockTokens, dpf);
+  }
 
   // B and C are staged two states at a time in a double-buffered LDS tile
   // (tile[buffer][state][B|C][lane run][KP]); while the 4 waves compute
@@ -263,6 +288,8 @@ void scan_kernel(ScanArgs p) {
   const int64_t nblk = (p.L + kBlockTokens - 1) / kBlockTokens;
   float *ck = (kCkpt && ch_ok) ? p.ckpt + bd * nblk * kStates : nullptr;
 
+  float upf[kTokensPerLane], dpf[kTokensPerLane];  // prefetched u, delta
+  const int64_t last_full = ct0 + ((ct1 - ct0) / kBlockTokens - 1) * kBlockTokens;
   int64_t t0 = ct0;
 #pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens) {
@@ -273,7 +300,9 @@ void scan_kernel(ScanArgs p) {
     }
     scan_block<T, kVec, true, kSoftplus, kConv, kZoh, kCkpt>(
         p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, Ach,
-        sT, hc, sdt_total, wc, cb, xc);
+        sT, hc, sdt_total, wc, cb, xc,
+        upf, dpf, t0 > ct0,
+        t0 + 2 * kBlockTokens <= ct1 ? t0 + kBlockTokens : last_full);
   }
   if (kCkpt && t0 < ct1 && ck && lane == 0) {
 #pragma unroll
@@ -284,7 +313,7 @@ void scan_kernel(ScanArgs p) {
     // register budget of the full-block loop)
     scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt>(
         p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, Ach,
-        sT, hc, sdt_total, wc, cb, xc);
+        sT, hc, sdt_total, wc, cb, xc, upf, dpf, false, t0);
 
   if (!ch_ok) return;
   if (p.n_chunks == 1) {
