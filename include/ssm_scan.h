@@ -289,9 +289,9 @@ int ssm_ssd_workspace_size(int64_t batch, int64_t ngroups, int64_t dstate,
  *  h0, h_final    fp32 (batch, nheads, headdim, dstate), nullable
  *  flags          SSM_FLAG_DELTA_SOFTPLUS (SSM_FLAG_ZOH_B: SSM_ERR_UNSUPPORTED)
  *  dtype          SSM_DTYPE_BF16 (SSM_DTYPE_F32: SSM_ERR_UNSUPPORTED)
- *  headdim 64 and dstate 64, 128 or 256 in this build (else
- *  SSM_ERR_UNSUPPORTED); workspace as ssm_ssd_workspace_size(), 256-byte
- *  aligned.  Conventions as for ssm_scan_fwd. */
+ *  headdim 64 and dstate 64, 128 or 256, dstate * seqlen < 2^30 in this
+ *  build (else SSM_ERR_UNSUPPORTED); workspace as ssm_ssd_workspace_size(),
+ *  256-byte aligned.  Conventions as for ssm_scan_fwd. */
 int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
                 const void *C, const float *D, const void *z,
                 const float *dt_bias, unsigned flags, const float *h0, void *y,

@@ -606,6 +606,10 @@ int check_ssd_sizes(int64_t batch, int64_t nheads, int64_t headdim, int64_t ngro
   if (batch > kMaxGridYZ || nheads >= (int64_t(1) << 31) ||
       (seqlen + ssm::kSsdChunk - 1) / ssm::kSsdChunk > (int64_t(1) << 30))
     return fail(SSM_ERR_UNSUPPORTED, "grid too large");
+  // the kernel reads a group's B and a head's rows through 32-bit byte views
+  if (dstate * seqlen * 2 >= (int64_t(1) << 31))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate*seqlen=%lld: at most 2^30 - 1 in this build",
+                (long long)(dstate * seqlen));
   return SSM_OK;
 }
 

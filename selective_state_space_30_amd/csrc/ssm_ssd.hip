@@ -96,6 +96,19 @@ __device__ __forceinline__ u32x4 load8_clamped(const uint16_t *row, int64_t t, i
   return w;
 }
 
+// Byte view of n consecutive bf16 elements from `base` (wave-uniform) for
+// buffer loads: reads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bf16_view(const uint16_t *base, int64_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0,
+                                           static_cast<int>(n * 2), kBufferWord3);
+}
+
+// 16 bytes at byte offset voff + soff of a view (voff per lane, soff
+// wave-uniform).
+__device__ __forceinline__ u32x4 buf_load8(__amdgpu_buffer_rsrc_t v, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v, voff, soff, 0));
+}
+
 // ----------------------------------------------------------- chunk prep ---
 // Per (batch, group, chunk): the causal G = C^T B (64 x 64, [t][s], zero
 // for s > t) as bf16 G_hi and G_lo = bf16(G - G_hi), and C transposed to
@@ -279,6 +292,18 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
             bf16x8,
             *reinterpret_cast<const u32x4 *>(base + (g_off + part * T * T + 32 * ks)));
   };
+  // Aligned rows (kVec) are read through buffer views of whole matrices: a
+  // loop-invariant 32-bit lane offset, the chunk's start as the scalar
+  // offset, no address arithmetic per chunk; an 8-token piece never
+  // straddles a row end, and pieces past L read the next row (weight 0: dt
+  // = 0 there) or, past the view, 0.  Unaligned rows clamp per element.
+  const __amdgpu_buffer_rsrc_t vB = bf16_view(Bg, N * L);
+  int bo[2][kNTW];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int k = 0; k < kNTW; ++k)
+      bo[ks][k] = static_cast<int>(((16 * (kNTW * tt + k) + li) * L + 32 * ks + kq) * 2);
   auto load_b = [&](int c) __attribute__((always_inline)) {
     const int64_t t0 = static_cast<int64_t>(c) * T;
 #pragma unroll
@@ -286,8 +311,9 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
 #pragma unroll
       for (int k = 0; k < kNTW; ++k)
         ba[ks][k] = __builtin_bit_cast(
-            bf16x8, load8_clamped<kVec>(Bg + (16 * (kNTW * tt + k) + li) * L,
-                                        t0 + 32 * ks + kq, L));
+            bf16x8, kVec ? buf_load8(vB, bo[ks][k], static_cast<int>(t0 * 2))
+                         : load8_clamped<kVec>(Bg + (16 * (kNTW * tt + k) + li) * L,
+                                               t0 + 32 * ks + kq, L));
   };
   // x and z as 16-byte pieces of rows (for LDS; with fewer pieces than
   // threads the upper threads repeat the lower ones' loads), dt one token a
@@ -296,19 +322,32 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   constexpr int kXP = R * (T / 8);
   constexpr int kXQ = (kXP + kThreads - 1) / kThreads;
   const uint16_t *zsrc = zh ? zh : xh;
+  const __amdgpu_buffer_rsrc_t vX = bf16_view(xh, R * L), vZ = bf16_view(zsrc, R * L);
+  const __amdgpu_buffer_rsrc_t vDt = bf16_view(dth, L);
+  int xo[kXQ];
+#pragma unroll
+  for (int i = 0; i < kXQ; ++i) {
+    const int q = (tid + kThreads * i) % kXP, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
+    xo[i] = static_cast<int>((r * L + t8) * 2);
+  }
   u32x4 rx[kXQ], rz[kXQ];
   auto load_xz = [&](int c) __attribute__((always_inline)) {
     const int64_t t0 = static_cast<int64_t>(c) * T;
 #pragma unroll
     for (int i = 0; i < kXQ; ++i) {
-      const int q = (tid + kThreads * i) % kXP, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
-      rx[i] = load8_clamped<kVec>(xh + r * L, t0 + t8, L);
-      rz[i] = load8_clamped<kVec>(zsrc + r * L, t0 + t8, L);
+      if (kVec) {
+        rx[i] = buf_load8(vX, xo[i], static_cast<int>(t0 * 2));
+        rz[i] = buf_load8(vZ, xo[i], static_cast<int>(t0 * 2));
+      } else {
+        const int q = (tid + kThreads * i) % kXP, r = q / (T / 8), t8 = (q % (T / 8)) * 8;
+        rx[i] = load8_clamped<kVec>(xh + r * L, t0 + t8, L);
+        rz[i] = load8_clamped<kVec>(zsrc + r * L, t0 + t8, L);
+      }
     }
   };
   auto load_dt = [&](int c) __attribute__((always_inline)) {
-    const int64_t t = static_cast<int64_t>(c) * T + lane;
-    return dth[t < L ? t : L - 1];  // steps past L count as 0 in steps()
+    // past L: 0 from the view (steps() gives those tokens dt = 0 anyway)
+    return __builtin_amdgcn_raw_buffer_load_b16(vDt, lane * 2, c * T * 2, 0);
   };
 
   // The chunk's step quantities from its raw steps (one token a lane) into
@@ -386,21 +425,24 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
         ry[i] = *reinterpret_cast<const u32x4 *>(&Zs[buf][at(r, t8)]);
     }
   };
+  // (a wave-uniform chunk base and 32-bit lane offsets: no 64-bit address
+  // arithmetic per store; `rem` = the chunk's tokens inside L)
   auto store_y = [&](int c) __attribute__((always_inline)) {
     const int64_t t0 = static_cast<int64_t>(c) * T;
+    uint16_t *yc = yh + t0;
+    const int rem = L - t0 < T ? static_cast<int>(L - t0) : T;
 #pragma unroll
     for (int i = 0; i < kXQ; ++i) {
-      const int pc = tid + kThreads * i, r = pc / (T / 8), t8 = (pc % (T / 8)) * 8;
+      const int pc = tid + kThreads * i, t8 = (pc % (T / 8)) * 8;
       if (kXP % kThreads == 0 || pc < kXP) {
-        const int64_t t = t0 + t8;
-        uint16_t *yr = yh + r * L + t;
-        if (kVec && t + 8 <= L) {
+        uint16_t *yr = yc + (xo[i] / 2);  // row pc / 8, token t8 of the chunk
+        if (kVec && t8 + 8 <= rem) {
           *reinterpret_cast<u32x4 *>(yr) = ry[i];
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const uint32_t w = ry[i][e >> 1];
-            if (t + e < L) yr[e] = static_cast<uint16_t>((e & 1) ? w >> 16 : w);
+            if (t8 + e < rem) yr[e] = static_cast<uint16_t>((e & 1) ? w >> 16 : w);
           }
         }
       }

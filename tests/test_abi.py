@@ -363,6 +363,7 @@ INVALID_SSD_CASES = [
     ("groups do not divide heads", dict(ngroups=3), 1),
     ("zoh flag", dict(flags=3), 2),
     ("zero seqlen", dict(seqlen=0), 1),
+    ("dstate*seqlen beyond 32-bit views", dict(dstate=256, seqlen=1 << 22), 2),
     ("y overlaps x", dict(y=FAKE + 64), 1),
     ("misaligned A", dict(A=FAKE + 2 * 0x08000000 + 2), 1),
     ("workspace missing", dict(ws=None), 3),
