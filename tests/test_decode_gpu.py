@@ -207,3 +207,32 @@ def test_decode_steps_replay_in_a_hip_graph():
         assert torch.equal(state, ref_state), rep
         for t, (y, r) in enumerate(zip(ys, ref_ys)):
             assert torch.equal(y, r), (rep, t)
+
+
+def test_decode_state_of_more_than_2_31_elements():
+    """A state of 8200 x 16384 x 16 fp32 (2.15e9 elements, 8.6 GB): one
+    step, checked against the oracle channel by channel on samples that
+    include the last channel (indices past 2^31)."""
+    cfg = syn.DecodeConfig("big", 8200, 16384, 16, 1, dtype="bf16", seed=61)
+    assert cfg.batch * cfg.dim * 16 > 2 ** 31
+    inp = syn.make_decode_inputs(cfg, DEV, with_h0=True)
+    s = syn.step_slice(inp, 0)
+    state = inp["h0"]
+    h_before = {}
+    r = np.random.default_rng(7)
+    chans = sorted({(0, 0), (cfg.batch - 1, cfg.dim - 1)} |
+                   {(int(r.integers(cfg.batch)), int(r.integers(cfg.dim)))
+                    for _ in range(6)})
+    for b, d in chans:
+        h_before[b, d] = state[b:b + 1, d:d + 1].double().cpu().numpy().copy()
+    y = ssm.ssm_state_update(state, s["x"], s["delta"], inp["A"], s["B"],
+                             s["C"], inp["D"], s["z"], inp["delta_bias"], True)
+    torch.cuda.synchronize()
+    for b, d in chans:
+        ref = h_before[b, d]
+        y_ref = oracle.step(ref, s["x"][b:b + 1, d:d + 1], s["delta"][b:b + 1, d:d + 1],
+                            inp["A"][d:d + 1], s["B"][b:b + 1], s["C"][b:b + 1],
+                            inp["D"][d:d + 1], s["z"][b:b + 1, d:d + 1],
+                            inp["delta_bias"][d:d + 1], True, False)
+        check(y[b:b + 1, d:d + 1], y_ref, 2e-2, "y (b=%d, d=%d)" % (b, d))
+        check(state[b:b + 1, d:d + 1], ref, 2e-2, "state (b=%d, d=%d)" % (b, d))

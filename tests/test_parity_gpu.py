@@ -225,6 +225,17 @@ def test_long_context_workload_sampled():
     full_workload_check(cfg, 4, 1e-4)
 
 
+def test_more_than_2_31_elements():
+    """2048 channels x 1,100,000 tokens (2.25e9 elements per activation
+    tensor, 4.5 GB in bf16; a ragged last block; split into chunks): every
+    element index past 2^31 must address the right element, checked on
+    sampled channels including the last one."""
+    from dataclasses import replace
+    cfg = replace(syn.LONG_1M, dim=2048, seqlen=1_100_000, dtype="bf16")
+    assert cfg.batch * cfg.dim * cfg.seqlen > 2 ** 31
+    full_workload_check(cfg, 5, 2e-2)
+
+
 # ------------------------------------------------ exact ZOH input term
 ZOH_CASES = [
     # (batch, dim, L, dtype, chunk, A kind)
