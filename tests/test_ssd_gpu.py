@@ -160,3 +160,21 @@ def test_ssd_layer_workload_sampled():
         check(y[b, h, p:p + 1], yr[0], "y (b=%d h=%d p=%d)" % (b, h, p))
         check(hf[b, h, p:p + 1], hr[0], "h_final (b=%d h=%d p=%d)" % (b, h, p))
     assert torch.isfinite(y.float()).all()
+
+
+def test_ssd_more_than_2_31_elements():
+    """40 heads x 64 rows x 2^20 tokens (2.7e9 elements per activation
+    tensor, d_state 64): sampled heads, including the last row of the last
+    head, against the recurrent scan oracle."""
+    from dataclasses import replace
+    cfg = replace(syn.MAMBA2_LAYER, batch=1, nheads=40, dstate=64,
+                  seqlen=1 << 20)
+    assert cfg.batch * cfg.nheads * cfg.headdim * cfg.seqlen > 2 ** 31
+    inp = syn.make_ssd_inputs(cfg, DEV)
+    y, hf = gpu_ssd(inp)
+    for b, h, p in [(0, 0, 0), (0, 17, 33), (0, cfg.nheads - 1, cfg.headdim - 1)]:
+        a = _as_scan_channel(inp, b, h, p)
+        yr, hr = oracle.scan(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"],
+                             a["z"], a["delta_bias"], True, False, None)
+        check(y[b, h, p:p + 1], yr[0], "y (b=%d h=%d p=%d)" % (b, h, p))
+        check(hf[b, h, p:p + 1], hr[0], "h_final (b=%d h=%d p=%d)" % (b, h, p))
