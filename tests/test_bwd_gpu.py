@@ -238,3 +238,31 @@ def test_fwd_save_then_bwd_skips_the_checkpoint_pass(case):
     torch.cuda.synchronize()
     check(y, y2.double(), TOL[dt], "y vs ssm_scan_fwd")
     check(hf, h2.double(), TOL[dt], "h_final vs ssm_scan_fwd")
+
+
+def test_bwd_more_than_2_31_elements():
+    """1100 channels x 2^21 tokens (2.3e9 elements per activation tensor,
+    ~40 GB of workspace): the per-channel gradients of sampled channels,
+    including the last one, against the oracle."""
+    from dataclasses import replace
+    cfg = replace(syn.MAMBA_2P8B, batch=1, dim=1100, seqlen=1 << 21)
+    assert cfg.batch * cfg.dim * cfg.seqlen > 2 ** 31
+    inp = syn.make_scan_inputs(cfg, DEV)
+    g = torch.Generator(device=DEV).manual_seed(cfg.seed + 8)
+    inp["dy"] = torch.randn(cfg.batch, cfg.dim, cfg.seqlen, generator=g,
+                            device=DEV).to(inp["u"].dtype)
+    got = ssm.ssm_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                           inp["D"], inp["z"], inp["delta_bias"], True, None,
+                           inp["dy"], None)
+    torch.cuda.synchronize()
+    for b, d in [(0, 0), (0, 613), (0, cfg.dim - 1)]:
+        sl = (slice(b, b + 1), slice(d, d + 1))
+        ref = oracle.scan_bwd(inp["u"][sl], inp["delta"][sl], inp["A"][d:d + 1],
+                              inp["B"][b:b + 1], inp["C"][b:b + 1],
+                              inp["D"][d:d + 1], inp["z"][sl],
+                              inp["delta_bias"][d:d + 1], True, None,
+                              inp["dy"][sl], None)
+        for k in ("du", "ddelta", "dz"):
+            check(got[k][sl], ref[k], 2e-2, "%s (b=%d, d=%d)" % (k, b, d))
+        check(got["dA"][d], ref["dA"][0], 1e-4, "dA[%d]" % d)
+    assert torch.isfinite(got["dB"]).all() and torch.isfinite(got["dC"]).all()
