@@ -97,8 +97,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
   }
 
   float h[U][4], a4[4];
-#pragma unroll
-  for (int u = 0; u < U; ++u) load_state4<kVec>(p.state + ch[u] * kStates + 4 * q, h[u]);
   if constexpr (kVec) {
     const float4 av = *reinterpret_cast<const float4 *>(p.A + d * kStates + 4 * q);
     a4[0] = av.x; a4[1] = av.y; a4[2] = av.z; a4[3] = av.w;
@@ -106,23 +104,35 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) a4[i] = p.A[d * kStates + 4 * q + i];
   }
-  const float bias = p.bias ? p.bias[d] : 0.0f;
-  const float Dd = p.D ? p.D[d] : 0.0f;
-  float x[U], xr[U], zz[U], b4[U][4], c4[U][4];
+  // Every load is unconditional (an absent bias, D or gate reads some other
+  // valid input and is zeroed at its use): a load under a branch would make
+  // the merge wait for every load in flight, the state's included, before
+  // the rest are issued.
+  const float bias_raw = (p.bias ? p.bias : p.A)[d];
+  const float D_raw = (p.D ? p.D : p.A)[d];
+  const T *zsrc = static_cast<const T *>(p.z ? p.z : p.x);
+  float x[U], dr[U], zz[U], b4[U][4], c4[U][4];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const size_t bsel = bc[u];
     x[u] = to_f32<T>(static_cast<const T *>(p.x)[ch[u]]);
-    xr[u] = to_f32<T>(static_cast<const T *>(p.delta)[ch[u]]) + bias;
-    zz[u] = p.z ? to_f32<T>(static_cast<const T *>(p.z)[ch[u]]) : 0.0f;
+    dr[u] = to_f32<T>(static_cast<const T *>(p.delta)[ch[u]]);
+    zz[u] = to_f32<T>(zsrc[ch[u]]);
     load_act4<T, kVec>(static_cast<const T *>(p.B) + bsel * kStates + 4 * q, b4[u]);
     load_act4<T, kVec>(static_cast<const T *>(p.C) + bsel * kStates + 4 * q, c4[u]);
   }
 
+  // the state last: the wait counter retires loads in order, so the
+  // arithmetic on the small inputs can start while the state is in flight
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_state4<kVec>(p.state + ch[u] * kStates + 4 * q, h[u]);
+  const float bias = p.bias ? bias_raw : 0.0f;
+  const float Dd = p.D ? D_raw : 0.0f;
   float part[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const float dt = p.softplus ? softplus_f(xr[u]) : xr[u];
+    const float xr = dr[u] + bias;
+    const float dt = p.softplus ? softplus_f(xr) : xr;
     const float dx = dt * x[u];
     float acc = 0.0f;
 #pragma unroll
