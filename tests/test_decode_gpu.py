@@ -236,3 +236,29 @@ def test_decode_state_of_more_than_2_31_elements():
                             inp["delta_bias"][d:d + 1], True, False)
         check(y[b:b + 1, d:d + 1], y_ref, 2e-2, "y (b=%d, d=%d)" % (b, d))
         check(state[b:b + 1, d:d + 1], ref, 2e-2, "state (b=%d, d=%d)" % (b, d))
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (1, 65), (2, 1)],
+                         ids=lambda s: "b%d_d%d" % s)
+def test_decode_degenerate_shapes(shape):
+    """Batch 1 (a thread's second batch entry is past the end) and a single
+    channel (63 of the workgroup's 64 channels are past the end)."""
+    batch, dim = shape
+    cfg = syn.DecodeConfig("degenerate", batch, dim, 16, 4, dtype="bf16", seed=71)
+    inp = syn.make_decode_inputs(cfg, "cpu", with_h0=True)
+    dinp = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v)
+            for k, v in inp.items()}
+    state = dinp["h0"].clone()
+    ref_state = inp["h0"].double().numpy().copy()
+    for t in range(cfg.steps):
+        s = syn.step_slice(dinp, t)
+        y = ssm.ssm_state_update(state, s["x"], s["delta"], dinp["A"], s["B"],
+                                 s["C"], dinp["D"], s["z"],
+                                 dinp["delta_bias"], True)
+        sh = syn.step_slice(inp, t)
+        y_ref = oracle.step(ref_state, sh["x"], sh["delta"], inp["A"],
+                            sh["B"], sh["C"], inp["D"], sh["z"],
+                            inp["delta_bias"], True, False)
+        torch.cuda.synchronize()
+        check(y, y_ref, 2e-2, "y step %d" % t)
+        check(state, ref_state, 2e-2, "state step %d" % t)
