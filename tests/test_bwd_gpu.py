@@ -76,6 +76,7 @@ CASES = [
     (1, 6, 999, "f32", 1, 0, 1, 1, 1, 1),     # unaligned rows
     (2, 8, 1024, "f32", 0, 0, 0, 0, 0, 0),    # bare, softplus off
     (1, 5, 1, "f32", 1, 1, 1, 1, 1, 1),       # a single token
+    (2, 1, 300, "f32", 1, 1, 1, 1, 1, 1),     # one channel: 7 of 8 waves idle
     (2, 20, 3072, "bf16", 1, 1, 1, 1, 1, 1),
     (1, 9, 1500, "bf16", 1, 1, 0, 0, 1, 1),
 ]
