@@ -466,9 +466,32 @@ def decode_measure(ssm, syn, dev, stream, passes, log):
     e1.record(cur)
     torch.cuda.synchronize()
     us_graph = e0.elapsed_time(e1) * 1e3 / (dcfg.steps * passes)
+
+    # the same steps with the width-4 conv prologue (ssm_conv_state_update),
+    # each state with its own kept window, captured the same way
+    cinp = syn.make_conv_decode_inputs(dcfg, dev, d_conv=4)
+    windows = [cinp["conv_state0"].clone() for _ in range(4)]
+    torch.cuda.synchronize()
+    cgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cgraph, stream=side):
+        for t, s in enumerate(steps):
+            ssm.ssm_conv_state_update(
+                states[t % 4], windows[t % 4], s["x"], cinp["conv_w"],
+                s["delta"], dinp["A"], s["B"], s["C"], dinp["D"], s["z"],
+                dinp["delta_bias"], True, conv_b=cinp["conv_b"], y=ys[t],
+                stream=side)
+    cgraph.replay()
+    torch.cuda.synchronize()
+    e0.record(cur)
+    for _ in range(passes):
+        cgraph.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    us_conv = e0.elapsed_time(e1) * 1e3 / (dcfg.steps * passes)
     nb = syn.decode_step_bytes(dcfg)
     return {"us_per_step": round(us, 3), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
-            "bytes_per_step": nb, "us_per_step_hip_graph": round(us_graph, 3)}
+            "bytes_per_step": nb, "us_per_step_hip_graph": round(us_graph, 3),
+            "us_per_step_conv4_hip_graph": round(us_conv, 3)}
 
 
 def ssd_measure(ssm, syn, dev, stream, reps, log):
@@ -734,10 +757,21 @@ def summarize_extras(d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace,
     out += summarize_workload(
         d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace, prof,
         title="decode step, workload %s (one ssm_state_update call)" % dcfg.name,
-        fname="step_kernel_%s.txt" % dcfg.name, keys=["step_kernel"],
+        fname="step_kernel_%s.txt" % dcfg.name,
+        keys=["step_kernel<unsigned short, true, false>"],
         tag="decode", only="only-decode", alg_bytes=syn.decode_step_bytes(dcfg),
         alg_note="fp32 state read and written, x, delta, z, B, C read, y "
                  "written")
+    out += summarize_workload(
+        d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace, prof,
+        title="decode step with a width-4 conv, workload %s (one "
+              "ssm_conv_state_update call)" % dcfg.name,
+        fname="step_conv4_kernel_%s.txt" % dcfg.name,
+        keys=["step_kernel<unsigned short, true, true>"],
+        tag="decode", only="only-decode",
+        alg_bytes=syn.conv_decode_step_bytes(dcfg, 4),
+        alg_note="the plain step's bytes, the 3-input window read and "
+                 "written, taps and conv bias read")
     out += summarize_workload(
         d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace, prof,
         title="backward, workload %s (checkpoint pass, sweep, reductions)"

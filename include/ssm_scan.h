@@ -172,13 +172,41 @@ int ssm_conv_scan_fwd(const void *x, const float *conv_w, const float *conv_b,
  *  B, C       required, activation dtype (batch, dstate)
  *  D, z, delta_bias, flags   as for ssm_scan_fwd
  *  y          required output, activation dtype (batch, dim)
- * Applying it to tokens 0..L-1 in order reproduces ssm_scan_fwd's y and,
- * in `state`, its h_final. */
+ * batch at most 131070 and batch * dim below 2^32 in this build (else
+ * SSM_ERR_UNSUPPORTED).  Applying it to tokens 0..L-1 in order reproduces
+ * ssm_scan_fwd's y and, in `state`, its h_final. */
 int ssm_state_update(float *state, const void *x, const void *delta,
                      const float *A, const void *B, const void *C,
                      const float *D, const void *z, const float *delta_bias,
                      unsigned flags, void *y, int64_t batch, int64_t dim,
                      int64_t dstate, int dtype, void *stream);
+
+/* One decoding step with the fused conv prologue of ssm_conv_scan_fwd: the
+ * token's input first goes through the depthwise causal conv1d and SiLU
+ * (the Mamba block's Conv1D -> SiLU before the SSM; "Mamba & State Space
+ * Models - Guide Complet", sections 4 and 7), whose window of the previous
+ * d_conv - 1 inputs is kept per channel, then the step of ssm_state_update:
+ *   u     = silu(conv_b[d] + sum_k conv_w[d, k] * w_k),
+ *           w = (conv_state[b, d, 0 .. d_conv-2], x[b, d])   (oldest first)
+ *   then ssm_state_update with u in place of x (D skip on u, gate by z);
+ *   conv_state[b, d, :] <- (w_1 .. w_{d_conv-1}), the window moved by one.
+ * A fresh sequence starts with conv_state zero (inputs before t = 0 count
+ * as 0, as in ssm_conv_scan_fwd), so T steps reproduce ssm_conv_scan_fwd
+ * over the same T tokens.
+ *  conv_state     in/out, activation dtype (batch, dim, d_conv - 1);
+ *                 may be NULL only when d_conv = 1
+ *  conv_w, conv_b fp32 (dim, d_conv) and (dim); conv_b nullable
+ *  d_conv         1..4 (larger: SSM_ERR_UNSUPPORTED)
+ *  the rest       as for ssm_state_update; conv_state must not overlap any
+ *                 other argument. */
+int ssm_conv_state_update(float *state, void *conv_state, const void *x,
+                          const float *conv_w, const float *conv_b, int d_conv,
+                          const void *delta, const float *A, const void *B,
+                          const void *C, const float *D, const void *z,
+                          const float *delta_bias, unsigned flags, void *y,
+                          int64_t batch, int64_t dim, int64_t dstate, int dtype,
+                          void *stream);
+
 
 /* Bytes of caller-provided device workspace ssm_scan_bwd needs for this
  * shape and activation dtype: the block-start checkpoints

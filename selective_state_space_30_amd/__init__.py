@@ -17,6 +17,8 @@ Names follow the C ABI:
 * :func:`ssm_state_update` -- one decoding step on an in-place fp32 state.
 * :func:`ssm_ssd_fwd` -- the Mamba-2 SSD form (one scalar decay per head,
   d_state 64-256) on the matrix cores; :func:`ssm_ssd_workspace_size`.
+* :func:`ssm_conv_state_update` -- the decoding step with the conv
+  prologue (its window kept per channel).
 * :func:`ssm_scan_bwd` -- gradients of :func:`ssm_scan_fwd` (Euler input
   term) with respect to every input, recomputing the states from block
   checkpoints; :func:`ssm_scan_bwd_workspace_size`;
@@ -45,6 +47,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
           3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
 EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
            "ssm_scan_fwd", "ssm_conv_scan_fwd", "ssm_state_update",
+           "ssm_conv_state_update",
            "ssm_scan_bwd_workspace_size", "ssm_scan_fwd_save", "ssm_scan_bwd",
            "ssm_ssd_workspace_size", "ssm_ssd_fwd", "ssm_last_error")
 
@@ -92,6 +95,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, U, P,
                                          I64, I64, I64, I, P]
         lib.ssm_state_update.restype = I
+        lib.ssm_conv_state_update.argtypes = [P, P, P, P, P, I, P, P, P, P, P,
+                                              P, P, U, P, I64, I64, I64, I, P]
+        lib.ssm_conv_state_update.restype = I
         lib.ssm_scan_bwd_workspace_size.argtypes = [
             I64, I64, I64, I64, I, ctypes.POINTER(ctypes.c_size_t)]
         lib.ssm_scan_bwd_workspace_size.restype = I
@@ -310,6 +316,44 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
     _check(load_library().ssm_state_update(
         ps, px, pd, pA, pB, pC, pD, pz, pbias, flags, py, batch, dim, N,
         code, _stream_handle(dev, stream)))
+    return y
+
+
+def ssm_conv_state_update(state, conv_state, x, conv_w, delta, A, B, C,
+                          D=None, z=None, delta_bias=None, delta_softplus=True,
+                          conv_b=None, y=None, stream=None, zoh_b=False):
+    """One decoding step with the fused conv prologue: ``x`` (batch, dim)
+    goes through the causal conv1d + SiLU over the window kept in
+    ``conv_state`` (batch, dim, d_conv - 1; activation dtype; updated in
+    place, zero for a fresh sequence), then advances ``state`` (batch, dim,
+    N) fp32 in place like :func:`ssm_state_update`.  ``conv_w`` (dim,
+    d_conv) and ``conv_b`` (dim,) fp32.  Returns y (batch, dim)."""
+    if state.dim() != 3:
+        raise ValueError("state must be (batch, dim, N)")
+    batch, dim, N = state.shape
+    dev = state.device
+    act = x.dtype
+    code = _dtype_code(x)
+    K = conv_w.shape[-1] if conv_w.dim() == 2 else 0
+    if y is None:
+        y = torch.empty((batch, dim), dtype=act, device=dev)
+    pcs = (_ptr(conv_state, "conv_state", act, (batch, dim, K - 1), dev)
+           if K > 1 else None)
+    _check(load_library().ssm_conv_state_update(
+        _ptr(state, "state", torch.float32, (batch, dim, N), dev), pcs,
+        _ptr(x, "x", act, (batch, dim), dev),
+        _ptr(conv_w, "conv_w", torch.float32, (dim, K), dev),
+        _ptr(conv_b, "conv_b", torch.float32, (dim,), dev), K,
+        _ptr(delta, "delta", act, (batch, dim), dev),
+        _ptr(A, "A", torch.float32, (dim, N), dev),
+        _ptr(B, "B", act, (batch, N), dev),
+        _ptr(C, "C", act, (batch, N), dev),
+        _ptr(D, "D", torch.float32, (dim,), dev),
+        _ptr(z, "z", act, (batch, dim), dev),
+        _ptr(delta_bias, "delta_bias", torch.float32, (dim,), dev),
+        _flags(delta_softplus, zoh_b),
+        _ptr(y, "y", act, (batch, dim), dev),
+        batch, dim, N, code, _stream_handle(dev, stream)))
     return y
 
 

@@ -172,6 +172,78 @@ int ssm_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
 
 namespace {
 
+// Shared by ssm_state_update and ssm_conv_state_update (d_conv > 0: the
+// conv prologue with its window in conv_state).
+int step_impl(float *state, void *conv_state, const void *x, const float *conv_w,
+              const float *conv_b, int d_conv, const void *delta, const float *A,
+              const void *B, const void *C, const float *D, const void *z,
+              const float *delta_bias, unsigned flags, void *y, int64_t batch,
+              int64_t dim, int64_t dstate, int dtype, void *stream) {
+  if (!state || !x || !delta || !A || !B || !C || !y)
+    return fail(SSM_ERR_INVALID_ARG, "required pointer is NULL");
+  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & ~kKnownFlags)
+    return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  int st = check_sizes(batch, dim, dstate, 1);
+  if (st != SSM_OK) return st;
+  // grid: (ceil(dim / 64), ceil(batch / 2)), the second extent at most 65535
+  int64_t e;
+  if ((batch + 1) / 2 > kMaxGridYZ || !mul_ok(batch * dim, dstate * 4, &e) ||
+      batch * dim >= (int64_t(1) << 32))
+    return fail(SSM_ERR_UNSUPPORTED, "batch=%lld dim=%lld: too large for the decode grid",
+                (long long)batch, (long long)dim);
+
+  const bool bf16 = dtype == SSM_DTYPE_BF16;
+  const int64_t es = bf16 ? 2 : 4;
+  const void *acts[] = {x, delta, B, C, z, y, conv_state};
+  for (const void *p : acts)
+    if (p && !aligned(p, es))
+      return fail(SSM_ERR_INVALID_ARG, "activation pointer %p not %lld-byte aligned", p,
+                  (long long)es);
+  const void *f32s[] = {state, A, D, delta_bias, conv_w, conv_b};
+  for (const void *p : f32s)
+    if (p && !aligned(p, 4))
+      return fail(SSM_ERR_INVALID_ARG, "fp32 pointer %p not 4-byte aligned", p);
+
+  const int64_t bdn = batch * dim * dstate * 4;
+  const int64_t bd = batch * dim * es;
+  const int64_t bn = batch * dstate * es;
+  const int64_t csb = d_conv > 1 ? batch * dim * (d_conv - 1) * es : 0;
+  const struct { const void *p; int64_t n; const char *name; } ins[] = {
+      {x, bd, "x"}, {delta, bd, "delta"}, {z, bd, "z"}, {B, bn, "B"}, {C, bn, "C"},
+      {A, dim * dstate * 4, "A"}, {D, dim * 4, "D"}, {delta_bias, dim * 4, "delta_bias"},
+      {conv_w, d_conv > 0 ? dim * d_conv * 4 : 0, "conv_w"},
+      {conv_b, d_conv > 0 ? dim * 4 : 0, "conv_b"}};
+  for (const auto &in : ins) {
+    if (overlaps(state, bdn, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "state overlaps input %s", in.name);
+    if (overlaps(y, bd, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "y overlaps input %s", in.name);
+    if (overlaps(conv_state, csb, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "conv_state overlaps input %s", in.name);
+  }
+  if (overlaps(y, bd, state, bdn))
+    return fail(SSM_ERR_INVALID_ARG, "y overlaps state");
+  if (overlaps(conv_state, csb, state, bdn) || overlaps(conv_state, csb, y, bd))
+    return fail(SSM_ERR_INVALID_ARG, "conv_state overlaps state or y");
+
+  const bool vec = aligned(state, 16) && aligned(A, 16) && aligned(B, 4 * es) &&
+                   aligned(C, 4 * es);
+  ssm::StepArgs a{};
+  a.state = state; a.x = x; a.delta = delta; a.B = B; a.C = C; a.z = z;
+  a.A = A; a.D = D; a.bias = delta_bias; a.y = y;
+  a.batch = batch; a.dim = dim;
+  a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+  a.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
+  a.conv_state = d_conv > 1 ? conv_state : nullptr;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.d_conv = d_conv;
+  const int err = ssm::launch_step(a, bf16, vec, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  return ok();
+}
+
 // Sizes of the backward pass that fit its grid and its workspace arithmetic.
 int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
   int st = check_sizes(batch, dim, dstate, seqlen);
@@ -378,65 +450,28 @@ int ssm_state_update(float *state, const void *x, const void *delta,
                      const float *D, const void *z, const float *delta_bias,
                      unsigned flags, void *y, int64_t batch, int64_t dim,
                      int64_t dstate, int dtype, void *stream) {
-  if (!state || !x || !delta || !A || !B || !C || !y)
-    return fail(SSM_ERR_INVALID_ARG, "required pointer is NULL");
-  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
-    return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (flags & ~kKnownFlags)
-    return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
-  int st = check_sizes(batch, dim, dstate, 1);
-  if (st != SSM_OK) return st;
-  int64_t threads;
-  if (!mul_ok(batch * dim, 4, &threads) || threads / 256 >= (int64_t(1) << 31))
-    return fail(SSM_ERR_UNSUPPORTED, "batch*dim too large");
+  return step_impl(state, nullptr, x, nullptr, nullptr, 0, delta, A, B, C, D, z,
+                   delta_bias, flags, y, batch, dim, dstate, dtype, stream);
+}
 
-  const bool bf16 = dtype == SSM_DTYPE_BF16;
-  const int64_t es = bf16 ? 2 : 4;
-  const void *acts[] = {x, delta, B, C, z, y};
-  for (const void *p : acts)
-    if (p && !aligned(p, es))
-      return fail(SSM_ERR_INVALID_ARG, "activation pointer %p not %lld-byte aligned", p,
-                  (long long)es);
-  const void *f32s[] = {state, A, D, delta_bias};
-  for (const void *p : f32s)
-    if (p && !aligned(p, 4))
-      return fail(SSM_ERR_INVALID_ARG, "fp32 pointer %p not 4-byte aligned", p);
-
-  const int64_t bdn = batch * dim * dstate * 4;
-  const int64_t bd = batch * dim * es;
-  const int64_t bn = batch * dstate * es;
-  const struct { const void *p; int64_t n; const char *name; } ins[] = {
-      {x, bd, "x"}, {delta, bd, "delta"}, {z, bd, "z"}, {B, bn, "B"}, {C, bn, "C"},
-      {A, dim * dstate * 4, "A"}, {D, dim * 4, "D"}, {delta_bias, dim * 4, "delta_bias"}};
-  for (const auto &in : ins) {
-    if (overlaps(state, bdn, in.p, in.n))
-      return fail(SSM_ERR_INVALID_ARG, "state overlaps input %s", in.name);
-    if (overlaps(y, bd, in.p, in.n))
-      return fail(SSM_ERR_INVALID_ARG, "y overlaps input %s", in.name);
-  }
-  if (overlaps(y, bd, state, bdn))
-    return fail(SSM_ERR_INVALID_ARG, "y overlaps state");
-
-  const bool vec = aligned(state, 16) && aligned(A, 16) && aligned(B, 4 * es) &&
-                   aligned(C, 4 * es);
-  ssm::StepArgs a{};
-  a.state = state; a.x = x; a.delta = delta; a.B = B; a.C = C; a.z = z;
-  a.A = A; a.D = D; a.bias = delta_bias; a.y = y;
-  a.batch = batch; a.dim = dim;
-  a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
-  a.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
-  const int err = ssm::launch_step(a, bf16, vec, stream);
-  if (err != 0)
-    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
-  return ok();
+int ssm_conv_state_update(float *state, void *conv_state, const void *x,
+                          const float *conv_w, const float *conv_b, int d_conv,
+                          const void *delta, const float *A, const void *B,
+                          const void *C, const float *D, const void *z,
+                          const float *delta_bias, unsigned flags, void *y,
+                          int64_t batch, int64_t dim, int64_t dstate, int dtype,
+                          void *stream) {
+  if (!conv_w) return fail(SSM_ERR_INVALID_ARG, "conv_w is NULL");
+  if (d_conv < 1 || d_conv > ssm::kMaxConv)
+    return fail(d_conv < 1 ? SSM_ERR_INVALID_ARG : SSM_ERR_UNSUPPORTED,
+                "d_conv=%d: supported 1..%d", d_conv, ssm::kMaxConv);
+  if (d_conv > 1 && !conv_state)
+    return fail(SSM_ERR_INVALID_ARG, "conv_state is NULL (d_conv=%d)", d_conv);
+  return step_impl(state, conv_state, x, conv_w, conv_b, d_conv, delta, A, B, C, D,
+                   z, delta_bias, flags, y, batch, dim, dstate, dtype, stream);
 }
 
 }  // extern "C"
-
-namespace {
-
-
-}  // namespace
 
 extern "C" {
 

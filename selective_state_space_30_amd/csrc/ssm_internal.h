@@ -84,6 +84,12 @@ struct StepArgs {
   int64_t batch, dim;
   int softplus;
   int zoh;
+  // conv prologue (d_conv > 0): u = silu(conv_b + sum_k conv_w[d, k] *
+  // window_k) over the d_conv - 1 inputs kept in conv_state and x; the
+  // state's window is shifted in place
+  void *conv_state;                   // (batch, dim, d_conv - 1), dtype
+  const float *conv_w, *conv_b;       // (dim, d_conv), (dim)
+  int d_conv;                         // 1..4, 0 = no prologue
 };
 
 // Workspace layout of the split (chunked) scan, in floats, each part

@@ -76,7 +76,9 @@ __device__ __forceinline__ void load_act4(const T *p, float (&v)[4]) {
 
 // grid: (ceil(dim / kStepChannels), ceil(batch / kStepBatch)); thread =
 // (channel d, states 4q .. 4q+3) for batch entries kStepBatch*blockIdx.y + u.
-template <typename T, bool kVec>
+// kConv: the input x passes through the causal conv1d + SiLU first (the
+// same prologue as the scan's), its window carried in conv_state.
+template <typename T, bool kVec, bool kConv>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
   constexpr int U = kStepBatch;
   const uint32_t dim = static_cast<uint32_t>(p.dim);
@@ -104,6 +106,35 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) a4[i] = p.A[d * kStates + 4 * q + i];
   }
+  // conv prologue.  Slots 0..kMaxConv-1 of a channel's conv input are the
+  // kMaxConv - 1 window positions, then x; the taps are aligned to the last
+  // slots and the kept inputs to the last window positions, so with d_conv
+  // taps the first kMaxConv - d_conv slots have neither (zeros).  Lane q of
+  // the quad loads tap q and window position q, once for the whole quad, at
+  // a clamped valid address; the values reach the other lanes by DPP
+  // broadcast and the absent slots are zeroed there, on a condition uniform
+  // across the wave (a per-lane select right after a load would make the
+  // compiler wait for it before the state loads are issued).
+  float wq = 0.0f, cb = 0.0f, wl[U];
+  int K = 0, H = 0;
+  if constexpr (kConv) {
+    K = p.d_conv;
+    H = K - 1;
+    const int ti = q - (kMaxConv - K);       // tap of lane q, or none
+    const int wi = q - (kMaxConv - 1 - H);   // kept input of lane q, or none
+    const float cb_raw = (p.conv_b ? p.conv_b : p.conv_w)[d];
+    wq = p.conv_w[d * K + (ti < 0 ? 0 : ti)];
+    // H = 0: no window; every lane reads x (stride 1, a valid address).  One
+    // address form for both, so the load is not branched.
+    const T *cs = static_cast<const T *>(H > 0 ? p.conv_state : p.x);
+    const uint32_t hs = H > 0 ? H : 1;
+    const int hmax = H > 0 ? H - 1 : 0;
+    const uint32_t idx = wi < 0 ? 0 : (wi > hmax ? hmax : wi);
+#pragma unroll
+    for (int u = 0; u < U; ++u) wl[u] = to_f32<T>(cs[ch[u] * hs + idx]);
+    cb = p.conv_b ? cb_raw : 0.0f;
+  }
+
   // Every load is unconditional (an absent bias, D or gate reads some other
   // valid input and is zeroed at its use): a load under a branch would make
   // the merge wait for every load in flight, the state's included, before
@@ -121,13 +152,37 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
     load_act4<T, kVec>(static_cast<const T *>(p.B) + bsel * kStates + 4 * q, b4[u]);
     load_act4<T, kVec>(static_cast<const T *>(p.C) + bsel * kStates + 4 * q, c4[u]);
   }
-
   // the state last: the wait counter retires loads in order, so the
   // arithmetic on the small inputs can start while the state is in flight
 #pragma unroll
   for (int u = 0; u < U; ++u) load_state4<kVec>(p.state + ch[u] * kStates + 4 * q, h[u]);
   const float bias = p.bias ? bias_raw : 0.0f;
   const float Dd = p.D ? D_raw : 0.0f;
+  float xin[U], wnew[U];  // the raw input; this lane's next window entry
+  if constexpr (kConv) {
+    static_assert(kMaxConv == 4, "one slot per lane of a quad");
+    const int lead = kMaxConv - K;  // slots with no tap and no kept input
+    const float wc[kMaxConv] = {lead > 0 ? 0.0f : dpp<0x00>(wq, wq),
+                                lead > 1 ? 0.0f : dpp<0x55>(wq, wq),
+                                lead > 2 ? 0.0f : dpp<0xAA>(wq, wq),
+                                dpp<0xFF>(wq, wq)};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float s0 = lead > 0 ? 0.0f : dpp<0x00>(wl[u], wl[u]);
+      const float s1 = lead > 1 ? 0.0f : dpp<0x55>(wl[u], wl[u]);
+      const float s2 = lead > 2 ? 0.0f : dpp<0xAA>(wl[u], wl[u]);
+      float acc = fmaf(wc[0], s0, cb);
+      acc = fmaf(wc[1], s1, acc);
+      acc = fmaf(wc[2], s2, acc);
+      acc = fmaf(wc[3], x[u], acc);
+      xin[u] = x[u];
+      x[u] = silu_f(acc);
+      // the window moves by one: kept input q becomes slot kMaxConv - H + q
+      // of (window, x)
+      const int sl = kMaxConv - H + q;
+      wnew[u] = sl == 1 ? s1 : (sl == 2 ? s2 : xin[u]);
+    }
+  }
   float part[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -154,6 +209,9 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
   for (int u = 0; u < U; ++u) {
     if (!ok[u]) continue;
     store_state4<kVec>(p.state + ch[u] * kStates + 4 * q, h[u]);
+    if constexpr (kConv) {
+      if (q < H) static_cast<T *>(p.conv_state)[ch[u] * H + q] = from_f32<T>(wnew[u]);
+    }
     if (q == 0) {
       float yv = fmaf(Dd, x[u], part[u]);
       if (p.z) yv *= silu_f(zz[u]);
@@ -166,7 +224,10 @@ template <typename T, bool kVec>
 hipError_t launch_step_t(const StepArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.dim + kStepChannels - 1) / kStepChannels),
                   static_cast<unsigned>((a.batch + kStepBatch - 1) / kStepBatch));
-  hipLaunchKernelGGL((step_kernel<T, kVec>), grid, dim3(kStepThreads), 0, s, a);
+  if (a.d_conv > 0)
+    hipLaunchKernelGGL((step_kernel<T, kVec, true>), grid, dim3(kStepThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((step_kernel<T, kVec, false>), grid, dim3(kStepThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -275,6 +275,30 @@ def make_decode_inputs(cfg: DecodeConfig, device="cpu", with_h0=False,
     return out
 
 
+def make_conv_decode_inputs(cfg: DecodeConfig, device="cpu", d_conv: int = 4,
+                            with_bias: bool = True, with_h0: bool = False,
+                            with_window: bool = False, **over) -> dict:
+    """A decode sequence for the step with the fused conv prologue: the
+    decode workload's tensors, ``u`` read as the pre-convolution input x,
+    plus ``conv_w`` (dim, d_conv) and ``conv_b`` (dim,) drawn like the conv
+    scan's, and ``conv_state0`` (batch, dim, d_conv - 1) in the activation
+    dtype: N(0,1) (a sequence already under way) with ``with_window``, else
+    zeros (a fresh one)."""
+    out = make_decode_inputs(cfg, device, with_h0=with_h0, **over)
+    if over:
+        cfg = replace(cfg, **over)
+    b, d, s = cfg.batch, cfg.dim, cfg.seed
+    lim = 1.0 / math.sqrt(d_conv)
+    out["conv_w"] = _uniform((d, d_conv), -lim, lim, device, s, 9)
+    out["conv_b"] = (_uniform((d,), -lim, lim, device, s, 10)
+                     if with_bias else None)
+    H = d_conv - 1
+    out["conv_state0"] = (_normal((b, d, H), device, s, 11) if with_window
+                          else torch.zeros((b, d, H), device=device)
+                          ).to(torch_dtype(cfg.dtype))
+    return out
+
+
 def step_slice(inputs: dict, t: int) -> dict:
     """Contiguous per-step tensors (x, delta, z: (batch, dim); B, C:
     (batch, N)) for token ``t`` of a decode sequence."""
@@ -317,6 +341,16 @@ def decode_step_bytes(cfg: DecodeConfig) -> int:
     by += 2 * cfg.batch * cfg.dstate * elem
     by += cfg.dim * cfg.dstate * 4 + 2 * cfg.dim * 4
     return by
+
+
+def conv_decode_step_bytes(cfg: DecodeConfig, d_conv: int = 4) -> int:
+    """Per decode step with the conv prologue: the plain step's bytes plus
+    the kept window (d_conv - 1 inputs per channel, activation dtype) read
+    and written, and the taps and conv bias (fp32) read."""
+    elem = 2 if cfg.dtype == "bf16" else 4
+    bd = cfg.batch * cfg.dim
+    return (decode_step_bytes(cfg) + 2 * bd * (d_conv - 1) * elem
+            + cfg.dim * (d_conv + 1) * 4)
 
 
 def backward_bytes(cfg: ScanConfig) -> int:

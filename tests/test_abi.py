@@ -135,6 +135,8 @@ INVALID_STEP_CASES = [
     ("misaligned state", dict(state=FAKE + 2), 1),
     ("y aliases state", dict(y=FAKE + 8), 1),
     ("state overlaps x", dict(x=FAKE + 16), 1),
+    ("batch beyond the grid", dict(batch=131071), 2),
+    ("batch*dim beyond 2^32", dict(batch=2, dim=1 << 31), 2),
 ]
 
 
@@ -142,6 +144,43 @@ INVALID_STEP_CASES = [
                          ids=[c[0] for c in INVALID_STEP_CASES])
 def test_step_rejects_invalid_arguments(lib, name, kw, status):
     assert _step(lib, **kw) == status
+    assert lib.ssm_last_error().decode()
+
+
+def _conv_step(lib, **kw):
+    a = dict(state=FAKE, cs=FAKE + 0x70000000, x=FAKE + 0x10000000,
+             w=FAKE + 0x78000000, cb=None, K=4, delta=FAKE + 0x20000000,
+             A=FAKE + 0x30000000, B=FAKE + 0x40000000, C=FAKE + 0x50000000,
+             D=None, z=None, bias=None, flags=1, y=FAKE + 0x60000000,
+             batch=2, dim=8, dstate=16, dtype=ssm.SSM_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return lib.ssm_conv_state_update(a["state"], a["cs"], a["x"], a["w"],
+                                     a["cb"], a["K"], a["delta"], a["A"],
+                                     a["B"], a["C"], a["D"], a["z"], a["bias"],
+                                     a["flags"], a["y"], a["batch"], a["dim"],
+                                     a["dstate"], a["dtype"], a["stream"])
+
+
+INVALID_CONV_STEP_CASES = [
+    ("null conv_w", dict(w=None), 1),
+    ("d_conv 0", dict(K=0), 1),
+    ("d_conv 5", dict(K=5), 2),
+    ("null conv_state", dict(cs=None), 1),
+    ("misaligned conv_state", dict(cs=FAKE + 0x70000001), 1),
+    ("misaligned conv_w", dict(w=FAKE + 0x78000002), 1),
+    ("conv_state overlaps state", dict(cs=FAKE + 64), 1),
+    ("conv_state overlaps y", dict(cs=FAKE + 0x60000000 + 4), 1),
+    ("conv_state overlaps x", dict(cs=FAKE + 0x10000000 + 2), 1),
+    ("state overlaps conv_w", dict(w=FAKE + 32), 1),
+    ("null state", dict(state=None), 1),
+    ("unknown flag", dict(flags=4), 1),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_CONV_STEP_CASES,
+                         ids=[c[0] for c in INVALID_CONV_STEP_CASES])
+def test_conv_step_rejects_invalid_arguments(lib, name, kw, status):
+    assert _conv_step(lib, **kw) == status, ssm.ssm_last_error()
     assert lib.ssm_last_error().decode()
 
 
