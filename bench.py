@@ -15,7 +15,8 @@ on its stream over the timed region) to the ALU ceiling that bounds it.
 ``cpu_baseline`` is the fp64 oracle on the same inputs on the host cores.
 
 Options beyond the contract: --no-cpu-baseline, --no-extra (skip the
-long-context and decode figures), --only-scan (nothing but the timed steps;
+other workloads: the 130M-shaped layer, long context, conv prologue, ZOH,
+backward, SSD and decode figures), --only-scan (nothing but the timed steps;
 for profiler runs), --only-ssd (only the Mamba-2 SSD figure, --steps calls;
 for profiler runs), --only-decode (the decode workload, --steps passes of
 its 64 steps), --only-bwd (the 2.8B-layer backward, --steps calls),
@@ -242,6 +243,43 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     """Long-context scan (chunked) and the decode step, timed with events.
     Reported for information beside the main line."""
     out = {}
+    # the 130M-shaped layer; three input sets rotated (305 MB, beyond the
+    # last-level cache)
+    scfg = syn.MAMBA_130M
+    log("130M-layer workload %s" % scfg.name)
+    ssets = []
+    for i in range(3):
+        s = syn.make_scan_inputs(scfg, dev, seed=scfg.seed + 100 * i)
+        s["y"] = torch.empty_like(s["u"])
+        s["h_final"] = torch.empty(scfg.batch, scfg.dim, 16, device=dev)
+        ssets.append(s)
+
+    def srun(i):
+        s = ssets[i % 3]
+        ssm.ssm_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"],
+                         s["z"], s["delta_bias"], True, None, y=s["y"],
+                         h_final=s["h_final"], stream=stream)
+    for i in range(6):
+        srun(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 60
+    e0.record(stream)
+    for i in range(reps):
+        srun(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb = syn.algorithmic_bytes(scfg)
+    out[scfg.name] = {
+        "ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+        "elements_per_s": round(scfg.elements / (ms * 1e-3)),
+        "chunk_len": ssm.ssm_scan_plan(scfg.batch, scfg.dim, 16, scfg.seqlen),
+        "algorithmic_bytes": nb}
+    del ssets
+    torch.cuda.empty_cache()
+
     cfg = syn.LONG_1M
     log("long-context workload %s" % cfg.name)
     inp = syn.make_scan_inputs(cfg, dev)
@@ -606,6 +644,30 @@ def summarize_profiles(d):
             _kernel_key(r["Name"])[:90], r["Calls"],
             float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6))
+    # The same scan instance also runs the 130M-shaped layer among the
+    # extras: per-dispatch durations from the trace, split by launch grid
+    # (the 2.8B layer: ceil(D/4) workgroups of 256 threads by batch).
+    import synthetic as syn
+    c2 = syn.MAMBA_2P8B
+    grid_c2 = ((c2.dim + 3) // 4 * 256, c2.batch, 1)
+    by_grid = {}
+    for f in _csvs(os.path.join(d, "trace"), "_kernel_trace.csv"):
+        for r in csv.DictReader(open(f)):
+            if _kernel_key(r["Kernel_Name"]) != SCAN_KERNEL:
+                continue
+            g = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]),
+                 int(r["Grid_Size_Z"]))
+            by_grid.setdefault(g, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if by_grid:
+        lines.append("# %s per launch grid (threads), from the kernel trace:"
+                     % SCAN_KERNEL)
+        for g in sorted(by_grid, key=lambda g: -len(by_grid[g])):
+            v = by_grid[g]
+            lines.append("grid %dx%dx%d%s | %d | %.2f | %.2f | %.2f | %.3f" % (
+                g + (" (Mamba-2.8B layer)" if g == grid_c2 else "",
+                     len(v), statistics.mean(v), min(v), max(v),
+                     sum(v) / 1e3)))
     with open(os.path.join(prof, "scan_kernel_mamba2p8b_kernel_stats.txt"),
               "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -631,7 +693,6 @@ def summarize_profiles(d):
     write_scale = COPY_BYTES / 1024 / write[COPY_KERNEL]
     fb = fetch[SCAN_KERNEL] * fetch_scale * 1024
     wb = write[SCAN_KERNEL] * write_scale * 1024
-    import synthetic as syn
     alg = syn.algorithmic_bytes(syn.MAMBA_2P8B)
     out = {"kernel": SCAN_KERNEL, "workload": syn.MAMBA_2P8B.name,
            "kernel_source_sha256_16": kernel_source_hash(),
