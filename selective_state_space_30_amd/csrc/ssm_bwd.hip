@@ -357,10 +357,39 @@ __global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kerne
   const int64_t gstride = kStates * p.L;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if ((p.L & 3) == 0 && t < p.L) {
-    const float *q = part + t;
-#pragma unroll 4
-    for (int64_t gi = slice; gi < p.groups; gi += kReduceWaves) {
-      const float4 v = *reinterpret_cast<const float4 *>(q + gi * gstride);
+    // This wave's groups slice, slice + 4, ... summed in order through a
+    // ring of kRing loads in flight: group g's value is added, then group
+    // g + kRing is requested into its register (the order of additions is
+    // that of one group at a time).  The scheduling barriers keep each load
+    // right after the add that frees its register; left to itself the
+    // scheduler groups the loads and waits for all of them at once.
+    constexpr int kRing = 8;
+    const int64_t step = kReduceWaves * gstride;
+    const int64_t ng = (p.groups - slice + kReduceWaves - 1) / kReduceWaves;
+    const float *q = part + t + slice * gstride;
+    int64_t g = 0;
+    if (ng >= kRing) {
+      float4 v[kRing];
+#pragma unroll
+      for (int k = 0; k < kRing; ++k)
+        v[k] = *reinterpret_cast<const float4 *>(q + k * step);
+      for (; g + 2 * kRing <= ng; g += kRing) {
+        const float *qn = q + (g + kRing) * step;
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+          acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+          v[k] = *reinterpret_cast<const float4 *>(qn + k * step);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kRing; ++k) {
+        acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+      }
+      g += kRing;
+    }
+    for (; g < ng; ++g) {
+      const float4 v = *reinterpret_cast<const float4 *>(q + g * step);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
   } else if (t < p.L) {
