@@ -590,12 +590,38 @@ def cpu_baseline(inp, cfg, nbytes, log):
                          host["C"], host["D"], host["z"], host["delta_bias"],
                          True, False, None, threads=threads)
     sec = time.perf_counter() - t0
+    # one thread on the first 256 channels of each batch entry (a bounded
+    # sample of the same workload)
+    nd = min(256, cfg.dim)
+    part = {k: (v[:, :nd] if k in ("u", "delta", "z") else
+                v[:nd] if k in ("A", "D", "delta_bias") else v)
+            for k, v in host.items()}
+    t1 = time.perf_counter()
+    oracle.scan_threaded(part["u"], part["delta"], part["A"], part["B"],
+                         part["C"], part["D"], part["z"], part["delta_bias"],
+                         True, False, None, threads=1)
+    sec1 = time.perf_counter() - t1
     return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": "the whole workload (%d x %d channels x %d tokens), "
                       "fp64, %.2f s wall" % (cfg.batch, cfg.dim, cfg.seqlen,
                                              sec),
-            "elements_per_s": round(cfg.elements / sec)}
+            "elements_per_s": round(cfg.elements / sec),
+            "one_thread_elements_per_s": round(cfg.batch * nd * cfg.seqlen / sec1),
+            "one_thread_sample": "%d x %d channels x %d tokens, %.2f s" % (
+                cfg.batch, nd, cfg.seqlen, sec1),
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # bf16 activations, vector loads, softplus on, no conv prologue, Euler input,
