@@ -188,3 +188,86 @@ def test_conv_decode_degenerate_shapes(shape):
         check(y[:, :, t], y_ref, 2e-2, "y step %d" % t)
     check(state, ref_state, 2e-2, "state")
     assert torch.equal(conv_state.cpu(), expected_window(inp))
+
+
+def _offset_copy(t, offset):
+    """t's values in a buffer that starts `offset` elements into a larger
+    allocation: the data pointer loses its 8- and 16-byte alignment."""
+    flat = torch.empty(t.numel() + offset, dtype=t.dtype, device=DEV)
+    v = flat[offset:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_decode_unaligned_inputs(dtype):
+    """B, the state, the taps and the window without 16-byte alignment (the
+    element-wise instance of the kernel): every step against the oracle,
+    with an odd batch and a ragged channel count."""
+    cfg = syn.DecodeConfig("conv_unaligned", 5, 70, 16, 6, dtype=dtype, seed=61)
+    inp = syn.make_conv_decode_inputs(cfg, "cpu", d_conv=4, with_h0=True,
+                                      with_window=True)
+    d = to_dev(inp)
+    state = _offset_copy(d["h0"], 1)
+    conv_state = _offset_copy(d["conv_state0"], 1)
+    conv_w = _offset_copy(d["conv_w"], 1)
+    u = oracle_conv_input(inp)
+    ref_state = inp["h0"].double().numpy().copy()
+    for t in range(cfg.steps):
+        s = syn.step_slice(d, t)
+        y = ssm.ssm_conv_state_update(
+            state, conv_state, s["x"], conv_w, s["delta"], d["A"],
+            _offset_copy(s["B"], 1), s["C"], d["D"], s["z"], d["delta_bias"],
+            True, conv_b=d["conv_b"])
+        sh = syn.step_slice(inp, t)
+        y_ref = oracle.step(ref_state, u[:, :, t], sh["delta"], inp["A"],
+                            sh["B"], sh["C"], inp["D"], sh["z"],
+                            inp["delta_bias"], True, False)
+        torch.cuda.synchronize()
+        check(y, y_ref, TOL[dtype], "y step %d" % t)
+    check(state, ref_state, TOL[dtype], "state")
+    assert torch.equal(conv_state.cpu(), expected_window(inp))
+
+
+def test_conv_decode_steps_replay_in_a_hip_graph():
+    """Six conv decode steps captured into a graph (one kernel per step, no
+    memsets), replayed three times with eager work between the replays;
+    every replay gives the eager run's state, window and outputs bit for
+    bit."""
+    cfg = syn.DecodeConfig("conv_graph", 4, 96, 16, 6, dtype="bf16", seed=57)
+    inp = syn.make_conv_decode_inputs(cfg, DEV, d_conv=4, with_h0=True,
+                                      with_window=True)
+    steps = [syn.step_slice(inp, t) for t in range(cfg.steps)]
+    side = torch.cuda.Stream()
+    state = inp["h0"].clone()
+    window = inp["conv_state0"].clone()
+    ys = [torch.empty(cfg.batch, cfg.dim, dtype=torch.bfloat16, device=DEV)
+          for _ in steps]
+
+    def enqueue():
+        for t, s in enumerate(steps):
+            ssm.ssm_conv_state_update(
+                state, window, s["x"], inp["conv_w"], s["delta"], inp["A"],
+                s["B"], s["C"], inp["D"], s["z"], inp["delta_bias"], True,
+                conv_b=inp["conv_b"], y=ys[t], stream=side)
+    torch.cuda.synchronize()
+    enqueue()
+    side.synchronize()
+    ref_state, ref_window = state.clone(), window.clone()
+    ref_ys = [y.clone() for y in ys]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        enqueue()
+    for rep in range(3):
+        state.copy_(inp["h0"])
+        window.copy_(inp["conv_state0"])
+        for y in ys:
+            y.fill_(rep + 1)
+        _ = (state * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state, ref_state), rep
+        assert torch.equal(window, ref_window), rep
+        for t, (y, r) in enumerate(zip(ys, ref_ys)):
+            assert torch.equal(y, r), (rep, t)
