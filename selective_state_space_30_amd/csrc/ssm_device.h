@@ -350,10 +350,11 @@ struct TileRun {
 
 // Float offset, inside one LDS tile buffer, of the run that lane `lane` of
 // wave `wave` stages: state (wave >> 1) of the phase's pair, matrix B (even
-// waves) or C (odd), run `lane`, padded stride K + 4.
+// waves) or C (odd), run `lane`, padded stride KP.
 static_assert(kWavesPerGroup == 2 * kPhaseStates, "one staging row per wave");
+template <int KP>
 __device__ __forceinline__ int staging_offset(int wave, int lane) {
-  return (wave * kWaveLanes + lane) * (kTokensPerLane + 4);
+  return (wave * kWaveLanes + lane) * KP;
 }
 
 }  // namespace dev

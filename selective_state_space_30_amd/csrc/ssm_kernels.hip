@@ -56,8 +56,11 @@ using namespace dev;
 template <typename T, bool kVec, bool kConv, bool kZoh, bool kCkpt>
 constexpr bool kPrefetch = sizeof(T) == 4 && kVec && !kConv && !kZoh && !kCkpt;
 
+// K: tokens per lane.  Full blocks use kTokensPerLane; the last, partial
+// block of a chunk uses the fewest of 4, 8, 16 that cover it, so its state
+// loop costs about its share of a block rather than a whole one.
 template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kConv,
-          bool kZoh, bool kCkpt>
+          bool kZoh, bool kCkpt, int K = kTokensPerLane>
 __device__ __forceinline__ void scan_block(
     const ScanArgs &p, int wave, int lane, int64_t t0, int64_t ct1,
     const T *__restrict__ Bb, const T *__restrict__ Cb,
@@ -67,8 +70,11 @@ __device__ __forceinline__ void scan_block(
     float (&hc)[kStates], float &sdt_total, const float (&wc)[kMaxConv], float cb,
     float (&xc)[kMaxConv - 1], float (&upf)[kTokensPerLane],
     float (&dpf)[kTokensPerLane], bool use_pf, int64_t pf_t0) {
-  constexpr int K = kTokensPerLane;
-  constexpr int KP = K + 4;  // padded LDS stride of one lane's run
+  static_assert(!kFull || K == kTokensPerLane, "full blocks: 16 tokens a lane");
+  static_assert(K == 4 || K == 8 || K == 16, "runs of 4, 8 or 16 tokens");
+  // padded LDS stride of one lane's run: a lane's 16-byte reads of 8
+  // consecutive runs fall on 32 different banks
+  constexpr int KP = K == 4 ? 12 : K + 4;
   const int64_t tend = kFull ? t0 + kBlockTokens : ct1;
   const int64_t tl = t0 + static_cast<int64_t>(lane) * K;
   constexpr int kPhases = kStates / 2;
@@ -80,7 +86,7 @@ __device__ __forceinline__ void scan_block(
   const int st = wave >> 1, mat = wave & 1;
   const T *src = mat ? Cb : Bb;
   const int64_t tq = tl;
-  const int toff = staging_offset(wave, lane);
+  const int toff = staging_offset<KP>(wave, lane);
   TileRun<T, K, kVec, kFull> run;
   run.load(src + st * p.L, t0, tq, tend);
 
@@ -308,12 +314,23 @@ void scan_kernel(ScanArgs p) {
 #pragma unroll
     for (int n = 0; n < kStates; ++n) ck[(t0 / kBlockTokens) * kStates + n] = hc[n];
   }
-  if (t0 < ct1)
-    // the last, partial block: branch-free scalar loads (rare; keeps the
-    // register budget of the full-block loop)
-    scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt>(
-        p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, Ach,
-        sT, hc, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+  if (t0 < ct1) {
+    // the last, partial block: branch-free scalar loads (keeps the register
+    // budget of the full-block loop), as few tokens per lane as cover it
+    const int64_t rem = ct1 - t0;
+    if (rem <= 4 * kWaveLanes)
+      scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt, 4>(
+          p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
+          Ach, sT, hc, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+    else if (rem <= 8 * kWaveLanes)
+      scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt, 8>(
+          p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
+          Ach, sT, hc, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+    else
+      scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt>(
+          p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
+          Ach, sT, hc, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+  }
 
   if (!ch_ok) return;
   if (p.n_chunks == 1) {
