@@ -68,16 +68,19 @@ __device__ __forceinline__ int region_index(int wave, int mat, int j, int lane) 
 // After every wave has written its region for state n: thread tid sums the
 // channels' contributions (in channel order) for 4 consecutive tokens of one
 // matrix and writes them to the workgroup's partial-sum row (a 16-byte
-// store when kVec; the partial block through the buffer view).
-template <bool kVec, bool kFull>
+// store when kVec; the partial block through the buffer view).  Runs of K
+// tokens (fewer than 16 in a short partial block): threads whose 4 tokens
+// lie past the run have nothing to write.
+template <bool kVec, bool kFull, int K = kTokensPerLane>
 __device__ __forceinline__ void flush_state(const float *sR, int tid, float *pB_row,
                                             float *pC_row, int64_t t0, int64_t tend) {
   constexpr int kPer = 2 * kTokensPerLane * kWaveLanes / kBwdThreads;  // 4
   constexpr int kParts = kTokensPerLane / kPer;                        // per run
   const int mat = tid / (kBwdThreads / 2);  // first half: dB, second: dC (wave-uniform)
   const int r = tid % (kBwdThreads / 2);
-  const int run = r / kParts;               // the lane run (16 tokens) ...
+  const int run = r / kParts;               // the lane run ...
   const int j0 = (r % kParts) * kPer;       // ... and which part of it
+  if (K < kTokensPerLane && j0 >= K) return;
   float v[kPer];
 #pragma unroll
   for (int jj = 0; jj < kPer; ++jj) {
@@ -87,7 +90,7 @@ __device__ __forceinline__ void flush_state(const float *sR, int tid, float *pB_
     v[jj] = acc;
   }
   float *row = mat ? pC_row : pB_row;
-  store_run<float, kPer, kVec, kFull>(row, t0, t0 + run * kTokensPerLane + j0, tend, v);
+  store_run<float, kPer, kVec, kFull>(row, t0, t0 + run * K + j0, tend, v);
 }
 
 // Per-state values of one channel kept one state per lane (lane n holds
@@ -101,14 +104,18 @@ __device__ __forceinline__ float set_state(float v, int lane, int n, float x) {
 // the block (checkpoint; lane n = state n); muv: dL/dh flowing in from the
 // right of the block (replaced by what flows out of its first token); dAv:
 // running dA sums of the channel (lane n = state n, already times 1/ln2).
-template <typename T, bool kVec, bool kFull, bool kSoftplus>
+// K: tokens per lane.  Full blocks use kTokensPerLane; the partial last
+// block uses the fewest of 4, 8, 16 that cover it, so its loops cost about
+// its share of a block.
+template <typename T, bool kVec, bool kFull, bool kSoftplus, int K = kTokensPerLane>
 __device__ __forceinline__ void bwd_block(
     const BwdArgs &p, int wave, int lane, int64_t t0, int64_t tend, int64_t b,
     int64_t bd, int64_t g, const T *__restrict__ Bb, const T *__restrict__ Cb,
     bool ch_ok, float bias, float Dd, float Av, float hfv, float &muv, float &dAv,
     float &dDl, float &dbl, float *sT, float *sR, int tid) {
-  constexpr int K = kTokensPerLane;
-  constexpr int KP = K + 4;
+  static_assert(!kFull || K == kTokensPerLane, "full blocks: 16 tokens a lane");
+  static_assert(K == 4 || K == 8 || K == 16, "runs of 4, 8 or 16 tokens");
+  constexpr int KP = K == 4 ? 12 : K + 4;  // a multiple of 4 floats: 16-byte runs
   const int64_t tl = t0 + static_cast<int64_t>(lane) * K;
   const T *urow = static_cast<const T *>(p.u) + bd * p.L;
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
@@ -116,16 +123,19 @@ __device__ __forceinline__ void bwd_block(
   const T *gyrow = static_cast<const T *>(p.dy) + bd * p.L;
 
   // staging role of this wave: matrix mat (B or C) of the next state,
-  // quarter `qr` of every lane run (4 tokens per lane)
-  constexpr int kQuarterRun = K / 4;
+  // 4-token piece `qr` of every lane run (runs shorter than 16 tokens have
+  // fewer pieces; the waves past them stage nothing)
+  constexpr int kQuarterRun = 4;
+  constexpr int kPieces = K / kQuarterRun;
   const int mat = wave & 1, qr = wave >> 1;
+  const bool stager = K == kTokensPerLane || qr < kPieces;
   const T *src = mat ? Cb : Bb;
   const int toff = (mat * kWaveLanes + lane) * KP + qr * kQuarterRun;
   const int64_t tq = tl + qr * kQuarterRun;
   float *pBg = p.pB + (b * p.groups + g) * kStates * p.L;  // this group's partial rows
   float *pCg = p.pC + (b * p.groups + g) * kStates * p.L;
   TileRun<T, kQuarterRun, kVec, kFull> run;
-  run.load(src, t0, tq, tend);  // state 0
+  if (stager) run.load(src, t0, tq, tend);  // state 0
 
   // per token: dt (as dt*log2 e), dt*u, the gated output gradient gc and
   // the sums over states s1 = sum lambda B, s2 = sum lambda a h_prev A
@@ -161,7 +171,7 @@ __device__ __forceinline__ void bwd_block(
 #pragma unroll
     for (int j = 0; j < K; ++j) gc[j] = du[j] = 0.0f;
   }
-  run.store(sT, toff);
+  if (stager) run.store(sT, toff);
   const float sdtl = sdt * kLog2e;
   // One barrier per state: state n reads tile buffer n & 1 and writes
   // region buffer n & 1; before its barrier each wave stores its share of
@@ -172,7 +182,7 @@ __device__ __forceinline__ void bwd_block(
 
 #pragma unroll 1
   for (int n = 0; n < kStates; ++n) {
-    if (n + 1 < kStates) run.load(src + (n + 1) * p.L, t0, tq, tend);
+    if (stager && n + 1 < kStates) run.load(src + (n + 1) * p.L, t0, tq, tend);
     const float *tile = sT + (n & 1) * kBwdTileFloats;
     float *reg = sR + (n & 1) * kRegionFloats;
     float An = state_of(Av, n);
@@ -247,9 +257,9 @@ __device__ __forceinline__ void bwd_block(
     float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
     asm volatile("" : "+s"(dA_sum));
     dAv += lane == n ? dA_sum : 0.0f;
-    if (n + 1 < kStates) run.store(sT + ((n + 1) & 1) * kBwdTileFloats, toff);
+    if (stager && n + 1 < kStates) run.store(sT + ((n + 1) & 1) * kBwdTileFloats, toff);
     __syncthreads();  // state n's contributions and state n+1's tile are in LDS
-    flush_state<kVec, kFull>(reg, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
+    flush_state<kVec, kFull, K>(reg, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
   }
 
   // per-token gradients
@@ -313,11 +323,22 @@ void bwd_kernel(BwdArgs p) {
 
   const float *ck = p.ckpt + bd * p.nblk * kStates;
   const int64_t nfull = p.L / kBlockTokens;
-  if (nfull * kBlockTokens < p.L)  // the partial last block comes first
-    bwd_block<T, false, false, kSoftplus>(p, wave, lane, nfull * kBlockTokens, p.L, b, bd, g,
-                                          Bb, Cb, ch_ok, bias, Dd, Av,
-                                          ck[nfull * kStates + ls], muv, dAv, dDl, dbl, sT,
-                                          sR, tid);
+  const int64_t rem = p.L - nfull * kBlockTokens;
+  if (rem > 0) {  // the partial last block comes first
+    const float hf = ck[nfull * kStates + ls];
+    if (rem <= 4 * kWaveLanes)
+      bwd_block<T, false, false, kSoftplus, 4>(p, wave, lane, nfull * kBlockTokens, p.L, b,
+                                               bd, g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv,
+                                               dAv, dDl, dbl, sT, sR, tid);
+    else if (rem <= 8 * kWaveLanes)
+      bwd_block<T, false, false, kSoftplus, 8>(p, wave, lane, nfull * kBlockTokens, p.L, b,
+                                               bd, g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv,
+                                               dAv, dDl, dbl, sT, sR, tid);
+    else
+      bwd_block<T, false, false, kSoftplus>(p, wave, lane, nfull * kBlockTokens, p.L, b, bd,
+                                            g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv, dAv,
+                                            dDl, dbl, sT, sR, tid);
+  }
 #pragma unroll 1
   for (int64_t k = nfull - 1; k >= 0; --k)
     bwd_block<T, kVec, true, kSoftplus>(p, wave, lane, k * kBlockTokens,
