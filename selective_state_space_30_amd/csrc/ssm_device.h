@@ -290,13 +290,15 @@ __device__ __forceinline__ float lane_broadcast(float v, int lane) {
 // the series dt * (1 + x/2 + x^2/6), x = dt*A, is used instead (truncation
 // below 4e-7 relative there).  A = 0 takes the series (arg = 0) and gives
 // dt, the limit; the infinite inv_a of the other operand is not selected.
+// The direct form is one fused a*(1/A) - 1/A: the exact a/A - 1/A rounded
+// once (a - 1 itself is exact for a in [1/2, 2]).
 __device__ __forceinline__ float zoh_coeff(float arg, float a, float dt,
                                            float inv_a) {
   constexpr float c1 = 0.34657359027997264f;   // ln2 / 2
   constexpr float c2 = 0.080075075008187500f;  // ln2^2 / 6
   const float q = fmaf(arg, fmaf(arg, c2, c1), 1.0f);
   const float series = dt * q;
-  const float direct = (a - 1.0f) * inv_a;
+  const float direct = fmaf(a, inv_a, -inv_a);  // (a - 1) / A, rounded once
   return fabsf(arg) < 0x1p-5f ? series : direct;
 }
 
