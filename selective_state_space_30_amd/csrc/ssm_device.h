@@ -285,19 +285,21 @@ __device__ __forceinline__ float lane_broadcast(float v, int lane) {
 // Exact zero-order-hold input coefficient of one state, (exp(dt*A) - 1) / A
 // ("Mamba & State Space Models - Guide Complet", section 1: B_bar =
 // (exp(dt A) - I) A^-1 B; for a diagonal A, per state).  `arg` = dt*A*log2(e)
-// (the exp2 argument), `a` = exp2(arg), `dt`, `inv_a` = 1/A.  Where |arg| <
-// 2^-5 the difference a - 1 would lose up to ~2^-18 relative accuracy, so
-// the series dt * (1 + x/2 + x^2/6), x = dt*A, is used instead (truncation
-// below 4e-7 relative there).  A = 0 takes the series (arg = 0) and gives
-// dt, the limit; the infinite inv_a of the other operand is not selected.
-// The direct form is one fused a*(1/A) - 1/A: the exact a/A - 1/A rounded
-// once (a - 1 itself is exact for a in [1/2, 2]).
-__device__ __forceinline__ float zoh_coeff(float arg, float a, float dt,
+// (the exp2 argument), `a` = exp2(arg), `dtl` = dt*log2(e), `inv_a` = 1/A.
+// Where |arg| < 2^-5 the difference a - 1 would lose up to ~2^-18 relative
+// accuracy, so the series dt * (1 + x/2 + x^2/6), x = dt*A = arg*ln2, is
+// used instead (truncation below 4e-7 relative there), written in dtl and
+// arg: dtl * (ln2 + arg ln2^2/2 + arg^2 ln2^3/6).  A = 0 takes the series
+// (arg = 0) and gives dt, the limit; the infinite inv_a of the other operand
+// is not selected.  The direct form is one fused a*(1/A) - 1/A: the exact
+// a/A - 1/A rounded once (a - 1 itself is exact for a in [1/2, 2]).
+__device__ __forceinline__ float zoh_coeff(float arg, float a, float dtl,
                                            float inv_a) {
-  constexpr float c1 = 0.34657359027997264f;   // ln2 / 2
-  constexpr float c2 = 0.080075075008187500f;  // ln2^2 / 6
-  const float q = fmaf(arg, fmaf(arg, c2, c1), 1.0f);
-  const float series = dt * q;
+  constexpr float c0 = 0.69314718055994531f;   // ln2
+  constexpr float c1 = 0.24022650695910071f;   // ln2^2 / 2
+  constexpr float c2 = 0.055504108664821580f;  // ln2^3 / 6
+  const float q = fmaf(arg, fmaf(arg, c2, c1), c0);
+  const float series = dtl * q;
   const float direct = fmaf(a, inv_a, -inv_a);  // (a - 1) / A, rounded once
   return fabsf(arg) < 0x1p-5f ? series : direct;
 }

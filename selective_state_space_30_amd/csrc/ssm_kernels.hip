@@ -180,7 +180,7 @@ __device__ __forceinline__ void scan_block(
         for (int j = 0; j < K; ++j) {
           const float arg = dtl[j] * An;
           a[j] = fast_exp2(arg);
-          bb[j] = zoh_coeff(arg, a[j], dtl[j] * kLn2, inv_a) * (du[j] * pb[j]);
+          bb[j] = zoh_coeff(arg, a[j], dtl[j], inv_a) * (du[j] * pb[j]);
         }
       } else {
 #pragma unroll

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
       const float e = fast_exp2(arg);
       float inp = dx * b4[u][i];
       if (p.zoh)  // exact ZOH: coefficient (e - 1)/A in place of dt
-        inp = zoh_coeff(arg, e, dt, 1.0f / a4[i]) * (x[u] * b4[u][i]);
+        inp = zoh_coeff(arg, e, dt * kLog2e, 1.0f / a4[i]) * (x[u] * b4[u][i]);
       h[u][i] = fmaf(e, h[u][i], inp);
       acc = fmaf(c4[u][i], h[u][i], acc);
     }
