@@ -219,6 +219,17 @@ def test_mamba2p8b_workload_sampled():
     full_workload_check(syn.MAMBA_2P8B, 32, 2e-2)
 
 
+@pytest.mark.parametrize("L", [4104, 4600, 4095, 100],
+                         ids=lambda L: "l%d" % L)
+def test_mamba2p8b_shape_ragged_lengths_sampled(L):
+    """The 2.8B layer's width with lengths that end in a partial block of
+    8, 504 and 1023 tokens (4 and 8 tokens per lane, and 16 with rows that
+    are not 16-byte aligned: the element-wise instance) and a sequence
+    shorter than one block."""
+    from dataclasses import replace
+    full_workload_check(replace(syn.MAMBA_2P8B, seqlen=L), 24, 2e-2)
+
+
 def test_long_context_workload_sampled():
     cfg = syn.LONG_1M
     assert ssm.ssm_scan_plan(cfg.batch, cfg.dim, 16, cfg.seqlen) < cfg.seqlen
