@@ -12,6 +12,8 @@ bf16 activations 2e-2.  The summed gradients (dA, dB, dC, dD, dbias) add up
 to batch*L (dA, dD, dbias) or dim (dB, dC) fp32 terms, whose rounding stays
 far below the fp32 bar at these sizes.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -126,8 +128,13 @@ def _sampled_channels(cfg, r, k=8):
                    for _ in range(k)})
 
 
-@pytest.mark.parametrize("cfg", [syn.MAMBA_130M, syn.MAMBA_2P8B],
-                         ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [
+    syn.MAMBA_130M, syn.MAMBA_2P8B,
+    # the 2.8B layer's width with partial last blocks of 8 and 404 tokens
+    # (4 and 8 tokens per lane)
+    replace(syn.MAMBA_2P8B, name="mamba2p8b_l4104", seqlen=4104),
+    replace(syn.MAMBA_2P8B, name="mamba2p8b_l4500", seqlen=4500)],
+    ids=lambda c: c.name)
 def test_bwd_layer_workload_sampled(cfg):
     inp = syn.make_scan_inputs(cfg, DEV, with_h0=True)
     g = torch.Generator(device=DEV).manual_seed(cfg.seed + 5)
@@ -169,11 +176,13 @@ def test_bwd_layer_workload_sampled(cfg):
     assert all(torch.isfinite(v.float()).all() for v in got.values())
 
 
-def test_bwd_channel_sums_by_homogeneity():
+@pytest.mark.parametrize("L", [2048, 2100], ids=lambda L: "l%d" % L)
+def test_bwd_channel_sums_by_homogeneity(L):
     """dB and dC at a layer's size: y is degree-one homogeneous in (B, h0)
     apart from the D skip, and in C when no final-state gradient flows, so
-    <dB, B> + <dh0, h0> and <dC, C> equal sum(dy * (y - skip))."""
-    cfg = syn.MAMBA_130M
+    <dB, B> + <dh0, h0> and <dC, C> equal sum(dy * (y - skip)).  L = 2100
+    ends in a partial block of 52 tokens (4 tokens per lane)."""
+    cfg = replace(syn.MAMBA_130M, seqlen=L)
     inp = syn.make_scan_inputs(cfg, DEV, with_h0=True)
     g = torch.Generator(device=DEV).manual_seed(cfg.seed + 6)
     inp["dy"] = torch.randn(cfg.batch, cfg.dim, cfg.seqlen, generator=g,
