@@ -251,13 +251,18 @@ def step(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
 
 
 def scan_channels(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                  delta_softplus=True, zoh_b=False, h0=None, channels=None):
+                  delta_softplus=True, zoh_b=False, h0=None, channels=None,
+                  threads=1):
     """Scan only the listed ``(b, d)`` channels (the oracle is independent
     per channel).  Inputs are full-size arrays or tensors; only the selected
-    rows are widened to fp64.  Returns ``(y[k, L], h_final[k, N])`` in the
-    order of ``channels``."""
-    ys, hs = [], []
-    for b, d in channels:
+    rows are widened to fp64.  ``threads`` > 1 runs the channels on that
+    many Python threads (ctypes releases the GIL); the arithmetic per
+    channel is the same.  Returns ``(y[k, L], h_final[k, N])`` in the order
+    of ``channels``."""
+    channels = list(channels)
+
+    def one(bd):
+        b, d = bd
         sl = (slice(b, b + 1), slice(d, d + 1))
         y, hf = scan(u[sl], delta[sl], A[d:d + 1], B[b:b + 1], C[b:b + 1],
                      None if D is None else D[d:d + 1],
@@ -265,9 +270,14 @@ def scan_channels(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                      None if delta_bias is None else delta_bias[d:d + 1],
                      delta_softplus, zoh_b,
                      None if h0 is None else h0[sl])
-        ys.append(y[0, 0])
-        hs.append(hf[0, 0])
-    return np.stack(ys), np.stack(hs)
+        return y[0, 0], hf[0, 0]
+
+    if threads > 1 and len(channels) > 1:
+        with ThreadPoolExecutor(max_workers=int(threads)) as ex:
+            res = list(ex.map(one, channels))
+    else:
+        res = [one(c) for c in channels]
+    return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])
 
 
 def scan_threaded(u, delta, A, B, C, D=None, z=None, delta_bias=None,
