@@ -26,10 +26,15 @@ Names follow the C ABI:
   the backward (which then skips its own checkpoint pass).
 * :func:`ssm_scan_plan`, :func:`ssm_scan_workspace_size`,
   :func:`ssm_last_error`, :func:`ssm_abi_version`.
+* :func:`ssm_roofline_hbm`, :func:`ssm_roofline_valu` -- microbenchmarks of
+  the HBM and VALU-issue ceilings (``include/ssm_roofline.h``), used by the
+  benchmark; not part of the method.
 """
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 import threading
 
@@ -49,7 +54,12 @@ EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
            "ssm_scan_fwd", "ssm_conv_scan_fwd", "ssm_state_update",
            "ssm_conv_state_update",
            "ssm_scan_bwd_workspace_size", "ssm_scan_fwd_save", "ssm_scan_bwd",
-           "ssm_ssd_workspace_size", "ssm_ssd_fwd", "ssm_last_error")
+           "ssm_ssd_workspace_size", "ssm_ssd_fwd", "ssm_last_error",
+           "ssm_roofline_hbm", "ssm_roofline_valu")
+SSM_ROOFLINE_HBM_QUANTUM = 16384
+SSM_ROOFLINE_VALU_QUANTUM = 256
+ROOFLINE_HBM_KINDS = {"copy": 0, "rmw": 1, "read": 2}
+ROOFLINE_VALU_KINDS = {"exp": 0, "fma": 1, "mixed": 2}
 
 _lib = None
 _lock = threading.Lock()
@@ -115,6 +125,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.ssm_ssd_fwd.argtypes = ([P] * 8 + [U] + [P] * 3 +
                                     [I64] * 6 + [I, P, ctypes.c_size_t, P])
         lib.ssm_ssd_fwd.restype = I
+        lib.ssm_roofline_hbm.argtypes = [I, P, P, ctypes.c_size_t, I, P]
+        lib.ssm_roofline_hbm.restype = I
+        lib.ssm_roofline_valu.argtypes = [I, P, I64, I, P]
+        lib.ssm_roofline_valu.restype = I
         lib.ssm_last_error.argtypes = []
         lib.ssm_last_error.restype = ctypes.c_char_p
         if path is None:
@@ -168,6 +182,24 @@ def _stream_handle(device, stream):
     return stream.cuda_stream
 
 
+def _on_stream(fn):
+    """Runs the wrapper with ``stream`` (when given) as torch's current
+    stream, so that the outputs and the workspace allocated inside belong to
+    the stream the kernels run on: the caching allocator then cannot hand a
+    freed workspace to work on another stream while these kernels still use
+    it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def ssm_scan_plan(batch, dim, dstate, seqlen, requested_chunk=0) -> int:
     out = ctypes.c_int64(0)
     _check(load_library().ssm_scan_plan(batch, dim, dstate, seqlen,
@@ -187,6 +219,7 @@ def _flags(delta_softplus, zoh_b):
             (SSM_FLAG_ZOH_B if zoh_b else 0))
 
 
+@_on_stream
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                  delta_softplus=True, h0=None, return_final_state=True,
                  chunk_len=0, y=None, h_final=None, workspace=None,
@@ -237,6 +270,7 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return y, h_final
 
 
+@_on_stream
 def ssm_conv_scan_fwd(x, conv_w, delta, A, B, C, D=None, z=None,
                       delta_bias=None, delta_softplus=True, h0=None,
                       conv_b=None, return_final_state=True, chunk_len=0,
@@ -288,6 +322,7 @@ def ssm_conv_scan_fwd(x, conv_w, delta, A, B, C, D=None, z=None,
     return y, h_final
 
 
+@_on_stream
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
                      delta_bias=None, delta_softplus=True, y=None,
                      stream=None, zoh_b=False):
@@ -319,6 +354,7 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
     return y
 
 
+@_on_stream
 def ssm_conv_state_update(state, conv_state, x, conv_w, delta, A, B, C,
                           D=None, z=None, delta_bias=None, delta_softplus=True,
                           conv_b=None, y=None, stream=None, zoh_b=False):
@@ -357,6 +393,7 @@ def ssm_conv_state_update(state, conv_state, x, conv_w, delta, A, B, C,
     return y
 
 
+@_on_stream
 def bind_state_update(state, x, delta, A, B, C, D=None, z=None,
                       delta_bias=None, delta_softplus=True, y=None,
                       stream=None, zoh_b=False):
@@ -403,6 +440,7 @@ def ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen,
     return out.value
 
 
+@_on_stream
 def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                       delta_softplus=True, h0=None, return_final_state=True,
                       y=None, h_final=None, workspace=None, stream=None):
@@ -447,6 +485,7 @@ def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return y, h_final, workspace
 
 
+@_on_stream
 def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                  delta_softplus=True, h0=None, dy=None, dh_final=None,
                  want_dz=True, want_dh0=True, out=None, workspace=None,
@@ -515,6 +554,7 @@ def ssm_ssd_workspace_size(batch, ngroups, dstate, seqlen) -> int:
     return out.value
 
 
+@_on_stream
 def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None,
                 dt_softplus=True, h0=None, return_final_state=True, y=None,
                 h_final=None, workspace=None, stream=None):
@@ -558,3 +598,26 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None,
         batch, nheads, P, ngroups, N, L, code, workspace.data_ptr(), wsn,
         _stream_handle(dev, stream)))
     return y, h_final
+
+
+def ssm_roofline_hbm(kind, a, b=None, repeats=1, stream=None):
+    """``repeats`` passes of an HBM microbenchmark over the bytes of ``a``:
+    kind "copy" (b = a, b the same size), "rmw" (a = a*0.5 + 0.25 in place)
+    or "read" (b: a 1-element fp32 sink).  Enqueues only."""
+    code = ROOFLINE_HBM_KINDS[kind]
+    nbytes = a.numel() * a.element_size()
+    pa = _ptr(a, "a")
+    pb = _ptr(b, "b") if b is not None else None
+    _check(load_library().ssm_roofline_hbm(code, pa, pb, nbytes, repeats,
+                                           _stream_handle(a.device, stream)))
+
+
+def ssm_roofline_valu(kind, out, iters, stream=None):
+    """One VALU-issue microbenchmark pass: ``out.numel()`` threads each run
+    ``iters`` iterations of 8 independent chains of kind "exp" (v_exp_f32),
+    "fma" (v_fma_f32) or "mixed" (half of each); 8 lane-operations per
+    thread and iteration.  Enqueues only."""
+    code = ROOFLINE_VALU_KINDS[kind]
+    _check(load_library().ssm_roofline_valu(
+        code, _ptr(out, "out", torch.float32), out.numel(), iters,
+        _stream_handle(out.device, stream)))
