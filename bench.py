@@ -10,8 +10,15 @@ sets are rotated so the 256 MB last-level cache cannot serve them.
 
 Prints ONE JSON line.  ``value`` is GB/s of algorithmic traffic (bytes the
 method must move: every input read once, y and the final state written
-once).  ``roofline`` relates the scan kernel's average duration (HIP events
-on its stream over the timed region) to the ALU ceiling that bounds it.
+once).  ``roofline`` relates the algorithmic bytes of one launch of the scan
+kernel to its average duration (HIP events around every step on the launch
+stream, over the timed region) and to the 8 TB/s HBM peak; ``valu`` beside
+it states the same launch against the VALU issue ceiling, which is what
+actually bounds the kernel at 16 states.  Both ceilings are also measured in
+the same run by hand-written microbenchmarks (include/ssm_roofline.h): a
+non-temporal copy, read-modify-write and read over 1 GiB buffers, and chains
+of v_exp_f32 and v_fma_f32.  They run before the timed steps, which also
+gives the timed steps a GPU whose clocks have settled under sustained load.
 ``cpu_baseline`` is the fp64 oracle on the same inputs on the host cores.
 
 Options beyond the contract: --no-cpu-baseline, --no-extra (skip the
@@ -61,13 +68,40 @@ FLOP_PER_STATE_UPDATE = 7
 FLOP_PER_ELEMENT = 13
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "scan_kernel_mamba2p8b_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "selective_state_space_30_amd", "csrc",
-                          "ssm_kernels.hip")
+SQ_FILE = os.path.join(ROOT, "profiles", "scan_kernel_mamba2p8b_sq_counters.txt")
+KERNEL_SRC_DIRS = [os.path.join(ROOT, "selective_state_space_30_amd", "csrc"),
+                   os.path.join(ROOT, "include")]
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over every source the kernels are built from (all of
+    csrc/ and include/, names and contents), so a profile taken before any
+    change to them is recognised as stale."""
+    h = hashlib.sha256()
+    for d in KERNEL_SRC_DIRS:
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if os.path.isfile(path):
+                h.update(name.encode() + b"\0")
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_valu_slots():
+    """VALU issue slots (SQ_ACTIVE_INST_VALU: instructions plus the extra
+    slots of transcendentals) per launch of the scan kernel, from the
+    committed SQ-counter summary, or None if the sources changed since."""
+    try:
+        text = open(SQ_FILE).read()
+    except OSError:
+        return None
+    if "sources sha256[:16] %s" % kernel_source_hash() not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("SQ_ACTIVE_INST_VALU"):
+            return float(line.split()[1])
+    return None
 
 
 def measured_traffic(n_launch_bytes):
@@ -139,6 +173,7 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
+    ceil = {} if args.only_scan else ceilings(torch, ssm, dev, stream, log)
 
     def step(i):
         s = sets[i % 3]
@@ -150,29 +185,32 @@ def main():
         step(i)
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event before the first step and after every step, on the launch
+    # stream: per-step durations (median, min) and the mean over all K
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
+    evs[0].record(stream)
     for i in range(args.steps):
         step(i)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_events = ev0.elapsed_time(ev1) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1])
+                      for i in range(args.steps))
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    ms_median = per_step[len(per_step) // 2]
+    ms_min = per_step[0]
     ms_wall = wall * 1e3 / args.steps
-    ms = ms_events
     sec = ms * 1e-3
     gbps = nbytes / sec / 1e9
-    log("scan: %.1f us/step (events), %.1f us/step (wall), %.0f GB/s"
-        % (ms * 1e3, ms_wall * 1e3, gbps))
+    log("scan: %.1f us/step mean, %.1f median, %.1f min (events), %.1f "
+        "(wall), %.0f GB/s" % (ms * 1e3, ms_median * 1e3, ms_min * 1e3,
+                               ms_wall * 1e3, gbps))
     if args.only_scan:
         return
 
     flops = (E * cfg.dstate * FLOP_PER_STATE_UPDATE + E * FLOP_PER_ELEMENT)
-    achieved = flops / sec / 1e12
-    traffic = measured_traffic(nbytes)
     result = {
         "metric": "selective-scan HBM GB/s (% of peak) + elements/s, "
                   "D=5120 L=4096 N=16",
@@ -196,41 +234,33 @@ def main():
         "elements_per_s": round(E / sec),
         "state_updates_per_s": round(E * cfg.dstate / sec),
         "algorithmic_bytes_per_step": nbytes,
+        "ms_per_step_median": round(ms_median, 5),
+        "ms_per_step_min": round(ms_min, 5),
         "ms_per_step_wall": round(ms_wall, 5),
+        # one step is one launch of the scan kernel (the sequence is not
+        # split at this shape), so the per-launch duration is the step's
         "roofline": {
-            "bound": "alu",
-            "achieved": round(achieved, 3),
-            "peak": round(VALU_PEAK_TFLOPS, 2),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / VALU_PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "kernel": "scan_kernel<bf16, vec>",
-            "flop_per_launch": flops,
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(nbytes),
+            "kernel": SCAN_KERNEL,
+            "algorithmic_bytes_per_launch": nbytes,
+            "launch_us_mean": round(ms * 1e3, 2),
         },
     }
-
-    # Copy ceiling: a plain device-to-device copy of 1 GiB (read + write).
-    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    b = torch.empty_like(a)
-    a.fill_(1.0)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        b.copy_(a)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * a.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del a, b
-    result["copy_ceiling_GBps"] = round(copy_gbps, 1)
-    result["pct_of_copy_ceiling"] = round(100 * gbps / copy_gbps, 2)
+    result["valu"] = valu_block(ceil, E * cfg.dstate, flops, sec)
+    if ceil:
+        result["hbm_ceilings_GBps"] = {k: ceil[k] for k in
+                                       ("copy", "rmw", "read")}
+        result["copy_ceiling_GBps"] = ceil["copy"]
+        result["pct_of_copy_ceiling"] = round(100 * gbps / ceil["copy"], 2)
 
     if not args.no_extra:
         result["other_workloads"] = extra_workloads(torch, ssm, syn, dev,
-                                                    stream, log)
+                                                    stream, log, ceil)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sets[0], cfg, nbytes, log)
@@ -239,7 +269,99 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def extra_workloads(torch, ssm, syn, dev, stream, log):
+def ceilings(torch, ssm, dev, stream, log):
+    """The HBM and VALU-issue ceilings, measured by the library's
+    microbenchmarks (include/ssm_roofline.h) on this GPU in this run.
+    HBM: GB/s (bytes read plus bytes written) of a non-temporal copy, an
+    in-place read-modify-write and a read-only pass over 1 GiB buffers (4x
+    the 256 MB last-level cache), best of 5 timings of 10 passes each.
+    VALU: lane-operations per second of chains of v_exp_f32, of v_fma_f32
+    and of both interleaved, over 8 waves per SIMD, best of 5."""
+    log("ceilings: HBM copy / read-modify-write / read over 1 GiB, "
+        "v_exp_f32 and v_fma_f32 issue rates")
+    out = {}
+    nb = 1 << 30
+    a = torch.empty(nb // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(0.5)
+    sink = torch.zeros(1, device=dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for kind, moved in (("copy", 2 * nb), ("rmw", 2 * nb), ("read", nb)):
+        bb = b if kind == "copy" else (sink if kind == "read" else None)
+        ssm.ssm_roofline_hbm(kind, a, bb, repeats=2, stream=stream)
+        best = None
+        for _ in range(5):
+            e0.record(stream)
+            ssm.ssm_roofline_hbm(kind, a, bb, repeats=10, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / 10
+            best = t if best is None else min(best, t)
+        out[kind] = round(moved / best / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    threads = 256 * 4 * 8 * 64      # 8 waves on each of the 1024 SIMDs
+    iters = 4096
+    vout = torch.empty(threads, device=dev)
+    for kind in ("exp", "fma", "mixed"):
+        ssm.ssm_roofline_valu(kind, vout, iters, stream=stream)
+        best = None
+        for _ in range(5):
+            e0.record(stream)
+            ssm.ssm_roofline_valu(kind, vout, iters, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+        out[kind + "_lane_ops_per_s"] = threads * iters * 8 / best
+    # the mixed chains take half of each kind: if a transcendental overlapped
+    # the FMAs, the mixed rate would approach the FMA rate; without overlap
+    # the time is the sum of the two halves
+    t_exp = 0.5 / out["exp_lane_ops_per_s"]
+    t_fma = 0.5 / out["fma_lane_ops_per_s"]
+    out["mixed_over_no_overlap"] = round(
+        (1.0 / out["mixed_lane_ops_per_s"]) / (t_exp + t_fma), 3)
+    log("ceilings: copy %.0f, rmw %.0f, read %.0f GB/s; exp %.3g, fma %.3g "
+        "lane-ops/s (mixed / no-overlap time %.2f)"
+        % (out["copy"], out["rmw"], out["read"], out["exp_lane_ops_per_s"],
+           out["fma_lane_ops_per_s"], out["mixed_over_no_overlap"]))
+    return out
+
+
+def valu_block(ceil, state_updates, flops, sec):
+    """The scan launch against the VALU issue ceiling: issue slots per
+    launch (SQ_ACTIVE_INST_VALU from the committed counter summary, while
+    the sources are unchanged) over the FMA issue rate measured in this run
+    give the time the instruction stream needs at full issue; that over the
+    launch's time is the fraction of the VALU ceiling reached.  The flop
+    count of the older alu figure (7 per state-update, an exp counted as one
+    flop although it takes two issue slots) is kept beside it, labelled."""
+    slots = measured_valu_slots()
+    out = {"what": "VALU issue: the ceiling that bounds this kernel at 16 "
+                   "states (no packed fp32)",
+           "alu_flops_per_launch_7_per_state_update": flops,
+           "alu_frac_of_78.6_TFLOPs_nonpacked_fp32":
+               round(flops / sec / 1e12 / VALU_PEAK_TFLOPS, 4)}
+    if ceil:
+        out["exp_lane_ops_per_s"] = float("%.4g" % ceil["exp_lane_ops_per_s"])
+        out["fma_lane_ops_per_s"] = float("%.4g" % ceil["fma_lane_ops_per_s"])
+        out["exp_issue_cost_in_fma_slots"] = round(
+            ceil["fma_lane_ops_per_s"] / ceil["exp_lane_ops_per_s"], 2)
+        out["mixed_over_no_overlap"] = ceil["mixed_over_no_overlap"]
+    if slots is not None:
+        lane_slots = slots * 64
+        out["issue_slots_per_launch"] = lane_slots
+        out["issue_slots_per_state_update"] = round(lane_slots / state_updates, 2)
+        out["source"] = "profiles/scan_kernel_mamba2p8b_sq_counters.txt"
+        if ceil:
+            floor = lane_slots / ceil["fma_lane_ops_per_s"]
+            out["issue_floor_us"] = round(floor * 1e6, 1)
+            out["frac"] = round(floor / sec, 4)
+    return out
+
+
+def extra_workloads(torch, ssm, syn, dev, stream, log, ceil):
     """Long-context scan (chunked) and the decode step, timed with events.
     Reported for information beside the main line."""
     out = {}
@@ -376,7 +498,7 @@ def extra_workloads(torch, ssm, syn, dev, stream, log):
     out[syn.MAMBA2_LAYER.name] = ssd_measure(ssm, syn, dev, stream, reps, log)
     torch.cuda.empty_cache()
 
-    out[syn.DECODE.name] = decode_measure(ssm, syn, dev, stream, 1, log)
+    out[syn.DECODE.name] = decode_measure(ssm, syn, dev, stream, 1, log, ceil)
     return out
 
 
@@ -451,21 +573,26 @@ def bwd_measure(ssm, syn, dev, stream, reps, log):
                     "ssm_scan_bwd reusing its checkpoints)"}
 
 
-def decode_measure(ssm, syn, dev, stream, passes, log):
+N_DECODE_STATES = 8
+
+
+def decode_measure(ssm, syn, dev, stream, passes, log, ceil=None):
     """The decode workload: ``passes`` times its 64 steps, each step one
-    ssm_state_update call bound in advance.  Four states (one per layer of a
-    stack) take the steps in turn: 336 MB, more than the last-level cache
-    holds."""
+    ssm_state_update call bound in advance.  Eight states (one per layer of
+    a stack) take the steps in turn: 671 MB, so a state comes back after
+    ~1.25 GB of other traffic, well past what the 256 MB last-level cache
+    holds.  Stated against the read-modify-write ceiling measured in the
+    same run (``ceil``)."""
     import torch
     dcfg = syn.DECODE
     log("decode workload %s" % dcfg.name)
     dinp = syn.make_decode_inputs(dcfg, dev)
     steps = [syn.step_slice(dinp, t) for t in range(dcfg.steps)]
     states = [torch.zeros(dcfg.batch, dcfg.dim, 16, device=dev)
-              for _ in range(4)]
+              for _ in range(N_DECODE_STATES)]
     ys = [torch.empty(dcfg.batch, dcfg.dim, dtype=torch.bfloat16, device=dev)
           for _ in range(dcfg.steps)]
-    calls = [ssm.bind_state_update(states[t % 4], s["x"], s["delta"], dinp["A"],
+    calls = [ssm.bind_state_update(states[t % N_DECODE_STATES], s["x"], s["delta"], dinp["A"],
                                    s["B"], s["C"], dinp["D"], s["z"],
                                    dinp["delta_bias"], True, y=ys[t],
                                    stream=stream)
@@ -486,7 +613,7 @@ def decode_measure(ssm, syn, dev, stream, passes, log):
     # the same 64 steps captured once into a HIP graph and replayed (bound
     # to a side stream, the capture stream)
     side = torch.cuda.Stream()
-    gcalls = [ssm.bind_state_update(states[t % 4], s["x"], s["delta"],
+    gcalls = [ssm.bind_state_update(states[t % N_DECODE_STATES], s["x"], s["delta"],
                                     dinp["A"], s["B"], s["C"], dinp["D"], s["z"],
                                     dinp["delta_bias"], True, y=ys[t], stream=side)
               for t, s in enumerate(steps)]
@@ -508,13 +635,13 @@ def decode_measure(ssm, syn, dev, stream, passes, log):
     # the same steps with the width-4 conv prologue (ssm_conv_state_update),
     # each state with its own kept window, captured the same way
     cinp = syn.make_conv_decode_inputs(dcfg, dev, d_conv=4)
-    windows = [cinp["conv_state0"].clone() for _ in range(4)]
+    windows = [cinp["conv_state0"].clone() for _ in range(N_DECODE_STATES)]
     torch.cuda.synchronize()
     cgraph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(cgraph, stream=side):
         for t, s in enumerate(steps):
             ssm.ssm_conv_state_update(
-                states[t % 4], windows[t % 4], s["x"], cinp["conv_w"],
+                states[t % N_DECODE_STATES], windows[t % N_DECODE_STATES], s["x"], cinp["conv_w"],
                 s["delta"], dinp["A"], s["B"], s["C"], dinp["D"], s["z"],
                 dinp["delta_bias"], True, conv_b=cinp["conv_b"], y=ys[t],
                 stream=side)
@@ -527,9 +654,17 @@ def decode_measure(ssm, syn, dev, stream, passes, log):
     torch.cuda.synchronize()
     us_conv = e0.elapsed_time(e1) * 1e3 / (dcfg.steps * passes)
     nb = syn.decode_step_bytes(dcfg)
-    return {"us_per_step": round(us, 3), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
-            "bytes_per_step": nb, "us_per_step_hip_graph": round(us_graph, 3),
-            "us_per_step_conv4_hip_graph": round(us_conv, 3)}
+    gbps = nb / (us * 1e-6) / 1e9
+    out = {"us_per_step": round(us, 3), "GBps": round(gbps, 1),
+           "bytes_per_step": nb, "states_rotated": N_DECODE_STATES,
+           "state_bytes_rotated": N_DECODE_STATES * dcfg.batch * dcfg.dim * 16 * 4,
+           "us_per_step_hip_graph": round(us_graph, 3),
+           "us_per_step_conv4_hip_graph": round(us_conv, 3)}
+    if ceil:
+        out["rmw_ceiling_GBps"] = ceil["rmw"]
+        out["frac_of_rmw_ceiling"] = round(gbps / ceil["rmw"], 4)
+        out["frac_of_hbm_peak"] = round(gbps / HBM_PEAK_GBPS, 4)
+    return out
 
 
 def ssd_measure(ssm, syn, dev, stream, reps, log):
@@ -578,37 +713,55 @@ def ssd_measure(ssm, syn, dev, stream, reps, log):
 
 def cpu_baseline(inp, cfg, nbytes, log):
     """The fp64 oracle, as it stands, over the whole workload on the host
-    cores (disjoint channel ranges on threads)."""
+    cores (disjoint channel ranges on threads), median of 3 runs; beside it
+    one thread on a bounded sample."""
+    import statistics
     import oracle
-    threads = min(16, os.cpu_count() or 1)
-    log("cpu baseline: oracle on %d threads" % threads)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    # the host CPU share of a one-GPU box is 16 cores, whatever the machine
+    # has in all
+    threads = max(1, min(16, avail))
+    log("cpu baseline: oracle on %d threads (%d usable, %s in the machine), "
+        "median of 3" % (threads, avail, os.cpu_count()))
     host = {k: (v.detach().to("cpu").double().numpy() if hasattr(v, "detach")
                 else v) for k, v in inp.items()
             if k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
-    t0 = time.perf_counter()
-    oracle.scan_threaded(host["u"], host["delta"], host["A"], host["B"],
-                         host["C"], host["D"], host["z"], host["delta_bias"],
-                         True, False, None, threads=threads)
-    sec = time.perf_counter() - t0
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.scan_threaded(host["u"], host["delta"], host["A"], host["B"],
+                             host["C"], host["D"], host["z"],
+                             host["delta_bias"], True, False, None,
+                             threads=threads)
+        times.append(time.perf_counter() - t0)
+    sec = statistics.median(times)
     # one thread on the first 256 channels of each batch entry (a bounded
-    # sample of the same workload)
+    # sample of the same workload), median of 3
     nd = min(256, cfg.dim)
     part = {k: (v[:, :nd] if k in ("u", "delta", "z") else
                 v[:nd] if k in ("A", "D", "delta_bias") else v)
             for k, v in host.items()}
-    t1 = time.perf_counter()
-    oracle.scan_threaded(part["u"], part["delta"], part["A"], part["B"],
-                         part["C"], part["D"], part["z"], part["delta_bias"],
-                         True, False, None, threads=1)
-    sec1 = time.perf_counter() - t1
+    times1 = []
+    for _ in range(3):
+        t1 = time.perf_counter()
+        oracle.scan_threaded(part["u"], part["delta"], part["A"], part["B"],
+                             part["C"], part["D"], part["z"],
+                             part["delta_bias"], True, False, None, threads=1)
+        times1.append(time.perf_counter() - t1)
+    sec1 = statistics.median(times1)
     return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": "the whole workload (%d x %d channels x %d tokens), "
-                      "fp64, %.2f s wall" % (cfg.batch, cfg.dim, cfg.seqlen,
-                                             sec),
+                      "fp64, median of 3 runs: %.2f s wall each (%.1f s of "
+                      "CPU work in all)" % (cfg.batch, cfg.dim, cfg.seqlen, sec,
+                                            sum(times) * threads),
             "elements_per_s": round(cfg.elements / sec),
+            "host_cpus_usable": avail, "host_cpus_total": os.cpu_count(),
             "one_thread_elements_per_s": round(cfg.batch * nd * cfg.seqlen / sec1),
-            "one_thread_sample": "%d x %d channels x %d tokens, %.2f s" % (
+            "one_thread_sample": "%d x %d channels x %d tokens, median %.2f s" % (
                 cfg.batch, nd, cfg.seqlen, sec1),
             "cpu_model": _cpu_model()}
 
@@ -747,7 +900,8 @@ def summarize_profiles(d):
                 fetch[SCAN_KERNEL], fb / 1e6, write[SCAN_KERNEL], wb / 1e6),
             "HBM bytes per launch %.1f MB vs algorithmic %.1f MB (ratio %.3f)" % (
                 (fb + wb) / 1e6, alg / 1e6, (fb + wb) / alg),
-            "kernel source sha256[:16] %s" % out["kernel_source_sha256_16"]]
+            "sources sha256[:16] %s (all of csrc/ and include/)"
+            % out["kernel_source_sha256_16"]]
     with open(os.path.join(prof, "scan_kernel_mamba2p8b_traffic.txt"), "w") as f:
         f.write("\n".join(txt) + "\n")
 
@@ -774,7 +928,9 @@ def summarize_profiles(d):
             "transcendentals per state-update: %.2f" % (
                 sq["SQ_INSTS_VALU_TRANS_F32"] * 64 / upd),
             "VALU busy time at 2.4 GHz, 4 cycles per wave64 slot, 1024 SIMDs: "
-            "%.1f us" % (slots * 4 / (1024 * 2.4e9) * 1e6)]
+            "%.1f us" % (slots * 4 / (1024 * 2.4e9) * 1e6),
+            "sources sha256[:16] %s (all of csrc/ and include/)"
+            % kernel_source_hash()]
         with open(os.path.join(prof, "scan_kernel_mamba2p8b_sq_counters.txt"),
                   "w") as f:
             f.write("\n".join(sq_txt) + "\n")

@@ -3,6 +3,7 @@
 // runs before the first HIP call, so an invalid request never touches the
 // device.
 #include "ssm_scan.h"
+#include "ssm_roofline.h"
 
 #include <cstdarg>
 #include <cstdio>
@@ -731,6 +732,54 @@ int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
   a.dstate = static_cast<int>(dstate);
   a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
   const int err = ssm::launch_ssd(a, vec, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ roofline microbenchmarks
+extern "C" {
+
+int ssm_roofline_hbm(int kind, void *a, void *b, size_t bytes, int repeats,
+                     void *stream) {
+  if (kind < SSM_ROOFLINE_COPY || kind > SSM_ROOFLINE_READ)
+    return fail(SSM_ERR_INVALID_ARG, "unknown HBM kind %d", kind);
+  if (bytes == 0 || bytes % SSM_ROOFLINE_HBM_QUANTUM != 0 || bytes >= (size_t(1) << 46))
+    return fail(SSM_ERR_INVALID_ARG, "bytes=%zu: must be a positive multiple of %d below 2^46",
+                bytes, SSM_ROOFLINE_HBM_QUANTUM);
+  if (repeats < 1 || repeats > 1000)
+    return fail(SSM_ERR_INVALID_ARG, "repeats=%d: must be 1..1000", repeats);
+  if (!a || !aligned(a, 16)) return fail(SSM_ERR_INVALID_ARG, "a: NULL or not 16-byte aligned");
+  if (kind == SSM_ROOFLINE_COPY) {
+    if (!b || !aligned(b, 16))
+      return fail(SSM_ERR_INVALID_ARG, "b: NULL or not 16-byte aligned");
+    if (overlaps(a, static_cast<int64_t>(bytes), b, static_cast<int64_t>(bytes)))
+      return fail(SSM_ERR_INVALID_ARG, "a and b overlap");
+  } else if (kind == SSM_ROOFLINE_READ) {
+    if (!b || !aligned(b, 4)) return fail(SSM_ERR_INVALID_ARG, "b: NULL or not 4-byte aligned");
+    if (overlaps(a, static_cast<int64_t>(bytes), b, 4))
+      return fail(SSM_ERR_INVALID_ARG, "a and b overlap");
+  }
+  const int err = ssm::launch_roofline_hbm(kind, a, b, static_cast<int64_t>(bytes / 16),
+                                           repeats, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  return ok();
+}
+
+int ssm_roofline_valu(int kind, float *out, int64_t threads, int iters, void *stream) {
+  if (kind < SSM_ROOFLINE_EXP || kind > SSM_ROOFLINE_MIXED)
+    return fail(SSM_ERR_INVALID_ARG, "unknown VALU kind %d", kind);
+  if (threads <= 0 || threads % SSM_ROOFLINE_VALU_QUANTUM != 0 || threads > (int64_t(1) << 26))
+    return fail(SSM_ERR_INVALID_ARG,
+                "threads=%lld: must be a positive multiple of %d, at most 2^26",
+                (long long)threads, SSM_ROOFLINE_VALU_QUANTUM);
+  if (iters < 1 || iters > (1 << 20))
+    return fail(SSM_ERR_INVALID_ARG, "iters=%d: must be 1..2^20", iters);
+  if (!out || !aligned(out, 4)) return fail(SSM_ERR_INVALID_ARG, "out: NULL or misaligned");
+  const int err = ssm::launch_roofline_valu(kind, out, threads, iters, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
   return ok();

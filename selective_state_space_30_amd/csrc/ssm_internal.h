@@ -105,6 +105,11 @@ int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream);
 int launch_step(const StepArgs &a, bool bf16, bool vec, void *stream);
 int launch_bwd(const BwdArgs &a, bool bf16, bool vec, void *stream);
 int launch_ssd(const SsdArgs &a, bool vec, void *stream);
+// Roofline microbenchmarks (ssm_roofline.hip): n16 16-byte pieces per pass.
+int launch_roofline_hbm(int kind, void *a, void *b, int64_t n16, int repeats,
+                        void *stream);
+int launch_roofline_valu(int kind, float *out, int64_t threads, int iters,
+                         void *stream);
 
 // Workspace layout of the backward pass, in bytes, each part 256-aligned.
 struct BwdLayout {

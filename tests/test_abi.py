@@ -1,7 +1,8 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry
-point include/ssm_scan.h declares, and rejects every invalid argument before
-any HIP call (the calls below never reach the device: each one fails
+point include/*.h declares, and rejects every invalid argument before any
+HIP call (the calls below never reach the device: each one fails
 validation first)."""
+import glob
 import ctypes
 import os
 import re
@@ -13,7 +14,7 @@ import torch
 import selective_state_space_30_amd as ssm
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 # Fake, never-dereferenced, suitably aligned addresses: every call using them
 # below is rejected by argument validation before any HIP call.
@@ -21,9 +22,11 @@ FAKE = 0x7F0000000000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -424,3 +427,47 @@ def test_ssd_workspace_size(lib):
     chunks = 2 * 1 * 64
     assert size.value >= chunks * (2 * 64 * 64 * 2 + 64 * 128 * 2)
     assert lib.ssm_ssd_workspace_size(2, 1, 100, 4096, ctypes.byref(size)) == 2
+
+
+INVALID_ROOFLINE_HBM = [
+    ("unknown kind", dict(kind=3), 1),
+    ("zero bytes", dict(nbytes=0), 1),
+    ("bytes not a multiple of the quantum", dict(nbytes=16384 + 16), 1),
+    ("zero repeats", dict(repeats=0), 1),
+    ("too many repeats", dict(repeats=1001), 1),
+    ("null a", dict(a=None), 1),
+    ("misaligned a", dict(a=FAKE + 8), 1),
+    ("copy without b", dict(b=None), 1),
+    ("copy onto itself", dict(b=FAKE + 16384), 1),
+    ("read sink inside a", dict(kind=2, b=FAKE + 64), 1),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_ROOFLINE_HBM,
+                         ids=[c[0] for c in INVALID_ROOFLINE_HBM])
+def test_roofline_hbm_rejects_invalid_arguments(lib, name, kw, status):
+    a = dict(kind=0, a=FAKE, b=FAKE + 0x10000000, nbytes=1 << 20, repeats=1)
+    a.update(kw)
+    assert lib.ssm_roofline_hbm(a["kind"], a["a"], a["b"], a["nbytes"],
+                                a["repeats"], None) == status, name
+    assert lib.ssm_last_error().decode()
+
+
+INVALID_ROOFLINE_VALU = [
+    ("unknown kind", dict(kind=-1), 1),
+    ("zero threads", dict(threads=0), 1),
+    ("threads not a multiple of the quantum", dict(threads=300), 1),
+    ("too many threads", dict(threads=(1 << 26) + 256), 1),
+    ("zero iterations", dict(iters=0), 1),
+    ("null out", dict(out=None), 1),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_ROOFLINE_VALU,
+                         ids=[c[0] for c in INVALID_ROOFLINE_VALU])
+def test_roofline_valu_rejects_invalid_arguments(lib, name, kw, status):
+    a = dict(kind=0, out=FAKE, threads=1024, iters=10)
+    a.update(kw)
+    assert lib.ssm_roofline_valu(a["kind"], a["out"], a["threads"], a["iters"],
+                                 None) == status, name
+    assert lib.ssm_last_error().decode()
