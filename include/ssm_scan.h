@@ -27,8 +27,10 @@
  *
  * Conventions shared by all entry points
  *  - Every array pointer is a DEVICE pointer owned by the caller.  The
- *    library never allocates, frees or retains memory; scratch space for the
- *    long-sequence split comes from the caller (see the workspace below).
+ *    library never allocates or frees memory and keeps no pointer of the
+ *    caller's; scratch space for the long-sequence split comes from the
+ *    caller (see the workspace below), except in ssm_scan_fwd_noalloc, which
+ *    uses a fixed scratch array of the library's own.
  *  - Arrays are dense and row-major with the token axis fastest:
  *      u, delta, z, y : (batch, dim, seqlen)      B, C : (batch, dstate, seqlen)
  *      A              : (dim, dstate) fp32        D, delta_bias : (dim) fp32
@@ -140,6 +142,28 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A,
                  int64_t dstate, int64_t seqlen, int dtype,
                  int64_t requested_chunk, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/* ssm_scan_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, computation and results, but no workspace argument.
+ * A sequence that ssm_scan_plan splits into chunks keeps its chunk states in
+ * a fixed scratch array inside the library (16 MiB per GPU, held by each GPU
+ * the library runs on until the process ends), so a split whose workspace
+ * (ssm_scan_workspace_size) exceeds 16 MiB returns SSM_ERR_WORKSPACE, before
+ * any HIP call.  Nothing is allocated, freed or cleared: every chunk state
+ * is written before it is read.  All calls on one GPU share that GPU's
+ * scratch, so calls whose work may overlap in time on one GPU (on different
+ * streams, or from different threads) race and must be serialised by the
+ * caller; calls enqueued in order on one stream are safe.  The scratch
+ * belongs to the device of `stream` (the current device for NULL); its
+ * address is looked up on the first call on that device. */
+int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A,
+                         const void *B, const void *C, const float *D,
+                         const void *z, const float *delta_bias, unsigned flags,
+                         const float *h0, void *y, float *h_final,
+                         int64_t batch, int64_t dim, int64_t dstate,
+                         int64_t seqlen, int dtype, int64_t requested_chunk,
+                         void *stream);
 
 /* Selective scan whose input u is produced inside the kernel from the
  * pre-convolution activations x by the Mamba block's depthwise causal

@@ -55,7 +55,8 @@ EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
            "ssm_conv_state_update",
            "ssm_scan_bwd_workspace_size", "ssm_scan_fwd_save", "ssm_scan_bwd",
            "ssm_ssd_workspace_size", "ssm_ssd_fwd", "ssm_last_error",
-           "ssm_roofline_hbm", "ssm_roofline_valu")
+           "ssm_roofline_hbm", "ssm_roofline_valu", "ssm_scan_fwd_noalloc")
+SCAN_SCRATCH_BYTES = 16 << 20  # the fixed scratch of ssm_scan_fwd_noalloc
 SSM_ROOFLINE_HBM_QUANTUM = 16384
 SSM_ROOFLINE_VALU_QUANTUM = 256
 ROOFLINE_HBM_KINDS = {"copy": 0, "rmw": 1, "read": 2}
@@ -98,6 +99,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                      I64, I64, I64, I64, I, I64, P,
                                      ctypes.c_size_t, P]
         lib.ssm_scan_fwd.restype = I
+        lib.ssm_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, U, P, P,
+                                             P, I64, I64, I64, I64, I, I64, P]
+        lib.ssm_scan_fwd_noalloc.restype = I
         lib.ssm_conv_scan_fwd.argtypes = [P, P, P, I, P, P, P, P, P, P, P, U,
                                           P, P, P, I64, I64, I64, I64, I, I64,
                                           P, ctypes.c_size_t, P]

@@ -272,7 +272,7 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
               const float *h0, void *y, float *h_final, int64_t batch,
               int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
               int64_t requested_chunk, void *workspace, size_t workspace_bytes,
-              void *saved, size_t saved_bytes, void *stream) {
+              void *saved, size_t saved_bytes, void *stream, bool use_scratch = false) {
   if (x) {
     if (!conv_w) return fail(SSM_ERR_INVALID_ARG, "conv_w is NULL");
     if (d_conv < 1 || d_conv > ssm::kMaxConv)
@@ -354,7 +354,25 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
                 (long long)kMaxGridYZ);
 
   ssm::ScanArgs a{};
-  if (n_chunks > 1) {
+  if (n_chunks > 1 && use_scratch) {
+    // the library's fixed device scratch; the size check is arithmetic
+    // only, the address lookup is the first HIP call
+    const ssm::SplitLayout l = ssm::split_layout(batch, dim, n_chunks);
+    if (l.total_bytes > ssm::kScanScratchBytes)
+      return fail(SSM_ERR_WORKSPACE,
+                  "this shape splits into %lld chunks and needs %zu bytes of scratch; "
+                  "the fixed scratch holds %zu (use ssm_scan_fwd with a workspace)",
+                  (long long)n_chunks, l.total_bytes, ssm::kScanScratchBytes);
+    void *p = nullptr;
+    const int err = ssm::scan_scratch(stream, &p);
+    if (err != 0)
+      return fail(SSM_ERR_HIP, "device scratch lookup failed: %s",
+                  ssm::hip_error_string(err));
+    char *w = static_cast<char *>(p);
+    a.ws_H = reinterpret_cast<float *>(w + l.off_H);
+    a.ws_S = reinterpret_cast<float *>(w + l.off_S);
+    a.ws_hin = reinterpret_cast<float *>(w + l.off_hin);
+  } else if (n_chunks > 1) {
     const ssm::SplitLayout l = ssm::split_layout(batch, dim, n_chunks);
     if (!workspace || workspace_bytes < l.total_bytes)
       return fail(SSM_ERR_WORKSPACE,
@@ -415,6 +433,19 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A,
                    delta_bias, flags, h0, y, h_final, batch, dim, dstate,
                    seqlen, dtype, requested_chunk, workspace, workspace_bytes,
                    nullptr, 0, stream);
+}
+
+int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A,
+                         const void *B, const void *C, const float *D, const void *z,
+                         const float *delta_bias, unsigned flags, const float *h0,
+                         void *y, float *h_final, int64_t batch, int64_t dim,
+                         int64_t dstate, int64_t seqlen, int dtype,
+                         int64_t requested_chunk, void *stream) {
+  if (!u) return fail(SSM_ERR_INVALID_ARG, "u is NULL");
+  return scan_impl(u, nullptr, nullptr, nullptr, 0, delta, A, B, C, D, z,
+                   delta_bias, flags, h0, y, h_final, batch, dim, dstate,
+                   seqlen, dtype, requested_chunk, nullptr, 0, nullptr, 0, stream,
+                   /*use_scratch=*/true);
 }
 
 int ssm_scan_fwd_save(const void *u, const void *delta, const float *A,

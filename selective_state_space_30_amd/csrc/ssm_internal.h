@@ -99,6 +99,12 @@ struct SplitLayout {
 };
 SplitLayout split_layout(int64_t batch, int64_t dim, int64_t n_chunks);
 
+// Size of the fixed device scratch of ssm_scan_fwd_noalloc (a split layout
+// must fit in it) and its device address for the device of `stream`
+// (returns a hipError_t value as int, 0 = success).
+constexpr size_t kScanScratchBytes = size_t(16) << 20;
+int scan_scratch(void *stream, void **ptr);
+
 // Kernel launchers.  Return a hipError_t value as int (0 = success).
 // `vec` selects 16-byte vector loads (the caller has checked alignment).
 int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream);

@@ -35,9 +35,17 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "ssm_device.h"
 #include "ssm_internal.h"
+
+// Fixed device scratch of the allocation-free scan entry point: the split
+// (chunked) scan's chunk end states, chunk dt sums and incoming states.  Each
+// GPU holds its own copy for the life of the process.  In host code this
+// name is only a handle for hipGetSymbolAddress: the device address comes
+// from scan_scratch() below and is the only form passed to kernels.
+static __device__ __align__(256) unsigned char scratch[ssm::kScanScratchBytes];
 
 namespace ssm {
 namespace {
@@ -467,6 +475,35 @@ int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream) {
   if (bf16)
     return vec ? launch_scan_t<uint16_t, true>(a, s) : launch_scan_t<uint16_t, false>(a, s);
   return vec ? launch_scan_t<float, true>(a, s) : launch_scan_t<float, false>(a, s);
+}
+
+// Device address of `scratch` on the device that `stream` belongs to (the
+// current device for the null stream), looked up once per device with that
+// device current and kept.
+int scan_scratch(void *stream, void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex m;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                        : hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(m);
+  if (!addr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return static_cast<int>(e);
+    void *p = nullptr;
+    const hipError_t eg = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return static_cast<int>(e);
+    if (eg != hipSuccess) return static_cast<int>(eg);
+    if (!p) return static_cast<int>(hipErrorInvalidSymbol);
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 const char *hip_error_string(int err) {

@@ -471,3 +471,46 @@ def test_roofline_valu_rejects_invalid_arguments(lib, name, kw, status):
     assert lib.ssm_roofline_valu(a["kind"], a["out"], a["threads"], a["iters"],
                                  None) == status, name
     assert lib.ssm_last_error().decode()
+
+
+def _noalloc(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE + 0x10000000, A=FAKE + 0x20000000,
+             B=FAKE + 0x30000000, C=FAKE + 0x40000000, D=None, z=None,
+             bias=None, flags=1, h0=None, y=FAKE + 0x50000000, h_final=None,
+             batch=1, dim=16, dstate=16, seqlen=256, dtype=ssm.SSM_DTYPE_F32,
+             chunk=0, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_fwd_noalloc(a["u"], a["delta"], a["A"], a["B"], a["C"],
+                                    a["D"], a["z"], a["bias"], a["flags"],
+                                    a["h0"], a["y"], a["h_final"], a["batch"],
+                                    a["dim"], a["dstate"], a["seqlen"],
+                                    a["dtype"], a["chunk"], a["stream"])
+
+
+INVALID_NOALLOC_CASES = [
+    ("null u", dict(u=None), 1),
+    ("null y", dict(y=None), 1),
+    ("dstate 32", dict(dstate=32), 2),
+    ("y aliases u", dict(y=FAKE + 64), 1),
+    # 64 x 1024 channels in 128 chunks: 1.1 GB of chunk states, far beyond
+    # the fixed 16 MiB scratch
+    ("split beyond the fixed scratch",
+     dict(batch=64, dim=1024, seqlen=128 * 1024, chunk=1024,
+          **{k: FAKE + (i + 1) * (1 << 40) for i, k in
+             enumerate(("delta", "A", "B", "C", "y"))}), 3),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_NOALLOC_CASES,
+                         ids=[c[0] for c in INVALID_NOALLOC_CASES])
+def test_noalloc_rejects_invalid_arguments(lib, name, kw, status):
+    assert _noalloc(lib, **kw) == status, name
+    assert lib.ssm_last_error().decode()
+
+
+def test_noalloc_scratch_limit_matches_the_workspace_size():
+    """A split fits the fixed scratch exactly when its workspace would."""
+    ok = ssm.ssm_scan_workspace_size(1, 1536, 16, 1 << 20)
+    assert 0 < ok <= ssm.SCAN_SCRATCH_BYTES
+    assert ssm.ssm_scan_workspace_size(64, 1024, 16, 128 * 1024, 1024) > \
+        ssm.SCAN_SCRATCH_BYTES
