@@ -781,7 +781,7 @@ def _cpu_model():
 # not the checkpoint pass
 SCAN_KERNEL = "scan_kernel<unsigned short, true, true, false, false, false>"
 CKPT_KERNEL = "scan_kernel<unsigned short, true, true, false, false, true>"
-COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_KERNEL = "roof_copy_kernel"
 COPY_BYTES = 1 << 30  # each calibration copy reads and writes 1 GiB
 
 
