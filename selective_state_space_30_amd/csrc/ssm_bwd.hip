@@ -138,8 +138,12 @@ __device__ __forceinline__ void bwd_block(
   if (stager) run.load(src, t0, tq, tend);  // state 0
 
   // per token: dt (as dt*log2 e), dt*u, the gated output gradient gc and
-  // the sums over states s1 = sum lambda B, s2 = sum lambda a h_prev A
-  float dtl[K], du[K], gc[K], s1[K], s2[K];
+  // the sums over states s1 = sum lambda B, s2 = sum lambda a h_prev A;
+  // kept for the end of the block: us = u * sigmoid(delta + bias) and sg =
+  // sigmoid(delta + bias) (the derivative of softplus; u and 1 without
+  // softplus).  The gate's gradient dz needs nothing from the state loop
+  // and is formed and stored here.
+  float dtl[K], du[K], gc[K], s1[K], s2[K], us[K], sg[K];
   float sdt = 0.0f;
   {
     float uu[K], dr[K];
@@ -149,20 +153,48 @@ __device__ __forceinline__ void bwd_block(
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const float x = dr[j] + bias;
-      float v = kSoftplus ? softplus_f(x) : x;
+      float v = x, sgm = 1.0f;
+      if constexpr (kSoftplus) {
+        // softplus_f with its terms kept: e = exp(-|x|), w = 1 + e;
+        // sigmoid(x) = 1/w for x >= 0 and e/w below
+        const float e = fast_exp2(-fabsf(x) * kLog2e);
+        const float w = 1.0f + e;
+        const float r = e - (w - 1.0f);
+        v = fmaxf(x, 0.0f) + fmaf(__builtin_amdgcn_logf(w), kLn2, r);
+        sgm = (x >= 0.0f ? 1.0f : e) * __builtin_amdgcn_rcpf(w);
+      }
       if (!kFull) v = (tl + j < tend) ? v : 0.0f;  // identity step
       dtl[j] = v * kLog2e;
       du[j] = v * uu[j];
       sdt += v;
+      us[j] = uu[j] * sgm;
+      sg[j] = sgm;
       s1[j] = 0.0f;
       s2[j] = 0.0f;
     }
-  }
-  if (zrow) {
-    float zz[K];
-    load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
+    if (zrow) {
+      float zz[K];
+      load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
+      if (p.dz) {
+        // dz = dy * yc * silu'(z), yc the pre-gate output the checkpoint
+        // pass stored; silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
+        float yv[K];
+        load_run<T, K, kVec, kFull>(static_cast<const T *>(p.yc) + bd * p.L, t0, tl, tend, yv);
 #pragma unroll
-    for (int j = 0; j < K; ++j) gc[j] *= silu_f(zz[j]);
+        for (int j = 0; j < K; ++j) {
+          const float sz = sigmoid_f(zz[j]);
+          yv[j] = gc[j] * yv[j] * (sz * fmaf(zz[j], 1.0f - sz, 1.0f));
+          gc[j] *= zz[j] * sz;  // dy * silu(z)
+        }
+        if (ch_ok)
+          store_run<T, K, kVec, kFull>(static_cast<T *>(p.dz) + bd * p.L, t0, tl, tend, yv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) gc[j] *= silu_f(zz[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) dDl = fmaf(gc[j], uu[j], dDl);
   }
   if (!ch_ok) {
     // a wave past the last channel: with gc = dt*u = 0 its dB and dC
@@ -262,36 +294,18 @@ __device__ __forceinline__ void bwd_block(
     flush_state<kVec, kFull, K>(reg, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
   }
 
-  // per-token gradients
-  float uu[K], dr[K];
-  load_run<T, K, kVec, kFull>(urow, t0, tl, tend, uu);
-  load_run<T, K, kVec, kFull>(drow, t0, tl, tend, dr);
+  // per-token gradients: du = dt * sum lambda B + gc D, ddelta = (u *
+  // sum lambda B + sum lambda a h_prev A) * sigmoid(delta + bias)
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const float x = dr[j] + bias;
-    const float dt = kSoftplus ? softplus_f(x) : x;
-    const float ddt = fmaf(uu[j], s1[j], s2[j]);
-    const float dx = kSoftplus ? ddt * sigmoid_f(x) : ddt;
+    const float dx = fmaf(us[j], s1[j], s2[j] * sg[j]);
     dbl += (kFull || tl + j < tend) ? dx : 0.0f;
-    dDl = fmaf(gc[j], uu[j], dDl);
-    s1[j] = fmaf(dt, s1[j], gc[j] * Dd);  // du
-    s2[j] = dx;                            // ddelta
+    s1[j] = fmaf(dtl[j] * kLn2, s1[j], gc[j] * Dd);  // du
+    s2[j] = dx;                                       // ddelta
   }
   if (ch_ok) {
     store_run<T, K, kVec, kFull>(static_cast<T *>(p.du) + bd * p.L, t0, tl, tend, s1);
     store_run<T, K, kVec, kFull>(static_cast<T *>(p.ddelta) + bd * p.L, t0, tl, tend, s2);
-  }
-  if (zrow && p.dz) {
-    // the gate: dz = dy * yc * silu'(z), yc the pre-gate output the
-    // checkpoint pass stored
-    float zz[K], gy[K], yv[K];
-    load_run<T, K, kVec, kFull>(zrow, t0, tl, tend, zz);
-    load_run<T, K, kVec, kFull>(gyrow, t0, tl, tend, gy);
-    load_run<T, K, kVec, kFull>(static_cast<const T *>(p.yc) + bd * p.L, t0, tl, tend, yv);
-#pragma unroll
-    for (int j = 0; j < K; ++j) yv[j] = gy[j] * yv[j] * dsilu_f(zz[j]);
-    if (ch_ok)
-      store_run<T, K, kVec, kFull>(static_cast<T *>(p.dz) + bd * p.L, t0, tl, tend, yv);
   }
 }
 
