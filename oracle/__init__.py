@@ -18,8 +18,8 @@ and state at a time).  This module only marshals numpy arrays into it:
 * :func:`causal_conv1d_silu` -- the depthwise causal convolution and SiLU
   that produce the scan's input u inside the Mamba block (the Guide
   Complet's section 4 architecture figure and section 7 block).
-* :func:`scan_bwd` -- gradients of :func:`scan` (Euler input term) by the
-  chain rule through the recurrence, in reverse token order.
+* :func:`scan_bwd` -- gradients of :func:`scan` (Euler or exact-ZOH input
+  term) by the chain rule through the recurrence, in reverse token order.
 * :func:`ssd` -- the Mamba-2 "state space dual" form with one scalar decay
   per head: the masked matrix product y = (L o S) x of the Guide Complet's
   section 5, computed directly.
@@ -79,7 +79,7 @@ def _load():
         lib.oracle_causal_conv1d_silu_f64.argtypes = [P, P, P, I64, P, I64,
                                                       I64, I64]
         lib.oracle_causal_conv1d_silu_f64.restype = I
-        lib.oracle_scan_bwd_f64.argtypes = [P] * 8 + [I] + [P] * 12 + [I64] * 4
+        lib.oracle_scan_bwd_f64.argtypes = [P] * 8 + [I, I] + [P] * 12 + [I64] * 4
         lib.oracle_scan_bwd_f64.restype = I
         lib.oracle_ssd_f64.argtypes = [P] * 8 + [I] + [P] * 3 + [I64] * 6
         lib.oracle_ssd_f64.restype = I
@@ -156,8 +156,9 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 
 
 def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-             delta_softplus=True, h0=None, dy=None, dh_final=None):
-    """Gradients of ``scan`` (Euler input term) for a loss whose gradient is
+             delta_softplus=True, h0=None, dy=None, dh_final=None, zoh_b=False):
+    """Gradients of ``scan`` (Euler input term, or exact ZOH with ``zoh_b``)
+    for a loss whose gradient is
     ``dy`` with respect to y and ``dh_final`` (or 0) with respect to the
     final state.  Returns a dict of fp64 arrays: du, ddelta, dA, dB, dC and,
     where the matching input is given, dD, ddelta_bias, dz; dh0 always."""
@@ -185,8 +186,8 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         out["dz"] = np.empty((batch, dim, L))
     rc = _load().oracle_scan_bwd_f64(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy),
-        _ptr(dh_final), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+        _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zoh_b)),
+        _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
         _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
         _ptr(out.get("ddelta_bias")), _ptr(out.get("dz")), _ptr(out["dh0"]),
         batch, dim, N, L)

@@ -35,12 +35,14 @@ static double oracle_silu(double z)
  *  zoh_b == 0: Euler, dB = dt * B ("SSM as RNN": B_scaled = B * delta).
  *  zoh_b == 1: exact zero-order hold for a diagonal A,
  *              dB = (exp(dt*a) - 1) / a * B  ("Discretisation", Guide
- *              Complet section 1); at a == 0 this is its limit dt * B. */
+ *              Complet section 1); at a == 0 this is its limit dt * B.
+ *              exp(dt*a) - 1 is evaluated by expm1, which does not lose the
+ *              relative accuracy of the difference when dt*a is small. */
 static double oracle_input_coeff(double dt, double a, int zoh_b)
 {
     if (!zoh_b || a == 0.0)
         return dt;
-    return (exp(dt * a) - 1.0) / a;
+    return expm1(dt * a) / a;
 }
 
 /* One token for one channel: updates h[0..N-1] in place and returns y.
@@ -170,14 +172,39 @@ static double oracle_dsilu(double z)
     return s * (1.0 + z * (1.0 - s));
 }
 
+/* Derivatives of the input coefficient c(dt, a) of oracle_input_coeff:
+ * *dc_ddt = dc/ddt and *dc_da = dc/da.  Euler: c = dt, so 1 and 0.  ZOH:
+ * c = (exp(dt a) - 1)/a, dc/ddt = exp(dt a), dc/da = (dt exp(dt a) - c)/a;
+ * where |dt a| < 1e-3 that difference cancels, so dc/da is taken from the
+ * series dt^2 (1/2 + x/3 + x^2/8 + x^3/30 + x^4/144), x = dt a (the
+ * derivative of c = dt sum_k x^k/(k+1)!; truncated below 1e-18 relative),
+ * whose value at a = 0 is the limit dt^2/2. */
+static void oracle_input_coeff_grad(double dt, double a, int zoh_b,
+                                    double *dc_ddt, double *dc_da)
+{
+    if (!zoh_b) {
+        *dc_ddt = 1.0;
+        *dc_da = 0.0;
+        return;
+    }
+    double x = dt * a;
+    double e = exp(x);
+    *dc_ddt = e;
+    if (fabs(x) < 1e-3)
+        *dc_da = dt * dt * (0.5 + x * (1.0 / 3.0 + x * (0.125 + x * (1.0 / 30.0 + x / 144.0))));
+    else
+        *dc_da = (dt * e - oracle_input_coeff(dt, a, zoh_b)) / a;
+}
+
 int oracle_scan_bwd_f64(const double *u, const double *delta, const double *A,
                         const double *B, const double *C, const double *D,
                         const double *z, const double *delta_bias,
-                        int delta_softplus, const double *h0, const double *dy,
-                        const double *dh_final, double *du, double *ddelta,
-                        double *dA, double *dB, double *dC, double *dD,
-                        double *ddelta_bias, double *dz, double *dh0,
-                        int64_t batch, int64_t dim, int64_t N, int64_t L)
+                        int delta_softplus, int zoh_b, const double *h0,
+                        const double *dy, const double *dh_final, double *du,
+                        double *ddelta, double *dA, double *dB, double *dC,
+                        double *dD, double *ddelta_bias, double *dz,
+                        double *dh0, int64_t batch, int64_t dim, int64_t N,
+                        int64_t L)
 {
     if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA ||
         !dB || !dC || (D && !dD))
@@ -216,7 +243,8 @@ int oracle_scan_bwd_f64(const double *u, const double *delta, const double *A,
                 double acc = 0.0;
                 for (int64_t n = 0; n < N; ++n) {
                     double h = exp(dt * Ad[n]) * hs[t * N + n] +
-                               dt * Bb[n * L + t] * u[row + t];
+                               oracle_input_coeff(dt, Ad[n], zoh_b) *
+                                   Bb[n * L + t] * u[row + t];
                     hs[(t + 1) * N + n] = h;
                     acc += Cb[n * L + t] * h;
                 }
@@ -242,14 +270,17 @@ int oracle_scan_bwd_f64(const double *u, const double *delta, const double *A,
                 }
                 for (int64_t n = 0; n < N; ++n) {
                     double a = exp(dt * Ad[n]);
+                    double c = oracle_input_coeff(dt, Ad[n], zoh_b);
+                    double dc_ddt, dc_da;
+                    oracle_input_coeff_grad(dt, Ad[n], zoh_b, &dc_ddt, &dc_da);
                     double hprev = hs[t * N + n];
                     double Bn = Bb[n * L + t];
                     g[n] += gc * Cb[n * L + t];
                     dC[b * N * L + n * L + t] += gc * hs[(t + 1) * N + n];
-                    ddt += g[n] * (Ad[n] * a * hprev + Bn * ut);
-                    dA[d * N + n] += g[n] * dt * a * hprev;
-                    dB[b * N * L + n * L + t] += g[n] * dt * ut;
-                    dut += g[n] * dt * Bn;
+                    ddt += g[n] * (Ad[n] * a * hprev + dc_ddt * Bn * ut);
+                    dA[d * N + n] += g[n] * (dt * a * hprev + dc_da * Bn * ut);
+                    dB[b * N * L + n * L + t] += g[n] * c * ut;
+                    dut += g[n] * c * Bn;
                     g[n] *= a;
                 }
                 du[row + t] = dut;

@@ -82,22 +82,26 @@ int oracle_causal_conv1d_silu_f64(const double *x, const double *w,
                                   const double *bias, int64_t K, double *u,
                                   int64_t batch, int64_t dim, int64_t seqlen);
 
-/* Gradients of the full scan (Euler input term), by the chain rule applied
- * to the recurrence above, token by token in reverse.  The loss is any
- * scalar whose gradient with respect to y is dy and with respect to h_final
- * is dh_final (NULL -> 0).  The inferownia.pl page ("Cena selekcji") states
- * that the backward pass recomputes the intermediate states rather than
- * storing them; this reference simply keeps the whole (L+1) x N state history
- * of one channel, which is the plain definition, not that optimisation.
+/* Gradients of the full scan, by the chain rule applied to the recurrence
+ * above, token by token in reverse.  The loss is any scalar whose gradient
+ * with respect to y is dy and with respect to h_final is dh_final (NULL ->
+ * 0).  The inferownia.pl page ("Cena selekcji") states that the backward
+ * pass recomputes the intermediate states rather than storing them; this
+ * reference simply keeps the whole (L+1) x N state history of one channel,
+ * which is the plain definition, not that optimisation.  With c the input
+ * coefficient of oracle_scan_f64 (dt for Euler; (exp(dt A_n) - 1)/A_n for
+ * exact zero-order hold, "Mamba & State Space Models - Guide Complet",
+ * section 1), dc/ddt = 1 (Euler) or exp(dt A_n) (ZOH) and dc/dA_n = 0
+ * (Euler) or (dt exp(dt A_n) - c)/A_n (ZOH; dt^2/2 at A_n = 0):
  *
  *   per (b, d): forward, keeping h_t for t = -1..L-1 and yc_t (pre-gate y);
  *   g = dh_final; for t = L-1 .. 0:
  *     s = silu(z_t), gc = dy_t * s;  dz_t = dy_t * yc_t * silu'(z_t)
  *     dD += gc * u_t;  du_t = gc * D
  *     for n: g[n] += gc * C[n,t];  dC[n,t] += gc * h_t[n]
- *            a = exp(dt A_n);  ddt += g[n] * (A_n a h_{t-1}[n] + B[n,t] u_t)
- *            dA[n] += g[n] dt a h_{t-1}[n];  dB[n,t] += g[n] dt u_t
- *            du_t += g[n] dt B[n,t];  g[n] *= a
+ *            a = exp(dt A_n);  ddt += g[n] * (A_n a h_{t-1}[n] + dc/ddt B[n,t] u_t)
+ *            dA[n] += g[n] (dt a h_{t-1}[n] + dc/dA_n B[n,t] u_t)
+ *            dB[n,t] += g[n] c u_t;  du_t += g[n] c B[n,t];  g[n] *= a
  *     dx = ddt * sigmoid(x) (softplus) or ddt;  ddelta_t = dx;  dbias += dx
  *   dh0 = g.
  * Outputs (fp64): du, ddelta (batch, dim, seqlen); dA (dim, dstate);
@@ -110,12 +114,12 @@ int oracle_causal_conv1d_silu_f64(const double *x, const double *w,
 int oracle_scan_bwd_f64(const double *u, const double *delta, const double *A,
                         const double *B, const double *C, const double *D,
                         const double *z, const double *delta_bias,
-                        int delta_softplus, const double *h0, const double *dy,
-                        const double *dh_final, double *du, double *ddelta,
-                        double *dA, double *dB, double *dC, double *dD,
-                        double *ddelta_bias, double *dz, double *dh0,
-                        int64_t batch, int64_t dim, int64_t dstate,
-                        int64_t seqlen);
+                        int delta_softplus, int zoh_b, const double *h0,
+                        const double *dy, const double *dh_final, double *du,
+                        double *ddelta, double *dA, double *dB, double *dC,
+                        double *dD, double *ddelta_bias, double *dz,
+                        double *dh0, int64_t batch, int64_t dim,
+                        int64_t dstate, int64_t seqlen);
 
 /* Mamba-2 "SSD" (state space dual) form ("Mamba & State Space Models -
  * Guide Complet", section 5: d_state 64-256, y = (L o S) u with L the causal

@@ -22,7 +22,8 @@ import oracle
 def loss(inp, dy, dhf):
     y, hf = oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
                         inp["D"], inp["z"], inp["delta_bias"],
-                        inp["delta_softplus"], False, inp["h0"])
+                        inp["delta_softplus"], inp.get("zoh_b", False),
+                        inp["h0"])
     return float(np.sum(dy * y) + (np.sum(dhf * hf) if dhf is not None else 0.0))
 
 
@@ -50,7 +51,8 @@ def make(seed, batch, dim, N, L, softplus=True, with_z=True, with_D=True,
 def grads(inp, dy, dhf):
     return oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"],
                            inp["C"], inp["D"], inp["z"], inp["delta_bias"],
-                           inp["delta_softplus"], inp["h0"], dy, dhf)
+                           inp["delta_softplus"], inp["h0"], dy, dhf,
+                           zoh_b=inp.get("zoh_b", False))
 
 
 GRAD_OF = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC",
@@ -65,9 +67,23 @@ VARIANTS = [
 ]
 
 
-@pytest.mark.parametrize("variant", VARIANTS, ids=["all", "bare", "mixed"])
-def test_finite_differences_every_element(variant):
+def _zoh_case(inp):
+    """Exact zero-order hold, with an A = 0 column (the Euler limit, dc/dA =
+    dt^2/2) and a column small enough that |dt*A| < 1e-3 (the series branch
+    of dc/dA)."""
+    inp["zoh_b"] = True
+    inp["A"][:, 0] = 0.0
+    inp["A"][:, 1] = -2e-4
+    return inp
+
+
+@pytest.mark.parametrize("variant,zoh", [(v, False) for v in VARIANTS] +
+                         [(VARIANTS[0], True), (VARIANTS[1], True)],
+                         ids=["all", "bare", "mixed", "zoh_all", "zoh_bare"])
+def test_finite_differences_every_element(variant, zoh):
     inp, dy, dhf = make(11, 2, 3, 4, 6, **variant)
+    if zoh:
+        inp = _zoh_case(inp)
     g = grads(inp, dy, dhf)
     eps = 1e-5
     for name, gname in GRAD_OF.items():
@@ -151,3 +167,33 @@ def test_gate_gradient_is_zero_where_output_vanishes():
     g = grads(inp, dy, None)
     assert np.all(g["dz"] == 0.0)
     assert np.all(g["du"] == 0.0) and np.all(g["dA"] == 0.0)
+
+
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+def test_zoh_linearity_in_u_and_h0(zoh):
+    """The exact-ZOH input term is linear in u as well: L(u, h0) = <du, u>
+    + <dh0, h0> with steps, A, B, C, D, z fixed (A with a zero column)."""
+    inp, dy, dhf = make(17, 2, 5, 16, 150)
+    if zoh:
+        inp = _zoh_case(inp)
+    g = grads(inp, dy, dhf)
+    lhs = loss(inp, dy, dhf)
+    rhs = _dot(g["du"], inp["u"]) + _dot(g["dh0"], inp["h0"])
+    assert abs(lhs - rhs) <= 1e-10 * (abs(lhs) + 1.0)
+
+
+def test_zoh_gradients_tend_to_euler_as_A_vanishes():
+    """For A -> 0 the ZOH coefficient (exp(dt A) - 1)/A tends to the Euler
+    coefficient dt, so every gradient but dA tends to the Euler one; at |A|
+    = 1e-9 they agree to ~1e-9 (the first-order term dt^2 A / 2).  dA does
+    not: the ZOH coefficient still depends on A there (dc/dA -> dt^2/2),
+    which the finite-difference pin checks at A = 0 exactly."""
+    inp, dy, dhf = make(18, 1, 3, 4, 30)
+    inp["A"][:] = -1e-9
+    ge = grads(inp, dy, dhf)
+    gz = grads(dict(inp, zoh_b=True), dy, dhf)
+    for k in ge:
+        if k == "dA":
+            continue
+        scale = 1.0 + np.max(np.abs(ge[k]))
+        assert np.max(np.abs(gz[k] - ge[k])) <= 1e-7 * scale, k
