@@ -241,7 +241,7 @@ int ssm_conv_state_update(float *state, void *conv_state, const void *x,
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                 int64_t seqlen, int dtype, size_t *bytes);
 
-/* Backward pass of ssm_scan_fwd with the Euler input term: the gradients of
+/* Backward pass of ssm_scan_fwd: the gradients of
  * a scalar loss with respect to every input, given its gradient dy with
  * respect to y and dh_final (nullable -> 0) with respect to the final state.
  * The chain rule through the recurrence, taken in reverse token order; the
@@ -258,10 +258,19 @@ int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *   dD       = sum_b,t dy_t silu(z_t) u_t    dbias  = sum_b,t ddelta_t
  *   dz_t     = dy_t yc_t silu'(z_t), yc_t = sum_n C_t,n h_t,n + D u_t
  *   dh0      = exp(dt_0 A) lambda_0
+ * With SSM_FLAG_ZOH_B the input coefficient dt becomes c_t,n = (exp(dt_t A_n)
+ * - 1)/A_n ("Mamba & State Space Models - Guide Complet", section 1), with
+ * dc/ddt = exp(dt A) and dc/dA = (dt exp(dt A) - c)/A (dt^2/2 at A = 0):
+ *   du_t     = sum_n lambda_t,n c_t,n B_t,n + dy_t silu(z_t) D
+ *   ddelta_t = (sum_n lambda_t,n exp(dt_t A_n) (B_t,n u_t + A_n h_t-1,n))
+ *              * sigmoid(delta_t + bias)
+ *   dA_n     = sum_b,t lambda_t,n (exp(dt_t A_n) h_t-1,n dt_t
+ *              + dc/dA_n B_t,n u_t)
+ *   dB_t,n   = sum_d lambda_t,n c_t,n u_t
  * Arguments:
  *  u, delta, A, B, C, D, z, delta_bias, flags, h0   as for ssm_scan_fwd
- *                      (flags: SSM_FLAG_DELTA_SOFTPLUS only; SSM_FLAG_ZOH_B
- *                      returns SSM_ERR_UNSUPPORTED)
+ *                      (flags: SSM_FLAG_DELTA_SOFTPLUS, SSM_FLAG_ZOH_B,
+ *                      SSM_FLAG_BWD_SAVED)
  *  dy                  required, activation dtype (batch, dim, seqlen)
  *  dh_final            nullable fp32 (batch, dim, dstate)
  *  du, ddelta          required outputs, activation dtype (batch, dim, seqlen)
@@ -302,8 +311,8 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
  * recomputes the intermediate states rather than storing them; here one
  * state per block is kept.)
  *  arguments as for ssm_scan_fwd, except:
- *  flags           SSM_FLAG_DELTA_SOFTPLUS (SSM_FLAG_ZOH_B: SSM_ERR_UNSUPPORTED,
- *                  the backward implements the Euler term only)
+ *  flags           SSM_FLAG_DELTA_SOFTPLUS and/or SSM_FLAG_ZOH_B (the following
+ *                  ssm_scan_bwd must be given the same flags)
  *  bwd_workspace   required, >= ssm_scan_bwd_workspace_size() bytes for the
  *                  same shape and dtype, 256-byte aligned, not overlapping any
  *                  argument; its checkpoint region is overwritten

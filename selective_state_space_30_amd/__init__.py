@@ -19,8 +19,8 @@ Names follow the C ABI:
   d_state 64-256) on the matrix cores; :func:`ssm_ssd_workspace_size`.
 * :func:`ssm_conv_state_update` -- the decoding step with the conv
   prologue (its window kept per channel).
-* :func:`ssm_scan_bwd` -- gradients of :func:`ssm_scan_fwd` (Euler input
-  term) with respect to every input, recomputing the states from block
+* :func:`ssm_scan_bwd` -- gradients of :func:`ssm_scan_fwd` (Euler or
+  exact-ZOH input term) with respect to every input, recomputing the states from block
   checkpoints; :func:`ssm_scan_bwd_workspace_size`;
   :func:`ssm_scan_fwd_save`, the forward that keeps those checkpoints for
   the backward (which then skips its own checkpoint pass).
@@ -447,7 +447,8 @@ def ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen,
 @_on_stream
 def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                       delta_softplus=True, h0=None, return_final_state=True,
-                      y=None, h_final=None, workspace=None, stream=None):
+                      y=None, h_final=None, workspace=None, stream=None,
+                      zoh_b=False):
     """:func:`ssm_scan_fwd` (whole sequences) that also keeps, in the
     backward's workspace, the state entering every 1024-token block and the
     pre-gate output.  Returns ``(y, h_final, workspace)``; pass that
@@ -480,7 +481,7 @@ def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(D, "D", f32, (dim,), dev),
         _ptr(z, "z", act, (batch, dim, L), dev),
         _ptr(delta_bias, "delta_bias", f32, (dim,), dev),
-        _flags(delta_softplus, False),
+        _flags(delta_softplus, zoh_b),
         _ptr(h0, "h0", f32, (batch, dim, N), dev),
         _ptr(y, "y", act, (batch, dim, L), dev),
         _ptr(h_final, "h_final", f32, (batch, dim, N), dev),
@@ -493,8 +494,9 @@ def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                  delta_softplus=True, h0=None, dy=None, dh_final=None,
                  want_dz=True, want_dh0=True, out=None, workspace=None,
-                 stream=None, saved=False):
-    """Gradients of :func:`ssm_scan_fwd` (Euler input term) for a loss with
+                 stream=None, saved=False, zoh_b=False):
+    """Gradients of :func:`ssm_scan_fwd` (Euler input term, or exact ZOH
+    with ``zoh_b``) for a loss with
     gradient ``dy`` (batch, dim, L; activation dtype) with respect to y and
     ``dh_final`` (batch, dim, N; fp32, or None) with respect to the final
     state.  Returns a dict: du, ddelta (activation dtype), dA, dB, dC, dD,
@@ -540,7 +542,7 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(D, "D", f32, (dim,), dev),
         _ptr(z, "z", act, (batch, dim, L), dev),
         _ptr(delta_bias, "delta_bias", f32, (dim,), dev),
-        _flags(delta_softplus, False) | (SSM_FLAG_BWD_SAVED if saved else 0),
+        _flags(delta_softplus, zoh_b) | (SSM_FLAG_BWD_SAVED if saved else 0),
         _ptr(h0, "h0", f32, (batch, dim, N), dev),
         _ptr(dy, "dy", act, (batch, dim, L), dev),
         _ptr(dh_final, "dh_final", f32, (batch, dim, N), dev),

@@ -326,9 +326,6 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
     return fail(SSM_ERR_INVALID_ARG, "y overlaps h_final");
 
   if (saved) {
-    if (flags & SSM_FLAG_ZOH_B)
-      return fail(SSM_ERR_UNSUPPORTED,
-                  "saving for the backward: the backward implements the Euler input term only");
     if (requested_chunk != 0)
       return fail(SSM_ERR_INVALID_ARG, "saving for the backward runs whole sequences "
                                        "(requested_chunk must be 0)");
@@ -533,8 +530,6 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
     return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (flags & ~(kKnownFlags | SSM_FLAG_BWD_SAVED))
     return fail(SSM_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
-  if (flags & SSM_FLAG_ZOH_B)
-    return fail(SSM_ERR_UNSUPPORTED, "the backward pass implements the Euler input term only");
   int st = check_bwd_sizes(batch, dim, dstate, seqlen);
   if (st != SSM_OK) return st;
 
@@ -604,7 +599,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   fa.batch = batch; fa.dim = dim; fa.L = seqlen;
   fa.chunk_len = seqlen; fa.n_chunks = 1;
   fa.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
-  fa.zoh = 0;
+  fa.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
   fa.ckpt = ckpt;
   int err = saved ? 0 : ssm::launch_scan(fa, bf16, vec, stream);
   if (err != 0)
@@ -626,6 +621,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   a.groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
   a.nblk = static_cast<int>((seqlen + ssm::kBlockTokens - 1) / ssm::kBlockTokens);
   a.softplus = fa.softplus;
+  a.zoh = fa.zoh;
   err = ssm::launch_bwd(a, bf16, vec, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));

@@ -1,5 +1,5 @@
 // ssm_bwd.hip -- gfx950 (CDNA4) kernels of the selective scan's backward
-// pass (Euler input term).
+// pass (Euler or exact zero-order-hold input term).
 //
 // Gradients of a loss with respect to u, delta (before softplus), A, B, C,
 // D, z, the delta bias and the initial state, given its gradients dy and
@@ -107,7 +107,7 @@ __device__ __forceinline__ float set_state(float v, int lane, int n, float x) {
 // K: tokens per lane.  Full blocks use kTokensPerLane; the partial last
 // block uses the fewest of 4, 8, 16 that cover it, so its loops cost about
 // its share of a block.
-template <typename T, bool kVec, bool kFull, bool kSoftplus, int K = kTokensPerLane>
+template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kZoh, int K = kTokensPerLane>
 __device__ __forceinline__ void bwd_block(
     const BwdArgs &p, int wave, int lane, int64_t t0, int64_t tend, int64_t b,
     int64_t bd, int64_t g, const T *__restrict__ Bb, const T *__restrict__ Cb,
@@ -165,7 +165,7 @@ __device__ __forceinline__ void bwd_block(
       }
       if (!kFull) v = (tl + j < tend) ? v : 0.0f;  // identity step
       dtl[j] = v * kLog2e;
-      du[j] = v * uu[j];
+      du[j] = kZoh ? uu[j] : v * uu[j];  // ZOH: the coefficient carries dt
       sdt += v;
       us[j] = uu[j] * sgm;
       sg[j] = sgm;
@@ -236,10 +236,14 @@ __device__ __forceinline__ void bwd_block(
     // forward recomputation of this lane's 16 states:
     // hin = the state before the lane's first token, hs[j] = after token j
     float a[K], hs[K];
+    const float inv_a = kZoh ? 1.0f / An : 0.0f;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      a[j] = fast_exp2(dtl[j] * An);
-      hs[j] = du[j] * bv[j];  // dt B u, replaced by the state below
+      const float arg = dtl[j] * An;
+      a[j] = fast_exp2(arg);
+      // the input term (dt B u, or the ZOH coefficient times B u), replaced
+      // by the state below
+      hs[j] = kZoh ? zoh_coeff(arg, a[j], dtl[j], inv_a) * (du[j] * bv[j]) : du[j] * bv[j];
     }
     float H = hs[0];
 #pragma unroll
@@ -278,12 +282,30 @@ __device__ __forceinline__ void bwd_block(
 #pragma unroll
     for (int j = K - 1; j >= 0; --j) {
       const float lam = fmaf(gc[j], cv[j], m);
-      s1[j] = fmaf(lam, bv[j], s1[j]);
+      const float hprev = j > 0 ? hs[j - 1] : hin;
       m = a[j] * lam;                                  // lambda a
-      const float q = m * (j > 0 ? hs[j - 1] : hin);   // lambda a h_{j-1}
-      s2[j] = fmaf(q, An, s2[j]);
+      const float q = m * hprev;                       // lambda a h_{j-1}
       dA_acc = fmaf(q, dtl[j], dA_acc);
-      reg[region_index(wave, 0, j, lane)] = lam * du[j];
+      if constexpr (kZoh) {
+        // c = (exp(dt A) - 1)/A recomputed; dc/ddt = a, dc/dA = (dt a -
+        // c)/A, or dt^2 (1/2 + x/3 + x^2/8 + x^3/30), x = dt A, where |dt
+        // A| < 2^-5 ln2 (the series branch of zoh_coeff); here du = u
+        const float arg = dtl[j] * An;
+        const float c = zoh_coeff(arg, a[j], dtl[j], inv_a);
+        const float bu = bv[j] * du[j];
+        s1[j] = fmaf(lam, c * bv[j], s1[j]);            // sum lambda c B
+        s2[j] = fmaf(m, fmaf(An, hprev, bu), s2[j]);    // sum lambda a (A h + B u)
+        const float dt = dtl[j] * kLn2;
+        const float x = arg * kLn2;
+        const float ser = dt * dt * fmaf(x, fmaf(x, fmaf(x, 1.0f / 30.0f, 0.125f), 1.0f / 3.0f), 0.5f);
+        const float dcda = fabsf(arg) < 0x1p-5f ? ser : (fmaf(dt, a[j], -c) * inv_a);
+        dA_acc = fmaf(lam * bu, dcda * kLog2e, dA_acc);  // accumulated in log2 units
+        reg[region_index(wave, 0, j, lane)] = lam * (c * du[j]);
+      } else {
+        s1[j] = fmaf(lam, bv[j], s1[j]);
+        s2[j] = fmaf(q, An, s2[j]);
+        reg[region_index(wave, 0, j, lane)] = lam * du[j];
+      }
       reg[region_index(wave, 1, j, lane)] = gc[j] * hs[j];
     }
     float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
@@ -298,10 +320,12 @@ __device__ __forceinline__ void bwd_block(
   // sum lambda B + sum lambda a h_prev A) * sigmoid(delta + bias)
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const float dx = fmaf(us[j], s1[j], s2[j] * sg[j]);
+    // Euler: ddt = u * sum lambda B + sum lambda a A h_prev, du = dt * sum
+    // lambda B; ZOH: ddt = sum lambda a (A h_prev + B u), du = sum lambda c B
+    const float dx = kZoh ? s2[j] * sg[j] : fmaf(us[j], s1[j], s2[j] * sg[j]);
     dbl += (kFull || tl + j < tend) ? dx : 0.0f;
-    s1[j] = fmaf(dtl[j] * kLn2, s1[j], gc[j] * Dd);  // du
-    s2[j] = dx;                                       // ddelta
+    s1[j] = kZoh ? fmaf(gc[j], Dd, s1[j]) : fmaf(dtl[j] * kLn2, s1[j], gc[j] * Dd);  // du
+    s2[j] = dx;                                                                        // ddelta
   }
   if (ch_ok) {
     store_run<T, K, kVec, kFull>(static_cast<T *>(p.du) + bd * p.L, t0, tl, tend, s1);
@@ -309,7 +333,7 @@ __device__ __forceinline__ void bwd_block(
   }
 }
 
-template <typename T, bool kVec, bool kSoftplus>
+template <typename T, bool kVec, bool kSoftplus, bool kZoh>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs p) {
   __shared__ float sT[2 * kBwdTileFloats];  // one state's B, C (fp32), double-buffered
@@ -341,21 +365,21 @@ void bwd_kernel(BwdArgs p) {
   if (rem > 0) {  // the partial last block comes first
     const float hf = ck[nfull * kStates + ls];
     if (rem <= 4 * kWaveLanes)
-      bwd_block<T, false, false, kSoftplus, 4>(p, wave, lane, nfull * kBlockTokens, p.L, b,
+      bwd_block<T, false, false, kSoftplus, kZoh, 4>(p, wave, lane, nfull * kBlockTokens, p.L, b,
                                                bd, g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv,
                                                dAv, dDl, dbl, sT, sR, tid);
     else if (rem <= 8 * kWaveLanes)
-      bwd_block<T, false, false, kSoftplus, 8>(p, wave, lane, nfull * kBlockTokens, p.L, b,
+      bwd_block<T, false, false, kSoftplus, kZoh, 8>(p, wave, lane, nfull * kBlockTokens, p.L, b,
                                                bd, g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv,
                                                dAv, dDl, dbl, sT, sR, tid);
     else
-      bwd_block<T, false, false, kSoftplus>(p, wave, lane, nfull * kBlockTokens, p.L, b, bd,
+      bwd_block<T, false, false, kSoftplus, kZoh>(p, wave, lane, nfull * kBlockTokens, p.L, b, bd,
                                             g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv, dAv,
                                             dDl, dbl, sT, sR, tid);
   }
 #pragma unroll 1
   for (int64_t k = nfull - 1; k >= 0; --k)
-    bwd_block<T, kVec, true, kSoftplus>(p, wave, lane, k * kBlockTokens,
+    bwd_block<T, kVec, true, kSoftplus, kZoh>(p, wave, lane, k * kBlockTokens,
                                         (k + 1) * kBlockTokens, b, bd, g, Bb, Cb, ch_ok, bias,
                                         Dd, Av, ck[k * kStates + ls], muv, dAv, dDl, dbl, sT,
                                         sR, tid);
@@ -479,10 +503,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_param_kernel(BwdArgs p) {
 template <typename T, bool kVec>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.groups), static_cast<unsigned>(a.batch));
-  if (a.softplus)
-    hipLaunchKernelGGL((bwd_kernel<T, kVec, true>), grid, dim3(kBwdThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_kernel<T, kVec, false>), grid, dim3(kBwdThreads), 0, s, a);
+  using Fn = void (*)(BwdArgs);
+  static constexpr Fn kernels[4] = {bwd_kernel<T, kVec, false, false>,
+                                    bwd_kernel<T, kVec, true, false>,
+                                    bwd_kernel<T, kVec, false, true>,
+                                    bwd_kernel<T, kVec, true, true>};
+  hipLaunchKernelGGL(kernels[(a.softplus ? 1 : 0) | (a.zoh ? 2 : 0)], grid,
+                     dim3(kBwdThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nwg = a.batch * kStates * ((a.L + kReduceTokens - 1) / kReduceTokens);

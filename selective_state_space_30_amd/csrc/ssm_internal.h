@@ -59,6 +59,7 @@ struct BwdArgs {
   int64_t groups;                     // ceil(dim / kBwdWaves)
   int nblk;                           // ceil(L / 1024)
   int softplus;
+  int zoh;                            // 1: exact ZOH input term
 };
 
 // Mamba-2 SSD forward (one scalar decay per head; bf16 activations).

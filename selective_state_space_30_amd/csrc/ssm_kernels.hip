@@ -449,11 +449,14 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
       scan_kernel<T, kVec, false, false, true>,  scan_kernel<T, kVec, true, false, true>,
       scan_kernel<T, kVec, false, true, true>,   scan_kernel<T, kVec, true, true, true>};
   const int which = (a.softplus ? 1 : 0) | (a.x ? 2 : 0) | (a.zoh ? 4 : 0);
-  // the backward's checkpoint pass (Euler, no conv prologue, unsplit) has
+  // the backward's checkpoint pass (no conv prologue, unsplit) has
   // instances of its own, so the forward instances carry none of its code
-  static constexpr KernelFn ckpt_kernels[2] = {scan_kernel<T, kVec, false, false, false, true>,
-                                               scan_kernel<T, kVec, true, false, false, true>};
-  hipLaunchKernelGGL(a.ckpt ? ckpt_kernels[a.softplus ? 1 : 0] : kernels[which], grid,
+  static constexpr KernelFn ckpt_kernels[4] = {scan_kernel<T, kVec, false, false, false, true>,
+                                               scan_kernel<T, kVec, true, false, false, true>,
+                                               scan_kernel<T, kVec, false, false, true, true>,
+                                               scan_kernel<T, kVec, true, false, true, true>};
+  hipLaunchKernelGGL(a.ckpt ? ckpt_kernels[(a.softplus ? 1 : 0) | (a.zoh ? 2 : 0)]
+                            : kernels[which], grid,
                      dim3(kWaveLanes * kWavesPerGroup), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;

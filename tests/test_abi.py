@@ -298,8 +298,8 @@ INVALID_BWD_CASES = [
     ("null dB", dict(dB=None), 1),
     ("null dC", dict(dC=None), 1),
     ("dz without z", dict(dz=FAKE + 0x70000000), 1),
-    ("zoh flag", dict(flags=3), 2),
-    ("zoh flag with saved", dict(flags=7), 2),
+    ("zoh flag, null dy", dict(flags=3, dy=None), 1),
+    ("zoh flag with saved, small workspace", dict(flags=7, ws_bytes=4096), 3),
     ("unknown flag", dict(flags=8), 1),
     ("dstate 8", dict(dstate=8), 2),
     ("zero seqlen", dict(seqlen=0), 1),
@@ -347,7 +347,7 @@ INVALID_SAVE_CASES = [
     ("workspace misaligned", dict(ws=FAKE + 6 * 0x08000000 + 64), 1),
     ("workspace overlaps y", dict(ws=FAKE + 5 * 0x08000000 + 256), 1),
     ("y overlaps u", dict(y=FAKE + 64), 1),
-    ("zoh flag", dict(flags=3), 2),
+    ("zoh flag, null y", dict(flags=3, y=None), 1),
     ("backward-only flag", dict(flags=5), 1),
     ("dstate 8", dict(dstate=8), 2),
     ("zero seqlen", dict(seqlen=0), 1),

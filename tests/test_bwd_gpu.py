@@ -276,3 +276,55 @@ def test_bwd_more_than_2_31_elements():
             check(got[k][sl], ref[k], 2e-2, "%s (b=%d, d=%d)" % (k, b, d))
         check(got["dA"][d], ref["dA"][0], 1e-4, "dA[%d]" % d)
     assert torch.isfinite(got["dB"]).all() and torch.isfinite(got["dC"]).all()
+
+
+# ------------------------------------------- exact zero-order-hold input term
+ZOH_CASES = [
+    # (batch, dim, L, dtype, A kind)
+    (2, 13, 2100, "f32", "arange"),     # ragged tail, partial block of 52
+    (1, 8, 1024, "f32", "zero_cols"),   # some A = 0: the Euler limit, dc/dA = dt^2/2
+    (1, 5, 777, "f32", "small"),        # |dt A| mostly below 2^-5: the series
+    (2, 20, 3072, "bf16", "arange"),
+]
+
+
+@pytest.mark.parametrize("case", ZOH_CASES, ids=lambda c: "b%d_d%d_l%d_%s_%s" % c)
+def test_bwd_zoh_matches_oracle(case):
+    """Gradients with the exact ZOH input term (the Guide Complet's section
+    1 coefficient (exp(dt A) - 1)/A) against the oracle's, pinned by finite
+    differences in test_oracle_bwd_pins.py."""
+    batch, dim, L, dt, akind = case
+    inp = make(batch, dim, L, dt, 900 + L + dim)
+    if akind == "zero_cols":
+        inp["A"][:, ::3] = 0.0
+    elif akind == "small":
+        inp["A"] = inp["A"] * 1e-3
+    ref = oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"],
+                          inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                          True, inp["h0"], inp["dy"], inp["dh_final"],
+                          zoh_b=True)
+    d = to_dev(inp)
+    got = ssm.ssm_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                           d["z"], d["delta_bias"], True, d["h0"], d["dy"],
+                           d["dh_final"], zoh_b=True)
+    torch.cuda.synchronize()
+    tol = TOL[dt]
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dh0", "dD", "ddelta_bias", "dz"):
+        check(got[k], ref[k], tol, k)
+    # the training pair: the ZOH forward that keeps the checkpoints, then the
+    # backward that reuses them, gives the same gradients and outputs
+    y, hf, ws = ssm.ssm_scan_fwd_save(d["u"], d["delta"], d["A"], d["B"],
+                                      d["C"], d["D"], d["z"], d["delta_bias"],
+                                      True, d["h0"], zoh_b=True)
+    got2 = ssm.ssm_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                            d["z"], d["delta_bias"], True, d["h0"], d["dy"],
+                            d["dh_final"], zoh_b=True, workspace=ws,
+                            saved=True)
+    y_ref, h_ref = oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"],
+                               inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                               True, True, inp["h0"])
+    torch.cuda.synchronize()
+    check(y, y_ref, tol, "y (saving forward)")
+    check(hf, h_ref, tol, "h_final (saving forward)")
+    for k in got:
+        assert torch.equal(got2[k], got[k]), k
