@@ -18,6 +18,8 @@ and state at a time).  This module only marshals numpy arrays into it:
 * :func:`causal_conv1d_silu` -- the depthwise causal convolution and SiLU
   that produce the scan's input u inside the Mamba block (the Guide
   Complet's section 4 architecture figure and section 7 block).
+* :func:`causal_conv1d_silu_bwd` -- its gradients with respect to x, the
+  taps and the conv bias.
 * :func:`scan_bwd` -- gradients of :func:`scan` (Euler or exact-ZOH input
   term) by the chain rule through the recurrence, in reverse token order.
 * :func:`ssd` -- the Mamba-2 "state space dual" form with one scalar decay
@@ -79,6 +81,9 @@ def _load():
         lib.oracle_causal_conv1d_silu_f64.argtypes = [P, P, P, I64, P, I64,
                                                       I64, I64]
         lib.oracle_causal_conv1d_silu_f64.restype = I
+        lib.oracle_causal_conv1d_silu_bwd_f64.argtypes = [P, P, P, I64, P, P,
+                                                          P, P, I64, I64, I64]
+        lib.oracle_causal_conv1d_silu_bwd_f64.restype = I
         lib.oracle_scan_bwd_f64.argtypes = [P] * 8 + [I, I] + [P] * 12 + [I64] * 4
         lib.oracle_scan_bwd_f64.restype = I
         lib.oracle_ssd_f64.argtypes = [P] * 8 + [I] + [P] * 3 + [I64] * 6
@@ -121,6 +126,28 @@ def causal_conv1d_silu(x, w, bias=None):
     if rc != 0:
         raise ValueError("oracle_causal_conv1d_silu_f64 rejected its arguments")
     return u
+
+
+def causal_conv1d_silu_bwd(x, w, bias, du):
+    """Gradients of :func:`causal_conv1d_silu` for a loss whose gradient
+    with respect to u is ``du``.  Returns ``(dx, dw, db)`` (db None when
+    ``bias`` is None) as fp64 arrays."""
+    x = _f64(x)
+    batch, dim, L = x.shape
+    w = _f64(w)
+    K = w.shape[1]
+    w = _f64(w, (dim, K))
+    bias = _f64(bias, (dim,))
+    du = _f64(du, (batch, dim, L))
+    dx = np.empty((batch, dim, L))
+    dw = np.empty((dim, K))
+    db = np.empty(dim) if bias is not None else None
+    rc = _load().oracle_causal_conv1d_silu_bwd_f64(
+        _ptr(x), _ptr(w), _ptr(bias), K, _ptr(du), _ptr(dx), _ptr(dw),
+        _ptr(db), batch, dim, L)
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d_silu_bwd_f64 rejected its arguments")
+    return dx, dw, db
 
 
 def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,

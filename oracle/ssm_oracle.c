@@ -172,6 +172,59 @@ static double oracle_dsilu(double z)
     return s * (1.0 + z * (1.0 - s));
 }
 
+int oracle_causal_conv1d_silu_bwd_f64(const double *x, const double *w,
+                                      const double *bias, int64_t K,
+                                      const double *du, double *dx, double *dw,
+                                      double *db, int64_t batch, int64_t dim,
+                                      int64_t seqlen)
+{
+    if (!x || !w || !du || !dx || !dw || K < 1 || batch < 0 || dim < 0 || seqlen < 0)
+        return -1;
+    double *g = malloc(sizeof(double) * (size_t)(seqlen + 1));
+    if (!g)
+        return -1;
+    memset(dw, 0, sizeof(double) * (size_t)(dim * K));
+    if (db)
+        memset(db, 0, sizeof(double) * (size_t)dim);
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const double *xr = x + (b * dim + d) * seqlen;
+            const double *dur = du + (b * dim + d) * seqlen;
+            double *dxr = dx + (b * dim + d) * seqlen;
+            /* g_t = du_t silu'(pre_t), the pre-activation recomputed */
+            for (int64_t t = 0; t < seqlen; ++t) {
+                double pre = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    int64_t s = t - (K - 1) + k;
+                    if (s >= 0)
+                        pre += w[d * K + k] * xr[s];
+                }
+                g[t] = dur[t] * oracle_dsilu(pre);
+            }
+            for (int64_t s = 0; s < seqlen; ++s) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    int64_t t = s + (K - 1) - k;   /* the outputs x[s] feeds */
+                    if (t < seqlen)
+                        acc += w[d * K + k] * g[t];
+                }
+                dxr[s] = acc;
+            }
+            for (int64_t t = 0; t < seqlen; ++t) {
+                for (int64_t k = 0; k < K; ++k) {
+                    int64_t s = t - (K - 1) + k;
+                    if (s >= 0)
+                        dw[d * K + k] += g[t] * xr[s];
+                }
+                if (db)
+                    db[d] += g[t];
+            }
+        }
+    }
+    free(g);
+    return 0;
+}
+
 /* Derivatives of the input coefficient c(dt, a) of oracle_input_coeff:
  * *dc_ddt = dc/ddt and *dc_da = dc/da.  Euler: c = dt, so 1 and 0.  ZOH:
  * c = (exp(dt a) - 1)/a, dc/ddt = exp(dt a), dc/da = (dt exp(dt a) - c)/a;

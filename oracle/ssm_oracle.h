@@ -82,6 +82,20 @@ int oracle_causal_conv1d_silu_f64(const double *x, const double *w,
                                   const double *bias, int64_t K, double *u,
                                   int64_t batch, int64_t dim, int64_t seqlen);
 
+/* Gradients of oracle_causal_conv1d_silu_f64 for a loss whose gradient
+ * with respect to u is du: with pre_t = bias + sum_k w[k] x[t-(K-1)+k] and
+ * g_t = du_t * silu'(pre_t),
+ *   dx[s]   = sum_k w[k] g_{s+(K-1)-k}   (terms with s+(K-1)-k < seqlen)
+ *   dw[d,k] = sum_{b,t} g_t x[t-(K-1)+k]  (x = 0 before t = 0)
+ *   db[d]   = sum_{b,t} g_t
+ * dx: (batch, dim, seqlen); dw: (dim, K), db: (dim) or NULL, overwritten.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_causal_conv1d_silu_bwd_f64(const double *x, const double *w,
+                                      const double *bias, int64_t K,
+                                      const double *du, double *dx, double *dw,
+                                      double *db, int64_t batch, int64_t dim,
+                                      int64_t seqlen);
+
 /* Gradients of the full scan, by the chain rule applied to the recurrence
  * above, token by token in reverse.  The loss is any scalar whose gradient
  * with respect to y is dy and with respect to h_final is dh_final (NULL ->

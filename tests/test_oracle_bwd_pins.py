@@ -197,3 +197,70 @@ def test_zoh_gradients_tend_to_euler_as_A_vanishes():
             continue
         scale = 1.0 + np.max(np.abs(ge[k]))
         assert np.max(np.abs(gz[k] - ge[k])) <= 1e-7 * scale, k
+
+
+# ------------------------------------------------- conv prologue gradients
+@pytest.mark.parametrize("K,with_bias", [(4, True), (3, False), (1, True)],
+                         ids=["k4_bias", "k3", "k1_bias"])
+def test_conv_bwd_finite_differences_every_element(K, with_bias):
+    """oracle.causal_conv1d_silu_bwd against central differences of the
+    forward conv oracle (pinned to numpy.convolve) for L = sum du * u."""
+    r = np.random.default_rng(30 + K)
+    batch, dim, L = 2, 3, 9
+    x = r.normal(size=(batch, dim, L))
+    w = r.normal(size=(dim, K))
+    b = r.normal(size=dim) if with_bias else None
+    du = r.normal(size=(batch, dim, L))
+    dx, dw, db = oracle.causal_conv1d_silu_bwd(x, w, b, du)
+
+    def f():
+        return float(np.sum(du * oracle.causal_conv1d_silu(x, w, b)))
+    eps = 1e-6
+    for arr, grad in ((x, dx), (w, dw)) + (((b, db),) if with_bias else ()):
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + eps
+            lp = f()
+            arr[idx] = keep - eps
+            lm = f()
+            arr[idx] = keep
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * (1.0 + abs(grad[idx])), (idx, fd, grad[idx])
+    if not with_bias:
+        assert db is None
+
+
+def test_conv_then_scan_chain_rule_finite_differences():
+    """The whole Mamba prologue + scan: y = scan(u = silu(conv(x))); the
+    gradient with respect to x, the taps and the conv bias is the conv
+    backward applied to the scan backward's du, checked by central
+    differences of the composed forward oracles."""
+    r = np.random.default_rng(41)
+    batch, dim, N, L, K = 1, 2, 4, 7, 4
+    x = r.normal(size=(batch, dim, L))
+    w = r.normal(size=(dim, K)) * 0.5
+    cb = r.normal(size=dim) * 0.1
+    inp, dy, dhf = make(42, batch, dim, N, L)
+
+    def f():
+        u = oracle.causal_conv1d_silu(x, w, cb)
+        y, hf = oracle.scan(u, inp["delta"], inp["A"], inp["B"], inp["C"],
+                            inp["D"], inp["z"], inp["delta_bias"], True, False,
+                            inp["h0"])
+        return float(np.sum(dy * y) + np.sum(dhf * hf))
+    u = oracle.causal_conv1d_silu(x, w, cb)
+    g = oracle.scan_bwd(u, inp["delta"], inp["A"], inp["B"], inp["C"],
+                        inp["D"], inp["z"], inp["delta_bias"], True,
+                        inp["h0"], dy, dhf)
+    dx, dw, db = oracle.causal_conv1d_silu_bwd(x, w, cb, g["du"])
+    eps = 1e-6
+    for arr, grad in ((x, dx), (w, dw), (cb, db)):
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + eps
+            lp = f()
+            arr[idx] = keep - eps
+            lm = f()
+            arr[idx] = keep
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * (1.0 + abs(grad[idx])), (idx, fd, grad[idx])
