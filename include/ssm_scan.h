@@ -324,6 +324,46 @@ int ssm_scan_fwd_save(const void *u, const void *delta, const float *A,
                       int64_t dstate, int64_t seqlen, int dtype, void *bwd_workspace,
                       size_t bwd_workspace_bytes, void *stream);
 
+/* Bytes of caller-provided device workspace ssm_conv_scan_bwd needs: that
+ * of ssm_scan_bwd_workspace_size for the same shape and dtype, then u and
+ * its gradient (batch*dim*seqlen each, activation dtype) and batch*dim*5
+ * fp32 per-row sums of the conv's gradients. */
+int ssm_conv_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                     int64_t seqlen, int dtype, size_t *bytes);
+
+/* Backward pass of ssm_conv_scan_fwd: the gradients of ssm_scan_bwd, with
+ * the gradient of u carried back through the SiLU and the depthwise causal
+ * convolution of the Mamba block's prologue ("Mamba & State Space Models -
+ * Guide Complet", section 4 architecture figure and section 7):
+ *   pre_t    = conv_b + sum_k conv_w[k] x_{t-d_conv+1+k},  u_t = silu(pre_t)
+ *   g_t      = du_t silu'(pre_t)       (du_t as ssm_scan_bwd defines it)
+ *   dx_s     = sum_k conv_w[k] g_{s+d_conv-1-k}
+ *   dconv_w[d,k] = sum_b,t g_t x_{t-d_conv+1+k},  dconv_b[d] = sum_b,t g_t
+ * u is formed again from x into the workspace (in the activation dtype: for
+ * bf16 runs it is the forward's fp32 u rounded to nearest even) and the
+ * scan's backward runs on it.
+ *  x, conv_w, conv_b, d_conv     as for ssm_conv_scan_fwd
+ *  delta ... dh_final, flags     as for ssm_scan_bwd (SSM_FLAG_BWD_SAVED is
+ *                                refused: there is no saving conv forward)
+ *  dx                required output, activation dtype (batch, dim, seqlen)
+ *  dconv_w           required output fp32 (dim, d_conv)
+ *  dconv_b           nullable output fp32 (dim)
+ *  ddelta ... dh0    as for ssm_scan_bwd (du is replaced by dx)
+ *  workspace         >= ssm_conv_scan_bwd_workspace_size() bytes, 256-byte
+ *                    aligned
+ * Conventions, limits and errors as for ssm_scan_bwd; every check runs
+ * before the first kernel is enqueued. */
+int ssm_conv_scan_bwd(const void *x, const float *conv_w, const float *conv_b,
+                      int d_conv, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D,
+                      const void *z, const float *delta_bias, unsigned flags,
+                      const float *h0, const void *dy, const float *dh_final,
+                      void *dx, float *dconv_w, float *dconv_b, void *ddelta,
+                      float *dA, float *dB, float *dC, float *dD,
+                      float *ddelta_bias, void *dz, float *dh0, int64_t batch,
+                      int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of caller-provided device workspace ssm_ssd_fwd needs: per chunk of
  * 64 tokens and group, the causal G = C^T B (64 x 64, as two bf16 arrays:
  * the value and its rounding error) and C transposed (64 x dstate bf16). */

@@ -24,6 +24,8 @@ Names follow the C ABI:
   checkpoints; :func:`ssm_scan_bwd_workspace_size`;
   :func:`ssm_scan_fwd_save`, the forward that keeps those checkpoints for
   the backward (which then skips its own checkpoint pass).
+* :func:`ssm_conv_scan_bwd` -- gradients of :func:`ssm_conv_scan_fwd`,
+  through the conv prologue as well; :func:`ssm_conv_scan_bwd_workspace_size`.
 * :func:`ssm_scan_plan`, :func:`ssm_scan_workspace_size`,
   :func:`ssm_last_error`, :func:`ssm_abi_version`.
 * :func:`ssm_roofline_hbm`, :func:`ssm_roofline_valu` -- microbenchmarks of
@@ -55,7 +57,8 @@ EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
            "ssm_conv_state_update",
            "ssm_scan_bwd_workspace_size", "ssm_scan_fwd_save", "ssm_scan_bwd",
            "ssm_ssd_workspace_size", "ssm_ssd_fwd", "ssm_last_error",
-           "ssm_roofline_hbm", "ssm_roofline_valu", "ssm_scan_fwd_noalloc")
+           "ssm_roofline_hbm", "ssm_roofline_valu", "ssm_scan_fwd_noalloc",
+           "ssm_conv_scan_bwd_workspace_size", "ssm_conv_scan_bwd")
 SCAN_SCRATCH_BYTES = 16 << 20  # the fixed scratch of ssm_scan_fwd_noalloc
 SSM_ROOFLINE_HBM_QUANTUM = 16384
 SSM_ROOFLINE_VALU_QUANTUM = 256
@@ -123,6 +126,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                           [I64, I64, I64, I64, I, P,
                                            ctypes.c_size_t, P])
         lib.ssm_scan_fwd_save.restype = I
+        lib.ssm_conv_scan_bwd_workspace_size.argtypes = [
+            I64, I64, I64, I64, I, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssm_conv_scan_bwd_workspace_size.restype = I
+        lib.ssm_conv_scan_bwd.argtypes = ([P, P, P, I] + [P] * 7 + [U] +
+                                          [P] * 14 + [I64] * 4 +
+                                          [I, P, ctypes.c_size_t, P])
+        lib.ssm_conv_scan_bwd.restype = I
         lib.ssm_ssd_workspace_size.argtypes = [
             I64, I64, I64, I64, ctypes.POINTER(ctypes.c_size_t)]
         lib.ssm_ssd_workspace_size.restype = I
@@ -548,6 +558,79 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(dh_final, "dh_final", f32, (batch, dim, N), dev),
         p["du"], p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"],
         p["ddelta_bias"], p.get("dz"), p.get("dh0"),
+        batch, dim, N, L, code, workspace.data_ptr(), wsn,
+        _stream_handle(dev, stream)))
+    return {k: out[k] for k in shapes}
+
+
+def ssm_conv_scan_bwd_workspace_size(batch, dim, dstate, seqlen,
+                                     dtype=torch.bfloat16) -> int:
+    out = ctypes.c_size_t(0)
+    code = SSM_DTYPE_BF16 if dtype == torch.bfloat16 else SSM_DTYPE_F32
+    _check(load_library().ssm_conv_scan_bwd_workspace_size(
+        batch, dim, dstate, seqlen, code, ctypes.byref(out)))
+    return out.value
+
+
+@_on_stream
+def ssm_conv_scan_bwd(x, conv_w, delta, A, B, C, D=None, z=None,
+                      delta_bias=None, delta_softplus=True, h0=None, dy=None,
+                      dh_final=None, conv_b=None, want_dz=True, want_dh0=True,
+                      out=None, workspace=None, stream=None, zoh_b=False):
+    """Gradients of :func:`ssm_conv_scan_fwd` for a loss with gradient
+    ``dy`` with respect to y and ``dh_final`` with respect to the final
+    state.  Returns a dict: dx, ddelta (activation dtype), dconv_w, dconv_b
+    (when conv_b is given), dA, dB, dC, dD, ddelta_bias, dh0 (fp32) and dz
+    (when z is given)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, dim, L)")
+    if dy is None:
+        raise ValueError("dy is required")
+    batch, dim, L = x.shape
+    N = A.shape[-1] if A.dim() == 2 else 0
+    K = conv_w.shape[-1] if conv_w.dim() == 2 else 0
+    dev = x.device
+    act = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    out = dict(out or {})
+    shapes = {"dx": ((batch, dim, L), act), "ddelta": ((batch, dim, L), act),
+              "dconv_w": ((dim, K), f32),
+              "dA": ((dim, N), f32), "dB": ((batch, N, L), f32),
+              "dC": ((batch, N, L), f32), "dD": ((dim,), f32),
+              "ddelta_bias": ((dim,), f32)}
+    if conv_b is not None:
+        shapes["dconv_b"] = ((dim,), f32)
+    if z is not None and want_dz:
+        shapes["dz"] = ((batch, dim, L), act)
+    if want_dh0:
+        shapes["dh0"] = ((batch, dim, N), f32)
+    for k, (shp, dt) in shapes.items():
+        if k not in out:
+            out[k] = torch.empty(shp, dtype=dt, device=dev)
+    p = {k: _ptr(out[k], k, shapes[k][1], shapes[k][0], dev) for k in shapes}
+    if workspace is None:
+        workspace = torch.empty(
+            ssm_conv_scan_bwd_workspace_size(batch, dim, N, L, act),
+            dtype=torch.uint8, device=dev)
+    wsn = workspace.numel() * workspace.element_size()
+    _check(load_library().ssm_conv_scan_bwd(
+        _ptr(x, "x", act, (batch, dim, L), dev),
+        _ptr(conv_w, "conv_w", f32, (dim, K), dev),
+        _ptr(conv_b, "conv_b", f32, (dim,), dev), K,
+        _ptr(delta, "delta", act, (batch, dim, L), dev),
+        _ptr(A, "A", f32, (dim, N), dev),
+        _ptr(B, "B", act, (batch, N, L), dev),
+        _ptr(C, "C", act, (batch, N, L), dev),
+        _ptr(D, "D", f32, (dim,), dev),
+        _ptr(z, "z", act, (batch, dim, L), dev),
+        _ptr(delta_bias, "delta_bias", f32, (dim,), dev),
+        _flags(delta_softplus, zoh_b),
+        _ptr(h0, "h0", f32, (batch, dim, N), dev),
+        _ptr(dy, "dy", act, (batch, dim, L), dev),
+        _ptr(dh_final, "dh_final", f32, (batch, dim, N), dev),
+        p["dx"], p["dconv_w"], p.get("dconv_b"), p["ddelta"], p["dA"],
+        p["dB"], p["dC"], p["dD"], p["ddelta_bias"], p.get("dz"), p.get("dh0"),
         batch, dim, N, L, code, workspace.data_ptr(), wsn,
         _stream_handle(dev, stream)))
     return {k: out[k] for k in shapes}

@@ -45,7 +45,7 @@ def _run(cmd):
 
 
 HIP_SOURCES = ["ssm_kernels.hip", "ssm_step.hip", "ssm_bwd.hip", "ssm_ssd.hip",
-               "ssm_roofline.hip"]
+               "ssm_roofline.hip", "ssm_conv_bwd.hip"]
 
 
 def build(verbose: bool = False) -> str:

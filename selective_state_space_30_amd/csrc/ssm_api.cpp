@@ -515,14 +515,22 @@ int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
   return ok();
 }
 
-int ssm_scan_bwd(const void *u, const void *delta, const float *A,
-                 const void *B, const void *C, const float *D, const void *z,
-                 const float *delta_bias, unsigned flags, const float *h0,
-                 const void *dy, const float *dh_final, void *du, void *ddelta,
-                 float *dA, float *dB, float *dC, float *dD,
-                 float *ddelta_bias, void *dz, float *dh0, int64_t batch,
-                 int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// ssm_scan_bwd's checks and launches; check_only: the checks alone (no HIP
+// call), so a caller that runs other kernels first can validate everything
+// before its first launch.
+int scan_bwd_impl(const void *u, const void *delta, const float *A,
+                  const void *B, const void *C, const float *D, const void *z,
+                  const float *delta_bias, unsigned flags, const float *h0,
+                  const void *dy, const float *dh_final, void *du, void *ddelta,
+                  float *dA, float *dB, float *dC, float *dD,
+                  float *ddelta_bias, void *dz, float *dh0, int64_t batch,
+                  int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                  void *workspace, size_t workspace_bytes, void *stream,
+                  bool check_only) {
   if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
     return fail(SSM_ERR_INVALID_ARG, "required pointer is NULL");
   if (dz && !z) return fail(SSM_ERR_INVALID_ARG, "dz given without z");
@@ -579,6 +587,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
     if (overlaps(workspace, static_cast<int64_t>(l.total_bytes), o.p, o.n))
       return fail(SSM_ERR_INVALID_ARG, "workspace overlaps output %s", o.name);
 
+  if (check_only) return SSM_OK;
   bool vec = (seqlen * es) % 16 == 0;
   for (const void *p : acts)
     if (p && !aligned(p, 16)) vec = false;
@@ -623,6 +632,148 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
   a.softplus = fa.softplus;
   a.zoh = fa.zoh;
   err = ssm::launch_bwd(a, bf16, vec, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_bwd(const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z,
+                 const float *delta_bias, unsigned flags, const float *h0,
+                 const void *dy, const float *dh_final, void *du, void *ddelta,
+                 float *dA, float *dB, float *dC, float *dD,
+                 float *ddelta_bias, void *dz, float *dh0, int64_t batch,
+                 int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, h0, dy, dh_final, du,
+                       ddelta, dA, dB, dC, dD, ddelta_bias, dz, dh0, batch, dim, dstate,
+                       seqlen, dtype, workspace, workspace_bytes, stream, false);
+}
+
+// Workspace of ssm_conv_scan_bwd: the scan backward's, then u and its
+// gradient (activation dtype) and the per-row conv sums, 256-byte aligned.
+struct ConvBwdLayout {
+  size_t off_u, off_du, off_part, total_bytes;
+};
+
+static ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t es) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t big = static_cast<size_t>(batch) * dim * seqlen * es;
+  ConvBwdLayout l;
+  l.off_u = up(ssm::bwd_layout(batch, dim, seqlen, es).total_bytes);
+  l.off_du = up(l.off_u + big);
+  l.off_part = up(l.off_du + big);
+  l.total_bytes = up(l.off_part + static_cast<size_t>(batch) * dim * (ssm::kMaxConv + 1) *
+                                      sizeof(float));
+  return l;
+}
+
+int ssm_conv_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                     int64_t seqlen, int dtype, size_t *bytes) {
+  size_t b0 = 0;
+  const int st = ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen, dtype, &b0);
+  if (st != SSM_OK) return st;
+  if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = conv_bwd_layout(batch, dim, seqlen, dtype == SSM_DTYPE_BF16 ? 2 : 4).total_bytes;
+  return ok();
+}
+
+int ssm_conv_scan_bwd(const void *x, const float *conv_w, const float *conv_b,
+                      int d_conv, const void *delta, const float *A, const void *B,
+                      const void *C, const float *D, const void *z,
+                      const float *delta_bias, unsigned flags, const float *h0,
+                      const void *dy, const float *dh_final, void *dx,
+                      float *dconv_w, float *dconv_b, void *ddelta, float *dA,
+                      float *dB, float *dC, float *dD, float *ddelta_bias, void *dz,
+                      float *dh0, int64_t batch, int64_t dim, int64_t dstate,
+                      int64_t seqlen, int dtype, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!x || !conv_w || !dx || !dconv_w)
+    return fail(SSM_ERR_INVALID_ARG, "required pointer is NULL (x, conv_w, dx, dconv_w)");
+  if (d_conv < 1 || d_conv > ssm::kMaxConv)
+    return fail(d_conv < 1 ? SSM_ERR_INVALID_ARG : SSM_ERR_UNSUPPORTED,
+                "d_conv=%d: supported 1..%d", d_conv, ssm::kMaxConv);
+  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & SSM_FLAG_BWD_SAVED)
+    return fail(SSM_ERR_INVALID_ARG, "SSM_FLAG_BWD_SAVED: the conv backward has no saving forward");
+  int st = check_bwd_sizes(batch, dim, dstate, seqlen);
+  if (st != SSM_OK) return st;
+  const int64_t es = dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(dx, es))
+    return fail(SSM_ERR_INVALID_ARG, "x or dx not %lld-byte aligned", (long long)es);
+  const void *f32s[] = {conv_w, conv_b, dconv_w, dconv_b};
+  for (const void *p : f32s)
+    if (p && !aligned(p, 4))
+      return fail(SSM_ERR_INVALID_ARG, "fp32 pointer %p not 4-byte aligned", p);
+  const ConvBwdLayout l = conv_bwd_layout(batch, dim, seqlen, es);
+  if (!workspace || workspace_bytes < l.total_bytes)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu bytes at %p)",
+                l.total_bytes, workspace_bytes, workspace);
+  if (!aligned(workspace, 256))
+    return fail(SSM_ERR_INVALID_ARG, "workspace %p not 256-byte aligned", workspace);
+  const int64_t big = batch * dim * seqlen * es;
+  const int64_t bc = batch * dstate * seqlen * es;
+  const int64_t sts = batch * dim * dstate * 4;
+  const int64_t ws = static_cast<int64_t>(l.total_bytes);
+  // the conv's own arrays against each other and the workspace (the scan
+  // backward's checks below cover the rest, with u and du in the workspace)
+  const struct { const void *p; int64_t n; const char *name; } ins[] = {
+      {x, big, "x"}, {conv_w, dim * d_conv * 4, "conv_w"}, {conv_b, conv_b ? dim * 4 : 0, "conv_b"},
+      {delta, big, "delta"}, {z, big, "z"}, {dy, big, "dy"}, {B, bc, "B"}, {C, bc, "C"},
+      {A, dim * dstate * 4, "A"}, {D, dim * 4, "D"}, {delta_bias, dim * 4, "delta_bias"},
+      {h0, sts, "h0"}, {dh_final, sts, "dh_final"}};
+  const struct { const void *p; int64_t n; const char *name; } outs[] = {
+      {dx, big, "dx"}, {dconv_w, dim * d_conv * 4, "dconv_w"},
+      {dconv_b, dconv_b ? dim * 4 : 0, "dconv_b"}};
+  for (const auto &o : outs) {
+    for (const auto &in : ins)
+      if (overlaps(o.p, o.n, in.p, in.n))
+        return fail(SSM_ERR_INVALID_ARG, "%s overlaps input %s", o.name, in.name);
+    if (overlaps(o.p, o.n, workspace, ws))
+      return fail(SSM_ERR_INVALID_ARG, "%s overlaps the workspace", o.name);
+    const void *sc[] = {ddelta, dA, dB, dC, dD, ddelta_bias, dz, dh0};
+    const int64_t scn[] = {big, dim * dstate * 4, batch * dstate * seqlen * 4,
+                           batch * dstate * seqlen * 4, dim * 4, dim * 4, big, sts};
+    for (int i = 0; i < 8; ++i)
+      if (overlaps(o.p, o.n, sc[i], scn[i]))
+        return fail(SSM_ERR_INVALID_ARG, "%s overlaps another gradient", o.name);
+  }
+  if (overlaps(dx, big, dconv_w, dim * d_conv * 4) ||
+      overlaps(dx, big, dconv_b, conv_b ? dim * 4 : 0) ||
+      overlaps(dconv_w, dim * d_conv * 4, dconv_b, dconv_b ? dim * 4 : 0))
+    return fail(SSM_ERR_INVALID_ARG, "dx, dconv_w and dconv_b overlap");
+  for (const auto &in : ins)
+    if (overlaps(workspace, ws, in.p, in.n))
+      return fail(SSM_ERR_INVALID_ARG, "workspace overlaps input %s", in.name);
+  char *w = static_cast<char *>(workspace);
+  void *u = w + l.off_u;
+  void *du = w + l.off_du;
+  const size_t bwd_bytes = l.off_u;  // the scan backward's part comes first
+  st = scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, h0, dy, dh_final, du, ddelta,
+                     dA, dB, dC, dD, ddelta_bias, dz, dh0, batch, dim, dstate, seqlen, dtype,
+                     workspace, bwd_bytes, stream, true);
+  if (st != SSM_OK) return st;
+
+  ssm::ConvBwdArgs c{};
+  c.x = x; c.conv_w = conv_w; c.conv_b = conv_b; c.d_conv = d_conv;
+  c.u = u; c.du = du; c.dx = dx;
+  c.part = reinterpret_cast<float *>(w + l.off_part);
+  c.dconv_w = dconv_w; c.dconv_b = dconv_b;
+  c.batch = batch; c.dim = dim; c.L = seqlen;
+  const bool bf16 = dtype == SSM_DTYPE_BF16;
+  int err = ssm::launch_conv_fwd(c, bf16, stream);
+  if (err != 0)
+    return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
+  st = scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, h0, dy, dh_final, du, ddelta,
+                     dA, dB, dC, dD, ddelta_bias, dz, dh0, batch, dim, dstate, seqlen, dtype,
+                     workspace, bwd_bytes, stream, false);
+  if (st != SSM_OK) return st;
+  err = ssm::launch_conv_bwd(c, bf16, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
   return ok();

@@ -62,6 +62,21 @@ struct BwdArgs {
   int zoh;                            // 1: exact ZOH input term
 };
 
+// Backward of the conv prologue (ssm_conv_bwd.hip): u formed into the
+// workspace for the scan's backward, then dx and the taps' and bias's
+// gradients from its du.
+struct ConvBwdArgs {
+  const void *x;                      // (batch, dim, L) activation dtype
+  const float *conv_w, *conv_b;       // (dim, d_conv), (dim) or null
+  int d_conv;                         // 1..4
+  void *u;                            // workspace: (batch, dim, L) activation dtype
+  const void *du;                     // the scan's gradient of u (activation dtype)
+  void *dx;                           // output (batch, dim, L) activation dtype
+  float *part;                        // workspace: (batch, dim, 5) per-row sums
+  float *dconv_w, *dconv_b;           // outputs (dim, d_conv), (dim) or null
+  int64_t batch, dim, L;
+};
+
 // Mamba-2 SSD forward (one scalar decay per head; bf16 activations).
 constexpr int kSsdChunk = 64;        // tokens per chunk
 constexpr int kSsdHeadDim = 64;      // rows (headdim) per head
@@ -112,6 +127,8 @@ int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream);
 int launch_step(const StepArgs &a, bool bf16, bool vec, void *stream);
 int launch_bwd(const BwdArgs &a, bool bf16, bool vec, void *stream);
 int launch_ssd(const SsdArgs &a, bool vec, void *stream);
+int launch_conv_fwd(const ConvBwdArgs &a, bool bf16, void *stream);
+int launch_conv_bwd(const ConvBwdArgs &a, bool bf16, void *stream);
 // Roofline microbenchmarks (ssm_roofline.hip): n16 16-byte pieces per pass.
 int launch_roofline_hbm(int kind, void *a, void *b, int64_t n16, int repeats,
                         void *stream);

@@ -514,3 +514,58 @@ def test_noalloc_scratch_limit_matches_the_workspace_size():
     assert 0 < ok <= ssm.SCAN_SCRATCH_BYTES
     assert ssm.ssm_scan_workspace_size(64, 1024, 16, 128 * 1024, 1024) > \
         ssm.SCAN_SCRATCH_BYTES
+
+
+def _conv_bwd(lib, **kw):
+    names = ["x", "w", "delta", "A", "B", "C", "dy", "dx", "dw", "ddelta",
+             "dA", "dB", "dC", "ws"]
+    step = 0x08000000
+    a = {n: FAKE + i * step for i, n in enumerate(names)}
+    a.update(cb=None, d_conv=4, D=None, z=None, bias=None, flags=1, h0=None,
+             dh_final=None, db=None, dD=None, dbias=None, dz=None, dh0=None,
+             batch=1, dim=16, dstate=16, seqlen=256,
+             dtype=ssm.SSM_DTYPE_F32, stream=None)
+    size = ctypes.c_size_t(0)
+    assert lib.ssm_conv_scan_bwd_workspace_size(1, 16, 16, 256, 0,
+                                                ctypes.byref(size)) == 0
+    a["ws_bytes"] = size.value
+    a.update(kw)
+    return lib.ssm_conv_scan_bwd(
+        a["x"], a["w"], a["cb"], a["d_conv"], a["delta"], a["A"], a["B"],
+        a["C"], a["D"], a["z"], a["bias"], a["flags"], a["h0"], a["dy"],
+        a["dh_final"], a["dx"], a["dw"], a["db"], a["ddelta"], a["dA"],
+        a["dB"], a["dC"], a["dD"], a["dbias"], a["dz"], a["dh0"], a["batch"],
+        a["dim"], a["dstate"], a["seqlen"], a["dtype"], a["ws"], a["ws_bytes"],
+        a["stream"])
+
+
+INVALID_CONV_BWD_CASES = [
+    ("null x", dict(x=None), 1),
+    ("null conv_w", dict(w=None), 1),
+    ("null dx", dict(dx=None), 1),
+    ("null dconv_w", dict(dw=None), 1),
+    ("zero taps", dict(d_conv=0), 1),
+    ("five taps", dict(d_conv=5), 2),
+    ("saved flag", dict(flags=5), 1),
+    ("null workspace", dict(ws=None), 3),
+    ("workspace too small", dict(ws_bytes=4096), 3),
+    ("dx overlaps x", dict(dx=FAKE + 64), 1),
+    ("null dy (scan backward's check)", dict(dy=None), 1),
+    ("dstate 8", dict(dstate=8), 2),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", INVALID_CONV_BWD_CASES,
+                         ids=[c[0] for c in INVALID_CONV_BWD_CASES])
+def test_conv_bwd_rejects_invalid_arguments(lib, name, kw, status):
+    assert _conv_bwd(lib, **kw) == status, name
+    assert lib.ssm_last_error().decode()
+
+
+def test_conv_bwd_workspace_size(lib):
+    a = ctypes.c_size_t(0)
+    b = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(2, 64, 16, 3000, 1, ctypes.byref(a)) == 0
+    assert lib.ssm_conv_scan_bwd_workspace_size(2, 64, 16, 3000, 1, ctypes.byref(b)) == 0
+    # u and du in bf16 plus the per-row sums, on top of the scan backward's
+    assert b.value >= a.value + 2 * (2 * 64 * 3000 * 2) + 2 * 64 * 5 * 4
