@@ -276,7 +276,9 @@ def ceilings(torch, ssm, dev, stream, log):
     in-place read-modify-write and a read-only pass over 1 GiB buffers (4x
     the 256 MB last-level cache), best of 5 timings of 10 passes each.
     VALU: lane-operations per second of chains of v_exp_f32, of v_fma_f32
-    and of both interleaved, over 8 waves per SIMD, best of 5."""
+    and of both interleaved, over 8 waves per SIMD, best of 5 timings of 20
+    launches each (about a quarter of a second of sustained VALU issue in
+    all, right before the scan's warm-up steps)."""
     log("ceilings: HBM copy / read-modify-write / read over 1 GiB, "
         "v_exp_f32 and v_fma_f32 issue rates")
     out = {}
@@ -303,16 +305,18 @@ def ceilings(torch, ssm, dev, stream, log):
     torch.cuda.empty_cache()
     threads = 256 * 4 * 8 * 64      # 8 waves on each of the 1024 SIMDs
     iters = 4096
+    launches = 20                   # per timing: ~10-20 ms of sustained issue
     vout = torch.empty(threads, device=dev)
     for kind in ("exp", "fma", "mixed"):
         ssm.ssm_roofline_valu(kind, vout, iters, stream=stream)
         best = None
         for _ in range(5):
             e0.record(stream)
-            ssm.ssm_roofline_valu(kind, vout, iters, stream=stream)
+            for _ in range(launches):
+                ssm.ssm_roofline_valu(kind, vout, iters, stream=stream)
             e1.record(stream)
             torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3
+            t = e0.elapsed_time(e1) * 1e-3 / launches
             best = t if best is None else min(best, t)
         out[kind + "_lane_ops_per_s"] = threads * iters * 8 / best
     # the mixed chains take half of each kind: if a transcendental overlapped
@@ -561,8 +565,41 @@ def bwd_measure(ssm, syn, dev, stream, reps, log):
     e1.record(stream)
     torch.cuda.synchronize()
     pair_ms = e0.elapsed_time(e1) / reps
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    # the same backward with the exact-ZOH input term
+    zoh_ms = timed(lambda: ssm.ssm_scan_bwd(
+        binp["u"], binp["delta"], binp["A"], binp["B"], binp["C"], binp["D"],
+        binp["z"], binp["delta_bias"], True, None, bdy, None, out=bout,
+        workspace=bws, stream=stream, zoh_b=True))
+    # through the conv prologue (x in place of u, width 4)
+    cinp = syn.make_conv_inputs(ccfg, dev)
+    cws = torch.empty(ssm.ssm_conv_scan_bwd_workspace_size(
+        ccfg.batch, ccfg.dim, 16, ccfg.seqlen, binp["u"].dtype),
+        dtype=torch.uint8, device=dev)
+    cout = ssm.ssm_conv_scan_bwd(cinp["x"], cinp["conv_w"], cinp["delta"],
+                                 cinp["A"], cinp["B"], cinp["C"], cinp["D"],
+                                 cinp["z"], cinp["delta_bias"], True, None,
+                                 bdy, None, conv_b=cinp["conv_b"],
+                                 workspace=cws, stream=stream)
+    conv_ms = timed(lambda: ssm.ssm_conv_scan_bwd(
+        cinp["x"], cinp["conv_w"], cinp["delta"], cinp["A"], cinp["B"],
+        cinp["C"], cinp["D"], cinp["z"], cinp["delta_bias"], True, None, bdy,
+        None, conv_b=cinp["conv_b"], out=cout, workspace=cws, stream=stream))
+    del cinp, cws, cout
     nb = syn.backward_bytes(ccfg)
     return {"ms_per_call": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+            "zoh_ms_per_call": round(zoh_ms, 4),
+            "conv_prologue_ms_per_call": round(conv_ms, 4),
             "elements_per_s": round(ccfg.elements / (ms * 1e-3)),
             "algorithmic_bytes": nb, "workspace_bytes": bws.numel(),
             "fwd_save_plus_bwd_saved_ms": round(pair_ms, 4),
@@ -570,7 +607,10 @@ def bwd_measure(ssm, syn, dev, stream, reps, log):
                     "recomputed from 1024-token checkpoints (ms_per_call: "
                     "the backward alone, with its own checkpoint pass; "
                     "fwd_save_plus_bwd_saved_ms: ssm_scan_fwd_save then "
-                    "ssm_scan_bwd reusing its checkpoints)"}
+                    "ssm_scan_bwd reusing its checkpoints; zoh_ms_per_call: "
+                    "with the exact-ZOH input term; "
+                    "conv_prologue_ms_per_call: ssm_conv_scan_bwd, x and the "
+                    "width-4 conv in place of u)"}
 
 
 N_DECODE_STATES = 8
@@ -781,6 +821,10 @@ def _cpu_model():
 # not the checkpoint pass
 SCAN_KERNEL = "scan_kernel<unsigned short, true, true, false, false, false>"
 CKPT_KERNEL = "scan_kernel<unsigned short, true, true, false, false, true>"
+# the Euler backward sweep (bf16, vector loads, softplus, no ZOH); the
+# --only-bwd run also times the ZOH and conv-prologue backward, whose
+# kernels are left out of that summary
+BWD_KERNEL = "bwd_kernel<unsigned short, true, true, false>"
 COPY_KERNEL = "roof_copy_kernel"
 COPY_BYTES = 1 << 30  # each calibration copy reads and writes 1 GiB
 
@@ -1017,10 +1061,10 @@ def summarize_extras(d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace,
                  "written, taps and conv bias read")
     out += summarize_workload(
         d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace, prof,
-        title="backward, workload %s (checkpoint pass, sweep, reductions)"
-              % bcfg.name,
+        title="backward, workload %s (checkpoint pass, sweep, reductions; "
+              "Euler input term)" % bcfg.name,
         fname="bwd_kernels_%s.txt" % bcfg.name,
-        keys=["bwd_", CKPT_KERNEL], tag="bwd", only="only-bwd",
+        keys=[BWD_KERNEL, "bwd_reduce", CKPT_KERNEL], tag="bwd", only="only-bwd",
         alg_bytes=syn.backward_bytes(bcfg),
         alg_note="inputs and dy read, gradients written once; the per-group "
                  "partial sums of dB and dC are extra by design")
