@@ -19,7 +19,8 @@
 // kFactorLimit (base 2) the factors cannot overflow fp32 or bf16; a chunk
 // with a steeper decay forms M = G o exp(a_t - a_s) dt_s element by element.
 // G and the carried state enter the products as a pair of bf16 values (the
-// value and its rounding error), so that neither is rounded to bf16 alone.
+// value and its rounding error), so that neither is rounded to bf16 alone;
+// so do G's columns scaled by v_s (and M), x being taken as it is stored.
 // All products run on v_mfma_f32_16x16x32_bf16 (A operand: lane l, element
 // e = A[l%16][8*(l/16)+e]; B: B[8*(l/16)+e][l%16]; result: lane l, element
 // e = D[4*(l/16)+e][l%16], checked on the hardware).
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
 // Each wave reads its own rows of C^T and G (the y products) and of B (the
 // state update), so those go from memory straight into operand registers;
 // the next chunk's are requested right after the last use.  LDS holds what
-// the waves share, double-buffered by chunk parity: x, x v and x w, z then
+// the waves share, double-buffered by chunk parity: x and x w, z then
 // y, the state entering the chunk (a bf16 pair); and the step quantities of
 // three chunks (chunk c+2's are formed during chunk c by wave (c+2) mod 4).
 //
@@ -212,7 +213,6 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   // (group g of row r at g ^ (r % 8)) so that 8 rows read at one group hit
   // 8 different bank sets.
   __shared__ __align__(16) __bf16 Xs[2][R * T];         // [p][t]: x_t
-  __shared__ __align__(16) __bf16 XVs[2][R * T];        // [p][t]: x_t v_t
   __shared__ __align__(16) __bf16 XWs[2][2][R * T];     // [p][t]: x_t w_t, hi, lo
   __shared__ __align__(16) __bf16 Zs[2][R * T];         // [p][t]: z, then y
   __shared__ __align__(16) __bf16 Ss[2][2][R * N];      // [p][n]: entering state, hi, lo
@@ -372,9 +372,9 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     q[5][lane] = fast_exp2(aend - a) * v;        // weight of token s in the new state
     return !__any(!(fabsf(a - aref) <= kFactorLimit));
   };
-  // x, x v, x w and z of a chunk into the LDS buffers of parity `buf` (the
+  // x, x w and z of a chunk into the LDS buffers of parity `buf` (the
   // step quantities q were just written by this wave, in order)
-  auto deposit = [&](bool factored, int buf, float (*q)[T]) __attribute__((always_inline)) {
+  auto deposit = [&](int buf, float (*q)[T]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kXQ; ++i) {
       const int pc = tid + kThreads * i, r = pc / (T / 8), t8 = (pc % (T / 8)) * 8;
@@ -399,16 +399,6 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
         }
         *reinterpret_cast<bf16x8 *>(&XWs[buf][0][at(r, t8)]) = o;
         *reinterpret_cast<bf16x8 *>(&XWs[buf][1][at(r, t8)]) = lo;
-        if (factored) {
-          const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&q[4][t8]);
-          const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&q[4][t8 + 4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] = static_cast<__bf16>(static_cast<float>(xv[e]) * v0[e]);
-            o[e + 4] = static_cast<__bf16>(static_cast<float>(xv[e + 4]) * v1[e]);
-          }
-          *reinterpret_cast<bf16x8 *>(&XVs[buf][at(r, t8)]) = o;
-        }
       }
     }
   };
@@ -463,7 +453,7 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
       Wf[0] = f0;
       Wf[1] = f1;
     }
-    deposit(f0, 0, Wq[0]);
+    deposit(0, Wq[0]);
   }
   uint16_t dtn = load_dt(2);
   load_xz(nch > 1 ? 1 : 0);
@@ -501,14 +491,14 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     __syncthreads();
     const bool factored = __builtin_amdgcn_readfirstlane(Wf[q0]) != 0;
     // 2. the previous chunk's y out; chunk c+2's step quantities (one
-    //    wave); the next chunk's x w, x v and z in (x and z were requested
+    //    wave); the next chunk's x w and z in (x and z were requested
     //    a chunk ago)
     if (c > 0) read_y(nxt);
     if (wave == ((c + 2) & 3) && c + 2 < nch) {
       const bool f = steps(dtn, t0 + 2 * T, Wq[q2]);
       if (lane == 0) Wf[q2] = f;
     }
-    if (more) deposit(__builtin_amdgcn_readfirstlane(Wf[q1]) != 0, nxt, Wq[q1]);
+    if (more) deposit(nxt, Wq[q1]);
     if (c > 0) store_y(c - 1);
     if (more) {
       dtn = load_dt(c + 3);
@@ -535,16 +525,30 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     load_ct(cn);
     const int nks = tt < 2 ? 1 : 2;
     if (factored) {
-      // u_t (G (X diag v)^T)[t, p]
+      // u_t ((G diag v) X^T)[t, p]: the columns of G (this lane's row ta,
+      // tokens s) scaled by v_s in fp32 and split into a bf16 pair, so that
+      // x enters the product exactly and nothing is rounded to one bf16
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        if (ks < nks)
+        if (ks < nks) {
+          const int s0 = 32 * ks + kq;
+          const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&q[4][s0]);
+          const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&q[4][s0 + 4]);
+          bf16x8 gh, gl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float gv = (static_cast<float>(ga[0][ks][e]) + static_cast<float>(ga[1][ks][e])) *
+                             (e < 4 ? v0[e] : v1[e - 4]);
+            gh[e] = static_cast<__bf16>(gv);
+            gl[e] = static_cast<__bf16>(gv - static_cast<float>(gh[e]));
+          }
 #pragma unroll
           for (int pt = 0; pt < RPW; ++pt) {
-            const bf16x8 xv = lds8(&XVs[cur][at(pr + 16 * pt + li, 32 * ks + kq)]);
-            ad[pt] = mfma(ga[0][ks], xv, ad[pt]);
-            ad2[pt] = mfma(ga[1][ks], xv, ad2[pt]);
+            const bf16x8 xs = lds8(&Xs[cur][at(pr + 16 * pt + li, s0)]);
+            ad[pt] = mfma(gh, xs, ad[pt]);
+            ad2[pt] = mfma(gl, xs, ad2[pt]);
           }
+        }
     } else {
       // M[t, s] = G[t, s] exp(a_t - a_s) dt_s formed in the operand
       // registers
@@ -553,16 +557,21 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
       for (int ks = 0; ks < 2; ++ks)
         if (ks < nks) {
           const int s0 = 32 * ks + kq;
-          bf16x8 m;
+          bf16x8 m, ml;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float ex = s0 + e <= ta ? Aq * (ct - q[1][s0 + e]) : -INFINITY;
             const float gv = static_cast<float>(ga[0][ks][e]) + static_cast<float>(ga[1][ks][e]);
-            m[e] = static_cast<__bf16>(gv * fast_exp2(ex) * q[0][s0 + e]);
+            const float mv = gv * fast_exp2(ex) * q[0][s0 + e];
+            m[e] = static_cast<__bf16>(mv);
+            ml[e] = static_cast<__bf16>(mv - static_cast<float>(m[e]));
           }
 #pragma unroll
-          for (int pt = 0; pt < RPW; ++pt)
-            ad[pt] = mfma(m, lds8(&Xs[cur][at(pr + 16 * pt + li, s0)]), ad[pt]);
+          for (int pt = 0; pt < RPW; ++pt) {
+            const bf16x8 xs = lds8(&Xs[cur][at(pr + 16 * pt + li, s0)]);
+            ad[pt] = mfma(m, xs, ad[pt]);
+            ad2[pt] = mfma(ml, xs, ad2[pt]);
+          }
         }
     }
     load_g(cn);

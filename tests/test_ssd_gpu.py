@@ -7,7 +7,8 @@ computation (A broadcast over the states; the two oracles are pinned to
 each other), which is linear in L.
 
 Bar: 2e-2 on the scaled error (bf16 activations; the chunk products take
-bf16 operands with fp32 accumulation, the carried state is fp32).
+bf16 operands -- G, the state, G's decay-scaled columns and x w as bf16
+pairs -- with fp32 accumulation, the carried state is fp32).
 """
 import numpy as np
 import pytest
@@ -48,6 +49,7 @@ CASES = [
     (2, 2, 1, 128, 333, 0, 1, 1),    # L % 8 != 0: element-wise loads
     (1, 2, 2, 64, 1, 1, 1, 1),       # a single token
     (1, 4, 4, 128, 512, 1, 1, 0),    # one head per group, 8 chunks
+    (1, 8, 1, 128, 1024, 1, 1, 1),   # 8 heads on one group, 16 chunks
 ]
 
 
