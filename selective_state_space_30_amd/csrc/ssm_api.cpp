@@ -103,6 +103,38 @@ int64_t choose_chunk(int64_t batch, int64_t dim, int64_t seqlen, int64_t request
   return chunk >= seqlen ? seqlen : chunk;
 }
 
+// Tokens per chunk of the backward's sweep: the whole sequence while the
+// channels alone give every SIMD two rounds of its 2 resident waves;
+// otherwise the count of block-aligned chunks (of at least kMinBwdChunk
+// tokens, at most kMaxBwdChunks) that minimises rounds x chunk length, the
+// fewest within 5 % of that minimum (each chunk after the first costs an
+// adjoint pre-pass over its decay horizon).
+constexpr int64_t kMinBwdChunk = 8192;
+constexpr int64_t kMaxBwdChunks = 16;
+int64_t bwd_chunk(int64_t batch, int64_t dim, int64_t seqlen) {
+  const int64_t slots = 2 * kSimds;
+  const int64_t waves = batch * ((dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves) * ssm::kBwdWaves;
+  if (waves >= 2 * slots || seqlen < 2 * kMinBwdChunk) return seqlen;
+  struct Pick { int64_t chunk; double cost; };
+  Pick best{seqlen, static_cast<double>((waves + slots - 1) / slots)};  // unsplit
+  Pick picks[kMaxBwdChunks];
+  int np = 0;
+  for (int64_t n = 2; n <= kMaxBwdChunks; ++n) {
+    const int64_t chunk = round_up((seqlen + n - 1) / n, ssm::kBlockTokens);
+    if (chunk < kMinBwdChunk) break;
+    const int64_t nc = (seqlen + chunk - 1) / chunk;
+    const double cost = static_cast<double>((waves * nc + slots - 1) / slots) *
+                        static_cast<double>(chunk) / static_cast<double>(seqlen);
+    picks[np++] = Pick{chunk, cost};
+    if (cost < best.cost) best = Pick{chunk, cost};
+  }
+  const double unsplit = static_cast<double>((waves + slots - 1) / slots);
+  if (unsplit <= 1.05 * best.cost) return seqlen;
+  for (int i = 0; i < np; ++i)  // fewest chunks (longest chunk) first
+    if (picks[i].cost <= 1.05 * best.cost) return picks[i].chunk;
+  return best.chunk;
+}
+
 }  // namespace
 
 namespace ssm {
@@ -113,14 +145,40 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t elem_by
   const size_t groups = static_cast<size_t>((dim + kBwdWaves - 1) / kBwdWaves);
   const size_t part = static_cast<size_t>(batch) * groups * kStates * seqlen * sizeof(float);
   BwdLayout l;
+  l.ckpt_chunk = choose_chunk(batch, dim, seqlen, 0);
+  l.ckpt_chunks = (seqlen + l.ckpt_chunk - 1) / l.ckpt_chunk;
+  l.chunk = bwd_chunk(batch, dim, seqlen);
+  l.n_chunks = (seqlen + l.chunk - 1) / l.chunk;
+  const size_t nc = static_cast<size_t>(l.n_chunks);
+  const size_t ncc = static_cast<size_t>(l.ckpt_chunks);
   l.off_ckpt = 0;
   l.off_yc = up(l.off_ckpt + bd * nblk * kStates * sizeof(float));
   l.off_pB = up(l.off_yc + bd * static_cast<size_t>(seqlen) * elem_bytes);
   l.off_pC = up(l.off_pB + part);
   l.off_pA = up(l.off_pC + part);
-  l.off_pD = up(l.off_pA + bd * kStates * sizeof(float));
-  l.off_pbias = up(l.off_pD + bd * sizeof(float));
-  l.total_bytes = up(l.off_pbias + bd * sizeof(float));
+  l.off_pD = up(l.off_pA + bd * nc * kStates * sizeof(float));
+  l.off_pbias = up(l.off_pD + bd * nc * sizeof(float));
+  size_t end = up(l.off_pbias + bd * nc * sizeof(float));
+  // the split checkpoint pass: block dt sums, chunk end states, dt sums and
+  // incoming states
+  l.off_cks = l.off_H = l.off_S = l.off_hin = 0;
+  if (ncc > 1) {
+    l.off_cks = end;
+    l.off_H = up(l.off_cks + bd * nblk * sizeof(float));
+    l.off_S = up(l.off_H + bd * ncc * kStates * sizeof(float));
+    l.off_hin = up(l.off_S + bd * ncc * sizeof(float));
+    end = up(l.off_hin + bd * ncc * kStates * sizeof(float));
+  }
+  // the split sweep: the chunks' adjoints from a zero right input, their
+  // decay products, and the adjoints entering them
+  l.off_mu0 = l.off_Pc = l.off_muin = 0;
+  if (nc > 1) {
+    l.off_mu0 = end;
+    l.off_Pc = up(l.off_mu0 + bd * nc * kStates * sizeof(float));
+    l.off_muin = up(l.off_Pc + bd * nc * kStates * sizeof(float));
+    end = up(l.off_muin + bd * nc * kStates * sizeof(float));
+  }
+  l.total_bytes = end;
   return l;
 }
 
@@ -254,6 +312,10 @@ int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) 
   if (groups >= (int64_t(1) << 31) || !mul_ok(batch * groups, ssm::kStates * seqlen, &e) ||
       !mul_ok(e, 8, &e))
     return fail(SSM_ERR_UNSUPPORTED, "backward workspace of this shape overflows");
+  // the checkpoint pass's chunks are a grid dimension
+  const int64_t cc = choose_chunk(batch, dim, seqlen, 0);
+  if ((seqlen + cc - 1) / cc > kMaxGridYZ)
+    return fail(SSM_ERR_UNSUPPORTED, "seqlen too long for the backward's checkpoint pass");
   // the channel-sum reduction launches one workgroup per 256 tokens of each
   // (batch, state) row
   if (batch * ssm::kStates * ((seqlen + 255) / 256) >= (int64_t(1) << 31))
@@ -599,17 +661,25 @@ int scan_bwd_impl(const void *u, const void *delta, const float *A,
 
   // 1. checkpoint pass: the forward scan without the gate, keeping the
   //    block-start states and the pre-gate output (for dz); skipped when
-  //    ssm_scan_fwd_save already left them in this workspace
+  //    ssm_scan_fwd_save already left them in this workspace.  Split like
+  //    the forward when the channels are few (chunks scanned from a zero
+  //    state, chained, the pre-gate output and the checkpoints fixed up).
   const bool saved = (flags & SSM_FLAG_BWD_SAVED) != 0;
   ssm::ScanArgs fa{};
   fa.u = u; fa.delta = delta; fa.B = B; fa.C = C; fa.z = nullptr;
   fa.A = A; fa.D = D; fa.bias = delta_bias; fa.h0 = h0;
   fa.y = yc; fa.h_final = nullptr;
   fa.batch = batch; fa.dim = dim; fa.L = seqlen;
-  fa.chunk_len = seqlen; fa.n_chunks = 1;
+  fa.chunk_len = l.ckpt_chunk; fa.n_chunks = static_cast<int>(l.ckpt_chunks);
   fa.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
   fa.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
   fa.ckpt = ckpt;
+  if (l.ckpt_chunks > 1) {
+    fa.ckpt_s = reinterpret_cast<float *>(w + l.off_cks);
+    fa.ws_H = reinterpret_cast<float *>(w + l.off_H);
+    fa.ws_S = reinterpret_cast<float *>(w + l.off_S);
+    fa.ws_hin = reinterpret_cast<float *>(w + l.off_hin);
+  }
   int err = saved ? 0 : ssm::launch_scan(fa, bf16, vec, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));
@@ -631,6 +701,13 @@ int scan_bwd_impl(const void *u, const void *delta, const float *A,
   a.nblk = static_cast<int>((seqlen + ssm::kBlockTokens - 1) / ssm::kBlockTokens);
   a.softplus = fa.softplus;
   a.zoh = fa.zoh;
+  a.n_chunks = static_cast<int>(l.n_chunks);
+  a.chunk_len = l.chunk;
+  if (l.n_chunks > 1) {
+    a.mu0 = reinterpret_cast<float *>(w + l.off_mu0);
+    a.Pc = reinterpret_cast<float *>(w + l.off_Pc);
+    a.mu_in = reinterpret_cast<float *>(w + l.off_muin);
+  }
   err = ssm::launch_bwd(a, bf16, vec, stream);
   if (err != 0)
     return fail(SSM_ERR_HIP, "kernel launch failed: %s", ssm::hip_error_string(err));

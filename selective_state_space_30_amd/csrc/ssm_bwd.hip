@@ -31,6 +31,15 @@
 // write their contributions to LDS, the workgroup sums them in a fixed order
 // (no atomics: deterministic) into a per-workgroup partial sum, and a
 // reduction kernel sums the partials.
+//
+// Sequence split (few channels, long sequences): the tokens are cut into
+// block-aligned chunks swept in parallel.  The reverse recurrence is linear
+// in what enters a chunk from its right, so bwd_adj_kernel first finds, for
+// each chunk after the first, what it passes to its left from a zero right
+// input and its decay product (over its decay horizon only), and
+// bwd_adj_carry_kernel chains those from the last chunk to the first; each
+// chunk's sweep then starts from its true incoming dL/dh.  The checkpoints
+// come from the checkpoint pass, split the same way as the forward.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -344,14 +353,20 @@ void bwd_kernel(BwdArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t b = blockIdx.y;
   const int64_t g = blockIdx.x;
+  const int c = blockIdx.z;  // chunk
   const int64_t d_raw = g * kBwdWaves + wave;
   const bool ch_ok = d_raw < p.dim;
   const int64_t d = ch_ok ? d_raw : p.dim - 1;  // clamped for reads
   const int64_t bd = b * p.dim + d;
+  const int64_t bdc = bd * p.n_chunks + c;
   const int ls = lane < kStates ? lane : 0;  // lane n <-> state n
+  const int64_t ct0 = static_cast<int64_t>(c) * p.chunk_len;
+  const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
 
   const float Av = p.A[d * kStates + ls];
-  float muv = p.dh_final ? p.dh_final[bd * kStates + ls] : 0.0f;
+  // dL/dh entering the chunk's last token from the right
+  float muv = p.n_chunks > 1 ? p.mu_in[bdc * kStates + ls]
+                             : (p.dh_final ? p.dh_final[bd * kStates + ls] : 0.0f);
   float dAv = 0.0f;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
@@ -359,43 +374,128 @@ void bwd_kernel(BwdArgs p) {
   const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
   float dDl = 0.0f, dbl = 0.0f;
 
-  const float *ck = p.ckpt + bd * p.nblk * kStates;
-  const int64_t nfull = p.L / kBlockTokens;
-  const int64_t rem = p.L - nfull * kBlockTokens;
+  // the chunk's blocks (chunks start on block boundaries; only the last
+  // chunk can end in a partial block), last to first
+  const float *ck = p.ckpt + (bd * p.nblk + ct0 / kBlockTokens) * kStates;
+  const int64_t nfull = (ct1 - ct0) / kBlockTokens;
+  const int64_t rem = (ct1 - ct0) - nfull * kBlockTokens;
   if (rem > 0) {  // the partial last block comes first
     const float hf = ck[nfull * kStates + ls];
+    const int64_t t0 = ct0 + nfull * kBlockTokens;
     if (rem <= 4 * kWaveLanes)
-      bwd_block<T, false, false, kSoftplus, kZoh, 4>(p, wave, lane, nfull * kBlockTokens, p.L, b,
-                                               bd, g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv,
-                                               dAv, dDl, dbl, sT, sR, tid);
+      bwd_block<T, false, false, kSoftplus, kZoh, 4>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+                                                     ch_ok, bias, Dd, Av, hf, muv, dAv, dDl,
+                                                     dbl, sT, sR, tid);
     else if (rem <= 8 * kWaveLanes)
-      bwd_block<T, false, false, kSoftplus, kZoh, 8>(p, wave, lane, nfull * kBlockTokens, p.L, b,
-                                               bd, g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv,
-                                               dAv, dDl, dbl, sT, sR, tid);
+      bwd_block<T, false, false, kSoftplus, kZoh, 8>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+                                                     ch_ok, bias, Dd, Av, hf, muv, dAv, dDl,
+                                                     dbl, sT, sR, tid);
     else
-      bwd_block<T, false, false, kSoftplus, kZoh>(p, wave, lane, nfull * kBlockTokens, p.L, b, bd,
-                                            g, Bb, Cb, ch_ok, bias, Dd, Av, hf, muv, dAv,
-                                            dDl, dbl, sT, sR, tid);
+      bwd_block<T, false, false, kSoftplus, kZoh>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+                                                  ch_ok, bias, Dd, Av, hf, muv, dAv, dDl, dbl,
+                                                  sT, sR, tid);
   }
 #pragma unroll 1
   for (int64_t k = nfull - 1; k >= 0; --k)
-    bwd_block<T, kVec, true, kSoftplus, kZoh>(p, wave, lane, k * kBlockTokens,
-                                        (k + 1) * kBlockTokens, b, bd, g, Bb, Cb, ch_ok, bias,
-                                        Dd, Av, ck[k * kStates + ls], muv, dAv, dDl, dbl, sT,
-                                        sR, tid);
+    bwd_block<T, kVec, true, kSoftplus, kZoh>(p, wave, lane, ct0 + k * kBlockTokens,
+                                        ct0 + (k + 1) * kBlockTokens, b, bd, g, Bb, Cb, ch_ok,
+                                        bias, Dd, Av, ck[k * kStates + ls], muv, dAv, dDl, dbl,
+                                        sT, sR, tid);
 
   if (!ch_ok) return;
   if (lane < kStates) {
-    p.pA[bd * kStates + lane] = dAv * kLn2;  // sum of q * dt = q * dtl * ln2
-    if (p.dh0) p.dh0[bd * kStates + lane] = muv;
+    p.pA[bdc * kStates + lane] = dAv * kLn2;  // sum of q * dt = q * dtl * ln2
+    if (p.dh0 && c == 0) p.dh0[bd * kStates + lane] = muv;
   }
   float sD = lane_broadcast(wave_inclusive_sum(dDl), kWaveLanes - 1);
   float sb = lane_broadcast(wave_inclusive_sum(dbl), kWaveLanes - 1);
   asm volatile("" : "+s"(sD), "+s"(sb));  // formed by the whole wave first
   if (lane == 0) {
-    p.pD[bd] = sD;
-    p.pbias[bd] = sb;
+    p.pD[bdc] = sD;
+    p.pbias[bdc] = sb;
   }
+}
+
+// ------------------------------------------- sequence split: adjoints ---
+// Chunk c >= 1 swept with nothing entering from its right passes to its
+// left neighbour mu0 = sum_t D_t gc_t C_t, D_t = prod_{r = start..t} a_r =
+// exp(A S_t) with S_t the chunk's sum of dt up to and including t, and any
+// dL/dh mu entering from its right arrives decayed by the chunk's product
+// Pc = exp(A S): mu_left = mu0 + Pc mu (the reverse recurrence is linear).
+// One wave per (batch, channel, chunk >= 1), 64 tokens per step from the
+// chunk start; like the forward's fix-up, it stops once every D_t is below
+// 2^-40 when they cannot grow again (all A < 0, dt >= 0 under softplus),
+// leaving Pc at that (negligible) value.
+template <typename T>
+__global__ __launch_bounds__(64) void bwd_adj_kernel(BwdArgs p) {
+  const int lane = threadIdx.x;
+  const int64_t d = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int c = blockIdx.z + 1;
+  const int64_t bd = b * p.dim + d;
+  const int64_t ct0 = static_cast<int64_t>(c) * p.chunk_len;
+  const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
+  float Aq[kStates], acc[kStates];
+  float amax = -INFINITY;
+#pragma unroll
+  for (int n = 0; n < kStates; ++n) {
+    Aq[n] = p.A[d * kStates + n] * kLog2e;
+    acc[n] = 0.0f;
+    amax = fmaxf(amax, Aq[n]);
+  }
+  const bool may_stop = p.softplus && amax < 0.0f;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
+  const T *gyrow = static_cast<const T *>(p.dy) + bd * p.L;
+  const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
+  const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
+  float S = 0.0f;
+  for (int64_t t0 = ct0; t0 < ct1; t0 += 64) {
+    const int64_t t = t0 + lane;
+    const bool in = t < ct1;
+    float dt = 0.0f, gc = 0.0f;
+    if (in) {
+      const float x = to_f32<T>(drow[t]) + bias;
+      dt = p.softplus ? softplus_f(x) : x;
+      gc = to_f32<T>(gyrow[t]);
+      if (zrow) gc *= silu_f(to_f32<T>(zrow[t]));
+    }
+    const float St = S + wave_inclusive_sum(dt);
+#pragma unroll
+    for (int n = 0; n < kStates; ++n) {
+      const float cn = in ? to_f32<T>(Cb[n * p.L + t]) : 0.0f;
+      acc[n] = fmaf(fast_exp2(Aq[n] * St) * gc, cn, acc[n]);
+    }
+    S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(St), 63));
+    if (may_stop && fast_exp2(amax * S) <= 0x1p-40f) break;
+  }
+  const int64_t base = (bd * p.n_chunks + c) * kStates;
+#pragma unroll
+  for (int n = 0; n < kStates; ++n) {
+    float m = lane_broadcast(wave_inclusive_sum(acc[n]), kWaveLanes - 1);
+    asm volatile("" : "+s"(m));  // formed by the whole wave, then stored by lane 0
+    if (lane == 0) {
+      p.mu0[base + n] = m;
+      p.Pc[base + n] = fast_exp2(Aq[n] * S);
+    }
+  }
+}
+
+// One thread per (batch, channel, state): the dL/dh entering each chunk
+// from its right, from the last chunk (dh_final) to the first.
+__global__ __launch_bounds__(256) void bwd_adj_carry_kernel(BwdArgs p) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= p.batch * p.dim * kStates) return;
+  const int64_t bd = gid >> 4;
+  const int n = static_cast<int>(gid & 15);
+  const int nc = p.n_chunks;
+  float mu = p.dh_final ? p.dh_final[gid] : 0.0f;
+  for (int c = nc - 1; c >= 1; --c) {
+    const int64_t i = (bd * nc + c) * kStates + n;
+    p.mu_in[i] = mu;
+    mu = fmaf(p.Pc[i], mu, p.mu0[i]);
+  }
+  p.mu_in[(bd * nc) * kStates + n] = mu;
 }
 
 // dB[b, n, t] (blockIdx.y = 0) or dC (1): the sum over channel groups of
@@ -481,20 +581,25 @@ __global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kerne
   }
 }
 
-// dA[d, n], dD[d], dbias[d]: sums over the batch of the per-(b, d) partials.
+// dA[d, n], dD[d], dbias[d]: sums over the batch and the chunks of the
+// per-(b, d, chunk) partials, in that order.
 __global__ __launch_bounds__(256) void bwd_reduce_param_kernel(BwdArgs p) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= p.dim * kStates) return;
   const int64_t d = i / kStates;
+  const int n = static_cast<int>(i % kStates);
+  const int nc = p.n_chunks;
   float sa = 0.0f;
-  for (int64_t b = 0; b < p.batch; ++b) sa += p.pA[(b * p.dim) * kStates + i];
+  for (int64_t b = 0; b < p.batch; ++b)
+    for (int c = 0; c < nc; ++c) sa += p.pA[((b * p.dim + d) * nc + c) * kStates + n];
   p.dA[i] = sa;
-  if ((i % kStates) == 0) {
+  if (n == 0) {
     float sd = 0.0f, sb = 0.0f;
-    for (int64_t b = 0; b < p.batch; ++b) {
-      sd += p.pD[b * p.dim + d];
-      sb += p.pbias[b * p.dim + d];
-    }
+    for (int64_t b = 0; b < p.batch; ++b)
+      for (int c = 0; c < nc; ++c) {
+        sd += p.pD[(b * p.dim + d) * nc + c];
+        sb += p.pbias[(b * p.dim + d) * nc + c];
+      }
     if (p.dD) p.dD[d] = sd;
     if (p.dbias) p.dbias[d] = sb;
   }
@@ -502,7 +607,21 @@ __global__ __launch_bounds__(256) void bwd_reduce_param_kernel(BwdArgs p) {
 
 template <typename T, bool kVec>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.groups), static_cast<unsigned>(a.batch));
+  if (a.n_chunks > 1) {
+    hipLaunchKernelGGL((bwd_adj_kernel<T>),
+                       dim3(static_cast<unsigned>(a.dim), static_cast<unsigned>(a.batch),
+                            static_cast<unsigned>(a.n_chunks - 1)),
+                       dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nthreads = a.batch * a.dim * kStates;
+    hipLaunchKernelGGL(bwd_adj_carry_kernel,
+                       dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(static_cast<unsigned>(a.groups), static_cast<unsigned>(a.batch),
+                  static_cast<unsigned>(a.n_chunks));
   using Fn = void (*)(BwdArgs);
   static constexpr Fn kernels[4] = {bwd_kernel<T, kVec, false, false>,
                                     bwd_kernel<T, kVec, true, false>,

@@ -39,6 +39,9 @@ struct ScanArgs {
                                       // ceil(L/1024), 16)
   void *yc;                           // with ckpt: the pre-gate output (dtype),
                                       // or null
+  float *ckpt_s;                      // with ckpt in split mode: the chunk's
+                                      // sum of dt before every block start
+                                      // (batch, dim, ceil(L/1024)); else null
 };
 
 // Backward pass.  Per-workgroup partial sums (a workgroup = kBwdWaves
@@ -52,14 +55,21 @@ struct BwdArgs {
   void *du, *ddelta;                  // activation dtype outputs
   float *dh0;                         // (batch, dim, 16) or null
   float *pB, *pC;                     // (batch, groups, 16, L) partial dB, dC
-  float *pA;                          // (batch, dim, 16) partial dA
-  float *pD, *pbias;                  // (batch, dim) partial dD, dbias
+  float *pA;                          // (batch, dim, n_chunks, 16) partial dA
+  float *pD, *pbias;                  // (batch, dim, n_chunks) partial dD, dbias
   float *dA, *dB, *dC, *dD, *dbias;   // reduced outputs (dD, dbias: or null)
   int64_t batch, dim, L;
   int64_t groups;                     // ceil(dim / kBwdWaves)
   int nblk;                           // ceil(L / 1024)
   int softplus;
   int zoh;                            // 1: exact ZOH input term
+  // sequence split (n_chunks > 1; chunk_len a multiple of 1024, the last
+  // chunk may be shorter): each chunk is swept from the dL/dh entering it
+  // from the right, mu_in; chunks >= 1 first get, from a zero right input,
+  // the dL/dh leaving their first token (mu0) and their decay product (Pc)
+  int n_chunks;
+  int64_t chunk_len;
+  float *mu0, *Pc, *mu_in;            // (batch, dim, n_chunks, 16)
 };
 
 // Backward of the conv prologue (ssm_conv_bwd.hip): u formed into the
@@ -136,8 +146,16 @@ int launch_roofline_valu(int kind, float *out, int64_t threads, int iters,
                          void *stream);
 
 // Workspace layout of the backward pass, in bytes, each part 256-aligned.
+// Workspace of the backward.  The checkpoint pass and the sweep each split
+// long sequences with few channels into chunks of their own (ckpt_chunk,
+// chunk: multiples of 1024 tokens, or the whole sequence).
 struct BwdLayout {
-  size_t off_ckpt, off_yc, off_pB, off_pC, off_pA, off_pD, off_pbias, total_bytes;
+  int64_t ckpt_chunk, ckpt_chunks;    // checkpoint pass (a forward scan)
+  int64_t chunk, n_chunks;            // sweep
+  size_t off_ckpt, off_yc, off_pB, off_pC, off_pA, off_pD, off_pbias;
+  size_t off_cks, off_H, off_S, off_hin;  // checkpoint pass split
+  size_t off_mu0, off_Pc, off_muin;       // sweep split
+  size_t total_bytes;
 };
 BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t elem_bytes);
 const char *hip_error_string(int err);

@@ -295,33 +295,41 @@ void scan_kernel(ScanArgs p) {
     xc[k] = (kConv && t >= 0) ? to_f32<T>(urow[t]) : 0.0f;
   }
 
-  // checkpoint instance (kCkpt; unsplit sequences): the state entering
-  // block k goes to ckpt[b, d, k, :]; with p.yc the pre-gate output goes
-  // there as well (the backward's own checkpoint pass runs without a gate
-  // and takes y itself as the pre-gate output)
+  // checkpoint instance (kCkpt): the state entering block k goes to
+  // ckpt[b, d, k, :]; with p.yc the pre-gate output goes there as well (the
+  // backward's own checkpoint pass runs without a gate and takes y itself
+  // as the pre-gate output).  Split into chunks (block-aligned), a chunk >= 1
+  // starts from a zero state; its blocks' sums of dt since the chunk start
+  // go to ckpt_s, from which ckpt_fix_kernel adds the true incoming state.
   const int64_t nblk = (p.L + kBlockTokens - 1) / kBlockTokens;
   float *ck = (kCkpt && ch_ok) ? p.ckpt + bd * nblk * kStates : nullptr;
+  auto store_ckpt = [&](int64_t t0) {
+    if (kCkpt && ck) {
+      if (p.ckpt_s) {
+        float s = lane_broadcast(wave_inclusive_sum(sdt_total), kWaveLanes - 1);
+        asm volatile("" : "+s"(s));  // formed by the whole wave, then stored by lane 0
+        if (lane == 0) p.ckpt_s[bd * nblk + t0 / kBlockTokens] = s;
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int n = 0; n < kStates; ++n) ck[(t0 / kBlockTokens) * kStates + n] = hc[n];
+      }
+    }
+  };
 
   float upf[kTokensPerLane], dpf[kTokensPerLane];  // prefetched u, delta
   const int64_t last_full = ct0 + ((ct1 - ct0) / kBlockTokens - 1) * kBlockTokens;
   int64_t t0 = ct0;
 #pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens) {
-    if (kCkpt && ck && lane == 0) {
-#pragma unroll
-      for (int n = 0; n < kStates; ++n)
-        ck[(t0 / kBlockTokens) * kStates + n] = hc[n];
-    }
+    store_ckpt(t0);
     scan_block<T, kVec, true, kSoftplus, kConv, kZoh, kCkpt>(
         p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, Ach,
         sT, hc, sdt_total, wc, cb, xc,
         upf, dpf, t0 > ct0,
         t0 + 2 * kBlockTokens <= ct1 ? t0 + kBlockTokens : last_full);
   }
-  if (kCkpt && t0 < ct1 && ck && lane == 0) {
-#pragma unroll
-    for (int n = 0; n < kStates; ++n) ck[(t0 / kBlockTokens) * kStates + n] = hc[n];
-  }
+  if (t0 < ct1) store_ckpt(t0);
   if (t0 < ct1) {
     // the last, partial block: branch-free scalar loads (keeps the register
     // budget of the full-block loop), as few tokens per lane as cover it
@@ -435,6 +443,30 @@ __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
   }
 }
 
+// ------------------------------------------- checkpoint fix-up ------
+// Checkpoint pass in split mode: a block of chunk c >= 1 stored the state
+// reached from a zero state at the chunk start; the true one adds the
+// chunk's incoming state carried over the block's dt sum S since the chunk
+// start: ckpt += exp(A_n * S) * h_in(c)_n (the first block: S = 0, so the
+// incoming state itself).  One thread per (batch, channel, block, state)
+// over the blocks of chunks >= 1.
+__global__ __launch_bounds__(256) void ckpt_fix_kernel(ScanArgs p) {
+  const int64_t nblk = (p.L + kBlockTokens - 1) / kBlockTokens;
+  const int64_t bpc = p.chunk_len / kBlockTokens;  // blocks per chunk
+  const int64_t nfix = nblk - bpc;                 // blocks of chunks >= 1
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= p.batch * p.dim * nfix * kStates) return;
+  const int n = static_cast<int>(gid & 15);
+  const int64_t r = gid >> 4;
+  const int64_t k = bpc + r % nfix;
+  const int64_t bd = r / nfix;
+  const int64_t c = k / bpc;
+  const float Aq = p.A[(bd % p.dim) * kStates + n] * kLog2e;
+  const float hin = p.ws_hin[(bd * p.n_chunks + c) * kStates + n];
+  float *q = p.ckpt + (bd * nblk + k) * kStates + n;
+  *q = fmaf(fast_exp2(Aq * p.ckpt_s[bd * nblk + k]), hin, *q);
+}
+
 template <typename T, bool kVec>
 hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.dim + kChannelsPerGroup - 1) /
@@ -449,8 +481,8 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
       scan_kernel<T, kVec, false, false, true>,  scan_kernel<T, kVec, true, false, true>,
       scan_kernel<T, kVec, false, true, true>,   scan_kernel<T, kVec, true, true, true>};
   const int which = (a.softplus ? 1 : 0) | (a.x ? 2 : 0) | (a.zoh ? 4 : 0);
-  // the backward's checkpoint pass (no conv prologue, unsplit) has
-  // instances of its own, so the forward instances carry none of its code
+  // the backward's checkpoint pass (no conv prologue) has instances of its
+  // own, so the forward instances carry none of its code
   static constexpr KernelFn ckpt_kernels[4] = {scan_kernel<T, kVec, false, false, false, true>,
                                                scan_kernel<T, kVec, true, false, false, true>,
                                                scan_kernel<T, kVec, false, false, true, true>,
@@ -468,6 +500,12 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   const dim3 fgrid(static_cast<unsigned>(a.dim), static_cast<unsigned>(a.batch),
                    static_cast<unsigned>(a.n_chunks - 1));
   hipLaunchKernelGGL((fixup_kernel<T>), fgrid, dim3(64), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || !a.ckpt) return e;
+  const int64_t nblk = (a.L + kBlockTokens - 1) / kBlockTokens;
+  const int64_t nfix = a.batch * a.dim * (nblk - a.chunk_len / kBlockTokens) * kStates;
+  hipLaunchKernelGGL(ckpt_fix_kernel, dim3(static_cast<unsigned>((nfix + 255) / 256)),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -376,6 +376,35 @@ def test_bwd_workspace_size(lib):
     assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 0, None) == 1
 
 
+def _bwd_ws(lib, batch, dim, L, dtype):
+    size = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(batch, dim, 16, L, dtype, ctypes.byref(size)) == 0
+    return size.value
+
+
+def _bwd_unsplit_bytes(batch, dim, L, es):
+    up = lambda x: (x + 255) // 256 * 256
+    bd, nblk, groups = batch * dim, -(-L // 1024), -(-dim // 8)
+    part = batch * groups * 16 * L * 4
+    return (up(bd * nblk * 16 * 4) + up(bd * L * es) + 2 * up(part) +
+            up(bd * 16 * 4) + 2 * up(bd * 4))
+
+
+def test_bwd_workspace_split_regions(lib):
+    """Shapes with many channels, or short rows, keep the unsplit layout;
+    few channels over long rows add the split buffers (the checkpoint pass's
+    block sums and chunk states, the sweep's per-chunk adjoints and
+    per-chunk parameter partials), which stay small next to the dB/dC
+    partials."""
+    for shape in [(2, 5120, 4096), (2, 13, 2100), (1, 8, 8192), (4, 1536, 2048)]:
+        assert _bwd_ws(lib, *shape, 1) == _bwd_unsplit_bytes(*shape, 2), shape
+    # (1, 8, 16383): only the checkpoint pass splits (chunks of 8192 tokens;
+    # the sweep splits from 2 x 8192)
+    for shape in [(1, 8, 16383), (1, 8, 25076), (2, 5, 20480), (1, 1536, 1 << 20)]:
+        got, base = _bwd_ws(lib, *shape, 0), _bwd_unsplit_bytes(*shape, 4)
+        assert base < got < base * 1.05 + 2**20, shape
+
+
 def _ssd(lib, **kw):
     step = 0x08000000
     names = ["x", "dt", "A", "B", "C", "y", "ws"]

@@ -328,3 +328,80 @@ def test_bwd_zoh_matches_oracle(case):
     check(hf, h_ref, tol, "h_final (saving forward)")
     for k in got:
         assert torch.equal(got2[k], got[k]), k
+
+
+# ------------------------------------------------------- sequence split
+def _unsplit_ws_bytes(batch, dim, L, es):
+    """The backward workspace without its split buffers (block checkpoints,
+    pre-gate output, dB/dC partials, per-channel partials; 256-byte
+    aligned regions)."""
+    up = lambda x: (x + 255) // 256 * 256
+    bd, nblk, groups = batch * dim, -(-L // 1024), -(-dim // 8)
+    part = batch * groups * 16 * L * 4
+    return (up(bd * nblk * 16 * 4) + up(bd * L * es) + 2 * up(part) +
+            up(bd * 16 * 4) + 2 * up(bd * 4))
+
+
+SPLIT_CASES = [
+    # (batch, dim, L, dtype, softplus, zoh, A kind); few channels and long
+    # rows, so the checkpoint pass and the sweep both cut the sequence
+    (1, 8, 25076, "f32", 1, 0, "arange"),  # 3 sweep chunks, ragged last one
+    (2, 5, 20480, "bf16", 1, 0, "arange"),
+    (1, 8, 18000, "f32", 1, 1, "arange"),  # exact ZOH input term
+    (1, 4, 17408, "f32", 0, 0, "arange"),  # softplus off: no early stop
+    (1, 8, 20000, "f32", 1, 0, "slow"),    # A / 100: decays span the chunks
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES,
+                         ids=lambda c: "b%d_d%d_l%d_%s_sp%d_zoh%d_%s" % c)
+def test_bwd_split_matches_oracle(case):
+    """The split backward (chunked checkpoint pass with its fix-up; per
+    chunk, the adjoint leaving it from a zero right input, chained from the
+    last chunk; chunks swept in parallel) against the unsplit oracle on
+    every gradient."""
+    batch, dim, L, dt, sp, zoh, akind = case
+    inp = make(batch, dim, L, dt, 1200 + L + dim, with_bias=bool(sp),
+               softplus=bool(sp))
+    if akind == "slow":
+        inp["A"] = inp["A"] / 100.0
+    es = 2 if dt == "bf16" else 4
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    assert ssm.ssm_scan_bwd_workspace_size(batch, dim, 16, L, tdt) > \
+        _unsplit_ws_bytes(batch, dim, L, es), "the shape did not split"
+    ref = oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"],
+                          inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                          bool(sp), inp["h0"], inp["dy"], inp["dh_final"],
+                          zoh_b=bool(zoh))
+    d = to_dev(inp)
+    got = ssm.ssm_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                           d["z"], d["delta_bias"], bool(sp), d["h0"], d["dy"],
+                           d["dh_final"], zoh_b=bool(zoh))
+    torch.cuda.synchronize()
+    tol = TOL[dt]
+    keys = ["du", "ddelta", "dA", "dB", "dC", "dh0", "dD", "dz"]
+    if sp:
+        keys.append("ddelta_bias")
+    for k in keys:
+        check(got[k], ref[k], tol, k)
+
+
+def test_bwd_split_saved_and_deterministic():
+    """With checkpoints from ssm_scan_fwd_save (whole sequence) the split
+    sweep gives the oracle's gradients; a repeated split call gives the same
+    bits."""
+    inp = make(1, 6, 19000, "f32", 1300)
+    ref = oracle_bwd(inp)
+    d = to_dev(inp)
+    y, hf, ws = ssm.ssm_scan_fwd_save(d["u"], d["delta"], d["A"], d["B"],
+                                      d["C"], d["D"], d["z"], d["delta_bias"],
+                                      True, d["h0"])
+    g_saved = ssm.ssm_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"],
+                               d["D"], d["z"], d["delta_bias"], True, d["h0"],
+                               d["dy"], d["dh_final"], workspace=ws, saved=True)
+    g1 = gpu_bwd(d)
+    g2 = gpu_bwd(d)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+        check(g_saved[k], ref[k], 1e-4, k + " (saved)")
+        check(g1[k], ref[k], 1e-4, k)
