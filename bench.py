@@ -421,7 +421,41 @@ def extra_workloads(torch, ssm, syn, dev, stream, log, ceil):
         "elements_per_s": round(cfg.elements / (ms * 1e-3)),
         "chunk_len": ssm.ssm_scan_plan(cfg.batch, cfg.dim, 16, cfg.seqlen),
         "algorithmic_bytes": nb}
-    del inp, y, hf, ws
+    del y, hf, ws
+    torch.cuda.empty_cache()
+
+    # its backward (1536 channels: the sequence is split across waves)
+    log("long-context backward %s" % cfg.name)
+    g = torch.Generator(device=dev).manual_seed(cfg.seed + 9)
+    dy = torch.randn(cfg.batch, cfg.dim, cfg.seqlen, generator=g, device=dev)
+    bws = torch.empty(ssm.ssm_scan_bwd_workspace_size(cfg.batch, cfg.dim, 16,
+                                                      cfg.seqlen, torch.float32),
+                      dtype=torch.uint8, device=dev)
+    grads = {}
+
+    def brun():
+        grads.update(ssm.ssm_scan_bwd(
+            inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+            inp["z"], inp["delta_bias"], True, None, dy, None, workspace=bws,
+            stream=stream))
+        grads.clear()
+    brun()
+    torch.cuda.synchronize()
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        brun()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb = syn.backward_bytes(cfg)
+    out[cfg.name + "_backward"] = {
+        "ms_per_call": round(ms, 3), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+        "algorithmic_bytes": nb,
+        "note": "ssm_scan_bwd, no dh_final: checkpoint pass (split like the "
+                "forward), adjoint pre-pass and carry, chunked sweep, "
+                "reductions; gradient outputs allocated per call"}
+    del inp, dy, bws
     torch.cuda.empty_cache()
 
     # the 2.8B layer with the exact zero-order-hold input term

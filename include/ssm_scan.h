@@ -237,7 +237,11 @@ int ssm_conv_state_update(float *state, void *conv_state, const void *x,
  * (batch*dim*ceil(seqlen/1024)*16 fp32), the pre-gate output (batch*dim*
  * seqlen, activation dtype), per-workgroup partial sums of dB and dC
  * (2 * batch*ceil(dim/8)*16*seqlen fp32: a workgroup holds 8 channels), and
- * per-channel partials of dA, dD and the bias. */
+ * per-(channel, chunk) partials of dA, dD and the bias.  Shapes with few
+ * channels and long rows split the sequence (below) and add, each under
+ * 1 % of the partial sums: the checkpoint pass's per-block dt sums and
+ * per-chunk states, and the sweep's per-chunk adjoints (3 x batch*dim*
+ * chunks*16 fp32). */
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                 int64_t seqlen, int dtype, size_t *bytes);
 
@@ -288,10 +292,17 @@ int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *                      checkpoint region must hold what ssm_scan_fwd_save
  *                      wrote for the same u, delta, A, B, C, D, delta_bias,
  *                      h0 and softplus flag (not checked)
- * No output may overlap an input, another output or the workspace.  The
- * sequence is not split across waves (one wave per channel over the whole
- * sequence), so shapes with few channels and very long sequences run with
- * few waves. */
+ * No output may overlap an input, another output or the workspace.
+ * A wave takes one channel.  When the channels alone give the GPU fewer
+ * than two rounds of waves and the rows hold at least 16384 tokens, the
+ * sequence is cut into up to 16 chunks of whole 1024-token blocks, swept in
+ * parallel: each chunk after the first first yields, from a zero input on
+ * its right, the dL/dh it passes to its left and its decay product (over
+ * its decay horizon: contributions below 2^-40 are dropped when every A < 0
+ * under softplus), these are chained from the last chunk, and each chunk
+ * is swept from its true incoming dL/dh.  The checkpoint pass is split like
+ * ssm_scan_fwd.  The results then differ from the unsplit order of
+ * summation by rounding only. */
 int ssm_scan_bwd(const void *u, const void *delta, const float *A,
                  const void *B, const void *C, const float *D, const void *z,
                  const float *delta_bias, unsigned flags, const float *h0,
