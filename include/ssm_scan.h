@@ -313,10 +313,12 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A,
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Forward pass for training: the same computation and outputs (y, h_final)
- * as ssm_scan_fwd over whole sequences (no split), which in addition keeps
- * what the backward recomputes otherwise -- the state entering every
- * 1024-token block and the output before the gate -- in the backward's
- * workspace.  A following ssm_scan_bwd on the same inputs with
+ * as ssm_scan_fwd, which in addition keeps what the backward recomputes
+ * otherwise -- the state entering every 1024-token block and the output
+ * before the gate -- in the backward's workspace.  It splits long rows of
+ * few channels exactly as ssm_scan_fwd with requested_chunk = 0 does (its
+ * chunk buffers are in that workspace), the checkpoints and the pre-gate
+ * output fixed up like y.  A following ssm_scan_bwd on the same inputs with
  * SSM_FLAG_BWD_SAVED and that workspace then skips its checkpoint pass.
  * (The inferownia.pl page on Mamba, section "Cena selekcji": the backward
  * recomputes the intermediate states rather than storing them; here one

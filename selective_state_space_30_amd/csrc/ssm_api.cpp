@@ -389,7 +389,7 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
 
   if (saved) {
     if (requested_chunk != 0)
-      return fail(SSM_ERR_INVALID_ARG, "saving for the backward runs whole sequences "
+      return fail(SSM_ERR_INVALID_ARG, "saving for the backward chooses its own split "
                                        "(requested_chunk must be 0)");
     st = check_bwd_sizes(batch, dim, dstate, seqlen);
     if (st != SSM_OK) return st;
@@ -406,7 +406,9 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
       if (overlaps(saved, static_cast<int64_t>(l.total_bytes), all[i], sizes[i]))
         return fail(SSM_ERR_INVALID_ARG, "backward workspace overlaps an argument array");
   }
-  const int64_t chunk = saved ? seqlen : choose_chunk(batch, dim, seqlen, requested_chunk);
+  // (saving for the backward: the split of the backward's own checkpoint
+  // pass, whose buffers its workspace holds)
+  const int64_t chunk = choose_chunk(batch, dim, seqlen, requested_chunk);
   const int64_t n_chunks = (seqlen + chunk - 1) / chunk;
   if (n_chunks > kMaxGridYZ)
     return fail(SSM_ERR_UNSUPPORTED, "more than %lld chunks requested",
@@ -428,6 +430,13 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
       return fail(SSM_ERR_HIP, "device scratch lookup failed: %s",
                   ssm::hip_error_string(err));
     char *w = static_cast<char *>(p);
+    a.ws_H = reinterpret_cast<float *>(w + l.off_H);
+    a.ws_S = reinterpret_cast<float *>(w + l.off_S);
+    a.ws_hin = reinterpret_cast<float *>(w + l.off_hin);
+  } else if (n_chunks > 1 && saved) {
+    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen, es);
+    char *w = static_cast<char *>(saved);
+    a.ckpt_s = reinterpret_cast<float *>(w + l.off_cks);
     a.ws_H = reinterpret_cast<float *>(w + l.off_H);
     a.ws_S = reinterpret_cast<float *>(w + l.off_S);
     a.ws_hin = reinterpret_cast<float *>(w + l.off_hin);

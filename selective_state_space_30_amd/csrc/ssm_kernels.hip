@@ -502,6 +502,15 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((fixup_kernel<T>), fgrid, dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || !a.ckpt) return e;
+  if (a.yc) {
+    // the saving forward's pre-gate output, fixed up the same way
+    ScanArgs ac = a;
+    ac.y = a.yc;
+    ac.z = nullptr;
+    hipLaunchKernelGGL((fixup_kernel<T>), fgrid, dim3(64), 0, s, ac);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t nblk = (a.L + kBlockTokens - 1) / kBlockTokens;
   const int64_t nfix = a.batch * a.dim * (nblk - a.chunk_len / kBlockTokens) * kStates;
   hipLaunchKernelGGL(ckpt_fix_kernel, dim3(static_cast<unsigned>((nfix + 255) / 256)),
