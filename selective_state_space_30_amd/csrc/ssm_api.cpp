@@ -64,9 +64,9 @@ int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
     return fail(SSM_ERR_INVALID_ARG,
                 "sizes must be positive (batch=%lld dim=%lld dstate=%lld seqlen=%lld)",
                 (long long)batch, (long long)dim, (long long)dstate, (long long)seqlen);
-  if (dstate != ssm::kStates)
-    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld: this build supports dstate=16 only",
-                (long long)dstate);
+  if (dstate > ssm::kMaxStates)
+    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld: this build supports dstate 1..%d",
+                (long long)dstate, ssm::kMaxStates);
   int64_t e, e2;
   if (!mul_ok(batch, dim, &e) || !mul_ok(e, seqlen, &e2) || !mul_ok(e2, 8, &e2))
     return fail(SSM_ERR_INVALID_ARG, "batch*dim*seqlen overflows");
@@ -138,12 +138,14 @@ int64_t bwd_chunk(int64_t batch, int64_t dim, int64_t seqlen) {
 }  // namespace
 
 namespace ssm {
-BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t elem_bytes) {
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t N, int64_t seqlen,
+                     int64_t elem_bytes) {
+  const size_t ns = static_cast<size_t>(N);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t bd = static_cast<size_t>(batch) * dim;
   const size_t nblk = static_cast<size_t>((seqlen + kBlockTokens - 1) / kBlockTokens);
   const size_t groups = static_cast<size_t>((dim + kBwdWaves - 1) / kBwdWaves);
-  const size_t part = static_cast<size_t>(batch) * groups * kStates * seqlen * sizeof(float);
+  const size_t part = static_cast<size_t>(batch) * groups * ns * seqlen * sizeof(float);
   BwdLayout l;
   l.ckpt_chunk = choose_chunk(batch, dim, seqlen, 0);
   l.ckpt_chunks = (seqlen + l.ckpt_chunk - 1) / l.ckpt_chunk;
@@ -152,11 +154,11 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t elem_by
   const size_t nc = static_cast<size_t>(l.n_chunks);
   const size_t ncc = static_cast<size_t>(l.ckpt_chunks);
   l.off_ckpt = 0;
-  l.off_yc = up(l.off_ckpt + bd * nblk * kStates * sizeof(float));
+  l.off_yc = up(l.off_ckpt + bd * nblk * ns * sizeof(float));
   l.off_pB = up(l.off_yc + bd * static_cast<size_t>(seqlen) * elem_bytes);
   l.off_pC = up(l.off_pB + part);
   l.off_pA = up(l.off_pC + part);
-  l.off_pD = up(l.off_pA + bd * nc * kStates * sizeof(float));
+  l.off_pD = up(l.off_pA + bd * nc * ns * sizeof(float));
   l.off_pbias = up(l.off_pD + bd * nc * sizeof(float));
   size_t end = up(l.off_pbias + bd * nc * sizeof(float));
   // the split checkpoint pass: block dt sums, chunk end states, dt sums and
@@ -165,31 +167,31 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t elem_by
   if (ncc > 1) {
     l.off_cks = end;
     l.off_H = up(l.off_cks + bd * nblk * sizeof(float));
-    l.off_S = up(l.off_H + bd * ncc * kStates * sizeof(float));
+    l.off_S = up(l.off_H + bd * ncc * ns * sizeof(float));
     l.off_hin = up(l.off_S + bd * ncc * sizeof(float));
-    end = up(l.off_hin + bd * ncc * kStates * sizeof(float));
+    end = up(l.off_hin + bd * ncc * ns * sizeof(float));
   }
   // the split sweep: the chunks' adjoints from a zero right input, their
   // decay products, and the adjoints entering them
   l.off_mu0 = l.off_Pc = l.off_muin = 0;
   if (nc > 1) {
     l.off_mu0 = end;
-    l.off_Pc = up(l.off_mu0 + bd * nc * kStates * sizeof(float));
-    l.off_muin = up(l.off_Pc + bd * nc * kStates * sizeof(float));
-    end = up(l.off_muin + bd * nc * kStates * sizeof(float));
+    l.off_Pc = up(l.off_mu0 + bd * nc * ns * sizeof(float));
+    l.off_muin = up(l.off_Pc + bd * nc * ns * sizeof(float));
+    end = up(l.off_muin + bd * nc * ns * sizeof(float));
   }
   l.total_bytes = end;
   return l;
 }
 
-SplitLayout split_layout(int64_t batch, int64_t dim, int64_t n_chunks) {
+SplitLayout split_layout(int64_t batch, int64_t dim, int64_t N, int64_t n_chunks) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t bdc = static_cast<size_t>(batch) * dim * n_chunks;
   SplitLayout l;
   l.off_H = 0;
-  l.off_S = up(l.off_H + bdc * kStates * sizeof(float));
+  l.off_S = up(l.off_H + bdc * N * sizeof(float));
   l.off_hin = up(l.off_S + bdc * sizeof(float));
-  l.total_bytes = up(l.off_hin + bdc * kStates * sizeof(float));
+  l.total_bytes = up(l.off_hin + bdc * N * sizeof(float));
   return l;
 }
 }  // namespace ssm
@@ -223,7 +225,7 @@ int ssm_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
   int st = ssm_scan_plan(batch, dim, dstate, seqlen, requested_chunk, &chunk);
   if (st != SSM_OK) return st;
   const int64_t n_chunks = (seqlen + chunk - 1) / chunk;
-  *bytes = n_chunks > 1 ? ssm::split_layout(batch, dim, n_chunks).total_bytes : 0;
+  *bytes = n_chunks > 1 ? ssm::split_layout(batch, dim, dstate, n_chunks).total_bytes : 0;
   return ok();
 }
 
@@ -292,7 +294,7 @@ int step_impl(float *state, void *conv_state, const void *x, const float *conv_w
   ssm::StepArgs a{};
   a.state = state; a.x = x; a.delta = delta; a.B = B; a.C = C; a.z = z;
   a.A = A; a.D = D; a.bias = delta_bias; a.y = y;
-  a.batch = batch; a.dim = dim;
+  a.batch = batch; a.dim = dim; a.N = static_cast<int>(dstate);
   a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
   a.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
   a.conv_state = d_conv > 1 ? conv_state : nullptr;
@@ -309,7 +311,7 @@ int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) 
   if (st != SSM_OK) return st;
   const int64_t groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
   int64_t e;
-  if (groups >= (int64_t(1) << 31) || !mul_ok(batch * groups, ssm::kStates * seqlen, &e) ||
+  if (groups >= (int64_t(1) << 31) || !mul_ok(batch * groups, dstate * seqlen, &e) ||
       !mul_ok(e, 8, &e))
     return fail(SSM_ERR_UNSUPPORTED, "backward workspace of this shape overflows");
   // the checkpoint pass's chunks are a grid dimension
@@ -318,7 +320,7 @@ int check_bwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) 
     return fail(SSM_ERR_UNSUPPORTED, "seqlen too long for the backward's checkpoint pass");
   // the channel-sum reduction launches one workgroup per 256 tokens of each
   // (batch, state) row
-  if (batch * ssm::kStates * ((seqlen + 255) / 256) >= (int64_t(1) << 31))
+  if (batch * dstate * ((seqlen + 255) / 256) >= (int64_t(1) << 31))
     return fail(SSM_ERR_UNSUPPORTED, "batch*seqlen too large for the backward reduction");
   return SSM_OK;
 }
@@ -393,7 +395,7 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
                                        "(requested_chunk must be 0)");
     st = check_bwd_sizes(batch, dim, dstate, seqlen);
     if (st != SSM_OK) return st;
-    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen, es);
+    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, dstate, seqlen, es);
     if (saved_bytes < l.total_bytes)
       return fail(SSM_ERR_WORKSPACE, "backward workspace of %zu bytes needed (got %zu bytes at %p)",
                   l.total_bytes, saved_bytes, saved);
@@ -418,7 +420,7 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
   if (n_chunks > 1 && use_scratch) {
     // the library's fixed device scratch; the size check is arithmetic
     // only, the address lookup is the first HIP call
-    const ssm::SplitLayout l = ssm::split_layout(batch, dim, n_chunks);
+    const ssm::SplitLayout l = ssm::split_layout(batch, dim, dstate, n_chunks);
     if (l.total_bytes > ssm::kScanScratchBytes)
       return fail(SSM_ERR_WORKSPACE,
                   "this shape splits into %lld chunks and needs %zu bytes of scratch; "
@@ -434,14 +436,14 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
     a.ws_S = reinterpret_cast<float *>(w + l.off_S);
     a.ws_hin = reinterpret_cast<float *>(w + l.off_hin);
   } else if (n_chunks > 1 && saved) {
-    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen, es);
+    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, dstate, seqlen, es);
     char *w = static_cast<char *>(saved);
     a.ckpt_s = reinterpret_cast<float *>(w + l.off_cks);
     a.ws_H = reinterpret_cast<float *>(w + l.off_H);
     a.ws_S = reinterpret_cast<float *>(w + l.off_S);
     a.ws_hin = reinterpret_cast<float *>(w + l.off_hin);
   } else if (n_chunks > 1) {
-    const ssm::SplitLayout l = ssm::split_layout(batch, dim, n_chunks);
+    const ssm::SplitLayout l = ssm::split_layout(batch, dim, dstate, n_chunks);
     if (!workspace || workspace_bytes < l.total_bytes)
       return fail(SSM_ERR_WORKSPACE,
                   "workspace of %zu bytes needed (got %zu bytes at %p)", l.total_bytes,
@@ -469,13 +471,13 @@ int scan_impl(const void *u, const void *x, const float *conv_w,
   a.x = x; a.conv_w = conv_w; a.conv_b = conv_b; a.d_conv = x ? d_conv : 0;
   a.A = A; a.D = D; a.bias = delta_bias; a.h0 = h0;
   a.y = y; a.h_final = h_final;
-  a.batch = batch; a.dim = dim; a.L = seqlen;
+  a.batch = batch; a.dim = dim; a.L = seqlen; a.N = static_cast<int>(dstate);
   a.chunk_len = chunk;
   a.n_chunks = static_cast<int>(n_chunks);
   a.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
   a.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
   if (saved) {
-    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen, es);
+    const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, dstate, seqlen, es);
     a.ckpt = reinterpret_cast<float *>(static_cast<char *>(saved) + l.off_ckpt);
     a.yc = static_cast<char *>(saved) + l.off_yc;
   }
@@ -582,7 +584,8 @@ int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
     return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int st = check_bwd_sizes(batch, dim, dstate, seqlen);
   if (st != SSM_OK) return st;
-  *bytes = ssm::bwd_layout(batch, dim, seqlen, dtype == SSM_DTYPE_BF16 ? 2 : 4).total_bytes;
+  *bytes = ssm::bwd_layout(batch, dim, dstate, seqlen, dtype == SSM_DTYPE_BF16 ? 2 : 4)
+               .total_bytes;
   return ok();
 }
 
@@ -645,7 +648,7 @@ int scan_bwd_impl(const void *u, const void *delta, const float *A,
         return fail(SSM_ERR_INVALID_ARG, "%s overlaps %s", o.name, o2.name);
   }
 
-  const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, seqlen, es);
+  const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, dstate, seqlen, es);
   if (!workspace || workspace_bytes < l.total_bytes)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu bytes at %p)",
                 l.total_bytes, workspace_bytes, workspace);
@@ -678,7 +681,7 @@ int scan_bwd_impl(const void *u, const void *delta, const float *A,
   fa.u = u; fa.delta = delta; fa.B = B; fa.C = C; fa.z = nullptr;
   fa.A = A; fa.D = D; fa.bias = delta_bias; fa.h0 = h0;
   fa.y = yc; fa.h_final = nullptr;
-  fa.batch = batch; fa.dim = dim; fa.L = seqlen;
+  fa.batch = batch; fa.dim = dim; fa.L = seqlen; fa.N = static_cast<int>(dstate);
   fa.chunk_len = l.ckpt_chunk; fa.n_chunks = static_cast<int>(l.ckpt_chunks);
   fa.softplus = (flags & SSM_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
   fa.zoh = (flags & SSM_FLAG_ZOH_B) ? 1 : 0;
@@ -705,7 +708,7 @@ int scan_bwd_impl(const void *u, const void *delta, const float *A,
   a.pD = reinterpret_cast<float *>(w + l.off_pD);
   a.pbias = reinterpret_cast<float *>(w + l.off_pbias);
   a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dbias = ddelta_bias;
-  a.batch = batch; a.dim = dim; a.L = seqlen;
+  a.batch = batch; a.dim = dim; a.L = seqlen; a.N = static_cast<int>(dstate);
   a.groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
   a.nblk = static_cast<int>((seqlen + ssm::kBlockTokens - 1) / ssm::kBlockTokens);
   a.softplus = fa.softplus;
@@ -746,11 +749,12 @@ struct ConvBwdLayout {
   size_t off_u, off_du, off_part, total_bytes;
 };
 
-static ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t es) {
+static ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t dim, int64_t N, int64_t seqlen,
+                                     int64_t es) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t big = static_cast<size_t>(batch) * dim * seqlen * es;
   ConvBwdLayout l;
-  l.off_u = up(ssm::bwd_layout(batch, dim, seqlen, es).total_bytes);
+  l.off_u = up(ssm::bwd_layout(batch, dim, N, seqlen, es).total_bytes);
   l.off_du = up(l.off_u + big);
   l.off_part = up(l.off_du + big);
   l.total_bytes = up(l.off_part + static_cast<size_t>(batch) * dim * (ssm::kMaxConv + 1) *
@@ -764,7 +768,8 @@ int ssm_conv_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
   const int st = ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen, dtype, &b0);
   if (st != SSM_OK) return st;
   if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = conv_bwd_layout(batch, dim, seqlen, dtype == SSM_DTYPE_BF16 ? 2 : 4).total_bytes;
+  *bytes = conv_bwd_layout(batch, dim, dstate, seqlen, dtype == SSM_DTYPE_BF16 ? 2 : 4)
+               .total_bytes;
   return ok();
 }
 
@@ -796,7 +801,7 @@ int ssm_conv_scan_bwd(const void *x, const float *conv_w, const float *conv_b,
   for (const void *p : f32s)
     if (p && !aligned(p, 4))
       return fail(SSM_ERR_INVALID_ARG, "fp32 pointer %p not 4-byte aligned", p);
-  const ConvBwdLayout l = conv_bwd_layout(batch, dim, seqlen, es);
+  const ConvBwdLayout l = conv_bwd_layout(batch, dim, dstate, seqlen, es);
   if (!workspace || workspace_bytes < l.total_bytes)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu bytes at %p)",
                 l.total_bytes, workspace_bytes, workspace);

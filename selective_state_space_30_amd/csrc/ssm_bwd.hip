@@ -141,8 +141,8 @@ __device__ __forceinline__ void bwd_block(
   const T *src = mat ? Cb : Bb;
   const int toff = (mat * kWaveLanes + lane) * KP + qr * kQuarterRun;
   const int64_t tq = tl + qr * kQuarterRun;
-  float *pBg = p.pB + (b * p.groups + g) * kStates * p.L;  // this group's partial rows
-  float *pCg = p.pC + (b * p.groups + g) * kStates * p.L;
+  float *pBg = p.pB + (b * p.groups + g) * p.N * p.L;  // this group's partial rows
+  float *pCg = p.pC + (b * p.groups + g) * p.N * p.L;
   TileRun<T, kQuarterRun, kVec, kFull> run;
   if (stager) run.load(src, t0, tq, tend);  // state 0
 
@@ -222,8 +222,8 @@ __device__ __forceinline__ void bwd_block(
   __syncthreads();  // the tile of state 0 (and the previous block's last sums read)
 
 #pragma unroll 1
-  for (int n = 0; n < kStates; ++n) {
-    if (stager && n + 1 < kStates) run.load(src + (n + 1) * p.L, t0, tq, tend);
+  for (int n = 0; n < p.N; ++n) {
+    if (stager && n + 1 < p.N) run.load(src + (n + 1) * p.L, t0, tq, tend);
     const float *tile = sT + (n & 1) * kBwdTileFloats;
     float *reg = sR + (n & 1) * kRegionFloats;
     float An = state_of(Av, n);
@@ -320,7 +320,7 @@ __device__ __forceinline__ void bwd_block(
     float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
     asm volatile("" : "+s"(dA_sum));
     dAv += lane == n ? dA_sum : 0.0f;
-    if (stager && n + 1 < kStates) run.store(sT + ((n + 1) & 1) * kBwdTileFloats, toff);
+    if (stager && n + 1 < p.N) run.store(sT + ((n + 1) & 1) * kBwdTileFloats, toff);
     __syncthreads();  // state n's contributions and state n+1's tile are in LDS
     flush_state<kVec, kFull, K>(reg, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
   }
@@ -359,28 +359,29 @@ void bwd_kernel(BwdArgs p) {
   const int64_t d = ch_ok ? d_raw : p.dim - 1;  // clamped for reads
   const int64_t bd = b * p.dim + d;
   const int64_t bdc = bd * p.n_chunks + c;
-  const int ls = lane < kStates ? lane : 0;  // lane n <-> state n
+  const int N = p.N;
+  const int ls = lane < N ? lane : 0;  // lane n <-> state n
   const int64_t ct0 = static_cast<int64_t>(c) * p.chunk_len;
   const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
 
-  const float Av = p.A[d * kStates + ls];
+  const float Av = p.A[d * N + ls];
   // dL/dh entering the chunk's last token from the right
-  float muv = p.n_chunks > 1 ? p.mu_in[bdc * kStates + ls]
-                             : (p.dh_final ? p.dh_final[bd * kStates + ls] : 0.0f);
+  float muv = p.n_chunks > 1 ? p.mu_in[bdc * N + ls]
+                             : (p.dh_final ? p.dh_final[bd * N + ls] : 0.0f);
   float dAv = 0.0f;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
-  const T *Bb = static_cast<const T *>(p.B) + b * kStates * p.L;
-  const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
+  const T *Bb = static_cast<const T *>(p.B) + b * N * p.L;
+  const T *Cb = static_cast<const T *>(p.C) + b * N * p.L;
   float dDl = 0.0f, dbl = 0.0f;
 
   // the chunk's blocks (chunks start on block boundaries; only the last
   // chunk can end in a partial block), last to first
-  const float *ck = p.ckpt + (bd * p.nblk + ct0 / kBlockTokens) * kStates;
+  const float *ck = p.ckpt + (bd * p.nblk + ct0 / kBlockTokens) * N;
   const int64_t nfull = (ct1 - ct0) / kBlockTokens;
   const int64_t rem = (ct1 - ct0) - nfull * kBlockTokens;
   if (rem > 0) {  // the partial last block comes first
-    const float hf = ck[nfull * kStates + ls];
+    const float hf = ck[nfull * N + ls];
     const int64_t t0 = ct0 + nfull * kBlockTokens;
     if (rem <= 4 * kWaveLanes)
       bwd_block<T, false, false, kSoftplus, kZoh, 4>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
@@ -399,13 +400,13 @@ void bwd_kernel(BwdArgs p) {
   for (int64_t k = nfull - 1; k >= 0; --k)
     bwd_block<T, kVec, true, kSoftplus, kZoh>(p, wave, lane, ct0 + k * kBlockTokens,
                                         ct0 + (k + 1) * kBlockTokens, b, bd, g, Bb, Cb, ch_ok,
-                                        bias, Dd, Av, ck[k * kStates + ls], muv, dAv, dDl, dbl,
+                                        bias, Dd, Av, ck[k * N + ls], muv, dAv, dDl, dbl,
                                         sT, sR, tid);
 
   if (!ch_ok) return;
-  if (lane < kStates) {
-    p.pA[bdc * kStates + lane] = dAv * kLn2;  // sum of q * dt = q * dtl * ln2
-    if (p.dh0 && c == 0) p.dh0[bd * kStates + lane] = muv;
+  if (lane < N) {
+    p.pA[bdc * N + lane] = dAv * kLn2;  // sum of q * dt = q * dtl * ln2
+    if (p.dh0 && c == 0) p.dh0[bd * N + lane] = muv;
   }
   float sD = lane_broadcast(wave_inclusive_sum(dDl), kWaveLanes - 1);
   float sb = lane_broadcast(wave_inclusive_sum(dbl), kWaveLanes - 1);
@@ -428,55 +429,59 @@ void bwd_kernel(BwdArgs p) {
 // leaving Pc at that (negligible) value.
 template <typename T>
 __global__ __launch_bounds__(64) void bwd_adj_kernel(BwdArgs p) {
+  constexpr int kG = 16;  // states per pass over the horizon
   const int lane = threadIdx.x;
   const int64_t d = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int c = blockIdx.z + 1;
   const int64_t bd = b * p.dim + d;
+  const int N = p.N;
   const int64_t ct0 = static_cast<int64_t>(c) * p.chunk_len;
   const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
-  float Aq[kStates], acc[kStates];
   float amax = -INFINITY;
-#pragma unroll
-  for (int n = 0; n < kStates; ++n) {
-    Aq[n] = p.A[d * kStates + n] * kLog2e;
-    acc[n] = 0.0f;
-    amax = fmaxf(amax, Aq[n]);
-  }
+  for (int n = 0; n < N; ++n) amax = fmaxf(amax, p.A[d * N + n] * kLog2e);
   const bool may_stop = p.softplus && amax < 0.0f;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
   const T *gyrow = static_cast<const T *>(p.dy) + bd * p.L;
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
-  const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
-  float S = 0.0f;
-  for (int64_t t0 = ct0; t0 < ct1; t0 += 64) {
-    const int64_t t = t0 + lane;
-    const bool in = t < ct1;
-    float dt = 0.0f, gc = 0.0f;
-    if (in) {
-      const float x = to_f32<T>(drow[t]) + bias;
-      dt = p.softplus ? softplus_f(x) : x;
-      gc = to_f32<T>(gyrow[t]);
-      if (zrow) gc *= silu_f(to_f32<T>(zrow[t]));
-    }
-    const float St = S + wave_inclusive_sum(dt);
+  const T *Cb = static_cast<const T *>(p.C) + b * N * p.L;
+  const int64_t base = (bd * p.n_chunks + c) * N;
+  for (int n0 = 0; n0 < N; n0 += kG) {
+    float Aq[kG], acc[kG];
 #pragma unroll
-    for (int n = 0; n < kStates; ++n) {
-      const float cn = in ? to_f32<T>(Cb[n * p.L + t]) : 0.0f;
-      acc[n] = fmaf(fast_exp2(Aq[n] * St) * gc, cn, acc[n]);
+    for (int n = 0; n < kG; ++n) {
+      Aq[n] = n0 + n < N ? p.A[d * N + n0 + n] * kLog2e : 0.0f;
+      acc[n] = 0.0f;
     }
-    S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(St), 63));
-    if (may_stop && fast_exp2(amax * S) <= 0x1p-40f) break;
-  }
-  const int64_t base = (bd * p.n_chunks + c) * kStates;
+    float S = 0.0f;
+    for (int64_t t0 = ct0; t0 < ct1; t0 += 64) {
+      const int64_t t = t0 + lane;
+      const bool in = t < ct1;
+      float dt = 0.0f, gc = 0.0f;
+      if (in) {
+        const float x = to_f32<T>(drow[t]) + bias;
+        dt = p.softplus ? softplus_f(x) : x;
+        gc = to_f32<T>(gyrow[t]);
+        if (zrow) gc *= silu_f(to_f32<T>(zrow[t]));
+      }
+      const float St = S + wave_inclusive_sum(dt);
 #pragma unroll
-  for (int n = 0; n < kStates; ++n) {
-    float m = lane_broadcast(wave_inclusive_sum(acc[n]), kWaveLanes - 1);
-    asm volatile("" : "+s"(m));  // formed by the whole wave, then stored by lane 0
-    if (lane == 0) {
-      p.mu0[base + n] = m;
-      p.Pc[base + n] = fast_exp2(Aq[n] * S);
+      for (int n = 0; n < kG; ++n) {
+        const float cn = (in && n0 + n < N) ? to_f32<T>(Cb[(n0 + n) * p.L + t]) : 0.0f;
+        acc[n] = fmaf(fast_exp2(Aq[n] * St) * gc, cn, acc[n]);
+      }
+      S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(St), 63));
+      if (may_stop && fast_exp2(amax * S) <= 0x1p-40f) break;
+    }
+#pragma unroll
+    for (int n = 0; n < kG; ++n) {
+      float m = lane_broadcast(wave_inclusive_sum(acc[n]), kWaveLanes - 1);
+      asm volatile("" : "+s"(m));  // formed by the whole wave, then stored by lane 0
+      if (lane == 0 && n0 + n < N) {
+        p.mu0[base + n0 + n] = m;
+        p.Pc[base + n0 + n] = fast_exp2(Aq[n] * S);
+      }
     }
   }
 }
@@ -485,17 +490,18 @@ __global__ __launch_bounds__(64) void bwd_adj_kernel(BwdArgs p) {
 // from its right, from the last chunk (dh_final) to the first.
 __global__ __launch_bounds__(256) void bwd_adj_carry_kernel(BwdArgs p) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (gid >= p.batch * p.dim * kStates) return;
-  const int64_t bd = gid >> 4;
-  const int n = static_cast<int>(gid & 15);
+  const int N = p.N;
+  if (gid >= p.batch * p.dim * N) return;
+  const int64_t bd = gid / N;
+  const int n = static_cast<int>(gid - bd * N);
   const int nc = p.n_chunks;
   float mu = p.dh_final ? p.dh_final[gid] : 0.0f;
   for (int c = nc - 1; c >= 1; --c) {
-    const int64_t i = (bd * nc + c) * kStates + n;
+    const int64_t i = (bd * nc + c) * N + n;
     p.mu_in[i] = mu;
     mu = fmaf(p.Pc[i], mu, p.mu0[i]);
   }
-  p.mu_in[(bd * nc) * kStates + n] = mu;
+  p.mu_in[(bd * nc) * N + n] = mu;
 }
 
 // dB[b, n, t] (blockIdx.y = 0) or dC (1): the sum over channel groups of
@@ -509,11 +515,11 @@ __global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kerne
   const int lane = threadIdx.x & 63;
   const int slice = threadIdx.x >> 6;
   const int64_t ntb = (p.L + kReduceTokens - 1) / kReduceTokens;
-  const int64_t row = blockIdx.x / ntb;  // b * 16 + n
+  const int64_t row = blockIdx.x / ntb;  // b * N + n
   const int64_t t = (blockIdx.x - row * ntb) * kReduceTokens + lane * 4;
-  const int64_t b = row / kStates, n = row - b * kStates;
-  const float *part = (blockIdx.y ? p.pC : p.pB) + (b * p.groups * kStates + n) * p.L;
-  const int64_t gstride = kStates * p.L;
+  const int64_t b = row / p.N, n = row - b * p.N;
+  const float *part = (blockIdx.y ? p.pC : p.pB) + (b * p.groups * p.N + n) * p.L;
+  const int64_t gstride = p.N * p.L;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if ((p.L & 3) == 0 && t < p.L) {
     // This wave's groups slice, slice + 4, ... summed in order through a
@@ -585,13 +591,14 @@ __global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kerne
 // per-(b, d, chunk) partials, in that order.
 __global__ __launch_bounds__(256) void bwd_reduce_param_kernel(BwdArgs p) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= p.dim * kStates) return;
-  const int64_t d = i / kStates;
-  const int n = static_cast<int>(i % kStates);
+  const int N = p.N;
+  if (i >= p.dim * N) return;
+  const int64_t d = i / N;
+  const int n = static_cast<int>(i % N);
   const int nc = p.n_chunks;
   float sa = 0.0f;
   for (int64_t b = 0; b < p.batch; ++b)
-    for (int c = 0; c < nc; ++c) sa += p.pA[((b * p.dim + d) * nc + c) * kStates + n];
+    for (int c = 0; c < nc; ++c) sa += p.pA[((b * p.dim + d) * nc + c) * N + n];
   p.dA[i] = sa;
   if (n == 0) {
     float sd = 0.0f, sb = 0.0f;
@@ -614,7 +621,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
                        dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nthreads = a.batch * a.dim * kStates;
+    const int64_t nthreads = a.batch * a.dim * a.N;
     hipLaunchKernelGGL(bwd_adj_carry_kernel,
                        dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256), 0, s, a);
     e = hipGetLastError();
@@ -631,13 +638,13 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
                      dim3(kBwdThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nwg = a.batch * kStates * ((a.L + kReduceTokens - 1) / kReduceTokens);
+  const int64_t nwg = a.batch * a.N * ((a.L + kReduceTokens - 1) / kReduceTokens);
   hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>(nwg), 2), dim3(256), 0,
                      s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_param_kernel,
-                     dim3(static_cast<unsigned>((a.dim * kStates + 255) / 256)), dim3(256), 0,
+                     dim3(static_cast<unsigned>((a.dim * a.N + 255) / 256)), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }

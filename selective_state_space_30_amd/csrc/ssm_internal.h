@@ -8,7 +8,8 @@
 
 namespace ssm {
 
-constexpr int kStates = 16;          // d_state supported by this build
+constexpr int kStates = 16;          // d_state of the tuned instances
+constexpr int kMaxStates = 64;       // any d_state up to this: one state per lane
 constexpr int kWaveLanes = 64;       // one channel per 64-lane wave
 constexpr int kWavesPerGroup = 4;    // waves (channels) per workgroup
 constexpr int kChannelsPerGroup = kWavesPerGroup;                  // 4
@@ -30,6 +31,7 @@ struct ScanArgs {
   float *ws_S;                        // split mode: chunk sums of dt (b,d,c)
   float *ws_hin;                      // split mode: chunk incoming states (b,d,c,n)
   int64_t batch, dim, L;
+  int N;                              // d_state (kStates: the tuned instances)
   int64_t chunk_len;                  // tokens per chunk (== L when not split)
   int n_chunks;
   int softplus;                       // 1: dt = softplus(delta + bias)
@@ -59,6 +61,7 @@ struct BwdArgs {
   float *pD, *pbias;                  // (batch, dim, n_chunks) partial dD, dbias
   float *dA, *dB, *dC, *dD, *dbias;   // reduced outputs (dD, dbias: or null)
   int64_t batch, dim, L;
+  int N;                              // d_state (<= kMaxStates: lane n = state n)
   int64_t groups;                     // ceil(dim / kBwdWaves)
   int nblk;                           // ceil(L / 1024)
   int softplus;
@@ -108,6 +111,7 @@ struct StepArgs {
   const float *A, *D, *bias;
   void *y;
   int64_t batch, dim;
+  int N;                              // d_state
   int softplus;
   int zoh;
   // conv prologue (d_conv > 0): u = silu(conv_b + sum_k conv_w[d, k] *
@@ -123,7 +127,7 @@ struct StepArgs {
 struct SplitLayout {
   size_t off_H, off_S, off_hin, total_bytes;
 };
-SplitLayout split_layout(int64_t batch, int64_t dim, int64_t n_chunks);
+SplitLayout split_layout(int64_t batch, int64_t dim, int64_t N, int64_t n_chunks);
 
 // Size of the fixed device scratch of ssm_scan_fwd_noalloc (a split layout
 // must fit in it) and its device address for the device of `stream`
@@ -157,7 +161,8 @@ struct BwdLayout {
   size_t off_mu0, off_Pc, off_muin;       // sweep split
   size_t total_bytes;
 };
-BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t seqlen, int64_t elem_bytes);
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t N, int64_t seqlen,
+                     int64_t elem_bytes);
 const char *hip_error_string(int err);
 
 }  // namespace ssm

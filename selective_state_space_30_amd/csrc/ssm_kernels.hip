@@ -36,6 +36,7 @@
 
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "ssm_device.h"
 #include "ssm_internal.h"
@@ -57,6 +58,32 @@ using namespace dev;
 // nothing is masked; otherwise positions from ct1 on are identity steps
 // (dt = 0, u = 0) and are not stored.  hc[n]: the channel's state carried in
 // (wave-uniform), replaced by the state after the block.
+// The channel's A and carried state (both wave-uniform).  StaticStates:
+// the tuned 16 states in scalar registers, indexed by a fully unrolled
+// state loop.  LaneStates: any count up to 64, state n in lane n of a
+// vector register, read with v_readlane in a state loop that is not
+// unrolled.
+struct StaticStates {
+  static constexpr bool kStatic = true;
+  float A[kStates], h[kStates];
+  __device__ __forceinline__ float a(int n) const { return A[n]; }
+  __device__ __forceinline__ float get(int n) const { return h[n]; }
+  __device__ __forceinline__ void set(int n, float v) { h[n] = v; }
+};
+struct LaneStates {
+  static constexpr bool kStatic = false;
+  float Av, hv;
+  int lane;
+  __device__ __forceinline__ float a(int n) const { return lane_broadcast(Av, n); }
+  __device__ __forceinline__ float get(int n) const { return lane_broadcast(hv, n); }
+  __device__ __forceinline__ void set(int n, float v) {
+    asm volatile("" : "+s"(v));  // a wave-uniform value, formed before the select
+    hv = lane == n ? v : hv;
+  }
+};
+template <int kN>
+using StatesFor = typename std::conditional<kN == kStates, StaticStates, LaneStates>::type;
+
 // Instances that carry the next block's u and delta in registers across
 // the block loop: aligned fp32 rows with the Euler term and no conv
 // prologue (their register budget, sized for 3 waves per SIMD, has the 32
@@ -68,14 +95,14 @@ constexpr bool kPrefetch = sizeof(T) == 4 && kVec && !kConv && !kZoh && !kCkpt;
 // block of a chunk uses the fewest of 4, 8, 16 that cover it, so its state
 // loop costs about its share of a block rather than a whole one.
 template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kConv,
-          bool kZoh, bool kCkpt, int K = kTokensPerLane>
+          bool kZoh, bool kCkpt, int K = kTokensPerLane, typename SS>
 __device__ __forceinline__ void scan_block(
     const ScanArgs &p, int wave, int lane, int64_t t0, int64_t ct1,
     const T *__restrict__ Bb, const T *__restrict__ Cb,
     const T *__restrict__ urow, const T *__restrict__ drow,
     const T *__restrict__ zrow, T *__restrict__ yrow, T *__restrict__ ycrow,
-    bool ch_ok, float bias, float Dd, const float (&Ach)[kStates], float *sT,
-    float (&hc)[kStates], float &sdt_total, const float (&wc)[kMaxConv], float cb,
+    bool ch_ok, float bias, float Dd, SS &S, float *sT,
+    float &sdt_total, const float (&wc)[kMaxConv], float cb,
     float (&xc)[kMaxConv - 1], float (&upf)[kTokensPerLane],
     float (&dpf)[kTokensPerLane], bool use_pf, int64_t pf_t0) {
   static_assert(!kFull || K == kTokensPerLane, "full blocks: 16 tokens a lane");
@@ -85,8 +112,12 @@ __device__ __forceinline__ void scan_block(
   constexpr int KP = K == 4 ? 12 : K + 4;
   const int64_t tend = kFull ? t0 + kBlockTokens : ct1;
   const int64_t tl = t0 + static_cast<int64_t>(lane) * K;
-  constexpr int kPhases = kStates / 2;
+  constexpr bool kPf = kPrefetch<T, kVec, kConv, kZoh, kCkpt> && SS::kStatic;
+  const int nst = SS::kStatic ? kStates : p.N;  // states
+  const int nph = (nst + 1) / 2;                // phases of two states
   constexpr int kTileFloats = 2 * 2 * kWaveLanes * KP;
+  // B/C row of state r (an odd count's last phase stages its last row twice)
+  auto row = [&](int r) { return SS::kStatic ? r : (r < nst ? r : nst - 1); };
 
   // Staging role of this wave: state (2*ph + st) of matrix B or C (both
   // wave-uniform, so the row is a valid buffer base in the partial block);
@@ -96,7 +127,7 @@ __device__ __forceinline__ void scan_block(
   const int64_t tq = tl;
   const int toff = staging_offset<KP>(wave, lane);
   TileRun<T, K, kVec, kFull> run;
-  run.load(src + st * p.L, t0, tq, tend);
+  run.load(src + row(st) * p.L, t0, tq, tend);
 
   // This lane's tokens: the step dt (kept as dt*log2(e) for exp2), dt*u
   // and the D skip.
@@ -104,7 +135,7 @@ __device__ __forceinline__ void scan_block(
   float sdt = 0.0f;
   {
     float uu[K], dr[K];
-    if (kPrefetch<T, kVec, kConv, kZoh, kCkpt> && kFull && use_pf) {
+    if (kPf && kFull && use_pf) {
 #pragma unroll
       for (int j = 0; j < K; ++j) uu[j] = upf[j];
     } else {
@@ -135,7 +166,7 @@ __device__ __forceinline__ void scan_block(
         uu[j] = silu_f(acc);
       }
     }
-    if (kPrefetch<T, kVec, kConv, kZoh, kCkpt> && kFull && use_pf) {
+    if (kPf && kFull && use_pf) {
 #pragma unroll
       for (int j = 0; j < K; ++j) dr[j] = dpf[j];
     } else {
@@ -157,7 +188,7 @@ __device__ __forceinline__ void scan_block(
   const float sdtl = sdt * kLog2e;
   // u and delta of the full block at pf_t0 (the next one, or this one
   // again when none follows), in flight during this block's state loop
-  if constexpr (kPrefetch<T, kVec, kConv, kZoh, kCkpt> && kFull) {
+  if constexpr (kPf && kFull) {
     const int64_t tlp = pf_t0 + static_cast<int64_t>(lane) * K;
     load_run<T, K, kVec, true>(urow, pf_t0, tlp, pf_t0 + kBlockTokens, upf);
     load_run<T, K, kVec, true>(drow, pf_t0, tlp, pf_t0 + kBlockTokens, dpf);
@@ -166,16 +197,19 @@ __device__ __forceinline__ void scan_block(
   // B and C are staged two states at a time in a double-buffered LDS tile
   // (tile[buffer][state][B|C][lane run][KP]); while the 4 waves compute
   // phase ph, each thread already holds phase ph+1's run in registers.
-#pragma unroll
-  for (int ph = 0; ph < kPhases; ++ph) {
-    if (ph + 1 < kPhases)
-      run.load(src + (2 * (ph + 1) + st) * p.L, t0, tq, tend);
+  // (the tuned instances unroll all 8 phases; the others loop)
+  constexpr int kPhaseUnroll = SS::kStatic ? kStates / 2 : 1;
+#pragma unroll kPhaseUnroll
+  for (int ph = 0; ph < nph; ++ph) {
+    if (ph + 1 < nph)
+      run.load(src + row(2 * (ph + 1) + st) * p.L, t0, tq, tend);
     __syncthreads();  // phase ph's tile is complete and visible
     const float *tile = sT + (ph & 1) * kTileFloats;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int n = 2 * ph + s2;
-      float An = Ach[n];
+      if (!SS::kStatic && n >= nst) break;  // an odd count's last phase
+      float An = S.a(n);
       asm volatile("" : "+s"(An));  // keep this state's work after the previous state's
       const float *pb = &tile[((s2 * 2 + 0) * kWaveLanes + lane) * KP];
       const float *pc = &tile[((s2 * 2 + 1) * kWaveLanes + lane) * KP];
@@ -203,21 +237,22 @@ __device__ __forceinline__ void scan_block(
       for (int j = 1; j < K; ++j) H = fmaf(a[j], H, bb[j]);
       float P = fast_exp2(sdtl * An);
       // The carried state enters through lane 0, then the maps compose.
-      H = fmaf(P, lane == 0 ? hc[n] : 0.0f, H);
+      const float hcn = S.get(n);
+      H = fmaf(P, lane == 0 ? hcn : 0.0f, H);
       wave_affine_scan(P, H);
       // H_i is the true state after lane i's last token; lane i starts from
       // lane i-1's (lane 0 from the carried state) and replays its tokens.
-      float h = wave_shift_in(H, hc[n]);
+      float h = wave_shift_in(H, hcn);
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         h = fmaf(a[j], h, bb[j]);
         y[j] = fmaf(pc[j], h, y[j]);
       }
-      hc[n] = lane_broadcast(h, kWaveLanes - 1);
+      S.set(n, lane_broadcast(h, kWaveLanes - 1));
     }
     // Every wave has passed this phase's barrier, so the other buffer (read
     // in phase ph-1) is free: fill it with phase ph+1.
-    if (ph + 1 < kPhases) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
+    if (ph + 1 < nph) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
   }
 
   // checkpoint instance: the pre-gate output, for the backward's dz
@@ -241,7 +276,9 @@ __device__ __forceinline__ void scan_block(
 template <typename T, bool kVec, bool kZoh>
 constexpr int kOccupancy = (sizeof(T) == 2 && kVec && !kZoh) ? 4 : 3;
 
-template <typename T, bool kVec, bool kSoftplus, bool kConv, bool kZoh, bool kCkpt = false>
+// kN: kStates (the tuned 16-state instances) or 0 (any d_state up to 64).
+template <typename T, bool kVec, bool kSoftplus, bool kConv, bool kZoh, bool kCkpt = false,
+          int kN = kStates>
 __global__ __launch_bounds__(kWaveLanes * kWavesPerGroup)
 __attribute__((amdgpu_waves_per_eu(kOccupancy<T, kVec, kZoh>)))
 void scan_kernel(ScanArgs p) {
@@ -260,23 +297,33 @@ void scan_kernel(ScanArgs p) {
   const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
   const int64_t bd = b * p.dim + d;
 
-  float Ach[kStates];  // the channel's A (wave-uniform)
+  // the channel's A and carried state (wave-uniform)
+  using SS = StatesFor<kN>;
+  constexpr bool kStatic = SS::kStatic;
+  const int N = kStatic ? kStates : p.N;
+  SS S;
+  if constexpr (kStatic) {
 #pragma unroll
-  for (int n = 0; n < kStates; ++n) Ach[n] = p.A[d * kStates + n];
+    for (int n = 0; n < kStates; ++n) S.A[n] = p.A[d * kStates + n];
+#pragma unroll
+    for (int n = 0; n < kStates; ++n)
+      S.h[n] = (chunk == 0 && p.h0) ? p.h0[bd * kStates + n] : 0.0f;
+  } else {
+    S.lane = lane;
+    const int ls = lane < N ? lane : 0;  // clamped for reads
+    S.Av = p.A[d * N + ls];
+    S.hv = (chunk == 0 && p.h0 && lane < N) ? p.h0[bd * N + lane] : 0.0f;
+  }
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
-  float hc[kStates];  // the channel's carried state (wave-uniform)
-#pragma unroll
-  for (int n = 0; n < kStates; ++n)
-    hc[n] = (chunk == 0 && p.h0) ? p.h0[bd * kStates + n] : 0.0f;
 
   const T *urow = static_cast<const T *>(kConv ? p.x : p.u) + bd * p.L;
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
   T *yrow = static_cast<T *>(p.y) + bd * p.L;
   T *ycrow = (kCkpt && p.yc) ? static_cast<T *>(p.yc) + bd * p.L : nullptr;
-  const T *Bb = static_cast<const T *>(p.B) + b * kStates * p.L;
-  const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
+  const T *Bb = static_cast<const T *>(p.B) + b * N * p.L;
+  const T *Cb = static_cast<const T *>(p.C) + b * N * p.L;
   float sdt_total = 0.0f;
 
   // Conv prologue (wave-uniform): taps aligned to the last kMaxConv tokens
@@ -302,7 +349,7 @@ void scan_kernel(ScanArgs p) {
   // starts from a zero state; its blocks' sums of dt since the chunk start
   // go to ckpt_s, from which ckpt_fix_kernel adds the true incoming state.
   const int64_t nblk = (p.L + kBlockTokens - 1) / kBlockTokens;
-  float *ck = (kCkpt && ch_ok) ? p.ckpt + bd * nblk * kStates : nullptr;
+  float *ck = (kCkpt && ch_ok) ? p.ckpt + bd * nblk * N : nullptr;
   auto store_ckpt = [&](int64_t t0) {
     if (kCkpt && ck) {
       if (p.ckpt_s) {
@@ -310,9 +357,13 @@ void scan_kernel(ScanArgs p) {
         asm volatile("" : "+s"(s));  // formed by the whole wave, then stored by lane 0
         if (lane == 0) p.ckpt_s[bd * nblk + t0 / kBlockTokens] = s;
       }
-      if (lane == 0) {
+      if constexpr (kStatic) {
+        if (lane == 0) {
 #pragma unroll
-        for (int n = 0; n < kStates; ++n) ck[(t0 / kBlockTokens) * kStates + n] = hc[n];
+          for (int n = 0; n < kStates; ++n) ck[(t0 / kBlockTokens) * kStates + n] = S.h[n];
+        }
+      } else {
+        if (lane < N) ck[(t0 / kBlockTokens) * N + lane] = S.hv;
       }
     }
   };
@@ -324,8 +375,8 @@ void scan_kernel(ScanArgs p) {
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens) {
     store_ckpt(t0);
     scan_block<T, kVec, true, kSoftplus, kConv, kZoh, kCkpt>(
-        p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, Ach,
-        sT, hc, sdt_total, wc, cb, xc,
+        p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, S,
+        sT, sdt_total, wc, cb, xc,
         upf, dpf, t0 > ct0,
         t0 + 2 * kBlockTokens <= ct1 ? t0 + kBlockTokens : last_full);
   }
@@ -337,32 +388,37 @@ void scan_kernel(ScanArgs p) {
     if (rem <= 4 * kWaveLanes)
       scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt, 4>(
           p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
-          Ach, sT, hc, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0);
     else if (rem <= 8 * kWaveLanes)
       scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt, 8>(
           p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
-          Ach, sT, hc, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0);
     else
       scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt>(
           p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
-          Ach, sT, hc, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0);
   }
 
   if (!ch_ok) return;
-  if (p.n_chunks == 1) {
-    if (p.h_final && lane == 0) {
-#pragma unroll
-      for (int n = 0; n < kStates; ++n) p.h_final[bd * kStates + n] = hc[n];
-    }
-  } else {
-    // sum of dt over the chunk (all lanes), for the chunk carry
+  // the state after the chunk: the final state, or the chunk's end state
+  // (from its own start) and dt sum for the chunk carry
+  float *hout = p.n_chunks == 1 ? p.h_final
+                                : p.ws_H + (bd * p.n_chunks + chunk) * N;
+  if (p.n_chunks > 1) {
     float s = lane_broadcast(wave_inclusive_sum(sdt_total), kWaveLanes - 1);
     asm volatile("" : "+s"(s));  // formed by the whole wave, then stored by lane 0
-    if (lane == 0) {
-      const int64_t base = bd * p.n_chunks + chunk;
+    if (lane == 0) p.ws_S[bd * p.n_chunks + chunk] = s;
+  } else if (hout) {
+    hout += bd * N;
+  }
+  if (hout) {
+    if constexpr (kStatic) {
+      if (lane == 0) {
 #pragma unroll
-      for (int n = 0; n < kStates; ++n) p.ws_H[base * kStates + n] = hc[n];
-      p.ws_S[base] = s;
+        for (int n = 0; n < kStates; ++n) hout[n] = S.h[n];
+      }
+    } else {
+      if (lane < N) hout[lane] = S.hv;
     }
   }
 }
@@ -372,20 +428,20 @@ void scan_kernel(ScanArgs p) {
 // order, h_in[c+1] = exp(A * sum_dt[c]) * h_in[c] + H[c], and records each
 // chunk's incoming state; the last one is the sequence's final state.
 __global__ __launch_bounds__(256) void carry_kernel(ScanArgs p) {
+  const int N = p.N;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (gid >= p.batch * p.dim * kStates) return;
-  const int64_t bd = gid >> 4;
-  const int n = static_cast<int>(gid & 15);
+  if (gid >= p.batch * p.dim * N) return;
+  const int64_t bd = gid / N;
+  const int n = static_cast<int>(gid - bd * N);
   const int64_t d = bd % p.dim;
-  const float Aq = p.A[d * kStates + n] * kLog2e;
+  const float Aq = p.A[d * N + n] * kLog2e;
   const int nc = p.n_chunks;
-  float h = p.ws_H[(bd * nc) * kStates + n];
+  float h = p.ws_H[(bd * nc) * N + n];
   for (int c = 1; c < nc; ++c) {
-    p.ws_hin[(bd * nc + c) * kStates + n] = h;
-    h = fmaf(fast_exp2(Aq * p.ws_S[bd * nc + c]), h,
-             p.ws_H[(bd * nc + c) * kStates + n]);
+    p.ws_hin[(bd * nc + c) * N + n] = h;
+    h = fmaf(fast_exp2(Aq * p.ws_S[bd * nc + c]), h, p.ws_H[(bd * nc + c) * N + n]);
   }
-  if (p.h_final) p.h_final[bd * kStates + n] = h;
+  if (p.h_final) p.h_final[bd * N + n] = h;
 }
 
 // --------------------------------------------------- chunk fix-up -------
@@ -394,9 +450,13 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanArgs p) {
 // exp(A_n * S_t) * h_in,n, S_t = running sum of dt inside the chunk.  One
 // wave per (batch, channel, chunk), 64 tokens per step.  Stops once every
 // decay factor is below 2^-40 when the factors cannot grow again (all A < 0
-// and dt >= 0); otherwise covers the whole chunk.
-template <typename T>
+// and dt >= 0); otherwise covers the whole chunk.  kN = kStates keeps the
+// 16 states' A and h_in in registers; kN = 0 (any count up to 64) holds
+// state n in lane n and reads it with v_readlane.
+template <typename T, int kN>
 __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
+  constexpr bool kStatic = kN == kStates;
+  const int N = kStatic ? kStates : p.N;
   const int lane = threadIdx.x;
   const int64_t d = blockIdx.x;
   const int64_t b = blockIdx.y;
@@ -404,19 +464,26 @@ __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
   const int64_t bd = b * p.dim + d;
   const int64_t ct0 = static_cast<int64_t>(c) * p.chunk_len;
   const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
-  float Aq[kStates], hin[kStates];
+  float Aq[kStatic ? kStates : 1], hin[kStatic ? kStates : 1];
   float amax = -INFINITY;
+  if constexpr (kStatic) {
 #pragma unroll
-  for (int n = 0; n < kStates; ++n) {
-    Aq[n] = p.A[d * kStates + n] * kLog2e;
-    hin[n] = p.ws_hin[(bd * p.n_chunks + c) * kStates + n];
-    amax = fmaxf(amax, Aq[n]);
+    for (int n = 0; n < kStates; ++n) {
+      Aq[n] = p.A[d * kStates + n] * kLog2e;
+      hin[n] = p.ws_hin[(bd * p.n_chunks + c) * kStates + n];
+      amax = fmaxf(amax, Aq[n]);
+    }
+  } else {
+    const int ls = lane < N ? lane : 0;
+    Aq[0] = p.A[d * N + ls] * kLog2e;
+    hin[0] = p.ws_hin[(bd * p.n_chunks + c) * N + ls];
+    for (int n = 0; n < N; ++n) amax = fmaxf(amax, lane_broadcast(Aq[0], n));
   }
   const bool may_stop = p.softplus && amax < 0.0f;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const T *drow = static_cast<const T *>(p.delta) + bd * p.L;
   const T *zrow = p.z ? static_cast<const T *>(p.z) + bd * p.L : nullptr;
-  const T *Cb = static_cast<const T *>(p.C) + b * kStates * p.L;
+  const T *Cb = static_cast<const T *>(p.C) + b * N * p.L;
   T *yrow = static_cast<T *>(p.y) + bd * p.L;
   float S = 0.0f;
   for (int64_t t0 = ct0; t0 < ct1; t0 += 64) {
@@ -429,10 +496,18 @@ __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
     }
     const float St = S + wave_inclusive_sum(dt);
     float corr = 0.0f;
+    if constexpr (kStatic) {
 #pragma unroll
-    for (int n = 0; n < kStates; ++n) {
-      const float cn = in ? to_f32<T>(Cb[n * p.L + t]) : 0.0f;
-      corr = fmaf(cn, fast_exp2(Aq[n] * St) * hin[n], corr);
+      for (int n = 0; n < kStates; ++n) {
+        const float cn = in ? to_f32<T>(Cb[n * p.L + t]) : 0.0f;
+        corr = fmaf(cn, fast_exp2(Aq[n] * St) * hin[n], corr);
+      }
+    } else {
+      for (int n = 0; n < N; ++n) {
+        const float cn = in ? to_f32<T>(Cb[n * p.L + t]) : 0.0f;
+        corr = fmaf(cn, fast_exp2(lane_broadcast(Aq[0], n) * St) * lane_broadcast(hin[0], n),
+                    corr);
+      }
     }
     if (in) {
       const float g = zrow ? silu_f(to_f32<T>(zrow[t])) : 1.0f;
@@ -451,23 +526,24 @@ __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
 // incoming state itself).  One thread per (batch, channel, block, state)
 // over the blocks of chunks >= 1.
 __global__ __launch_bounds__(256) void ckpt_fix_kernel(ScanArgs p) {
+  const int N = p.N;
   const int64_t nblk = (p.L + kBlockTokens - 1) / kBlockTokens;
   const int64_t bpc = p.chunk_len / kBlockTokens;  // blocks per chunk
   const int64_t nfix = nblk - bpc;                 // blocks of chunks >= 1
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (gid >= p.batch * p.dim * nfix * kStates) return;
-  const int n = static_cast<int>(gid & 15);
-  const int64_t r = gid >> 4;
+  if (gid >= p.batch * p.dim * nfix * N) return;
+  const int64_t r = gid / N;
+  const int n = static_cast<int>(gid - r * N);
   const int64_t k = bpc + r % nfix;
   const int64_t bd = r / nfix;
   const int64_t c = k / bpc;
-  const float Aq = p.A[(bd % p.dim) * kStates + n] * kLog2e;
-  const float hin = p.ws_hin[(bd * p.n_chunks + c) * kStates + n];
-  float *q = p.ckpt + (bd * nblk + k) * kStates + n;
+  const float Aq = p.A[(bd % p.dim) * N + n] * kLog2e;
+  const float hin = p.ws_hin[(bd * p.n_chunks + c) * N + n];
+  float *q = p.ckpt + (bd * nblk + k) * N + n;
   *q = fmaf(fast_exp2(Aq * p.ckpt_s[bd * nblk + k]), hin, *q);
 }
 
-template <typename T, bool kVec>
+template <typename T, bool kVec, int kN>
 hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.dim + kChannelsPerGroup - 1) /
                                         kChannelsPerGroup),
@@ -476,30 +552,35 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   // (conv prologue, softplus, ZOH) -> kernel instance
   using KernelFn = void (*)(ScanArgs);
   static constexpr KernelFn kernels[8] = {
-      scan_kernel<T, kVec, false, false, false>, scan_kernel<T, kVec, true, false, false>,
-      scan_kernel<T, kVec, false, true, false>,  scan_kernel<T, kVec, true, true, false>,
-      scan_kernel<T, kVec, false, false, true>,  scan_kernel<T, kVec, true, false, true>,
-      scan_kernel<T, kVec, false, true, true>,   scan_kernel<T, kVec, true, true, true>};
+      scan_kernel<T, kVec, false, false, false, false, kN>,
+      scan_kernel<T, kVec, true, false, false, false, kN>,
+      scan_kernel<T, kVec, false, true, false, false, kN>,
+      scan_kernel<T, kVec, true, true, false, false, kN>,
+      scan_kernel<T, kVec, false, false, true, false, kN>,
+      scan_kernel<T, kVec, true, false, true, false, kN>,
+      scan_kernel<T, kVec, false, true, true, false, kN>,
+      scan_kernel<T, kVec, true, true, true, false, kN>};
   const int which = (a.softplus ? 1 : 0) | (a.x ? 2 : 0) | (a.zoh ? 4 : 0);
   // the backward's checkpoint pass (no conv prologue) has instances of its
   // own, so the forward instances carry none of its code
-  static constexpr KernelFn ckpt_kernels[4] = {scan_kernel<T, kVec, false, false, false, true>,
-                                               scan_kernel<T, kVec, true, false, false, true>,
-                                               scan_kernel<T, kVec, false, false, true, true>,
-                                               scan_kernel<T, kVec, true, false, true, true>};
+  static constexpr KernelFn ckpt_kernels[4] = {
+      scan_kernel<T, kVec, false, false, false, true, kN>,
+      scan_kernel<T, kVec, true, false, false, true, kN>,
+      scan_kernel<T, kVec, false, false, true, true, kN>,
+      scan_kernel<T, kVec, true, false, true, true, kN>};
   hipLaunchKernelGGL(a.ckpt ? ckpt_kernels[(a.softplus ? 1 : 0) | (a.zoh ? 2 : 0)]
                             : kernels[which], grid,
                      dim3(kWaveLanes * kWavesPerGroup), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
-  const int64_t nthreads = a.batch * a.dim * kStates;
+  const int64_t nthreads = a.batch * a.dim * a.N;
   hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>((nthreads + 255) / 256)),
                      dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 fgrid(static_cast<unsigned>(a.dim), static_cast<unsigned>(a.batch),
                    static_cast<unsigned>(a.n_chunks - 1));
-  hipLaunchKernelGGL((fixup_kernel<T>), fgrid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL((fixup_kernel<T, kN>), fgrid, dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || !a.ckpt) return e;
   if (a.yc) {
@@ -507,15 +588,20 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
     ScanArgs ac = a;
     ac.y = a.yc;
     ac.z = nullptr;
-    hipLaunchKernelGGL((fixup_kernel<T>), fgrid, dim3(64), 0, s, ac);
+    hipLaunchKernelGGL((fixup_kernel<T, kN>), fgrid, dim3(64), 0, s, ac);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t nblk = (a.L + kBlockTokens - 1) / kBlockTokens;
-  const int64_t nfix = a.batch * a.dim * (nblk - a.chunk_len / kBlockTokens) * kStates;
+  const int64_t nfix = a.batch * a.dim * (nblk - a.chunk_len / kBlockTokens) * a.N;
   hipLaunchKernelGGL(ckpt_fix_kernel, dim3(static_cast<unsigned>((nfix + 255) / 256)),
                      dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, bool kVec>
+hipError_t launch_scan_n(const ScanArgs &a, hipStream_t s) {
+  return a.N == kStates ? launch_scan_t<T, kVec, kStates>(a, s) : launch_scan_t<T, kVec, 0>(a, s);
 }
 
 }  // namespace
@@ -523,8 +609,8 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
 int launch_scan(const ScanArgs &a, bool bf16, bool vec, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (bf16)
-    return vec ? launch_scan_t<uint16_t, true>(a, s) : launch_scan_t<uint16_t, false>(a, s);
-  return vec ? launch_scan_t<float, true>(a, s) : launch_scan_t<float, false>(a, s);
+    return vec ? launch_scan_n<uint16_t, true>(a, s) : launch_scan_n<uint16_t, false>(a, s);
+  return vec ? launch_scan_n<float, true>(a, s) : launch_scan_n<float, false>(a, s);
 }
 
 // Device address of `scratch` on the device that `stream` belongs to (the

@@ -11,7 +11,8 @@
 // The fp32 state (batch, dim, 16) is read and written once per step, so the
 // kernel is bound by HBM: it is laid out for coalesced 16-byte accesses and
 // enough loads in flight, and its arithmetic is a few dozen instructions per
-// channel.
+// channel.  Other state counts (up to 64) take a plainer one-wave-per-channel
+// kernel.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -220,8 +221,76 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
   }
 }
 
+// Any other d_state up to 64: one wave per (batch, channel), state n in
+// lane n; the readout is a wave sum.  The same arithmetic per state as
+// step_kernel (and its conv window: the d_conv - 1 kept inputs, oldest
+// first, then x; the window moves by one).
+constexpr int kLaneStepWaves = 4;  // channels per workgroup
+
+template <typename T, bool kConv>
+__global__ __launch_bounds__(kLaneStepWaves * kWaveLanes) void step_lanes_kernel(StepArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kLaneStepWaves + (threadIdx.x >> 6);
+  const int64_t b = blockIdx.y;
+  const bool d_ok = d_raw < p.dim;
+  const int64_t d = d_ok ? d_raw : p.dim - 1;  // clamped for reads
+  const int N = p.N;
+  const bool on = lane < N;
+  const int ls = on ? lane : 0;  // clamped for reads
+  const int64_t ch = b * p.dim + d;
+  const float An = p.A[d * N + ls];
+  float h = p.state[ch * N + ls];
+  const float Bn = to_f32<T>(static_cast<const T *>(p.B)[b * N + ls]);
+  const float Cn = to_f32<T>(static_cast<const T *>(p.C)[b * N + ls]);
+  float x = to_f32<T>(static_cast<const T *>(p.x)[ch]);
+  const float dr = to_f32<T>(static_cast<const T *>(p.delta)[ch]);
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float Dd = p.D ? p.D[d] : 0.0f;
+  float wnew = 0.0f;  // lane k < d_conv - 1: the window's next entry k
+  int H = 0;
+  if constexpr (kConv) {
+    const int K = p.d_conv;
+    H = K - 1;
+    const T *cs = static_cast<const T *>(p.conv_state) + ch * (H > 0 ? H : 0);
+    float acc = p.conv_b ? p.conv_b[d] : 0.0f;
+    for (int k = 0; k < H; ++k) acc = fmaf(p.conv_w[d * K + k], to_f32<T>(cs[k]), acc);
+    acc = fmaf(p.conv_w[d * K + H], x, acc);
+    if (lane < H) wnew = lane + 1 < H ? to_f32<T>(cs[lane + 1]) : x;
+    x = silu_f(acc);
+  }
+  const float xr = dr + bias;
+  const float dt = p.softplus ? softplus_f(xr) : xr;
+  const float arg = dt * An * kLog2e;
+  const float e = fast_exp2(arg);
+  float inp = dt * x * Bn;
+  if (p.zoh)  // exact ZOH: coefficient (e - 1)/A in place of dt
+    inp = zoh_coeff(arg, e, dt * kLog2e, 1.0f / An) * (x * Bn);
+  h = fmaf(e, h, inp);
+  float sum = lane_broadcast(wave_inclusive_sum(on ? Cn * h : 0.0f), kWaveLanes - 1);
+  asm volatile("" : "+s"(sum));  // formed by the whole wave first
+  if (!d_ok) return;
+  if (on) p.state[ch * N + lane] = h;
+  if (kConv && lane < H) static_cast<T *>(p.conv_state)[ch * H + lane] = from_f32<T>(wnew);
+  if (lane == 0) {
+    float yv = fmaf(Dd, x, sum);
+    if (p.z) yv *= silu_f(to_f32<T>(static_cast<const T *>(p.z)[ch]));
+    static_cast<T *>(p.y)[ch] = from_f32<T>(yv);
+  }
+}
+
 template <typename T, bool kVec>
 hipError_t launch_step_t(const StepArgs &a, hipStream_t s) {
+  if (a.N != kStates) {
+    const dim3 lgrid(static_cast<unsigned>((a.dim + kLaneStepWaves - 1) / kLaneStepWaves),
+                     static_cast<unsigned>(a.batch));
+    if (a.d_conv > 0)
+      hipLaunchKernelGGL((step_lanes_kernel<T, true>), lgrid, dim3(kLaneStepWaves * kWaveLanes),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((step_lanes_kernel<T, false>), lgrid, dim3(kLaneStepWaves * kWaveLanes),
+                         0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((a.dim + kStepChannels - 1) / kStepChannels),
                   static_cast<unsigned>((a.batch + kStepBatch - 1) / kStepBatch));
   if (a.d_conv > 0)
