@@ -241,14 +241,14 @@ int ssm_conv_state_update(float *state, void *conv_state, const void *x,
 
 /* Bytes of caller-provided device workspace ssm_scan_bwd needs for this
  * shape and activation dtype: the block-start checkpoints
- * (batch*dim*ceil(seqlen/1024)*16 fp32), the pre-gate output (batch*dim*
- * seqlen, activation dtype), per-workgroup partial sums of dB and dC
- * (2 * batch*ceil(dim/8)*16*seqlen fp32: a workgroup holds 8 channels), and
- * per-(channel, chunk) partials of dA, dD and the bias.  Shapes with few
- * channels and long rows split the sequence (below) and add, each under
- * 1 % of the partial sums: the checkpoint pass's per-block dt sums and
- * per-chunk states, and the sweep's per-chunk adjoints (3 x batch*dim*
- * chunks*16 fp32). */
+ * (batch*dim*ceil(seqlen/1024)*dstate fp32), the pre-gate output
+ * (batch*dim*seqlen, activation dtype), per-workgroup partial sums of dB and
+ * dC (2 * batch*ceil(dim/8)*dstate*seqlen fp32: a workgroup holds 8
+ * channels), and per-(channel, chunk) partials of dA, dD and the bias.
+ * Shapes with few channels and long rows split the sequence (below) and
+ * add, each under 1 % of the partial sums: the checkpoint pass's per-block
+ * dt sums and per-chunk states, and the sweep's per-chunk adjoints (3 x
+ * batch*dim*chunks*dstate fp32). */
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                 int64_t seqlen, int dtype, size_t *bytes);
 

@@ -639,7 +639,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nwg = a.batch * a.N * ((a.L + kReduceTokens - 1) / kReduceTokens);
-  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>(nwg), 2), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>(nwg), 2),
+                     dim3(kReduceWaves * kWaveLanes), 0,
                      s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
