@@ -869,8 +869,8 @@ def _cpu_model():
 
 # bf16 activations, vector loads, softplus on, no conv prologue, Euler input,
 # not the checkpoint pass
-SCAN_KERNEL = "scan_kernel<unsigned short, true, true, false, false, false>"
-CKPT_KERNEL = "scan_kernel<unsigned short, true, true, false, false, true>"
+SCAN_KERNEL = "scan_kernel<unsigned short, true, true, false, false, false, 16>"
+CKPT_KERNEL = "scan_kernel<unsigned short, true, true, false, false, true, 16>"
 # the Euler backward sweep (bf16, vector loads, softplus, no ZOH); the
 # --only-bwd run also times the ZOH and conv-prologue backward, whose
 # kernels are left out of that summary
@@ -1041,6 +1041,9 @@ def summarize_workload(d, rows, per_dispatch, fetch_scale, write_scale,
     traffic per dispatch from the ``--<only> --steps 3`` counter passes under
     DIR/<tag>fetch and DIR/<tag>write, scaled by the same copy calibration
     as the scan kernel's; every listed kernel runs once per call."""
+    import csv
+    import statistics
+
     def match(k):
         return any(k.startswith(p) for p in keys)
     txt = ["# %s" % title,
@@ -1053,6 +1056,25 @@ def summarize_workload(d, rows, per_dispatch, fetch_scale, write_scale,
                 k[:90], r["Calls"], float(r["AverageNs"]) / 1e3,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
                 float(r["TotalDurationNs"]) / 1e6))
+    # a kernel that other workloads of the benchmark launch too (another
+    # shape, the same instance): its dispatches by launch grid
+    by = {}
+    for f in _csvs(os.path.join(d, "trace"), "_kernel_trace.csv"):
+        for r in csv.DictReader(open(f)):
+            k = _kernel_key(r["Kernel_Name"])
+            if match(k):
+                g = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]),
+                     int(r["Grid_Size_Z"]))
+                by.setdefault(k, {}).setdefault(g, []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    for k in sorted(by):
+        if len(by[k]) < 2:
+            continue
+        txt.append("# %s per launch grid (threads), from the kernel trace:" % k[:90])
+        for g in sorted(by[k], key=lambda g: -len(by[k][g])):
+            v = by[k][g]
+            txt.append("grid %dx%dx%d | %d | %.2f | %.2f | %.2f | %.3f" % (
+                g + (len(v), statistics.mean(v), min(v), max(v), sum(v) / 1e3)))
     if not os.path.isdir(os.path.join(d, tag + "fetch")):
         return []
     fetch = per_dispatch(tag + "fetch", "FETCH_SIZE")
