@@ -842,6 +842,33 @@ def cpu_baseline(inp, cfg, nbytes, log):
                              part["delta_bias"], True, False, None, threads=1)
         times1.append(time.perf_counter() - t1)
     sec1 = statistics.median(times1)
+
+    # the 130M-shaped layer whole (median of 3) and a bounded sample of the
+    # long-context workload (64 channels over all 2^20 tokens, once), on the
+    # same threads
+    import synthetic as syn
+
+    def host_inputs(c, **over):
+        t = syn.make_scan_inputs(c, "cpu", **over)
+        return {k: (v.double().numpy() if hasattr(v, "double") else v)
+                for k, v in t.items()}
+
+    def run_oracle(h, th):
+        t0 = time.perf_counter()
+        oracle.scan_threaded(h["u"], h["delta"], h["A"], h["B"], h["C"], h["D"],
+                             h["z"], h["delta_bias"], True, False, None,
+                             threads=th)
+        return time.perf_counter() - t0
+    c1 = syn.MAMBA_130M
+    h1 = host_inputs(c1)
+    sec_c1 = statistics.median([run_oracle(h1, threads) for _ in range(3)])
+    del h1
+    c3 = syn.LONG_1M
+    n3 = 64
+    h3 = host_inputs(c3, dim=n3)
+    sec_c3 = run_oracle(h3, threads)
+    del h3
+    e3 = c3.batch * n3 * c3.seqlen
     return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": "the whole workload (%d x %d channels x %d tokens), "
@@ -853,6 +880,12 @@ def cpu_baseline(inp, cfg, nbytes, log):
             "one_thread_elements_per_s": round(cfg.batch * nd * cfg.seqlen / sec1),
             "one_thread_sample": "%d x %d channels x %d tokens, median %.2f s" % (
                 cfg.batch, nd, cfg.seqlen, sec1),
+            c1.name: {"elements_per_s": round(c1.elements / sec_c1),
+                      "GBps": round(syn.algorithmic_bytes(c1) / sec_c1 / 1e9, 4),
+                      "sample": "whole workload, median of 3: %.2f s" % sec_c1},
+            c3.name: {"elements_per_s": round(e3 / sec_c3),
+                      "sample": "%d of its %d channels over all %d tokens, "
+                                "once: %.2f s" % (n3, c3.dim, c3.seqlen, sec_c3)},
             "cpu_model": _cpu_model()}
 
 
