@@ -179,15 +179,40 @@ def main():
     # (the clocks settling under its sustained VALU load) before it comes
     # down to its steady value, so the headline is timed on a GPU that has
     # been busy for a while (its own warm-up count is unchanged).
-    extras = None
-    if not (args.only_scan or args.no_extra):
-        extras = extra_workloads(torch, ssm, syn, dev, stream, log, ceil)
-
     def step(i):
         s = sets[i % 3]
         ssm.ssm_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"],
                          s["z"], s["delta_bias"], True, None,
                          y=s["y"], h_final=s["h_final"], stream=stream)
+
+    extras = None
+    if not (args.only_scan or args.no_extra):
+        extras = extra_workloads(torch, ssm, syn, dev, stream, log, ceil)
+        # the last of them: the headline step 300 times back to back, timed
+        # per step, so the settling of the clock under this load is on
+        # record (by position in the run); the headline's own warm-up and
+        # timed steps follow it
+        n_ss = 300
+        log("consecutive steps: %d headline steps back to back" % n_ss)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ss + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n_ss):
+            step(i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n_ss)]
+
+        def mean(v):
+            return round(sum(v) / len(v), 1)
+        extras[cfg.name + "_consecutive_steps"] = {
+            "steps": n_ss, "us_mean_steps_0_19": mean(us[:20]),
+            "us_mean_steps_20_99": mean(us[20:100]),
+            "us_mean_steps_100_299": mean(us[100:]),
+            "us_median": round(sorted(us)[n_ss // 2], 1), "us_min": round(min(us), 1),
+            "note": "the headline step run back to back after the other "
+                    "workloads, one event per step: the step time by position "
+                    "shows the clock settling under the sustained load"}
 
     for i in range(args.warmup):
         step(i)
