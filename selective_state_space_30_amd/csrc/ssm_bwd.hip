@@ -102,26 +102,63 @@ __device__ __forceinline__ void flush_state(const float *sR, int tid, float *pB_
   store_run<float, kPer, kVec, kFull>(row, t0, t0 + run * K + j0, tend, v);
 }
 
-// Per-state values of one channel kept one state per lane (lane n holds
-// state n) in a single register instead of 16 scalar registers.
-__device__ __forceinline__ float state_of(float v, int n) { return lane_broadcast(v, n); }
-__device__ __forceinline__ float set_state(float v, int lane, int n, float x) {
-  return lane == n ? x : v;
+// Per-state values of one channel (wave-uniform), state n in lane n % 64
+// of register n / 64 of kR vector registers (up to 64 kR states) rather
+// than N scalar registers; the register of a state is picked by the
+// wave-uniform n.
+template <int kR>
+struct PerState {
+  float v[kR];
+};
+template <int kR>
+__device__ __forceinline__ float state_of(const PerState<kR> &s, int n) {
+  if constexpr (kR == 1) {
+    return lane_broadcast(s.v[0], n);
+  } else {
+    const int k = n >> 6, l = n & 63;
+    float r = lane_broadcast(s.v[0], l);
+#pragma unroll
+    for (int i = 1; i < kR; ++i) r = k == i ? lane_broadcast(s.v[i], l) : r;
+    return r;
+  }
+}
+// x must be wave-uniform and already formed by the whole wave
+template <int kR>
+__device__ __forceinline__ void set_state(PerState<kR> &s, int lane, int n, float x) {
+  if constexpr (kR == 1) {
+    s.v[0] = lane == n ? x : s.v[0];
+  } else {
+    const int k = n >> 6, l = n & 63;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) s.v[i] = (k == i && lane == l) ? x : s.v[i];
+  }
+}
+template <int kR>
+__device__ __forceinline__ void add_state(PerState<kR> &s, int lane, int n, float x) {
+  if constexpr (kR == 1) {
+    s.v[0] += lane == n ? x : 0.0f;
+  } else {
+    const int k = n >> 6, l = n & 63;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) s.v[i] += (k == i && lane == l) ? x : 0.0f;
+  }
 }
 
 // One block of one channel, in reverse.  hfv: the forward states entering
-// the block (checkpoint; lane n = state n); muv: dL/dh flowing in from the
-// right of the block (replaced by what flows out of its first token); dAv:
-// running dA sums of the channel (lane n = state n, already times 1/ln2).
+// the block (checkpoint); muv: dL/dh flowing in from the right of the block
+// (replaced by what flows out of its first token); dAv: running dA sums of
+// the channel (already times 1/ln2); all per state as PerState<kR>.
 // K: tokens per lane.  Full blocks use kTokensPerLane; the partial last
 // block uses the fewest of 4, 8, 16 that cover it, so its loops cost about
 // its share of a block.
-template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kZoh, int K = kTokensPerLane>
+template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kZoh, int kR,
+          int K = kTokensPerLane>
 __device__ __forceinline__ void bwd_block(
     const BwdArgs &p, int wave, int lane, int64_t t0, int64_t tend, int64_t b,
     int64_t bd, int64_t g, const T *__restrict__ Bb, const T *__restrict__ Cb,
-    bool ch_ok, float bias, float Dd, float Av, float hfv, float &muv, float &dAv,
-    float &dDl, float &dbl, float *sT, float *sR, int tid) {
+    bool ch_ok, float bias, float Dd, const PerState<kR> &Av, const PerState<kR> &hfv,
+    PerState<kR> &muv, PerState<kR> &dAv, float &dDl, float &dbl, float *sT, float *sR,
+    int tid) {
   static_assert(!kFull || K == kTokensPerLane, "full blocks: 16 tokens a lane");
   static_assert(K == 4 || K == 8 || K == 16, "runs of 4, 8 or 16 tokens");
   constexpr int KP = K == 4 ? 12 : K + 4;  // a multiple of 4 floats: 16-byte runs
@@ -284,7 +321,7 @@ __device__ __forceinline__ void bwd_block(
     // may move the DPP / readlane under the lane == n mask
     float mu_out = lane_broadcast(Mr, kWaveLanes - 1);
     asm volatile("" : "+s"(mu_out));
-    muv = set_state(muv, lane, n, mu_out);
+    set_state(muv, lane, n, mu_out);
     float m = wave_reverse(wave_shift_in(Mr, mun), lane);
     // reverse replay: lambda_j = dL/dh_j, then the gradients of token j
     float dA_acc = 0.0f;
@@ -319,7 +356,7 @@ __device__ __forceinline__ void bwd_block(
     }
     float dA_sum = lane_broadcast(wave_inclusive_sum(dA_acc), kWaveLanes - 1);
     asm volatile("" : "+s"(dA_sum));
-    dAv += lane == n ? dA_sum : 0.0f;
+    add_state(dAv, lane, n, dA_sum);
     if (stager && n + 1 < p.N) run.store(sT + ((n + 1) & 1) * kBwdTileFloats, toff);
     __syncthreads();  // state n's contributions and state n+1's tile are in LDS
     flush_state<kVec, kFull, K>(reg, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
@@ -342,7 +379,8 @@ __device__ __forceinline__ void bwd_block(
   }
 }
 
-template <typename T, bool kVec, bool kSoftplus, bool kZoh>
+// kR: vector registers per per-state value (1: up to 64 states; 4: up to 256)
+template <typename T, bool kVec, bool kSoftplus, bool kZoh, int kR>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs p) {
   __shared__ float sT[2 * kBwdTileFloats];  // one state's B, C (fp32), double-buffered
@@ -360,15 +398,21 @@ void bwd_kernel(BwdArgs p) {
   const int64_t bd = b * p.dim + d;
   const int64_t bdc = bd * p.n_chunks + c;
   const int N = p.N;
-  const int ls = lane < N ? lane : 0;  // lane n <-> state n
   const int64_t ct0 = static_cast<int64_t>(c) * p.chunk_len;
   const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
 
-  const float Av = p.A[d * N + ls];
-  // dL/dh entering the chunk's last token from the right
-  float muv = p.n_chunks > 1 ? p.mu_in[bdc * N + ls]
-                             : (p.dh_final ? p.dh_final[bd * N + ls] : 0.0f);
-  float dAv = 0.0f;
+  // per state: A, dL/dh entering the chunk's last token from the right,
+  // the dA sums (state n in lane n % 64 of register n / 64; reads clamped)
+  PerState<kR> Av, muv, dAv;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int n = kWaveLanes * i + lane;
+    const int ns = n < N ? n : 0;
+    Av.v[i] = p.A[d * N + ns];
+    muv.v[i] = p.n_chunks > 1 ? p.mu_in[bdc * N + ns]
+                              : (p.dh_final ? p.dh_final[bd * N + ns] : 0.0f);
+    dAv.v[i] = 0.0f;
+  }
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
   const T *Bb = static_cast<const T *>(p.B) + b * N * p.L;
@@ -378,35 +422,48 @@ void bwd_kernel(BwdArgs p) {
   // the chunk's blocks (chunks start on block boundaries; only the last
   // chunk can end in a partial block), last to first
   const float *ck = p.ckpt + (bd * p.nblk + ct0 / kBlockTokens) * N;
+  auto ckpt_of = [&](int64_t k) {  // the forward states entering block k
+    PerState<kR> h;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const int n = kWaveLanes * i + lane;
+      h.v[i] = ck[k * N + (n < N ? n : 0)];
+    }
+    return h;
+  };
   const int64_t nfull = (ct1 - ct0) / kBlockTokens;
   const int64_t rem = (ct1 - ct0) - nfull * kBlockTokens;
   if (rem > 0) {  // the partial last block comes first
-    const float hf = ck[nfull * N + ls];
+    const PerState<kR> hf = ckpt_of(nfull);
     const int64_t t0 = ct0 + nfull * kBlockTokens;
     if (rem <= 4 * kWaveLanes)
-      bwd_block<T, false, false, kSoftplus, kZoh, 4>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+      bwd_block<T, false, false, kSoftplus, kZoh, kR, 4>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
                                                      ch_ok, bias, Dd, Av, hf, muv, dAv, dDl,
                                                      dbl, sT, sR, tid);
     else if (rem <= 8 * kWaveLanes)
-      bwd_block<T, false, false, kSoftplus, kZoh, 8>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+      bwd_block<T, false, false, kSoftplus, kZoh, kR, 8>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
                                                      ch_ok, bias, Dd, Av, hf, muv, dAv, dDl,
                                                      dbl, sT, sR, tid);
     else
-      bwd_block<T, false, false, kSoftplus, kZoh>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+      bwd_block<T, false, false, kSoftplus, kZoh, kR>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
                                                   ch_ok, bias, Dd, Av, hf, muv, dAv, dDl, dbl,
                                                   sT, sR, tid);
   }
 #pragma unroll 1
   for (int64_t k = nfull - 1; k >= 0; --k)
-    bwd_block<T, kVec, true, kSoftplus, kZoh>(p, wave, lane, ct0 + k * kBlockTokens,
-                                        ct0 + (k + 1) * kBlockTokens, b, bd, g, Bb, Cb, ch_ok,
-                                        bias, Dd, Av, ck[k * N + ls], muv, dAv, dDl, dbl,
-                                        sT, sR, tid);
+    bwd_block<T, kVec, true, kSoftplus, kZoh, kR>(p, wave, lane, ct0 + k * kBlockTokens,
+                                            ct0 + (k + 1) * kBlockTokens, b, bd, g, Bb, Cb,
+                                            ch_ok, bias, Dd, Av, ckpt_of(k), muv, dAv, dDl,
+                                            dbl, sT, sR, tid);
 
   if (!ch_ok) return;
-  if (lane < N) {
-    p.pA[bdc * N + lane] = dAv * kLn2;  // sum of q * dt = q * dtl * ln2
-    if (p.dh0 && c == 0) p.dh0[bd * N + lane] = muv;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int n = kWaveLanes * i + lane;
+    if (n < N) {
+      p.pA[bdc * N + n] = dAv.v[i] * kLn2;  // sum of q * dt = q * dtl * ln2
+      if (p.dh0 && c == 0) p.dh0[bd * N + n] = muv.v[i];
+    }
   }
   float sD = lane_broadcast(wave_inclusive_sum(dDl), kWaveLanes - 1);
   float sb = lane_broadcast(wave_inclusive_sum(dbl), kWaveLanes - 1);
@@ -630,11 +687,14 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.groups), static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(a.n_chunks));
   using Fn = void (*)(BwdArgs);
-  static constexpr Fn kernels[4] = {bwd_kernel<T, kVec, false, false>,
-                                    bwd_kernel<T, kVec, true, false>,
-                                    bwd_kernel<T, kVec, false, true>,
-                                    bwd_kernel<T, kVec, true, true>};
-  hipLaunchKernelGGL(kernels[(a.softplus ? 1 : 0) | (a.zoh ? 2 : 0)], grid,
+  // [more than 64 states][softplus | zoh]
+  static constexpr Fn kernels[2][4] = {
+      {bwd_kernel<T, kVec, false, false, 1>, bwd_kernel<T, kVec, true, false, 1>,
+       bwd_kernel<T, kVec, false, true, 1>, bwd_kernel<T, kVec, true, true, 1>},
+      {bwd_kernel<T, kVec, false, false, 4>, bwd_kernel<T, kVec, true, false, 4>,
+       bwd_kernel<T, kVec, false, true, 4>, bwd_kernel<T, kVec, true, true, 4>}};
+  hipLaunchKernelGGL(kernels[a.N > kWaveLanes ? 1 : 0][(a.softplus ? 1 : 0) | (a.zoh ? 2 : 0)],
+                     grid,
                      dim3(kBwdThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

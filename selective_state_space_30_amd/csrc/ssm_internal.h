@@ -9,7 +9,7 @@
 namespace ssm {
 
 constexpr int kStates = 16;          // d_state of the tuned instances
-constexpr int kMaxStates = 64;       // any d_state up to this: one state per lane
+constexpr int kMaxStates = 256;      // any d_state up to this (state n in lane n % 64)
 constexpr int kWaveLanes = 64;       // one channel per 64-lane wave
 constexpr int kWavesPerGroup = 4;    // waves (channels) per workgroup
 constexpr int kChannelsPerGroup = kWavesPerGroup;                  // 4
@@ -61,7 +61,7 @@ struct BwdArgs {
   float *pD, *pbias;                  // (batch, dim, n_chunks) partial dD, dbias
   float *dA, *dB, *dC, *dD, *dbias;   // reduced outputs (dD, dbias: or null)
   int64_t batch, dim, L;
-  int N;                              // d_state (<= kMaxStates: lane n = state n)
+  int N;                              // d_state (<= kMaxStates: lane n % 64, register n / 64)
   int64_t groups;                     // ceil(dim / kBwdWaves)
   int nblk;                           // ceil(L / 1024)
   int softplus;

@@ -60,9 +60,9 @@ using namespace dev;
 // (wave-uniform), replaced by the state after the block.
 // The channel's A and carried state (both wave-uniform).  StaticStates:
 // the tuned 16 states in scalar registers, indexed by a fully unrolled
-// state loop.  LaneStates: any count up to 64, state n in lane n of a
-// vector register, read with v_readlane in a state loop that is not
-// unrolled.
+// state loop.  LaneStates<kR>: any count up to 64 * kR, state n in lane
+// n % 64 of vector register n / 64, read with v_readlane in a state loop
+// that is not unrolled (the register is picked by the wave-uniform n).
 struct StaticStates {
   static constexpr bool kStatic = true;
   float A[kStates], h[kStates];
@@ -70,19 +70,41 @@ struct StaticStates {
   __device__ __forceinline__ float get(int n) const { return h[n]; }
   __device__ __forceinline__ void set(int n, float v) { h[n] = v; }
 };
+template <int kR>
 struct LaneStates {
   static constexpr bool kStatic = false;
-  float Av, hv;
+  float Av[kR], hv[kR];
   int lane;
-  __device__ __forceinline__ float a(int n) const { return lane_broadcast(Av, n); }
-  __device__ __forceinline__ float get(int n) const { return lane_broadcast(hv, n); }
+  __device__ __forceinline__ static float pick(const float (&v)[kR], int n) {
+    if constexpr (kR == 1) {
+      return lane_broadcast(v[0], n);
+    } else {
+      const int k = n >> 6, l = n & 63;
+      float r = lane_broadcast(v[0], l);
+#pragma unroll
+      for (int i = 1; i < kR; ++i) r = k == i ? lane_broadcast(v[i], l) : r;
+      return r;
+    }
+  }
+  __device__ __forceinline__ float a(int n) const { return pick(Av, n); }
+  __device__ __forceinline__ float get(int n) const { return pick(hv, n); }
   __device__ __forceinline__ void set(int n, float v) {
     asm volatile("" : "+s"(v));  // a wave-uniform value, formed before the select
-    hv = lane == n ? v : hv;
+    if constexpr (kR == 1) {
+      hv[0] = lane == n ? v : hv[0];
+    } else {
+      const int k = n >> 6, l = n & 63;
+#pragma unroll
+      for (int i = 0; i < kR; ++i) hv[i] = (k == i && lane == l) ? v : hv[i];
+    }
   }
 };
+// kN: kStates (the tuned instances), kMaxLaneStates (up to 64 states) or
+// kMaxStates (up to 256)
+constexpr int kMaxLaneStates = kWaveLanes;
 template <int kN>
-using StatesFor = typename std::conditional<kN == kStates, StaticStates, LaneStates>::type;
+using StatesFor = typename std::conditional<
+    kN == kStates, StaticStates, LaneStates<(kN + kWaveLanes - 1) / kWaveLanes>>::type;
 
 // Instances that carry the next block's u and delta in registers across
 // the block loop: aligned fp32 rows with the Euler term and no conv
@@ -276,7 +298,8 @@ __device__ __forceinline__ void scan_block(
 template <typename T, bool kVec, bool kZoh>
 constexpr int kOccupancy = (sizeof(T) == 2 && kVec && !kZoh) ? 4 : 3;
 
-// kN: kStates (the tuned 16-state instances) or 0 (any d_state up to 64).
+// kN: kStates (the tuned 16-state instances), kMaxLaneStates (any d_state
+// up to 64) or kMaxStates (up to 256).
 template <typename T, bool kVec, bool kSoftplus, bool kConv, bool kZoh, bool kCkpt = false,
           int kN = kStates>
 __global__ __launch_bounds__(kWaveLanes * kWavesPerGroup)
@@ -310,9 +333,12 @@ void scan_kernel(ScanArgs p) {
       S.h[n] = (chunk == 0 && p.h0) ? p.h0[bd * kStates + n] : 0.0f;
   } else {
     S.lane = lane;
-    const int ls = lane < N ? lane : 0;  // clamped for reads
-    S.Av = p.A[d * N + ls];
-    S.hv = (chunk == 0 && p.h0 && lane < N) ? p.h0[bd * N + lane] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < int(sizeof(S.hv) / sizeof(float)); ++i) {
+      const int n = kWaveLanes * i + lane;
+      S.Av[i] = p.A[d * N + (n < N ? n : 0)];  // clamped for reads
+      S.hv[i] = (chunk == 0 && p.h0 && n < N) ? p.h0[bd * N + n] : 0.0f;
+    }
   }
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float Dd = p.D ? p.D[d] : 0.0f;
@@ -363,7 +389,11 @@ void scan_kernel(ScanArgs p) {
           for (int n = 0; n < kStates; ++n) ck[(t0 / kBlockTokens) * kStates + n] = S.h[n];
         }
       } else {
-        if (lane < N) ck[(t0 / kBlockTokens) * N + lane] = S.hv;
+#pragma unroll
+        for (int i = 0; i < int(sizeof(S.hv) / sizeof(float)); ++i) {
+          const int n = kWaveLanes * i + lane;
+          if (n < N) ck[(t0 / kBlockTokens) * N + n] = S.hv[i];
+        }
       }
     }
   };
@@ -418,7 +448,11 @@ void scan_kernel(ScanArgs p) {
         for (int n = 0; n < kStates; ++n) hout[n] = S.h[n];
       }
     } else {
-      if (lane < N) hout[lane] = S.hv;
+#pragma unroll
+      for (int i = 0; i < int(sizeof(S.hv) / sizeof(float)); ++i) {
+        const int n = kWaveLanes * i + lane;
+        if (n < N) hout[n] = S.hv[i];
+      }
     }
   }
 }
@@ -451,8 +485,8 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanArgs p) {
 // wave per (batch, channel, chunk), 64 tokens per step.  Stops once every
 // decay factor is below 2^-40 when the factors cannot grow again (all A < 0
 // and dt >= 0); otherwise covers the whole chunk.  kN = kStates keeps the
-// 16 states' A and h_in in registers; kN = 0 (any count up to 64) holds
-// state n in lane n and reads it with v_readlane.
+// 16 states' A and h_in in registers; kN = 0 (any other count) reads them
+// per state from memory (wave-uniform scalar loads).
 template <typename T, int kN>
 __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
   constexpr bool kStatic = kN == kStates;
@@ -466,18 +500,17 @@ __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
   const int64_t ct1 = ct0 + p.chunk_len < p.L ? ct0 + p.chunk_len : p.L;
   float Aq[kStatic ? kStates : 1], hin[kStatic ? kStates : 1];
   float amax = -INFINITY;
+  const float *Arow = p.A + d * N;
+  const float *hrow = p.ws_hin + (bd * p.n_chunks + c) * N;
   if constexpr (kStatic) {
 #pragma unroll
     for (int n = 0; n < kStates; ++n) {
-      Aq[n] = p.A[d * kStates + n] * kLog2e;
-      hin[n] = p.ws_hin[(bd * p.n_chunks + c) * kStates + n];
+      Aq[n] = Arow[n] * kLog2e;
+      hin[n] = hrow[n];
       amax = fmaxf(amax, Aq[n]);
     }
   } else {
-    const int ls = lane < N ? lane : 0;
-    Aq[0] = p.A[d * N + ls] * kLog2e;
-    hin[0] = p.ws_hin[(bd * p.n_chunks + c) * N + ls];
-    for (int n = 0; n < N; ++n) amax = fmaxf(amax, lane_broadcast(Aq[0], n));
+    for (int n = 0; n < N; ++n) amax = fmaxf(amax, Arow[n] * kLog2e);
   }
   const bool may_stop = p.softplus && amax < 0.0f;
   const float bias = p.bias ? p.bias[d] : 0.0f;
@@ -505,8 +538,7 @@ __global__ __launch_bounds__(64) void fixup_kernel(ScanArgs p) {
     } else {
       for (int n = 0; n < N; ++n) {
         const float cn = in ? to_f32<T>(Cb[n * p.L + t]) : 0.0f;
-        corr = fmaf(cn, fast_exp2(lane_broadcast(Aq[0], n) * St) * lane_broadcast(hin[0], n),
-                    corr);
+        corr = fmaf(cn, fast_exp2(Arow[n] * kLog2e * St) * hrow[n], corr);
       }
     }
     if (in) {
@@ -580,7 +612,8 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const dim3 fgrid(static_cast<unsigned>(a.dim), static_cast<unsigned>(a.batch),
                    static_cast<unsigned>(a.n_chunks - 1));
-  hipLaunchKernelGGL((fixup_kernel<T, kN>), fgrid, dim3(64), 0, s, a);
+  constexpr int kFixN = kN == kStates ? kStates : 0;
+  hipLaunchKernelGGL((fixup_kernel<T, kFixN>), fgrid, dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || !a.ckpt) return e;
   if (a.yc) {
@@ -588,7 +621,7 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
     ScanArgs ac = a;
     ac.y = a.yc;
     ac.z = nullptr;
-    hipLaunchKernelGGL((fixup_kernel<T, kN>), fgrid, dim3(64), 0, s, ac);
+    hipLaunchKernelGGL((fixup_kernel<T, kFixN>), fgrid, dim3(64), 0, s, ac);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -601,7 +634,9 @@ hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
 
 template <typename T, bool kVec>
 hipError_t launch_scan_n(const ScanArgs &a, hipStream_t s) {
-  return a.N == kStates ? launch_scan_t<T, kVec, kStates>(a, s) : launch_scan_t<T, kVec, 0>(a, s);
+  if (a.N == kStates) return launch_scan_t<T, kVec, kStates>(a, s);
+  if (a.N <= kMaxLaneStates) return launch_scan_t<T, kVec, kMaxLaneStates>(a, s);
+  return launch_scan_t<T, kVec, kMaxStates>(a, s);
 }
 
 }  // namespace

@@ -11,8 +11,8 @@
 // The fp32 state (batch, dim, 16) is read and written once per step, so the
 // kernel is bound by HBM: it is laid out for coalesced 16-byte accesses and
 // enough loads in flight, and its arithmetic is a few dozen instructions per
-// channel.  Other state counts (up to 64) take a plainer one-wave-per-channel
-// kernel.
+// channel.  Other state counts (up to 256) take a plainer
+// one-wave-per-channel kernel.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -221,11 +221,12 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p) {
   }
 }
 
-// Any other d_state up to 64: one wave per (batch, channel), state n in
-// lane n; the readout is a wave sum.  The same arithmetic per state as
-// step_kernel (and its conv window: the d_conv - 1 kept inputs, oldest
-// first, then x; the window moves by one).
+// Any other d_state up to 256: one wave per (batch, channel), state n in
+// lane n % 64 (up to four per lane); the readout is a wave sum.  The same
+// arithmetic per state as step_kernel (and its conv window: the d_conv - 1
+// kept inputs, oldest first, then x; the window moves by one).
 constexpr int kLaneStepWaves = 4;  // channels per workgroup
+constexpr int kLaneStepStates = 4;  // states per lane at most
 
 template <typename T, bool kConv>
 __global__ __launch_bounds__(kLaneStepWaves * kWaveLanes) void step_lanes_kernel(StepArgs p) {
@@ -235,13 +236,7 @@ __global__ __launch_bounds__(kLaneStepWaves * kWaveLanes) void step_lanes_kernel
   const bool d_ok = d_raw < p.dim;
   const int64_t d = d_ok ? d_raw : p.dim - 1;  // clamped for reads
   const int N = p.N;
-  const bool on = lane < N;
-  const int ls = on ? lane : 0;  // clamped for reads
   const int64_t ch = b * p.dim + d;
-  const float An = p.A[d * N + ls];
-  float h = p.state[ch * N + ls];
-  const float Bn = to_f32<T>(static_cast<const T *>(p.B)[b * N + ls]);
-  const float Cn = to_f32<T>(static_cast<const T *>(p.C)[b * N + ls]);
   float x = to_f32<T>(static_cast<const T *>(p.x)[ch]);
   const float dr = to_f32<T>(static_cast<const T *>(p.delta)[ch]);
   const float bias = p.bias ? p.bias[d] : 0.0f;
@@ -260,16 +255,32 @@ __global__ __launch_bounds__(kLaneStepWaves * kWaveLanes) void step_lanes_kernel
   }
   const float xr = dr + bias;
   const float dt = p.softplus ? softplus_f(xr) : xr;
-  const float arg = dt * An * kLog2e;
-  const float e = fast_exp2(arg);
-  float inp = dt * x * Bn;
-  if (p.zoh)  // exact ZOH: coefficient (e - 1)/A in place of dt
-    inp = zoh_coeff(arg, e, dt * kLog2e, 1.0f / An) * (x * Bn);
-  h = fmaf(e, h, inp);
-  float sum = lane_broadcast(wave_inclusive_sum(on ? Cn * h : 0.0f), kWaveLanes - 1);
+  float h[kLaneStepStates], part = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kLaneStepStates; ++i) {
+    const int n = kWaveLanes * i + lane;
+    const bool on = n < N;
+    const int ns = on ? n : 0;  // clamped for reads
+    const float An = p.A[d * N + ns];
+    const float Bn = to_f32<T>(static_cast<const T *>(p.B)[b * N + ns]);
+    const float Cn = to_f32<T>(static_cast<const T *>(p.C)[b * N + ns]);
+    h[i] = p.state[ch * N + ns];
+    const float arg = dt * An * kLog2e;
+    const float e = fast_exp2(arg);
+    float inp = dt * x * Bn;
+    if (p.zoh)  // exact ZOH: coefficient (e - 1)/A in place of dt
+      inp = zoh_coeff(arg, e, dt * kLog2e, 1.0f / An) * (x * Bn);
+    h[i] = fmaf(e, h[i], inp);
+    part += on ? Cn * h[i] : 0.0f;
+  }
+  float sum = lane_broadcast(wave_inclusive_sum(part), kWaveLanes - 1);
   asm volatile("" : "+s"(sum));  // formed by the whole wave first
   if (!d_ok) return;
-  if (on) p.state[ch * N + lane] = h;
+#pragma unroll
+  for (int i = 0; i < kLaneStepStates; ++i) {
+    const int n = kWaveLanes * i + lane;
+    if (n < N) p.state[ch * N + n] = h[i];
+  }
   if (kConv && lane < H) static_cast<T *>(p.conv_state)[ch * H + lane] = from_f32<T>(wnew);
   if (lane == 0) {
     float yv = fmaf(Dd, x, sum);

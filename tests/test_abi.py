@@ -83,8 +83,8 @@ INVALID_SCAN_CASES = [
     ("negative dim", dict(dim=-3), 1),
     ("zero seqlen", dict(seqlen=0), 1),
     ("zero dstate", dict(dstate=0), 1),
-    ("dstate 65 unsupported", dict(dstate=65), 2),
-    ("dstate 128 unsupported", dict(dstate=128), 2),
+    ("dstate 257 unsupported", dict(dstate=257), 2),
+    ("dstate 1024 unsupported", dict(dstate=1024), 2),
     ("bad dtype", dict(dtype=7), 1),
     ("unknown flag", dict(flags=0x10), 1),
     ("unknown flag bit 2", dict(flags=0x4), 1),
@@ -132,7 +132,7 @@ INVALID_STEP_CASES = [
     ("null x", dict(x=None), 1),
     ("null y", dict(y=None), 1),
     ("zero batch", dict(batch=0), 1),
-    ("dstate 65", dict(dstate=65), 2),
+    ("dstate 257", dict(dstate=257), 2),
     ("bad dtype", dict(dtype=-1), 1),
     ("unknown flag", dict(flags=4), 1),
     ("misaligned state", dict(state=FAKE + 2), 1),
@@ -202,7 +202,7 @@ def test_plan_and_workspace(lib):
     assert ssm.ssm_scan_plan(1, 4, 16, 3000, 100) == 1024
     assert ssm.ssm_scan_plan(1, 4, 16, 1000, 5000) == 1000
     with pytest.raises(ssm.SSMError):
-        ssm.ssm_scan_plan(1, 4, 65, 1000)
+        ssm.ssm_scan_plan(1, 4, 257, 1000)
 
 
 def test_last_error_is_cleared_by_success(lib):
@@ -256,7 +256,7 @@ INVALID_CONV_CASES = [
     ("misaligned conv_w", dict(w=FAKE + 0x08000002), 1),
     ("y aliases x", dict(y=FAKE + 32), 1),
     ("y overlaps conv_w", dict(y=FAKE + 0x08000000 - 16), 1),
-    ("dstate 65", dict(dstate=65), 2),
+    ("dstate 257", dict(dstate=257), 2),
     ("split without workspace", dict(chunk=1024, seqlen=4096), 3),
 ]
 
@@ -301,7 +301,7 @@ INVALID_BWD_CASES = [
     ("zoh flag, null dy", dict(flags=3, dy=None), 1),
     ("zoh flag with saved, small workspace", dict(flags=7, ws_bytes=4096), 3),
     ("unknown flag", dict(flags=8), 1),
-    ("dstate 65", dict(dstate=65), 2),
+    ("dstate 257", dict(dstate=257), 2),
     ("zero seqlen", dict(seqlen=0), 1),
     ("bad dtype", dict(dtype=5), 1),
     ("misaligned dy", dict(dy=FAKE + 5 * 0x08000000 + 2), 1),
@@ -349,7 +349,7 @@ INVALID_SAVE_CASES = [
     ("y overlaps u", dict(y=FAKE + 64), 1),
     ("zoh flag, null y", dict(flags=3, y=None), 1),
     ("backward-only flag", dict(flags=5), 1),
-    ("dstate 65", dict(dstate=65), 2),
+    ("dstate 257", dict(dstate=257), 2),
     ("zero seqlen", dict(seqlen=0), 1),
     ("misaligned bf16 activation", dict(u=FAKE + 1, dtype=1), 1),
 ]
@@ -372,7 +372,7 @@ def test_bwd_workspace_size(lib):
     assert partials + checkpoints + pregate <= size.value < (
         partials + checkpoints + pregate + 2 * 2**20)
     assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 7, ctypes.byref(size)) == 1
-    assert lib.ssm_scan_bwd_workspace_size(1, 16, 65, 256, 0, ctypes.byref(size)) == 2
+    assert lib.ssm_scan_bwd_workspace_size(1, 16, 257, 256, 0, ctypes.byref(size)) == 2
     assert lib.ssm_scan_bwd_workspace_size(1, 16, 16, 256, 0, None) == 1
 
 
@@ -519,7 +519,7 @@ def _noalloc(lib, **kw):
 INVALID_NOALLOC_CASES = [
     ("null u", dict(u=None), 1),
     ("null y", dict(y=None), 1),
-    ("dstate 65", dict(dstate=65), 2),
+    ("dstate 257", dict(dstate=257), 2),
     ("y aliases u", dict(y=FAKE + 64), 1),
     # 64 x 1024 channels in 128 chunks: 1.1 GB of chunk states, far beyond
     # the fixed 16 MiB scratch
@@ -580,7 +580,7 @@ INVALID_CONV_BWD_CASES = [
     ("workspace too small", dict(ws_bytes=4096), 3),
     ("dx overlaps x", dict(dx=FAKE + 64), 1),
     ("null dy (scan backward's check)", dict(dy=None), 1),
-    ("dstate 65", dict(dstate=65), 2),
+    ("dstate 257", dict(dstate=257), 2),
 ]
 
 

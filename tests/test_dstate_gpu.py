@@ -2,14 +2,17 @@
 
 The S6 module takes d_state as a parameter ("Mamba & State Space Models -
 Guide Complet", section 4: A is (d_model, d_state), B and C (batch, L,
-d_state)); d_state = 16 runs the tuned instances, any other count up to 64
-holds state n in lane n.  Every case compares with the fp64 oracle, which
+d_state); section 5 gives 64-256 for the larger states of Mamba-2);
+d_state = 16 runs the tuned instances, any other count up to 256 holds
+state n in lane n % 64 of register n / 64 (one register up to 64 states,
+four above).  Every case compares with the fp64 oracle, which
 takes any N: the forward (whole sequence, split into chunks, exact ZOH, conv
 prologue), the decode step (plain and with the conv window), and the
 backward (whole sequence, split, and after the saving forward).  Counts
 cover one state, odd counts (the last B/C staging phase holds one state), a
 count above 16 that is not a multiple of 16 (the backward's adjoint
-pre-pass works 16 states at a time) and the maximum, 64.
+pre-pass works 16 states at a time), 64 (one full register) and counts
+above it up to the maximum, 256.
 
 Bars: fp32 activations 1e-4, bf16 2e-2 on the scaled error (as for N = 16).
 """
@@ -51,6 +54,10 @@ FWD_CASES = [
     (32, 1, 8, 1500, "bf16"),
     (40, 1, 4, 1100, "f32"),
     (64, 2, 6, 2048, "f32"),
+    (65, 1, 5, 1100, "f32"),   # one state in the second register
+    (128, 2, 4, 1500, "bf16"),
+    (200, 1, 3, 1300, "f32"),
+    (256, 1, 3, 1024, "f32"),
 ]
 
 
@@ -69,7 +76,7 @@ def test_scan_other_state_counts(case):
     check(hf, h_ref, TOL[dt], "h_final")
 
 
-@pytest.mark.parametrize("N", [7, 64])
+@pytest.mark.parametrize("N", [7, 64, 130])
 def test_scan_other_state_counts_split_and_zoh(N):
     """A sequence split into 1024-token chunks (carry and fix-up over N
     states), and the exact ZOH input term."""
@@ -87,7 +94,7 @@ def test_scan_other_state_counts_split_and_zoh(N):
         check(hf, h_ref, 1e-4, "h_final (zoh=%d)" % zoh)
 
 
-@pytest.mark.parametrize("N", [4, 24])
+@pytest.mark.parametrize("N", [4, 24, 96])
 def test_conv_scan_other_state_counts(N):
     inp = syn.make_conv_inputs(syn.TINY, "cpu", batch=2, dim=7, dstate=N,
                                seqlen=1800, dtype="f32", with_h0=True,
@@ -106,7 +113,8 @@ def test_conv_scan_other_state_counts(N):
     check(hf, h_ref, 1e-4, "h_final")
 
 
-@pytest.mark.parametrize("case", [(1, "f32"), (8, "bf16"), (13, "f32"), (64, "f32")],
+@pytest.mark.parametrize("case", [(1, "f32"), (8, "bf16"), (13, "f32"), (64, "f32"),
+                                  (100, "f32"), (256, "bf16")],
                          ids=lambda c: "n%d_%s" % c)
 def test_decode_other_state_counts(case):
     """Every step against the oracle's step, the ZOH term on the second
@@ -186,7 +194,8 @@ BWD_KEYS = ("du", "ddelta", "dA", "dB", "dC", "dh0", "dD", "ddelta_bias", "dz")
 
 
 @pytest.mark.parametrize("case", [(1, "f32", 0), (5, "f32", 1), (8, "bf16", 0),
-                                  (24, "f32", 0), (64, "f32", 1)],
+                                  (24, "f32", 0), (64, "f32", 1), (65, "f32", 1),
+                                  (128, "bf16", 0), (256, "f32", 0)],
                          ids=lambda c: "n%d_%s_zoh%d" % c)
 def test_bwd_other_state_counts(case):
     N, dt, zoh = case
@@ -196,7 +205,7 @@ def test_bwd_other_state_counts(case):
         check(got[k], ref[k], TOL[dt], k)
 
 
-@pytest.mark.parametrize("N", [8, 40])
+@pytest.mark.parametrize("N", [8, 40, 130])
 def test_bwd_other_state_counts_split_and_saved(N):
     """Few channels over 19000 tokens: the checkpoint pass and the sweep
     split; then the saving forward and the backward reusing its checkpoints
