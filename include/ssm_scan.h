@@ -36,7 +36,7 @@
  *      A              : (dim, dstate) fp32        D, delta_bias : (dim) fp32
  *      h0, h_final    : (batch, dim, dstate) fp32
  *    For the decode step: x, delta, z, y : (batch, dim); B, C : (batch,
- *    dstate); state : (batch, dim, dstate) fp32.  dstate (N) is 1..64 for
+ *    dstate); state : (batch, dim, dstate) fp32.  dstate (N) is 1..256 for
  *    the scan, decode and backward entry points (see ssm_scan_fwd).
  *  - One activation dtype (ssm_dtype) covers u, delta, B, C, z and y.  A, D,
  *    the bias and every state are fp32.  Arithmetic is fp32 throughout.
@@ -72,7 +72,7 @@ typedef enum {
 typedef enum {
     SSM_OK = 0,
     SSM_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size, aliasing, misalignment */
-    SSM_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (e.g. dstate > 64) */
+    SSM_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (e.g. dstate > 256) */
     SSM_ERR_WORKSPACE = 3,    /* workspace missing or smaller than ssm_scan_workspace_size() */
     SSM_ERR_HIP = 4           /* a HIP runtime call failed (no device, launch failure) */
 } ssm_status;
@@ -122,13 +122,14 @@ int ssm_scan_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *                      any input
  *  h_final             nullable fp32 output: the state after the last token;
  *                      must not overlap h0
- *  batch, dim, seqlen  >= 1;  dstate 1..64 (the S6 module's d_state, "Mamba
- *                      & State Space Models - Guide Complet", section 4; 16,
- *                      the pages' value, runs the tuned instances, with A and
- *                      the carried state in scalar registers; any other count
- *                      holds state n in lane n of a wave).  The same range
- *                      holds for every scan, decode and backward entry point
- *                      below; larger states are the SSD form's (64..256)
+ *  batch, dim, seqlen  >= 1;  dstate 1..256 (the S6 module's d_state,
+ *                      "Mamba & State Space Models - Guide Complet", section
+ *                      4, and the larger states of its section 5; 16, the
+ *                      pages' value, runs the tuned instances, with A and the
+ *                      carried state in scalar registers; any other count
+ *                      holds state n in lane n % 64 of vector register n / 64
+ *                      of a wave).  The same range holds for every scan,
+ *                      decode and backward entry point below
  *  requested_chunk     0 = automatic; see ssm_scan_plan
  *  workspace           device scratch of >= ssm_scan_workspace_size() bytes,
  *                      256-byte aligned; may be NULL when that size is 0.  Its
