@@ -932,7 +932,7 @@ CKPT_KERNEL = "scan_kernel<unsigned short, true, true, false, false, true, 16>"
 # the Euler backward sweep (bf16, vector loads, softplus, no ZOH); the
 # --only-bwd run also times the ZOH and conv-prologue backward, whose
 # kernels are left out of that summary
-BWD_KERNEL = "bwd_kernel<unsigned short, true, true, false>"
+BWD_KERNEL = "bwd_kernel<unsigned short, true, true, false, 1>"
 COPY_KERNEL = "roof_copy_kernel"
 COPY_BYTES = 1 << 30  # each calibration copy reads and writes 1 GiB
 
