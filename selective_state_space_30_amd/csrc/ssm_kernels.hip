@@ -19,8 +19,9 @@
 // 64 lanes x 16 = 1024 tokens):
 //   * B and C of the block are read from HBM once per workgroup, two states
 //     at a time into a double-buffered LDS tile (the next pair is fetched
-//     while the current one is used), widened to fp32 and shared by the
-//     workgroup's 4 channels;
+//     while the current one is used), as fp32, shared by the workgroup's 4
+//     channels: bf16 rows through registers (widened there), aligned fp32
+//     rows of full blocks straight into LDS;
 //   * per lane and state n: dA and dB*u of its 16 tokens stay in registers;
 //     the lane folds them into one affine pair (P, H); a 6-step DPP scan over
 //     the 64 lanes composes the pairs (the state carried in from the previous
@@ -52,6 +53,45 @@ namespace ssm {
 namespace {
 
 using namespace dev;
+
+// Full blocks of fp32 rows whose starts are 16-byte aligned stage B and C
+// straight from memory into LDS (buffer loads with an LDS destination): no
+// staging registers, no LDS stores.  One staging row of the phase tile (64
+// runs of kTokensPerLane floats at the padded stride of kTokensPerLane + 4)
+// is 5 such loads of 1 KB (64 lanes x 16 bytes, written to consecutive LDS
+// addresses); slot s = 64 i + lane of the row holds quad s % 5 of run s / 5,
+// the fifth quad being the stride's padding, filled with a copy of the
+// fourth.  bf16 rows keep register staging: the tile is fp32, and widening
+// once per workgroup in registers is cheaper than any conversion in LDS.
+template <typename T, bool kVec>
+constexpr bool kDirectStage = sizeof(T) == 4 && kVec;
+constexpr int kDirectLoads = 5;
+static_assert(kWaveLanes * (kTokensPerLane + 4) * 4 == kDirectLoads * kWaveLanes * 16,
+              "a staging row is kDirectLoads loads of 16 bytes a lane");
+
+// This lane's byte offsets into a block's row for each of the 5 loads.
+__device__ __forceinline__ void direct_offsets(int lane, int (&off)[kDirectLoads]) {
+#pragma unroll
+  for (int i = 0; i < kDirectLoads; ++i) {
+    const int s = kWaveLanes * i + lane, q = s % 5;
+    off[i] = (s / 5) * kTokensPerLane * 4 + (q < 4 ? q : 3) * 16;
+  }
+}
+
+// Stages the 1024 floats row[0 .. 1024) into a staging row at `dst` (LDS,
+// 16-byte aligned).  `row` and `dst` are wave-uniform.  The loads complete
+// in LDS by the next wait for all vector memory operations (every barrier
+// of the phase loop waits for them).
+__device__ __forceinline__ void stage_row_direct(float *dst, const float *row,
+                                                 const int (&off)[kDirectLoads]) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(row), 0, kBlockTokens * 4, kBufferWord3);
+#pragma unroll
+  for (int i = 0; i < kDirectLoads; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)(dst + i * 4 * kWaveLanes), 16,
+        off[i], 0, 0, 0);
+}
 
 // One block of 1024 tokens of one channel per wave (4 channels of one batch
 // entry per workgroup).  kFull: the block lies wholly inside [t0, ct1), so
@@ -126,7 +166,8 @@ __device__ __forceinline__ void scan_block(
     bool ch_ok, float bias, float Dd, SS &S, float *sT,
     float &sdt_total, const float (&wc)[kMaxConv], float cb,
     float (&xc)[kMaxConv - 1], float (&upf)[kTokensPerLane],
-    float (&dpf)[kTokensPerLane], bool use_pf, int64_t pf_t0) {
+    float (&dpf)[kTokensPerLane], bool use_pf, int64_t pf_t0,
+    const int (&doff)[kDirectLoads], int64_t next_t0) {
   static_assert(!kFull || K == kTokensPerLane, "full blocks: 16 tokens a lane");
   static_assert(K == 4 || K == 8 || K == 16, "runs of 4, 8 or 16 tokens");
   // padded LDS stride of one lane's run: a lane's 16-byte reads of 8
@@ -149,7 +190,21 @@ __device__ __forceinline__ void scan_block(
   const int64_t tq = tl;
   const int toff = staging_offset<KP>(wave, lane);
   TileRun<T, K, kVec, kFull> run;
-  run.load(src + row(st) * p.L, t0, tq, tend);
+  // Direct staging (full blocks of aligned fp32 rows): the tuned instances
+  // request the next block's phase-0 tile during this block's last phase
+  // (their phase count is even, so buffer 0 is free then); the others
+  // request it here.  Register staging loads phase 0's run here.
+  // Either way, when the phase count is odd the previous block's last phase
+  // read buffer 0, so a barrier comes first.
+  constexpr bool kDirect = kFull && kDirectStage<T, kVec>;
+  const float *srcf = reinterpret_cast<const float *>(src);
+  float *const sdst = sT + wave * kWaveLanes * KP;  // this wave's staging row
+  if constexpr (kDirect && !SS::kStatic) {
+    if (nph & 1) __syncthreads();
+    stage_row_direct(sdst, srcf + row(st) * p.L + t0, doff);
+  } else if constexpr (!kDirect) {
+    run.load(src + row(st) * p.L, t0, tq, tend);
+  }
 
   // This lane's tokens: the step dt (kept as dt*log2(e) for exp2), dt*u
   // and the D skip.
@@ -205,8 +260,12 @@ __device__ __forceinline__ void scan_block(
       sdt += v;
     }
   }
-  // Phase 0's tile: its buffer was last read two phases ago, by every wave.
-  run.store(sT, toff);
+  // Phase 0's tile: its buffer was last read two phases ago, by every wave
+  // (by the previous block's last phase when the phase count is odd).
+  if constexpr (!kDirect) {
+    if (!SS::kStatic && (nph & 1)) __syncthreads();
+    run.store(sT, toff);
+  }
   const float sdtl = sdt * kLog2e;
   // u and delta of the full block at pf_t0 (the next one, or this one
   // again when none follows), in flight during this block's state loop
@@ -223,9 +282,17 @@ __device__ __forceinline__ void scan_block(
   constexpr int kPhaseUnroll = SS::kStatic ? kStates / 2 : 1;
 #pragma unroll kPhaseUnroll
   for (int ph = 0; ph < nph; ++ph) {
-    if (ph + 1 < nph)
+    if (!kDirect && ph + 1 < nph)
       run.load(src + row(2 * (ph + 1) + st) * p.L, t0, tq, tend);
     __syncthreads();  // phase ph's tile is complete and visible
+    if constexpr (kDirect) {
+      // the other buffer was last read in phase ph-1, before this barrier
+      if (ph + 1 < nph)
+        stage_row_direct(sdst + ((ph + 1) & 1) * kTileFloats,
+                         srcf + row(2 * (ph + 1) + st) * p.L + t0, doff);
+      else if (SS::kStatic)
+        stage_row_direct(sdst, srcf + row(st) * p.L + next_t0, doff);
+    }
     const float *tile = sT + (ph & 1) * kTileFloats;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -274,7 +341,7 @@ __device__ __forceinline__ void scan_block(
     }
     // Every wave has passed this phase's barrier, so the other buffer (read
     // in phase ph-1) is free: fill it with phase ph+1.
-    if (ph + 1 < nph) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
+    if (!kDirect && ph + 1 < nph) run.store(sT + ((ph + 1) & 1) * kTileFloats, toff);
   }
 
   // checkpoint instance: the pre-gate output, for the backward's dz
@@ -306,7 +373,7 @@ __global__ __launch_bounds__(kWaveLanes * kWavesPerGroup)
 __attribute__((amdgpu_waves_per_eu(kOccupancy<T, kVec, kZoh>)))
 void scan_kernel(ScanArgs p) {
   constexpr int KP = kTokensPerLane + 4;
-  __shared__ float sT[2 * 2 * 2 * kWaveLanes * KP];  // 2 buffers x 2 states x B, C
+  __shared__ __attribute__((aligned(16))) float sT[2 * 2 * 2 * kWaveLanes * KP];  // 2 buffers x 2 states x B, C
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -398,18 +465,35 @@ void scan_kernel(ScanArgs p) {
     }
   };
 
+  int doff[kDirectLoads];  // direct staging: this lane's load offsets
+  direct_offsets(lane, doff);
   float upf[kTokensPerLane], dpf[kTokensPerLane];  // prefetched u, delta
   const int64_t last_full = ct0 + ((ct1 - ct0) / kBlockTokens - 1) * kBlockTokens;
   int64_t t0 = ct0;
+  // direct staging in the tuned instances: the first full block's phase-0
+  // tile is requested here, every later one by the block before it
+  constexpr bool kDirectNext = kDirectStage<T, kVec> && kStatic;
+  const bool any_full = ct0 + kBlockTokens <= ct1;  // the same in every wave
+  if (kDirectNext && any_full)
+    stage_row_direct(sT + wave * kWaveLanes * KP,
+                     reinterpret_cast<const float *>((wave & 1) ? Cb : Bb) +
+                         (wave >> 1) * p.L + ct0,
+                     doff);
 #pragma unroll 1
   for (; t0 + kBlockTokens <= ct1; t0 += kBlockTokens) {
     store_ckpt(t0);
+    // the block whose phase-0 tile this block's last phase requests: the
+    // next one, or (a valid source that nothing reads) this one again
+    const int64_t next_t0 = t0 + 2 * kBlockTokens <= ct1 ? t0 + kBlockTokens : t0;
     scan_block<T, kVec, true, kSoftplus, kConv, kZoh, kCkpt>(
         p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd, S,
         sT, sdt_total, wc, cb, xc,
         upf, dpf, t0 > ct0,
-        t0 + 2 * kBlockTokens <= ct1 ? t0 + kBlockTokens : last_full);
+        t0 + 2 * kBlockTokens <= ct1 ? t0 + kBlockTokens : last_full, doff, next_t0);
   }
+  // the last full block's extra request lands before LDS is written again
+  // or released
+  if (kDirectNext && any_full) __syncthreads();
   if (t0 < ct1) store_ckpt(t0);
   if (t0 < ct1) {
     // the last, partial block: branch-free scalar loads (keeps the register
@@ -418,15 +502,15 @@ void scan_kernel(ScanArgs p) {
     if (rem <= 4 * kWaveLanes)
       scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt, 4>(
           p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
-          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0, doff, t0);
     else if (rem <= 8 * kWaveLanes)
       scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt, 8>(
           p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
-          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0, doff, t0);
     else
       scan_block<T, false, false, kSoftplus, kConv, kZoh, kCkpt>(
           p, wave, lane, t0, ct1, Bb, Cb, urow, drow, zrow, yrow, ycrow, ch_ok, bias, Dd,
-          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0);
+          S, sT, sdt_total, wc, cb, xc, upf, dpf, false, t0, doff, t0);
   }
 
   if (!ch_ok) return;
