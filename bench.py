@@ -397,6 +397,27 @@ def valu_block(ceil, state_updates, flops, sec):
     return out
 
 
+SETTLE_MS = 30.0
+
+
+def settle(torch, fn, stream, ms=SETTLE_MS):
+    """Runs ``fn`` untimed for about ``ms`` of GPU time before a timed loop.
+    Under a new sustained compute load the step time of these kernels drifts
+    for some tens of milliseconds (the clocks settling; the headline's
+    consecutive-steps record shows it) before it holds steady, so every
+    compute-bound measurement below starts after this."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    for _ in range(int(ms / max(e0.elapsed_time(e1), 1e-3))):
+        fn()
+    torch.cuda.synchronize()
+
+
 def extra_workloads(torch, ssm, syn, dev, stream, log, ceil):
     """The decode step, the SSD form, the backward, the long-context scan
     (chunked), the ZOH and conv-prologue variants and the 130M-shaped layer,
@@ -429,8 +450,7 @@ def extra_workloads(torch, ssm, syn, dev, stream, log, ceil):
         ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
                          inp["D"], inp["z"], inp["delta_bias"], True, None,
                          y=y, h_final=hf, workspace=ws, stream=stream)
-    run()
-    torch.cuda.synchronize()
+    settle(torch, run, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     reps = 5
@@ -495,8 +515,7 @@ def extra_workloads(torch, ssm, syn, dev, stream, log, ceil):
                          zinp["C"], zinp["D"], zinp["z"], zinp["delta_bias"],
                          True, None, y=zy, h_final=zhf, stream=stream,
                          zoh_b=True)
-    zrun()
-    torch.cuda.synchronize()
+    settle(torch, zrun, stream)
     e0.record(stream)
     for _ in range(reps):
         zrun()
@@ -524,8 +543,7 @@ def extra_workloads(torch, ssm, syn, dev, stream, log, ceil):
                               cinp["z"], cinp["delta_bias"], True, None,
                               conv_b=cinp["conv_b"], y=cy, h_final=chf,
                               stream=stream)
-    crun()
-    torch.cuda.synchronize()
+    settle(torch, crun, stream)
     reps = 20
     e0.record(stream)
     for _ in range(reps):
@@ -557,9 +575,8 @@ def extra_workloads(torch, ssm, syn, dev, stream, log, ceil):
         ssm.ssm_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"],
                          s["z"], s["delta_bias"], True, None, y=s["y"],
                          h_final=s["h_final"], stream=stream)
-    for i in range(6):
-        srun(i)
-    torch.cuda.synchronize()
+    it = iter(range(1 << 30))
+    settle(torch, lambda: srun(next(it)), stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     reps = 60
@@ -603,8 +620,7 @@ def bwd_measure(ssm, syn, dev, stream, reps, log):
                          binp["C"], binp["D"], binp["z"], binp["delta_bias"],
                          True, None, bdy, None, out=bout, workspace=bws,
                          stream=stream)
-    brun()
-    torch.cuda.synchronize()
+    settle(torch, brun, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -630,9 +646,7 @@ def bwd_measure(ssm, syn, dev, stream, reps, log):
                          binp["C"], binp["D"], binp["z"], binp["delta_bias"],
                          True, None, bdy, None, out=bout, workspace=bws,
                          stream=stream, saved=True)
-    frun()
-    srun()
-    torch.cuda.synchronize()
+    settle(torch, lambda: (frun(), srun()), stream)
     e0.record(stream)
     for _ in range(reps):
         frun()
@@ -642,8 +656,7 @@ def bwd_measure(ssm, syn, dev, stream, reps, log):
     pair_ms = e0.elapsed_time(e1) / reps
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
+        settle(torch, fn, stream)
         e0.record(stream)
         for _ in range(reps):
             fn()
@@ -804,9 +817,8 @@ def ssd_measure(ssm, syn, dev, stream, reps, log):
         ssm.ssm_ssd_fwd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
                         s["z"], s["dt_bias"], True, None, y=sy, h_final=shf,
                         workspace=sws, stream=stream)
-    for i in range(3):
-        srun(i)
-    torch.cuda.synchronize()
+    it = iter(range(1 << 30))
+    settle(torch, lambda: srun(next(it)), stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
