@@ -98,7 +98,7 @@ struct SsdArgs {
   const float *A, *D, *dt_bias, *h0;  // (h), (h), (h), (b,h,P,N)
   void *y;                            // bf16 (b,h,P,L)
   float *h_final;                     // (b,h,P,N) or null
-  void *G;                            // workspace: bf16 (b,g,chunk,2,64,64) causal C^T B, hi and lo
+  void *G;                            // workspace: fp32 (b,g,chunk,64,64) causal C^T B
   void *Ct;                           // workspace: bf16 (b,g,chunk,64,N) C transposed
   int64_t batch, nheads, ngroups, L;
   int nchunks, dstate;

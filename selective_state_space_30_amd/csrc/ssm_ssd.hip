@@ -18,14 +18,15 @@
 // plain product with the group's G.  While every |a_t - a_m| stays below
 // kFactorLimit (base 2) the factors cannot overflow fp32 or bf16; a chunk
 // with a steeper decay forms M = G o exp(a_t - a_s) dt_s element by element.
-// G and the carried state enter the products as a pair of bf16 values (the
-// value and its rounding error), so that neither is rounded to bf16 alone;
-// so do G's columns scaled by v_s (and M), x being taken as it is stored.
+// The carried state and G's columns scaled by v_s (or M) enter the
+// products as a pair of bf16 values (the value and its rounding error), so
+// that none of them is rounded to bf16 alone; x is taken as it is stored,
+// and G itself is kept in fp32.
 // All products run on v_mfma_f32_16x16x32_bf16 (A operand: lane l, element
 // e = A[l%16][8*(l/16)+e]; B: B[8*(l/16)+e][l%16]; result: lane l, element
 // e = D[4*(l/16)+e][l%16], checked on the hardware).
 //
-// Work layout: ssd_prep_kernel forms the causal G (bf16 pair) and C^T per
+// Work layout: ssd_prep_kernel forms the causal G (fp32) and C^T per
 // (batch, group, chunk); ssd_kernel runs one workgroup per (batch, head,
 // slice of the head's rows) over the chunks in order, the state staying in
 // matrix-core accumulators for the whole sequence.
@@ -52,6 +53,7 @@ constexpr int T = kSsdChunk;     // 64 tokens per chunk
 constexpr int P = kSsdHeadDim;   // 64 rows per head
 constexpr int kPad = 8;          // bf16 padding of LDS rows
 constexpr int kRowT = T + kPad;  // row stride of [row][token] tiles
+constexpr int kRowG = T + 4;     // row stride of the prep kernel's fp32 G tile
 // largest |a_t - a_m| (base-2 exponent) of the factored chunk term
 constexpr float kFactorLimit = 96.0f;
 constexpr int kRef = 31;         // reference token m of the factored decay
@@ -112,14 +114,14 @@ __device__ __forceinline__ u32x4 buf_load8(__amdgpu_buffer_rsrc_t v, int voff, i
 
 // ----------------------------------------------------------- chunk prep ---
 // Per (batch, group, chunk): the causal G = C^T B (64 x 64, [t][s], zero
-// for s > t) as bf16 G_hi and G_lo = bf16(G - G_hi), and C transposed to
+// for s > t) in fp32, and C transposed to
 // [token][state] (the layout the y product reads).  Positions past L are 0.
 template <int N, bool kVec>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
   constexpr int kRowN = N + kPad;
   __shared__ __align__(16) __bf16 CtL[T * kRowN];  // [t][n]
   __shared__ __align__(16) __bf16 BtL[T * kRowN];  // [s][n]
-  __shared__ __align__(16) __bf16 GL[2][T * kRowT];  // [t][s]: hi, lo
+  __shared__ __align__(16) float GL[T * kRowG];      // [t][s]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -156,18 +158,14 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * wave + 4 * (lane >> 4) + e;
-      const float gv = s <= t ? acc[e] : 0.0f;
-      const __bf16 hi = static_cast<__bf16>(gv);
-      GL[0][t * kRowT + s] = hi;
-      GL[1][t * kRowT + s] = static_cast<__bf16>(gv - static_cast<float>(hi));
+      GL[t * kRowG + s] = s <= t ? acc[e] : 0.0f;
     }
   }
   __syncthreads();
-  uint16_t *Gw = static_cast<uint16_t *>(p.G) + (bg * p.nchunks + c) * 2 * T * T;
-  for (int q = tid; q < 2 * T * (T / 8); q += 256) {
-    const int part = q / (T * (T / 8)), t = (q / (T / 8)) % T, s8 = (q % (T / 8)) * 8;
-    *reinterpret_cast<uint4 *>(Gw + (part * T + t) * T + s8) =
-        *reinterpret_cast<const uint4 *>(&GL[part][t * kRowT + s8]);
+  float *Gw = static_cast<float *>(p.G) + (bg * p.nchunks + c) * T * T;
+  for (int q = tid; q < T * (T / 4); q += 256) {
+    const int t = q / (T / 4), s4 = (q % (T / 4)) * 4;
+    *reinterpret_cast<f32x4 *>(Gw + t * T + s4) = *reinterpret_cast<const f32x4 *>(&GL[t * kRowG + s4]);
   }
   // C^T of this chunk, [t][n] contiguous
   uint16_t *Ctw = static_cast<uint16_t *>(p.Ct) + (bg * p.nchunks + c) * T * N;
@@ -243,7 +241,7 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
   const uint16_t *dth = static_cast<const uint16_t *>(p.dt) + bh * L;
   const uint16_t *Bg = static_cast<const uint16_t *>(p.B) + bg * N * L;
   const uint16_t *Ctg = static_cast<const uint16_t *>(p.Ct) + bg * nch * T * N;
-  const uint16_t *Gg = static_cast<const uint16_t *>(p.G) + bg * nch * 2 * T * T;
+  const float *Gg = static_cast<const float *>(p.G) + bg * nch * T * T;
   uint16_t *yh = static_cast<uint16_t *>(p.y) + (bh * P + row0) * L;
   const int kq = 8 * lq;                         // operand k offset of this lane
   const int ta = 16 * tt + li;                   // token row of this lane's A operands
@@ -269,9 +267,10 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
     }
 
   // operand registers of the chunk being computed: C^T row ta (states
-  // 32 ks + kq ..), G row ta (tokens 32 ks + kq .., hi and lo), B rows of
+  // 32 ks + kq ..), G row ta (tokens 32 ks + kq .., fp32), B rows of
   // this wave's state tiles (tokens 32 ks + kq ..)
-  bf16x8 ca[N / 32], ga[2][2], ba[2][kNTW];
+  bf16x8 ca[N / 32], ba[2][kNTW];
+  f32x4 ga[2][2];  // [ks][half]
   // (a chunk's C^T and G are small: a wave-uniform base and a 32-bit lane
   // offset address them)
   const int ct_off = ta * N + kq, g_off = ta * T + kq;
@@ -283,14 +282,12 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
                                   *reinterpret_cast<const u32x4 *>(base + (ct_off + 32 * ks)));
   };
   auto load_g = [&](int c) __attribute__((always_inline)) {
-    const uint16_t *base = Gg + static_cast<int64_t>(c) * 2 * T * T;
+    const float *base = Gg + static_cast<int64_t>(c) * T * T;
 #pragma unroll
-    for (int part = 0; part < 2; ++part)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        ga[part][ks] = __builtin_bit_cast(
-            bf16x8,
-            *reinterpret_cast<const u32x4 *>(base + (g_off + part * T * T + 32 * ks)));
+      for (int hf = 0; hf < 2; ++hf)
+        ga[ks][hf] = *reinterpret_cast<const f32x4 *>(base + (g_off + 32 * ks + 4 * hf));
   };
   // Aligned rows (kVec) are read through buffer views of whole matrices: a
   // loop-invariant 32-bit lane offset, the chunk's start as the scalar
@@ -537,8 +534,7 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
           bf16x8 gh, gl;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float gv = (static_cast<float>(ga[0][ks][e]) + static_cast<float>(ga[1][ks][e])) *
-                             (e < 4 ? v0[e] : v1[e - 4]);
+            const float gv = (e < 4 ? ga[ks][0][e] : ga[ks][1][e - 4]) * (e < 4 ? v0[e] : v1[e - 4]);
             gh[e] = static_cast<__bf16>(gv);
             gl[e] = static_cast<__bf16>(gv - static_cast<float>(gh[e]));
           }
@@ -561,7 +557,7 @@ __global__ __launch_bounds__(64 * kW) void ssd_kernel(SsdArgs p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float ex = s0 + e <= ta ? Aq * (ct - q[1][s0 + e]) : -INFINITY;
-            const float gv = static_cast<float>(ga[0][ks][e]) + static_cast<float>(ga[1][ks][e]);
+            const float gv = e < 4 ? ga[ks][0][e] : ga[ks][1][e - 4];
             const float mv = gv * fast_exp2(ex) * q[0][s0 + e];
             m[e] = static_cast<__bf16>(mv);
             ml[e] = static_cast<__bf16>(mv - static_cast<float>(m[e]));
