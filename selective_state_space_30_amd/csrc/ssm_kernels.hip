@@ -361,13 +361,14 @@ __device__ __forceinline__ void scan_block(
 }
 
 // Waves per SIMD the register budget is sized for: 4 (128 VGPRs; 4
-// workgroups x 40 KB fill a CU's 160 KB of LDS) for aligned bf16 rows with
-// the Euler input term; 3 (168 VGPRs) otherwise, where the longer ZOH state
-// loop, the wider fp32 loads or the element-wise loads of unaligned rows
-// would spill or stall at 128 (measured: fp32 and unaligned bf16 run faster
-// at 3).
+// workgroups x 40 KB fill a CU's 160 KB of LDS) for aligned bf16 rows, the
+// Euler and the ZOH input term alike (with each state scheduled on its own
+// the ZOH state loop fits 128 without spills: 264 vs 277 us at 3 on the
+// 2.8B layer); 3 (168 VGPRs) otherwise, where the wider fp32 loads or the
+// element-wise loads of unaligned rows would spill or stall at 128
+// (measured: fp32 and unaligned bf16 run faster at 3).
 template <typename T, bool kVec, bool kZoh>
-constexpr int kOccupancy = (sizeof(T) == 2 && kVec && !kZoh) ? 4 : 3;
+constexpr int kOccupancy = (sizeof(T) == 2 && kVec) ? 4 : 3;
 
 // kN: kStates (the tuned 16-state instances), kMaxLaneStates (any d_state
 // up to 64) or kMaxStates (up to 256).
