@@ -361,14 +361,15 @@ __device__ __forceinline__ void scan_block(
 }
 
 // Waves per SIMD the register budget is sized for: 4 (128 VGPRs; 4
-// workgroups x 40 KB fill a CU's 160 KB of LDS) for aligned bf16 rows, the
-// Euler and the ZOH input term alike (with each state scheduled on its own
-// the ZOH state loop fits 128 without spills: 264 vs 277 us at 3 on the
-// 2.8B layer); 3 (168 VGPRs) otherwise, where the wider fp32 loads or the
-// element-wise loads of unaligned rows would spill or stall at 128
-// (measured: fp32 and unaligned bf16 run faster at 3).
+// workgroups x 40 KB fill a CU's 160 KB of LDS) for bf16 rows, aligned or
+// not, with the Euler or the ZOH input term (with each state scheduled on
+// its own these fit 128 with at most a few spilled registers, measured on
+// the 2.8B layer at 4 against 3: ZOH 264 vs 277 us, unaligned rows 313 vs
+// 330 us); 3 (168 VGPRs) for fp32 rows, whose wider loads and the next
+// block's u and delta carried in registers need the room (4 without that
+// prefetch measured slower).
 template <typename T, bool kVec, bool kZoh>
-constexpr int kOccupancy = (sizeof(T) == 2 && kVec) ? 4 : 3;
+constexpr int kOccupancy = sizeof(T) == 2 ? 4 : 3;
 
 // kN: kStates (the tuned 16-state instances), kMaxLaneStates (any d_state
 // up to 64) or kMaxStates (up to 256).
