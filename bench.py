@@ -104,6 +104,20 @@ def measured_valu_slots():
     return None
 
 
+def profiled_launch_us():
+    """Kernel-trace average duration (us) of the scan kernel over the 2.8B
+    layer's dispatches in the committed profile, or None if the sources
+    changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("kernel_trace_us_mean")
+
+
 def measured_traffic(n_launch_bytes):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or
     None if the kernel source changed since they were taken."""
@@ -282,6 +296,9 @@ def main():
             "kernel": SCAN_KERNEL,
             "algorithmic_bytes_per_launch": nbytes,
             "launch_us_mean": round(ms * 1e3, 2),
+            # the same kernel's average in the committed rocprofv3 trace
+            # (another box; boxes differ by a few per cent)
+            "profiled_launch_us_mean": profiled_launch_us(),
         },
     }
     result["valu"] = valu_block(ceil, E * cfg.dstate, flops, sec)
@@ -1048,6 +1065,10 @@ def summarize_profiles(d):
            "hbm_bytes_per_launch": int(fb + wb),
            "algorithmic_bytes_per_launch": alg,
            "traffic_over_algorithmic": (fb + wb) / alg,
+           # the kernel-trace average over the 2.8B-layer dispatches of the
+           # same profiled sources, to set beside a live run's events
+           "kernel_trace_us_mean": (round(statistics.mean(by_grid[grid_c2]), 2)
+                                    if grid_c2 in by_grid else None),
            "commands": [cmd_pmc.format(c="FETCH_SIZE", d="fetch"),
                         cmd_pmc.format(c="WRITE_SIZE", d="write"),
                         "python3 bench.py --summarize DIR"]}
