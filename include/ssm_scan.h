@@ -243,9 +243,12 @@ int ssm_conv_state_update(float *state, void *conv_state, const void *x,
 /* Bytes of caller-provided device workspace ssm_scan_bwd needs for this
  * shape and activation dtype: the block-start checkpoints
  * (batch*dim*ceil(seqlen/1024)*dstate fp32), the pre-gate output
- * (batch*dim*seqlen, activation dtype), per-workgroup partial sums of dB and
- * dC (2 * batch*ceil(dim/8)*dstate*seqlen fp32: a workgroup holds 8
- * channels), and per-(channel, chunk) partials of dA, dD and the bias.
+ * (batch*dim*seqlen, activation dtype), partial sums of dB and dC (2 *
+ * batch*slots*dstate*seqlen fp32: a workgroup holds 8 channels, and takes
+ * ceil(groups/slots) of the groups = ceil(dim/8) one after another, adding
+ * into one row; slots is the smallest count that costs no extra round of 256
+ * resident workgroups: 128 of 640 groups for the 2.8B layer's batch of 2),
+ * and per-(channel, chunk) partials of dA, dD and the bias.
  * Shapes with few channels and long rows split the sequence (below) and
  * add, each under 1 % of the partial sums: the checkpoint pass's per-block
  * dt sums and per-chunk states, and the sweep's per-chunk adjoints (3 x

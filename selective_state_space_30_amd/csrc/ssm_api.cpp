@@ -135,6 +135,27 @@ int64_t bwd_chunk(int64_t batch, int64_t dim, int64_t seqlen) {
   return best.chunk;
 }
 
+// dB/dC partial-sum rows per batch entry.  Each sweep workgroup takes u
+// channel groups one after another and adds them into one row, so the
+// reduction reads groups / u rows instead of groups.  u is the largest
+// count that needs no more rounds of kBwdResident workgroups than one group
+// per workgroup does (the 2.8B layer: 1280 groups in 5 rounds -> 256
+// workgroups of 5 groups each).
+int64_t bwd_slots(int64_t batch, int64_t dim, int64_t n_chunks) {
+  const int64_t groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
+  const int64_t per_slot = batch * n_chunks;  // workgroups of one slot index
+  auto rounds = [&](int64_t slots) {
+    return (per_slot * slots + ssm::kBwdResident - 1) / ssm::kBwdResident;
+  };
+  const int64_t r1 = rounds(groups);
+  int64_t best = groups;
+  for (int64_t u = 2; u <= groups && u <= r1; ++u) {
+    const int64_t slots = (groups + u - 1) / u;
+    if (rounds(slots) * u <= r1) best = slots;
+  }
+  return best;
+}
+
 }  // namespace
 
 namespace ssm {
@@ -144,13 +165,14 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t N, int64_t seqlen,
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t bd = static_cast<size_t>(batch) * dim;
   const size_t nblk = static_cast<size_t>((seqlen + kBlockTokens - 1) / kBlockTokens);
-  const size_t groups = static_cast<size_t>((dim + kBwdWaves - 1) / kBwdWaves);
-  const size_t part = static_cast<size_t>(batch) * groups * ns * seqlen * sizeof(float);
   BwdLayout l;
   l.ckpt_chunk = choose_chunk(batch, dim, seqlen, 0);
   l.ckpt_chunks = (seqlen + l.ckpt_chunk - 1) / l.ckpt_chunk;
   l.chunk = bwd_chunk(batch, dim, seqlen);
   l.n_chunks = (seqlen + l.chunk - 1) / l.chunk;
+  l.slots = bwd_slots(batch, dim, l.n_chunks);
+  const size_t part =
+      static_cast<size_t>(batch) * static_cast<size_t>(l.slots) * ns * seqlen * sizeof(float);
   const size_t nc = static_cast<size_t>(l.n_chunks);
   const size_t ncc = static_cast<size_t>(l.ckpt_chunks);
   l.off_ckpt = 0;
@@ -710,6 +732,7 @@ int scan_bwd_impl(const void *u, const void *delta, const float *A,
   a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dbias = ddelta_bias;
   a.batch = batch; a.dim = dim; a.L = seqlen; a.N = static_cast<int>(dstate);
   a.groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
+  a.slots = l.slots;
   a.nblk = static_cast<int>((seqlen + ssm::kBlockTokens - 1) / ssm::kBlockTokens);
   a.softplus = fa.softplus;
   a.zoh = fa.zoh;

@@ -74,32 +74,48 @@ __device__ __forceinline__ int region_index(int wave, int mat, int j, int lane) 
   return ((wave * 2 + mat) * kTokensPerLane + j) * kWaveLanes + (lane ^ ((j >> 2) << 3));
 }
 
-// After every wave has written its region for state n: thread tid sums the
-// channels' contributions (in channel order) for 4 consecutive tokens of one
-// matrix and writes them to the workgroup's partial-sum row (a 16-byte
-// store when kVec; the partial block through the buffer view).  Runs of K
+// The flush's share of thread tid (after every wave has written its region
+// for a state): 4 consecutive tokens of one matrix (the first half of the
+// threads dB, the second dC: wave-uniform) in one lane run.  Runs of K
 // tokens (fewer than 16 in a short partial block): threads whose 4 tokens
 // lie past the run have nothing to write.
-template <bool kVec, bool kFull, int K = kTokensPerLane>
-__device__ __forceinline__ void flush_state(const float *sR, int tid, float *pB_row,
-                                            float *pC_row, int64_t t0, int64_t tend) {
-  constexpr int kPer = 2 * kTokensPerLane * kWaveLanes / kBwdThreads;  // 4
-  constexpr int kParts = kTokensPerLane / kPer;                        // per run
-  const int mat = tid / (kBwdThreads / 2);  // first half: dB, second: dC (wave-uniform)
+constexpr int kFlushPer = 2 * kTokensPerLane * kWaveLanes / kBwdThreads;  // 4
+struct FlushPos {
+  int mat, run, j0;
+  bool active;
+};
+template <int K>
+__device__ __forceinline__ FlushPos flush_pos(int tid) {
+  constexpr int kParts = kTokensPerLane / kFlushPer;  // per run
+  FlushPos f;
+  f.mat = tid / (kBwdThreads / 2);
   const int r = tid % (kBwdThreads / 2);
-  const int run = r / kParts;               // the lane run ...
-  const int j0 = (r % kParts) * kPer;       // ... and which part of it
-  if (K < kTokensPerLane && j0 >= K) return;
-  float v[kPer];
+  f.run = r / kParts;
+  f.j0 = (r % kParts) * kFlushPer;
+  f.active = K == kTokensPerLane || f.j0 < K;
+  return f;
+}
+
+// Sums the channels' contributions (in channel order) to its 4 tokens,
+// adds them to what the slot's earlier channel groups left in its
+// partial-sum row (prev, zeros for the slot's first group) and writes the
+// row (a 16-byte store when kVec; the partial block through the buffer
+// view).
+template <bool kVec, bool kFull, int K = kTokensPerLane>
+__device__ __forceinline__ void flush_state(const float *sR, const FlushPos &f,
+                                            const float (&prev)[kFlushPer], float *pB_row,
+                                            float *pC_row, int64_t t0, int64_t tend) {
+  if (!f.active) return;
+  float v[kFlushPer];
 #pragma unroll
-  for (int jj = 0; jj < kPer; ++jj) {
+  for (int jj = 0; jj < kFlushPer; ++jj) {
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kBwdWaves; ++w) acc += sR[region_index(w, mat, j0 + jj, run)];
-    v[jj] = acc;
+    for (int w = 0; w < kBwdWaves; ++w) acc += sR[region_index(w, f.mat, f.j0 + jj, f.run)];
+    v[jj] = prev[jj] + acc;
   }
-  float *row = mat ? pC_row : pB_row;
-  store_run<float, kPer, kVec, kFull>(row, t0, t0 + run * K + j0, tend, v);
+  float *row = f.mat ? pC_row : pB_row;
+  store_run<float, kFlushPer, kVec, kFull>(row, t0, t0 + f.run * K + f.j0, tend, v);
 }
 
 // Per-state values of one channel (wave-uniform), state n in lane n % 64
@@ -155,7 +171,7 @@ template <typename T, bool kVec, bool kFull, bool kSoftplus, bool kZoh, int kR,
           int K = kTokensPerLane>
 __device__ __forceinline__ void bwd_block(
     const BwdArgs &p, int wave, int lane, int64_t t0, int64_t tend, int64_t b,
-    int64_t bd, int64_t g, const T *__restrict__ Bb, const T *__restrict__ Cb,
+    int64_t bd, int64_t slot, bool accum, const T *__restrict__ Bb, const T *__restrict__ Cb,
     bool ch_ok, float bias, float Dd, const PerState<kR> &Av, const PerState<kR> &hfv,
     PerState<kR> &muv, PerState<kR> &dAv, float &dDl, float &dbl, float *sT, float *sR,
     int tid) {
@@ -178,8 +194,10 @@ __device__ __forceinline__ void bwd_block(
   const T *src = mat ? Cb : Bb;
   const int toff = (mat * kWaveLanes + lane) * KP + qr * kQuarterRun;
   const int64_t tq = tl + qr * kQuarterRun;
-  float *pBg = p.pB + (b * p.groups + g) * p.N * p.L;  // this group's partial rows
-  float *pCg = p.pC + (b * p.groups + g) * p.N * p.L;
+  float *pBg = p.pB + (b * p.slots + slot) * p.N * p.L;  // this slot's partial rows
+  float *pCg = p.pC + (b * p.slots + slot) * p.N * p.L;
+  const FlushPos fp = flush_pos<K>(tid);
+  const int64_t tf = t0 + fp.run * K + fp.j0;  // the flush's first token
   TileRun<T, kQuarterRun, kVec, kFull> run;
   if (stager) run.load(src, t0, tq, tend);  // state 0
 
@@ -261,6 +279,11 @@ __device__ __forceinline__ void bwd_block(
 #pragma unroll 1
   for (int n = 0; n < p.N; ++n) {
     if (stager && n + 1 < p.N) run.load(src + (n + 1) * p.L, t0, tq, tend);
+    // what the slot's earlier channel groups summed for this state's tokens,
+    // requested now and added at the flush, after the state's work
+    float prev[kFlushPer] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (accum && fp.active)
+      load_run<float, kFlushPer, kVec, kFull>((fp.mat ? pCg : pBg) + n * p.L, t0, tf, tend, prev);
     const float *tile = sT + (n & 1) * kBwdTileFloats;
     float *reg = sR + (n & 1) * kRegionFloats;
     float An = state_of(Av, n);
@@ -359,7 +382,7 @@ __device__ __forceinline__ void bwd_block(
     add_state(dAv, lane, n, dA_sum);
     if (stager && n + 1 < p.N) run.store(sT + ((n + 1) & 1) * kBwdTileFloats, toff);
     __syncthreads();  // state n's contributions and state n+1's tile are in LDS
-    flush_state<kVec, kFull, K>(reg, tid, pBg + n * p.L, pCg + n * p.L, t0, tend);
+    flush_state<kVec, kFull, K>(reg, fp, prev, pBg + n * p.L, pCg + n * p.L, t0, tend);
   }
 
   // per-token gradients: du = dt * sum lambda B + gc D, ddelta = (u *
@@ -379,18 +402,17 @@ __device__ __forceinline__ void bwd_block(
   }
 }
 
+// One channel group g (kBwdWaves channels of batch entry blockIdx.y) over
+// chunk blockIdx.z, its dB/dC channel sums added into partial-sum row
+// `slot` (accum: an earlier group of the slot has written it).
 // kR: vector registers per per-state value (1: up to 64 states; 4: up to 256)
 template <typename T, bool kVec, bool kSoftplus, bool kZoh, int kR>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_kernel(BwdArgs p) {
-  __shared__ float sT[2 * kBwdTileFloats];  // one state's B, C (fp32), double-buffered
-  __shared__ float sR[2 * kRegionFloats];   // dB, dC contributions of the 8 channels, double-buffered
-
+__device__ __forceinline__ void bwd_group(const BwdArgs &p, int64_t g, int64_t slot, bool accum,
+                                          float *sT, float *sR) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t b = blockIdx.y;
-  const int64_t g = blockIdx.x;
   const int c = blockIdx.z;  // chunk
   const int64_t d_raw = g * kBwdWaves + wave;
   const bool ch_ok = d_raw < p.dim;
@@ -437,26 +459,26 @@ void bwd_kernel(BwdArgs p) {
     const PerState<kR> hf = ckpt_of(nfull);
     const int64_t t0 = ct0 + nfull * kBlockTokens;
     if (rem <= 4 * kWaveLanes)
-      bwd_block<T, false, false, kSoftplus, kZoh, kR, 4>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+      bwd_block<T, false, false, kSoftplus, kZoh, kR, 4>(p, wave, lane, t0, ct1, b, bd, slot, accum, Bb, Cb,
                                                      ch_ok, bias, Dd, Av, hf, muv, dAv, dDl,
                                                      dbl, sT, sR, tid);
     else if (rem <= 8 * kWaveLanes)
-      bwd_block<T, false, false, kSoftplus, kZoh, kR, 8>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+      bwd_block<T, false, false, kSoftplus, kZoh, kR, 8>(p, wave, lane, t0, ct1, b, bd, slot, accum, Bb, Cb,
                                                      ch_ok, bias, Dd, Av, hf, muv, dAv, dDl,
                                                      dbl, sT, sR, tid);
     else
-      bwd_block<T, false, false, kSoftplus, kZoh, kR>(p, wave, lane, t0, ct1, b, bd, g, Bb, Cb,
+      bwd_block<T, false, false, kSoftplus, kZoh, kR>(p, wave, lane, t0, ct1, b, bd, slot, accum, Bb, Cb,
                                                   ch_ok, bias, Dd, Av, hf, muv, dAv, dDl, dbl,
                                                   sT, sR, tid);
   }
 #pragma unroll 1
   for (int64_t k = nfull - 1; k >= 0; --k)
     bwd_block<T, kVec, true, kSoftplus, kZoh, kR>(p, wave, lane, ct0 + k * kBlockTokens,
-                                            ct0 + (k + 1) * kBlockTokens, b, bd, g, Bb, Cb,
+                                            ct0 + (k + 1) * kBlockTokens, b, bd, slot, accum, Bb, Cb,
                                             ch_ok, bias, Dd, Av, ckpt_of(k), muv, dAv, dDl,
                                             dbl, sT, sR, tid);
 
-  if (!ch_ok) return;
+  if (!ch_ok) return;  // (only in the last group: nothing follows it)
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
     const int n = kWaveLanes * i + lane;
@@ -472,6 +494,20 @@ void bwd_kernel(BwdArgs p) {
     p.pD[bdc] = sD;
     p.pbias[bdc] = sb;
   }
+}
+
+// Launch `unit` of the sweep: workgroup (slot, b, c) takes channel group
+// slot + unit * slots.  The launches run in unit order on one stream, so
+// each partial-sum row is a fixed-order sum.
+template <typename T, bool kVec, bool kSoftplus, bool kZoh, int kR>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_kernel(BwdArgs p) {
+  __shared__ float sT[2 * kBwdTileFloats];  // one state's B, C (fp32), double-buffered
+  __shared__ float sR[2 * kRegionFloats];   // dB, dC contributions of the 8 channels, double-buffered
+  const int64_t slot = blockIdx.x;
+  const int64_t g = slot + p.unit * p.slots;
+  if (g >= p.groups) return;  // the whole workgroup
+  bwd_group<T, kVec, kSoftplus, kZoh, kR>(p, g, slot, p.unit > 0, sT, sR);
 }
 
 // ------------------------------------------- sequence split: adjoints ---
@@ -561,10 +597,10 @@ __global__ __launch_bounds__(256) void bwd_adj_carry_kernel(BwdArgs p) {
   p.mu_in[(bd * nc) * N + n] = mu;
 }
 
-// dB[b, n, t] (blockIdx.y = 0) or dC (1): the sum over channel groups of
-// the partial rows.  A workgroup takes 256 consecutive tokens (64 lanes x 4)
-// of one (b, n) row; its 4 waves take every 4th group (16-byte loads, 1 KB
-// per wave and group) and add up in LDS at the end.
+// dB[b, n, t] (blockIdx.y = 0) or dC (1): the sum over slots of the
+// partial rows.  A workgroup takes 256 consecutive tokens (64 lanes x 4)
+// of one (b, n) row; its 4 waves take every 4th slot (16-byte loads, 1 KB
+// per wave and slot) and add up in LDS at the end.
 constexpr int kReduceWaves = 4;
 constexpr int kReduceTokens = 4 * kWaveLanes;  // per workgroup
 __global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kernel(BwdArgs p) {
@@ -575,7 +611,7 @@ __global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kerne
   const int64_t row = blockIdx.x / ntb;  // b * N + n
   const int64_t t = (blockIdx.x - row * ntb) * kReduceTokens + lane * 4;
   const int64_t b = row / p.N, n = row - b * p.N;
-  const float *part = (blockIdx.y ? p.pC : p.pB) + (b * p.groups * p.N + n) * p.L;
+  const float *part = (blockIdx.y ? p.pC : p.pB) + (b * p.slots * p.N + n) * p.L;
   const int64_t gstride = p.N * p.L;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if ((p.L & 3) == 0 && t < p.L) {
@@ -587,7 +623,7 @@ __global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kerne
     // scheduler groups the loads and waits for all of them at once.
     constexpr int kRing = 8;
     const int64_t step = kReduceWaves * gstride;
-    const int64_t ng = (p.groups - slice + kReduceWaves - 1) / kReduceWaves;
+    const int64_t ng = (p.slots - slice + kReduceWaves - 1) / kReduceWaves;
     const float *q = part + t + slice * gstride;
     int64_t g = 0;
     if (ng >= kRing) {
@@ -616,7 +652,7 @@ __global__ __launch_bounds__(kReduceWaves * kWaveLanes) void bwd_reduce_bc_kerne
     }
   } else if (t < p.L) {
     const int cnt = p.L - t < 4 ? static_cast<int>(p.L - t) : 4;
-    for (int64_t gi = slice; gi < p.groups; gi += kReduceWaves) {
+    for (int64_t gi = slice; gi < p.slots; gi += kReduceWaves) {
       const float *q = part + gi * gstride + t;
       acc.x += q[0];
       if (cnt > 1) acc.y += q[1];
@@ -684,7 +720,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid(static_cast<unsigned>(a.groups), static_cast<unsigned>(a.batch),
+  const dim3 grid(static_cast<unsigned>(a.slots), static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(a.n_chunks));
   using Fn = void (*)(BwdArgs);
   // [more than 64 states][softplus | zoh]
@@ -693,11 +729,16 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
        bwd_kernel<T, kVec, false, true, 1>, bwd_kernel<T, kVec, true, true, 1>},
       {bwd_kernel<T, kVec, false, false, 4>, bwd_kernel<T, kVec, true, false, 4>,
        bwd_kernel<T, kVec, false, true, 4>, bwd_kernel<T, kVec, true, true, 4>}};
-  hipLaunchKernelGGL(kernels[a.N > kWaveLanes ? 1 : 0][(a.softplus ? 1 : 0) | (a.zoh ? 2 : 0)],
-                     grid,
-                     dim3(kBwdThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const Fn sweep = kernels[a.N > kWaveLanes ? 1 : 0][(a.softplus ? 1 : 0) | (a.zoh ? 2 : 0)];
+  const int64_t units = (a.groups + a.slots - 1) / a.slots;
+  hipError_t e = hipSuccess;
+  for (int64_t k = 0; k < units; ++k) {
+    BwdArgs ak = a;
+    ak.unit = k;
+    hipLaunchKernelGGL(sweep, grid, dim3(kBwdThreads), 0, s, ak);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t nwg = a.batch * a.N * ((a.L + kReduceTokens - 1) / kReduceTokens);
   hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>(nwg), 2),
                      dim3(kReduceWaves * kWaveLanes), 0,

@@ -18,6 +18,11 @@ constexpr int kBlockTokens = kWaveLanes * kTokensPerLane;         // 1024
 constexpr int kPhaseStates = 2;      // states per double-buffered B/C LDS tile
 constexpr int kMaxConv = 4;          // taps of the fused causal conv1d prologue
 constexpr int kBwdWaves = 8;         // waves (channels) per backward workgroup
+// Backward sweep workgroups resident at once on the chip: one per compute
+// unit (the sweep's LDS tiles take 148 KB of a CU's 160 KB), 256 CUs.  A
+// fixed count, not a queried one, so that the order of the dB/dC sums (and
+// so their bits) is the same on every device.
+constexpr int kBwdResident = 256;
 
 struct ScanArgs {
   const void *u, *delta, *B, *C, *z;  // activations (dtype); u null with conv
@@ -46,8 +51,11 @@ struct ScanArgs {
                                       // (batch, dim, ceil(L/1024)); else null
 };
 
-// Backward pass.  Per-workgroup partial sums (a workgroup = kBwdWaves
-// channels of one batch entry) are reduced by a second kernel.
+// Backward pass.  A workgroup sweeps kBwdWaves channels of one batch entry;
+// the sweep is launched ceil(groups / slots) times in a row, launch k taking
+// channel groups k * slots .. (k + 1) * slots - 1, and each adds its dB/dC
+// channel sums into partial-sum row `slot` (fixed order); a second kernel
+// sums the slots' rows.
 struct BwdArgs {
   const void *u, *delta, *B, *C, *z, *dy;  // activation dtype
   const float *A, *D, *bias, *h0, *dh_final;
@@ -56,13 +64,15 @@ struct BwdArgs {
   void *dz;                           // activation dtype output, or null
   void *du, *ddelta;                  // activation dtype outputs
   float *dh0;                         // (batch, dim, 16) or null
-  float *pB, *pC;                     // (batch, groups, 16, L) partial dB, dC
+  float *pB, *pC;                     // (batch, slots, N, L) partial dB, dC
   float *pA;                          // (batch, dim, n_chunks, 16) partial dA
   float *pD, *pbias;                  // (batch, dim, n_chunks) partial dD, dbias
   float *dA, *dB, *dC, *dD, *dbias;   // reduced outputs (dD, dbias: or null)
   int64_t batch, dim, L;
   int N;                              // d_state (<= kMaxStates: lane n % 64, register n / 64)
   int64_t groups;                     // ceil(dim / kBwdWaves)
+  int64_t slots;                      // partial-sum rows per batch entry (<= groups)
+  int64_t unit;                       // sweep launch: channel group slot + unit * slots
   int nblk;                           // ceil(L / 1024)
   int softplus;
   int zoh;                            // 1: exact ZOH input term
@@ -156,6 +166,7 @@ int launch_roofline_valu(int kind, float *out, int64_t threads, int iters,
 struct BwdLayout {
   int64_t ckpt_chunk, ckpt_chunks;    // checkpoint pass (a forward scan)
   int64_t chunk, n_chunks;            // sweep
+  int64_t slots;                      // dB/dC partial-sum rows per batch entry
   size_t off_ckpt, off_yc, off_pB, off_pC, off_pA, off_pD, off_pbias;
   size_t off_cks, off_H, off_S, off_hin;  // checkpoint pass split
   size_t off_mu0, off_Pc, off_muin;       // sweep split

@@ -365,8 +365,10 @@ def test_fwd_save_rejects_invalid_arguments(lib, name, kw, status):
 def test_bwd_workspace_size(lib):
     size = ctypes.c_size_t(0)
     assert lib.ssm_scan_bwd_workspace_size(2, 5120, 16, 4096, 1, ctypes.byref(size)) == 0
-    groups = 5120 // 8  # channels per backward workgroup
-    partials = 2 * (2 * groups * 16 * 4096 * 4)
+    # 640 groups of 8 channels per batch entry, swept in 5 launches of 128
+    # workgroups per batch entry: 128 partial-sum rows per batch entry
+    assert _bwd_slots(2, 5120, 1) == 128
+    partials = 2 * (2 * 128 * 16 * 4096 * 4)
     checkpoints = 2 * 5120 * 4 * 16 * 4
     pregate = 2 * 5120 * 4096 * 2  # bf16
     assert partials + checkpoints + pregate <= size.value < (
@@ -382,10 +384,34 @@ def _bwd_ws(lib, batch, dim, L, dtype):
     return size.value
 
 
-def _bwd_unsplit_bytes(batch, dim, L, es):
+def _bwd_slots(batch, dim, n_chunks):
+    """dB/dC partial-sum rows per batch entry: the most channel groups per
+    sweep workgroup (taken one launch after another) that need no more rounds
+    of 256 resident workgroups than one group per workgroup."""
+    groups = -(-dim // 8)
+    rounds = lambda slots: -(-(batch * n_chunks * slots) // 256)
+    best = groups
+    for u in range(2, min(groups, rounds(groups)) + 1):
+        slots = -(-groups // u)
+        if rounds(slots) * u <= rounds(groups):
+            best = slots
+    return best
+
+
+def test_bwd_slots_rule():
+    # 130M layer: 4 x 192 groups = 3 rounds -> 64 slots of 3 groups
+    assert _bwd_slots(4, 1536, 1) == 64
+    # long context, 4 sweep chunks: 4 x 192 -> 64
+    assert _bwd_slots(1, 1536, 4) == 64
+    # fewer groups than resident workgroups: one group per slot
+    assert _bwd_slots(1, 1536, 1) == 192
+    assert _bwd_slots(2, 13, 1) == 2
+
+
+def _bwd_unsplit_bytes(batch, dim, L, es, n_chunks=1):
     up = lambda x: (x + 255) // 256 * 256
-    bd, nblk, groups = batch * dim, -(-L // 1024), -(-dim // 8)
-    part = batch * groups * 16 * L * 4
+    bd, nblk = batch * dim, -(-L // 1024)
+    part = batch * _bwd_slots(batch, dim, n_chunks) * 16 * L * 4
     return (up(bd * nblk * 16 * 4) + up(bd * L * es) + 2 * up(part) +
             up(bd * 16 * 4) + 2 * up(bd * 4))
 
@@ -400,8 +426,11 @@ def test_bwd_workspace_split_regions(lib):
         assert _bwd_ws(lib, *shape, 1) == _bwd_unsplit_bytes(*shape, 2), shape
     # (1, 8, 16383): only the checkpoint pass splits (chunks of 8192 tokens;
     # the sweep splits from 2 x 8192)
-    for shape in [(1, 8, 16383), (1, 8, 25076), (2, 5, 20480), (1, 1536, 1 << 20)]:
-        got, base = _bwd_ws(lib, *shape, 0), _bwd_unsplit_bytes(*shape, 4)
+    # (the long-context shape sweeps 4 chunks: its partial-sum rows follow
+    # the 4 x 192 workgroups of one group each)
+    for shape, nc in [((1, 8, 16383), 1), ((1, 8, 25076), 1), ((2, 5, 20480), 1),
+                      ((1, 1536, 1 << 20), 4)]:
+        got, base = _bwd_ws(lib, *shape, 0), _bwd_unsplit_bytes(*shape, 4, nc)
         assert base < got < base * 1.05 + 2**20, shape
 
 
