@@ -1044,7 +1044,7 @@ def summarize_profiles(d):
 
     # HBM traffic from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by
     # what the same counter reads for the 1 GiB calibration copy.
-    def per_dispatch(sub, counter):
+    def per_dispatch(sub, counter, stat=statistics.median):
         vals = {}
         for f in _csvs(os.path.join(d, sub), "_counter_collection.csv"):
             for r in csv.DictReader(open(f)):
@@ -1052,7 +1052,7 @@ def summarize_profiles(d):
                     continue
                 k = _kernel_key(r["Kernel_Name"])
                 vals.setdefault(k, []).append(float(r["Counter_Value"]))
-        return {k: statistics.median(v) for k, v in vals.items()}
+        return {k: stat(v) for k, v in vals.items()}
     fetch = per_dispatch("fetch", "FETCH_SIZE")
     write = per_dispatch("write", "WRITE_SIZE")
     for k in (SCAN_KERNEL, COPY_KERNEL):
@@ -1136,12 +1136,14 @@ def summarize_profiles(d):
 
 def summarize_workload(d, rows, per_dispatch, fetch_scale, write_scale,
                        cmd_trace, prof, *, title, fname, keys, tag, only,
-                       alg_bytes, alg_note):
+                       alg_bytes, alg_note, per_call=None):
     """profiles/<fname>: the trace statistics (from the full benchmark run)
     of the kernels whose names start with one of ``keys``, and their HBM
     traffic per dispatch from the ``--<only> --steps 3`` counter passes under
     DIR/<tag>fetch and DIR/<tag>write, scaled by the same copy calibration
-    as the scan kernel's; every listed kernel runs once per call."""
+    as the scan kernel's.  A listed kernel runs once per call unless
+    ``per_call`` gives its dispatches per call (then its figure is the mean
+    dispatch times that count)."""
     import csv
     import statistics
 
@@ -1178,8 +1180,14 @@ def summarize_workload(d, rows, per_dispatch, fetch_scale, write_scale,
                 g + (len(v), statistics.mean(v), min(v), max(v), sum(v) / 1e3)))
     if not os.path.isdir(os.path.join(d, tag + "fetch")):
         return []
+    per_call = per_call or {}
     fetch = per_dispatch(tag + "fetch", "FETCH_SIZE")
     write = per_dispatch(tag + "write", "WRITE_SIZE")
+    if per_call:
+        fetch.update({k: v * per_call[k] for k, v in per_dispatch(
+            tag + "fetch", "FETCH_SIZE", statistics.mean).items() if k in per_call})
+        write.update({k: v * per_call[k] for k, v in per_dispatch(
+            tag + "write", "WRITE_SIZE", statistics.mean).items() if k in per_call})
     cmd = ("rocprofv3 --pmc {c} --output-format csv -d DIR/{d} -o {d} -- "
            "python3 bench.py --%s --steps 3" % only)
     txt += ["# HBM traffic per dispatch from (from /tmp, TMPDIR=/tmp):",
@@ -1194,7 +1202,9 @@ def summarize_workload(d, rows, per_dispatch, fetch_scale, write_scale,
         fb = fetch[k] * fetch_scale * 1024
         wb = write[k] * write_scale * 1024
         total += fb + wb
-        txt.append("%s: read %.1f MB, written %.1f MB" % (k, fb / 1e6, wb / 1e6))
+        txt.append("%s: read %.1f MB, written %.1f MB%s" % (
+            k, fb / 1e6, wb / 1e6,
+            " (%d dispatches per call)" % per_call[k] if k in per_call else ""))
     txt.append("per call: %.1f MB vs algorithmic %.1f MB (ratio %.3f; %s)"
                % (total / 1e6, alg_bytes / 1e6, total / alg_bytes, alg_note))
     with open(os.path.join(prof, fname), "w") as f:
@@ -1205,6 +1215,7 @@ def summarize_workload(d, rows, per_dispatch, fetch_scale, write_scale,
 def summarize_extras(d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace,
                      prof):
     """The SSD, decode and backward summaries under profiles/."""
+    import selective_state_space_30_amd as ssm
     import synthetic as syn
     scfg, dcfg, bcfg = syn.MAMBA2_LAYER, syn.DECODE, syn.MAMBA_2P8B
     out = []
@@ -1239,8 +1250,11 @@ def summarize_extras(d, rows, per_dispatch, fetch_scale, write_scale, cmd_trace,
         fname="bwd_kernels_%s.txt" % bcfg.name,
         keys=[BWD_KERNEL, "bwd_reduce", CKPT_KERNEL], tag="bwd", only="only-bwd",
         alg_bytes=syn.backward_bytes(bcfg),
-        alg_note="inputs and dy read, gradients written once; the per-group "
-                 "partial sums of dB and dC are extra by design")
+        alg_note="inputs and dy read, gradients written once; the partial "
+                 "sums of dB and dC (written by every sweep launch, read back "
+                 "by the next and by the reduction) are extra by design",
+        per_call={BWD_KERNEL: ssm.ssm_scan_bwd_plan(
+            bcfg.batch, bcfg.dim, bcfg.dstate, bcfg.seqlen)["sweep_launches"]})
     return out
 
 if __name__ == "__main__":

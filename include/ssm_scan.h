@@ -256,6 +256,18 @@ int ssm_conv_state_update(float *state, void *conv_state, const void *x,
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                 int64_t seqlen, int dtype, size_t *bytes);
 
+/* How ssm_scan_bwd will run this shape (no HIP call), in plan_out[4]:
+ *  [0] tokens per chunk of the reverse sweep (seqlen: not split)
+ *  [1] tokens per chunk of its checkpoint pass (a forward scan; seqlen: not
+ *      split)
+ *  [2] dB/dC partial-sum rows per batch entry (the workspace's partial sums)
+ *  [3] launches of the sweep kernel: launch k takes channel groups
+ *      k*[2] .. (k+1)*[2]-1 (8 channels a group), each adding into its
+ *      row, so the rows are sums in a fixed order
+ * Errors as ssm_scan_bwd_workspace_size (NULL plan_out: SSM_ERR_INVALID_ARG). */
+int ssm_scan_bwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                      int64_t *plan_out);
+
 /* Backward pass of ssm_scan_fwd: the gradients of
  * a scalar loss with respect to every input, given its gradient dy with
  * respect to y and dh_final (nullable -> 0) with respect to the final state.

@@ -55,7 +55,8 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED",
 EXPORTS = ("ssm_abi_version", "ssm_scan_plan", "ssm_scan_workspace_size",
            "ssm_scan_fwd", "ssm_conv_scan_fwd", "ssm_state_update",
            "ssm_conv_state_update",
-           "ssm_scan_bwd_workspace_size", "ssm_scan_fwd_save", "ssm_scan_bwd",
+           "ssm_scan_bwd_workspace_size", "ssm_scan_bwd_plan", "ssm_scan_fwd_save",
+           "ssm_scan_bwd",
            "ssm_ssd_workspace_size", "ssm_ssd_fwd", "ssm_last_error",
            "ssm_roofline_hbm", "ssm_roofline_valu", "ssm_scan_fwd_noalloc",
            "ssm_conv_scan_bwd_workspace_size", "ssm_conv_scan_bwd")
@@ -118,6 +119,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.ssm_scan_bwd_workspace_size.argtypes = [
             I64, I64, I64, I64, I, ctypes.POINTER(ctypes.c_size_t)]
         lib.ssm_scan_bwd_workspace_size.restype = I
+        lib.ssm_scan_bwd_plan.argtypes = [I64, I64, I64, I64, ctypes.POINTER(I64)]
+        lib.ssm_scan_bwd_plan.restype = I
         lib.ssm_scan_bwd.argtypes = ([P] * 8 + [U] + [P] * 12 +
                                      [I64, I64, I64, I64, I, P,
                                       ctypes.c_size_t, P])
@@ -452,6 +455,16 @@ def ssm_scan_bwd_workspace_size(batch, dim, dstate, seqlen,
     _check(load_library().ssm_scan_bwd_workspace_size(
         batch, dim, dstate, seqlen, code, ctypes.byref(out)))
     return out.value
+
+
+def ssm_scan_bwd_plan(batch, dim, dstate, seqlen) -> dict:
+    """How :func:`ssm_scan_bwd` runs this shape: sweep and checkpoint-pass
+    chunk lengths (seqlen = not split), dB/dC partial-sum rows per batch
+    entry, and launches of the sweep kernel."""
+    out = (ctypes.c_int64 * 4)()
+    _check(load_library().ssm_scan_bwd_plan(batch, dim, dstate, seqlen, out))
+    return {"sweep_chunk": out[0], "ckpt_chunk": out[1],
+            "partial_rows": out[2], "sweep_launches": out[3]}
 
 
 @_on_stream

@@ -611,6 +611,20 @@ int ssm_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
   return ok();
 }
 
+int ssm_scan_bwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                      int64_t *plan_out) {
+  if (!plan_out) return fail(SSM_ERR_INVALID_ARG, "plan_out is NULL");
+  int st = check_bwd_sizes(batch, dim, dstate, seqlen);
+  if (st != SSM_OK) return st;
+  const ssm::BwdLayout l = ssm::bwd_layout(batch, dim, dstate, seqlen, 4);
+  const int64_t groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
+  plan_out[0] = l.chunk;
+  plan_out[1] = l.ckpt_chunk;
+  plan_out[2] = l.slots;
+  plan_out[3] = (groups + l.slots - 1) / l.slots;
+  return ok();
+}
+
 }  // extern "C"
 
 namespace {

@@ -408,6 +408,29 @@ def test_bwd_slots_rule():
     assert _bwd_slots(2, 13, 1) == 2
 
 
+def test_bwd_plan(lib):
+    """The backward's plan: partial-sum rows and sweep launches follow the
+    rule above; the rows size the workspace."""
+    for shape, nc in [((2, 5120, 4096), 1), ((4, 1536, 2048), 1), ((1, 2056, 1100), 1),
+                      ((2, 2056, 600), 1), ((2, 13, 2100), 1), ((1, 1536, 1 << 20), 4)]:
+        p = ssm.ssm_scan_bwd_plan(shape[0], shape[1], 16, shape[2])
+        rows = _bwd_slots(shape[0], shape[1], nc)
+        groups = -(-shape[1] // 8)
+        assert p["partial_rows"] == rows, shape
+        assert p["sweep_launches"] == -(-groups // rows), shape
+        assert (p["sweep_chunk"] == shape[2]) == (nc == 1), shape
+    p = ssm.ssm_scan_bwd_plan(2, 5120, 16, 4096)
+    assert p == {"sweep_chunk": 4096, "ckpt_chunk": 4096, "partial_rows": 128,
+                 "sweep_launches": 5}
+    # the long-context shape: 8 checkpoint-pass chunks, 4 sweep chunks
+    p = ssm.ssm_scan_bwd_plan(1, 1536, 16, 1 << 20)
+    assert (p["ckpt_chunk"], p["sweep_chunk"]) == (1 << 17, 1 << 18)
+    out = (ctypes.c_int64 * 4)()
+    assert lib.ssm_scan_bwd_plan(1, 16, 16, 256, None) == 1
+    assert lib.ssm_scan_bwd_plan(1, 16, 257, 256, out) == 2
+    assert lib.ssm_scan_bwd_plan(0, 16, 16, 256, out) == 1
+
+
 def _bwd_unsplit_bytes(batch, dim, L, es, n_chunks=1):
     up = lambda x: (x + 255) // 256 * 256
     bd, nblk = batch * dim, -(-L // 1024)

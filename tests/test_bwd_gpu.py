@@ -81,6 +81,12 @@ CASES = [
     (2, 1, 300, "f32", 1, 1, 1, 1, 1, 1),     # one channel: 7 of 8 waves idle
     (2, 20, 3072, "bf16", 1, 1, 1, 1, 1, 1),
     (1, 9, 1500, "bf16", 1, 1, 0, 0, 1, 1),
+    # 257 channel groups: 129 partial-sum rows taken in 2 sweep launches,
+    # the last row holding a single group
+    (1, 2056, 1100, "f32", 1, 1, 1, 1, 1, 1),
+    # 2 x 257 groups: 86 rows per batch entry over 3 launches, the last row
+    # holding 2 groups
+    (2, 2056, 600, "bf16", 1, 1, 1, 0, 1, 1),
 ]
 
 
@@ -336,7 +342,10 @@ def _unsplit_ws_bytes(batch, dim, L, es):
     pre-gate output, dB/dC partials, per-channel partials; 256-byte
     aligned regions)."""
     up = lambda x: (x + 255) // 256 * 256
+    # (the split shapes here have one channel group: one partial-sum row
+    # per batch entry)
     bd, nblk, groups = batch * dim, -(-L // 1024), -(-dim // 8)
+    assert groups == 1
     part = batch * groups * 16 * L * 4
     return (up(bd * nblk * 16 * 4) + up(bd * L * es) + 2 * up(part) +
             up(bd * 16 * 4) + 2 * up(bd * 4))
