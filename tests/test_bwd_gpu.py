@@ -128,6 +128,32 @@ def test_bwd_bitwise_deterministic():
         assert torch.equal(g1[k], g2[k]), k
 
 
+@pytest.mark.parametrize("shape", [(2, 2056, 600), (4, 1536, 1100)],
+                         ids=["b2_d2056_l600", "b4_d1536_l1100"])
+def test_bwd_ignores_workspace_contents(shape):
+    """Shapes whose sweep runs in several launches (partial-sum rows added
+    into by later launches): a workspace holding NaN bytes on entry gives
+    bitwise the gradients of a zeroed one -- the first launch writes every
+    row it owns before any later launch reads it."""
+    batch, dim, L = shape
+    p = ssm.ssm_scan_bwd_plan(batch, dim, 16, L)
+    assert p["sweep_launches"] > 1
+    inp = to_dev(make(batch, dim, L, "bf16", 31))
+    nbytes = ssm.ssm_scan_bwd_workspace_size(batch, dim, 16, L, torch.bfloat16)
+    grads = []
+    for fill in (0x00, 0xFF):  # 0xFFFFFFFF is a NaN as fp32
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        g = ssm.ssm_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                             inp["D"], inp["z"], inp["delta_bias"],
+                             inp["delta_softplus"], inp["h0"], inp["dy"],
+                             inp["dh_final"], workspace=ws)
+        torch.cuda.synchronize()
+        grads.append(g)
+    for k in grads[0]:
+        assert torch.equal(grads[0][k], grads[1][k]), k
+        assert bool(torch.isfinite(grads[1][k]).all()), k
+
+
 def _sampled_channels(cfg, r, k=8):
     return sorted({(0, 0), (cfg.batch - 1, cfg.dim - 1)} |
                   {(int(r.integers(cfg.batch)), int(r.integers(cfg.dim)))
