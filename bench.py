@@ -42,7 +42,12 @@ Profiling commands (run from /tmp with TMPDIR=/tmp; DIR = an output folder):
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/ssdwrite -o ssdwrite \
       -- python3 bench.py --only-ssd --steps 3
   (the same two passes with --only-decode into DIR/decodefetch and
-  DIR/decodewrite, and with --only-bwd into DIR/bwdfetch and DIR/bwdwrite)
+  DIR/decodewrite, and with --only-bwd into DIR/bwdfetch and DIR/bwdwrite;
+  and, for the SQ counters of those kernels, one pass each of
+  --pmc SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_VALU_TRANS_F32
+  SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES
+  SQ_LDS_BANK_CONFLICT with --only-bwd, --only-ssd and --only-decode into
+  DIR/bwdsq, DIR/ssdsq and DIR/decodesq)
   python3 bench.py --summarize DIR
 """
 from __future__ import annotations
@@ -1207,8 +1212,43 @@ def summarize_workload(d, rows, per_dispatch, fetch_scale, write_scale,
             " (%d dispatches per call)" % per_call[k] if k in per_call else ""))
     txt.append("per call: %.1f MB vs algorithmic %.1f MB (ratio %.3f; %s)"
                % (total / 1e6, alg_bytes / 1e6, total / alg_bytes, alg_note))
+    txt += summarize_sq(d, per_dispatch, rows, tag + "sq", only, match)
     with open(os.path.join(prof, fname), "w") as f:
         f.write("\n".join(txt) + "\n")
+    return txt
+
+
+SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_TRANS_F32",
+               "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES",
+               "SQ_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT"]
+
+
+def summarize_sq(d, per_dispatch, rows, sub, only, match):
+    """SQ counters per dispatch (mean over the --<only> --steps 3 run under
+    DIR/<sub>) of the matching kernels, with the VALU issue time they imply
+    (4 cycles per wave64 issue slot over 1024 SIMDs at 2.4 GHz) beside the
+    kernel-trace average: how busy the VALU keeps each kernel."""
+    import statistics
+    if not os.path.isdir(os.path.join(d, sub)):
+        return []
+    vals = {c: per_dispatch(sub, c, statistics.mean) for c in SQ_COUNTERS}
+    avg_us = {_kernel_key(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
+    txt = ["# SQ counters per dispatch (mean), from (from /tmp, TMPDIR=/tmp):",
+           "#   rocprofv3 --pmc %s --output-format csv -d DIR/%s -o %s -- "
+           "python3 bench.py --%s --steps 3" % (" ".join(SQ_COUNTERS), sub, sub, only)]
+    for k in sorted(vals["SQ_ACTIVE_INST_VALU"]):
+        if not match(k) or any(k not in vals[c] for c in SQ_COUNTERS):
+            continue
+        txt.append("%s:" % k)
+        txt += ["  %-24s %16.0f" % (c, vals[c][k]) for c in SQ_COUNTERS]
+        busy_us = vals["SQ_ACTIVE_INST_VALU"][k] * 4 / (1024 * 2.4e9) * 1e6
+        line = "  VALU issue time %.1f us" % busy_us
+        if k in avg_us:
+            line += " against a kernel-trace average of %.1f us (%.0f %% busy)" % (
+                avg_us[k], 100.0 * busy_us / avg_us[k])
+        txt.append(line)
+        txt.append("  waiting share SQ_WAIT_ANY / SQ_WAVE_CYCLES %.2f" % (
+            vals["SQ_WAIT_ANY"][k] / max(vals["SQ_WAVE_CYCLES"][k], 1.0)))
     return txt
 
 
