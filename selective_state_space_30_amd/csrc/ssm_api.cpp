@@ -135,12 +135,13 @@ int64_t bwd_chunk(int64_t batch, int64_t dim, int64_t seqlen) {
   return best.chunk;
 }
 
-// dB/dC partial-sum rows per batch entry.  Each sweep workgroup takes u
-// channel groups one after another and adds them into one row, so the
-// reduction reads groups / u rows instead of groups.  u is the largest
-// count that needs no more rounds of kBwdResident workgroups than one group
-// per workgroup does (the 2.8B layer: 1280 groups in 5 rounds -> 256
-// workgroups of 5 groups each).
+// dB/dC partial-sum rows per batch entry.  The sweep is launched u times,
+// each launch taking `slots` channel groups per batch entry and adding
+// group slot + k * slots into row `slot`, so the reduction reads
+// ceil(groups / u) rows instead of groups.  u is the largest count whose u
+// launches need no more rounds of kBwdResident workgroups than a single
+// launch of every group does (the 2.8B layer: 2 x 640 groups, 5 rounds ->
+// 5 launches of 2 x 128 workgroups).
 int64_t bwd_slots(int64_t batch, int64_t dim, int64_t n_chunks) {
   const int64_t groups = (dim + ssm::kBwdWaves - 1) / ssm::kBwdWaves;
   const int64_t per_slot = batch * n_chunks;  // workgroups of one slot index

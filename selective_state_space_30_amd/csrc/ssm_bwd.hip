@@ -29,8 +29,9 @@
 // each lane the mu entering from its right.  dB and dC are sums over all
 // channels of a batch entry: after each state the 8 channels of a workgroup
 // write their contributions to LDS, the workgroup sums them in a fixed order
-// (no atomics: deterministic) into a per-workgroup partial sum, and a
-// reduction kernel sums the partials.
+// (no atomics: deterministic) and adds them into its slot's partial-sum row
+// (the sweep runs as several launches in a row, each giving every slot its
+// next channel group), and a reduction kernel sums the slots' rows.
 //
 // Sequence split (few channels, long sequences): the tokens are cut into
 // block-aligned chunks swept in parallel.  The reverse recurrence is linear
