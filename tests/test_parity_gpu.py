@@ -284,6 +284,32 @@ def test_long_context_workload_sampled():
     assert torch.isfinite(y).all() and torch.isfinite(hf).all()
 
 
+def test_long_context_workload_whole_output():
+    """The long-context workload on every element: all 1536 channels x 2^20
+    tokens of y and every final state, against the oracle in ranges of 96
+    channels (each range's inputs converted to fp64 on its own, so the
+    host holds ~4 GB at a time; the scaled error takes each range's rms,
+    over 1e8 elements of one distribution).  Every chunk boundary, fix-up
+    length and wave position of the launch is covered."""
+    cfg = syn.LONG_1M
+    assert ssm.ssm_scan_plan(cfg.batch, cfg.dim, 16, cfg.seqlen) < cfg.seqlen
+    inp = syn.make_scan_inputs(cfg, DEV)
+    y, hf = gpu_scan(inp)
+    step = 96
+    worst = 0.0
+    for d0 in range(0, cfg.dim, step):
+        d1 = min(cfg.dim, d0 + step)
+        sl = lambda t: None if t is None else t[:, d0:d1].contiguous()
+        y_ref, h_ref, _ = oracle.scan_threaded(
+            sl(inp["u"]), sl(inp["delta"]), inp["A"][d0:d1], inp["B"], inp["C"],
+            inp["D"][d0:d1], sl(inp["z"]), inp["delta_bias"][d0:d1]
+            if inp["delta_bias"] is not None else None,
+            inp["delta_softplus"], False, sl(inp["h0"]), threads=HOST_THREADS)
+        worst = max(worst, check(y[:, d0:d1], y_ref, 1e-4, "y channels %d..%d" % (d0, d1)))
+        check(hf[:, d0:d1], h_ref, 1e-4, "h_final channels %d..%d" % (d0, d1))
+    print("long context, whole output: worst scaled error %.3g" % worst)
+
+
 def test_chunked_mixed_fixup_lengths_in_one_launch():
     """One launch with 8 chunks per channel in which some channels stop
     their fix-up early (A < 0, fast decay), some run it over the whole chunk
