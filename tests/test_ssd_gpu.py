@@ -10,6 +10,8 @@ Bar: 2e-2 on the scaled error (bf16 activations; the chunk products take
 bf16 operands -- G, the state, G's decay-scaled columns and x w as bf16
 pairs -- with fp32 accumulation, the carried state is fp32).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -162,6 +164,28 @@ def test_ssd_layer_workload_sampled():
         check(y[b, h, p:p + 1], yr[0], "y (b=%d h=%d p=%d)" % (b, h, p))
         check(hf[b, h, p:p + 1], hr[0], "h_final (b=%d h=%d p=%d)" % (b, h, p))
     assert torch.isfinite(y.float()).all()
+
+
+def test_ssd_layer_workload_whole_output():
+    """The Mamba-2 layer workload on every element: its 2 x 80 heads x 64
+    rows are 10240 one-channel Mamba-1 scans with the head's A broadcast over
+    the 128 states (the recurrence the SSD oracle is pinned to), run by the
+    threaded scan oracle over all of them; y and every final state."""
+    cfg = syn.MAMBA2_LAYER
+    assert cfg.ngroups == 1
+    inp = syn.make_ssd_inputs(cfg, DEV)
+    y, hf = gpu_ssd(inp)
+    b, H, P, N, L = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.seqlen
+    rows = lambda t: t.repeat_interleave(P)  # per head -> per head row
+    y_ref, h_ref, _ = oracle.scan_threaded(
+        inp["x"].reshape(b, H * P, L),
+        inp["dt"][:, :, None, :].expand(b, H, P, L).reshape(b, H * P, L),
+        rows(inp["A"])[:, None].expand(H * P, N).contiguous(),
+        inp["B"][:, 0], inp["C"][:, 0], rows(inp["D"]),
+        inp["z"].reshape(b, H * P, L), rows(inp["dt_bias"]), True, False, None,
+        threads=min(16, os.cpu_count() or 1))
+    check(y.reshape(b, H * P, L), y_ref, "y (all %d elements)" % y_ref.size)
+    check(hf.reshape(b, H * P, N), h_ref, "h_final (all %d elements)" % h_ref.size)
 
 
 def test_ssd_more_than_2_31_elements():
