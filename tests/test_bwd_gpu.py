@@ -14,6 +14,8 @@ far below the fp32 bar at these sizes.
 """
 from dataclasses import replace
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -206,6 +208,48 @@ def test_bwd_layer_workload_sampled(cfg):
               np.array([sum(x["ddelta_bias"][0] for x in refs)]), 1e-4,
               "dbias[%d]" % d)
     assert all(torch.isfinite(v.float()).all() for v in got.values())
+
+
+@pytest.mark.parametrize("cfg", [syn.MAMBA_130M, syn.MAMBA_2P8B],
+                         ids=lambda c: c.name)
+def test_bwd_layer_workload_whole_output(cfg):
+    """Every gradient of the Mamba-layer workloads on every element: the
+    oracle's backward over ranges of 160 channels on host threads (each
+    range exact for its channels' du, ddelta, dz, dh0, dA, dD, dbias; its dB
+    and dC are that range's share of the channel sums, added in fp64)."""
+    from concurrent.futures import ThreadPoolExecutor
+    inp = syn.make_scan_inputs(cfg, DEV, with_h0=True)
+    g = torch.Generator(device=DEV).manual_seed(cfg.seed + 5)
+    inp["dy"] = torch.randn(cfg.batch, cfg.dim, cfg.seqlen, generator=g,
+                            device=DEV).to(inp["u"].dtype)
+    inp["dh_final"] = torch.randn(cfg.batch, cfg.dim, 16, generator=g,
+                                  device=DEV)
+    got = gpu_bwd(inp)
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    step = 160
+    ranges = [(d0, min(cfg.dim, d0 + step)) for d0 in range(0, cfg.dim, step)]
+
+    def run(r):
+        d0, d1 = r
+        sl = lambda t: t[:, d0:d1]
+        return oracle.scan_bwd(sl(host["u"]), sl(host["delta"]), host["A"][d0:d1],
+                               host["B"], host["C"], host["D"][d0:d1], sl(host["z"]),
+                               host["delta_bias"][d0:d1], True, sl(host["h0"]),
+                               sl(host["dy"]), sl(host["dh_final"]))
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        parts = list(ex.map(run, ranges))
+    ref = {k: np.concatenate([p[k] for p in parts], axis=1)
+           for k in ("du", "ddelta", "dz", "dh0")}
+    ref.update({k: np.concatenate([p[k] for p in parts], axis=0)
+                for k in ("dA", "dD", "ddelta_bias")})
+    ref["dB"] = sum(p["dB"] for p in parts)
+    ref["dC"] = sum(p["dC"] for p in parts)
+    # du, ddelta, dz are stored in the activation dtype (its bar); the rest
+    # are fp32 outputs (measured at ~2e-6 of the fp32 bar's 1e-4)
+    for k in ("du", "ddelta", "dz"):
+        check(got[k], ref[k], TOL[cfg.dtype], "%s (all %d elements)" % (k, ref[k].size))
+    for k in ("dh0", "dA", "dD", "ddelta_bias", "dB", "dC"):
+        check(got[k], ref[k], TOL["f32"], "%s (all %d elements)" % (k, ref[k].size))
 
 
 @pytest.mark.parametrize("L", [2048, 2100], ids=lambda L: "l%d" % L)
