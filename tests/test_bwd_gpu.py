@@ -156,6 +156,45 @@ def test_bwd_ignores_workspace_contents(shape):
         assert bool(torch.isfinite(grads[1][k]).all()), k
 
 
+def test_bwd_replays_in_a_hip_graph():
+    """A training step captured once and replayed: the backward of a shape
+    whose sweep runs in 3 launches (the checkpoint pass, the launches adding
+    into the partial-sum rows, the reductions; kernels only, no memsets)
+    captured into a graph and replayed three times, with the outputs and
+    the workspace overwritten and eager work between the replays; every
+    replay gives the eager gradients bit for bit."""
+    batch, dim, L = 2, 2056, 600
+    assert ssm.ssm_scan_bwd_plan(batch, dim, 16, L)["sweep_launches"] == 3
+    inp = to_dev(make(batch, dim, L, "bf16", 61))
+    side = torch.cuda.Stream()
+    ws = torch.empty(ssm.ssm_scan_bwd_workspace_size(batch, dim, 16, L, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+
+    def call(out=None):
+        return ssm.ssm_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                inp["D"], inp["z"], inp["delta_bias"],
+                                inp["delta_softplus"], inp["h0"], inp["dy"],
+                                inp["dh_final"], out=out, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        out = call()
+    side.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call(out)
+    for rep in range(3):
+        for v in out.values():
+            v.fill_(rep + 7)
+        ws.fill_(0xFF)
+        _ = (inp["dy"].float() * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), (rep, k)
+
+
 def _sampled_channels(cfg, r, k=8):
     return sorted({(0, 0), (cfg.batch - 1, cfg.dim - 1)} |
                   {(int(r.integers(cfg.batch)), int(r.integers(cfg.dim)))
