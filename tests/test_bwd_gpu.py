@@ -367,7 +367,7 @@ def test_fwd_save_then_bwd_skips_the_checkpoint_pass(case):
 
 def test_bwd_more_than_2_31_elements():
     """1100 channels x 2^21 tokens (2.3e9 elements per activation tensor,
-    ~40 GB of workspace): the per-channel gradients of sampled channels,
+    a 14 GB workspace): the per-channel gradients of sampled channels,
     including the last one, against the oracle."""
     from dataclasses import replace
     cfg = replace(syn.MAMBA_2P8B, batch=1, dim=1100, seqlen=1 << 21)
