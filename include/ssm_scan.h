@@ -185,6 +185,9 @@ int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A,
  *  x        required, activation dtype (batch, dim, seqlen)
  *  conv_w   required fp32 (dim, d_conv); conv_b nullable fp32 (dim)
  *  d_conv   1..4 (SSM_ERR_UNSUPPORTED above 4)
+ *  dstate   1..64 here (SSM_ERR_UNSUPPORTED above: with more states the
+ *           fused prologue gave intermittent wrong outputs near the start
+ *           of the sequence, cause not yet found)
  * All other arguments, conventions, the chunk plan and the workspace are
  * those of ssm_scan_fwd. */
 int ssm_conv_scan_fwd(const void *x, const float *conv_w, const float *conv_b,
